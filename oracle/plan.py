@@ -1,0 +1,85 @@
+"""Host decisions around the layer: hot read and arena re-plan -- oracle side.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+hot_read follows the TideLM README's "How adaptive expert loading works",
+item 3, GLM-5.3 bullet: a layer's heaviest miss carrying at least 0.2 of a
+token's routing weight is read before that layer's experts run and is kept in
+place of the coldest expert.  replan follows item 1: one arena is shared by
+all layers, re-planned from the demand history, so a busy layer takes slots
+from a quiet one.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def pick_shares(p: np.ndarray, topk_expert: np.ndarray) -> np.ndarray:
+    """share[t,j] = p[t,e_j] / sum over the token's unrestricted picks."""
+    v = np.take_along_axis(p, topk_expert, axis=1)
+    return v / v.sum(axis=1, keepdims=True)
+
+
+def hot_read(p, topk_expert, expert_slot, hist_after, n_arena, threshold=0.2):
+    """O12.  Returns (e_star, c, new_expert_slot) or None when no miss qualifies.
+
+    e_star: the non-routable expert with the largest share >= threshold over
+    all tokens (ties: lower expert id, then lower token).  c: the arena-resident
+    expert (slot < n_arena; hot-ring slots excluded) with the smallest demand
+    history, ties to the lower id.  e_star takes c's slot; c becomes
+    non-routable.
+    """
+    es = np.asarray(expert_slot)
+    share = pick_shares(p, topk_expert)
+    best = None  # (share, -e, -t) maximised
+    T, k = topk_expert.shape
+    for t in range(T):
+        for j in range(k):
+            e = int(topk_expert[t, j])
+            if es[e] >= 0 or share[t, j] < threshold:
+                continue
+            key = (share[t, j], -e, -t)
+            if best is None or key > best:
+                best = key
+    if best is None:
+        return None
+    e_star = -best[1]
+    arena = [e for e in range(es.shape[0]) if 0 <= es[e] < n_arena]
+    c = min(arena, key=lambda e: (hist_after[e], e))
+    new = es.copy()
+    new[e_star] = es[c]
+    new[c] = -1
+    return e_star, c, new
+
+
+def replan(hist: np.ndarray, expert_slot: np.ndarray, n_swap: int, k: int):
+    """O13 over a [L,E] demand history and [L,E] slot table.
+
+    Evict the n_swap resident (l,e) with the smallest history (ties: lower
+    (l,e)), skipping any eviction that would leave a layer with fewer than k
+    routable experts; load the n_swap non-resident (l,e) with the largest
+    history (ties: lower (l,e)).  The i-th evicted slot receives the i-th
+    loaded pair.  Returns (evicted list, loaded list, new slot table).
+    """
+    hist = np.asarray(hist, dtype=np.float64)
+    es = np.asarray(expert_slot)
+    L, E = es.shape
+    res = [(hist[l, e], l, e) for l in range(L) for e in range(E) if es[l, e] >= 0]
+    non = [(-hist[l, e], l, e) for l in range(L) for e in range(E) if es[l, e] < 0]
+    res.sort()
+    non.sort()
+    count = (es >= 0).sum(axis=1)
+    evicted = []
+    for _, l, e in res:
+        if len(evicted) == n_swap:
+            break
+        if count[l] - 1 < k:
+            continue
+        count[l] -= 1
+        evicted.append((l, e))
+    loaded = [(l, e) for _, l, e in non[:len(evicted)]]
+    new = es.copy()
+    for (le, ee), (ll, el) in zip(evicted, loaded):
+        new[ll, el] = es[le, ee]
+        new[le, ee] = -1
+    return evicted, loaded, new

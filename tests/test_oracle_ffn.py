@@ -1,0 +1,111 @@
+"""Pins for the oracle's expert FFN, combine and whole-layer assembly (CPU only).
+
+Brute force with Python scalar loops and math.fsum on tiny shapes, textbook
+SwiGLU special cases, and the identical-experts invariant (when every routable
+slot holds the same expert, the layer output is that expert's FFN of the
+token, whatever the routing, because the renormalised weights sum to one).
+"""
+import math
+
+import numpy as np
+
+import fixtures
+from oracle import moe, mxfp4
+
+
+def _weights(H, I, seed):
+    return fixtures.expert_weights(seed, 0, H, I)
+
+
+def _quantise_scalar(vals):
+    """Encode/decode one row via the oracle encoder (pinned in test_oracle_mxfp4)."""
+    return list(mxfp4.quantise(np.array([vals], dtype=np.float64))[0])
+
+
+def brute_ffn(xhat_row, wg, wu, wd):
+    I, H = wg.shape
+    g = [math.fsum(xhat_row[h] * wg[i, h] for h in range(H)) for i in range(I)]
+    u = [math.fsum(xhat_row[h] * wu[i, h] for h in range(H)) for i in range(I)]
+    h = [gi / (1.0 + math.exp(-gi)) * ui for gi, ui in zip(g, u)]
+    hq = _quantise_scalar(h)
+    return [math.fsum(hq[i] * wd[n, i] for i in range(I)) for n in range(wd.shape[0])]
+
+
+def check_ffn_bruteforce():
+    H, I = 64, 32
+    for seed in range(3):
+        buf = fixtures.pack_expert(*_weights(H, I, 50 + seed))
+        W = moe.decode_expert(buf, H, I)
+        x = fixtures.draw_tokens(seed, 3, H)
+        xhat = moe.quantise_rows(moe.bf16_to_f64(x))
+        y = moe.expert_ffn(xhat, W)
+        for t in range(3):
+            ref = brute_ffn(list(xhat[t]), *W)
+            assert np.allclose(y[t], ref, rtol=1e-12, atol=1e-15), seed
+
+
+def test_ffn_bruteforce():
+    check_ffn_bruteforce()
+
+
+def test_silu_zero_and_zero_gate():
+    assert moe.silu(np.array([0.0]))[0] == 0.0
+    H, I = 64, 32
+    wg, wu, wd = _weights(H, I, 60)
+    W = moe.decode_expert(fixtures.pack_expert(np.zeros_like(wg), wu, wd), H, I)
+    xhat = moe.quantise_rows(moe.bf16_to_f64(fixtures.draw_tokens(1, 4, H)))
+    assert (moe.expert_ffn(xhat, W) == 0).all()
+    W = moe.decode_expert(fixtures.pack_expert(wg, np.zeros_like(wu), wd), H, I)
+    assert (moe.expert_ffn(xhat, W) == 0).all()
+
+
+def test_k1_single_expert_is_textbook_swiglu():
+    """k = 1 and one routable expert: the layer is that expert's SwiGLU MLP."""
+    H, I, E = 64, 32, 5
+    lay = fixtures.tiny_layer(T=6, H=H, E=E, k=1, I=I, n_routable=1, seed=12)
+    buf = fixtures.pack_expert(*_weights(H, I, 70))
+    r = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, 1, lambda s: buf, H, I,
+                  act="bf16")
+    wg, wu, wd = moe.decode_expert(buf, H, I)
+    x = moe.bf16_to_f64(lay.x_bits)
+    g = x @ wg.T
+    textbook = (g * (1 / (1 + np.exp(-g))) * (x @ wu.T)) @ wd.T
+    assert np.allclose(r["out"], textbook, rtol=1e-13, atol=1e-16)
+    assert (r["sel_weight"][:, 0] == 1.0).all()
+
+
+def check_identical_experts():
+    H, I, E, k = 64, 32, 12, 4
+    buf = fixtures.pack_expert(*_weights(H, I, 80))
+    W = moe.decode_expert(buf, H, I)
+    for seed, nr in ((1, 12), (2, 7), (3, 4)):
+        lay = fixtures.tiny_layer(T=10, H=H, E=E, k=k, I=I, n_routable=nr, seed=seed, bias_scale=1.0)
+        r = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k, lambda s: buf, H, I)
+        xhat = moe.quantise_rows(moe.bf16_to_f64(lay.x_bits))
+        assert np.allclose(r["out"], moe.expert_ffn(xhat, W), rtol=1e-12, atol=1e-15)
+
+
+def test_identical_experts_invariant():
+    check_identical_experts()
+
+
+def test_combine_order_and_padding():
+    y = np.arange(2 * 3 * 4, dtype=np.float64).reshape(2, 3, 4)
+    w = np.array([[0.5, 0.25, 0.25], [1.0, 0.0, 0.0]])
+    se = np.array([[1, 2, 3], [4, -1, -1]])
+    y[1, 1:] = np.nan    # padded picks are never read
+    out = moe.combine(y, w, se)
+    assert np.array_equal(out[0], 0.5 * y[0, 0] + 0.25 * y[0, 1] + 0.25 * y[0, 2])
+    assert np.array_equal(out[1], y[1, 0])
+
+
+def test_decode_expert_sections():
+    H, I = 64, 32
+    wg, wu, wd = _weights(H, I, 90)
+    buf = fixtures.pack_expert(wg, wu, wd)
+    g, u, d = moe.decode_expert(buf, H, I)
+    assert g.shape == (I, H) and u.shape == (I, H) and d.shape == (H, I)
+    # each decoded matrix is its float32 source quantised row-wise
+    for got, src in ((g, wg), (u, wu), (d, wd)):
+        assert np.array_equal(got, mxfp4.quantise(src.astype(np.float64)))
+        assert np.abs(got - src).max() <= np.abs(src).max() / 2   # coarse but tight enough

@@ -1,0 +1,105 @@
+"""The pins are strong enough: plant plausible mistakes in the oracle (on the CPU,
+via monkeypatch) and check that a pin fails for each one."""
+import numpy as np
+import pytest
+
+from oracle import moe, mxfp4
+import test_oracle_ffn as tf
+import test_oracle_mxfp4 as tm
+import test_oracle_routing as tr
+
+
+def _fails(check):
+    with pytest.raises(AssertionError):
+        check()
+
+
+def test_wrong_e2m1_value(monkeypatch):
+    bad = mxfp4.VALUE.copy()
+    bad[5] = 2.5
+    monkeypatch.setattr(mxfp4, "VALUE", bad)
+    _fails(tm.check_decode_exhaustive)
+
+
+def test_wrong_scale_bias(monkeypatch):
+    orig = mxfp4.decode
+
+    def dec(p, s):
+        return orig(p, np.minimum(np.asarray(s, dtype=np.int64) + 1, 254).astype(np.uint8))
+    monkeypatch.setattr(mxfp4, "decode", dec)
+    _fails(tm.check_decode_exhaustive)
+
+
+def test_wrong_tie_rule(monkeypatch):
+    monkeypatch.setattr(mxfp4, "_MANT_ODD", 1 - mxfp4._MANT_ODD)
+    _fails(tm.check_encode_golden)
+    _fails(tm.check_bf16_window)
+
+
+def test_wrong_scale_exponent(monkeypatch):
+    orig = np.frexp
+
+    class NP:  # frexp off by one inside the encoder only
+        def __getattr__(self, k):
+            return getattr(np, k)
+
+        @staticmethod
+        def frexp(a):
+            m, e = orig(a)
+            return m, e + 1
+    monkeypatch.setattr(mxfp4, "np", NP())
+    _fails(tm.check_roundtrip)
+
+
+def test_dropped_bias(monkeypatch):
+    orig = moe.router_logits
+    monkeypatch.setattr(moe, "router_logits", lambda x, w, b=None: orig(x, w, None))
+    _fails(tr.check_logits_fsum)
+
+
+def test_reversed_ties(monkeypatch):
+    def bad(z_row, allowed=None):
+        ids = np.arange(z_row.shape[0]) if allowed is None else np.flatnonzero(allowed)
+        order = np.argsort(-z_row[ids][::-1], kind="stable")[::-1][::-1]
+        return ids[::-1][order]
+    monkeypatch.setattr(moe, "rank_order", bad)
+    _fails(tr.check_topk_bruteforce)
+
+
+def test_missing_renormalisation(monkeypatch):
+    monkeypatch.setattr(moe, "renormalise", lambda p, picks: moe.gather(p, picks))
+    _fails(tr.check_softmax_and_renorm)
+
+
+def test_demand_skips_a_pick(monkeypatch):
+    orig = moe.demand
+    monkeypatch.setattr(moe, "demand", lambda te, ts, E: orig(te[:, 1:], ts[:, 1:], E))
+    _fails(tr.check_demand)
+
+
+def test_unstable_bucket(monkeypatch):
+    def bad(sel_slot, S):
+        c, o, p = orig(sel_slot, S)
+        for s in range(S):
+            p[o[s]:o[s + 1]] = p[o[s]:o[s + 1]][::-1]
+        return c, o, p
+    orig = moe.bucket
+    monkeypatch.setattr(moe, "bucket", bad)
+    _fails(tr.check_bucket)
+
+
+def test_wrong_silu_sign(monkeypatch):
+    monkeypatch.setattr(moe, "silu", lambda v: v / (1.0 + np.exp(v)))
+    _fails(tf.check_ffn_bruteforce)
+
+
+def test_gate_up_swapped(monkeypatch):
+    orig = moe.expert_ffn
+    monkeypatch.setattr(moe, "expert_ffn", lambda x, W, act="mxfp4": orig(x, (W[1], W[0], W[2]), act))
+    _fails(tf.check_ffn_bruteforce)
+
+
+def test_combine_drops_last_pick(monkeypatch):
+    orig = moe.combine
+    monkeypatch.setattr(moe, "combine", lambda y, w, se: orig(y[:, :-1], w[:, :-1], se[:, :-1]))
+    _fails(tf.check_identical_experts)

@@ -1,0 +1,87 @@
+"""Pins for the host decisions: hot read (O12) and arena re-plan (O13). CPU only.
+
+Constructed cases with known answers and brute force over small tables.
+"""
+import itertools
+
+import numpy as np
+
+from oracle import plan
+
+
+def test_hot_read_planted_miss():
+    E, k = 8, 2
+    p = np.full((3, E), 0.01)
+    p[1, 5] = 0.5     # token 1 wants expert 5 (not resident) with share > 0.2
+    p[1, 0] = 0.4
+    p[0, 2] = 0.3
+    p[0, 3] = 0.3
+    p[2, 6] = 0.9
+    p[2, 7] = 0.05
+    p /= p.sum(axis=1, keepdims=True)
+    te = np.array([[2, 3], [0, 5], [6, 7]])
+    es = np.array([0, 1, 2, 3, -1, -1, 4, -1])
+    hist = np.array([5.0, 0.5, 0.5, 2.0, 0, 0, 1.0, 0])
+    r = plan.hot_read(p, te, es, hist, n_arena=5)
+    assert r is not None
+    e_star, c, new = r
+    # expert 7 is a miss too but its share (0.05/0.95) is below 0.2
+    assert e_star == 5
+    assert c == 1                      # ties at 0.5 between experts 1 and 2 -> lower id
+    assert new[5] == 1 and new[1] == -1 and (new[[0, 2, 3, 6]] == es[[0, 2, 3, 6]]).all()
+
+
+def test_hot_read_none_below_threshold():
+    p = np.array([[0.4, 0.35, 0.25]])
+    te = np.array([[0, 1]])
+    es = np.array([0, -1, 1])
+    # share of expert 1 = 0.35/0.75 = 0.467 > 0.2 -> one candidate
+    assert plan.hot_read(p, te, es, np.zeros(3), 2)[0] == 1
+    p = np.array([[0.9, 0.1, 0.0]])
+    te = np.array([[0, 1]])
+    es = np.array([0, -1, -1])
+    p2 = np.array([[0.95, 0.05, 0.0]])
+    assert plan.hot_read(p2, te, es, np.zeros(3), 1) is None      # share 0.05 < 0.2
+    assert plan.hot_read(p, te, es, np.zeros(3), 1) is None       # share exactly 0.1
+
+
+def test_hot_read_ring_slots_never_evicted():
+    p = np.array([[0.5, 0.5, 0.0, 0.0]])
+    te = np.array([[0, 1]])
+    es = np.array([-1, 2, 0, 1])         # slot 2 is a ring slot (n_arena = 2)
+    hist = np.array([0.0, 0.0, 3.0, 4.0])  # expert 1 is coldest but lives in the ring
+    e_star, c, new = plan.hot_read(p, te, es, hist, n_arena=2)
+    assert e_star == 0 and c == 2
+
+
+def brute_replan(hist, es, n, k):
+    L, E = es.shape
+    res = sorted(((hist[l, e], l, e) for l in range(L) for e in range(E) if es[l, e] >= 0))
+    out = []
+    cnt = {l: int((es[l] >= 0).sum()) for l in range(L)}
+    for h, l, e in res:
+        if len(out) < n and cnt[l] > k:
+            out.append((l, e))
+            cnt[l] -= 1
+    non = sorted(((-hist[l, e], l, e) for l in range(L) for e in range(E) if es[l, e] < 0))
+    return out, [(l, e) for _, l, e in non[:len(out)]]
+
+
+def test_replan_bruteforce_and_floor():
+    rng = np.random.default_rng(3)
+    for trial in range(40):
+        L, E, k = 3, 6, 2
+        es = np.full((L, E), -1)
+        slots = iter(range(100))
+        for l in range(L):
+            for e in rng.choice(E, size=int(rng.integers(2, 6)), replace=False):
+                es[l, e] = next(slots)
+        hist = rng.integers(0, 4, size=(L, E)).astype(float)   # many ties
+        n = int(rng.integers(1, 5))
+        ev, ld, new = plan.replan(hist, es, n, k)
+        bev, bld = brute_replan(hist, es, n, k)
+        assert ev == bev and ld == bld
+        assert ((new >= 0).sum(axis=1) >= np.minimum((es >= 0).sum(axis=1), k)).all()
+        assert sorted(new[new >= 0]) == sorted(es[es >= 0])   # slots are conserved
+        for (le, ee), (ll, el) in zip(ev, ld):
+            assert new[ll, el] == es[le, ee]
