@@ -1,0 +1,243 @@
+/*
+ * moe_arena.h -- C ABI of libmoe_arena.so: one routed-expert MoE layer running
+ * against a partially resident expert arena, on an AMD Instinct MI355X (gfx950).
+ *
+ * The method (TideLM README, "How adaptive expert loading works"):
+ *   item 1  every routed pick the router wants, resident or not, is recorded
+ *           per (layer, expert), weighted by its routing score;
+ *   item 2  the router only picks resident experts; a missing pick is replaced
+ *           by the next-best resident expert for that token;
+ *   item 3  hot reads copy a missing expert into a slot (a ring entry, or the
+ *           slot of the coldest expert) so it becomes routable.
+ * Rows are named by index rather than copied per expert, and the per-expert
+ * results of a row are added in one fixed order (colibri cluster page, wire
+ * protocol paragraphs on COLIEX01 v2 and on the fixed summation order).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory owned by the caller unless marked (host).
+ *     The library allocates nothing and never synchronises the device.
+ *   - Every call only validates its arguments and enqueues work on the given
+ *     HIP stream; results are ready when that stream reaches them.
+ *   - All validation happens before the first HIP call, so a rejected call has
+ *     no side effect.  No call aborts, prints or throws.
+ *   - Calls are reentrant; two calls that share an output or a workspace must
+ *     be ordered by the caller (same stream or events).
+ *   - Inputs must be finite (no NaN or Inf in activations or weights).
+ *   - The k picks of a token are always listed in ascending expert id; every
+ *     order-dependent sum follows that order.
+ *
+ * Formats:
+ *   bf16      : uint16_t bit pattern of a bfloat16.
+ *   MXFP4 row : K/2 bytes of E2M1 codes (element 2i in the low nibble of byte
+ *               i; code = sign<<3 | exponent<<1 | mantissa, exponent bias 1)
+ *               followed, at byte K/2, by K/32 E8M0 scale bytes (value
+ *               2^(byte-127)), one per 32 consecutive elements; a row occupies
+ *               moe_mxfp4_row_bytes(K) bytes (padded to 16).  OCP MX v1.0.
+ *               Activation rows are encoded with X = 2^(floor(log2 amax) - 2)
+ *               clamped to 2^-127..2^127, round to nearest E2M1 value with ties
+ *               to the even mantissa, saturation at +-6, sign bit copied from
+ *               the input, and scale byte 0 with all-zero codes for a block
+ *               whose amax is 0.
+ *   slot      : one SwiGLU expert, six sections, each starting on a 256-byte
+ *               boundary (offsets from moe_slot_sections):
+ *                 gate codes [I][H/2] | gate scales [I][H/32] |
+ *                 up codes   [I][H/2] | up scales   [I][H/32] |
+ *                 down codes [H][I/2] | down scales [H][I/32]
+ *               rows are contraction-contiguous (row n holds output n's weights).
+ *   arena     : S slots at arena + s*slot_stride; slot ids are global: arena
+ *               slots first, hot-ring slots after them (TideLM README, "Settings
+ *               worth knowing": the ring's slots are on top of the budget).
+ *   expert_slot[e] : slot of expert e, or -1 if e is not routable.  Values
+ *               outside [0, S) are treated as -1.  Distinct routable experts
+ *               must have distinct slots.
+ */
+#ifndef MOE_ARENA_H
+#define MOE_ARENA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MOE_OK 0
+#define MOE_EINVAL -1        /* null pointer, negative or inconsistent size, misalignment */
+#define MOE_EUNSUPPORTED -2  /* H or I not a multiple of 32, k > min(E, 32), E > 1024, S > 8192 */
+#define MOE_EWORKSPACE -3    /* ws_bytes below moe_workspace_bytes(...) */
+#define MOE_EHIP -4          /* a HIP launch or copy reported an error */
+
+/* Workspace selectors for moe_workspace_bytes. */
+#define MOE_OP_ROUTE 0
+#define MOE_OP_DEMAND 1
+#define MOE_OP_EXPERTS 2
+
+#define MOE_MAX_E 1024
+#define MOE_MAX_K 32
+#define MOE_MAX_S 8192
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* moe_status_string(int status);
+
+/* Bytes of one MXFP4 row of K elements (K % 32 == 0): K/2 + K/32 rounded up to 16. */
+size_t moe_mxfp4_row_bytes(int K);
+
+/* Byte size of one packed expert slot (the slot format above); 0 if H or I is
+ * not a positive multiple of 32. */
+size_t moe_slot_bytes(int H, int I);
+
+/* Section offsets of a slot, in the order gate codes, gate scales, up codes,
+ * up scales, down codes, down scales.  out6 (host) receives 6 values.
+ * Returns MOE_OK, MOE_EINVAL (null out6) or MOE_EUNSUPPORTED. */
+int moe_slot_sections(int H, int I, size_t* out6);
+
+/* Workspace bytes an operation needs for the given shape (0 if none; the
+ * workspace pointer may then be NULL).  op is one of MOE_OP_*.  Unused
+ * arguments are ignored.  Returns (size_t)-1 for an invalid op or shape. */
+size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
+
+/*
+ * moe_route -- router scores, demand picks, masked top-k, bucketing, and
+ * MXFP4 activations for one layer call.
+ *
+ * Steps (TideLM README, "How adaptive expert loading works", items 1-2):
+ *   z[t,e]  = sum_h x[t,h] * w_router[e,h] + bias[e], accumulated in float64:
+ *             the sum over h runs in chunks of 128 (a fused multiply-add chain
+ *             over each chunk, ascending h), the chunk sums are added in
+ *             ascending chunk order, then the bias.
+ *   p[t,:]  = softmax over all E experts of z[t,:] (float64).
+ *   topk    = the k experts with the largest z (ties to the lower id), listed in
+ *             ascending id, with score p[t,e]: the picks demand is recorded over.
+ *   sel     = the min(k, |R|) routable experts with the largest z (same order
+ *             rule), R = {e : 0 <= expert_slot[e] < S}; remaining entries are
+ *             padded with expert -1, weight 0, slot -1.  A routable pick that
+ *             was also wanted is kept; each miss is replaced by the next-best
+ *             routable expert.
+ *   sel_weight[t,j] = p[t,e_j] / sum_j' p[t,e_j'] over the present picks.
+ *   bucketing: assignment a = t*k + j goes to slot sel_slot[t,j];
+ *             slot_offsets[s] = number of assignments in slots < s (S+1 entries);
+ *             perm lists assignments by slot, ascending a within a slot;
+ *             perm[slot_offsets[S] .. T*k) = -1 (padded picks).
+ *   xq      = each token row of x encoded as an MXFP4 row (format above).
+ *
+ * Inputs : x [T][H] bf16; w_router [E][H] float; bias [E] float (nullable =
+ *          zero); expert_slot [E] int32.
+ * Outputs: topk_expert, sel_expert, sel_slot [T][k] int32; topk_score,
+ *          sel_weight [T][k] float; slot_offsets [S+1] int32; perm [T*k] int32;
+ *          xq [T][moe_mxfp4_row_bytes(H)] uint8 (16-byte aligned).
+ * Workspace: moe_workspace_bytes(MOE_OP_ROUTE, T, H, E, k, 0, S) bytes, 256-byte
+ *          aligned.  Contents on return are unspecified.
+ * T = 0 is valid (only slot_offsets is written, all zero).
+ */
+typedef struct moe_route_args {
+  int T, H, E, k, S;
+  const uint16_t* x;
+  const float* w_router;
+  const float* bias;
+  const int32_t* expert_slot;
+  int32_t* topk_expert;
+  float* topk_score;
+  int32_t* sel_expert;
+  float* sel_weight;
+  int32_t* sel_slot;
+  int32_t* slot_offsets;
+  int32_t* perm;
+  uint8_t* xq;
+  void* ws;
+  size_t ws_bytes;
+} moe_route_args;
+
+int moe_route(const moe_route_args* args, hipStream_t stream);
+
+/*
+ * moe_demand_accumulate -- record the router's demand for one layer call
+ * (TideLM README, "How adaptive expert loading works", item 1: every pick the
+ * router wants, resident or not, weighted by its routing score).
+ *
+ *   delta[e]    = sum over tokens t (ascending) of topk_score[t,j] where
+ *                 topk_expert[t,j] == e, accumulated in float64 in a fixed order;
+ *   hist_row[e] += delta[e]   (float64 running history of this layer).
+ * Independent of the resident mask.  Entries of topk_expert outside [0, E) are
+ * ignored.
+ * Inputs : topk_expert [T][k] int32, topk_score [T][k] float.
+ * In/out : hist_row [E] double (e.g. hist + layer*E).
+ * Output : delta [E] float (nullable).
+ * Workspace: moe_workspace_bytes(MOE_OP_DEMAND, T, 0, E, k, 0, 0) bytes.
+ */
+int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, int T, int k,
+                          int E, double* hist_row, float* delta, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * moe_experts_forward -- the grouped SwiGLU expert FFNs over arena slots and the
+ * weighted combine (steps after bucketing).
+ *
+ * For every slot s with assignments, rows p in [slot_offsets[s], slot_offsets[s+1])
+ * name assignment a = perm[p] of token t = a / k:
+ *   g = xq[t] . Wg^T, u = xq[t] . Wu^T   (MXFP4 x MXFP4 products, float32 sums)
+ *   h = silu(g) * u, silu(v) = v / (1 + exp(-v))
+ *   y[a] = MXFP4(h) . Wd^T               (h encoded like an activation row, along I)
+ * then out[t] = sum over j ascending (ascending expert id) of sel_weight[t,j] *
+ * y[t*k+j], skipping picks with sel_slot[t,j] < 0, rounded once to bf16.
+ * Only the slots that hold assignments are read.
+ *
+ * Inputs : xq, slot_offsets, perm, sel_slot, sel_weight as written by moe_route
+ *          for the same T, k, S; arena (256-byte aligned), slot_stride (multiple
+ *          of 256, >= moe_slot_bytes(H, I)).  Indices out of range are skipped,
+ *          never dereferenced.
+ * Output : out [T][H] bf16.
+ * Workspace: moe_workspace_bytes(MOE_OP_EXPERTS, T, H, 0, k, I, S) bytes.
+ * Any copy into a slot the call reads (arena_load_slot) must be ordered before
+ * it by the caller (hipStreamWaitEvent on the load's event).
+ */
+typedef struct moe_experts_args {
+  int T, H, I, k, S;
+  const uint8_t* xq;
+  const uint8_t* arena;
+  size_t slot_stride;
+  const int32_t* slot_offsets;
+  const int32_t* perm;
+  const int32_t* sel_slot;
+  const float* sel_weight;
+  uint16_t* out;
+  void* ws;
+  size_t ws_bytes;
+} moe_experts_args;
+
+int moe_experts_forward(const moe_experts_args* args, hipStream_t stream);
+
+/*
+ * arena_load_slot -- copy one expert, read by the host, into a slot or hot-ring
+ * entry (TideLM README, "How adaptive expert loading works", item 3).
+ *
+ * Enqueues an asynchronous host-to-device copy of `bytes` bytes from host_src
+ * (host; page-locked memory for a truly asynchronous copy) to
+ * arena + slot*slot_stride on side_stream, then records `done` (nullable) on
+ * it.  The caller makes the slot routable (expert_slot) only after `done`, so
+ * a copy in flight or a failed copy leaves the expert non-routable and its
+ * tokens are served by substitutes.  host_src must stay valid until `done`.
+ * Errors: MOE_EINVAL for a null pointer, slot outside [0, num_slots), bytes 0
+ * or above slot_stride, or slot_stride not a multiple of 256; MOE_EHIP if the
+ * copy or the event record fails.
+ */
+int arena_load_slot(uint8_t* arena, size_t slot_stride, int num_slots, int slot,
+                    const void* host_src, size_t bytes, hipStream_t side_stream, hipEvent_t done);
+
+/*
+ * moe_test_mxfp4_probe -- test-only: one wave runs one block-scaled MXFP4
+ * matrix instruction (16x16 output, contraction 128) on raw per-lane operands,
+ * so a test can check the hardware's decoding of E2M1 codes and E8M0 scales and
+ * its lane layout.  a, b: [64 lanes][16 bytes] codes; a_scale, b_scale: [64]
+ * scale bytes; d: [64 lanes][4] float results as the lanes hold them.
+ */
+int moe_test_mxfp4_probe(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+                         const uint8_t* b_scale, float* d, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ARENA_H */

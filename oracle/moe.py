@@ -242,14 +242,15 @@ def experts_forward(x_bits, sel_expert, sel_weight, sel_slot, slot_bytes_fn, H, 
     xhat = quantise_rows(bf16_to_f64(np.asarray(x_bits)[tok]), act)
     y = np.zeros((tok.size, k, H), dtype=np.float64)
     ss = np.asarray(sel_slot)[tok]
-    cache = {}
-    for s in np.unique(ss[ss >= 0]):
-        s = int(s)
+    # slots whose byte buffers are the same object are decoded once
+    slots = sorted((int(s) for s in np.unique(ss[ss >= 0])), key=lambda s: id(slot_bytes_fn(s)))
+    cached_key, cached = None, None
+    for s in slots:
         rows, cols = np.nonzero(ss == s)
-        if s not in cache:
-            cache.clear()
-            cache[s] = decode_expert(slot_bytes_fn(s), H, I)
-        y[rows, cols] = expert_ffn(xhat[rows], cache[s], act)
+        src = slot_bytes_fn(s)
+        if id(src) != cached_key:
+            cached_key, cached = id(src), decode_expert(src, H, I)
+        y[rows, cols] = expert_ffn(xhat[rows], cached, act)
     out = combine(y, np.asarray(sel_weight)[tok], np.asarray(sel_expert)[tok])
     return out, y
 

@@ -1,0 +1,195 @@
+"""ctypes binding of libmoe_arena.so -- argument marshalling only.
+
+Every function here has the name and argument order of the C entry point it
+wraps (include/moe_arena.h) and returns that entry point's status code.
+Pointer arguments accept an int address, None (NULL) or any object with a
+data_ptr() method (a torch tensor); stream arguments accept an int handle,
+None (the null stream) or an object with a cuda_stream attribute (a torch
+stream); event arguments accept an int, None or an object with cuda_event.
+No computation of the layer happens in Python.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_arena.so")
+
+MOE_OK = 0
+MOE_EINVAL = -1
+MOE_EUNSUPPORTED = -2
+MOE_EWORKSPACE = -3
+MOE_EHIP = -4
+MOE_OP_ROUTE = 0
+MOE_OP_DEMAND = 1
+MOE_OP_EXPERTS = 2
+MOE_MAX_E = 1024
+MOE_MAX_K = 32
+MOE_MAX_S = 8192
+
+EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
+           "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
+           "arena_load_slot", "moe_test_mxfp4_probe")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class RouteArgs(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("H", ctypes.c_int), ("E", ctypes.c_int),
+                ("k", ctypes.c_int), ("S", ctypes.c_int),
+                ("x", ctypes.c_void_p), ("w_router", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("expert_slot", ctypes.c_void_p), ("topk_expert", ctypes.c_void_p),
+                ("topk_score", ctypes.c_void_p), ("sel_expert", ctypes.c_void_p),
+                ("sel_weight", ctypes.c_void_p), ("sel_slot", ctypes.c_void_p),
+                ("slot_offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("xq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+class ExpertsArgs(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int),
+                ("k", ctypes.c_int), ("S", ctypes.c_int),
+                ("xq", ctypes.c_void_p), ("arena", ctypes.c_void_p),
+                ("slot_stride", ctypes.c_size_t), ("slot_offsets", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("sel_slot", ctypes.c_void_p),
+                ("sel_weight", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m resident_expert_routing_amd.build`")
+    # torch ships its own HIP runtime (libamdhip64.so, soname libamdhip64.so.7).  Loading
+    # torch first makes this library's libamdhip64.so.7 dependency resolve to that same
+    # copy, so device pointers and streams from torch are valid here; loading this
+    # library first would map a second, independent HIP runtime into the process.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.moe_status_string.argtypes = [i]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_mxfp4_row_bytes.argtypes = [i]
+    lib.moe_mxfp4_row_bytes.restype = sz
+    lib.moe_slot_bytes.argtypes = [i, i]
+    lib.moe_slot_bytes.restype = sz
+    lib.moe_slot_sections.argtypes = [i, i, ctypes.POINTER(sz)]
+    lib.moe_slot_sections.restype = i
+    lib.moe_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.moe_workspace_bytes.restype = sz
+    lib.moe_route.argtypes = [ctypes.POINTER(RouteArgs), vp]
+    lib.moe_route.restype = i
+    lib.moe_demand_accumulate.argtypes = [vp, vp, i, i, i, vp, vp, vp, sz, vp]
+    lib.moe_demand_accumulate.restype = i
+    lib.moe_experts_forward.argtypes = [ctypes.POINTER(ExpertsArgs), vp]
+    lib.moe_experts_forward.restype = i
+    lib.arena_load_slot.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
+    lib.arena_load_slot.restype = i
+    lib.moe_test_mxfp4_probe.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.moe_test_mxfp4_probe.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(p) -> int | None:
+    if p is None:
+        return None
+    if isinstance(p, int):
+        return p
+    return int(p.data_ptr())
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _event(e) -> int | None:
+    if e is None:
+        return None
+    if isinstance(e, int):
+        return e
+    return int(e.cuda_event)
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+moe_status_string = status_string
+
+
+def moe_mxfp4_row_bytes(K: int) -> int:
+    return int(load().moe_mxfp4_row_bytes(int(K)))
+
+
+def moe_slot_bytes(H: int, I: int) -> int:
+    return int(load().moe_slot_bytes(int(H), int(I)))
+
+
+def moe_slot_sections(H: int, I: int):
+    out = (ctypes.c_size_t * 6)()
+    st = load().moe_slot_sections(int(H), int(I), out)
+    if st != MOE_OK:
+        raise MoeError(st, "moe_slot_sections")
+    return [int(v) for v in out]
+
+
+def moe_workspace_bytes(op: int, T: int, H: int, E: int, k: int, I: int, S: int) -> int:
+    return int(load().moe_workspace_bytes(op, T, H, E, k, I, S))
+
+
+def moe_route(T, H, E, k, S, x, w_router, bias, expert_slot, topk_expert, topk_score,
+              sel_expert, sel_weight, sel_slot, slot_offsets, perm, xq, ws, ws_bytes,
+              stream=None) -> int:
+    a = RouteArgs(int(T), int(H), int(E), int(k), int(S), _ptr(x), _ptr(w_router), _ptr(bias),
+                  _ptr(expert_slot), _ptr(topk_expert), _ptr(topk_score), _ptr(sel_expert),
+                  _ptr(sel_weight), _ptr(sel_slot), _ptr(slot_offsets), _ptr(perm), _ptr(xq),
+                  _ptr(ws), int(ws_bytes))
+    return int(load().moe_route(ctypes.byref(a), _stream(stream)))
+
+
+def moe_demand_accumulate(topk_expert, topk_score, T, k, E, hist_row, delta, ws, ws_bytes,
+                          stream=None) -> int:
+    return int(load().moe_demand_accumulate(_ptr(topk_expert), _ptr(topk_score), int(T), int(k),
+                                            int(E), _ptr(hist_row), _ptr(delta), _ptr(ws),
+                                            int(ws_bytes), _stream(stream)))
+
+
+def moe_experts_forward(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm, sel_slot,
+                        sel_weight, out, ws, ws_bytes, stream=None) -> int:
+    a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
+                    int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
+                    _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes))
+    return int(load().moe_experts_forward(ctypes.byref(a), _stream(stream)))
+
+
+def arena_load_slot(arena, slot_stride, num_slots, slot, host_src, nbytes, side_stream=None,
+                    done=None) -> int:
+    return int(load().arena_load_slot(_ptr(arena), int(slot_stride), int(num_slots), int(slot),
+                                      _ptr(host_src), int(nbytes), _stream(side_stream),
+                                      _event(done)))
+
+
+def moe_test_mxfp4_probe(a, a_scale, b, b_scale, d, stream=None) -> int:
+    return int(load().moe_test_mxfp4_probe(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale),
+                                           _ptr(d), _stream(stream)))
+
+
+def check(status: int, what: str = "moe") -> None:
+    if status != MOE_OK:
+        raise MoeError(status, what)

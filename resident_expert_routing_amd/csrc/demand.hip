@@ -1,0 +1,86 @@
+// moe_demand_accumulate: score-weighted demand per expert over the router's
+// unrestricted picks (TideLM README, "How adaptive expert loading works",
+// item 1: every routed pick the router wants, resident or not, is recorded per
+// (layer, expert), weighted by its routing score).
+//
+// Deterministic: per chunk of 64 tokens each expert's sum runs over ascending
+// tokens; chunk sums are added in ascending chunk order, in float64.
+#include "common.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(1024) void demand_chunks(const int32_t* __restrict__ te,
+                                                      const float* __restrict__ ts, int T, int k,
+                                                      int E, double* __restrict__ part,
+                                                      double* __restrict__ hist,
+                                                      float* __restrict__ delta) {
+  __shared__ int se[kDemandChunk * MOE_MAX_K];
+  __shared__ float ss[kDemandChunk * MOE_MAX_K];
+  const int c = blockIdx.x;
+  const int t0 = c * kDemandChunk;
+  const int nt = min(kDemandChunk, T - t0);
+  const int n = nt * k;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    se[i] = te[(size_t)t0 * k + i];
+    ss[i] = ts[(size_t)t0 * k + i];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i)
+      if (se[i] == e) acc += (double)ss[i];
+    if (part) {
+      part[(size_t)c * E + e] = acc;
+    } else {
+      hist[e] += acc;
+      if (delta) delta[e] = (float)acc;
+    }
+  }
+}
+
+__global__ __launch_bounds__(1024) void demand_finalize(const double* __restrict__ part, int nchunk,
+                                                        int E, double* __restrict__ hist,
+                                                        float* __restrict__ delta) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    double acc = 0.0;
+    for (int c = 0; c < nchunk; ++c) acc += part[(size_t)c * E + e];
+    hist[e] += acc;
+    if (delta) delta[e] = (float)acc;
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+size_t moe_demand_ws_bytes_internal(int T, int E) {
+  if (T <= kDemandChunk) return 0;
+  const size_t nchunk = (size_t)(T + kDemandChunk - 1) / kDemandChunk;
+  return up_to(nchunk * E * sizeof(double), 256);
+}
+
+extern "C" MOE_EXPORT int moe_demand_accumulate(const int32_t* topk_expert,
+                                                const float* topk_score, int T, int k, int E,
+                                                double* hist_row, float* delta, void* ws,
+                                                size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || k <= 0 || E <= 0) return MOE_EINVAL;
+  if (k > MOE_MAX_K || E > MOE_MAX_E) return MOE_EUNSUPPORTED;
+  if (!hist_row) return MOE_EINVAL;
+  if (T > 0 && (!topk_expert || !topk_score)) return MOE_EINVAL;
+  if (!aligned(hist_row, 8)) return MOE_EINVAL;
+  const size_t need = moe_demand_ws_bytes_internal(T, E);
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (need > 0 && (!ws || !aligned(ws, 256))) return MOE_EINVAL;
+  const int threads = E <= 256 ? 256 : 1024;
+  if (T <= kDemandChunk) {
+    demand_chunks<<<1, threads, 0, stream>>>(topk_expert, topk_score, T, k, E, nullptr, hist_row,
+                                             delta);
+    return hip_status();
+  }
+  const int nchunk = (T + kDemandChunk - 1) / kDemandChunk;
+  double* part = static_cast<double*>(ws);
+  demand_chunks<<<nchunk, threads, 0, stream>>>(topk_expert, topk_score, T, k, E, part, hist_row,
+                                                delta);
+  demand_finalize<<<1, threads, 0, stream>>>(part, nchunk, E, hist_row, delta);
+  return hip_status();
+}

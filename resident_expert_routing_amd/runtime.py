@@ -1,0 +1,109 @@
+"""torch plumbing around the C ABI: device buffers, arena upload, one layer step.
+
+torch supplies device memory and streams only; every step of the layer runs in
+libmoe_arena's HIP kernels through the functions of binding.py.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+def _ws(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    # torch allocations are 256-byte aligned (caching allocator blocks are 512-aligned)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class LayerBuffers:
+    """Outputs and workspaces of one layer call of shape (T, H, E, k, I, S)."""
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    S: int
+    device: torch.device
+
+    def __post_init__(self):
+        T, H, E, k, I, S, dev = self.T, self.H, self.E, self.k, self.I, self.S, self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.topk_expert = torch.empty((T, k), **i32)
+        self.topk_score = torch.empty((T, k), **f32)
+        self.sel_expert = torch.empty((T, k), **i32)
+        self.sel_weight = torch.empty((T, k), **f32)
+        self.sel_slot = torch.empty((T, k), **i32)
+        self.slot_offsets = torch.empty(S + 1, **i32)
+        self.perm = torch.empty(T * k, **i32)
+        self.xq_row = B.moe_mxfp4_row_bytes(H)
+        self.xq = torch.empty((T, self.xq_row), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.int16, device=dev)  # bf16 bits
+        self.delta = torch.empty(E, **f32)
+        self.ws_route_bytes = B.moe_workspace_bytes(B.MOE_OP_ROUTE, T, H, E, k, I, S)
+        self.ws_demand_bytes = B.moe_workspace_bytes(B.MOE_OP_DEMAND, T, H, E, k, I, S)
+        self.ws_experts_bytes = B.moe_workspace_bytes(B.MOE_OP_EXPERTS, T, H, E, k, I, S)
+        self.ws_route = _ws(self.ws_route_bytes, dev)
+        self.ws_demand = _ws(self.ws_demand_bytes, dev)
+        self.ws_experts = _ws(self.ws_experts_bytes, dev)
+
+
+class Arena:
+    """S expert slots of slot_stride bytes in one device allocation."""
+
+    def __init__(self, S: int, H: int, I: int, device, stride: int | None = None):
+        self.H, self.I, self.S = H, I, S
+        self.slot_bytes = B.moe_slot_bytes(H, I)
+        self.stride = stride or self.slot_bytes
+        assert self.stride % 256 == 0 and self.stride >= self.slot_bytes
+        self.mem = torch.empty(S * self.stride, dtype=torch.uint8, device=device)
+
+    def upload(self, slot_bytes_fn, slots=None, stream=None):
+        """Copy packed host bytes into slots (plain torch copies, setup only)."""
+        slots = range(self.S) if slots is None else slots
+        cache = {}
+        for s in slots:
+            host = slot_bytes_fn(s)
+            key = id(host)
+            if key not in cache:
+                cache[key] = torch.from_numpy(np.ascontiguousarray(host)).pin_memory()
+            self.mem[s * self.stride: s * self.stride + self.slot_bytes].copy_(cache[key],
+                                                                            non_blocking=True)
+        torch.cuda.current_stream(self.mem.device).synchronize()
+
+    def ptr(self) -> int:
+        return self.mem.data_ptr()
+
+
+def route(buf: LayerBuffers, x, w_router, bias, expert_slot, stream=None) -> None:
+    B.check(B.moe_route(buf.T, buf.H, buf.E, buf.k, buf.S, x, w_router, bias, expert_slot,
+                        buf.topk_expert, buf.topk_score, buf.sel_expert, buf.sel_weight,
+                        buf.sel_slot, buf.slot_offsets, buf.perm, buf.xq, buf.ws_route,
+                        buf.ws_route_bytes, stream), "moe_route")
+
+
+def demand(buf: LayerBuffers, hist_row, stream=None, delta=True) -> None:
+    B.check(B.moe_demand_accumulate(buf.topk_expert, buf.topk_score, buf.T, buf.k, buf.E,
+                                    hist_row, buf.delta if delta else None, buf.ws_demand,
+                                    buf.ws_demand_bytes, stream), "moe_demand_accumulate")
+
+
+def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None) -> None:
+    B.check(B.moe_experts_forward(buf.T, buf.H, buf.I, buf.k, buf.S, buf.xq, arena_ptr,
+                                  slot_stride, buf.slot_offsets, buf.perm, buf.sel_slot,
+                                  buf.sel_weight, buf.out, buf.ws_experts, buf.ws_experts_bytes,
+                                  stream), "moe_experts_forward")
+
+
+def layer_step(buf: LayerBuffers, x, w_router, bias, expert_slot, hist_row, arena_ptr,
+               slot_stride, stream=None) -> None:
+    """One pass of the whole layer: route, demand, experts and combine."""
+    route(buf, x, w_router, bias, expert_slot, stream)
+    demand(buf, hist_row, stream)
+    experts(buf, arena_ptr, slot_stride, stream)

@@ -1,0 +1,195 @@
+"""C-ABI contract on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented codes before touching HIP."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_arena.h")
+
+import resident_expert_routing_amd as m  # noqa: E402
+from resident_expert_routing_amd import binding as B  # noqa: E402
+import fixtures  # noqa: E402
+from oracle import moe as omoe  # noqa: E402
+
+FAKE = 1 << 20  # a non-null, 256-aligned address that is never dereferenced on reject paths
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = B.load()
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_no_unexpected_exports():
+    out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    ours = {s for s in syms if s.startswith(("moe_", "arena_"))}
+    assert ours == set(B.EXPORTS)
+
+
+def test_status_strings():
+    for code in (B.MOE_OK, B.MOE_EINVAL, B.MOE_EUNSUPPORTED, B.MOE_EWORKSPACE, B.MOE_EHIP):
+        s = B.status_string(code)
+        assert s.startswith("MOE_")
+    assert B.status_string(12345) == "unknown moe status"
+
+
+def test_layout_helpers_match_documented_format():
+    assert B.moe_mxfp4_row_bytes(4096) == 2176
+    assert B.moe_mxfp4_row_bytes(256) == 144
+    assert B.moe_mxfp4_row_bytes(100) == 0
+    for H, I in ((256, 128), (4096, 2048), (6144, 2048), (96, 64)):
+        lay = fixtures.SlotLayout(H, I)
+        assert B.moe_slot_bytes(H, I) == lay.nbytes
+        assert B.moe_slot_sections(H, I) == [lay.sections[n][0] for n in (
+            "gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")]
+        sec = omoe.slot_sections(H, I)
+        assert sec["total"] == lay.nbytes
+    assert B.moe_slot_bytes(100, 64) == 0
+    with pytest.raises(B.MoeError):
+        B.moe_slot_sections(64, 48)
+
+
+def test_workspace_sizes():
+    ws = B.moe_workspace_bytes
+    assert ws(B.MOE_OP_ROUTE, 0, 4096, 256, 8, 0, 230) == 0
+    assert ws(B.MOE_OP_ROUTE, 8, 4096, 256, 8, 0, 230) == 32 * 8 * 256 * 8
+    assert ws(B.MOE_OP_ROUTE, 2048, 4096, 256, 8, 0, 166) == 2048 * 256 * 8
+    assert ws(B.MOE_OP_DEMAND, 64, 0, 256, 8, 0, 0) == 0
+    assert ws(B.MOE_OP_DEMAND, 65, 0, 256, 8, 0, 0) == 2 * 256 * 8
+    e = ws(B.MOE_OP_EXPERTS, 8, 4096, 0, 8, 2048, 230)
+    assert e >= 64 * (1088 + 4096 * 4) and e % 256 == 0
+    assert ws(7, 8, 4096, 256, 8, 2048, 230) == (1 << 64) - 1
+    assert ws(B.MOE_OP_ROUTE, 8, 100, 256, 8, 0, 230) == (1 << 64) - 1
+
+
+def _route(**kw):
+    a = dict(T=8, H=256, E=16, k=4, S=10, x=FAKE, w_router=FAKE, bias=None, expert_slot=FAKE,
+             topk_expert=FAKE, topk_score=FAKE, sel_expert=FAKE, sel_weight=FAKE, sel_slot=FAKE,
+             slot_offsets=FAKE, perm=FAKE, xq=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return B.moe_route(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), B.MOE_EINVAL),
+    (dict(w_router=None), B.MOE_EINVAL),
+    (dict(slot_offsets=None), B.MOE_EINVAL),
+    (dict(perm=None), B.MOE_EINVAL),
+    (dict(xq=None), B.MOE_EINVAL),
+    (dict(T=-1), B.MOE_EINVAL),
+    (dict(H=0), B.MOE_EINVAL),
+    (dict(H=100), B.MOE_EUNSUPPORTED),
+    (dict(k=17), B.MOE_EUNSUPPORTED),
+    (dict(k=33, E=64), B.MOE_EUNSUPPORTED),
+    (dict(E=2048), B.MOE_EUNSUPPORTED),
+    (dict(S=9000), B.MOE_EUNSUPPORTED),
+    (dict(ws_bytes=16), B.MOE_EWORKSPACE),
+    (dict(ws=None), B.MOE_EINVAL),
+    (dict(x=FAKE + 2), B.MOE_EINVAL),
+    (dict(xq=FAKE + 8), B.MOE_EINVAL),
+])
+def test_route_rejects(kw, code):
+    assert _route(**kw) == code
+
+
+def test_route_null_args_struct():
+    assert B.load().moe_route(None, None) == B.MOE_EINVAL
+
+
+def test_demand_rejects():
+    d = B.moe_demand_accumulate
+    assert d(FAKE, FAKE, 8, 4, 16, None, None, None, 0) == B.MOE_EINVAL
+    assert d(None, FAKE, 8, 4, 16, FAKE, None, None, 0) == B.MOE_EINVAL
+    assert d(FAKE, FAKE, 8, 40, 16, FAKE, None, None, 0) == B.MOE_EUNSUPPORTED
+    assert d(FAKE, FAKE, 8, 4, 2000, FAKE, None, None, 0) == B.MOE_EUNSUPPORTED
+    assert d(FAKE, FAKE, 100, 4, 16, FAKE, None, None, 0) == B.MOE_EWORKSPACE
+    assert d(FAKE, FAKE, 100, 4, 16, FAKE, None, None, 1 << 20) == B.MOE_EINVAL
+    assert d(FAKE, FAKE, -1, 4, 16, FAKE, None, None, 0) == B.MOE_EINVAL
+
+
+def _experts(**kw):
+    a = dict(T=8, H=256, I=128, k=4, S=10, xq=FAKE, arena=FAKE, slot_stride=52224,
+             slot_offsets=FAKE, perm=FAKE, sel_slot=FAKE, sel_weight=FAKE, out=FAKE, ws=FAKE,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return B.moe_experts_forward(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(xq=None), B.MOE_EINVAL),
+    (dict(arena=None), B.MOE_EINVAL),
+    (dict(out=None), B.MOE_EINVAL),
+    (dict(perm=None), B.MOE_EINVAL),
+    (dict(I=100), B.MOE_EUNSUPPORTED),
+    (dict(H=96 + 8), B.MOE_EUNSUPPORTED),
+    (dict(slot_stride=52224 - 256), B.MOE_EINVAL),
+    (dict(slot_stride=52224 + 16), B.MOE_EINVAL),
+    (dict(arena=FAKE + 16), B.MOE_EINVAL),
+    (dict(ws_bytes=100), B.MOE_EWORKSPACE),
+    (dict(ws=None), B.MOE_EINVAL),
+    (dict(S=9000), B.MOE_EUNSUPPORTED),
+    (dict(k=0), B.MOE_EINVAL),
+])
+def test_experts_rejects(kw, code):
+    assert _experts(**kw) == code
+
+
+def test_experts_empty_batch_is_ok_without_hip():
+    assert _experts(T=0, xq=None, arena=None, out=None, ws=None, ws_bytes=0) == B.MOE_OK
+
+
+def test_arena_load_rejects():
+    buf = np.zeros(512, dtype=np.uint8)
+    host = buf.ctypes.data
+    L = B.arena_load_slot
+    assert L(None, 256, 4, 0, host, 256) == B.MOE_EINVAL
+    assert L(FAKE, 256, 4, 0, None, 256) == B.MOE_EINVAL
+    assert L(FAKE, 256, 4, 4, host, 256) == B.MOE_EINVAL
+    assert L(FAKE, 256, 4, -1, host, 256) == B.MOE_EINVAL
+    assert L(FAKE, 256, 4, 0, host, 257) == B.MOE_EINVAL
+    assert L(FAKE, 256, 4, 0, host, 0) == B.MOE_EINVAL
+    assert L(FAKE, 300, 4, 0, host, 200) == B.MOE_EINVAL
+    assert L(FAKE, 256, 0, 0, host, 200) == B.MOE_EINVAL
+
+
+def test_probe_rejects():
+    assert B.moe_test_mxfp4_probe(None, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+    assert B.moe_test_mxfp4_probe(FAKE + 4, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        B.load()
+
+
+def hip_runtimes_mapped():
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            p = line.split()[-1]
+            if "libamdhip64" in p:
+                paths.add(os.path.realpath(p))
+    return paths
+
+
+def test_single_hip_runtime_in_process():
+    """The library must share torch's HIP runtime, never map a second one."""
+    B.load()
+    import torch  # noqa: F401
+    assert len(hip_runtimes_mapped()) == 1, hip_runtimes_mapped()

@@ -1,0 +1,359 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: routing picks, slots, offsets, permutation and MXFP4 activation bytes
+bit-exact; scores and renormalised weights within 1e-6; demand within 1e-5
+relative per bin (exact zeros where nothing was picked); layer output within
+relative L2 error 5e-3 of the float64 oracle.
+"""
+import numpy as np
+import pytest
+
+import fixtures
+from oracle import moe, mxfp4
+from gpu_helpers import GpuLayer, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+OUT_REL_L2 = 5e-3
+DEMAND_REL = 1e-5
+WEIGHT_ABS = 1e-6
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import resident_expert_routing_amd  # noqa: F401  (loads libmoe_arena.so)
+    from test_abi import hip_runtimes_mapped
+    assert len(hip_runtimes_mapped()) == 1, hip_runtimes_mapped()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+_LAYERS = {}
+
+
+def gpu_layer(name, T=None):
+    key = (name, T)
+    if key not in _LAYERS:
+        say(f"workload {name} T={T}: generating inputs and uploading the arena")
+        lay = fixtures.make_layer(name, T=T)
+        _LAYERS[key] = GpuLayer(lay)
+    return _LAYERS[key]
+
+
+def oracle_route(g):
+    r = moe.route(g.x_bits, g.lay.w_router, g.lay.bias, g.expert_slot_np, g.k)
+    _, offsets, perm = moe.bucket(r["sel_slot"], g.S)
+    r["slot_offsets"], r["perm"] = offsets, perm
+    return r
+
+
+def check_route(g, r):
+    got = g.routing()
+    for key in ("topk_expert", "sel_expert", "sel_slot", "slot_offsets", "perm"):
+        assert np.array_equal(got[key], r[key]), key
+    np.testing.assert_allclose(got["topk_score"], r["topk_score"], rtol=1e-6, atol=1e-9)
+    np.testing.assert_allclose(got["sel_weight"], r["sel_weight"], rtol=0, atol=WEIGHT_ABS)
+    H = g.H
+    if g.T:
+        codes, scales = mxfp4.encode(moe.bf16_to_f64(g.x_bits))
+        assert np.array_equal(got["xq"][:, :H // 2], codes), "xq codes"
+        assert np.array_equal(got["xq"][:, H // 2:H // 2 + H // 32], scales), "xq scales"
+    return got
+
+
+# --------------------------------------------------------------------------
+# hardware probe: every E2M1 code at every scale whose result is a normal fp32
+# --------------------------------------------------------------------------
+def _probe(a_codes, a_scale, b_codes, b_scale):
+    """Codes [64 lanes][32] (values 0..15), scales [64] -> lane outputs [64][4]."""
+    import torch
+    import resident_expert_routing_amd as m
+    pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    A = to_dev(pack(a_codes))
+    Bq = to_dev(pack(b_codes))
+    sa = to_dev(np.asarray(a_scale, dtype=np.uint8))
+    sb = to_dev(np.asarray(b_scale, dtype=np.uint8))
+    d = torch.zeros((64, 4), dtype=torch.float32, device=A.device)
+    m.check(m.moe_test_mxfp4_probe(A, sa, Bq, sb, d))
+    torch.cuda.synchronize()
+    return d.cpu().numpy()
+
+
+def lane_matrix(d):
+    """Lane outputs -> D[16][16] under the layout lane l, reg v = D[4*(l//16)+v][l%16]."""
+    D = np.zeros((16, 16), dtype=np.float32)
+    for l in range(64):
+        for v in range(4):
+            D[4 * (l // 16) + v, l % 16] = d[l, v]
+    return D
+
+
+def test_probe_every_code_and_scale():
+    say("probe: one-hot A against B codes (j+k)%16, B scales 2..250")
+    # A row i holds 1.0 (code 2) at K position k_i = 32*(i%4) + 5*(i//4) + 1
+    kpos = [32 * (i % 4) + 5 * (i // 4) + 1 for i in range(16)]
+    a_codes = np.zeros((64, 32), dtype=np.uint8)
+    for i, kk in enumerate(kpos):
+        a_codes[16 * (kk // 32) + i, kk % 32] = 2
+    b_codes = np.zeros((64, 32), dtype=np.uint8)
+    for l in range(64):
+        j, g = l % 16, l // 16
+        for m_ in range(32):
+            b_codes[l, m_] = (j + 32 * g + m_) % 16
+    for s in range(2, 251):
+        d = _probe(a_codes, [127] * 64, b_codes, [s] * 64)
+        D = lane_matrix(d)
+        for i, kk in enumerate(kpos):
+            for j in range(16):
+                want = mxfp4.VALUE[(j + kk) % 16] * 2.0 ** (s - 127)
+                assert D[i, j] == np.float32(want), (s, i, j, D[i, j], want)
+    say("probe: A-side decode (B one-hot)")
+    for s in (2, 60, 127, 200, 250):
+        d = _probe(b_codes, [s] * 64, a_codes, [127] * 64)
+        D = lane_matrix(d)
+        for j, kk in enumerate(kpos):
+            for i in range(16):
+                want = mxfp4.VALUE[(i + kk) % 16] * 2.0 ** (s - 127)
+                assert D[i, j] == np.float32(want)
+
+
+def test_probe_full_contraction():
+    say("probe: random 16x16x128 contraction")
+    rng = np.random.default_rng(0)
+    a = rng.integers(0, 16, size=(64, 32)).astype(np.uint8)
+    b = rng.integers(0, 16, size=(64, 32)).astype(np.uint8)
+    sa = rng.integers(120, 134, size=64)
+    sb = rng.integers(120, 134, size=64)
+    D = lane_matrix(_probe(a, sa, b, sb))
+    # A[i][k], k = 32*g + m held by lane 16g+i; B[k][j] by lane 16g+j
+    Am = np.zeros((16, 128))
+    Bm = np.zeros((128, 16))
+    for l in range(64):
+        i, g = l % 16, l // 16
+        Am[i, 32 * g:32 * g + 32] = mxfp4.VALUE[a[l]] * 2.0 ** (sa[l] - 127)
+        Bm[32 * g:32 * g + 32, i] = mxfp4.VALUE[b[l]] * 2.0 ** (sb[l] - 127)
+    want = Am @ Bm   # exact in float64 for these ranges
+    bound = 8 * 2.0 ** -24 * (np.abs(Am) @ np.abs(Bm))   # a few fp32 roundings inside
+    assert np.all(np.abs(D - want) <= bound)
+
+
+# --------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill", "long"])
+def test_route_parity(name):
+    g = gpu_layer(name)
+    say(f"moe_route parity on {name}: T={g.T} H={g.H} E={g.E} k={g.k} S={g.S}")
+    g.route()
+    check_route(g, oracle_route(g))
+
+
+def test_route_worked_example_ties():
+    """Exact ties (one-hot tokens) resolve to the lower expert id, on the GPU."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    say("moe_route on the hand-worked tie example")
+    E, H, k = 6, 32, 3
+    w = np.zeros((E, H), dtype=np.float32)
+    w[:, 0] = [0.5, 2.0, 1.0, 2.0, -1.0, 1.5]
+    w[:, 1] = [3.0, 0.0, 0.0, 1.0, 2.5, -2.0]
+    x = np.zeros((2, H), dtype=np.float32)
+    x[0, 0] = x[1, 1] = 1.0
+    es = np.array([0, -1, 1, 2, -1, 3], dtype=np.int32)
+    buf = R.LayerBuffers(2, H, E, k, 32, 4, torch.device("cuda", 0))
+    R.route(buf, to_dev(fixtures.f32_to_bf16_bits(x).view(np.int16)), to_dev(w), None, to_dev(es))
+    torch.cuda.synchronize()
+    assert buf.topk_expert.cpu().numpy().tolist() == [[1, 3, 5], [0, 3, 4]]
+    assert buf.sel_expert.cpu().numpy().tolist() == [[2, 3, 5], [0, 2, 3]]
+    assert buf.sel_slot.cpu().numpy().tolist() == [[1, 2, 3], [0, 1, 2]]
+    assert buf.slot_offsets.cpu().numpy().tolist() == [0, 1, 3, 5, 6]
+    assert buf.perm.cpu().numpy().tolist() == [3, 0, 4, 1, 5, 2]
+
+
+@pytest.mark.parametrize("T,E,k,nr,S,H", [
+    (1, 16, 4, 10, 10, 256),     # single token
+    (13, 16, 4, 10, 10, 256),    # ragged token count
+    (70, 40, 6, 3, 3, 96),       # fewer routable than k: padding; H not a multiple of 128
+    (65, 16, 4, 16, 16, 256),    # all resident, T just above the split-router limit
+    (5, 1024, 32, 700, 8192, 64),  # maximum E, k and S
+])
+def test_route_edge_shapes(T, E, k, nr, S, H):
+    say(f"moe_route edge T={T} E={E} k={k} routable={nr} S={S} H={H}")
+    lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=32, n_routable=nr, seed=T * 7 + E,
+                              bias_scale=0.5)
+    es = lay.expert_slot.copy()
+    if S > nr:   # spread the routable experts over a sparse slot range
+        rng = np.random.default_rng(1)
+        slots = rng.choice(S, size=nr, replace=False)
+        es[es >= 0] = slots[es[es >= 0]]
+    g = GpuLayer.__new__(GpuLayer)
+    _init_route_only(g, lay, es, S)
+    g.route()
+    check_route(g, oracle_route(g))
+
+
+def _init_route_only(g, lay, es, S):
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    g.lay, g.x_bits, g.T = lay, lay.x_bits, lay.x_bits.shape[0]
+    g.H, g.E, g.k, g.I, g.S = lay.cfg.H, lay.cfg.E, lay.cfg.k, lay.cfg.I, S
+    g.expert_slot_np = es
+    g.x = to_dev(lay.x_bits.view(np.int16))
+    g.w_router, g.bias = to_dev(lay.w_router), to_dev(lay.bias)
+    g.expert_slot = to_dev(es.astype(np.int32))
+    g.buf = R.LayerBuffers(g.T, g.H, g.E, g.k, g.I, S, torch.device("cuda", 0))
+    g.hist = torch.zeros(g.E, dtype=torch.float64, device=torch.device("cuda", 0))
+
+
+def test_route_empty_batch():
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    say("moe_route with T=0")
+    buf = R.LayerBuffers(0, 256, 16, 4, 128, 10, torch.device("cuda", 0))
+    buf.slot_offsets.fill_(77)
+    x = torch.empty((0, 256), dtype=torch.int16, device="cuda")
+    R.route(buf, x, torch.zeros((16, 256), device="cuda"), None,
+            torch.zeros(16, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert (buf.slot_offsets.cpu().numpy() == 0).all()
+
+
+# --------------------------------------------------------------------------
+# demand
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_demand_parity(name):
+    import torch
+    g = gpu_layer(name)
+    say(f"moe_demand_accumulate parity on {name}")
+    g.route()
+    g.hist.zero_()
+    g.demand()
+    g.demand()   # accumulates: hist = 2 * delta
+    torch.cuda.synchronize()
+    r = oracle_route(g)
+    want = moe.demand(r["topk_expert"], r["topk_score"], g.E)
+    delta = g.buf.delta.cpu().numpy().astype(np.float64)
+    hist = g.hist.cpu().numpy()
+    nz = want > 0
+    assert (delta[~nz] == 0).all() and (hist[~nz] == 0).all()
+    assert np.all(np.abs(delta[nz] - want[nz]) <= DEMAND_REL * want[nz])
+    assert np.all(np.abs(hist[nz] - 2 * want[nz]) <= DEMAND_REL * 2 * want[nz])
+    # demand totals equal the sum of the recorded (float32) scores, up to float64
+    # summation order; and the oracle's float64 scores up to float32 rounding (2^-24 each)
+    rec = g.buf.topk_score.cpu().numpy().astype(np.float64).sum()
+    assert abs(hist.sum() - 2 * rec) <= 1e-12 * hist.sum()
+    assert abs(hist.sum() - 2 * r["topk_score"].sum()) <= 2.0 ** -23 * hist.sum()
+
+
+# --------------------------------------------------------------------------
+# whole layer
+# --------------------------------------------------------------------------
+def _layer_parity(g, tokens=None):
+    g.route()
+    g.experts()
+    out = g.out_f64()
+    r = oracle_route(g)
+    check_route(g, r)
+    o, _ = moe.experts_forward(g.x_bits, r["sel_expert"], r["sel_weight"], r["sel_slot"],
+                               g.slot_bytes_fn(), g.H, g.I, tokens=tokens)
+    got = out if tokens is None else out[tokens]
+    err = moe.rel_l2(got, o)
+    say(f"  rel-L2 {err:.3e} over {got.shape[0]} tokens")
+    assert err <= OUT_REL_L2, err
+    return err
+
+
+def test_layer_parity_tiny():
+    say("layer parity tiny (all 64 tokens)")
+    _layer_parity(gpu_layer("tiny"))
+
+
+def test_layer_parity_decode():
+    say("layer parity decode (all 8 tokens, ring slots routable)")
+    _layer_parity(gpu_layer("decode"))
+
+
+def test_layer_parity_prefill_sampled():
+    g = gpu_layer("prefill")
+    rng = np.random.default_rng(5)
+    tok = np.unique(np.concatenate([[0, g.T - 1], rng.choice(g.T, 30, replace=False)]))
+    say(f"layer parity prefill, {tok.size} sampled tokens")
+    _layer_parity(g, tok)
+
+
+def test_layer_parity_long_sampled():
+    g = gpu_layer("long")
+    rng = np.random.default_rng(6)
+    tok = np.unique(np.concatenate([[0, g.T - 1], rng.choice(g.T, 20, replace=False)]))
+    say(f"layer parity long, {tok.size} sampled tokens")
+    _layer_parity(g, tok)
+
+
+@pytest.mark.parametrize("T,E,k,nr,H,I", [
+    (1, 16, 4, 10, 256, 128),
+    (13, 16, 4, 10, 256, 128),
+    (70, 12, 6, 3, 96, 64),      # padding picks; partial 512-wide super-chunks
+    (40, 8, 2, 8, 544, 160),     # H, I not multiples of 128
+])
+def test_layer_edge_shapes(T, E, k, nr, H, I):
+    say(f"layer edge T={T} E={E} k={k} routable={nr} H={H} I={I}")
+    lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=I, n_routable=nr, seed=T + 3 * E,
+                              bias_scale=0.5)
+    _layer_parity(GpuLayer(lay))
+
+
+def test_layer_nothing_routable():
+    import torch
+    say("layer with no routable expert (S=0): output is zero")
+    lay = fixtures.tiny_layer(T=5, H=256, E=16, k=4, I=128, n_routable=0, seed=9)
+    g = GpuLayer(lay)
+    g.route()
+    g.experts()
+    assert (g.out_f64() == 0).all()
+    got = g.routing()
+    assert (got["sel_expert"] == -1).all() and (got["slot_offsets"] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# metamorphic properties (no oracle needed)
+# --------------------------------------------------------------------------
+def test_determinism_and_batch_invariance():
+    import torch
+    g = gpu_layer("decode")
+    say("determinism: decode layer twice")
+    g.route()
+    g.experts()
+    a = g.out_f64().copy()
+    g.route()
+    g.experts()
+    assert np.array_equal(a, g.out_f64())
+    say("batch invariance: each decode token alone")
+    for t in (0, 3, 7):
+        one = GpuLayer(g.lay, x_bits=g.x_bits[t:t + 1], arena=g.arena)
+        one.route()
+        one.experts()
+        assert np.array_equal(one.out_f64()[0], a[t]), t
+
+
+def test_scale_bump_doubles_expert():
+    """Adding 1 to every E8M0 scale byte of an expert's down matrix doubles that
+    expert's y exactly; with identical experts everywhere the output doubles."""
+    import torch
+    say("metamorphic: down-scale bump doubles the output (identical experts)")
+    lay = fixtures.tiny_layer(T=16, H=256, E=8, k=2, I=128, n_routable=8, seed=21, n_contents=1)
+    g = GpuLayer(lay)
+    g.route()
+    g.experts()
+    base = g.out_f64().copy()
+    sec = fixtures.SlotLayout(256, 128).sections
+    so, ss = sec["down_scales"]
+    mem = g.arena.mem.view(g.S, -1)
+    mem[:, so:so + ss] += 1
+    g.experts()
+    bumped = g.out_f64()
+    # out is bf16(sum w*y); doubling every y doubles the fp32 sum exactly
+    assert np.array_equal(bumped, 2 * base)
