@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Routed tokens/s of one masked-top-k MXFP4 MoE layer on one MI355X.
+
+A step is one pass of the whole layer over one batch of tokens already
+resident in HBM: moe_route (router, demand picks, masked top-k, renormalise,
+bucket, MXFP4 activations) -> moe_demand_accumulate -> moe_experts_forward
+(grouped SwiGLU experts on MXFP4 arena slots + fixed-order combine).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+Prints one JSON line.  Inputs are seeded synthetic workloads (fixtures/): the
+default is the decode batch (8 tokens, hidden 4096, 256 experts, top-8,
+SwiGLU intermediate 2048, 166 resident + 64 hot-ring slots, Zipf-skewed
+router).  Steps rotate over 4 token batches and 4 copies of the arena so the
+256 MB Infinity Cache cannot serve expert bytes reused from a previous step.
+
+The roofline object reports the dominant kernel (the grouped gate/up GEMM,
+2/3 of the expert bytes): achieved = algorithmic bytes per launch (distinct
+slots used x gate+up bytes per slot, plus the activation rows it reads and
+the MXFP4 h rows it writes) / its mean launch time from HIP events recorded on
+the launch stream inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4, vendor figure
+METRIC = "routed tokens/s per MoE layer; % peak HBM GB/s (decode), % MXFP4 MFMA (prefill)"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "resident_expert_routing_amd", "csrc", "experts.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "long", "tiny"])
+    ap.add_argument("--rotate", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (to scale HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+
+
+def gateup_bytes_per_slot(H: int, I: int) -> int:
+    return 2 * I * (H // 2 + H // 32)
+
+
+def expert_bytes(H: int, I: int) -> int:
+    return 3 * H * I // 2 + 3 * H * I // 32
+
+
+def traffic_from_profile(workload: str, algo_bytes: float):
+    """HBM bytes per gate/up launch from the committed rocprofv3 PMC summary.
+
+    Returns None if there is no summary or the kernel source changed since."""
+    path = os.path.join(PROFILE_DIR, f"gateup_kernel_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        p = json.load(f)
+    if p.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return p.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(lay, k: int):
+    """The oracle (numpy float64) on one decode step, timed on the host cores."""
+    import numpy as np
+    from oracle import moe
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    cfg = lay.cfg
+    sc = lay.slot_content()
+    t0 = time.perf_counter()
+    r = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k,
+                  lambda s: lay.content_bytes(sc[s]), cfg.H, cfg.I)
+    dt = time.perf_counter() - t0
+    T = lay.x_bits.shape[0]
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
+            "sample": f"one full {cfg.name} layer call ({T} tokens: float64 router, softmax, "
+                      f"top-k, masked top-k, demand, MXFP4 decode of every used expert, SwiGLU, "
+                      f"combine) in {dt:.2f} s; numpy elementwise on 1 thread, BLAS on {blas}",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this layer build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+    import fixtures
+    import resident_expert_routing_amd  # noqa: F401  (loads libmoe_arena.so; fails loudly)
+    from resident_expert_routing_amd import runtime as R
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    name = args.workload
+    base = fixtures.make_layer(name)
+    cfg = base.cfg
+    T, H, E, k, I, S = base.x_bits.shape[0], cfg.H, cfg.E, cfg.k, cfg.I, base.S
+    nrot = max(1, args.rotate)
+
+    # ---- inputs resident in HBM ----
+    log(f"workload {name}: T={T} H={H} E={E} k={k} I={I} S={S}; packing expert contents")
+    base.prepack()
+    layers = [base] + [fixtures.make_layer(name, x_stream=i) for i in range(1, nrot)]
+    xs = [torch.from_numpy(l.x_bits.view(np.int16)).to(dev) for l in layers]
+    w_router = torch.from_numpy(base.w_router).to(dev)
+    bias = torch.from_numpy(base.bias).to(dev)
+    expert_slot = torch.from_numpy(base.expert_slot.astype(np.int32)).to(dev)
+    sc = base.slot_content()
+    arenas = []
+    for i in range(nrot):
+        a = R.Arena(S, H, I, dev)
+        a.upload(lambda s: base.content_bytes(sc[s]))
+        arenas.append(a)
+    log(f"{nrot} arena copies of {S} slots uploaded")
+    buf = R.LayerBuffers(T, H, E, k, I, S, dev)
+    hist = torch.zeros(E, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev_r=None, ev_e=None):
+        j = i % nrot
+        R.route(buf, xs[j], w_router, bias, expert_slot, stream, ev_r)
+        R.demand(buf, hist, stream)
+        R.experts(buf, arenas[j].ptr(), arenas[j].stride, stream, ev_e)
+
+    # distinct slots used by each rotation's routing (deterministic)
+    U = []
+    for j in range(nrot):
+        step(j)
+        torch.cuda.synchronize()
+        off = buf.slot_offsets.cpu().numpy()
+        U.append(int(np.count_nonzero(np.diff(off))))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev_r = [[mk() for _ in range(5)] for _ in range(K)]
+    ev_e = [[mk() for _ in range(5)] for _ in range(K)]
+    start, end = mk(), mk()
+    for e in [e for row in ev_r + ev_e for e in row]:
+        e.record(stream)   # torch creates the HIP event on first record
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        step(i, ev_r[i], ev_e[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+
+    # per-stage times (ms, mean over the timed steps)
+    def stage(evs, a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
+    stages = {
+        "router_logits": stage(ev_r, 0, 1), "select": stage(ev_r, 1, 2),
+        "bucket_count": stage(ev_r, 2, 3), "bucket_scatter": stage(ev_r, 3, 4),
+        "worklist": stage(ev_e, 0, 1), "gateup": stage(ev_e, 1, 2), "down": stage(ev_e, 2, 3),
+        "combine": stage(ev_e, 3, 4),
+    }
+    A = T * k
+    u_steps = [U[i % nrot] for i in range(K)]
+    gu_bytes = float(np.mean([u * gateup_bytes_per_slot(H, I) for u in u_steps])) \
+        + T * (H // 2 + H // 32) + A * (I // 2 + I // 32)
+    gu_ms = stages["gateup"]
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    layer_bytes = float(np.mean([u * expert_bytes(H, I) for u in u_steps])) + H * E * 4 + 2 * T * H * 2
+    layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
+    flops = 6.0 * H * I * A
+
+    traffic = traffic_from_profile(name, gu_bytes)
+    result = {
+        "metric": METRIC,
+        "value": T * K / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: T={T} H={H} E={E} k={k} I={I} "
+                               f"resident={cfg.resident} ring={cfg.ring} S={S}",
+                   "T": T, "H": H, "E": E, "k": k, "I": I, "S": S, "rotate": nrot,
+                   "zipf_beta": base.beta},
+        "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algo_bytes_per_launch": gu_bytes,
+                     "mean_launch_us": gu_ms * 1e3},
+        "layer": {"algo_bytes_per_step": layer_bytes, "GB_per_s": layer_gbs,
+                  "hbm_frac": layer_gbs / HBM_PEAK_GBS, "distinct_slots_used": U,
+                  "assignments_per_s": A * K / (total_ms * 1e-3),
+                  "mxfp4_tflops": flops / (ms_step * 1e-3) / 1e12,
+                  "stage_us": {kk: v * 1e3 for kk, v in stages.items()},
+                  "wall_s": wall},
+    }
+    log(f"timed {K} steps: {ms_step * 1e3:.1f} us/step")
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one layer call")
+        result["cpu_baseline"] = cpu_baseline(base, k)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

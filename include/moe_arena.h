@@ -131,7 +131,13 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  * Workspace: moe_workspace_bytes(MOE_OP_ROUTE, T, H, E, k, 0, S) bytes, 256-byte
  *          aligned.  Contents on return are unspecified.
  * T = 0 is valid (only slot_offsets is written, all zero).
+ * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
+ *          `stream` when T > 0: before the router logits, before selection,
+ *          before bucket counting, before the scatter, and after it -- so a
+ *          caller can time each kernel stage.  Recording changes no result.
  */
+#define MOE_STAGE_EVENTS 5
+
 typedef struct moe_route_args {
   int T, H, E, k, S;
   const uint16_t* x;
@@ -148,6 +154,7 @@ typedef struct moe_route_args {
   uint8_t* xq;
   void* ws;
   size_t ws_bytes;
+  hipEvent_t* stage_events;
 } moe_route_args;
 
 int moe_route(const moe_route_args* args, hipStream_t stream);
@@ -192,6 +199,10 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  * Workspace: moe_workspace_bytes(MOE_OP_EXPERTS, T, H, 0, k, I, S) bytes.
  * Any copy into a slot the call reads (arena_load_slot) must be ordered before
  * it by the caller (hipStreamWaitEvent on the load's event).
+ * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
+ *          `stream` when T > 0 and S > 0: before the work list, before the
+ *          gate/up kernel, before the down kernel, before the combine, and after
+ *          it.  Recording changes no result.
  */
 typedef struct moe_experts_args {
   int T, H, I, k, S;
@@ -205,6 +216,7 @@ typedef struct moe_experts_args {
   uint16_t* out;
   void* ws;
   size_t ws_bytes;
+  hipEvent_t* stage_events;
 } moe_experts_args;
 
 int moe_experts_forward(const moe_experts_args* args, hipStream_t stream);

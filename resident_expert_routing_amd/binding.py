@@ -47,7 +47,8 @@ class RouteArgs(ctypes.Structure):
                 ("topk_score", ctypes.c_void_p), ("sel_expert", ctypes.c_void_p),
                 ("sel_weight", ctypes.c_void_p), ("sel_slot", ctypes.c_void_p),
                 ("slot_offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
-                ("xq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+                ("xq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("stage_events", ctypes.c_void_p)]
 
 
 class ExpertsArgs(ctypes.Structure):
@@ -57,9 +58,11 @@ class ExpertsArgs(ctypes.Structure):
                 ("slot_stride", ctypes.c_size_t), ("slot_offsets", ctypes.c_void_p),
                 ("perm", ctypes.c_void_p), ("sel_slot", ctypes.c_void_p),
                 ("sel_weight", ctypes.c_void_p), ("out", ctypes.c_void_p),
-                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t)]
+                ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
+                ("stage_events", ctypes.c_void_p)]
 
 
+MOE_STAGE_EVENTS = 5
 _lib = None
 
 
@@ -126,6 +129,16 @@ def _event(e) -> int | None:
     return int(e.cuda_event)
 
 
+def _events(evs):
+    """Sequence of MOE_STAGE_EVENTS events -> (ctypes array, its address) or (None, None)."""
+    if evs is None:
+        return None, None
+    if len(evs) != MOE_STAGE_EVENTS:
+        raise ValueError(f"stage_events needs {MOE_STAGE_EVENTS} events")
+    arr = (ctypes.c_void_p * MOE_STAGE_EVENTS)(*[_event(e) for e in evs])
+    return arr, ctypes.addressof(arr)
+
+
 def status_string(status: int) -> str:
     return load().moe_status_string(int(status)).decode()
 
@@ -155,11 +168,12 @@ def moe_workspace_bytes(op: int, T: int, H: int, E: int, k: int, I: int, S: int)
 
 def moe_route(T, H, E, k, S, x, w_router, bias, expert_slot, topk_expert, topk_score,
               sel_expert, sel_weight, sel_slot, slot_offsets, perm, xq, ws, ws_bytes,
-              stream=None) -> int:
+              stream=None, stage_events=None) -> int:
+    keep, evp = _events(stage_events)
     a = RouteArgs(int(T), int(H), int(E), int(k), int(S), _ptr(x), _ptr(w_router), _ptr(bias),
                   _ptr(expert_slot), _ptr(topk_expert), _ptr(topk_score), _ptr(sel_expert),
                   _ptr(sel_weight), _ptr(sel_slot), _ptr(slot_offsets), _ptr(perm), _ptr(xq),
-                  _ptr(ws), int(ws_bytes))
+                  _ptr(ws), int(ws_bytes), evp)
     return int(load().moe_route(ctypes.byref(a), _stream(stream)))
 
 
@@ -171,10 +185,11 @@ def moe_demand_accumulate(topk_expert, topk_score, T, k, E, hist_row, delta, ws,
 
 
 def moe_experts_forward(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm, sel_slot,
-                        sel_weight, out, ws, ws_bytes, stream=None) -> int:
+                        sel_weight, out, ws, ws_bytes, stream=None, stage_events=None) -> int:
+    keep, evp = _events(stage_events)
     a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
                     int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
-                    _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes))
+                    _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp)
     return int(load().moe_experts_forward(ctypes.byref(a), _stream(stream)))
 
 

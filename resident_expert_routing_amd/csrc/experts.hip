@@ -376,8 +376,11 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   float* y = reinterpret_cast<float*>(ws + W.y_off);
   const int A = T * k;
   const int maxU = S < A ? S : A;
+  hipEvent_t* ev = a->stage_events;
 
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_EHIP;
   build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_EHIP;
 
   GateUpArgs g;
   g.xq = a->xq;
@@ -404,6 +407,8 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   else
     gateup_kernel<false><<<gblocks, 256, 0, stream>>>(g);
 
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_EHIP;
+
   DownArgs d;
   d.hq = hq;
   d.hrow = g.hrow;
@@ -423,8 +428,10 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     down_kernel<true><<<dblocks, 256, 0, stream>>>(d);
   else
     down_kernel<false><<<dblocks, 256, 0, stream>>>(d);
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_EHIP;
 
   dim3 cgrid(T, (H + 1023) / 1024);
   combine_kernel<<<cgrid, 256, 0, stream>>>(y, a->sel_weight, a->sel_slot, T, H, k, S, a->out);
+  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_EHIP;
   return hip_status();
 }

@@ -395,9 +395,11 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     fill_i32<<<(S + 1 + 255) / 256, 256, 0, stream>>>(a->slot_offsets, S + 1, 0);
     return hip_status();
   }
+  hipEvent_t* ev = a->stage_events;
   double* zbuf = static_cast<double*>(a->ws);
   const int nchunk = (H + kRouterChunk - 1) / kRouterChunk;
   int nsplit = 0;
+  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_EHIP;
   if (T <= kSplitRouterMaxT) {
     dim3 grid((E + 63) / 64, (T + 3) / 4, nchunk);
     router_chunks_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, zbuf);
@@ -406,11 +408,15 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     dim3 grid((E + RT_E - 1) / RT_E, (T + RT_T - 1) / RT_T);
     router_full_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, zbuf);
   }
+  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_EHIP;
   route_select<<<(T + 3) / 4, 256, 0, stream>>>(
       zbuf, nsplit, a->bias, a->expert_slot, a->x, T, H, E, k, S, a->topk_expert, a->topk_score,
       a->sel_expert, a->sel_weight, a->sel_slot, a->xq, mxfp4_row_bytes(H));
   const int A = T * k;
+  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_EHIP;
   bucket_count_scan<<<1, 1024, 0, stream>>>(a->sel_slot, A, S, a->slot_offsets, a->perm);
+  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_EHIP;
   if (S > 0) bucket_scatter<<<S, 256, 0, stream>>>(a->sel_slot, A, a->slot_offsets, a->perm);
+  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_EHIP;
   return hip_status();
 }

@@ -81,11 +81,12 @@ class Arena:
         return self.mem.data_ptr()
 
 
-def route(buf: LayerBuffers, x, w_router, bias, expert_slot, stream=None) -> None:
+def route(buf: LayerBuffers, x, w_router, bias, expert_slot, stream=None,
+          stage_events=None) -> None:
     B.check(B.moe_route(buf.T, buf.H, buf.E, buf.k, buf.S, x, w_router, bias, expert_slot,
                         buf.topk_expert, buf.topk_score, buf.sel_expert, buf.sel_weight,
                         buf.sel_slot, buf.slot_offsets, buf.perm, buf.xq, buf.ws_route,
-                        buf.ws_route_bytes, stream), "moe_route")
+                        buf.ws_route_bytes, stream, stage_events), "moe_route")
 
 
 def demand(buf: LayerBuffers, hist_row, stream=None, delta=True) -> None:
@@ -94,11 +95,12 @@ def demand(buf: LayerBuffers, hist_row, stream=None, delta=True) -> None:
                                     buf.ws_demand_bytes, stream), "moe_demand_accumulate")
 
 
-def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None) -> None:
+def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None,
+            stage_events=None) -> None:
     B.check(B.moe_experts_forward(buf.T, buf.H, buf.I, buf.k, buf.S, buf.xq, arena_ptr,
                                   slot_stride, buf.slot_offsets, buf.perm, buf.sel_slot,
                                   buf.sel_weight, buf.out, buf.ws_experts, buf.ws_experts_bytes,
-                                  stream), "moe_experts_forward")
+                                  stream, stage_events), "moe_experts_forward")
 
 
 def layer_step(buf: LayerBuffers, x, w_router, bias, expert_slot, hist_row, arena_ptr,
