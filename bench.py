@@ -2,9 +2,10 @@
 """Routed tokens/s of one masked-top-k MXFP4 MoE layer on one MI355X.
 
 A step is one pass of the whole layer over one batch of tokens already
-resident in HBM: moe_route (router, demand picks, masked top-k, renormalise,
-bucket, MXFP4 activations) -> moe_demand_accumulate -> moe_experts_forward
-(grouped SwiGLU experts on MXFP4 arena slots + fixed-order combine).
+resident in HBM: moe_route (router logits, demand picks, masked top-k,
+renormalisation, bucketing by slot, MXFP4 activations, and the demand
+histogram update) followed by moe_experts_forward (grouped SwiGLU experts on
+MXFP4 arena slots and the fixed-order weighted combine).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
 
@@ -14,11 +15,13 @@ SwiGLU intermediate 2048, 166 resident + 64 hot-ring slots, Zipf-skewed
 router).  Steps rotate over 4 token batches and 4 copies of the arena so the
 256 MB Infinity Cache cannot serve expert bytes reused from a previous step.
 
-The roofline object reports the dominant kernel (the grouped gate/up GEMM,
-2/3 of the expert bytes): achieved = algorithmic bytes per launch (distinct
-slots used x gate+up bytes per slot, plus the activation rows it reads and
-the MXFP4 h rows it writes) / its mean launch time from HIP events recorded on
-the launch stream inside the timed region.
+Timing: W warmup steps, then K steps between two events on the launch stream
+(no other instrumentation) give `value` and `ms_per_step`.  A second run of K
+steps records HIP events only around the dominant kernel -- the grouped
+gate/up GEMM, 2/3 of the expert bytes -- for the roofline: achieved =
+algorithmic bytes per launch (distinct slots used x gate+up bytes per slot,
+plus the activation rows it reads and the MXFP4 h rows it writes) / mean
+launch time.
 """
 from __future__ import annotations
 
@@ -80,7 +83,7 @@ def expert_bytes(H: int, I: int) -> int:
     return 3 * H * I // 2 + 3 * H * I // 32
 
 
-def traffic_from_profile(workload: str, algo_bytes: float):
+def traffic_from_profile(workload: str):
     """HBM bytes per gate/up launch from the committed rocprofv3 PMC summary.
 
     Returns None if there is no summary or the kernel source changed since."""
@@ -95,8 +98,7 @@ def traffic_from_profile(workload: str, algo_bytes: float):
 
 
 def cpu_baseline(lay, k: int):
-    """The oracle (numpy float64) on one decode step, timed on the host cores."""
-    import numpy as np
+    """The oracle (numpy float64) on one full layer call, timed on the host cores."""
     from oracle import moe
     try:
         from threadpoolctl import threadpool_info
@@ -106,8 +108,8 @@ def cpu_baseline(lay, k: int):
     cfg = lay.cfg
     sc = lay.slot_content()
     t0 = time.perf_counter()
-    r = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k,
-                  lambda s: lay.content_bytes(sc[s]), cfg.H, cfg.I)
+    moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k,
+              lambda s: lay.content_bytes(sc[s]), cfg.H, cfg.I)
     dt = time.perf_counter() - t0
     T = lay.x_bits.shape[0]
     return {"value": T / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
@@ -161,10 +163,10 @@ def main():
     hist = torch.zeros(E, dtype=torch.float64, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev_r=None, ev_e=None):
+    def step(i, ev_e=None):
         j = i % nrot
-        R.route(buf, xs[j], w_router, bias, expert_slot, stream, ev_r)
-        R.demand(buf, hist, stream)
+        # demand is accumulated inside moe_route (same result as moe_demand_accumulate)
+        R.route(buf, xs[j], w_router, bias, expert_slot, stream, hist_row=hist)
         R.experts(buf, arenas[j].ptr(), arenas[j].stride, stream, ev_e)
 
     # distinct slots used by each rotation's routing (deterministic)
@@ -179,44 +181,46 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # ---- the timed steps ----
     K = args.steps
     mk = lambda: torch.cuda.Event(enable_timing=True)
-    ev_r = [[mk() for _ in range(5)] for _ in range(K)]
-    ev_e = [[mk() for _ in range(5)] for _ in range(K)]
     start, end = mk(), mk()
-    for e in [e for row in ev_r + ev_e for e in row]:
-        e.record(stream)   # torch creates the HIP event on first record
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for i in range(K):
-        step(i, ev_r[i], ev_e[i])
+        step(i)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K
+    log(f"timed {K} steps: {ms_step * 1e3:.1f} us/step")
 
-    # per-stage times (ms, mean over the timed steps)
-    def stage(evs, a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in evs]))
-    stages = {
-        "router_logits": stage(ev_r, 0, 1), "select": stage(ev_r, 1, 2),
-        "bucket_count": stage(ev_r, 2, 3), "bucket_scatter": stage(ev_r, 3, 4),
-        "worklist": stage(ev_e, 0, 1), "gateup": stage(ev_e, 1, 2), "down": stage(ev_e, 2, 3),
-        "combine": stage(ev_e, 3, 4),
-    }
+    # ---- the dominant kernel, timed with events on its launch stream ----
+    ev = [(mk(), mk()) for _ in range(K)]
+    for a_, b_ in ev:
+        a_.record(stream)   # torch creates the HIP event on first record
+        b_.record(stream)
+    torch.cuda.synchronize()
+    r0, r1 = mk(), mk()
+    r0.record(stream)
+    for i in range(K):
+        step(i, [None, ev[i][0], ev[i][1], None, None])
+    r1.record(stream)
+    torch.cuda.synchronize()
+    gu_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in ev]))
+    ms_step_ev = r0.elapsed_time(r1) / K
+
     A = T * k
     u_steps = [U[i % nrot] for i in range(K)]
     gu_bytes = float(np.mean([u * gateup_bytes_per_slot(H, I) for u in u_steps])) \
         + T * (H // 2 + H // 32) + A * (I // 2 + I // 32)
-    gu_ms = stages["gateup"]
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
     layer_bytes = float(np.mean([u * expert_bytes(H, I) for u in u_steps])) + H * E * 4 + 2 * T * H * 2
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
     flops = 6.0 * H * I * A
 
-    traffic = traffic_from_profile(name, gu_bytes)
     result = {
         "metric": METRIC,
         "value": T * K / (total_ms * 1e-3),
@@ -236,16 +240,15 @@ def main():
                    "zipf_beta": base.beta},
         "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algo_bytes_per_launch": gu_bytes,
-                     "mean_launch_us": gu_ms * 1e3},
+                     "traffic": traffic_from_profile(name), "algo_bytes_per_launch": gu_bytes,
+                     "mean_launch_us": gu_ms * 1e3,
+                     "ms_per_step_with_these_events": ms_step_ev},
         "layer": {"algo_bytes_per_step": layer_bytes, "GB_per_s": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS, "distinct_slots_used": U,
                   "assignments_per_s": A * K / (total_ms * 1e-3),
-                  "mxfp4_tflops": flops / (ms_step * 1e-3) / 1e12,
-                  "stage_us": {kk: v * 1e3 for kk, v in stages.items()},
-                  "wall_s": wall},
+                  "mxfp4_tflops": flops / (ms_step * 1e-3) / 1e12, "wall_s": wall},
     }
-    log(f"timed {K} steps: {ms_step * 1e3:.1f} us/step")
+    log(f"gate/up: {gu_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one layer call")
         result["cpu_baseline"] = cpu_baseline(base, k)

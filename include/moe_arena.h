@@ -105,7 +105,7 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *
  * Steps (TideLM README, "How adaptive expert loading works", items 1-2):
  *   z[t,e]  = sum_h x[t,h] * w_router[e,h] + bias[e], accumulated in float64:
- *             the sum over h runs in chunks of 128 (a fused multiply-add chain
+ *             the sum over h runs in chunks of 32 (a fused multiply-add chain
  *             over each chunk, ascending h), the chunk sums are added in
  *             ascending chunk order, then the bias.
  *   p[t,:]  = softmax over all E experts of z[t,:] (float64).
@@ -134,7 +134,16 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
  *          `stream` when T > 0: before the router logits, before selection,
  *          before bucket counting, before the scatter, and after it -- so a
- *          caller can time each kernel stage.  Recording changes no result.
+ *          caller can time each kernel stage.  For T <= 16 and E <= 256,
+ *          selection and bucketing run as one kernel and the last three events
+ *          are recorded together after it.  A null entry is not recorded.
+ *          Recording changes no result, but each record costs a few
+ *          microseconds of stream time.
+ * hist_row, delta (nullable): when hist_row is non-null the call also does
+ *          moe_demand_accumulate's work for this batch (same definition, same
+ *          float64 result): hist_row[e] += delta[e], delta (if non-null) gets
+ *          the per-call demand.  For small batches this runs inside the
+ *          selection kernel and saves a launch.
  */
 #define MOE_STAGE_EVENTS 5
 
@@ -155,6 +164,8 @@ typedef struct moe_route_args {
   void* ws;
   size_t ws_bytes;
   hipEvent_t* stage_events;
+  double* hist_row;
+  float* delta;
 } moe_route_args;
 
 int moe_route(const moe_route_args* args, hipStream_t stream);
@@ -202,7 +213,7 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
  *          `stream` when T > 0 and S > 0: before the work list, before the
  *          gate/up kernel, before the down kernel, before the combine, and after
- *          it.  Recording changes no result.
+ *          it.  A null entry is not recorded.  Recording changes no result.
  */
 typedef struct moe_experts_args {
   int T, H, I, k, S;

@@ -12,7 +12,8 @@
 namespace moe {
 
 constexpr int kWave = 64;
-constexpr int kRouterChunk = 128;   // h-chunk of the float64 router sum
+constexpr int kRouterChunk = 32;    // h-chunk of the float64 router sum
+constexpr int kRouterTile = 128;    // h staged per LDS tile by the tiled router
 constexpr int kSplitRouterMaxT = 64;  // at or below: chunk partials in parallel
 constexpr int kDemandChunk = 64;    // tokens per demand partial
 
@@ -47,6 +48,13 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 inline int hip_status() {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+// Records stage event i when the caller passed an array with a non-null entry
+// there; false only if the record itself fails.
+inline bool record_stage(hipEvent_t* ev, int i, hipStream_t stream) {
+  if (!ev || !ev[i]) return true;
+  return hipEventRecord(ev[i], stream) == hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

@@ -59,6 +59,22 @@ size_t moe_demand_ws_bytes_internal(int T, int E) {
   return up_to(nchunk * E * sizeof(double), 256);
 }
 
+// Enqueues the demand kernels (arguments already validated; ws holds
+// moe_demand_ws_bytes_internal(T, E) bytes).
+int moe_demand_launch_internal(const int32_t* te, const float* ts, int T, int k, int E,
+                               double* hist, float* delta, void* ws, hipStream_t stream) {
+  const int threads = E <= 256 ? 256 : 1024;
+  if (T <= kDemandChunk) {
+    demand_chunks<<<1, threads, 0, stream>>>(te, ts, T, k, E, nullptr, hist, delta);
+    return hip_status();
+  }
+  const int nchunk = (T + kDemandChunk - 1) / kDemandChunk;
+  double* part = static_cast<double*>(ws);
+  demand_chunks<<<nchunk, threads, 0, stream>>>(te, ts, T, k, E, part, hist, delta);
+  demand_finalize<<<1, threads, 0, stream>>>(part, nchunk, E, hist, delta);
+  return hip_status();
+}
+
 extern "C" MOE_EXPORT int moe_demand_accumulate(const int32_t* topk_expert,
                                                 const float* topk_score, int T, int k, int E,
                                                 double* hist_row, float* delta, void* ws,
@@ -71,16 +87,5 @@ extern "C" MOE_EXPORT int moe_demand_accumulate(const int32_t* topk_expert,
   const size_t need = moe_demand_ws_bytes_internal(T, E);
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if (need > 0 && (!ws || !aligned(ws, 256))) return MOE_EINVAL;
-  const int threads = E <= 256 ? 256 : 1024;
-  if (T <= kDemandChunk) {
-    demand_chunks<<<1, threads, 0, stream>>>(topk_expert, topk_score, T, k, E, nullptr, hist_row,
-                                             delta);
-    return hip_status();
-  }
-  const int nchunk = (T + kDemandChunk - 1) / kDemandChunk;
-  double* part = static_cast<double*>(ws);
-  demand_chunks<<<nchunk, threads, 0, stream>>>(topk_expert, topk_score, T, k, E, part, hist_row,
-                                                delta);
-  demand_finalize<<<1, threads, 0, stream>>>(part, nchunk, E, hist_row, delta);
-  return hip_status();
+  return moe_demand_launch_internal(topk_expert, topk_score, T, k, E, hist_row, delta, ws, stream);
 }

@@ -9,62 +9,128 @@
 //
 // Contraction layout shared by every GEMM here (so any token's result is the
 // same whatever batch it runs in): K is walked in 512-wide super-chunks
-// (16 MX blocks).  MFMA step i (0..3) of a super-chunk has lane group g (lanes
-// 16g..16g+15) supply MX block 4g+i, so a lane reads one contiguous 64-byte
-// run of codes and one aligned 4-byte word of scales per super-chunk, and the
-// scale byte for step i is selected in-instruction (op_sel = i).
+// (16 MX blocks) in ascending order; MFMA step i (0..3) of a super-chunk covers
+// blocks 4i..4i+3, lane group g (lanes 16g..16g+15) supplying block 4i+g.  One
+// load instruction thus reads 64 contiguous bytes of each of 16 rows.  A lane
+// reads the super-chunk's 16 scale bytes as one 16-byte word and shifts its
+// own byte (4i+g) into place for step i.
 #include "common.hpp"
 
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+constexpr int kInlineWorklistMaxS = 1024;
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int SEL>
 __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, uint32_t sa,
                                         uint32_t sb) {
   const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
-  // cbsz = blgp = 4: both operands E2M1; op_sel picks byte SEL of each scale word.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SEL, (int)sa, SEL,
+  // cbsz = blgp = 4: both operands E2M1; the scale is byte 0 of each scale word.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0,
                                                           (int)sb);
 }
 
+// One super-chunk of an MXFP4 row as this lane supplies it: codes of blocks
+// 4i+g (i = 0..3) and, in byte 0 of s[i], their scales.
+struct RowSC {
+  uint4 q[4];
+  uint32_t s[4];
+};
+
 // Four MFMA steps of one super-chunk for one 16-row tile.
-__device__ __forceinline__ v4f mfma_superchunk(const uint4* a, uint32_t sa, const uint4* b,
-                                               uint32_t sb, v4f c) {
-  c = mfma_fp4<0>(a[0], b[0], c, sa, sb);
-  c = mfma_fp4<1>(a[1], b[1], c, sa, sb);
-  c = mfma_fp4<2>(a[2], b[2], c, sa, sb);
-  c = mfma_fp4<3>(a[3], b[3], c, sa, sb);
+__device__ __forceinline__ v4f mfma_superchunk(const RowSC& a, const RowSC& b, v4f c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = mfma_fp4(a.q[i], b.q[i], c, a.s[i], b.s[i]);
   return c;
 }
 
-// Load this lane's share of super-chunk sc of an MXFP4 row: 4 blocks of codes
-// (64 bytes) and their 4 scale bytes.  Blocks at or past nblk read as zero.
+__device__ __forceinline__ void zero_sc(RowSC& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r.q[i] = make_uint4(0u, 0u, 0u, 0u);
+    r.s[i] = 127u;
+  }
+}
+
+// Load this lane's share of super-chunk sc of an MXFP4 row.  FULL: the row has
+// a multiple of 16 blocks and 16-byte aligned scales.  Blocks at or past nblk
+// read as zero codes.
 template <bool FULL>
 __device__ __forceinline__ void load_row_sc(const uint8_t* codes, const uint8_t* scales, int sc,
-                                            int g, int nblk, uint4* q, uint32_t& s) {
-  const int b0 = sc * 16 + g * 4;
-  if (FULL || b0 + 4 <= nblk) {
-    const uint4* p = reinterpret_cast<const uint4*>(codes + (size_t)b0 * 16);
-    q[0] = p[0];
-    q[1] = p[1];
-    q[2] = p[2];
-    q[3] = p[3];
-    s = *reinterpret_cast<const uint32_t*>(scales + b0);
+                                            int g, int nblk, RowSC& r) {
+  const int b0 = sc * 16;
+  if (FULL) {
+    const uint4* p = reinterpret_cast<const uint4*>(codes + (size_t)b0 * 16) + g;
+    r.q[0] = p[0];
+    r.q[1] = p[4];
+    r.q[2] = p[8];
+    r.q[3] = p[12];
+    const uint4 sv = *reinterpret_cast<const uint4*>(scales + b0);
+    const int sh = 8 * g;
+    r.s[0] = sv.x >> sh;
+    r.s[1] = sv.y >> sh;
+    r.s[2] = sv.z >> sh;
+    r.s[3] = sv.w >> sh;
   } else {
-    s = 0x7F7F7F7Fu;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (b0 + i < nblk) {
-        q[i] = reinterpret_cast<const uint4*>(codes + (size_t)(b0 + i) * 16)[0];
-        s = (s & ~(0xFFu << (8 * i))) | ((uint32_t)scales[b0 + i] << (8 * i));
+      const int bi = b0 + 4 * i + g;
+      if (bi < nblk) {
+        r.q[i] = reinterpret_cast<const uint4*>(codes + (size_t)bi * 16)[0];
+        r.s[i] = scales[bi];
       } else {
-        q[i] = make_uint4(0u, 0u, 0u, 0u);
+        r.q[i] = make_uint4(0u, 0u, 0u, 0u);
+        r.s[i] = 127u;
       }
     }
   }
+}
+
+// The u-th slot (ascending) that holds assignments, found by the whole
+// workgroup from slot_offsets; -1 if fewer slots are used.  Each thread scans a
+// contiguous range, then a workgroup prefix of the per-thread counts.
+__device__ int wg_nth_used_slot(int u, const int32_t* __restrict__ offsets, int S, int A) {
+  __shared__ int wsum[4];
+  __shared__ int found;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) found = -1;
+  const int per = (S + 255) / 256;
+  const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int local = 0;
+  for (int s = lo; s < hi; ++s) {
+    const int a = offsets[s], b = offsets[s + 1];
+    local += (b > a && a >= 0 && b <= A) ? 1 : 0;
+  }
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < wv; ++i) run += wsum[i];
+  if (u >= run && u < run + local) {
+    for (int s = lo; s < hi; ++s) {
+      const int a = offsets[s], b = offsets[s + 1];
+      if (b > a && a >= 0 && b <= A) {
+        if (run == u) found = s;
+        ++run;
+      }
+    }
+  }
+  __syncthreads();
+  return found;
+}
+
+// Slot of work item u: from the prebuilt list when there is one, else found
+// in place (small slot counts).
+__device__ __forceinline__ int work_slot(int u, const int32_t* used, const int32_t* offsets, int S,
+                                         int A) {
+  if (used) return u < used[0] ? used[1 + u] : -1;
+  return wg_nth_used_slot(u, offsets, S, A);
 }
 
 // ---------------------------------------------------------------------------
@@ -117,18 +183,18 @@ struct GateUpArgs {
   size_t off_gc, off_gs, off_uc, off_us;
   const int32_t* offsets;
   const int32_t* perm;
-  const int32_t* used;
+  const int32_t* used;  // prebuilt work list, or null: found in place
   uint8_t* hq;
   size_t hrow;
-  int T, H, I, k, A;
+  int T, H, I, k, A, S;
 };
 
 template <bool FULL>
 __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
   const int nbps = (p.I + 127) / 128;
   const int u = blockIdx.x / nbps, nb = blockIdx.x % nbps;
-  if (u >= p.used[0]) return;
-  const int s = p.used[1 + u];
+  const int s = work_slot(u, p.used, p.offsets, p.S, p.A);
+  if (s < 0) return;
   const int p0 = p.offsets[s], p1 = p.offsets[s + 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = nb * 128 + wave * 32;
@@ -159,22 +225,19 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
     const uint8_t* xc = t >= 0 ? p.xq + (size_t)t * p.xrow : nullptr;
     v4f ag0 = {0.f, 0.f, 0.f, 0.f}, ag1 = ag0, au0 = ag0, au1 = ag0;
     for (int sc = 0; sc < nsc; ++sc) {
-      uint4 qg0[4], qg1[4], qu0[4], qu1[4], qx[4];
-      uint32_t sg0, sg1, su0, su1, sx;
-      load_row_sc<FULL>(gc0, gs0, sc, g, nblk, qg0, sg0);
-      load_row_sc<FULL>(gc1, gs1, sc, g, nblk, qg1, sg1);
-      load_row_sc<FULL>(uc0, us0, sc, g, nblk, qu0, su0);
-      load_row_sc<FULL>(uc1, us1, sc, g, nblk, qu1, su1);
-      if (xc) {
-        load_row_sc<FULL>(xc, xc + H / 2, sc, g, nblk, qx, sx);
-      } else {
-        qx[0] = qx[1] = qx[2] = qx[3] = make_uint4(0u, 0u, 0u, 0u);
-        sx = 0x7F7F7F7Fu;
-      }
-      ag0 = mfma_superchunk(qg0, sg0, qx, sx, ag0);
-      ag1 = mfma_superchunk(qg1, sg1, qx, sx, ag1);
-      au0 = mfma_superchunk(qu0, su0, qx, sx, au0);
-      au1 = mfma_superchunk(qu1, su1, qx, sx, au1);
+      RowSC wg0, wg1, wu0, wu1, x;
+      load_row_sc<FULL>(gc0, gs0, sc, g, nblk, wg0);
+      load_row_sc<FULL>(gc1, gs1, sc, g, nblk, wg1);
+      load_row_sc<FULL>(uc0, us0, sc, g, nblk, wu0);
+      load_row_sc<FULL>(uc1, us1, sc, g, nblk, wu1);
+      if (xc)
+        load_row_sc<FULL>(xc, xc + H / 2, sc, g, nblk, x);
+      else
+        zero_sc(x);
+      ag0 = mfma_superchunk(wg0, x, ag0);
+      ag1 = mfma_superchunk(wg1, x, ag1);
+      au0 = mfma_superchunk(wu0, x, au0);
+      au1 = mfma_superchunk(wu1, x, au1);
     }
     // Epilogue.  Lane (c = lane&15, g) holds rows n0+4g+v (tile 0) and
     // n0+16+4g+v (tile 1) of column c.
@@ -223,17 +286,17 @@ struct DownArgs {
   size_t off_dc, off_ds;
   const int32_t* offsets;
   const int32_t* perm;
-  const int32_t* used;
+  const int32_t* used;  // prebuilt work list, or null: found in place
   float* y;
-  int H, I, A;
+  int H, I, A, S;
 };
 
 template <bool FULL>
 __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
   const int nbps = (p.H + 255) / 256;
   const int u = blockIdx.x / nbps, nb = blockIdx.x % nbps;
-  if (u >= p.used[0]) return;
-  const int s = p.used[1 + u];
+  const int s = work_slot(u, p.used, p.offsets, p.S, p.A);
+  if (s < 0) return;
   const int p0 = p.offsets[s], p1 = p.offsets[s + 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = nb * 256 + wave * 64;
@@ -261,21 +324,17 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl) acc[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
     for (int sc = 0; sc < nsc; ++sc) {
-      uint4 qx[4];
-      uint32_t sx;
-      if (hc) {
-        load_row_sc<FULL>(hc, hc + I / 2, sc, g, nblk, qx, sx);
-      } else {
-        qx[0] = qx[1] = qx[2] = qx[3] = make_uint4(0u, 0u, 0u, 0u);
-        sx = 0x7F7F7F7Fu;
-      }
+      RowSC x;
+      if (hc)
+        load_row_sc<FULL>(hc, hc + I / 2, sc, g, nblk, x);
+      else
+        zero_sc(x);
 #pragma unroll
       for (int tl = 0; tl < 4; ++tl) {
         if (tv[tl]) {
-          uint4 qw[4];
-          uint32_t sw;
-          load_row_sc<FULL>(dc[tl], ds[tl], sc, g, nblk, qw, sw);
-          acc[tl] = mfma_superchunk(qw, sw, qx, sx, acc[tl]);
+          RowSC w;
+          load_row_sc<FULL>(dc[tl], ds[tl], sc, g, nblk, w);
+          acc[tl] = mfma_superchunk(w, x, acc[tl]);
         }
       }
     }
@@ -378,9 +437,12 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   const int maxU = S < A ? S : A;
   hipEvent_t* ev = a->stage_events;
 
-  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_EHIP;
-  build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
-  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_EHIP;
+  // Work list of used slots: built once for large slot counts, else each
+  // workgroup finds its slot in place (saves a launch on decode batches).
+  const bool prebuilt = S > kInlineWorklistMaxS;
+  if (!record_stage(ev,0, stream)) return MOE_EHIP;
+  if (prebuilt) build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
+  if (!record_stage(ev,1, stream)) return MOE_EHIP;
 
   GateUpArgs g;
   g.xq = a->xq;
@@ -393,7 +455,7 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   g.off_us = L.off[3];
   g.offsets = a->slot_offsets;
   g.perm = a->perm;
-  g.used = used;
+  g.used = prebuilt ? used : nullptr;
   g.hq = hq;
   g.hrow = mxfp4_row_bytes(I);
   g.T = T;
@@ -401,13 +463,14 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   g.I = I;
   g.k = k;
   g.A = A;
+  g.S = S;
   const int gblocks = maxU * ((I + 127) / 128);
   if (H % 512 == 0)
     gateup_kernel<true><<<gblocks, 256, 0, stream>>>(g);
   else
     gateup_kernel<false><<<gblocks, 256, 0, stream>>>(g);
 
-  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_EHIP;
+  if (!record_stage(ev,2, stream)) return MOE_EHIP;
 
   DownArgs d;
   d.hq = hq;
@@ -418,20 +481,21 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   d.off_ds = L.off[5];
   d.offsets = a->slot_offsets;
   d.perm = a->perm;
-  d.used = used;
+  d.used = prebuilt ? used : nullptr;
   d.y = y;
   d.H = H;
   d.I = I;
   d.A = A;
+  d.S = S;
   const int dblocks = maxU * ((H + 255) / 256);
   if (I % 512 == 0)
     down_kernel<true><<<dblocks, 256, 0, stream>>>(d);
   else
     down_kernel<false><<<dblocks, 256, 0, stream>>>(d);
-  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_EHIP;
+  if (!record_stage(ev,3, stream)) return MOE_EHIP;
 
   dim3 cgrid(T, (H + 1023) / 1024);
   combine_kernel<<<cgrid, 256, 0, stream>>>(y, a->sel_weight, a->sel_slot, T, H, k, S, a->out);
-  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_EHIP;
+  if (!record_stage(ev,4, stream)) return MOE_EHIP;
   return hip_status();
 }

@@ -10,59 +10,124 @@
 
 namespace moe {
 
+constexpr int kFusedMaxT = 16;   // at or below: selection + bucketing in one workgroup
+
 // ---------------------------------------------------------------------------
 // Router logits in float64.  Definition shared by both kernels below:
-//   S_c = fma chain over h in chunk c (128 wide), ascending, starting from 0
+//   S_c = fma chain over h in chunk c (32 wide), ascending, starting from 0
 //   z   = S_0 + S_1 + ... (ascending c, starting from 0); bias added later.
 // Both kernels compute bit-identical values for a (t, e) whatever T is.
 // ---------------------------------------------------------------------------
 
-// One thread per (t, e, c): chunk partials, for small T (decode batches).
-__global__ __launch_bounds__(256) void router_chunks_f64(const uint16_t* __restrict__ x,
-                                                         const float* __restrict__ w, int T, int H,
-                                                         int E, double* __restrict__ zpart) {
-  const int e = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int t = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int c = blockIdx.z;
-  if (e >= E || t >= T) return;
-  const int h0 = c * kRouterChunk;
-  const int hn = min(kRouterChunk, H - h0);  // multiple of 32
-  const float4* wr = reinterpret_cast<const float4*>(w + (size_t)e * H + h0);
-  const uint2* xr = reinterpret_cast<const uint2*>(x + (size_t)t * H + h0);
-  double s = 0.0;
-  for (int q = 0; q < hn / 4; ++q) {
-    const float4 wv = wr[q];
-    const uint2 xv = xr[q];
-    s = fma((double)bf16_to_f32(xv.x & 0xFFFFu), (double)wv.x, s);
-    s = fma((double)bf16_to_f32(xv.x >> 16), (double)wv.y, s);
-    s = fma((double)bf16_to_f32(xv.y & 0xFFFFu), (double)wv.z, s);
-    s = fma((double)bf16_to_f32(xv.y >> 16), (double)wv.w, s);
+// MXFP4 activation rows, one element per thread: each aligned group of 32
+// threads encodes one block (amax by shuffles within the group), even lanes
+// write a byte of two codes, lane 0 the scale.  gid and gstride are multiples
+// of 32 and T*H is a multiple of 32, so a group is always whole.
+__device__ void quantize_x_elements(const uint16_t* __restrict__ x, int T, int H,
+                                    uint8_t* __restrict__ xq, size_t xq_row, size_t gid,
+                                    size_t gstride) {
+  const size_t n = (size_t)T * H;
+  for (size_t q = gid; q < n; q += gstride) {
+    const int t = (int)(q / H), h = (int)(q % H);
+    const float v = bf16_to_f32(x[q]);
+    float a = fabsf(v);
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) a = fmaxf(a, __shfl_xor(a, d, 32));
+    uint32_t code = 0u, scale = 0u;
+    if (a > 0.f) {
+      const int e = mx_block_exp(a);
+      code = e2m1_code(v, e);
+      scale = (uint32_t)(e + 127);
+    }
+    const uint32_t odd = __shfl_down(code, 1, 32);
+    const int li = (int)(q & 31);
+    uint8_t* row = xq + (size_t)t * xq_row;
+    if ((li & 1) == 0) row[h / 2] = (uint8_t)(code | (odd << 4));
+    if (li == 0) row[H / 2 + h / 32] = (uint8_t)scale;
   }
-  zpart[((size_t)c * T + t) * E + e] = s;
 }
 
-// Tiled full-K router for larger T: a workgroup owns 64 experts x 16 tokens; the
-// 128-wide chunk of W and x is staged in LDS; each thread keeps 4 tokens x 1
-// expert, with a per-chunk fma chain added into the running sum.
+// Small T (decode batches): a workgroup owns one expert and up to RS_T tokens;
+// thread c owns chunk c for all of them (the router chunk is loaded once, RS_T
+// independent fma chains); the chunk sums meet in LDS and are added in
+// ascending chunk order.  Workgroups from `nrb` on encode the activation rows
+// instead (one element per thread), alongside the dot products.
+constexpr int RS_T = 8;
+constexpr int RS_MAX_CHUNKS = 256;
+__global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restrict__ x,
+                                                        const float* __restrict__ w, int T, int H,
+                                                        int E, double* __restrict__ z,
+                                                        uint8_t* __restrict__ xq, size_t xq_row,
+                                                        int nrb) {
+  if ((int)blockIdx.x >= nrb) {
+    quantize_x_elements(x, T, H, xq, xq_row, (size_t)(blockIdx.x - nrb) * 256 + threadIdx.x,
+                        (size_t)(gridDim.x - nrb) * 256);
+    return;
+  }
+  __shared__ double part[RS_T][RS_MAX_CHUNKS + 1];
+  const int ntg = (T + RS_T - 1) / RS_T;
+  const int e = blockIdx.x / ntg, t0 = (blockIdx.x % ntg) * RS_T;
+  const int nt = min(RS_T, T - t0);
+  const int nchunk = H / kRouterChunk;  // H % 32 == 0
+  const int c = threadIdx.x;
+  if (c < nchunk) {
+    const int h0 = c * kRouterChunk;
+    const float4* w4 = reinterpret_cast<const float4*>(w + (size_t)e * H + h0);
+    float4 wv[kRouterChunk / 4];
+#pragma unroll
+    for (int q = 0; q < kRouterChunk / 4; ++q) wv[q] = w4[q];
+#pragma unroll
+    for (int i = 0; i < RS_T; ++i) {
+      if (i < nt) {
+        const uint4* x4 = reinterpret_cast<const uint4*>(x + (size_t)(t0 + i) * H + h0);
+        uint4 xv[kRouterChunk / 8];
+#pragma unroll
+        for (int q = 0; q < kRouterChunk / 8; ++q) xv[q] = x4[q];
+        double s = 0.0;
+#pragma unroll
+        for (int q = 0; q < kRouterChunk / 8; ++q) {
+          const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+          const float4 wa = wv[2 * q], wb = wv[2 * q + 1];
+          const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const uint32_t bits = (r & 1) ? (xw[r >> 1] >> 16) : (xw[r >> 1] & 0xFFFFu);
+            s = fma((double)bf16_to_f32(bits), (double)ww[r], s);
+          }
+        }
+        part[i][c] = s;
+      }
+    }
+  }
+  __syncthreads();
+  if (c < nt) {
+    double acc = 0.0;
+    for (int cc = 0; cc < nchunk; ++cc) acc += part[c][cc];
+    z[(size_t)(t0 + c) * E + e] = acc;
+  }
+}
+
+// Tiled full-K router for larger T: a workgroup owns 64 experts x 16 tokens; a
+// 128-wide tile of W and x is staged in LDS; each thread keeps 4 tokens x 1
+// expert, and each 32-wide chunk's fma chain is added into the running sum.
 constexpr int RT_E = 64, RT_T = 16, RT_TPT = 4;
 __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restrict__ x,
                                                        const float* __restrict__ w, int T, int H,
                                                        int E, double* __restrict__ z) {
-  __shared__ float ws[RT_E][kRouterChunk + 1];
-  __shared__ double xs[kRouterChunk][RT_T];
+  __shared__ float ws[RT_E][kRouterTile + 1];
+  __shared__ double xs[kRouterTile][RT_T];
   const int tid = threadIdx.x;
   const int el = tid & 63, tg = tid >> 6;
   const int e0 = blockIdx.x * RT_E, t0 = blockIdx.y * RT_T;
   double acc[RT_TPT], part[RT_TPT];
 #pragma unroll
   for (int i = 0; i < RT_TPT; ++i) acc[i] = 0.0;
-  const int nchunk = (H + kRouterChunk - 1) / kRouterChunk;
-  for (int c = 0; c < nchunk; ++c) {
-    const int h0 = c * kRouterChunk;
-    const int hn = min(kRouterChunk, H - h0);
-    // W tile: 64 rows x hn floats
-    for (int i = tid; i < RT_E * (kRouterChunk / 4); i += 256) {
-      const int r = i / (kRouterChunk / 4), q = i % (kRouterChunk / 4);
+  const int ntile = (H + kRouterTile - 1) / kRouterTile;
+  for (int c = 0; c < ntile; ++c) {
+    const int h0 = c * kRouterTile;
+    const int hn = min(kRouterTile, H - h0);
+    for (int i = tid; i < RT_E * (kRouterTile / 4); i += 256) {
+      const int r = i / (kRouterTile / 4), q = i % (kRouterTile / 4);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e0 + r < E && q * 4 < hn)
         v = *reinterpret_cast<const float4*>(w + (size_t)(e0 + r) * H + h0 + q * 4);
@@ -71,9 +136,8 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
       ws[r][q * 4 + 2] = v.z;
       ws[r][q * 4 + 3] = v.w;
     }
-    // x tile: 16 tokens x hn bf16, stored [h][t] as float64
-    for (int i = tid; i < RT_T * (kRouterChunk / 4); i += 256) {
-      const int r = i / (kRouterChunk / 4), q = i % (kRouterChunk / 4);
+    for (int i = tid; i < RT_T * (kRouterTile / 4); i += 256) {
+      const int r = i / (kRouterTile / 4), q = i % (kRouterTile / 4);
       uint2 v = make_uint2(0u, 0u);
       if (t0 + r < T && q * 4 < hn)
         v = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + r) * H + h0 + q * 4);
@@ -83,15 +147,17 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
       xs[q * 4 + 3][r] = (double)bf16_to_f32(v.y >> 16);
     }
     __syncthreads();
+    for (int c0 = 0; c0 < hn; c0 += kRouterChunk) {  // hn is a multiple of the chunk
 #pragma unroll
-    for (int i = 0; i < RT_TPT; ++i) part[i] = 0.0;
-    for (int h = 0; h < hn; ++h) {
-      const double wv = (double)ws[el][h];
+      for (int i = 0; i < RT_TPT; ++i) part[i] = 0.0;
+      for (int h = c0; h < c0 + kRouterChunk; ++h) {
+        const double wv = (double)ws[el][h];
 #pragma unroll
-      for (int i = 0; i < RT_TPT; ++i) part[i] = fma(xs[h][tg * RT_TPT + i], wv, part[i]);
+        for (int i = 0; i < RT_TPT; ++i) part[i] = fma(xs[h][tg * RT_TPT + i], wv, part[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < RT_TPT; ++i) acc[i] += part[i];
     }
-#pragma unroll
-    for (int i = 0; i < RT_TPT; ++i) acc[i] += part[i];
     __syncthreads();
   }
   const int e = e0 + el;
@@ -106,50 +172,107 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
 // ---------------------------------------------------------------------------
 // Per-token selection: one wave per token, expert e = lane + 64*i.
 // ---------------------------------------------------------------------------
-constexpr int kMaxPerLane = MOE_MAX_E / 64;
+// NPER: experts per lane held in registers (4 for E <= 256, 16 for E <= 1024).
 
-// Adds to `sel` (bit i = expert lane+64i) the best `want` experts among
-// `allowed & ~sel` by key (higher z, then lower id).  Returns how many were found.
-__device__ int wave_select(const double* z, uint32_t allowed, int nper, int want,
-                           uint32_t& sel) {
-  const int lane = threadIdx.x & 63;
-  int got = 0;
-  for (int r = 0; r < want; ++r) {
-    double bz = -INFINITY;
-    int be = 0x7FFFFFFF;
-    const uint32_t cand = allowed & ~sel;
+// Order-preserving map of a finite double to an unsigned key (larger z,
+// larger key; every key of a finite value is nonzero).
+__device__ __forceinline__ uint64_t order_key(double z) {
+  const uint64_t u = (uint64_t)__double_as_longlong(z);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Top-k selection by radix select over the 64-bit keys with wave ballots.
+// It selects (bit i = expert lane+64i) the min(want, #allowed) allowed experts
+// with the largest z, ties to the lower expert id: bit by bit from the top,
+// keep the branch that holds the want-th largest key, stopping as soon as the
+// keys matching the prefix are exactly the ones still needed; keys above the
+// prefix are taken, and keys equal to it fill the rest in ascending expert id.
+struct RadixSel {
+  uint64_t prefix, mask;
+  int remaining, match, total, n;
+  uint32_t allowed;
+  bool done;
+};
+
+template <int NPER>
+__device__ __forceinline__ void radix_init(RadixSel& s, uint32_t allowed, int want) {
+  s.allowed = allowed;
+  int total = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      if (i < nper && ((cand >> i) & 1u)) {
-        const int e = lane + 64 * i;
-        if (z[i] > bz || (z[i] == bz && e < be)) {
-          bz = z[i];
-          be = e;
-        }
-      }
-    }
+  for (int i = 0; i < NPER; ++i) total += __popcll(__ballot((allowed >> i) & 1u));
+  s.total = total;
+  s.n = min(want, total);
+  s.prefix = 0;
+  s.mask = 0;
+  s.remaining = s.n;
+  s.match = total;
+  s.done = s.n == 0 || s.n == total;
+}
+
+template <int NPER>
+__device__ __forceinline__ void radix_step(RadixSel& s, const uint64_t* key, int b) {
+  const uint64_t bit = 1ull << b;
+  int c1 = 0;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-      const double oz = __shfl_xor(bz, d, kWave);
-      const int oe = __shfl_xor(be, d, kWave);
-      if (oz > bz || (oz == bz && oe < be)) {
-        bz = oz;
-        be = oe;
-      }
-    }
-    if (be == 0x7FFFFFFF) break;  // wave-uniform: no candidate left
-    if ((be & 63) == lane) sel |= 1u << (be >> 6);
-    ++got;
+  for (int i = 0; i < NPER; ++i) {
+    const bool m = ((s.allowed >> i) & 1u) && ((key[i] & s.mask) == s.prefix) && (key[i] & bit);
+    c1 += __popcll(__ballot(m));
   }
-  return got;
+  if (c1 >= s.remaining) {
+    s.prefix |= bit;
+    s.match = c1;
+  } else {
+    s.remaining -= c1;
+    s.match -= c1;
+  }
+  s.mask |= bit;
+  if (s.match == s.remaining) s.done = true;
+}
+
+template <int NPER>
+__device__ __forceinline__ uint32_t radix_finish(const RadixSel& s, const uint64_t* key) {
+  if (s.n == 0) return 0u;
+  if (s.n == s.total) return s.allowed;
+  const uint64_t lt = lanemask_lt();
+  uint32_t sel = 0;
+  int before = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const bool a = (s.allowed >> i) & 1u;
+    const uint64_t hi = key[i] & s.mask;
+    const bool eq = a && hi == s.prefix;
+    const uint64_t meq = __ballot(eq);
+    const int rank = before + __popcll(meq & lt);
+    before += __popcll(meq);
+    if (a && (hi > s.prefix || (eq && rank < s.remaining))) sel |= 1u << i;
+  }
+  return sel;
+}
+
+// The unrestricted and the masked selection together, their bit steps
+// interleaved in one loop so the two independent chains of ballots overlap.
+template <int NPER>
+__device__ void wave_select_pair(const uint64_t* key, uint32_t allow_u, uint32_t allow_m, int want,
+                                 uint32_t& sel_u, uint32_t& sel_m, int& got_m) {
+  RadixSel u, m;
+  radix_init<NPER>(u, allow_u, want);
+  radix_init<NPER>(m, allow_m, want);
+  for (int b = 63; b >= 0 && !(u.done && m.done); --b) {
+    if (!u.done) radix_step<NPER>(u, key, b);
+    if (!m.done) radix_step<NPER>(m, key, b);
+  }
+  sel_u = radix_finish<NPER>(u, key);
+  sel_m = radix_finish<NPER>(m, key);
+  got_m = m.n;
 }
 
 // Position of each selected expert in ascending-id order.
+template <int NPER>
 __device__ __forceinline__ void selected_positions(uint32_t sel, int nper, int* pos) {
   const uint64_t lt = lanemask_lt();
   int base = 0;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NPER; ++i) {
     if (i < nper) {
       const uint64_t m = __ballot((sel >> i) & 1u);
       pos[i] = base + __popcll(m & lt);
@@ -158,39 +281,50 @@ __device__ __forceinline__ void selected_positions(uint32_t sel, int nper, int* 
   }
 }
 
-__global__ __launch_bounds__(256) void route_select(
-    const double* __restrict__ zsrc, int nsplit, const float* __restrict__ bias,
-    const int32_t* __restrict__ expert_slot, const uint16_t* __restrict__ x, int T, int H, int E,
-    int k, int S, int32_t* __restrict__ topk_expert, float* __restrict__ topk_score,
-    int32_t* __restrict__ sel_expert, float* __restrict__ sel_weight,
-    int32_t* __restrict__ sel_slot, uint8_t* __restrict__ xq, size_t xq_row) {
+struct SelectArgs {
+  const double* z;  // [T][E] logits without bias
+  const float* bias;
+  const int32_t* expert_slot;
+  const uint16_t* x;
+  int T, H, E, k, S;
+  int32_t* topk_expert;
+  float* topk_score;
+  int32_t* sel_expert;
+  float* sel_weight;
+  int32_t* sel_slot;
+  uint8_t* xq;
+  size_t xq_row;
+  int quantize_x;   // encode the activation row here (else the router kernel did)
+  double* hist;     // nullable: demand accumulated by the one-workgroup kernel
+  float* delta;
+};
+
+// One wave: everything per token t.  If sl is non-null the token's k slot
+// picks are also written there (sl[j], padded with -1), and if te is non-null
+// its demand picks and scores (te[j], ts[j]).
+template <int NPER>
+__device__ void select_token(const SelectArgs& p, int t, int* sl, int* te = nullptr,
+                             float* ts = nullptr) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // wave-uniform
+  const int E = p.E, k = p.k, H = p.H;
   const int nper = (E + 63) / 64;
 
-  // ---- logits: ascending chunk sums, then bias ----
-  double z[kMaxPerLane];
+  // ---- logits plus bias ----
+  double z[NPER];
   uint32_t valid = 0, routable = 0;
-  int slot_of[kMaxPerLane];
+  int slot_of[NPER];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NPER; ++i) {
     z[i] = -INFINITY;
     slot_of[i] = -1;
     const int e = lane + 64 * i;
     if (i < nper && e < E) {
-      double s = 0.0;
-      if (nsplit > 0) {
-        for (int c = 0; c < nsplit; ++c) s += zsrc[((size_t)c * T + t) * E + e];
-      } else {
-        s = zsrc[(size_t)t * E + e];
-      }
-      z[i] = s + (bias ? (double)bias[e] : 0.0);
+      z[i] = p.z[(size_t)t * E + e] + (p.bias ? (double)p.bias[e] : 0.0);
       valid |= 1u << i;
-      const int sl = expert_slot[e];
-      if (sl >= 0 && sl < S) {
+      const int s = p.expert_slot[e];
+      if (s >= 0 && s < p.S) {
         routable |= 1u << i;
-        slot_of[i] = sl;
+        slot_of[i] = s;
       }
     }
   }
@@ -198,13 +332,13 @@ __global__ __launch_bounds__(256) void route_select(
   // ---- softmax over all experts (float64) ----
   double m = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
+  for (int i = 0; i < NPER; ++i)
     if (i < nper) m = fmax(m, z[i]);
   m = wave_max(m);
-  double ex[kMaxPerLane];
+  double ex[NPER];
   double lsum = 0.0;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NPER; ++i) {
     ex[i] = 0.0;
     if (i < nper && ((valid >> i) & 1u)) {
       ex[i] = exp(z[i] - m);
@@ -214,48 +348,58 @@ __global__ __launch_bounds__(256) void route_select(
   const double denom = wave_sum(lsum);
 
   // ---- unrestricted top-k (demand picks) ----
-  uint32_t usel = 0;
-  wave_select(z, valid, nper, k, usel);
-  int pos[kMaxPerLane];
-  selected_positions(usel, nper, pos);
+  uint64_t key[NPER];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NPER; ++i) key[i] = order_key(z[i] + 0.0);  // -0 and +0 tie
+  uint32_t usel = 0, msel = 0;
+  int got = 0;
+  wave_select_pair<NPER>(key, valid, routable, k, usel, msel, got);
+  int pos[NPER];
+  selected_positions<NPER>(usel, nper, pos);
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
     if (i < nper && ((usel >> i) & 1u)) {
       const size_t o = (size_t)t * k + pos[i];
-      topk_expert[o] = lane + 64 * i;
-      topk_score[o] = (float)(ex[i] / denom);
+      const float score = (float)(ex[i] / denom);
+      p.topk_expert[o] = lane + 64 * i;
+      p.topk_score[o] = score;
+      if (te) {
+        te[pos[i]] = lane + 64 * i;
+        ts[pos[i]] = score;
+      }
     }
   }
 
-  // ---- masked top-k over routable experts, renormalised ----
-  uint32_t msel = 0;
-  const int got = wave_select(z, routable, nper, k, msel);
-  selected_positions(msel, nper, pos);
+  // ---- masked top-k over routable experts (selected above), renormalised ----
+  selected_positions<NPER>(msel, nper, pos);
   double psel = 0.0;
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i)
+  for (int i = 0; i < NPER; ++i)
     if (i < nper && ((msel >> i) & 1u)) psel += ex[i] / denom;
   const double wsum = wave_sum(psel);
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < NPER; ++i) {
     if (i < nper && ((msel >> i) & 1u)) {
       const size_t o = (size_t)t * k + pos[i];
-      sel_expert[o] = lane + 64 * i;
-      sel_weight[o] = (float)((ex[i] / denom) / wsum);
-      sel_slot[o] = slot_of[i];
+      p.sel_expert[o] = lane + 64 * i;
+      p.sel_weight[o] = (float)((ex[i] / denom) / wsum);
+      p.sel_slot[o] = slot_of[i];
+      if (sl) sl[pos[i]] = slot_of[i];
     }
   }
   for (int j = got + lane; j < k; j += 64) {
     const size_t o = (size_t)t * k + j;
-    sel_expert[o] = -1;
-    sel_weight[o] = 0.f;
-    sel_slot[o] = -1;
+    p.sel_expert[o] = -1;
+    p.sel_weight[o] = 0.f;
+    p.sel_slot[o] = -1;
+    if (sl) sl[j] = -1;
   }
 
   // ---- MXFP4 activation row: lane per 32-block ----
+  if (!p.quantize_x) return;
   const int nblk = H / 32;
-  const uint16_t* xr = x + (size_t)t * H;
-  uint8_t* qr = xq + (size_t)t * xq_row;
+  const uint16_t* xr = p.x + (size_t)t * H;
+  uint8_t* qr = p.xq + (size_t)t * p.xq_row;
   for (int b = lane; b < nblk; b += 64) {
     const uint4* src = reinterpret_cast<const uint4*>(xr + b * 32);
     float v[32];
@@ -280,15 +424,122 @@ __global__ __launch_bounds__(256) void route_select(
 #pragma unroll
       for (int i = 0; i < 32; ++i) words[i >> 3] |= e2m1_code(v[i], e) << (4 * (i & 7));
     }
-    *reinterpret_cast<uint4*>(qr + (size_t)b * 16) = make_uint4(words[0], words[1], words[2], words[3]);
+    *reinterpret_cast<uint4*>(qr + (size_t)b * 16) =
+        make_uint4(words[0], words[1], words[2], words[3]);
     qr[H / 2 + b] = (uint8_t)scale;
   }
 }
 
+template <int NPER>
+__global__ __launch_bounds__(256) void route_select(SelectArgs p) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;  // wave-uniform
+  select_token<NPER>(p, t, nullptr);
+}
+
 // ---------------------------------------------------------------------------
-// Bucketing: counts + exclusive scan in one workgroup, then a stable scatter
-// with one workgroup per slot scanning the assignments in ascending order.
+// Bucketing.  Counts per slot, exclusive offsets, and a stable scatter
+// (ascending assignment index within a slot).
 // ---------------------------------------------------------------------------
+
+// Workgroup of 1024 threads: cnt[0..S) holds counts on entry and exclusive
+// offsets on return; offsets[0..S] are written to global memory.  Returns the
+// total.
+__device__ int wg_offsets_from_counts(int* cnt, int S, int32_t* __restrict__ offsets,
+                                      int* wsum) {
+  const int tid = threadIdx.x;
+  const int per = (S + 1023) / 1024;
+  const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int local = 0;
+  for (int s = lo; s < hi; ++s) local += cnt[s];
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < wv; ++i) run += wsum[i];
+  for (int s = lo; s < hi; ++s) {
+    const int c = cnt[s];
+    offsets[s] = run;
+    cnt[s] = run;
+    run += c;
+  }
+  int total = 0;
+  for (int i = 0; i < 16; ++i) total += wsum[i];
+  if (tid == 0) offsets[S] = total;
+  __syncthreads();
+  return total;
+}
+
+// Small batches (E <= 256): selection for every token (wave t), demand (if
+// asked) and bucketing, in one workgroup of 1024 threads -- one compute unit,
+// so the waves meet at workgroup barriers with no device-wide fence.
+__global__ __launch_bounds__(1024) void route_fused_small(SelectArgs p,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ perm) {
+  constexpr int kMaxA = kFusedMaxT * MOE_MAX_K;
+  __shared__ int cnt[MOE_MAX_S];
+  __shared__ int4 sl4[kMaxA / 4];
+  __shared__ int4 te4[kMaxA / 4];
+  __shared__ float4 ts4[kMaxA / 4];
+  __shared__ int wsum[16];
+  int* sl = reinterpret_cast<int*>(sl4);
+  int* te = reinterpret_cast<int*>(te4);
+  float* ts = reinterpret_cast<float*>(ts4);
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int S = p.S, A = p.T * p.k;
+  const int A4 = (A + 3) / 4;
+  for (int s = tid; s < S; s += 1024) cnt[s] = 0;
+  for (int a = A + tid; a < 4 * A4; a += 1024) {  // pad the last vector
+    sl[a] = -1;
+    te[a] = -1;
+    ts[a] = 0.f;
+  }
+  if (wv < p.T) select_token<4>(p, wv, sl + wv * p.k, te + wv * p.k, ts + wv * p.k);
+  __syncthreads();
+  if (p.hist) {
+    // picks in ascending order (token, then pick): the order of float64
+    // additions of moe_demand_accumulate for one chunk of tokens
+    for (int e = tid; e < p.E; e += 1024) {
+      double acc = 0.0;
+      for (int q = 0; q < A4; ++q) {
+        const int4 ev = te4[q];
+        const float4 sv = ts4[q];
+        if (ev.x == e) acc += (double)sv.x;
+        if (ev.y == e) acc += (double)sv.y;
+        if (ev.z == e) acc += (double)sv.z;
+        if (ev.w == e) acc += (double)sv.w;
+      }
+      p.hist[e] += acc;
+      if (p.delta) p.delta[e] = (float)acc;
+    }
+  }
+  for (int a = tid; a < A; a += 1024) {
+    const int s = sl[a];
+    if (s >= 0 && s < S) atomicAdd(&cnt[s], 1);
+  }
+  __syncthreads();
+  const int total = wg_offsets_from_counts(cnt, S, offsets, wsum);
+  for (int a = tid; a < A; a += 1024) {
+    const int s = sl[a];
+    if (s >= 0 && s < S) {
+      int rank = 0;
+      for (int q = 0; q < a / 4; ++q) {
+        const int4 v = sl4[q];
+        rank += (v.x == s) + (v.y == s) + (v.z == s) + (v.w == s);
+      }
+      for (int b = a & ~3; b < a; ++b) rank += sl[b] == s;
+      perm[cnt[s] + rank] = a;
+    }
+  }
+  for (int a = total + tid; a < A; a += 1024) perm[a] = -1;
+}
+
 __global__ __launch_bounds__(1024) void bucket_count_scan(const int32_t* __restrict__ sel_slot,
                                                           int A, int S,
                                                           int32_t* __restrict__ offsets,
@@ -303,30 +554,7 @@ __global__ __launch_bounds__(1024) void bucket_count_scan(const int32_t* __restr
     if (s >= 0 && s < S) atomicAdd(&cnt[s], 1);
   }
   __syncthreads();
-  const int per = (S + 1023) / 1024;
-  const int lo = min(S, tid * per), hi = min(S, lo + per);
-  int local = 0;
-  for (int s = lo; s < hi; ++s) local += cnt[s];
-  // block exclusive scan of `local`
-  const int lane = tid & 63, wv = tid >> 6;
-  int incl = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  int wbase = 0;
-  for (int i = 0; i < wv; ++i) wbase += wsum[i];
-  int run = wbase + incl - local;
-  for (int s = lo; s < hi; ++s) {
-    offsets[s] = run;
-    run += cnt[s];
-  }
-  int total = 0;
-  for (int i = 0; i < 16; ++i) total += wsum[i];
-  if (tid == 0) offsets[S] = total;
+  const int total = wg_offsets_from_counts(cnt, S, offsets, wsum);
   for (int a = total + tid; a < A; a += 1024) perm[a] = -1;
 }
 
@@ -363,12 +591,16 @@ __global__ void fill_i32(int32_t* p, int n, int v) {
 
 using namespace moe;
 
+size_t moe_demand_ws_bytes_internal(int T, int E);
+int moe_demand_launch_internal(const int32_t* te, const float* ts, int T, int k, int E,
+                               double* hist, float* delta, void* ws, hipStream_t stream);
+
+// Workspace: float64 logits [T][E], then the demand partials of the batch.
+static size_t route_z_bytes(int T, int E) { return up_to((size_t)T * E * sizeof(double), 256); }
+
 static size_t route_ws_bytes(int T, int H, int E) {
   if (T <= 0) return 0;
-  const size_t nchunk = (size_t)(H + kRouterChunk - 1) / kRouterChunk;
-  const size_t zb = T <= kSplitRouterMaxT ? nchunk * T * E * sizeof(double)
-                                          : (size_t)T * E * sizeof(double);
-  return up_to(zb, 256);
+  return route_z_bytes(T, E) + moe_demand_ws_bytes_internal(T, E);
 }
 
 size_t moe_route_ws_bytes_internal(int T, int H, int E) { return route_ws_bytes(T, H, E); }
@@ -381,6 +613,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     return MOE_EUNSUPPORTED;
   if ((size_t)T * k > (size_t)INT32_MAX || (size_t)T * H > ((size_t)1 << 40)) return MOE_EINVAL;
   if (!a->slot_offsets) return MOE_EINVAL;
+  if (a->hist_row && !aligned(a->hist_row, 8)) return MOE_EINVAL;
   if (T > 0) {
     if (!a->x || !a->w_router || !a->expert_slot || !a->topk_expert || !a->topk_score ||
         !a->sel_expert || !a->sel_weight || !a->sel_slot || !a->perm || !a->xq)
@@ -393,30 +626,72 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
 
   if (T == 0) {
     fill_i32<<<(S + 1 + 255) / 256, 256, 0, stream>>>(a->slot_offsets, S + 1, 0);
+    if (a->hist_row && a->delta)
+      fill_i32<<<(E + 255) / 256, 256, 0, stream>>>((int32_t*)a->delta, E, 0);
     return hip_status();
   }
   hipEvent_t* ev = a->stage_events;
-  double* zbuf = static_cast<double*>(a->ws);
-  const int nchunk = (H + kRouterChunk - 1) / kRouterChunk;
-  int nsplit = 0;
-  if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return MOE_EHIP;
-  if (T <= kSplitRouterMaxT) {
-    dim3 grid((E + 63) / 64, (T + 3) / 4, nchunk);
-    router_chunks_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, zbuf);
-    nsplit = nchunk;
+  double* z = static_cast<double*>(a->ws);
+  void* dws = static_cast<uint8_t*>(a->ws) + route_z_bytes(T, E);
+  const int nchunk = H / kRouterChunk;
+  const size_t xq_row = mxfp4_row_bytes(H);
+  const bool small_router = T <= kSplitRouterMaxT && nchunk <= RS_MAX_CHUNKS;
+  if (!record_stage(ev,0, stream)) return MOE_EHIP;
+  if (small_router) {
+    const int nrb = E * ((T + RS_T - 1) / RS_T);
+    const size_t nx = ((size_t)T * H + 255) / 256;
+    const int nxb = (int)(nx < 1024 ? nx : 1024);
+    router_small_f64<<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, a->xq, xq_row,
+                                                    nrb);
   } else {
     dim3 grid((E + RT_E - 1) / RT_E, (T + RT_T - 1) / RT_T);
-    router_full_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, zbuf);
+    router_full_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z);
   }
-  if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return MOE_EHIP;
-  route_select<<<(T + 3) / 4, 256, 0, stream>>>(
-      zbuf, nsplit, a->bias, a->expert_slot, a->x, T, H, E, k, S, a->topk_expert, a->topk_score,
-      a->sel_expert, a->sel_weight, a->sel_slot, a->xq, mxfp4_row_bytes(H));
+  if (!record_stage(ev,1, stream)) return MOE_EHIP;
+  SelectArgs p;
+  p.z = z;
+  p.bias = a->bias;
+  p.expert_slot = a->expert_slot;
+  p.x = a->x;
+  p.T = T;
+  p.H = H;
+  p.E = E;
+  p.k = k;
+  p.S = S;
+  p.topk_expert = a->topk_expert;
+  p.topk_score = a->topk_score;
+  p.sel_expert = a->sel_expert;
+  p.sel_weight = a->sel_weight;
+  p.sel_slot = a->sel_slot;
+  p.xq = a->xq;
+  p.xq_row = xq_row;
+  p.quantize_x = small_router ? 0 : 1;
+  p.hist = nullptr;
+  p.delta = nullptr;
   const int A = T * k;
-  if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return MOE_EHIP;
+  if (T <= kFusedMaxT && E <= 256 && small_router) {
+    // selection, demand and bucketing in one kernel; the remaining stage
+    // events are recorded back to back
+    p.hist = a->hist_row;
+    p.delta = a->delta;
+    route_fused_small<<<1, 1024, 0, stream>>>(p, a->slot_offsets, a->perm);
+    for (int i = 2; i <= 4; ++i)
+      if (!record_stage(ev,i, stream)) return MOE_EHIP;
+    return hip_status();
+  }
+  if (E <= 256)
+    route_select<4><<<(T + 3) / 4, 256, 0, stream>>>(p);
+  else
+    route_select<16><<<(T + 3) / 4, 256, 0, stream>>>(p);
+  if (a->hist_row) {
+    const int st = moe_demand_launch_internal(a->topk_expert, a->topk_score, T, k, E, a->hist_row,
+                                              a->delta, dws, stream);
+    if (st != MOE_OK) return st;
+  }
+  if (!record_stage(ev,2, stream)) return MOE_EHIP;
   bucket_count_scan<<<1, 1024, 0, stream>>>(a->sel_slot, A, S, a->slot_offsets, a->perm);
-  if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return MOE_EHIP;
+  if (!record_stage(ev,3, stream)) return MOE_EHIP;
   if (S > 0) bucket_scatter<<<S, 256, 0, stream>>>(a->sel_slot, A, a->slot_offsets, a->perm);
-  if (ev && hipEventRecord(ev[4], stream) != hipSuccess) return MOE_EHIP;
+  if (!record_stage(ev,4, stream)) return MOE_EHIP;
   return hip_status();
 }

@@ -82,11 +82,13 @@ class Arena:
 
 
 def route(buf: LayerBuffers, x, w_router, bias, expert_slot, stream=None,
-          stage_events=None) -> None:
+          stage_events=None, hist_row=None) -> None:
+    """moe_route; with hist_row it also accumulates this batch's demand."""
     B.check(B.moe_route(buf.T, buf.H, buf.E, buf.k, buf.S, x, w_router, bias, expert_slot,
                         buf.topk_expert, buf.topk_score, buf.sel_expert, buf.sel_weight,
                         buf.sel_slot, buf.slot_offsets, buf.perm, buf.xq, buf.ws_route,
-                        buf.ws_route_bytes, stream, stage_events), "moe_route")
+                        buf.ws_route_bytes, stream, stage_events, hist_row,
+                        buf.delta if hist_row is not None else None), "moe_route")
 
 
 def demand(buf: LayerBuffers, hist_row, stream=None, delta=True) -> None:
@@ -104,8 +106,15 @@ def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None,
 
 
 def layer_step(buf: LayerBuffers, x, w_router, bias, expert_slot, hist_row, arena_ptr,
-               slot_stride, stream=None) -> None:
-    """One pass of the whole layer: route, demand, experts and combine."""
-    route(buf, x, w_router, bias, expert_slot, stream)
-    demand(buf, hist_row, stream)
+               slot_stride, stream=None, fused_demand=True) -> None:
+    """One pass of the whole layer: route, demand, experts and combine.
+
+    fused_demand: demand is accumulated by moe_route (same result as the
+    separate moe_demand_accumulate call, one launch fewer for small batches).
+    """
+    if fused_demand:
+        route(buf, x, w_router, bias, expert_slot, stream, hist_row=hist_row)
+    else:
+        route(buf, x, w_router, bias, expert_slot, stream)
+        demand(buf, hist_row, stream)
     experts(buf, arena_ptr, slot_stride, stream)

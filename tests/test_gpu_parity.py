@@ -179,6 +179,9 @@ def test_route_worked_example_ties():
     (70, 40, 6, 3, 3, 96),       # fewer routable than k: padding; H not a multiple of 128
     (65, 16, 4, 16, 16, 256),    # all resident, T just above the split-router limit
     (5, 1024, 32, 700, 8192, 64),  # maximum E, k and S
+    (9, 200, 8, 150, 8192, 128),   # one-workgroup selection + bucketing with the maximum S
+    (16, 256, 8, 230, 230, 4096),  # largest batch of the one-workgroup path
+    (17, 256, 8, 230, 230, 4096),  # smallest batch of the multi-kernel path
 ])
 def test_route_edge_shapes(T, E, k, nr, S, H):
     say(f"moe_route edge T={T} E={E} k={k} routable={nr} S={S} H={H}")
@@ -306,6 +309,30 @@ def test_layer_edge_shapes(T, E, k, nr, H, I):
     _layer_parity(GpuLayer(lay))
 
 
+def test_layer_sparse_slots_prebuilt_worklist():
+    """More than 1024 slots: the expert kernels take their work from a list
+    built once instead of scanning slot_offsets in every workgroup."""
+    say("layer with 12 routable experts spread over 2000 slots")
+    T, H, E, k, I, S = 24, 256, 16, 4, 128, 2000
+    lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=I, n_routable=12, seed=31, bias_scale=0.5)
+    rng = np.random.default_rng(2)
+    spread = rng.choice(S, size=12, replace=False)
+    es = lay.expert_slot.copy()
+    es[es >= 0] = spread[es[es >= 0]]
+    slot_expert = np.full(S, -1)
+    slot_expert[es[es >= 0]] = np.flatnonzero(es >= 0)
+    lay.slot_expert = slot_expert.astype(np.int32)
+    g = GpuLayer.__new__(GpuLayer)
+    _init_route_only(g, lay, es, S)
+    from resident_expert_routing_amd import runtime as R
+    import torch
+    g.arena = R.Arena(S, H, I, torch.device("cuda", 0))
+    g.arena.mem.zero_()
+    g.arena.upload(lambda s: lay.expert_bytes(slot_expert[s]), slots=spread)
+    g.slot_bytes_fn = lambda: (lambda s: lay.expert_bytes(slot_expert[s]))
+    _layer_parity(g)
+
+
 def test_layer_nothing_routable():
     import torch
     say("layer with no routable expert (S=0): output is zero")
@@ -357,3 +384,25 @@ def test_scale_bump_doubles_expert():
     bumped = g.out_f64()
     # out is bf16(sum w*y); doubling every y doubles the fp32 sum exactly
     assert np.array_equal(bumped, 2 * base)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
+def test_route_with_demand_equals_separate_call(name):
+    """moe_route with hist_row gives bit-for-bit the demand of moe_demand_accumulate."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    g = gpu_layer(name)
+    say(f"moe_route with fused demand on {name}")
+    g.route()
+    g.hist.zero_()
+    g.demand()
+    torch.cuda.synchronize()
+    want_hist = g.hist.cpu().numpy().copy()
+    want_delta = g.buf.delta.cpu().numpy().copy()
+    g.hist.zero_()
+    g.buf.delta.fill_(-1.0)
+    R.route(g.buf, g.x, g.w_router, g.bias, g.expert_slot, hist_row=g.hist)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.hist.cpu().numpy(), want_hist)
+    assert np.array_equal(g.buf.delta.cpu().numpy(), want_delta)
+    check_route(g, oracle_route(g))
