@@ -14,13 +14,21 @@ from __future__ import annotations
 import numpy as np
 
 
-def pick_shares(p: np.ndarray, topk_expert: np.ndarray) -> np.ndarray:
-    """share[t,j] = p[t,e_j] / sum over the token's unrestricted picks."""
-    v = np.take_along_axis(p, topk_expert, axis=1)
-    return v / v.sum(axis=1, keepdims=True)
+def pick_shares(topk_score: np.ndarray) -> np.ndarray:
+    """share[t,j] = score[t,j] / sum over the token's unrestricted picks.
+
+    The scores are the recorded float32 routing scores; the arithmetic is
+    float64 with the sum taken in ascending pick order, so that the >= 0.2
+    decision is taken in one stated precision on every implementation.
+    """
+    v = np.asarray(topk_score, dtype=np.float32).astype(np.float64)
+    s = np.zeros(v.shape[0], dtype=np.float64)
+    for j in range(v.shape[1]):
+        s = s + v[:, j]
+    return v / s[:, None]
 
 
-def hot_read(p, topk_expert, expert_slot, hist_after, n_arena, threshold=0.2):
+def hot_read(topk_score, topk_expert, expert_slot, hist_after, n_arena, threshold=0.2):
     """O12.  Returns (e_star, c, new_expert_slot) or None when no miss qualifies.
 
     e_star: the non-routable expert with the largest share >= threshold over
@@ -30,7 +38,7 @@ def hot_read(p, topk_expert, expert_slot, hist_after, n_arena, threshold=0.2):
     non-routable.
     """
     es = np.asarray(expert_slot)
-    share = pick_shares(p, topk_expert)
+    share = pick_shares(topk_score)
     best = None  # (share, -e, -t) maximised
     T, k = topk_expert.shape
     for t in range(T):

@@ -65,5 +65,5 @@ def test_long_workload_has_a_hot_miss():
     lay = fixtures.make_layer("long")
     r = moe.route(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, 8)
     d = moe.demand_fast(r["topk_expert"], r["topk_score"], 192)
-    got = plan.hot_read(r["p"], r["topk_expert"], lay.expert_slot, d, n_arena=130)
+    got = plan.hot_read(r["topk_score"], r["topk_expert"], lay.expert_slot, d, n_arena=130)
     assert got is not None

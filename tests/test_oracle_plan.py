@@ -2,11 +2,19 @@
 
 Constructed cases with known answers and brute force over small tables.
 """
-import itertools
-
 import numpy as np
 
 from oracle import plan
+
+
+def scores(p, te):
+    return np.take_along_axis(p, te, axis=1).astype(np.float32)
+
+
+def test_pick_shares_sum_in_order():
+    ts = np.array([[0.25, 0.5, 0.25], [1.0, 0.0, 0.0]], dtype=np.float32)
+    s = plan.pick_shares(ts)
+    assert np.array_equal(s, [[0.25, 0.5, 0.25], [1.0, 0.0, 0.0]])
 
 
 def test_hot_read_planted_miss():
@@ -22,7 +30,7 @@ def test_hot_read_planted_miss():
     te = np.array([[2, 3], [0, 5], [6, 7]])
     es = np.array([0, 1, 2, 3, -1, -1, 4, -1])
     hist = np.array([5.0, 0.5, 0.5, 2.0, 0, 0, 1.0, 0])
-    r = plan.hot_read(p, te, es, hist, n_arena=5)
+    r = plan.hot_read(scores(p, te), te, es, hist, n_arena=5)
     assert r is not None
     e_star, c, new = r
     # expert 7 is a miss too but its share (0.05/0.95) is below 0.2
@@ -36,13 +44,22 @@ def test_hot_read_none_below_threshold():
     te = np.array([[0, 1]])
     es = np.array([0, -1, 1])
     # share of expert 1 = 0.35/0.75 = 0.467 > 0.2 -> one candidate
-    assert plan.hot_read(p, te, es, np.zeros(3), 2)[0] == 1
+    assert plan.hot_read(scores(p, te), te, es, np.zeros(3), 2)[0] == 1
     p = np.array([[0.9, 0.1, 0.0]])
     te = np.array([[0, 1]])
     es = np.array([0, -1, -1])
     p2 = np.array([[0.95, 0.05, 0.0]])
-    assert plan.hot_read(p2, te, es, np.zeros(3), 1) is None      # share 0.05 < 0.2
-    assert plan.hot_read(p, te, es, np.zeros(3), 1) is None       # share exactly 0.1
+    assert plan.hot_read(scores(p2, te), te, es, np.zeros(3), 1) is None   # share 0.05 < 0.2
+    assert plan.hot_read(scores(p, te), te, es, np.zeros(3), 1) is None    # share 0.1
+
+
+def test_hot_read_share_tie_breaks():
+    # two misses with the same share: lower expert id wins; same expert: lower token
+    te = np.array([[0, 3], [0, 2], [1, 3]])
+    ts = np.array([[0.5, 0.5], [0.5, 0.5], [0.5, 0.5]], dtype=np.float32)
+    es = np.array([0, 1, -1, -1])
+    e_star, c, _ = plan.hot_read(ts, te, es, np.array([1.0, 0.5, 0, 0]), n_arena=2)
+    assert e_star == 2 and c == 1
 
 
 def test_hot_read_ring_slots_never_evicted():
@@ -50,7 +67,7 @@ def test_hot_read_ring_slots_never_evicted():
     te = np.array([[0, 1]])
     es = np.array([-1, 2, 0, 1])         # slot 2 is a ring slot (n_arena = 2)
     hist = np.array([0.0, 0.0, 3.0, 4.0])  # expert 1 is coldest but lives in the ring
-    e_star, c, new = plan.hot_read(p, te, es, hist, n_arena=2)
+    e_star, c, new = plan.hot_read(scores(p, te), te, es, hist, n_arena=2)
     assert e_star == 0 and c == 2
 
 
