@@ -250,6 +250,31 @@ int arena_load_slot(uint8_t* arena, size_t slot_stride, int num_slots, int slot,
                     const void* host_src, size_t bytes, hipStream_t side_stream, hipEvent_t done);
 
 /*
+ * moe_hot_pick -- the hot-read decision for one layer call (TideLM README,
+ * "How adaptive expert loading works", item 3, GLM-5.3 bullet: a layer's
+ * heaviest miss carrying at least 0.2 of a token's routing weight is read
+ * before the layer's experts run and kept in place of the coldest expert).
+ *
+ *   share[t,j] = topk_score[t,j] / sum_j' topk_score[t,j'] over the token's
+ *                unrestricted picks, in float64 with the sum in ascending j;
+ *   out[0] = e*: among picks whose expert is not routable (expert_slot outside
+ *            [0, S)) and whose share >= threshold, the one with the largest
+ *            share, ties to the lower expert id, then the lower token; -1 if none;
+ *   out[1] = c: among experts with 0 <= expert_slot[e] < n_arena (arena slots;
+ *            hot-ring slots are never evicted), the one with the smallest
+ *            hist_row[e], ties to the lower id; -1 if none.
+ * Inputs : topk_expert, topk_score [T][k] as written by moe_route; expert_slot
+ *          [E]; hist_row [E] double (the history after this call's demand).
+ * Output : out [2] int32 (device).  One kernel; no workspace.
+ * The caller reads out, copies expert e*'s bytes into c's slot with
+ * arena_load_slot, sets expert_slot[e*] = old slot of c and expert_slot[c] = -1,
+ * routes again without demand, and orders moe_experts_forward after the copy.
+ */
+int moe_hot_pick(const int32_t* topk_expert, const float* topk_score, int T, int k, int E,
+                 const int32_t* expert_slot, int S, int n_arena, const double* hist_row,
+                 double threshold, int32_t* out, hipStream_t stream);
+
+/*
  * moe_test_mxfp4_probe -- test-only: one wave runs one block-scaled MXFP4
  * matrix instruction (16x16 output, contraction 128) on raw per-lane operands,
  * so a test can check the hardware's decoding of E2M1 codes and E8M0 scales and

@@ -30,7 +30,7 @@ MOE_MAX_S = 8192
 
 EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
-           "arena_load_slot", "moe_test_mxfp4_probe")
+           "arena_load_slot", "moe_hot_pick", "moe_test_mxfp4_probe")
 
 
 class MoeError(RuntimeError):
@@ -74,7 +74,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m resident_expert_routing_amd.build`")
+                          "`python resident_expert_routing_amd/build.py`")
     # torch ships its own HIP runtime (libamdhip64.so, soname libamdhip64.so.7).  Loading
     # torch first makes this library's libamdhip64.so.7 dependency resolve to that same
     # copy, so device pointers and streams from torch are valid here; loading this
@@ -100,6 +100,8 @@ def load() -> ctypes.CDLL:
     lib.moe_experts_forward.restype = i
     lib.arena_load_slot.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
     lib.arena_load_slot.restype = i
+    lib.moe_hot_pick.argtypes = [vp, vp, i, i, i, vp, i, i, vp, ctypes.c_double, vp, vp]
+    lib.moe_hot_pick.restype = i
     lib.moe_test_mxfp4_probe.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.moe_test_mxfp4_probe.restype = i
     _lib = lib
@@ -199,6 +201,13 @@ def arena_load_slot(arena, slot_stride, num_slots, slot, host_src, nbytes, side_
     return int(load().arena_load_slot(_ptr(arena), int(slot_stride), int(num_slots), int(slot),
                                       _ptr(host_src), int(nbytes), _stream(side_stream),
                                       _event(done)))
+
+
+def moe_hot_pick(topk_expert, topk_score, T, k, E, expert_slot, S, n_arena, hist_row, threshold,
+                 out, stream=None) -> int:
+    return int(load().moe_hot_pick(_ptr(topk_expert), _ptr(topk_score), int(T), int(k), int(E),
+                                   _ptr(expert_slot), int(S), int(n_arena), _ptr(hist_row),
+                                   float(threshold), _ptr(out), _stream(stream)))
 
 
 def moe_test_mxfp4_probe(a, a_scale, b, b_scale, d, stream=None) -> int:

@@ -1,6 +1,9 @@
 """Build libmoe_arena.so (all HIP sources, gfx950) in-tree.
 
-    python -m resident_expert_routing_amd.build
+    python resident_expert_routing_amd/build.py
+
+(run as a file: importing the package loads the library, which may be missing
+or stale before this has run).
 
 Every call compiles; objects go to _build/ at the repository root.
 """
@@ -17,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_arena.so")
-SOURCES = ["capi.cpp", "route.hip", "demand.hip", "experts.hip", "probe.hip"]
+SOURCES = ["capi.cpp", "route.hip", "demand.hip", "experts.hip", "plan.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -105,6 +105,69 @@ def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None,
                                   stream, stage_events), "moe_experts_forward")
 
 
+class HotReader:
+    """Host side of the hot read for one layer.
+
+    The decision runs on the GPU (moe_hot_pick); the host reads the two ids,
+    copies the missing expert's bytes from page-locked memory into the coldest
+    expert's slot with arena_load_slot on a side stream, and updates the
+    device expert_slot table on the layer's stream.
+    """
+
+    def __init__(self, expert_slot_host: np.ndarray, n_arena: int, device, threshold: float = 0.2):
+        self.es = np.asarray(expert_slot_host, dtype=np.int32).copy()
+        self.n_arena = int(n_arena)
+        self.threshold = float(threshold)
+        self.device = device
+        self.out = torch.empty(2, dtype=torch.int32, device=device)
+        self.side = torch.cuda.Stream(device)   # default priority
+        self.done = torch.cuda.Event()
+        self._pinned = {}
+
+    def pinned(self, host_bytes: np.ndarray) -> torch.Tensor:
+        key = id(host_bytes)
+        if key not in self._pinned:
+            self._pinned[key] = torch.from_numpy(np.ascontiguousarray(host_bytes)).pin_memory()
+        return self._pinned[key]
+
+    def pick_and_load(self, buf: LayerBuffers, expert_slot_dev, hist_row, arena: Arena,
+                      expert_bytes_fn, stream):
+        """Returns (e_star, c, slot) after enqueueing the copy, or None."""
+        B.check(B.moe_hot_pick(buf.topk_expert, buf.topk_score, buf.T, buf.k, buf.E,
+                               expert_slot_dev, buf.S, self.n_arena, hist_row, self.threshold,
+                               self.out, stream), "moe_hot_pick")
+        self.side.wait_stream(stream)
+        e_star, c = (int(v) for v in self.out.cpu())   # waits for the decision
+        if e_star < 0 or c < 0:
+            return None
+        slot = int(self.es[c])
+        src = self.pinned(expert_bytes_fn(e_star))
+        B.check(B.arena_load_slot(arena.mem, arena.stride, arena.S, slot, src, arena.slot_bytes,
+                                  self.side, self.done), "arena_load_slot")
+        self.es[e_star], self.es[c] = slot, -1
+        with torch.cuda.stream(stream):
+            expert_slot_dev[e_star] = slot
+            expert_slot_dev[c] = -1
+        return e_star, c, slot
+
+
+def layer_step_hot(buf: LayerBuffers, x, w_router, bias, expert_slot_dev, hist_row,
+                   arena: Arena, hot: HotReader, expert_bytes_fn, stream=None):
+    """One layer call with a hot read before the experts (long prefill chunks).
+
+    Route with demand, decide and start the copy, route again over the new
+    routable set (overlapping the copy), then run the experts after the copy.
+    """
+    stream = stream if stream is not None else torch.cuda.current_stream(hot.device)
+    route(buf, x, w_router, bias, expert_slot_dev, stream, hist_row=hist_row)
+    picked = hot.pick_and_load(buf, expert_slot_dev, hist_row, arena, expert_bytes_fn, stream)
+    if picked is not None:
+        route(buf, x, w_router, bias, expert_slot_dev, stream)
+        stream.wait_event(hot.done)
+    experts(buf, arena.ptr(), arena.stride, stream)
+    return picked
+
+
 def layer_step(buf: LayerBuffers, x, w_router, bias, expert_slot, hist_row, arena_ptr,
                slot_stride, stream=None, fused_demand=True) -> None:
     """One pass of the whole layer: route, demand, experts and combine.

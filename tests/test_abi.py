@@ -194,3 +194,14 @@ def test_single_hip_runtime_in_process():
     B.load()
     import torch  # noqa: F401
     assert len(hip_runtimes_mapped()) == 1, hip_runtimes_mapped()
+
+
+def test_hot_pick_rejects():
+    h = B.moe_hot_pick
+    assert h(FAKE, FAKE, 8, 4, 16, None, 10, 10, FAKE, 0.2, FAKE) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, None, 0.2, FAKE) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, 0.2, None) == B.MOE_EINVAL
+    assert h(None, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, 0.2, FAKE) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 8, 40, 16, FAKE, 10, 10, FAKE, 0.2, FAKE) == B.MOE_EUNSUPPORTED
+    assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, float("nan"), FAKE) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 8, 4, 16, FAKE, -1, 10, FAKE, 0.2, FAKE) == B.MOE_EINVAL

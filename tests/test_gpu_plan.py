@@ -1,0 +1,179 @@
+"""GPU parity of the hot read: moe_hot_pick against the oracle's decision, and
+the whole hot-read layer call (route with demand, pick, copy into the coldest
+expert's slot, re-route, experts) against the oracle run with the new table.
+
+Bars: the decision (e*, c) and every routing output bit-exact; the slot's bytes
+equal the loaded expert's packed bytes; output relative L2 within 5e-3.
+"""
+import numpy as np
+import pytest
+
+import fixtures
+from oracle import moe, plan
+from gpu_helpers import GpuLayer, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+OUT_REL_L2 = 5e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_ready():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import resident_expert_routing_amd  # noqa: F401
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def gpu_pick(te, ts, es, hist, n_arena, threshold=0.2):
+    import torch
+    import resident_expert_routing_amd as m
+    T, k = te.shape
+    E = es.shape[0]
+    S = int(es.max()) + 1 if (es >= 0).any() else 0
+    out = torch.full((2,), 7, dtype=torch.int32, device="cuda")
+    m.check(m.moe_hot_pick(to_dev(te.astype(np.int32)) if T else None,
+                           to_dev(ts.astype(np.float32)) if T else None, T, k, E,
+                           to_dev(es.astype(np.int32)), S, n_arena, to_dev(hist.astype(np.float64)),
+                           threshold, out), "moe_hot_pick")
+    torch.cuda.synchronize()
+    return [int(v) for v in out.cpu()]
+
+
+def oracle_pick(te, ts, es, hist, n_arena, threshold=0.2):
+    r = plan.hot_read(ts, te, es, hist, n_arena, threshold)
+    if r is None:
+        return None
+    return [r[0], r[1]]
+
+
+def test_hot_pick_random_tables_with_ties():
+    rng = np.random.default_rng(11)
+    cases = 0
+    for trial in range(60):
+        T = int(rng.integers(1, 3000))
+        E = int(rng.integers(4, 300))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        te = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        te.sort(axis=1)
+        # quantised scores give many equal shares
+        ts = (rng.integers(1, 9, size=(T, k)) / 16.0).astype(np.float32)
+        nres = int(rng.integers(1, E + 1))
+        es = np.full(E, -1, dtype=np.int32)
+        es[rng.choice(E, nres, replace=False)] = rng.permutation(nres)
+        n_arena = int(rng.integers(1, nres + 1))    # slot 0 is always an arena slot
+        hist = rng.integers(0, 4, size=E).astype(np.float64)
+        thr = float(rng.choice([0.0, 0.05, 0.2, 0.5]))
+        want = oracle_pick(te, ts, es, hist, n_arena, thr)
+        got = gpu_pick(te, ts, es, hist, n_arena, thr)
+        if want is None:
+            assert got[0] == -1, (trial, got)
+            arena = [e for e in range(E) if 0 <= es[e] < n_arena]
+            assert got[1] == min(arena, key=lambda e: (hist[e], e))
+        else:
+            assert got == want, (trial, T, E, k, got, want)
+            cases += 1
+    say(f"hot_pick: {cases} of 60 random tables had a qualifying miss")
+    assert cases > 20
+
+
+def test_hot_pick_empty_batch():
+    got = gpu_pick(np.zeros((0, 4), np.int32), np.zeros((0, 4), np.float32),
+                   np.array([0, 1, -1, 2]), np.array([3.0, 1.0, 0.0, 1.0]), 3)
+    assert got == [-1, 1]
+
+
+def test_hot_pick_ring_excluded_decode():
+    """Decode workload: ring slots (ids >= 166) are never the eviction choice."""
+    lay = fixtures.make_layer("decode")
+    r = moe.route(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, lay.cfg.k)
+    hist = moe.demand(r["topk_expert"], r["topk_score"], lay.cfg.E)
+    n_arena = lay.extra["n_resident"]
+    got = gpu_pick(r["topk_expert"], r["topk_score"], lay.expert_slot, hist, n_arena, 0.0)
+    want = oracle_pick(r["topk_expert"], r["topk_score"], lay.expert_slot, hist, n_arena, 0.0)
+    say(f"decode hot pick (threshold 0): gpu {got}, oracle {want}")
+    if want is None:
+        assert got[0] == -1
+    else:
+        assert got == want
+    assert 0 <= lay.expert_slot[got[1]] < n_arena
+
+
+def test_hot_read_layer_long():
+    """Long prefill chunk: the full hot-read call against the oracle."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    lay = fixtures.make_layer("long")
+    say("long workload: uploading a fresh arena for the hot read")
+    g = GpuLayer(lay)
+    n_arena = lay.extra["n_resident"]
+    es0 = lay.expert_slot.copy()
+    hot = R.HotReader(es0, n_arena, g.x.device)
+    stream = torch.cuda.current_stream()
+    picked = R.layer_step_hot(g.buf, g.x, g.w_router, g.bias, g.expert_slot, g.hist, g.arena,
+                              hot, lay.expert_bytes, stream)
+    torch.cuda.synchronize()
+
+    # decision on the recorded scores and this call's demand, as the oracle defines it
+    r0 = moe.route(g.x_bits, lay.w_router, lay.bias, es0, g.k)
+    got_te = g.buf.topk_expert.cpu().numpy()
+    got_ts = g.buf.topk_score.cpu().numpy()
+    assert np.array_equal(got_te, r0["topk_expert"])
+    hist = g.hist.cpu().numpy()
+    want_hist = moe.demand_fast(r0["topk_expert"], r0["topk_score"], g.E)
+    np.testing.assert_allclose(hist, want_hist, rtol=1e-5, atol=0)
+    want = plan.hot_read(got_ts, got_te, es0, hist, n_arena)
+    assert want is not None, "the long workload has a qualifying miss"
+    e_star, c, es1 = want
+    say(f"hot read: load expert {e_star} into the slot of expert {c} (slot {es0[c]})")
+    assert picked is not None and (picked[0], picked[1]) == (e_star, c)
+    assert np.array_equal(g.expert_slot.cpu().numpy(), es1)
+    assert np.array_equal(hot.es, es1)
+
+    # the slot now holds e*'s packed bytes, verbatim
+    slot = int(es1[e_star])
+    sb = g.arena.slot_bytes
+    got_bytes = g.arena.mem[slot * g.arena.stride: slot * g.arena.stride + sb].cpu().numpy()
+    assert np.array_equal(got_bytes, lay.expert_bytes(e_star)[:sb])
+
+    # re-routing over the new routable set and the experts on sampled tokens
+    r1 = moe.route(g.x_bits, lay.w_router, lay.bias, es1, g.k)
+    _, offsets, perm = moe.bucket(r1["sel_slot"], g.S)
+    got = g.routing()
+    for key in ("topk_expert", "sel_expert", "sel_slot"):
+        assert np.array_equal(got[key], r1[key]), key
+    assert np.array_equal(got["slot_offsets"], offsets)
+    assert np.array_equal(got["perm"], perm)
+    users = np.nonzero((r1["sel_expert"] == e_star).any(axis=1))[0]
+    assert users.size > 0, "some token now routes to the loaded expert"
+    rng = np.random.default_rng(12)
+    tok = np.unique(np.concatenate([users[:8], rng.choice(g.T, 12, replace=False)]))
+    sc = lay.slot_content()
+
+    def slot_bytes(s):
+        return lay.expert_bytes(e_star) if s == slot else lay.content_bytes(sc[s])
+
+    o, _ = moe.experts_forward(g.x_bits, r1["sel_expert"], r1["sel_weight"], r1["sel_slot"],
+                               slot_bytes, g.H, g.I, tokens=tok)
+    err = moe.rel_l2(g.out_f64()[tok], o)
+    say(f"  hot-read layer rel-L2 {err:.3e} over {tok.size} tokens "
+        f"({min(8, users.size)} of them use the loaded expert)")
+    assert err <= OUT_REL_L2
+
+
+def test_hot_read_layer_no_candidate():
+    """Nothing qualifies (threshold above every share): plain layer call, no copy."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    lay = fixtures.make_layer("tiny")
+    g = GpuLayer(lay)
+    hot = R.HotReader(lay.expert_slot, lay.S, g.x.device, threshold=1.5)
+    picked = R.layer_step_hot(g.buf, g.x, g.w_router, g.bias, g.expert_slot, g.hist, g.arena,
+                              hot, lay.expert_bytes)
+    torch.cuda.synchronize()
+    assert picked is None
+    assert np.array_equal(g.expert_slot.cpu().numpy(), lay.expert_slot)
+    r = moe.route(g.x_bits, lay.w_router, lay.bias, lay.expert_slot, g.k)
+    assert np.array_equal(g.buf.sel_slot.cpu().numpy(), r["sel_slot"])
