@@ -421,6 +421,8 @@ def arena40_layer_counts(seed: int = 505, L: int = 40, E: int = 256, total: int 
     g = rng(seed, "layer_split", 0)
     share = g.dirichlet(np.full(L, alpha))
     lo, hi = math.ceil(lo_frac * E), math.floor(hi_frac * E)
+    if not L * lo <= total <= L * hi:
+        raise ValueError(f"{total} residents cannot be split over {L} layers within [{lo}, {hi}]")
     raw = share * total
     cnt = np.clip(np.floor(raw), lo, hi).astype(np.int64)
     rem = raw - np.floor(raw)
@@ -434,3 +436,85 @@ def arena40_layer_counts(seed: int = 505, L: int = 40, E: int = 256, total: int 
             cand = [i for i in by_rem_desc[::-1] if cnt[i] > lo][:-diff]
             cnt[cand] -= 1
     return cnt
+
+
+# ----------------------------------------------------------------------------
+# several layers sharing one arena
+# ----------------------------------------------------------------------------
+@dataclass
+class ArenaModel:
+    """L layers of one model sharing one arena of S slots.
+
+    layers[l] holds layer l's router, bias and contents; its expert_slot holds
+    global slot ids (layer-major: layer 0's residents first).  Tokens of a step
+    are shared by all layers.
+    """
+    cfg: LayerConfig
+    layers: list
+    counts: np.ndarray          # resident experts per layer
+    x_seed: int
+
+    @property
+    def L(self) -> int:
+        return len(self.layers)
+
+    @property
+    def S(self) -> int:
+        return int(self.counts.sum())
+
+    def expert_slot_table(self) -> np.ndarray:
+        return np.stack([lay.expert_slot for lay in self.layers]).astype(np.int32)
+
+    def tokens(self, step: int, T: int | None = None) -> np.ndarray:
+        return draw_tokens(self.x_seed, self.cfg.T if T is None else T, self.cfg.H, step)
+
+    def pair_bytes(self, l: int, e: int) -> np.ndarray:
+        return self.layers[l].expert_bytes(e)
+
+    def slot_pairs(self, table: np.ndarray | None = None) -> np.ndarray:
+        """[S, 2] (layer, expert) held by each slot under a slot table."""
+        table = self.expert_slot_table() if table is None else table
+        out = np.full((self.S, 2), -1, dtype=np.int64)
+        l, e = np.nonzero(table >= 0)
+        out[table[l, e]] = np.stack([l, e], axis=1)
+        return out
+
+    def prepack(self):
+        for lay in self.layers:
+            prepack(lay.model_seed, np.unique(lay.expert_content), self.cfg.H, self.cfg.I,
+                    self.cfg.weight_std)
+
+
+def make_arena_model(cfg: LayerConfig | str = "arena40", distinct_layers: bool = False) -> ArenaModel:
+    """Per-layer routers, Zipf biases, residency draws and contents; one arena.
+
+    distinct_layers: layer l draws its contents from its own range of content
+    ids (no two layers share weights); otherwise the n_contents contents are
+    reused by every layer (addresses stay distinct, so traffic is unchanged).
+    """
+    cfg = CONFIGS[cfg] if isinstance(cfg, str) else cfg
+    L, E, H = cfg.layers, cfg.E, cfg.H
+    counts = arena40_layer_counts(cfg.seed, L, E, cfg.resident)
+    beta = zipf_beta(cfg.beta_key) if cfg.zipf else 0.0
+    layers, nxt = [], 0
+    for l in range(L):
+        w_router = rng(cfg.seed, "router", l).standard_normal((E, H), dtype=np.float32) \
+            * np.float32(cfg.router_std)
+        if cfg.zipf:
+            ranks = popularity_ranks(cfg.seed, E, l)
+            bias = zipf_bias(ranks, beta, cfg.zipf_s)
+        else:
+            ranks, bias = None, np.zeros(E, dtype=np.float32)
+        order = residency_order(cfg.seed, ranks, E, l, cfg.zipf_s)
+        c = int(counts[l])
+        expert_slot = np.full(E, -1, dtype=np.int32)
+        expert_slot[order[:c]] = np.arange(nxt, nxt + c, dtype=np.int32)
+        nxt += c
+        layers.append(Layer(cfg=cfg, x_bits=np.zeros((0, H), np.uint16), w_router=w_router,
+                            bias=bias, expert_slot=expert_slot,
+                            slot_expert=order[:c].astype(np.int32),
+                            expert_content=content_map(cfg.seed, E, cfg.n_contents, l)
+                            + (l * cfg.n_contents if distinct_layers else 0),
+                            ranks=ranks, order=order, model_seed=cfg.seed, beta=float(beta),
+                            extra={"n_resident": c, "n_ring": 0, "layer": l}))
+    return ArenaModel(cfg=cfg, layers=layers, counts=counts, x_seed=cfg.seed + 7)

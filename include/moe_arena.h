@@ -275,6 +275,33 @@ int moe_hot_pick(const int32_t* topk_expert, const float* topk_score, int T, int
                  double threshold, int32_t* out, hipStream_t stream);
 
 /*
+ * moe_replan -- re-plan of one arena shared by all layers (TideLM README, "How
+ * adaptive expert loading works", item 1: the arena is re-planned from the
+ * demand history, so a busy layer takes slots from a quiet one).  Host function:
+ * every pointer is host memory, no HIP call is made.
+ *
+ *   Eviction: resident pairs (l,e) (expert_slot[l*E+e] >= 0) in ascending
+ *   (hist, l, e); a pair is taken unless it would leave layer l with fewer than
+ *   k resident experts; stop after n_swap pairs.
+ *   Loading: non-resident pairs in descending hist, ties ascending (l, e); the
+ *   first n_done of them, n_done = number evicted.
+ *   The i-th loaded pair receives the i-th evicted pair's slot.
+ * Inputs : hist [L][E] double, expert_slot [L][E] int32 (-1 = not resident).
+ * Outputs: evict, load [n_swap][2] int32 (l, e) pairs (entries beyond n_done
+ *          are unspecified); new_expert_slot [L][E] (must not alias the
+ *          inputs); n_done (host int) = min(evictable pairs, non-resident
+ *          pairs, n_swap).
+ * The caller copies each loaded pair's bytes with arena_load_slot into its
+ * slot (after any kernel reading the evicted expert has finished) and installs
+ * new_expert_slot on the device after the copies' events.
+ * Errors: MOE_EINVAL for null pointers, L, E, k <= 0, n_swap < 0, a NaN in
+ * hist, or a slot id used twice; MOE_EUNSUPPORTED if E > MOE_MAX_E or k >
+ * MOE_MAX_K.
+ */
+int moe_replan(const double* hist, const int32_t* expert_slot, int L, int E, int k, int n_swap,
+               int32_t* evict, int32_t* load, int32_t* new_expert_slot, int* n_done);
+
+/*
  * moe_test_mxfp4_probe -- test-only: one wave runs one block-scaled MXFP4
  * matrix instruction (16x16 output, contraction 128) on raw per-lane operands,
  * so a test can check the hardware's decoding of E2M1 codes and E8M0 scales and

@@ -8,12 +8,12 @@ library and fails loudly if it has not been built.
 """
 from . import binding
 from .binding import (MoeError, arena_load_slot, check, moe_demand_accumulate,
-                      moe_experts_forward, moe_hot_pick, moe_mxfp4_row_bytes, moe_route,
+                      moe_experts_forward, moe_hot_pick, moe_mxfp4_row_bytes, moe_replan, moe_route,
                       moe_slot_bytes, moe_slot_sections, moe_status_string,
                       moe_test_mxfp4_probe, moe_workspace_bytes)
 
 binding.load()
 
 __all__ = ["binding", "MoeError", "arena_load_slot", "check", "moe_demand_accumulate",
-           "moe_experts_forward", "moe_hot_pick", "moe_mxfp4_row_bytes", "moe_route", "moe_slot_bytes",
+           "moe_experts_forward", "moe_hot_pick", "moe_mxfp4_row_bytes", "moe_replan", "moe_route", "moe_slot_bytes",
            "moe_slot_sections", "moe_status_string", "moe_test_mxfp4_probe", "moe_workspace_bytes"]

@@ -30,7 +30,7 @@ MOE_MAX_S = 8192
 
 EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
-           "arena_load_slot", "moe_hot_pick", "moe_test_mxfp4_probe")
+           "arena_load_slot", "moe_hot_pick", "moe_replan", "moe_test_mxfp4_probe")
 
 
 class MoeError(RuntimeError):
@@ -102,6 +102,8 @@ def load() -> ctypes.CDLL:
     lib.arena_load_slot.restype = i
     lib.moe_hot_pick.argtypes = [vp, vp, i, i, i, vp, i, i, vp, ctypes.c_double, vp, vp]
     lib.moe_hot_pick.restype = i
+    lib.moe_replan.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, ctypes.POINTER(i)]
+    lib.moe_replan.restype = i
     lib.moe_test_mxfp4_probe.argtypes = [vp, vp, vp, vp, vp, vp]
     lib.moe_test_mxfp4_probe.restype = i
     _lib = lib
@@ -114,6 +116,15 @@ def _ptr(p) -> int | None:
     if isinstance(p, int):
         return p
     return int(p.data_ptr())
+
+
+def _host(a) -> int | None:
+    """Address of a host buffer: None, an int, or a C-contiguous numpy array."""
+    if a is None or isinstance(a, int):
+        return a
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("host arrays must be C-contiguous")
+    return int(a.ctypes.data)
 
 
 def _stream(s) -> int | None:
@@ -140,6 +151,9 @@ def _events(evs):
         raise ValueError(f"stage_events needs {MOE_STAGE_EVENTS} events")
     arr = (ctypes.c_void_p * MOE_STAGE_EVENTS)(*[_event(e) for e in evs])
     return arr, ctypes.addressof(arr)
+
+
+load_lib = load
 
 
 def status_string(status: int) -> str:
@@ -208,6 +222,14 @@ def moe_hot_pick(topk_expert, topk_score, T, k, E, expert_slot, S, n_arena, hist
     return int(load().moe_hot_pick(_ptr(topk_expert), _ptr(topk_score), int(T), int(k), int(E),
                                    _ptr(expert_slot), int(S), int(n_arena), _ptr(hist_row),
                                    float(threshold), _ptr(out), _stream(stream)))
+
+
+def moe_replan(hist, expert_slot, L, E, k, n_swap, evict, load, new_expert_slot, n_done) -> int:
+    """Host function: hist, expert_slot, evict, load, new_expert_slot are host
+    buffers (numpy arrays or addresses); n_done is a ctypes.c_int."""
+    return int(load_lib().moe_replan(_host(hist), _host(expert_slot), int(L), int(E), int(k),
+                                     int(n_swap), _host(evict), _host(load),
+                                     _host(new_expert_slot), ctypes.byref(n_done)))
 
 
 def moe_test_mxfp4_probe(a, a_scale, b, b_scale, d, stream=None) -> int:

@@ -181,3 +181,69 @@ def layer_step(buf: LayerBuffers, x, w_router, bias, expert_slot, hist_row, aren
         route(buf, x, w_router, bias, expert_slot, stream)
         demand(buf, hist_row, stream)
     experts(buf, arena_ptr, slot_stride, stream)
+
+
+class SharedArena:
+    """One arena shared by L layers: the [L][E] slot table and the [L][E]
+    float64 demand history on the device, plus the re-plan flow.
+
+    Layer l routes with expert_slot = table[l] and accumulates demand into
+    hist[l] (both contiguous rows).  replan() reads the history (80 KB at
+    40 x 256), lets moe_replan pick the swaps, copies every loaded expert into
+    its new slot with arena_load_slot on a side stream, and installs the new
+    table on the layer stream after the copies.
+    """
+
+    def __init__(self, S: int, H: int, I: int, table_host: np.ndarray, device):
+        self.arena = Arena(S, H, I, device)
+        self.L, self.E = table_host.shape
+        self.table_host = np.ascontiguousarray(table_host, dtype=np.int32).copy()
+        self.table = torch.from_numpy(self.table_host.copy()).to(device)
+        self.hist = torch.zeros((self.L, self.E), dtype=torch.float64, device=device)
+        self.device = device
+        self.side = torch.cuda.Stream(device)   # default priority
+        self.done = torch.cuda.Event()
+        self._pinned = {}
+
+    def upload(self, pair_bytes_fn) -> None:
+        """Fill every slot with the bytes of the (layer, expert) it holds."""
+        l_idx, e_idx = np.nonzero(self.table_host >= 0)
+        owner = {int(self.table_host[l, e]): (int(l), int(e)) for l, e in zip(l_idx, e_idx)}
+        self.arena.upload(lambda s: pair_bytes_fn(*owner[s]), slots=sorted(owner))
+
+    def _pin(self, host: np.ndarray) -> torch.Tensor:
+        key = id(host)
+        if key not in self._pinned:
+            self._pinned[key] = torch.from_numpy(np.ascontiguousarray(host)).pin_memory()
+        return self._pinned[key]
+
+    def replan(self, k: int, n_swap: int, pair_bytes_fn, stream=None):
+        """Returns (evict [(l,e)], load [(l,e)]) once the copies are enqueued and
+        the new table is ordered after them on `stream`."""
+        import ctypes
+        stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        with torch.cuda.stream(stream):
+            hist = self.hist.cpu().numpy()                    # waits for the layers' demand
+        ev = np.empty((max(n_swap, 1), 2), dtype=np.int32)
+        ld = np.empty((max(n_swap, 1), 2), dtype=np.int32)
+        new = np.empty_like(self.table_host)
+        n_done = ctypes.c_int(0)
+        B.check(B.moe_replan(hist, self.table_host, self.L, self.E, k, n_swap, ev, ld, new,
+                             n_done), "moe_replan")
+        n = n_done.value
+        if n == 0:
+            return [], []
+        self.side.wait_stream(stream)       # nothing still reads an evicted slot
+        a = self.arena
+        for i in range(n):
+            slot = int(self.table_host[ev[i, 0], ev[i, 1]])
+            src = self._pin(pair_bytes_fn(int(ld[i, 0]), int(ld[i, 1])))
+            B.check(B.arena_load_slot(a.mem, a.stride, a.S, slot, src, a.slot_bytes, self.side,
+                                      self.done if i == n - 1 else None), "arena_load_slot")
+        stream.wait_event(self.done)
+        self.table_host = new
+        staged = torch.from_numpy(new.copy()).pin_memory()
+        with torch.cuda.stream(stream):
+            self.table.copy_(staged, non_blocking=True)
+        self._staged = staged                   # kept alive until the copy has run
+        return ([tuple(map(int, p)) for p in ev[:n]], [tuple(map(int, p)) for p in ld[:n]])
