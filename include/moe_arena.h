@@ -303,12 +303,16 @@ int moe_replan(const double* hist, const int32_t* expert_slot, int L, int E, int
 
 /*
  * moe_test_mxfp4_probe -- test-only: one wave runs one block-scaled MXFP4
- * matrix instruction (16x16 output, contraction 128) on raw per-lane operands,
- * so a test can check the hardware's decoding of E2M1 codes and E8M0 scales and
- * its lane layout.  a, b: [64 lanes][16 bytes] codes; a_scale, b_scale: [64]
- * scale bytes; d: [64 lanes][4] float results as the lanes hold them.
+ * matrix instruction on raw per-lane operands, so a test can check the
+ * hardware's decoding of E2M1 codes and E8M0 scales and its lane layout.
+ * shape 0: 16x16 output, contraction 128 (lane l: row or column l%16,
+ * elements 32(l/16) .. +31), d[l][0..3] used; shape 1: 32x32 output,
+ * contraction 64 (lane l: row or column l%32, elements 32(l/32) .. +31),
+ * d[l][0..15] used.  a, b: [64 lanes][16 bytes] codes; a_scale, b_scale:
+ * [64] scale bytes; d: [64 lanes][16] floats as the lanes hold them.
+ * MOE_EINVAL for another shape, a null pointer or misalignment.
  */
-int moe_test_mxfp4_probe(const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
+int moe_test_mxfp4_probe(int shape, const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
                          const uint8_t* b_scale, float* d, hipStream_t stream);
 
 #ifdef __cplusplus

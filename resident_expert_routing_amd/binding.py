@@ -104,7 +104,7 @@ def load() -> ctypes.CDLL:
     lib.moe_hot_pick.restype = i
     lib.moe_replan.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, ctypes.POINTER(i)]
     lib.moe_replan.restype = i
-    lib.moe_test_mxfp4_probe.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.moe_test_mxfp4_probe.argtypes = [i, vp, vp, vp, vp, vp, vp]
     lib.moe_test_mxfp4_probe.restype = i
     _lib = lib
     return lib
@@ -232,9 +232,9 @@ def moe_replan(hist, expert_slot, L, E, k, n_swap, evict, load, new_expert_slot,
                                      _host(new_expert_slot), ctypes.byref(n_done)))
 
 
-def moe_test_mxfp4_probe(a, a_scale, b, b_scale, d, stream=None) -> int:
-    return int(load().moe_test_mxfp4_probe(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale),
-                                           _ptr(d), _stream(stream)))
+def moe_test_mxfp4_probe(shape, a, a_scale, b, b_scale, d, stream=None) -> int:
+    return int(load().moe_test_mxfp4_probe(int(shape), _ptr(a), _ptr(a_scale), _ptr(b),
+                                           _ptr(b_scale), _ptr(d), _stream(stream)))
 
 
 def check(status: int, what: str = "moe") -> None:

@@ -7,21 +7,42 @@
 // one fixed order (the fixed-summation-order paragraph) -- here ascending
 // expert id, which is the order of a token's picks.
 //
-// Contraction layout shared by every GEMM here (so any token's result is the
-// same whatever batch it runs in): K is walked in 512-wide super-chunks
-// (16 MX blocks) in ascending order; MFMA step i (0..3) of a super-chunk covers
-// blocks 4i..4i+3, lane group g (lanes 16g..16g+15) supplying block 4i+g.  One
-// load instruction thus reads 64 contiguous bytes of each of 16 rows.  A lane
-// reads the super-chunk's 16 scale bytes as one 16-byte word and shifts its
-// own byte (4i+g) into place for step i.
+// Two kernel families, each with one fixed contraction order (so a token's
+// result does not depend on the other tokens of its batch within a family):
+//
+// * Small batches (decode): the weights stream from HBM straight into
+//   registers with v_mfma_scale_f32_16x16x128_f8f6f4.  K is walked in
+//   512-wide super-chunks (16 MX blocks) in ascending order; MFMA step i
+//   (0..3) covers blocks 4i..4i+3, lane group g (lanes 16g..16g+15)
+//   supplying block 4i+g, so one load instruction reads 64 contiguous bytes
+//   of each of 16 rows.  A lane reads the super-chunk's 16 scale bytes as one
+//   16-byte word and shifts its own byte (4i+g) into place for step i.
+//
+// * Larger batches: operands are staged in LDS and the MFMA is
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (on gfx950 the 16x16x128 form runs at
+//   half the E2M1 rate).  Lane l supplies row (or column) l%32 and one MX
+//   block of 32 elements with its E8M0 scale; the 32x32 fp32 result sits in
+//   lane l, register v at row 8(v/4) + 4(l/32) + v%4, column l%32.  K is
+//   walked in chunks of 256 (8 MX blocks) in ascending order; step s (0..3)
+//   of chunk c takes blocks 8c + 4(s/2) + (s%2) (lanes 0-31) and
+//   8c + 4(s/2) + 2 + (s%2) (lanes 32-63).
+//
+// The families agree to float32 rounding of their sums, not bit for bit.
 #include "common.hpp"
 
 namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-constexpr int kInlineWorklistMaxS = 1024;
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int kInlineWorklistMaxS = 1024;
 
+// silu(g) * u, the SwiGLU product of one element.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// ===========================================================================
+// 16x16x128 helpers (small-batch kernels)
+// ===========================================================================
 __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, uint32_t sa,
                                         uint32_t sb) {
   const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
@@ -85,6 +106,114 @@ __device__ __forceinline__ void load_row_sc(const uint8_t* codes, const uint8_t*
       }
     }
   }
+}
+
+// SwiGLU of one column of a wave's 32 rows of I and its MXFP4 encoding
+// (16x16x128 result layout).  Lane (c = lane&15, g) holds rows n0+4g+v (tile
+// 0) and n0+16+4g+v (tile 1) of gate (ag*) and up (au*) for column c; the 32
+// rows are one MX block of h.  hr: the column's hq row, or null when the
+// column is absent (every lane still takes part in the shuffles).
+__device__ __forceinline__ void swiglu_quant_store16(const v4f& ag0, const v4f& ag1,
+                                                     const v4f& au0, const v4f& au1, int g,
+                                                     uint8_t* hr, int n0, int I) {
+  float h[8];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    h[v] = silu_mul(ag0[v], au0[v]);
+    h[4 + v] = silu_mul(ag1[v], au1[v]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  uint32_t codes[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t scale = 0u;
+  if (amax > 0.f) {
+    const int e = mx_block_exp(amax);
+    scale = (uint32_t)(e + 127);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) codes[i] = e2m1_code(h[i], e);
+  }
+  if (hr) {
+    const uint16_t w0 =
+        (uint16_t)(codes[0] | (codes[1] << 4) | (codes[2] << 8) | (codes[3] << 12));
+    const uint16_t w1 =
+        (uint16_t)(codes[4] | (codes[5] << 4) | (codes[6] << 8) | (codes[7] << 12));
+    *reinterpret_cast<uint16_t*>(hr + n0 / 2 + 2 * g) = w0;
+    *reinterpret_cast<uint16_t*>(hr + n0 / 2 + 8 + 2 * g) = w1;
+    if (g == 0) hr[I / 2 + n0 / 32] = (uint8_t)scale;
+  }
+}
+
+// ===========================================================================
+// 32x32x64 helpers (pipelined kernels)
+// ===========================================================================
+__device__ __forceinline__ v16f mfma32(const uint4& a, const uint4& b, v16f c, uint32_t sa,
+                                       uint32_t sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  // cbsz = blgp = 4: both operands E2M1; the scale is byte 0 of each scale word.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0,
+                                                         (int)sb);
+}
+
+__device__ __forceinline__ v16f zero16() {
+  v16f z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Scale of step s for lane half hh, in byte 0, from the scale bytes 8c..8c+7
+// of chunk c held as two words.
+__device__ __forceinline__ uint32_t step_scale(uint32_t w0, uint32_t w1, int s, int hh) {
+  return ((s >> 1) ? w1 : w0) >> (16 * hh + 8 * (s & 1));
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU of one column of a wave's 32 rows of I and its MXFP4 encoding
+// (32x32x64 result layout).  Lane (column l%32, half hh = l/32) holds gate (G) and up (U) rows
+// n0 + 8(v/4) + 4hh + v%4; the 32 rows are one MX block of h.  hr: the
+// column's hq row, or null when the column is absent (every lane still takes
+// part in the shuffle).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void swiglu_quant_store32(const v16f& G, const v16f& U, int hh,
+                                                   uint8_t* hr, int n0, int I) {
+  float h[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) h[v] = silu_mul(G[v], U[v]);
+  float amax = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(h[v]));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  uint32_t code[16];
+  uint32_t scale = 0u;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) code[v] = 0u;
+  if (amax > 0.f) {
+    const int e = mx_block_exp(amax);
+    scale = (uint32_t)(e + 127);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) code[v] = e2m1_code(h[v], e);
+  }
+  if (hr) {
+    // rows 8q+4hh .. 8q+4hh+3 are bytes 4q+2hh, 4q+2hh+1 of the block's codes
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint16_t*>(hr + n0 / 2 + 4 * q + 2 * hh) =
+          (uint16_t)(code[4 * q] | (code[4 * q + 1] << 4) | (code[4 * q + 2] << 8) |
+                     (code[4 * q + 3] << 12));
+    if (hh == 0) hr[I / 2 + n0 / 32] = (uint8_t)scale;
+  }
+}
+
+// y rows n0 + 8q + 4hh .. +3 of one column (an fp32 row of H).
+__device__ __forceinline__ void store_y(float* yr, int n0, int hh, const v16f& acc) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *reinterpret_cast<float4*>(yr + n0 + 8 * q + 4 * hh) =
+        make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
 }
 
 // The u-th slot (ascending) that holds assignments, found by the whole
@@ -169,7 +298,9 @@ __global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ o
   }
 }
 
-// ---------------------------------------------------------------------------
+// ===========================================================================
+// Small-batch kernels
+// ===========================================================================
 // Gate/up + SwiGLU + MXFP4(h).  Workgroup = 4 waves = 128 rows of I of one
 // slot; wave = 32 rows (two 16-row tiles of gate and of up).  Columns are the
 // slot's assignment rows p, 16 per MFMA tile.  Output: hq row p (an MXFP4 row
@@ -239,37 +370,9 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
       au0 = mfma_superchunk(wu0, x, au0);
       au1 = mfma_superchunk(wu1, x, au1);
     }
-    // Epilogue.  Lane (c = lane&15, g) holds rows n0+4g+v (tile 0) and
-    // n0+16+4g+v (tile 1) of column c.
-    const int c = lane & 15;
-    const int pcol = cb + c;
-    float h[8];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      h[v] = ag0[v] / (1.0f + expf(-ag0[v])) * au0[v];
-      h[4 + v] = ag1[v] / (1.0f + expf(-ag1[v])) * au1[v];
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-    uint32_t codes[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t scale = 0u;
-    if (amax > 0.f) {
-      const int e = mx_block_exp(amax);
-      scale = (uint32_t)(e + 127);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) codes[i] = e2m1_code(h[i], e);
-    }
-    if (pcol < p1) {
-      uint8_t* hr = p.hq + (size_t)pcol * p.hrow;
-      const uint16_t w0 = (uint16_t)(codes[0] | (codes[1] << 4) | (codes[2] << 8) | (codes[3] << 12));
-      const uint16_t w1 = (uint16_t)(codes[4] | (codes[5] << 4) | (codes[6] << 8) | (codes[7] << 12));
-      *reinterpret_cast<uint16_t*>(hr + n0 / 2 + 2 * g) = w0;
-      *reinterpret_cast<uint16_t*>(hr + n0 / 2 + 8 + 2 * g) = w1;
-      if (g == 0) hr[p.I / 2 + n0 / 32] = (uint8_t)scale;
-    }
+    const int pcol = cb + (lane & 15);
+    swiglu_quant_store16(ag0, ag1, au0, au1, g,
+                         pcol < p1 ? p.hq + (size_t)pcol * p.hrow : nullptr, n0, p.I);
   }
 }
 
@@ -383,19 +486,401 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(out + (size_t)t * H + h) = make_uint2(lo, hi);
 }
 
+// ===========================================================================
+// Pipelined path for larger batches (rows of 256-multiple length).  A work
+// item is one M-tile of up to kTileM consecutive assignment rows of one slot;
+// the grid is work items x N-tiles.  Every operand reaches LDS through direct
+// global-to-LDS loads (lane i of a load lands at the LDS base + size * i),
+// issued two K chunks ahead of use into a ring of three stages.  A stage
+// holds one chunk (K = 256: 128 code bytes and 8 scale bytes per row) of the
+// four waves' 64 weight rows each and of the tile's 128 activation rows.
+// Bytes in flight cost no registers, so the one wave per SIMD that the
+// accumulators allow still keeps ~100 KB of loads in flight per CU.
+// The 16-byte block b of a 128-byte stage row r sits at position
+// b ^ ((r >> 1) & 7): the 16 rows a fragment read touches hit 16 distinct
+// 4-bank groups.
+// ===========================================================================
+constexpr int kTileM = 128;                    // assignment rows per work item
+constexpr int kStageA = 4 * 64 * 128;          // weight code rows of the four waves
+constexpr int kStageB = kTileM * 128;          // activation code rows
+constexpr int kStageSA = 4 * 64 * 8;           // weight scale bytes
+constexpr int kStageSB = kTileM * 8;           // activation scale bytes
+constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;  // 52,224 bytes
+constexpr int kRing = 3;
+constexpr int kPipeLds = kRing * kStage;       // 156,672 bytes
+constexpr int kZeroPage = 256;                 // zeroed workspace bytes absent rows load from
+// Loads issued by each wave per stage: 8 weight-code, 4 activation-code,
+// 2 weight-scale and 1 activation-scale loads.
+constexpr int kLoadsPerStage = 15;
+
+// Work list of M-tiles: items[0] = count, then per item (slot, first row of
+// the tile within the slot, index of the slot's first item, the slot's item
+// count), slots ascending.  Also clears the zero page.
+__global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int S,
+                                                    int A, int32_t* __restrict__ items,
+                                                    uint32_t* __restrict__ zero_page) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < kZeroPage / 4) zero_page[tid] = 0u;
+  const int per = (S + 1023) / 1024;
+  const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int local = 0;
+  for (int s = lo; s < hi; ++s) {
+    const int a = offsets[s], b = offsets[s + 1];
+    if (b > a && a >= 0 && b <= A) local += (b - a + kTileM - 1) / kTileM;
+  }
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < wv; ++i) run += wsum[i];
+  for (int s = lo; s < hi; ++s) {
+    const int a = offsets[s], b = offsets[s + 1];
+    if (b > a && a >= 0 && b <= A) {
+      const int first = run, cnt = (b - a + kTileM - 1) / kTileM;
+      for (int m = 0; m < cnt; ++m) {
+        int32_t* it = items + 1 + 4 * run;
+        it[0] = s;
+        it[1] = m * kTileM;
+        it[2] = first;
+        it[3] = cnt;
+        ++run;
+      }
+    }
+  }
+  if (tid == 0) {
+    int total = 0;
+    for (int i = 0; i < 16; ++i) total += wsum[i];
+    items[0] = total;
+  }
+}
+
+// Work index of this workgroup.  Workgroups are dispatched round-robin over
+// the 8 XCDs; this mapping gives each XCD a contiguous range of work indices.
+// gridDim.x is a multiple of 8.
+__device__ __forceinline__ int xcd_work_index() {
+  return (int)((blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3));
+}
+
+// The (M-tile, N-tile) of work index w.  A slot's items x nN tiles are
+// consecutive work indices, ordered in groups of up to 8 M-tiles: within a
+// group the M-tile runs fastest, so the workgroups in flight on one XCD share
+// a few weight N-tiles and a few activation M-tiles in its L2.  Returns false
+// past the end of the list.
+struct TileRef {
+  int slot, p0, rows, nt;
+};
+
+__device__ __forceinline__ bool tile_of(int w, int nN, const int32_t* __restrict__ items,
+                                        const int32_t* __restrict__ offsets, TileRef& t) {
+  const int item = w / nN;
+  if (item >= items[0]) return false;
+  const int32_t* it = items + 1 + 4 * item;
+  const int first = it[2], cnt = it[3];
+  const int local = w - first * nN;
+  const int mg = local / (8 * nN);
+  const int gm = min(8, cnt - 8 * mg);
+  const int lg = local - mg * 8 * nN;
+  const int m = 8 * mg + lg % gm;
+  t.slot = it[0];
+  t.nt = lg / gm;
+  t.p0 = offsets[t.slot] + m * kTileM;
+  t.rows = min(kTileM, offsets[t.slot + 1] - t.p0);
+  return true;
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct loads to LDS at lds_base + size * lane (lds_base is wave-uniform and
+// goes to M0).  Inline assembly, so that the compiler does not add a wait for
+// every outstanding load before each LDS read: the pipeline waits for them
+// explicitly (pipe_wait).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is written here on purpose
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(g)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(m0), "v"(g)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Per-lane sources of the direct loads; stage q reads code bytes
+// [128 q, 128 q + 128) and scale bytes [8 q, 8 q + 8) of every row.
+struct PipeSrc {
+  const uint8_t* a[8];   // weight codes, load j: wave row 8j + lane/8, block already swizzled
+  const uint8_t* as[2];  // weight scales, load j: wave row 32j + lane/2, dword lane%2
+  const uint8_t* b[4];   // activation codes, load j: tile row (4 wave + j) * 8 + lane/8
+  int bstep[4];          // code bytes per stage (128; 0 for an absent row on the zero page)
+  const uint8_t* bs;     // activation scales: tile row 32 wave + lane/2, dword lane%2
+  int bsstep;            // scale bytes per stage (8; 0 for an absent row)
+};
+
+__device__ __forceinline__ void pipe_issue(uint8_t* smem, const PipeSrc& src, int q, int wave) {
+  uint8_t* st = smem + (q % kRing) * kStage;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma16(src.a[j] + (size_t)q * 128, st + wave * 8192 + j * 1024);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + (4 * wave + j) * 1024);
+  uint8_t* ss = st + kStageA + kStageB;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma4(src.as[j] + (size_t)q * 8, ss + wave * 512 + j * 256);
+  dma4(src.bs + (size_t)q * src.bsstep, ss + kStageSA + wave * 256);
+}
+
+// Waits until this wave's loads of stage q have landed (those of stage q+1
+// may still be in flight), then a workgroup barrier makes every wave's share
+// visible and frees the stage read in the previous iteration for reuse.
+__device__ __forceinline__ void pipe_wait(int q, int Q) {
+  static_assert(kLoadsPerStage == 15, "wait count below");
+  if (q + 1 < Q)
+    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// The four MFMA steps of stage q: 2 weight tiles x 4 column tiles of 32.
+// Every fragment of the stage is read before the first MFMA (the sched
+// barrier keeps the compiler from sinking each read next to its use).
+__device__ __forceinline__ void pipe_compute(const uint8_t* smem, int q, int wave, int r, int hh,
+                                             v16f (&acc)[2][4]) {
+  const uint8_t* st = smem + (q % kRing) * kStage;
+  const uint8_t* ss = st + kStageA + kStageB;
+  const int swz = (r >> 1) & 7;
+  uint2 aw[2], bw[4];
+  uint4 a[4][2], b[4][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    aw[t] = *reinterpret_cast<const uint2*>(ss + wave * 512 + (32 * t + r) * 8);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    bw[cb] = *reinterpret_cast<const uint2*>(ss + kStageSA + (32 * cb + r) * 8);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int pb = ((4 * (s >> 1) + 2 * hh + (s & 1)) ^ swz) * 16;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      a[s][t] = *reinterpret_cast<const uint4*>(st + wave * 8192 + (32 * t + r) * 128 + pb);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      b[s][cb] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * cb + r) * 128 + pb);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const uint32_t bsc = step_scale(bw[cb].x, bw[cb].y, s, hh);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[t][cb] =
+            mfma32(a[s][t], b[s][cb], acc[t][cb], step_scale(aw[t].x, aw[t].y, s, hh), bsc);
+    }
+  }
+}
+
+// The whole K loop over Q = K / 256 stages.
+__device__ __forceinline__ void pipe_mainloop(uint8_t* smem, const PipeSrc& src, int Q, int wave,
+                                              int lane, v16f (&acc)[2][4]) {
+  const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[t][cb] = zero16();
+  pipe_issue(smem, src, 0, wave);
+  if (Q > 1) pipe_issue(smem, src, 1, wave);
+  for (int q = 0; q < Q; ++q) {
+    pipe_wait(q, Q);
+    if (q + 2 < Q) pipe_issue(smem, src, q + 2, wave);
+    pipe_compute(smem, q, wave, r, hh, acc);
+  }
+}
+
+// Weight-side sources: wave row wr (0..63) of the stage is row wrow[wr / 32] +
+// wr % 32 of the section at wcodes[wr / 32] / wscales[wr / 32].
+__device__ __forceinline__ void pipe_weight_src(PipeSrc& src, const uint8_t* const (&wcodes)[2],
+                                                const uint8_t* const (&wscales)[2],
+                                                const int (&wrow)[2], size_t crow, size_t srow,
+                                                int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int wr = 8 * j + (lane >> 3), t = wr >> 5, rr = wr & 31;
+    const int b = (lane & 7) ^ ((wr >> 1) & 7);
+    src.a[j] = wcodes[t] + (size_t)(wrow[t] + rr) * crow + b * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    src.as[j] = wscales[j] + (size_t)(wrow[j] + (lane >> 1)) * srow + 4 * (lane & 1);
+}
+
+// Activation-side sources: tile row `row` reads from rowptr(row) (codes at +0,
+// scales at +scale_off) or, when absent, from the zero page.
+template <typename RowPtr>
+__device__ __forceinline__ void pipe_act_src(PipeSrc& src, RowPtr rowptr, size_t scale_off,
+                                             const uint8_t* zero, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (4 * wave + j) * 8 + (lane >> 3);
+    const int b = (lane & 7) ^ ((row >> 1) & 7);
+    const uint8_t* rp = rowptr(row);
+    src.b[j] = (rp ? rp : zero) + b * 16;
+    src.bstep[j] = rp ? 128 : 0;
+  }
+  const int row = 32 * wave + (lane >> 1);
+  const uint8_t* rp = rowptr(row);
+  src.bs = (rp ? rp + scale_off : zero) + 4 * (lane & 1);
+  src.bsstep = rp ? 8 : 0;
+}
+
+struct PipeArgs {
+  const uint8_t* act;  // gate/up: xq rows by token; down: hq rows by position p
+  size_t arow;
+  const uint8_t* arena;
+  size_t stride;
+  size_t off_c0, off_s0, off_c1, off_s1;  // gate/up: gate, up sections; down: down (c0, s0)
+  const int32_t* offsets;
+  const int32_t* perm;
+  const int32_t* items;
+  const uint8_t* zero;
+  uint8_t* hq;  // gate/up output
+  size_t hrow;
+  float* y;     // down output
+  int H, I, k, A, nN;
+};
+
+// Gate/up: N-tile = 128 rows of I; wave w: rows n0 = 32w.. of gate (tile 0)
+// and of up (tile 1); K = H.
+__global__ __launch_bounds__(256) void gateup_pipe(PipeArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
+  TileRef tr;
+  if (!tile_of(xcd_work_index(), p.nN, p.items, p.offsets, tr)) return;  // no barrier yet
+  const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int H = p.H;
+  const int n0 = tr.nt * 128 + wave * 32;
+  const bool active = n0 < p.I;
+  const int nb = active ? n0 : 0;  // an idle wave still loads (row 0) and meets every barrier
+  const uint8_t* base = p.arena + (size_t)s * p.stride;
+  const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c1};
+  const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s1};
+  const int wrow[2] = {nb, nb};
+  PipeSrc src;
+  pipe_weight_src(src, wc, wsc, wrow, (size_t)H / 2, (size_t)H / 32, lane);
+  pipe_act_src(
+      src,
+      [&](int row) -> const uint8_t* {
+        if (row >= rows) return nullptr;
+        const int a = p.perm[p0 + row];
+        return (a >= 0 && a < p.A) ? p.act + (size_t)(a / p.k) * p.arow : nullptr;
+      },
+      (size_t)H / 2, p.zero, wave, lane);
+  v16f acc[2][4];
+  pipe_mainloop(smem, src, H / 256, wave, lane, acc);
+  if (!active) return;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    if (32 * cb < rows) {
+      const int lr = 32 * cb + r;
+      swiglu_quant_store32(acc[0][cb], acc[1][cb], hh,
+                         lr < rows ? p.hq + (size_t)(p0 + lr) * p.hrow : nullptr, n0, p.I);
+    }
+  }
+}
+
+// Down: N-tile = 256 rows of H; wave w: rows n0 = 64w.. (two 32-row tiles);
+// K = I; the B rows are the slot's hq rows p0.. (contiguous).
+__global__ __launch_bounds__(256) void down_pipe(PipeArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
+  TileRef tr;
+  if (!tile_of(xcd_work_index(), p.nN, p.items, p.offsets, tr)) return;
+  const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int I = p.I;
+  const int n0 = tr.nt * 256 + wave * 64;
+  const uint8_t* base = p.arena + (size_t)s * p.stride;
+  const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c0};
+  const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s0};
+  bool tv[2];
+  int wrow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    tv[t] = n0 + 32 * t < p.H;  // tiles past H load row 0 and are never stored
+    wrow[t] = tv[t] ? n0 + 32 * t : 0;
+  }
+  PipeSrc src;
+  pipe_weight_src(src, wc, wsc, wrow, (size_t)I / 2, (size_t)I / 32, lane);
+  pipe_act_src(
+      src,
+      [&](int row) -> const uint8_t* {
+        return row < rows ? p.act + (size_t)(p0 + row) * p.arow : nullptr;
+      },
+      (size_t)I / 2, p.zero, wave, lane);
+  v16f acc[2][4];
+  pipe_mainloop(smem, src, I / 256, wave, lane, acc);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int lr = 32 * cb + r;
+    if (lr < rows) {
+      const int a = p.perm[p0 + lr];
+      if (a >= 0 && a < p.A) {
+        float* yr = p.y + (size_t)a * p.H;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (tv[t]) store_y(yr, n0 + 32 * t, hh, acc[t][cb]);
+      }
+    }
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
 
 struct ExpertsWs {
-  size_t used_off, hq_off, y_off, total;
+  size_t used_off, items_off, zero_off, hq_off, y_off, total;
 };
+
+// Batches of at least this many tokens, with H and I multiples of 256, take
+// the pipelined path; every other batch the small-batch kernels.
+constexpr int kPipeMinT = 32;
+
+static bool use_pipe(int T, int H, int I) {
+  return T >= kPipeMinT && H % 256 == 0 && I % 256 == 0;
+}
+
+// Upper bound on the M-tiles of a batch: one partial tile per used slot plus
+// the full ones.
+static size_t max_tiles(size_t A, int S) {
+  return (A < (size_t)S ? A : (size_t)S) + (A + kTileM - 1) / kTileM;
+}
 
 static ExpertsWs experts_ws(int T, int H, int k, int I, int S) {
   ExpertsWs w;
   const size_t A = (size_t)T * k;
+  const bool pipe = use_pipe(T, H, I);
   w.used_off = 0;
-  w.hq_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
+  w.items_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
+  const size_t items = pipe ? (1 + 4 * max_tiles(A, S)) * sizeof(int32_t) : 0;
+  w.zero_off = up_to(w.items_off + items, 256);
+  w.hq_off = w.zero_off + (pipe ? kZeroPage : 0);
   w.y_off = up_to(w.hq_off + A * mxfp4_row_bytes(I), 256);
   w.total = up_to(w.y_off + A * (size_t)H * sizeof(float), 256);
   return w;
@@ -422,6 +907,12 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   const ExpertsWs W = experts_ws(T, H, k, I, S);
   if (a->ws_bytes < W.total) return MOE_EWORKSPACE;
   if (!a->ws || !aligned(a->ws, 256)) return MOE_EINVAL;
+  const int A = T * k;
+  const bool pipe = use_pipe(T, H, I);
+  const size_t ntile = max_tiles((size_t)A, S);
+  const size_t g1 = up_to(ntile * (size_t)((I + 127) / 128), 8);
+  const size_t g2 = up_to(ntile * (size_t)((H + 255) / 256), 8);
+  if (pipe && (g1 > 0x7FFFFFFFu || g2 > 0x7FFFFFFFu)) return MOE_EUNSUPPORTED;
   if (S == 0) {
     // nothing routable: every pick is padding, the output is zero
     dim3 grid(T, (H + 1023) / 1024);
@@ -430,72 +921,106 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     return hip_status();
   }
   uint8_t* ws = static_cast<uint8_t*>(a->ws);
-  int32_t* used = reinterpret_cast<int32_t*>(ws + W.used_off);
   uint8_t* hq = ws + W.hq_off;
   float* y = reinterpret_cast<float*>(ws + W.y_off);
-  const int A = T * k;
-  const int maxU = S < A ? S : A;
   hipEvent_t* ev = a->stage_events;
 
-  // Work list of used slots: built once for large slot counts, else each
-  // workgroup finds its slot in place (saves a launch on decode batches).
-  const bool prebuilt = S > kInlineWorklistMaxS;
-  if (!record_stage(ev,0, stream)) return MOE_EHIP;
-  if (prebuilt) build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
-  if (!record_stage(ev,1, stream)) return MOE_EHIP;
-
-  GateUpArgs g;
-  g.xq = a->xq;
-  g.xrow = mxfp4_row_bytes(H);
-  g.arena = a->arena;
-  g.stride = a->slot_stride;
-  g.off_gc = L.off[0];
-  g.off_gs = L.off[1];
-  g.off_uc = L.off[2];
-  g.off_us = L.off[3];
-  g.offsets = a->slot_offsets;
-  g.perm = a->perm;
-  g.used = prebuilt ? used : nullptr;
-  g.hq = hq;
-  g.hrow = mxfp4_row_bytes(I);
-  g.T = T;
-  g.H = H;
-  g.I = I;
-  g.k = k;
-  g.A = A;
-  g.S = S;
-  const int gblocks = maxU * ((I + 127) / 128);
-  if (H % 512 == 0)
-    gateup_kernel<true><<<gblocks, 256, 0, stream>>>(g);
-  else
-    gateup_kernel<false><<<gblocks, 256, 0, stream>>>(g);
-
-  if (!record_stage(ev,2, stream)) return MOE_EHIP;
-
-  DownArgs d;
-  d.hq = hq;
-  d.hrow = g.hrow;
-  d.arena = a->arena;
-  d.stride = a->slot_stride;
-  d.off_dc = L.off[4];
-  d.off_ds = L.off[5];
-  d.offsets = a->slot_offsets;
-  d.perm = a->perm;
-  d.used = prebuilt ? used : nullptr;
-  d.y = y;
-  d.H = H;
-  d.I = I;
-  d.A = A;
-  d.S = S;
-  const int dblocks = maxU * ((H + 255) / 256);
-  if (I % 512 == 0)
-    down_kernel<true><<<dblocks, 256, 0, stream>>>(d);
-  else
-    down_kernel<false><<<dblocks, 256, 0, stream>>>(d);
-  if (!record_stage(ev,3, stream)) return MOE_EHIP;
-
+  if (pipe) {
+    int32_t* items = reinterpret_cast<int32_t*>(ws + W.items_off);
+    uint8_t* zero = ws + W.zero_off;
+    if (!record_stage(ev, 0, stream)) return MOE_EHIP;
+    build_tiles<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, items,
+                                        reinterpret_cast<uint32_t*>(zero));
+    if (!record_stage(ev, 1, stream)) return MOE_EHIP;
+    PipeArgs t;
+    t.act = a->xq;
+    t.arow = mxfp4_row_bytes(H);
+    t.arena = a->arena;
+    t.stride = a->slot_stride;
+    t.off_c0 = L.off[0];
+    t.off_s0 = L.off[1];
+    t.off_c1 = L.off[2];
+    t.off_s1 = L.off[3];
+    t.offsets = a->slot_offsets;
+    t.perm = a->perm;
+    t.items = items;
+    t.zero = zero;
+    t.hq = hq;
+    t.hrow = mxfp4_row_bytes(I);
+    t.y = y;
+    t.H = H;
+    t.I = I;
+    t.k = k;
+    t.A = A;
+    t.nN = (I + 127) / 128;
+    gateup_pipe<<<(unsigned)g1, 256, 0, stream>>>(t);
+    if (!record_stage(ev, 2, stream)) return MOE_EHIP;
+    t.act = hq;
+    t.arow = t.hrow;
+    t.off_c0 = L.off[4];
+    t.off_s0 = L.off[5];
+    t.nN = (H + 255) / 256;
+    down_pipe<<<(unsigned)g2, 256, 0, stream>>>(t);
+    if (!record_stage(ev, 3, stream)) return MOE_EHIP;
+  } else {
+    int32_t* used = reinterpret_cast<int32_t*>(ws + W.used_off);
+    const int maxU = S < A ? S : A;
+    // Work list of used slots: built once for large slot counts, else each
+    // workgroup finds its slot in place (saves a launch on decode batches).
+    const bool prebuilt = S > kInlineWorklistMaxS;
+    if (!record_stage(ev, 0, stream)) return MOE_EHIP;
+    if (prebuilt) build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
+    if (!record_stage(ev, 1, stream)) return MOE_EHIP;
+    GateUpArgs g;
+    g.xq = a->xq;
+    g.xrow = mxfp4_row_bytes(H);
+    g.arena = a->arena;
+    g.stride = a->slot_stride;
+    g.off_gc = L.off[0];
+    g.off_gs = L.off[1];
+    g.off_uc = L.off[2];
+    g.off_us = L.off[3];
+    g.offsets = a->slot_offsets;
+    g.perm = a->perm;
+    g.used = prebuilt ? used : nullptr;
+    g.hq = hq;
+    g.hrow = mxfp4_row_bytes(I);
+    g.T = T;
+    g.H = H;
+    g.I = I;
+    g.k = k;
+    g.A = A;
+    g.S = S;
+    const int gblocks = maxU * ((I + 127) / 128);
+    if (H % 512 == 0)
+      gateup_kernel<true><<<gblocks, 256, 0, stream>>>(g);
+    else
+      gateup_kernel<false><<<gblocks, 256, 0, stream>>>(g);
+    if (!record_stage(ev, 2, stream)) return MOE_EHIP;
+    DownArgs d;
+    d.hq = hq;
+    d.hrow = g.hrow;
+    d.arena = a->arena;
+    d.stride = a->slot_stride;
+    d.off_dc = L.off[4];
+    d.off_ds = L.off[5];
+    d.offsets = a->slot_offsets;
+    d.perm = a->perm;
+    d.used = prebuilt ? used : nullptr;
+    d.y = y;
+    d.H = H;
+    d.I = I;
+    d.A = A;
+    d.S = S;
+    const int dblocks = maxU * ((H + 255) / 256);
+    if (I % 512 == 0)
+      down_kernel<true><<<dblocks, 256, 0, stream>>>(d);
+    else
+      down_kernel<false><<<dblocks, 256, 0, stream>>>(d);
+    if (!record_stage(ev, 3, stream)) return MOE_EHIP;
+  }
   dim3 cgrid(T, (H + 1023) / 1024);
   combine_kernel<<<cgrid, 256, 0, stream>>>(y, a->sel_weight, a->sel_slot, T, H, k, S, a->out);
-  if (!record_stage(ev,4, stream)) return MOE_EHIP;
+  if (!record_stage(ev, 4, stream)) return MOE_EHIP;
   return hip_status();
 }

@@ -168,8 +168,9 @@ def test_arena_load_rejects():
 
 
 def test_probe_rejects():
-    assert B.moe_test_mxfp4_probe(None, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
-    assert B.moe_test_mxfp4_probe(FAKE + 4, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+    assert B.moe_test_mxfp4_probe(0, None, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+    assert B.moe_test_mxfp4_probe(1, FAKE + 4, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+    assert B.moe_test_mxfp4_probe(2, FAKE, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

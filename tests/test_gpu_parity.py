@@ -65,10 +65,15 @@ def check_route(g, r):
 
 
 # --------------------------------------------------------------------------
-# hardware probe: every E2M1 code at every scale whose result is a normal fp32
+# hardware probe: every E2M1 code at every scale whose result is a normal fp32,
+# for both block-scaled instructions the expert kernels use
 # --------------------------------------------------------------------------
-def _probe(a_codes, a_scale, b_codes, b_scale):
-    """Codes [64 lanes][32] (values 0..15), scales [64] -> lane outputs [64][4]."""
+# shape -> (output side n, lanes per K block): 0 = 16x16x128, 1 = 32x32x64
+SHAPES = {0: 16, 1: 32}
+
+
+def _probe(shape, a_codes, a_scale, b_codes, b_scale):
+    """Codes [64 lanes][32] (values 0..15), scales [64] -> lane outputs [64][16]."""
     import torch
     import resident_expert_routing_amd as m
     pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
@@ -76,63 +81,90 @@ def _probe(a_codes, a_scale, b_codes, b_scale):
     Bq = to_dev(pack(b_codes))
     sa = to_dev(np.asarray(a_scale, dtype=np.uint8))
     sb = to_dev(np.asarray(b_scale, dtype=np.uint8))
-    d = torch.zeros((64, 4), dtype=torch.float32, device=A.device)
-    m.check(m.moe_test_mxfp4_probe(A, sa, Bq, sb, d))
+    d = torch.zeros((64, 16), dtype=torch.float32, device=A.device)
+    m.check(m.moe_test_mxfp4_probe(shape, A, sa, Bq, sb, d))
     torch.cuda.synchronize()
     return d.cpu().numpy()
 
 
-def lane_matrix(d):
-    """Lane outputs -> D[16][16] under the layout lane l, reg v = D[4*(l//16)+v][l%16]."""
-    D = np.zeros((16, 16), dtype=np.float32)
+def lane_matrix(shape, d):
+    """Lane outputs -> D[n][n].  16x16x128: lane l, reg v = D[4*(l//16)+v][l%16];
+    32x32x64: lane l, reg v = D[8*(v//4) + 4*(l//32) + v%4][l%32]."""
+    n = SHAPES[shape]
+    D = np.zeros((n, n), dtype=np.float32)
     for l in range(64):
-        for v in range(4):
-            D[4 * (l // 16) + v, l % 16] = d[l, v]
+        if shape == 0:
+            for v in range(4):
+                D[4 * (l // 16) + v, l % 16] = d[l, v]
+        else:
+            for v in range(16):
+                D[8 * (v // 4) + 4 * (l // 32) + v % 4, l % 32] = d[l, v]
     return D
 
 
-def test_probe_every_code_and_scale():
-    say("probe: one-hot A against B codes (j+k)%16, B scales 2..250")
-    # A row i holds 1.0 (code 2) at K position k_i = 32*(i%4) + 5*(i//4) + 1
-    kpos = [32 * (i % 4) + 5 * (i // 4) + 1 for i in range(16)]
-    a_codes = np.zeros((64, 32), dtype=np.uint8)
-    for i, kk in enumerate(kpos):
-        a_codes[16 * (kk // 32) + i, kk % 32] = 2
-    b_codes = np.zeros((64, 32), dtype=np.uint8)
+def kpos(shape):
+    """A row i holds 1.0 at K position k_i (every row a different one)."""
+    n = SHAPES[shape]
+    nb = 64 // n   # K blocks per instruction
+    return [32 * (i % nb) + (nb * (i // nb)) % 32 + 1 for i in range(n)]
+
+
+def one_hot_rows(shape):
+    n = SHAPES[shape]
+    a = np.zeros((64, 32), dtype=np.uint8)
+    for i, kk in enumerate(kpos(shape)):
+        a[n * (kk // 32) + i, kk % 32] = 2      # lane n*block + row holds that block
+    return a
+
+
+def ramp_cols(shape):
+    n = SHAPES[shape]
+    b = np.zeros((64, 32), dtype=np.uint8)
     for l in range(64):
-        j, g = l % 16, l // 16
+        j, g = l % n, l // n
         for m_ in range(32):
-            b_codes[l, m_] = (j + 32 * g + m_) % 16
+            b[l, m_] = (j + 32 * g + m_) % 16
+    return b
+
+
+@pytest.mark.parametrize("shape", [0, 1])
+def test_probe_every_code_and_scale(shape):
+    n = SHAPES[shape]
+    say(f"probe shape {shape}: one-hot A against B codes (j+k)%16, B scales 2..250")
+    a_codes, b_codes = one_hot_rows(shape), ramp_cols(shape)
+    ks = kpos(shape)
+    assert len(set(ks)) == n and max(ks) < 2048 // n
     for s in range(2, 251):
-        d = _probe(a_codes, [127] * 64, b_codes, [s] * 64)
-        D = lane_matrix(d)
-        for i, kk in enumerate(kpos):
-            for j in range(16):
+        D = lane_matrix(shape, _probe(shape, a_codes, [127] * 64, b_codes, [s] * 64))
+        for i, kk in enumerate(ks):
+            for j in range(n):
                 want = mxfp4.VALUE[(j + kk) % 16] * 2.0 ** (s - 127)
                 assert D[i, j] == np.float32(want), (s, i, j, D[i, j], want)
-    say("probe: A-side decode (B one-hot)")
+    say(f"probe shape {shape}: A-side decode (B one-hot)")
     for s in (2, 60, 127, 200, 250):
-        d = _probe(b_codes, [s] * 64, a_codes, [127] * 64)
-        D = lane_matrix(d)
-        for j, kk in enumerate(kpos):
-            for i in range(16):
+        D = lane_matrix(shape, _probe(shape, b_codes, [s] * 64, a_codes, [127] * 64))
+        for j, kk in enumerate(ks):
+            for i in range(n):
                 want = mxfp4.VALUE[(i + kk) % 16] * 2.0 ** (s - 127)
                 assert D[i, j] == np.float32(want)
 
 
-def test_probe_full_contraction():
-    say("probe: random 16x16x128 contraction")
-    rng = np.random.default_rng(0)
+@pytest.mark.parametrize("shape", [0, 1])
+def test_probe_full_contraction(shape):
+    n = SHAPES[shape]
+    kdim = 2048 // n
+    say(f"probe shape {shape}: random {n}x{n}x{kdim} contraction")
+    rng = np.random.default_rng(shape)
     a = rng.integers(0, 16, size=(64, 32)).astype(np.uint8)
     b = rng.integers(0, 16, size=(64, 32)).astype(np.uint8)
     sa = rng.integers(120, 134, size=64)
     sb = rng.integers(120, 134, size=64)
-    D = lane_matrix(_probe(a, sa, b, sb))
-    # A[i][k], k = 32*g + m held by lane 16g+i; B[k][j] by lane 16g+j
-    Am = np.zeros((16, 128))
-    Bm = np.zeros((128, 16))
+    D = lane_matrix(shape, _probe(shape, a, sa, b, sb))
+    # A[i][k], k = 32*g + m held by lane n*g+i; B[k][j] by lane n*g+j
+    Am = np.zeros((n, kdim))
+    Bm = np.zeros((kdim, n))
     for l in range(64):
-        i, g = l % 16, l // 16
+        i, g = l % n, l // n
         Am[i, 32 * g:32 * g + 32] = mxfp4.VALUE[a[l]] * 2.0 ** (sa[l] - 127)
         Bm[32 * g:32 * g + 32, i] = mxfp4.VALUE[b[l]] * 2.0 ** (sb[l] - 127)
     want = Am @ Bm   # exact in float64 for these ranges
@@ -301,6 +333,11 @@ def test_layer_parity_long_sampled():
     (13, 16, 4, 10, 256, 128),
     (70, 12, 6, 3, 96, 64),      # padding picks; partial 512-wide super-chunks
     (40, 8, 2, 8, 544, 160),     # H, I not multiples of 128
+    (31, 16, 4, 10, 256, 128),   # largest batch on the small-batch kernels
+    (32, 16, 4, 10, 256, 128),   # smallest batch on the tiled kernels
+    (300, 8, 2, 5, 256, 128),    # slots with several 128-row tiles
+    (129, 4, 1, 2, 544, 96),     # ragged last tile, partial super-chunks in both GEMMs
+    (600, 6, 6, 6, 1024, 512),   # every expert picked by every token: 600 rows per slot
 ])
 def test_layer_edge_shapes(T, E, k, nr, H, I):
     say(f"layer edge T={T} E={E} k={k} routable={nr} H={H} I={I}")
@@ -316,6 +353,29 @@ def test_layer_sparse_slots_prebuilt_worklist():
     T, H, E, k, I, S = 24, 256, 16, 4, 128, 2000
     lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=I, n_routable=12, seed=31, bias_scale=0.5)
     rng = np.random.default_rng(2)
+    spread = rng.choice(S, size=12, replace=False)
+    es = lay.expert_slot.copy()
+    es[es >= 0] = spread[es[es >= 0]]
+    slot_expert = np.full(S, -1)
+    slot_expert[es[es >= 0]] = np.flatnonzero(es >= 0)
+    lay.slot_expert = slot_expert.astype(np.int32)
+    g = GpuLayer.__new__(GpuLayer)
+    _init_route_only(g, lay, es, S)
+    from resident_expert_routing_amd import runtime as R
+    import torch
+    g.arena = R.Arena(S, H, I, torch.device("cuda", 0))
+    g.arena.mem.zero_()
+    g.arena.upload(lambda s: lay.expert_bytes(slot_expert[s]), slots=spread)
+    g.slot_bytes_fn = lambda: (lambda s: lay.expert_bytes(slot_expert[s]))
+    _layer_parity(g)
+
+
+def test_layer_sparse_slots_tiled():
+    """Tiled path with used slots spread over 3000 slot ids."""
+    say("tiled layer with 12 routable experts spread over 3000 slots")
+    T, H, E, k, I, S = 200, 256, 16, 4, 128, 3000
+    lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=I, n_routable=12, seed=33, bias_scale=0.5)
+    rng = np.random.default_rng(3)
     spread = rng.choice(S, size=12, replace=False)
     es = lay.expert_slot.copy()
     es[es >= 0] = spread[es[es >= 0]]
@@ -364,6 +424,29 @@ def test_determinism_and_batch_invariance():
         one.route()
         one.experts()
         assert np.array_equal(one.out_f64()[0], a[t]), t
+
+
+def test_batch_invariance_pipelined_path():
+    """A token's output is bit-identical whether it runs in the 2048-token
+    batch or in a 64-token batch (both on the pipelined kernels); alone (the
+    small-batch kernels) it agrees to float32 rounding of the sums."""
+    g = gpu_layer("prefill")
+    say("batch invariance: 64 prefill tokens vs the same tokens in the 2048-token batch")
+    g.route()
+    g.experts()
+    full = g.out_f64().copy()
+    sub = GpuLayer(g.lay, x_bits=g.x_bits[100:164], arena=g.arena)
+    sub.route()
+    sub.experts()
+    assert np.array_equal(sub.out_f64(), full[100:164])
+    for t in (0, 777, 2047):
+        one = GpuLayer(g.lay, x_bits=g.x_bits[t:t + 1], arena=g.arena)
+        one.route()
+        one.experts()
+        # each path rounds its fp32 sums differently (and so may round an h
+        # element to a neighbouring E2M1 code): the outputs agree to the
+        # layer's tolerance, not bit for bit
+        assert moe.rel_l2(one.out_f64()[0], full[t]) <= OUT_REL_L2, t
 
 
 def test_scale_bump_doubles_expert():
