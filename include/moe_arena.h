@@ -104,10 +104,13 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  * MXFP4 activations for one layer call.
  *
  * Steps (TideLM README, "How adaptive expert loading works", items 1-2):
- *   z[t,e]  = sum_h x[t,h] * w_router[e,h] + bias[e], accumulated in float64:
- *             the sum over h runs in chunks of 32 (a fused multiply-add chain
- *             over each chunk, ascending h), the chunk sums are added in
- *             ascending chunk order, then the bias.
+ *   z[t,e]  = sum_h x[t,h] * w_router[e,h] + bias[e] in float64 (every
+ *             product is exact): for T <= 64 the sum over h runs in chunks
+ *             of 32 (a fused multiply-add chain over each chunk, ascending h)
+ *             whose sums are added in ascending order; for larger T it is the
+ *             chain over h in steps of 4 of the float64 matrix instruction;
+ *             then the bias.  Within each regime a token's z does not depend
+ *             on the rest of the batch.
  *   p[t,:]  = softmax over all E experts of z[t,:] (float64).
  *   topk    = the k experts with the largest z (ties to the lower id), listed in
  *             ascending id, with score p[t,e]: the picks demand is recorded over.

@@ -13,7 +13,6 @@ namespace moe {
 
 constexpr int kWave = 64;
 constexpr int kRouterChunk = 32;    // h-chunk of the float64 router sum
-constexpr int kRouterTile = 128;    // h staged per LDS tile by the tiled router
 constexpr int kSplitRouterMaxT = 64;  // at or below: chunk partials in parallel
 constexpr int kDemandChunk = 64;    // tokens per demand partial
 

@@ -107,65 +107,84 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
   }
 }
 
-// Tiled full-K router for larger T: a workgroup owns 64 experts x 16 tokens; a
-// 128-wide tile of W and x is staged in LDS; each thread keeps 4 tokens x 1
-// expert, and each 32-wide chunk's fma chain is added into the running sum.
-constexpr int RT_E = 64, RT_T = 16, RT_TPT = 4;
+// Router for larger T on the float64 matrix cores (v_mfma_f64_16x16x4f64):
+// bf16 x fp32 products are exact in float64 and every sum is float64; each
+// z[t,e] is the chain, over h in steps of 4 ascending, of the instruction's
+// float64 sum of its four products added to the running value (one fixed,
+// batch-independent order).  A workgroup owns 32 tokens x 64 experts; wave w
+// owns experts 16w..16w+15 of it (two 16x16 tiles, tokens 0-15 and 16-31).
+// K tiles of 32 are staged in LDS as float32 (exact for bf16 and fp32),
+// k-major with a 16-float pad so a fragment read hits 64 distinct banks, and
+// double-buffered through registers.
+typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr int RM_T = 32, RM_E = 64, RM_K = 32;
+constexpr int RM_XS = RM_T + 16, RM_WS = RM_E + 16;
+
 __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restrict__ x,
                                                        const float* __restrict__ w, int T, int H,
                                                        int E, double* __restrict__ z) {
-  __shared__ float ws[RT_E][kRouterTile + 1];
-  __shared__ double xs[kRouterTile][RT_T];
-  const int tid = threadIdx.x;
-  const int el = tid & 63, tg = tid >> 6;
-  const int e0 = blockIdx.x * RT_E, t0 = blockIdx.y * RT_T;
-  double acc[RT_TPT], part[RT_TPT];
-#pragma unroll
-  for (int i = 0; i < RT_TPT; ++i) acc[i] = 0.0;
-  const int ntile = (H + kRouterTile - 1) / kRouterTile;
+  __shared__ float xs[2][RM_K][RM_XS];
+  __shared__ float ws[2][RM_K][RM_WS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.y * RM_T, e0 = blockIdx.x * RM_E;
+  // staging roles: x -- token tid/8, h 4(tid%8)..+3; w -- expert tid/4, h 8(tid%4)..+7
+  const int xt = tid >> 3, xq = tid & 7;
+  const int we = tid >> 2, wq = tid & 3;
+  const bool xin = t0 + xt < T, win = e0 + we < E;
+  const uint16_t* xrow = x + (size_t)(xin ? t0 + xt : 0) * H + 4 * xq;
+  const float* wrow = w + (size_t)(win ? e0 + we : 0) * H + 8 * wq;
+  uint2 xv = xin ? *reinterpret_cast<const uint2*>(xrow) : make_uint2(0u, 0u);
+  float4 w0 = win ? *reinterpret_cast<const float4*>(wrow) : make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 w1 = win ? *reinterpret_cast<const float4*>(wrow + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  auto stage = [&](int b) {
+    xs[b][4 * xq + 0][xt] = bf16_to_f32(xv.x & 0xFFFFu);
+    xs[b][4 * xq + 1][xt] = bf16_to_f32(xv.x >> 16);
+    xs[b][4 * xq + 2][xt] = bf16_to_f32(xv.y & 0xFFFFu);
+    xs[b][4 * xq + 3][xt] = bf16_to_f32(xv.y >> 16);
+    ws[b][8 * wq + 0][we] = w0.x;
+    ws[b][8 * wq + 1][we] = w0.y;
+    ws[b][8 * wq + 2][we] = w0.z;
+    ws[b][8 * wq + 3][we] = w0.w;
+    ws[b][8 * wq + 4][we] = w1.x;
+    ws[b][8 * wq + 5][we] = w1.y;
+    ws[b][8 * wq + 6][we] = w1.z;
+    ws[b][8 * wq + 7][we] = w1.w;
+  };
+  stage(0);
+  __syncthreads();
+  v4d acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
+  const int r = lane & 15, kq = lane >> 4;
+  const int ntile = H / RM_K;
   for (int c = 0; c < ntile; ++c) {
-    const int h0 = c * kRouterTile;
-    const int hn = min(kRouterTile, H - h0);
-    for (int i = tid; i < RT_E * (kRouterTile / 4); i += 256) {
-      const int r = i / (kRouterTile / 4), q = i % (kRouterTile / 4);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e0 + r < E && q * 4 < hn)
-        v = *reinterpret_cast<const float4*>(w + (size_t)(e0 + r) * H + h0 + q * 4);
-      ws[r][q * 4 + 0] = v.x;
-      ws[r][q * 4 + 1] = v.y;
-      ws[r][q * 4 + 2] = v.z;
-      ws[r][q * 4 + 3] = v.w;
+    const int b = c & 1;
+    if (c + 1 < ntile) {
+      const int h0 = (c + 1) * RM_K;
+      xv = xin ? *reinterpret_cast<const uint2*>(xrow + h0) : make_uint2(0u, 0u);
+      w0 = win ? *reinterpret_cast<const float4*>(wrow + h0) : make_float4(0.f, 0.f, 0.f, 0.f);
+      w1 = win ? *reinterpret_cast<const float4*>(wrow + h0 + 4)
+               : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    for (int i = tid; i < RT_T * (kRouterTile / 4); i += 256) {
-      const int r = i / (kRouterTile / 4), q = i % (kRouterTile / 4);
-      uint2 v = make_uint2(0u, 0u);
-      if (t0 + r < T && q * 4 < hn)
-        v = *reinterpret_cast<const uint2*>(x + (size_t)(t0 + r) * H + h0 + q * 4);
-      xs[q * 4 + 0][r] = (double)bf16_to_f32(v.x & 0xFFFFu);
-      xs[q * 4 + 1][r] = (double)bf16_to_f32(v.x >> 16);
-      xs[q * 4 + 2][r] = (double)bf16_to_f32(v.y & 0xFFFFu);
-      xs[q * 4 + 3][r] = (double)bf16_to_f32(v.y >> 16);
+#pragma unroll
+    for (int ks = 0; ks < RM_K / 4; ++ks) {
+      const int k = 4 * ks + kq;
+      const double a0 = (double)xs[b][k][r];
+      const double a1 = (double)xs[b][k][16 + r];
+      const double bw = (double)ws[b][k][16 * wave + r];
+      acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, bw, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, bw, acc1, 0, 0, 0);
     }
-    __syncthreads();
-    for (int c0 = 0; c0 < hn; c0 += kRouterChunk) {  // hn is a multiple of the chunk
-#pragma unroll
-      for (int i = 0; i < RT_TPT; ++i) part[i] = 0.0;
-      for (int h = c0; h < c0 + kRouterChunk; ++h) {
-        const double wv = (double)ws[el][h];
-#pragma unroll
-        for (int i = 0; i < RT_TPT; ++i) part[i] = fma(xs[h][tg * RT_TPT + i], wv, part[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < RT_TPT; ++i) acc[i] += part[i];
-    }
+    if (c + 1 < ntile) stage(b ^ 1);
     __syncthreads();
   }
-  const int e = e0 + el;
+  // lane l holds rows (tokens) l/16 + 4v, column (expert) l%16 of each tile
+  // (the float64 instruction's result layout, confirmed on the hardware)
+  const int e = e0 + 16 * wave + r;
   if (e >= E) return;
 #pragma unroll
-  for (int i = 0; i < RT_TPT; ++i) {
-    const int t = t0 + tg * RT_TPT + i;
-    if (t < T) z[(size_t)t * E + e] = acc[i];
+  for (int v = 0; v < 4; ++v) {
+    const int ta = t0 + kq + 4 * v, tb = ta + 16;
+    if (ta < T) z[(size_t)ta * E + e] = acc0[v];
+    if (tb < T) z[(size_t)tb * E + e] = acc1[v];
   }
 }
 
@@ -644,7 +663,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     router_small_f64<<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, a->xq, xq_row,
                                                     nrb);
   } else {
-    dim3 grid((E + RT_E - 1) / RT_E, (T + RT_T - 1) / RT_T);
+    dim3 grid((E + RM_E - 1) / RM_E, (T + RM_T - 1) / RM_T);
     router_full_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z);
   }
   if (!record_stage(ev,1, stream)) return MOE_EHIP;
