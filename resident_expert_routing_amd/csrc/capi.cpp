@@ -4,7 +4,7 @@
 // item 3).
 #include "common.hpp"
 
-size_t moe_route_ws_bytes_internal(int T, int H, int E);
+size_t moe_route_ws_bytes_internal(int T, int H, int E, int S);
 size_t moe_demand_ws_bytes_internal(int T, int E);
 size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S);
 
@@ -47,7 +47,7 @@ extern "C" MOE_EXPORT size_t moe_workspace_bytes(int op, int T, int H, int E, in
   switch (op) {
     case MOE_OP_ROUTE:
       if (H <= 0 || E <= 0 || H % 32 != 0) return bad;
-      return moe_route_ws_bytes_internal(T, H, E);
+      return moe_route_ws_bytes_internal(T, H, E, S);
     case MOE_OP_DEMAND:
       if (E <= 0) return bad;
       return moe_demand_ws_bytes_internal(T, E);

@@ -559,45 +559,117 @@ __global__ __launch_bounds__(1024) void route_fused_small(SelectArgs p,
   for (int a = total + tid; a < A; a += 1024) perm[a] = -1;
 }
 
-__global__ __launch_bounds__(1024) void bucket_count_scan(const int32_t* __restrict__ sel_slot,
-                                                          int A, int S,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ perm) {
-  __shared__ int cnt[MOE_MAX_S];
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x;
-  for (int s = tid; s < S; s += 1024) cnt[s] = 0;
+// Bucketing for larger batches, stable by (slot, assignment).  The k picks of
+// a token lie in distinct slots (distinct routable experts have distinct
+// slots), so within a slot the assignments of a chunk of 64 tokens are
+// ordered by token, and a token's rank among them is the number of the
+// chunk's earlier tokens whose bit is set in the slot's 64-bit token mask.
+constexpr int kBucketChunk = 64;
+
+// Token mask of every slot for chunk blockIdx.x, in LDS (S 64-bit words).
+__device__ void chunk_token_masks(const int32_t* __restrict__ sel_slot, int T, int k, int S,
+                                  unsigned long long* bits) {
+  const int c = blockIdx.x, t0 = c * kBucketChunk;
+  const int n = min(kBucketChunk, T - t0) * k;
+  for (int s = threadIdx.x; s < S; s += blockDim.x) bits[s] = 0ull;
   __syncthreads();
-  for (int a = tid; a < A; a += 1024) {
-    const int s = sel_slot[a];
-    if (s >= 0 && s < S) atomicAdd(&cnt[s], 1);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int s = sel_slot[(size_t)t0 * k + i];
+    if (s >= 0 && s < S) atomicOr(&bits[s], 1ull << (i / k));
   }
   __syncthreads();
-  const int total = wg_offsets_from_counts(cnt, S, offsets, wsum);
+}
+
+// counts[s * nchunk + c] = tokens of chunk c with a pick in slot s.
+__global__ __launch_bounds__(256) void bucket_hist(const int32_t* __restrict__ sel_slot, int T,
+                                                   int k, int S, int nchunk,
+                                                   int32_t* __restrict__ counts) {
+  extern __shared__ unsigned long long bits[];
+  chunk_token_masks(sel_slot, T, k, S, bits);
+  for (int s = threadIdx.x; s < S; s += blockDim.x)
+    counts[(size_t)s * nchunk + blockIdx.x] = __popcll(bits[s]);
+}
+
+// One workgroup: offsets = exclusive scan of the slot totals (S+1 entries),
+// and counts[s][c] replaced by the first perm position of chunk c's
+// assignments in slot s.  perm entries past the total are set to -1.  A wave
+// handles one slot at a time (lanes over chunks); one pass of 1024 threads
+// scans the slot totals.
+__global__ __launch_bounds__(1024) void bucket_scan(int32_t* __restrict__ counts, int S,
+                                                    int nchunk, int A,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm) {
+  __shared__ int tot[MOE_MAX_S];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int s = wv; s < S; s += 16) {
+    const int32_t* cs = counts + (size_t)s * nchunk;
+    int v = 0;
+    for (int c = lane; c < nchunk; c += 64) v += cs[c];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    if (lane == 0) tot[s] = v;
+  }
+  __syncthreads();
+  const int per = (S + 1023) / 1024;
+  const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int local = 0;
+  for (int s = lo; s < hi; ++s) local += tot[s];
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < wv; ++i) run += wsum[i];
+  for (int s = lo; s < hi; ++s) {
+    const int n = tot[s];
+    tot[s] = run;  // exclusive offset of slot s
+    offsets[s] = run;
+    run += n;
+  }
+  int total = 0;
+  for (int i = 0; i < 16; ++i) total += wsum[i];
+  if (tid == 0) offsets[S] = total;
+  __syncthreads();
+  for (int s = wv; s < S; s += 16) {
+    int32_t* cs = counts + (size_t)s * nchunk;
+    int carry = tot[s];
+    for (int c0 = 0; c0 < nchunk; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = c < nchunk ? cs[c] : 0;
+      int inc = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+      }
+      if (c < nchunk) cs[c] = carry + inc - v;
+      carry += __shfl(inc, 63, kWave);
+    }
+  }
   for (int a = total + tid; a < A; a += 1024) perm[a] = -1;
 }
 
-__global__ __launch_bounds__(256) void bucket_scatter(const int32_t* __restrict__ sel_slot, int A,
-                                                      const int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ perm) {
-  __shared__ int wcnt[4];
-  const int s = blockIdx.x;
-  const int base0 = offsets[s];
-  const int n = offsets[s + 1] - base0;
-  if (n <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int found = 0;
-  for (int a0 = 0; a0 < A && found < n; a0 += 256) {
-    const int a = a0 + tid;
-    const bool hit = a < A && sel_slot[a] == s;
-    const uint64_t m = __ballot(hit);
-    if (lane == 0) wcnt[wv] = __popcll(m);
-    __syncthreads();
-    int before = 0;
-    for (int i = 0; i < wv; ++i) before += wcnt[i];
-    if (hit) perm[base0 + found + before + __popcll(m & lanemask_lt())] = a;
-    found += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-    __syncthreads();
+// perm[base[s][c] + rank] = a for every assignment a of chunk c in slot s.
+__global__ __launch_bounds__(256) void bucket_place(const int32_t* __restrict__ sel_slot, int T,
+                                                    int k, int S, int nchunk,
+                                                    const int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ perm) {
+  extern __shared__ unsigned long long bits[];
+  chunk_token_masks(sel_slot, T, k, S, bits);
+  const int c = blockIdx.x, t0 = c * kBucketChunk;
+  const int n = min(kBucketChunk, T - t0) * k;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int s = sel_slot[(size_t)t0 * k + i];
+    if (s >= 0 && s < S) {
+      const int tl = i / k;
+      const int rank = __popcll(bits[s] & ((1ull << tl) - 1ull));
+      perm[base[(size_t)s * nchunk + c] + rank] = t0 * k + i;
+    }
   }
 }
 
@@ -617,12 +689,20 @@ int moe_demand_launch_internal(const int32_t* te, const float* ts, int T, int k,
 // Workspace: float64 logits [T][E], then the demand partials of the batch.
 static size_t route_z_bytes(int T, int E) { return up_to((size_t)T * E * sizeof(double), 256); }
 
-static size_t route_ws_bytes(int T, int H, int E) {
-  if (T <= 0) return 0;
-  return route_z_bytes(T, E) + moe_demand_ws_bytes_internal(T, E);
+// Per-(slot, chunk) bucket counts of the larger-batch bucketing.
+static size_t route_bucket_bytes(int T, int S) {
+  const size_t nchunk = (size_t)(T + kBucketChunk - 1) / kBucketChunk;
+  return up_to(nchunk * (size_t)(S > 0 ? S : 1) * sizeof(int32_t), 256);
 }
 
-size_t moe_route_ws_bytes_internal(int T, int H, int E) { return route_ws_bytes(T, H, E); }
+static size_t route_ws_bytes(int T, int H, int E, int S) {
+  if (T <= 0) return 0;
+  return route_z_bytes(T, E) + moe_demand_ws_bytes_internal(T, E) + route_bucket_bytes(T, S);
+}
+
+size_t moe_route_ws_bytes_internal(int T, int H, int E, int S) {
+  return route_ws_bytes(T, H, E, S);
+}
 
 extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream) {
   if (!a) return MOE_EINVAL;
@@ -638,7 +718,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
         !a->sel_expert || !a->sel_weight || !a->sel_slot || !a->perm || !a->xq)
       return MOE_EINVAL;
     if (!aligned(a->x, 16) || !aligned(a->w_router, 16) || !aligned(a->xq, 16)) return MOE_EINVAL;
-    const size_t need = route_ws_bytes(T, H, E);
+    const size_t need = route_ws_bytes(T, H, E, S);
     if (a->ws_bytes < need) return MOE_EWORKSPACE;
     if (need > 0 && (!a->ws || !aligned(a->ws, 256))) return MOE_EINVAL;
   }
@@ -708,9 +788,14 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     if (st != MOE_OK) return st;
   }
   if (!record_stage(ev,2, stream)) return MOE_EHIP;
-  bucket_count_scan<<<1, 1024, 0, stream>>>(a->sel_slot, A, S, a->slot_offsets, a->perm);
+  const int nbc = (T + kBucketChunk - 1) / kBucketChunk;
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a->ws) + route_z_bytes(T, E) +
+                                               moe_demand_ws_bytes_internal(T, E));
+  const size_t mask_lds = (size_t)(S > 0 ? S : 1) * sizeof(unsigned long long);
+  if (S > 0) bucket_hist<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts);
+  bucket_scan<<<1, 1024, 0, stream>>>(counts, S, nbc, A, a->slot_offsets, a->perm);
   if (!record_stage(ev,3, stream)) return MOE_EHIP;
-  if (S > 0) bucket_scatter<<<S, 256, 0, stream>>>(a->sel_slot, A, a->slot_offsets, a->perm);
+  if (S > 0) bucket_place<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts, a->perm);
   if (!record_stage(ev,4, stream)) return MOE_EHIP;
   return hip_status();
 }

@@ -66,9 +66,12 @@ def test_layout_helpers_match_documented_format():
 def test_workspace_sizes():
     ws = B.moe_workspace_bytes
     assert ws(B.MOE_OP_ROUTE, 0, 4096, 256, 8, 0, 230) == 0
-    # float64 logits, then demand partials (chunks of 64 tokens x 256 experts)
-    assert ws(B.MOE_OP_ROUTE, 8, 4096, 256, 8, 0, 230) == 8 * 256 * 8
-    assert ws(B.MOE_OP_ROUTE, 2048, 4096, 256, 8, 0, 166) == 2048 * 256 * 8 + 32 * 256 * 8
+    # float64 logits, demand partials (chunks of 64 tokens x 256 experts), then
+    # bucket counts (chunks of 64 tokens x slots, 256-byte aligned)
+    up = lambda v: (v + 255) // 256 * 256
+    assert ws(B.MOE_OP_ROUTE, 8, 4096, 256, 8, 0, 230) == 8 * 256 * 8 + up(230 * 4)
+    assert ws(B.MOE_OP_ROUTE, 2048, 4096, 256, 8, 0, 166) == \
+        2048 * 256 * 8 + 32 * 256 * 8 + up(32 * 166 * 4)
     assert ws(B.MOE_OP_DEMAND, 64, 0, 256, 8, 0, 0) == 0
     assert ws(B.MOE_OP_DEMAND, 65, 0, 256, 8, 0, 0) == 2 * 256 * 8
     e = ws(B.MOE_OP_EXPERTS, 8, 4096, 0, 8, 2048, 230)
