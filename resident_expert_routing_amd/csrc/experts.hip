@@ -208,12 +208,13 @@ __device__ __forceinline__ void swiglu_quant_store32(const v16f& G, const v16f& 
   }
 }
 
-// y rows n0 + 8q + 4hh .. +3 of one column (an fp32 row of H).
-__device__ __forceinline__ void store_y(float* yr, int n0, int hh, const v16f& acc) {
+// y rows n0 + 8q + 4hh .. +3 of one column, rounded to bf16 (a bf16 row of H).
+__device__ __forceinline__ void store_y_bf16(uint16_t* yr, int n0, int hh, const v16f& acc) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    *reinterpret_cast<float4*>(yr + n0 + 8 * q + 4 * hh) =
-        make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    *reinterpret_cast<uint2*>(yr + n0 + 8 * q + 4 * hh) =
+        make_uint2(f32_to_bf16(acc[4 * q]) | (f32_to_bf16(acc[4 * q + 1]) << 16),
+                   f32_to_bf16(acc[4 * q + 2]) | (f32_to_bf16(acc[4 * q + 3]) << 16));
 }
 
 // The u-th slot (ascending) that holds assignments, found by the whole
@@ -460,9 +461,21 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Combine: out[t] = sum_j (ascending) w[t,j] * y[t*k+j], rounded once to bf16.
+// Combine: out[t] = sum_j (ascending) w[t,j] * y[t*k+j] in float32, rounded
+// once to bf16.  y rows are float32 (small-batch kernels) or bf16 (pipelined).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+__device__ __forceinline__ float4 load_y4(const float* y, size_t i) {
+  return *reinterpret_cast<const float4*>(y + i);
+}
+
+__device__ __forceinline__ float4 load_y4(const uint16_t* y, size_t i) {
+  const uint2 v = *reinterpret_cast<const uint2*>(y + i);
+  return make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16),
+                     bf16_to_f32(v.y & 0xFFFFu), bf16_to_f32(v.y >> 16));
+}
+
+template <typename YT>
+__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ sel_slot, int T,
                                                       int H, int k, int S,
@@ -475,7 +488,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int sl = sel_slot[(size_t)t * k + j];
     if (sl < 0 || sl >= S) continue;
     const float wj = w[(size_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)t * k + j) * H + h);
+    const float4 v = load_y4(y, ((size_t)t * k + j) * H + h);
     a0 = fmaf(wj, v.x, a0);
     a1 = fmaf(wj, v.y, a1);
     a2 = fmaf(wj, v.z, a2);
@@ -760,7 +773,7 @@ struct PipeArgs {
   const uint8_t* zero;
   uint8_t* hq;  // gate/up output
   size_t hrow;
-  float* y;     // down output
+  uint16_t* y;  // down output, bf16 rows
   int H, I, k, A, nN;
 };
 
@@ -841,10 +854,10 @@ __global__ __launch_bounds__(256) void down_pipe(PipeArgs p) {
     if (lr < rows) {
       const int a = p.perm[p0 + lr];
       if (a >= 0 && a < p.A) {
-        float* yr = p.y + (size_t)a * p.H;
+        uint16_t* yr = p.y + (size_t)a * p.H;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          if (tv[t]) store_y(yr, n0 + 32 * t, hh, acc[t][cb]);
+          if (tv[t]) store_y_bf16(yr, n0 + 32 * t, hh, acc[t][cb]);
       }
     }
   }
@@ -916,8 +929,8 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   if (S == 0) {
     // nothing routable: every pick is padding, the output is zero
     dim3 grid(T, (H + 1023) / 1024);
-    combine_kernel<<<grid, 256, 0, stream>>>(nullptr, a->sel_weight, a->sel_slot, T, H, k, S,
-                                             a->out);
+    combine_kernel<float><<<grid, 256, 0, stream>>>(nullptr, a->sel_weight, a->sel_slot, T, H,
+                                                    k, S, a->out);
     return hip_status();
   }
   uint8_t* ws = static_cast<uint8_t*>(a->ws);
@@ -947,7 +960,7 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     t.zero = zero;
     t.hq = hq;
     t.hrow = mxfp4_row_bytes(I);
-    t.y = y;
+    t.y = reinterpret_cast<uint16_t*>(y);
     t.H = H;
     t.I = I;
     t.k = k;
@@ -1020,7 +1033,13 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   }
   dim3 cgrid(T, (H + 1023) / 1024);
-  combine_kernel<<<cgrid, 256, 0, stream>>>(y, a->sel_weight, a->sel_slot, T, H, k, S, a->out);
+  if (pipe)
+    combine_kernel<uint16_t><<<cgrid, 256, 0, stream>>>(reinterpret_cast<const uint16_t*>(y),
+                                                        a->sel_weight, a->sel_slot, T, H, k, S,
+                                                        a->out);
+  else
+    combine_kernel<float><<<cgrid, 256, 0, stream>>>(y, a->sel_weight, a->sel_slot, T, H, k, S,
+                                                     a->out);
   if (!record_stage(ev, 4, stream)) return MOE_EHIP;
   return hip_status();
 }
