@@ -871,12 +871,14 @@ struct ExpertsWs {
   size_t used_off, items_off, zero_off, hq_off, y_off, total;
 };
 
-// Batches of at least this many tokens, with H and I multiples of 256, take
-// the pipelined path; every other batch the small-batch kernels.
-constexpr int kPipeMinT = 32;
+// Batches of at least this many assignments (T*k), with H and I multiples of
+// 256, take the pipelined path; every other batch the small-batch kernels.
+// Measured crossover on the 4096/2048 model with 166 slots: the small-batch
+// kernels win up to 1024 assignments, the pipelined ones from 2048.
+constexpr int kPipeMinA = 2048;
 
-static bool use_pipe(int T, int H, int I) {
-  return T >= kPipeMinT && H % 256 == 0 && I % 256 == 0;
+static bool use_pipe(int T, int k, int H, int I) {
+  return (size_t)T * k >= (size_t)kPipeMinA && H % 256 == 0 && I % 256 == 0;
 }
 
 // Upper bound on the M-tiles of a batch: one partial tile per used slot plus
@@ -888,7 +890,7 @@ static size_t max_tiles(size_t A, int S) {
 static ExpertsWs experts_ws(int T, int H, int k, int I, int S) {
   ExpertsWs w;
   const size_t A = (size_t)T * k;
-  const bool pipe = use_pipe(T, H, I);
+  const bool pipe = use_pipe(T, k, H, I);
   w.used_off = 0;
   w.items_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
   const size_t items = pipe ? (1 + 4 * max_tiles(A, S)) * sizeof(int32_t) : 0;
@@ -921,7 +923,7 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   if (a->ws_bytes < W.total) return MOE_EWORKSPACE;
   if (!a->ws || !aligned(a->ws, 256)) return MOE_EINVAL;
   const int A = T * k;
-  const bool pipe = use_pipe(T, H, I);
+  const bool pipe = use_pipe(T, k, H, I);
   const size_t ntile = max_tiles((size_t)A, S);
   const size_t g1 = up_to(ntile * (size_t)((I + 127) / 128), 8);
   const size_t g2 = up_to(ntile * (size_t)((H + 255) / 256), 8);

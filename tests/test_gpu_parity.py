@@ -333,10 +333,11 @@ def test_layer_parity_long_sampled():
     (13, 16, 4, 10, 256, 128),
     (70, 12, 6, 3, 96, 64),      # padding picks; partial 512-wide super-chunks
     (40, 8, 2, 8, 544, 160),     # H, I not multiples of 128
-    (31, 16, 4, 10, 256, 128),   # largest batch on the small-batch kernels
-    (32, 16, 4, 10, 256, 128),   # smallest batch on the tiled kernels
-    (300, 8, 2, 5, 256, 128),    # slots with several 128-row tiles
-    (129, 4, 1, 2, 544, 96),     # ragged last tile, partial super-chunks in both GEMMs
+    (300, 8, 2, 5, 256, 128),    # small-batch kernels, many 16-column tiles per slot
+    (129, 4, 1, 2, 544, 96),     # partial super-chunks in both GEMMs
+    (511, 16, 4, 10, 256, 256),  # 2044 assignments: largest batch on the small-batch kernels
+    (512, 16, 4, 10, 256, 256),  # 2048 assignments: smallest batch on the pipelined kernels
+    (515, 12, 4, 7, 512, 256),   # pipelined: several 128-row tiles, ragged last tile
     (600, 6, 6, 6, 1024, 512),   # every expert picked by every token: 600 rows per slot
 ])
 def test_layer_edge_shapes(T, E, k, nr, H, I):
@@ -371,9 +372,9 @@ def test_layer_sparse_slots_prebuilt_worklist():
 
 
 def test_layer_sparse_slots_tiled():
-    """Tiled path with used slots spread over 3000 slot ids."""
-    say("tiled layer with 12 routable experts spread over 3000 slots")
-    T, H, E, k, I, S = 200, 256, 16, 4, 128, 3000
+    """Pipelined path with used slots spread over 3000 slot ids."""
+    say("pipelined layer with 12 routable experts spread over 3000 slots")
+    T, H, E, k, I, S = 600, 256, 16, 4, 256, 3000
     lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=I, n_routable=12, seed=33, bias_scale=0.5)
     rng = np.random.default_rng(3)
     spread = rng.choice(S, size=12, replace=False)
@@ -428,19 +429,19 @@ def test_determinism_and_batch_invariance():
 
 def test_batch_invariance_pipelined_path():
     """A token's output is bit-identical whether it runs in the 2048-token
-    batch or in a 128-token batch (both on the matrix-core router and the
+    batch or in a 256-token batch (both on the matrix-core router and the
     pipelined kernels); alone (the small-batch kernels) it agrees to the
     layer's tolerance."""
     g = gpu_layer("prefill")
-    say("batch invariance: 128 prefill tokens vs the same tokens in the 2048-token batch")
+    say("batch invariance: 256 prefill tokens vs the same tokens in the 2048-token batch")
     g.route()
     g.experts()
     full = g.out_f64().copy()
-    sub = GpuLayer(g.lay, x_bits=g.x_bits[100:228], arena=g.arena)
+    sub = GpuLayer(g.lay, x_bits=g.x_bits[100:356], arena=g.arena)
     sub.route()
     sub.experts()
-    assert np.array_equal(sub.routing()["topk_score"], g.routing()["topk_score"][100:228])
-    assert np.array_equal(sub.out_f64(), full[100:228])
+    assert np.array_equal(sub.routing()["topk_score"], g.routing()["topk_score"][100:356])
+    assert np.array_equal(sub.out_f64(), full[100:356])
     for t in (0, 777, 2047):
         one = GpuLayer(g.lay, x_bits=g.x_bits[t:t + 1], arena=g.arena)
         one.route()
