@@ -56,7 +56,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "long", "tiny"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "long", "tiny", "arena40"])
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -119,6 +120,90 @@ def cpu_baseline(lay, k: int):
             "seconds": dt}
 
 
+def bench_arena40(args):
+    """40 layers x 256 experts sharing one 6666-slot arena, T=32 tokens per layer
+    call; then the 5 % re-plan (333 slot swaps), timed on its own."""
+    import numpy as np
+    import torch
+    import fixtures
+    import resident_expert_routing_amd  # noqa: F401
+    from resident_expert_routing_amd import runtime as R
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    model = fixtures.make_arena_model("arena40")
+    cfg = model.cfg
+    L, T, H, E, k, I, S = model.L, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, model.S
+    log(f"arena40: {L} layers, T={T} H={H} E={E} k={k} I={I}, {S} shared slots; packing")
+    model.prepack()
+    sa = R.SharedArena(S, H, I, model.expert_slot_table(), dev)
+    t0 = time.perf_counter()
+    sa.upload(model.pair_bytes)
+    log(f"arena of {S * sa.arena.stride / 1e9:.1f} GB uploaded in {time.perf_counter() - t0:.1f} s")
+    ws = [torch.from_numpy(l.w_router).to(dev) for l in model.layers]
+    bs = [torch.from_numpy(l.bias).to(dev) for l in model.layers]
+    nx = 4
+    xs = [torch.from_numpy(model.tokens(s).view(np.int16)).to(dev) for s in range(nx)]
+    buf = R.LayerBuffers(T, H, E, k, I, S, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def layer(x, l):
+        R.route(buf, x, ws[l], bs[l], sa.table[l], stream, hist_row=sa.hist[l])
+        R.experts(buf, sa.arena.ptr(), sa.arena.stride, stream)
+
+    def step(s):
+        for l in range(L):
+            layer(xs[s % nx], l)
+
+    used = 0
+    for l in range(L):   # distinct slots per layer call, one step's worth (deterministic)
+        layer(xs[0], l)
+        torch.cuda.synchronize()
+        used += int(np.count_nonzero(np.diff(buf.slot_offsets.cpu().numpy())))
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(K):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per_layer_us = ms * 1e3 / (K * L)
+    be = expert_bytes(H, I)
+    algo = used / L * be + H * E * 4 + 2 * T * H * 2   # per layer call, mean over the layers
+    n_swap = S // 20
+    torch.cuda.synchronize()
+    r0 = time.perf_counter()
+    ev, ld = sa.replan(k, n_swap, model.pair_bytes, stream)
+    torch.cuda.synchronize()
+    replan_s = time.perf_counter() - r0
+    moved = sum(1 for (le, _), (ll, _) in zip(ev, ld) if le != ll)
+    for i in range(2):   # the layers run on the new tables
+        step(K + i)
+    torch.cuda.synchronize()
+    result = {
+        "metric": METRIC,
+        "value": T / (per_layer_us * 1e-6),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
+        "config": {"workload": f"arena40: {L} layers x E={E}, T={T} per layer call, H={H} k={k} "
+                               f"I={I}, {S} shared slots", "layers": L, "T": T, "S": S},
+        "layer": {"us_per_layer_call": per_layer_us, "distinct_slots_per_call": used / L,
+                  "algo_bytes_per_call": algo,
+                  "GB_per_s": algo / (per_layer_us * 1e-6) / 1e9,
+                  "hbm_frac": algo / (per_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+        "replan": {"swaps": len(ev), "cross_layer_swaps": moved,
+                   "bytes_h2d": len(ev) * sa.arena.slot_bytes, "seconds": replan_s,
+                   "GB_per_s_h2d": len(ev) * sa.arena.slot_bytes / replan_s / 1e9},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -128,6 +213,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload == "arena40":
+        bench_arena40(args)
         return
 
     import numpy as np

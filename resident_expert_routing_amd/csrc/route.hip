@@ -592,9 +592,11 @@ __global__ __launch_bounds__(256) void bucket_hist(const int32_t* __restrict__ s
 
 // One workgroup: offsets = exclusive scan of the slot totals (S+1 entries),
 // and counts[s][c] replaced by the first perm position of chunk c's
-// assignments in slot s.  perm entries past the total are set to -1.  A wave
-// handles one slot at a time (lanes over chunks); one pass of 1024 threads
-// scans the slot totals.
+// assignments in slot s.  perm entries past the total are set to -1.  With
+// few chunks a thread walks whole slots; with many, a wave handles one slot
+// at a time (lanes over chunks).  One pass of 1024 threads scans the totals.
+constexpr int kScanWaveMinChunks = 16;
+
 __global__ __launch_bounds__(1024) void bucket_scan(int32_t* __restrict__ counts, int S,
                                                     int nchunk, int A,
                                                     int32_t* __restrict__ offsets,
@@ -602,13 +604,23 @@ __global__ __launch_bounds__(1024) void bucket_scan(int32_t* __restrict__ counts
   __shared__ int tot[MOE_MAX_S];
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int s = wv; s < S; s += 16) {
-    const int32_t* cs = counts + (size_t)s * nchunk;
-    int v = 0;
-    for (int c = lane; c < nchunk; c += 64) v += cs[c];
+  const bool by_wave = nchunk >= kScanWaveMinChunks;
+  if (by_wave) {
+    for (int s = wv; s < S; s += 16) {
+      const int32_t* cs = counts + (size_t)s * nchunk;
+      int v = 0;
+      for (int c = lane; c < nchunk; c += 64) v += cs[c];
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    if (lane == 0) tot[s] = v;
+      for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+      if (lane == 0) tot[s] = v;
+    }
+  } else {
+    for (int s = tid; s < S; s += 1024) {
+      const int32_t* cs = counts + (size_t)s * nchunk;
+      int v = 0;
+      for (int c = 0; c < nchunk; ++c) v += cs[c];
+      tot[s] = v;
+    }
   }
   __syncthreads();
   const int per = (S + 1023) / 1024;
@@ -635,20 +647,32 @@ __global__ __launch_bounds__(1024) void bucket_scan(int32_t* __restrict__ counts
   for (int i = 0; i < 16; ++i) total += wsum[i];
   if (tid == 0) offsets[S] = total;
   __syncthreads();
-  for (int s = wv; s < S; s += 16) {
-    int32_t* cs = counts + (size_t)s * nchunk;
-    int carry = tot[s];
-    for (int c0 = 0; c0 < nchunk; c0 += 64) {
-      const int c = c0 + lane;
-      const int v = c < nchunk ? cs[c] : 0;
-      int inc = v;
+  if (by_wave) {
+    for (int s = wv; s < S; s += 16) {
+      int32_t* cs = counts + (size_t)s * nchunk;
+      int carry = tot[s];
+      for (int c0 = 0; c0 < nchunk; c0 += 64) {
+        const int c = c0 + lane;
+        const int v = c < nchunk ? cs[c] : 0;
+        int inc = v;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(inc, d, kWave);
-        if (lane >= d) inc += o;
+        for (int d = 1; d < 64; d <<= 1) {
+          const int o = __shfl_up(inc, d, kWave);
+          if (lane >= d) inc += o;
+        }
+        if (c < nchunk) cs[c] = carry + inc - v;
+        carry += __shfl(inc, 63, kWave);
       }
-      if (c < nchunk) cs[c] = carry + inc - v;
-      carry += __shfl(inc, 63, kWave);
+    }
+  } else {
+    for (int s = tid; s < S; s += 1024) {
+      int32_t* cs = counts + (size_t)s * nchunk;
+      int b = tot[s];
+      for (int c = 0; c < nchunk; ++c) {
+        const int n = cs[c];
+        cs[c] = b;
+        b += n;
+      }
     }
   }
   for (int a = total + tid; a < A; a += 1024) perm[a] = -1;
