@@ -105,12 +105,13 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *
  * Steps (TideLM README, "How adaptive expert loading works", items 1-2):
  *   z[t,e]  = sum_h x[t,h] * w_router[e,h] + bias[e] in float64 (every
- *             product is exact): for T <= 64 the sum over h runs in chunks
- *             of 32 (a fused multiply-add chain over each chunk, ascending h)
- *             whose sums are added in ascending order; for larger T it is the
- *             chain over h in steps of 4 of the float64 matrix instruction;
- *             then the bias.  Within each regime a token's z does not depend
- *             on the rest of the batch.
+ *             product is exact): for T <= 64 and H <= 8192 the sum over h
+ *             runs in chunks of 32 (a fused multiply-add chain over each
+ *             chunk, ascending h); the chunk sums are added in runs of 16
+ *             consecutive chunks and the run sums in ascending order; for
+ *             larger batches it is the chain over h in steps of 4 of the
+ *             float64 matrix instruction; then the bias.  Within each regime a
+ *             token's z does not depend on the rest of the batch.
  *   p[t,:]  = softmax over all E experts of z[t,:] (float64).
  *   topk    = the k experts with the largest z (ties to the lower id), listed in
  *             ascending id, with score p[t,e]: the picks demand is recorded over.
@@ -137,9 +138,10 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
  *          `stream` when T > 0: before the router logits, before selection,
  *          before bucket counting, before the scatter, and after it -- so a
- *          caller can time each kernel stage.  For T <= 16 and E <= 256,
- *          selection and bucketing run as one kernel and the last three events
- *          are recorded together after it.  A null entry is not recorded.
+ *          caller can time each kernel stage.  For T <= 64, E <= 256 and
+ *          H <= 8192, selection and bucketing run as one kernel and the last
+ *          three events are recorded together after it.  A null entry is not
+ *          recorded.
  *          Recording changes no result, but each record costs a few
  *          microseconds of stream time.
  * hist_row, delta (nullable): when hist_row is non-null the call also does
@@ -213,10 +215,12 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  * Workspace: moe_workspace_bytes(MOE_OP_EXPERTS, T, H, 0, k, I, S) bytes.
  * Any copy into a slot the call reads (arena_load_slot) must be ordered before
  * it by the caller (hipStreamWaitEvent on the load's event).
- * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
- *          `stream` when T > 0 and S > 0: before the work list, before the
- *          gate/up kernel, before the down kernel, before the combine, and after
- *          it.  A null entry is not recorded.  Recording changes no result.
+ * stage_events (host array, nullable): MOE_STAGE_EVENTS events on `stream`
+ *          when T > 0 and S > 0: [0] before the work list; [1] and [2] the
+ *          start and the end of the gate/up kernel itself, taken from its
+ *          dispatch (hipExtLaunchKernel), so their interval is that kernel's
+ *          duration; [3] after the down kernel; [4] after the combine.  A null
+ *          entry is not recorded.  Recording changes no result.
  */
 typedef struct moe_experts_args {
   int T, H, I, k, S;

@@ -95,23 +95,75 @@ __device__ __forceinline__ uint32_t e2m1_code(float v, int e) {
   return m | ((__float_as_uint(v) >> 31) << 3);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
-  return v;
+// ---------------------------------------------------------------------------
+// Wave reductions through DPP; the result is read from lane 63, so it is a
+// uniform value.  Steps: within quads (lane i with i^1, then i^2), half rows
+// (i with 7-i), rows (i with 15-i), then lane 15 of each row into rows 1 and
+// 3 and lane 31 into rows 2 and 3, after which lane 63 holds the whole wave.
+// ---------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141,
+              kDppMirror = 0x140, kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Lane values of v moved by one DPP step; rows outside ROW_MASK get `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v, double old) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v), o = (uint64_t)__double_as_longlong(old);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)o, (int)(uint32_t)u,
+                                                            CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(
+      (int)(uint32_t)(o >> 32), (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double lane63_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
 __device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmax(v, __shfl_xor(v, d, kWave));
-  return v;
+  v = fmax(v, dpp_f64<kDppQuadXor1, 0xF>(v, v));
+  v = fmax(v, dpp_f64<kDppQuadXor2, 0xF>(v, v));
+  v = fmax(v, dpp_f64<kDppHalfMirror, 0xF>(v, v));
+  v = fmax(v, dpp_f64<kDppMirror, 0xF>(v, v));
+  v = fmax(v, dpp_f64<kDppBcast15, 0xA>(v, v));
+  v = fmax(v, dpp_f64<kDppBcast31, 0xC>(v, v));
+  return lane63_f64(v);
 }
 
-// Butterfly sum: every lane ends with the same value (a+b == b+a per step).
+// Sum in the fixed order of the steps above (rows outside a step's mask add 0).
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int d = 1; d <= 32; d <<= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  v += dpp_f64<kDppQuadXor1, 0xF>(v, 0.0);
+  v += dpp_f64<kDppQuadXor2, 0xF>(v, 0.0);
+  v += dpp_f64<kDppHalfMirror, 0xF>(v, 0.0);
+  v += dpp_f64<kDppMirror, 0xF>(v, 0.0);
+  v += dpp_f64<kDppBcast15, 0xA>(v, 0.0);
+  v += dpp_f64<kDppBcast31, 0xC>(v, 0.0);
+  return lane63_f64(v);
+}
+
+// Two independent 32-bit maxima (lanes whose DPP source does not exist read
+// 0, the identity, so every step can write all rows and fold into v_max_u32).
+__device__ __forceinline__ void wave_umax32x2(uint32_t& a, uint32_t& b) {
+#define MOE_UMAX_STEP(CTRL)                                                         \
+  a = max(a, (uint32_t)__builtin_amdgcn_mov_dpp((int)a, CTRL, 0xF, 0xF, true)); \
+  b = max(b, (uint32_t)__builtin_amdgcn_mov_dpp((int)b, CTRL, 0xF, 0xF, true));
+  MOE_UMAX_STEP(kDppQuadXor1)
+  MOE_UMAX_STEP(kDppQuadXor2)
+  MOE_UMAX_STEP(kDppHalfMirror)
+  MOE_UMAX_STEP(kDppMirror)
+  MOE_UMAX_STEP(kDppBcast15)
+  MOE_UMAX_STEP(kDppBcast31)
+#undef MOE_UMAX_STEP
+  a = (uint32_t)__builtin_amdgcn_readlane((int)a, 63);
+  b = (uint32_t)__builtin_amdgcn_readlane((int)b, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_umax32(uint32_t a) {
+  uint32_t b = 0;
+  wave_umax32x2(a, b);
+  return a;
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {

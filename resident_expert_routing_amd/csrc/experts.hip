@@ -16,7 +16,8 @@
 //   (0..3) covers blocks 4i..4i+3, lane group g (lanes 16g..16g+15)
 //   supplying block 4i+g, so one load instruction reads 64 contiguous bytes
 //   of each of 16 rows.  A lane reads the super-chunk's 16 scale bytes as one
-//   16-byte word and shifts its own byte (4i+g) into place for step i.
+//   16-byte word and shifts its own byte (4i+g) into place for step i; the
+//   weight rows' scales are first copied to LDS by the workgroup.
 //
 // * Larger batches: operands are staged in LDS and the MFMA is
 //   v_mfma_scale_f32_32x32x64_f8f6f4 (on gfx950 the 16x16x128 form runs at
@@ -28,6 +29,8 @@
 //   8c + 4(s/2) + 2 + (s%2) (lanes 32-63).
 //
 // The families agree to float32 rounding of their sums, not bit for bit.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 
 namespace moe {
@@ -302,6 +305,37 @@ __global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ o
 // ===========================================================================
 // Small-batch kernels
 // ===========================================================================
+// Weight scales of the rows a workgroup streams are staged in LDS once.  A
+// row's scale bytes share one or two cache lines that the K loop would
+// otherwise touch once per super-chunk; between touches the workgroup streams
+// enough code bytes for the line to leave L2, so it would be fetched again
+// from memory every time.  LDS row stride 16*((K/512) | 1) bytes: an odd
+// number of 16-byte units, so the 16 rows of one fragment read fall on 16
+// distinct 4-bank groups.
+constexpr int kStagedRows = 256;            // rows staged per workgroup (at most)
+constexpr int kStagedLdsMax = 64 * 1024;    // LDS budget of the staged scales
+
+__host__ __device__ constexpr int staged_scale_stride(int K) { return 16 * ((K / 512) | 1); }
+
+// Full-row kernels (K a multiple of 512) with staged scales: the workgroup's
+// scale rows fit the LDS budget.
+static bool staged_ok(int K) {
+  return K % 512 == 0 && (size_t)kStagedRows * staged_scale_stride(K) <= (size_t)kStagedLdsMax;
+}
+
+// Rows [0, nrows) of a contiguous scale block (rbytes per row, a multiple of
+// 16) into LDS rows of `stride` bytes, by the whole workgroup.
+__device__ __forceinline__ void stage_scale_rows(const uint8_t* __restrict__ src, int nrows,
+                                                 int rbytes, int stride, uint8_t* lds) {
+  const int per_row = rbytes / 16;
+  const int n = nrows * per_row;
+  for (int q = threadIdx.x; q < n; q += blockDim.x) {
+    const int row = q / per_row, c = q - row * per_row;
+    *reinterpret_cast<uint4*>(lds + row * stride + c * 16) =
+        *reinterpret_cast<const uint4*>(src + (size_t)row * rbytes + c * 16);
+  }
+}
+
 // Gate/up + SwiGLU + MXFP4(h).  Workgroup = 4 waves = 128 rows of I of one
 // slot; wave = 32 rows (two 16-row tiles of gate and of up).  Columns are the
 // slot's assignment rows p, 16 per MFMA tile.  Output: hq row p (an MXFP4 row
@@ -330,21 +364,39 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
   const int p0 = p.offsets[s], p1 = p.offsets[s + 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = nb * 128 + wave * 32;
-  if (n0 >= p.I) return;
   const int r = lane & 15, g = lane >> 4;
   const int H = p.H;
   const int nblk = H / 32;
   const int nsc = (nblk + 15) / 16;
   const uint8_t* base = p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)H / 2, srow = (size_t)H / 32;
+  const uint8_t* gs0;
+  const uint8_t* us0;
+  int sstep;  // bytes from a tile-0 scale row to its tile-1 row
+  if (FULL) {
+    // gate scales of the workgroup's rows at LDS row 0.., up scales at row 128..
+    extern __shared__ __align__(16) uint8_t wscale[];
+    const int sstr = staged_scale_stride(H);
+    const int nrow = min(128, p.I - nb * 128);
+    stage_scale_rows(base + p.off_gs + (size_t)nb * 128 * srow, nrow, (int)srow, sstr, wscale);
+    stage_scale_rows(base + p.off_us + (size_t)nb * 128 * srow, nrow, (int)srow, sstr,
+                     wscale + 128 * sstr);
+    __syncthreads();
+    gs0 = wscale + (wave * 32 + r) * sstr;
+    us0 = gs0 + 128 * sstr;
+    sstep = 16 * sstr;
+  } else {
+    gs0 = base + p.off_gs + (size_t)(n0 + r) * srow;
+    us0 = base + p.off_us + (size_t)(n0 + r) * srow;
+    sstep = 16 * (int)srow;
+  }
+  if (n0 >= p.I) return;
+  const uint8_t* gs1 = gs0 + sstep;
+  const uint8_t* us1 = us0 + sstep;
   const uint8_t* gc0 = base + p.off_gc + (size_t)(n0 + r) * crow;
   const uint8_t* gc1 = gc0 + 16 * crow;
-  const uint8_t* gs0 = base + p.off_gs + (size_t)(n0 + r) * srow;
-  const uint8_t* gs1 = gs0 + 16 * srow;
   const uint8_t* uc0 = base + p.off_uc + (size_t)(n0 + r) * crow;
   const uint8_t* uc1 = uc0 + 16 * crow;
-  const uint8_t* us0 = base + p.off_us + (size_t)(n0 + r) * srow;
-  const uint8_t* us1 = us0 + 16 * srow;
 
   for (int cb = p0; cb < p1; cb += 16) {
     // this lane's column (assignment row) for the B operand
@@ -404,13 +456,20 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
   const int p0 = p.offsets[s], p1 = p.offsets[s + 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = nb * 256 + wave * 64;
-  if (n0 >= p.H) return;
   const int r = lane & 15, g = lane >> 4;
   const int I = p.I;
   const int nblk = I / 32;
   const int nsc = (nblk + 15) / 16;
   const uint8_t* base = p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)I / 2, srow = (size_t)I / 32;
+  extern __shared__ __align__(16) uint8_t wscale[];  // FULL: the workgroup's scale rows
+  const int sstr = staged_scale_stride(I);
+  if (FULL) {
+    stage_scale_rows(base + p.off_ds + (size_t)nb * 256 * srow, min(256, p.H - nb * 256),
+                     (int)srow, sstr, wscale);
+    __syncthreads();
+  }
+  if (n0 >= p.H) return;
   const uint8_t* dc[4];
   const uint8_t* ds[4];
   bool tv[4];
@@ -419,7 +478,7 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
     tv[tl] = n0 + 16 * tl < p.H;  // whole tile valid (H % 16 == 0)
     const int row = tv[tl] ? n0 + 16 * tl + r : n0 + r;
     dc[tl] = base + p.off_dc + (size_t)row * crow;
-    ds[tl] = base + p.off_ds + (size_t)row * srow;
+    ds[tl] = FULL ? wscale + (row - nb * 256) * sstr : base + p.off_ds + (size_t)row * srow;
   }
   for (int cb = p0; cb < p1; cb += 16) {
     const int pc = cb + r;
@@ -946,7 +1005,6 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
     build_tiles<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, items,
                                         reinterpret_cast<uint32_t*>(zero));
-    if (!record_stage(ev, 1, stream)) return MOE_EHIP;
     PipeArgs t;
     t.act = a->xq;
     t.arow = mxfp4_row_bytes(H);
@@ -968,8 +1026,8 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     t.k = k;
     t.A = A;
     t.nN = (I + 127) / 128;
-    gateup_pipe<<<(unsigned)g1, 256, 0, stream>>>(t);
-    if (!record_stage(ev, 2, stream)) return MOE_EHIP;
+    hipExtLaunchKernelGGL(gateup_pipe, dim3((unsigned)g1), dim3(256), 0, stream,
+                          ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, 0, t);
     t.act = hq;
     t.arow = t.hrow;
     t.off_c0 = L.off[4];
@@ -985,7 +1043,6 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     const bool prebuilt = S > kInlineWorklistMaxS;
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
     if (prebuilt) build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
-    if (!record_stage(ev, 1, stream)) return MOE_EHIP;
     GateUpArgs g;
     g.xq = a->xq;
     g.xrow = mxfp4_row_bytes(H);
@@ -1007,11 +1064,13 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     g.A = A;
     g.S = S;
     const int gblocks = maxU * ((I + 127) / 128);
-    if (H % 512 == 0)
-      gateup_kernel<true><<<gblocks, 256, 0, stream>>>(g);
+    hipEvent_t gu0 = ev ? ev[1] : nullptr, gu1 = ev ? ev[2] : nullptr;
+    if (staged_ok(H))
+      hipExtLaunchKernelGGL(gateup_kernel<true>, dim3(gblocks), dim3(256),
+                            2 * 128 * staged_scale_stride(H), stream, gu0, gu1, 0, g);
     else
-      gateup_kernel<false><<<gblocks, 256, 0, stream>>>(g);
-    if (!record_stage(ev, 2, stream)) return MOE_EHIP;
+      hipExtLaunchKernelGGL(gateup_kernel<false>, dim3(gblocks), dim3(256), 0, stream, gu0, gu1,
+                            0, g);
     DownArgs d;
     d.hq = hq;
     d.hrow = g.hrow;
@@ -1028,8 +1087,8 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     d.A = A;
     d.S = S;
     const int dblocks = maxU * ((H + 255) / 256);
-    if (I % 512 == 0)
-      down_kernel<true><<<dblocks, 256, 0, stream>>>(d);
+    if (staged_ok(I))
+      down_kernel<true><<<dblocks, 256, 256 * staged_scale_stride(I), stream>>>(d);
     else
       down_kernel<false><<<dblocks, 256, 0, stream>>>(d);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;

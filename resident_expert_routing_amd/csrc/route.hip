@@ -10,13 +10,11 @@
 
 namespace moe {
 
-constexpr int kFusedMaxT = 16;   // at or below: selection + bucketing in one workgroup
-
 // ---------------------------------------------------------------------------
-// Router logits in float64.  Definition shared by both kernels below:
-//   S_c = fma chain over h in chunk c (32 wide), ascending, starting from 0
-//   z   = S_0 + S_1 + ... (ascending c, starting from 0); bias added later.
-// Both kernels compute bit-identical values for a (t, e) whatever T is.
+// Router logits in float64 (every bf16 x fp32 product is exact).  Two regimes,
+// each with one fixed summation order, so within a regime a token's z does
+// not depend on the rest of its batch: router_small_f64 (chunk chains, then
+// runs of chunk sums) and router_full_f64 (the float64 matrix instruction).
 // ---------------------------------------------------------------------------
 
 // MXFP4 activation rows, one element per thread: each aligned group of 32
@@ -49,16 +47,21 @@ __device__ void quantize_x_elements(const uint16_t* __restrict__ x, int T, int H
 
 // Small T (decode batches): a workgroup owns one expert and up to RS_T tokens;
 // thread c owns chunk c for all of them (the router chunk is loaded once, RS_T
-// independent fma chains); the chunk sums meet in LDS and are added in
-// ascending chunk order.  Workgroups from `nrb` on encode the activation rows
-// instead (one element per thread), alongside the dot products.
+// independent fma chains); the chunk sums meet in LDS.  They are added in runs
+// of RS_RUN consecutive chunks (ascending, from 0), and the run sums in
+// ascending order (from 0).  Workgroups from `nrb` on encode the activation
+// rows instead (one element per thread), alongside the dot products.
+// Workgroup 0 also zeroes `counter` (nullable) for the selection kernel that
+// follows.
 constexpr int RS_T = 8;
 constexpr int RS_MAX_CHUNKS = 256;
+constexpr int RS_RUN = 16;
 __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restrict__ x,
                                                         const float* __restrict__ w, int T, int H,
                                                         int E, double* __restrict__ z,
                                                         uint8_t* __restrict__ xq, size_t xq_row,
-                                                        int nrb) {
+                                                        int nrb, uint32_t* __restrict__ counter) {
+  if (counter && blockIdx.x == 0 && threadIdx.x == 0) *counter = 0u;
   if ((int)blockIdx.x >= nrb) {
     quantize_x_elements(x, T, H, xq, xq_row, (size_t)(blockIdx.x - nrb) * 256 + threadIdx.x,
                         (size_t)(gridDim.x - nrb) * 256);
@@ -100,9 +103,22 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
     }
   }
   __syncthreads();
+  // thread (token i, run q) adds the chunk sums of run q
+  __shared__ double runs[RS_T][RS_MAX_CHUNKS / RS_RUN];
+  const int nrun = (nchunk + RS_RUN - 1) / RS_RUN;
+  {
+    const int i = c / nrun, q = c % nrun;
+    if (i < nt) {
+      double acc = 0.0;
+      const int c1 = min(nchunk, (q + 1) * RS_RUN);
+      for (int cc = q * RS_RUN; cc < c1; ++cc) acc += part[i][cc];
+      runs[i][q] = acc;
+    }
+  }
+  __syncthreads();
   if (c < nt) {
     double acc = 0.0;
-    for (int cc = 0; cc < nchunk; ++cc) acc += part[c][cc];
+    for (int q = 0; q < nrun; ++q) acc += runs[c][q];
     z[(size_t)(t0 + c) * E + e] = acc;
   }
 }
@@ -200,89 +216,158 @@ __device__ __forceinline__ uint64_t order_key(double z) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Top-k selection by radix select over the 64-bit keys with wave ballots.
-// It selects (bit i = expert lane+64i) the min(want, #allowed) allowed experts
-// with the largest z, ties to the lower expert id: bit by bit from the top,
-// keep the branch that holds the want-th largest key, stopping as soon as the
-// keys matching the prefix are exactly the ones still needed; keys above the
-// prefix are taken, and keys equal to it fill the rest in ascending expert id.
-struct RadixSel {
-  uint64_t prefix, mask;
-  int remaining, match, total, n;
-  uint32_t allowed;
-  bool done;
+// Top-k selection: the min(want, #allowed) allowed experts with the largest
+// key, ties to the lower expert id (bit i of a lane's masks = expert
+// lane+64i).  Each lane first sorts its allowed experts (key descending, ties
+// to the lower i); a round then takes the wave maximum of the upper key words
+// of the lanes' list heads, and the lane holding the winner drops its head.
+// Only when several heads share that maximum are the lower words compared,
+// and only when full keys tie does the lowest id decide (a lane's equal keys
+// are already in id order, so the lowest id is always a head).
+// The unrestricted and the masked selection share the rounds, so their two
+// reductions overlap.
+template <int NPER>
+struct LaneList {
+  uint32_t hi[NPER], lo[NPER];
+  int idx[NPER];
+  bool ok[NPER];
+  int n;  // allowed experts of this lane not yet taken; entry 0 is the head
+};
+
+// Compare-exchange of entries A < B, placing first the one that goes first
+// (FIRST_FIRST) or last: an allowed entry before a disallowed one, then the
+// larger key, then the lower i.
+template <int A, int B, bool FIRST_FIRST, int NPER>
+__device__ __forceinline__ void lane_ce(LaneList<NPER>& L) {
+  const uint64_t ka = ((uint64_t)L.hi[A] << 32) | L.lo[A];
+  const uint64_t kb = ((uint64_t)L.hi[B] << 32) | L.lo[B];
+  const bool a_first =
+      (L.ok[A] != L.ok[B]) ? L.ok[A] : (ka != kb ? ka > kb : L.idx[A] < L.idx[B]);
+  const bool sw = FIRST_FIRST ? !a_first : a_first;
+  const uint32_t ha = L.hi[A], la = L.lo[A];
+  const int ia = L.idx[A];
+  const bool oa = L.ok[A];
+  L.hi[A] = sw ? L.hi[B] : ha;
+  L.lo[A] = sw ? L.lo[B] : la;
+  L.idx[A] = sw ? L.idx[B] : ia;
+  L.ok[A] = sw ? L.ok[B] : oa;
+  L.hi[B] = sw ? ha : L.hi[B];
+  L.lo[B] = sw ? la : L.lo[B];
+  L.idx[B] = sw ? ia : L.idx[B];
+  L.ok[B] = sw ? oa : L.ok[B];
+}
+
+// Bitonic sorting network over the NPER entries, generated at compile time
+// so that every index is a constant (the lists stay in registers).
+template <int NPER, int KK, int JJ, int A>
+struct BitonicPass {
+  __device__ static __forceinline__ void run(LaneList<NPER>& L) {
+    if constexpr ((A ^ JJ) > A) lane_ce<A, (A ^ JJ), (A & KK) == 0, NPER>(L);
+    if constexpr (A + 1 < NPER) BitonicPass<NPER, KK, JJ, A + 1>::run(L);
+  }
+};
+
+template <int NPER, int KK, int JJ>
+struct BitonicMerge {
+  __device__ static __forceinline__ void run(LaneList<NPER>& L) {
+    BitonicPass<NPER, KK, JJ, 0>::run(L);
+    if constexpr (JJ > 1) BitonicMerge<NPER, KK, JJ / 2>::run(L);
+  }
+};
+
+template <int NPER, int KK>
+struct BitonicSort {
+  __device__ static __forceinline__ void run(LaneList<NPER>& L) {
+    BitonicMerge<NPER, KK, KK / 2>::run(L);
+    if constexpr (KK < NPER) BitonicSort<NPER, KK * 2>::run(L);
+  }
 };
 
 template <int NPER>
-__device__ __forceinline__ void radix_init(RadixSel& s, uint32_t allowed, int want) {
-  s.allowed = allowed;
+__device__ __forceinline__ void build_list(const uint64_t* key, uint32_t allowed,
+                                           LaneList<NPER>& L) {
+  L.n = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    L.ok[i] = (allowed >> i) & 1u;
+    L.hi[i] = (uint32_t)(key[i] >> 32);
+    L.lo[i] = (uint32_t)key[i];
+    L.idx[i] = i;
+    L.n += L.ok[i] ? 1 : 0;
+  }
+  BitonicSort<NPER, 2>::run(L);
+}
+
+template <int NPER>
+__device__ __forceinline__ uint32_t head_hi(const LaneList<NPER>& L) {
+  return L.n > 0 ? L.hi[0] : 0u;
+}
+
+// The winner among the heads whose upper word is `best` leaves its list (the
+// lists shift down; all indices are static, so they stay in registers).
+template <int NPER>
+__device__ __forceinline__ void take_head(LaneList<NPER>& L, uint32_t best, uint32_t& sel) {
+  const int lane = threadIdx.x & 63;
+  bool hit = L.n > 0 && L.hi[0] == best;
+  uint64_t b = __ballot(hit);
+  int winner;
+  if (__popcll(b) == 1) {
+    winner = __builtin_ctzll(b);
+  } else {  // uniform; ties in the upper word are rare
+    // (the reductions run in every lane: never under a short-circuit)
+    const uint32_t l = hit ? L.lo[0] : 0u;
+    const uint32_t lb = wave_umax32(l);
+    hit = hit && l == lb;
+    b = __ballot(hit);
+    if (__popcll(b) == 1) {
+      winner = __builtin_ctzll(b);
+    } else {  // equal keys: the lowest expert id (the maximum of ~id)
+      const uint32_t ne = hit ? ~(uint32_t)(lane + 64 * L.idx[0]) : 0u;
+      const uint32_t nmax = wave_umax32(ne);
+      winner = (int)(~nmax & 63u);
+    }
+  }
+  const bool won = lane == winner;
+  sel |= won ? 1u << L.idx[0] : 0u;
+#pragma unroll
+  for (int i = 0; i + 1 < NPER; ++i) {
+    L.hi[i] = won ? L.hi[i + 1] : L.hi[i];
+    L.lo[i] = won ? L.lo[i + 1] : L.lo[i];
+    L.idx[i] = won ? L.idx[i + 1] : L.idx[i];
+  }
+  L.n -= won ? 1 : 0;
+}
+
+template <int NPER>
+__device__ __forceinline__ int count_allowed(uint32_t allowed) {
   int total = 0;
 #pragma unroll
   for (int i = 0; i < NPER; ++i) total += __popcll(__ballot((allowed >> i) & 1u));
-  s.total = total;
-  s.n = min(want, total);
-  s.prefix = 0;
-  s.mask = 0;
-  s.remaining = s.n;
-  s.match = total;
-  s.done = s.n == 0 || s.n == total;
+  return total;
 }
 
-template <int NPER>
-__device__ __forceinline__ void radix_step(RadixSel& s, const uint64_t* key, int b) {
-  const uint64_t bit = 1ull << b;
-  int c1 = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const bool m = ((s.allowed >> i) & 1u) && ((key[i] & s.mask) == s.prefix) && (key[i] & bit);
-    c1 += __popcll(__ballot(m));
-  }
-  if (c1 >= s.remaining) {
-    s.prefix |= bit;
-    s.match = c1;
-  } else {
-    s.remaining -= c1;
-    s.match -= c1;
-  }
-  s.mask |= bit;
-  if (s.match == s.remaining) s.done = true;
-}
-
-template <int NPER>
-__device__ __forceinline__ uint32_t radix_finish(const RadixSel& s, const uint64_t* key) {
-  if (s.n == 0) return 0u;
-  if (s.n == s.total) return s.allowed;
-  const uint64_t lt = lanemask_lt();
-  uint32_t sel = 0;
-  int before = 0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const bool a = (s.allowed >> i) & 1u;
-    const uint64_t hi = key[i] & s.mask;
-    const bool eq = a && hi == s.prefix;
-    const uint64_t meq = __ballot(eq);
-    const int rank = before + __popcll(meq & lt);
-    before += __popcll(meq);
-    if (a && (hi > s.prefix || (eq && rank < s.remaining))) sel |= 1u << i;
-  }
-  return sel;
-}
-
-// The unrestricted and the masked selection together, their bit steps
-// interleaved in one loop so the two independent chains of ballots overlap.
+// do_u / do_m (uniform): which of the two selections to make.
 template <int NPER>
 __device__ void wave_select_pair(const uint64_t* key, uint32_t allow_u, uint32_t allow_m, int want,
-                                 uint32_t& sel_u, uint32_t& sel_m, int& got_m) {
-  RadixSel u, m;
-  radix_init<NPER>(u, allow_u, want);
-  radix_init<NPER>(m, allow_m, want);
-  for (int b = 63; b >= 0 && !(u.done && m.done); --b) {
-    if (!u.done) radix_step<NPER>(u, key, b);
-    if (!m.done) radix_step<NPER>(m, key, b);
+                                 bool do_u, bool do_m, uint32_t& sel_u, uint32_t& sel_m,
+                                 int& got_m) {
+  LaneList<NPER> U, M;
+  U.n = 0;
+  M.n = 0;
+  if (do_u) build_list<NPER>(key, allow_u, U);
+  if (do_m) build_list<NPER>(key, allow_m, M);
+  const int nu = do_u ? min(want, count_allowed<NPER>(allow_u)) : 0;
+  const int nm = do_m ? min(want, count_allowed<NPER>(allow_m)) : 0;
+  sel_u = 0u;
+  sel_m = 0u;
+  const int rounds = max(nu, nm);
+  for (int j = 0; j < rounds; ++j) {
+    uint32_t bu = head_hi<NPER>(U), bm = head_hi<NPER>(M);
+    wave_umax32x2(bu, bm);
+    if (j < nu) take_head<NPER>(U, bu, sel_u);
+    if (j < nm) take_head<NPER>(M, bm, sel_m);
   }
-  sel_u = radix_finish<NPER>(u, key);
-  sel_m = radix_finish<NPER>(m, key);
-  got_m = m.n;
+  got_m = nm;
 }
 
 // Position of each selected expert in ascending-id order.
@@ -318,14 +403,87 @@ struct SelectArgs {
   float* delta;
 };
 
-// One wave: everything per token t.  If sl is non-null the token's k slot
-// picks are also written there (sl[j], padded with -1), and if te is non-null
-// its demand picks and scores (te[j], ts[j]).
+// Routed picks of token t (bit i of msel: expert lane+64i), in ascending id,
+// with weights renormalised over them; positions past `got` are padding.
 template <int NPER>
-__device__ void select_token(const SelectArgs& p, int t, int* sl, int* te = nullptr,
-                             float* ts = nullptr) {
+__device__ __forceinline__ void select_write_routed(const SelectArgs& p, int t, uint32_t msel,
+                                                    int got, const double* ex, double denom,
+                                                    const int* slot_of) {
   const int lane = threadIdx.x & 63;
-  const int E = p.E, k = p.k, H = p.H;
+  const int k = p.k, nper = (p.E + 63) / 64;
+  int pos[NPER];
+  selected_positions<NPER>(msel, nper, pos);
+  double psel = 0.0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i)
+    if (i < nper && ((msel >> i) & 1u)) psel += ex[i] / denom;
+  const double wsum = wave_sum(psel);
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    if (i < nper && ((msel >> i) & 1u)) {
+      const size_t o = (size_t)t * k + pos[i];
+      p.sel_expert[o] = lane + 64 * i;
+      p.sel_weight[o] = (float)((ex[i] / denom) / wsum);
+      p.sel_slot[o] = slot_of[i];
+    }
+  }
+  for (int j = got + lane; j < k; j += 64) {
+    const size_t o = (size_t)t * k + j;
+    p.sel_expert[o] = -1;
+    p.sel_weight[o] = 0.f;
+    p.sel_slot[o] = -1;
+  }
+}
+
+// MXFP4 activation row of token t (when p.quantize_x): lane per 32-block.
+__device__ __forceinline__ void quantize_row(const SelectArgs& p, int t) {
+  if (!p.quantize_x) return;
+  const int lane = threadIdx.x & 63;
+  const int H = p.H;
+  const int nblk = H / 32;
+  const uint16_t* xr = p.x + (size_t)t * H;
+  uint8_t* qr = p.xq + (size_t)t * p.xq_row;
+  for (int b = lane; b < nblk; b += 64) {
+    const uint4* src = reinterpret_cast<const uint4*>(xr + b * 32);
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 u = src[q];
+      const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[q * 8 + r * 2 + 0] = bf16_to_f32(wds[r] & 0xFFFFu);
+        v[q * 8 + r * 2 + 1] = bf16_to_f32(wds[r] >> 16);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    uint32_t words[4] = {0u, 0u, 0u, 0u};
+    uint32_t scale = 0u;
+    if (amax > 0.f) {
+      const int e = mx_block_exp(amax);
+      scale = (uint32_t)(e + 127);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) words[i >> 3] |= e2m1_code(v[i], e) << (4 * (i & 7));
+    }
+    *reinterpret_cast<uint4*>(qr + (size_t)b * 16) =
+        make_uint4(words[0], words[1], words[2], words[3]);
+    qr[H / 2 + b] = (uint8_t)scale;
+  }
+}
+
+// What one wave does for its token: the demand picks (unrestricted top-k
+// and scores), the routed picks (masked top-k, renormalised weights, slots),
+// or both.  Each selection is a serial chain of rounds, so two waves that
+// split them finish sooner than one wave doing both.
+constexpr int kSelDemand = 1, kSelRouted = 2, kSelBoth = 3;
+
+// One wave, token t.  Activation rows are encoded too when p.quantize_x.
+template <int NPER>
+__device__ void select_token(const SelectArgs& p, int t, int role) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.E, k = p.k;
   const int nper = (E + 63) / 64;
 
   // ---- logits plus bias ----
@@ -366,94 +524,35 @@ __device__ void select_token(const SelectArgs& p, int t, int* sl, int* te = null
   }
   const double denom = wave_sum(lsum);
 
-  // ---- unrestricted top-k (demand picks) ----
+  // ---- selections: demand picks (all experts), routed picks (routable) ----
   uint64_t key[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) key[i] = order_key(z[i] + 0.0);  // -0 and +0 tie
+  const bool do_u = role & kSelDemand, do_m = role & kSelRouted;
   uint32_t usel = 0, msel = 0;
   int got = 0;
-  wave_select_pair<NPER>(key, valid, routable, k, usel, msel, got);
+  wave_select_pair<NPER>(key, valid, routable, k, do_u, do_m, usel, msel, got);
   int pos[NPER];
-  selected_positions<NPER>(usel, nper, pos);
+  if (do_u) {
+    selected_positions<NPER>(usel, nper, pos);
 #pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    if (i < nper && ((usel >> i) & 1u)) {
-      const size_t o = (size_t)t * k + pos[i];
-      const float score = (float)(ex[i] / denom);
-      p.topk_expert[o] = lane + 64 * i;
-      p.topk_score[o] = score;
-      if (te) {
-        te[pos[i]] = lane + 64 * i;
-        ts[pos[i]] = score;
+    for (int i = 0; i < NPER; ++i) {
+      if (i < nper && ((usel >> i) & 1u)) {
+        const size_t o = (size_t)t * k + pos[i];
+        p.topk_expert[o] = lane + 64 * i;
+        p.topk_score[o] = (float)(ex[i] / denom);
       }
     }
   }
-
-  // ---- masked top-k over routable experts (selected above), renormalised ----
-  selected_positions<NPER>(msel, nper, pos);
-  double psel = 0.0;
-#pragma unroll
-  for (int i = 0; i < NPER; ++i)
-    if (i < nper && ((msel >> i) & 1u)) psel += ex[i] / denom;
-  const double wsum = wave_sum(psel);
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    if (i < nper && ((msel >> i) & 1u)) {
-      const size_t o = (size_t)t * k + pos[i];
-      p.sel_expert[o] = lane + 64 * i;
-      p.sel_weight[o] = (float)((ex[i] / denom) / wsum);
-      p.sel_slot[o] = slot_of[i];
-      if (sl) sl[pos[i]] = slot_of[i];
-    }
-  }
-  for (int j = got + lane; j < k; j += 64) {
-    const size_t o = (size_t)t * k + j;
-    p.sel_expert[o] = -1;
-    p.sel_weight[o] = 0.f;
-    p.sel_slot[o] = -1;
-    if (sl) sl[j] = -1;
-  }
-
-  // ---- MXFP4 activation row: lane per 32-block ----
-  if (!p.quantize_x) return;
-  const int nblk = H / 32;
-  const uint16_t* xr = p.x + (size_t)t * H;
-  uint8_t* qr = p.xq + (size_t)t * p.xq_row;
-  for (int b = lane; b < nblk; b += 64) {
-    const uint4* src = reinterpret_cast<const uint4*>(xr + b * 32);
-    float v[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 u = src[q];
-      const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[q * 8 + r * 2 + 0] = bf16_to_f32(wds[r] & 0xFFFFu);
-        v[q * 8 + r * 2 + 1] = bf16_to_f32(wds[r] >> 16);
-      }
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    uint32_t words[4] = {0u, 0u, 0u, 0u};
-    uint32_t scale = 0u;
-    if (amax > 0.f) {
-      const int e = mx_block_exp(amax);
-      scale = (uint32_t)(e + 127);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) words[i >> 3] |= e2m1_code(v[i], e) << (4 * (i & 7));
-    }
-    *reinterpret_cast<uint4*>(qr + (size_t)b * 16) =
-        make_uint4(words[0], words[1], words[2], words[3]);
-    qr[H / 2 + b] = (uint8_t)scale;
-  }
+  if (do_m) select_write_routed<NPER>(p, t, msel, got, ex, denom, slot_of);
+  if (role & kSelRouted) quantize_row(p, t);
 }
 
 template <int NPER>
 __global__ __launch_bounds__(256) void route_select(SelectArgs p) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= p.T) return;  // wave-uniform
-  select_token<NPER>(p, t, nullptr);
+  select_token<NPER>(p, t, kSelBoth);
 }
 
 // ---------------------------------------------------------------------------
@@ -461,102 +560,120 @@ __global__ __launch_bounds__(256) void route_select(SelectArgs p) {
 // (ascending assignment index within a slot).
 // ---------------------------------------------------------------------------
 
-// Workgroup of 1024 threads: cnt[0..S) holds counts on entry and exclusive
-// offsets on return; offsets[0..S] are written to global memory.  Returns the
-// total.
-__device__ int wg_offsets_from_counts(int* cnt, int S, int32_t* __restrict__ offsets,
-                                      int* wsum) {
-  const int tid = threadIdx.x;
-  const int per = (S + 1023) / 1024;
-  const int lo = min(S, tid * per), hi = min(S, lo + per);
-  int local = 0;
-  for (int s = lo; s < hi; ++s) local += cnt[s];
-  const int lane = tid & 63, wv = tid >> 6;
-  int incl = local;
+// Batches of up to kFusedMaxT tokens (E <= 256, small-T router): selection,
+// demand and bucketing in one launch.  Workgroup b selects tokens 2b and
+// 2b+1, two waves each (one per SIMD): one for the demand picks, one for the
+// routed picks.  Each workgroup then counts itself done on a
+// counter that the router kernel of the same call set to zero; the last one
+// reads every token's picks back and does the demand update and the
+// bucketing alone.  Both bucket picks with 64-bit token masks -- demand picks
+// by expert, routed picks by slot (a token picks an expert, and a slot, at
+// most once) -- so a pick's rank in its bucket is the number of earlier
+// tokens in the mask.  Expert e's demand: its bucket of scores added in
+// ascending token order -- the float64 additions of moe_demand_accumulate.
+constexpr int kFusedMaxT = 64;
+constexpr int kFusedWgTokens = 2;
+constexpr int kFusedMaxA = kFusedMaxT * MOE_MAX_K;
+
+// Exclusive scan over the workgroup's 256 threads (one value each); `part`
+// holds 4 ints of LDS.  Returns the thread's offset; *total gets the sum.
+// Ends with a barrier.
+__device__ __forceinline__ int wg256_exclusive_scan(int v, int* part, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int incl = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int o = __shfl_up(incl, d, kWave);
     if (lane >= d) incl += o;
   }
-  if (lane == 63) wsum[wv] = incl;
+  if (lane == 63) part[wv] = incl;
   __syncthreads();
-  int run = incl - local;
-  for (int i = 0; i < wv; ++i) run += wsum[i];
-  for (int s = lo; s < hi; ++s) {
-    const int c = cnt[s];
-    offsets[s] = run;
-    cnt[s] = run;
-    run += c;
-  }
-  int total = 0;
-  for (int i = 0; i < 16; ++i) total += wsum[i];
-  if (tid == 0) offsets[S] = total;
+  int run = incl - v;
+  for (int i = 0; i < wv; ++i) run += part[i];
+  *total = part[0] + part[1] + part[2] + part[3];
   __syncthreads();
-  return total;
+  return run;
 }
 
-// Small batches (E <= 256): selection for every token (wave t), demand (if
-// asked) and bucketing, in one workgroup of 1024 threads -- one compute unit,
-// so the waves meet at workgroup barriers with no device-wide fence.
-__global__ __launch_bounds__(1024) void route_fused_small(SelectArgs p,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ perm) {
-  constexpr int kMaxA = kFusedMaxT * MOE_MAX_K;
-  __shared__ int cnt[MOE_MAX_S];
-  __shared__ int4 sl4[kMaxA / 4];
-  __shared__ int4 te4[kMaxA / 4];
-  __shared__ float4 ts4[kMaxA / 4];
-  __shared__ int wsum[16];
-  int* sl = reinterpret_cast<int*>(sl4);
-  int* te = reinterpret_cast<int*>(te4);
-  float* ts = reinterpret_cast<float*>(ts4);
-  const int tid = threadIdx.x, wv = tid >> 6;
-  const int S = p.S, A = p.T * p.k;
-  const int A4 = (A + 3) / 4;
-  for (int s = tid; s < S; s += 1024) cnt[s] = 0;
-  for (int a = A + tid; a < 4 * A4; a += 1024) {  // pad the last vector
-    sl[a] = -1;
-    te[a] = -1;
-    ts[a] = 0.f;
-  }
-  if (wv < p.T) select_token<4>(p, wv, sl + wv * p.k, te + wv * p.k, ts + wv * p.k);
+__global__ __launch_bounds__(256) void route_fused(SelectArgs p, uint32_t* __restrict__ counter,
+                                                   int32_t* __restrict__ offsets,
+                                                   int32_t* __restrict__ perm) {
+  __shared__ unsigned long long smask[MOE_MAX_S];  // tokens routed to slot s
+  __shared__ unsigned long long emask[256];        // tokens with a demand pick of expert e
+  __shared__ int off[MOE_MAX_S];                   // first perm position of slot s
+  __shared__ int eoff[256];                        // first bucket position of expert e
+  __shared__ int te[kFusedMaxA];
+  __shared__ float ts[kFusedMaxA];
+  __shared__ int sl[kFusedMaxA];
+  __shared__ float elist[kFusedMaxA];  // demand scores bucketed by expert
+  __shared__ int part[2][4];
+  __shared__ int last;
+  const int tid = threadIdx.x;
+  const int T = p.T, k = p.k, E = p.E, S = p.S, A = T * k;
+  double h_old = 0.0;
+  if (p.hist && tid < E) h_old = p.hist[tid];  // used only by the last workgroup
+  // waves 2j and 2j+1: demand and routed picks of token kFusedWgTokens*b + j
+  const int t = blockIdx.x * kFusedWgTokens + (tid >> 7);
+  if (t < T) select_token<4>(p, t, (tid >> 6) & 1 ? kSelRouted : kSelDemand);
+  __threadfence();  // this workgroup's picks, visible device-wide before it counts itself
   __syncthreads();
-  if (p.hist) {
-    // picks in ascending order (token, then pick): the order of float64
-    // additions of moe_demand_accumulate for one chunk of tokens
-    for (int e = tid; e < p.E; e += 1024) {
-      double acc = 0.0;
-      for (int q = 0; q < A4; ++q) {
-        const int4 ev = te4[q];
-        const float4 sv = ts4[q];
-        if (ev.x == e) acc += (double)sv.x;
-        if (ev.y == e) acc += (double)sv.y;
-        if (ev.z == e) acc += (double)sv.z;
-        if (ev.w == e) acc += (double)sv.w;
-      }
-      p.hist[e] += acc;
-      if (p.delta) p.delta[e] = (float)acc;
-    }
+  if (tid == 0) last = atomicAdd(counter, 1u) == gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();  // every other workgroup's picks
+
+  for (int a = tid; a < A; a += 256) {
+    te[a] = p.topk_expert[a];
+    ts[a] = p.topk_score[a];
+    sl[a] = p.sel_slot[a];
   }
-  for (int a = tid; a < A; a += 1024) {
-    const int s = sl[a];
-    if (s >= 0 && s < S) atomicAdd(&cnt[s], 1);
+  for (int s = tid; s < S; s += 256) smask[s] = 0ull;
+  emask[tid] = 0ull;
+  __syncthreads();
+  for (int a = tid; a < A; a += 256) {
+    const unsigned long long bit = 1ull << (a / k);
+    const int e = te[a], s = sl[a];
+    if (e >= 0 && e < E) atomicOr(&emask[e], bit);
+    if (s >= 0 && s < S) atomicOr(&smask[s], bit);
   }
   __syncthreads();
-  const int total = wg_offsets_from_counts(cnt, S, offsets, wsum);
-  for (int a = tid; a < A; a += 1024) {
-    const int s = sl[a];
-    if (s >= 0 && s < S) {
-      int rank = 0;
-      for (int q = 0; q < a / 4; ++q) {
-        const int4 v = sl4[q];
-        rank += (v.x == s) + (v.y == s) + (v.z == s) + (v.w == s);
-      }
-      for (int b = a & ~3; b < a; ++b) rank += sl[b] == s;
-      perm[cnt[s] + rank] = a;
-    }
+
+  // ---- bucket offsets: experts one per thread, slots a range per thread ----
+  int etot;
+  const int ecount = tid < E ? __popcll(emask[tid]) : 0;
+  eoff[tid] = wg256_exclusive_scan(ecount, part[0], &etot);
+  const int per = (S + 255) / 256;
+  const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int local = 0;
+  for (int s = lo; s < hi; ++s) local += __popcll(smask[s]);
+  int total;
+  int run = wg256_exclusive_scan(local, part[1], &total);
+  for (int s = lo; s < hi; ++s) {
+    off[s] = run;
+    offsets[s] = run;
+    run += __popcll(smask[s]);
   }
-  for (int a = total + tid; a < A; a += 1024) perm[a] = -1;
+  if (tid == 0) offsets[S] = total;
+  __syncthreads();
+
+  // ---- place: demand scores by expert, assignments by slot ----
+  for (int a = tid; a < A; a += 256) {
+    const unsigned long long before = (1ull << (a / k)) - 1ull;
+    const int e = te[a], s = sl[a];
+    if (e >= 0 && e < E) elist[eoff[e] + __popcll(emask[e] & before)] = ts[a];
+    if (s >= 0 && s < S) perm[off[s] + __popcll(smask[s] & before)] = a;
+  }
+  for (int a = total + tid; a < A; a += 256) perm[a] = -1;
+  __syncthreads();
+
+  // ---- demand ----
+  if (p.hist && tid < E) {
+    double acc = 0.0;
+    const int b0 = eoff[tid];
+    for (int q = 0; q < ecount; ++q) acc += (double)elist[b0 + q];
+    p.hist[tid] = h_old + acc;
+    if (p.delta) p.delta[tid] = (float)acc;
+  }
 }
 
 // Bucketing for larger batches, stable by (slot, assignment).  The k picks of
@@ -759,13 +876,19 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   const int nchunk = H / kRouterChunk;
   const size_t xq_row = mxfp4_row_bytes(H);
   const bool small_router = T <= kSplitRouterMaxT && nchunk <= RS_MAX_CHUNKS;
+  // the fused kernel's completion counter: the first word of the bucket-count
+  // area, which that path does not use otherwise
+  const bool fused = small_router && T <= kFusedMaxT && E <= 256;
+  uint32_t* counter = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a->ws) +
+                                                  route_z_bytes(T, E) +
+                                                  moe_demand_ws_bytes_internal(T, E));
   if (!record_stage(ev,0, stream)) return MOE_EHIP;
   if (small_router) {
     const int nrb = E * ((T + RS_T - 1) / RS_T);
     const size_t nx = ((size_t)T * H + 255) / 256;
     const int nxb = (int)(nx < 1024 ? nx : 1024);
     router_small_f64<<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, a->xq, xq_row,
-                                                    nrb);
+                                                    nrb, fused ? counter : nullptr);
   } else {
     dim3 grid((E + RM_E - 1) / RM_E, (T + RM_T - 1) / RM_T);
     router_full_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z);
@@ -792,12 +915,13 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   p.hist = nullptr;
   p.delta = nullptr;
   const int A = T * k;
-  if (T <= kFusedMaxT && E <= 256 && small_router) {
+  if (fused) {
     // selection, demand and bucketing in one kernel; the remaining stage
     // events are recorded back to back
     p.hist = a->hist_row;
     p.delta = a->delta;
-    route_fused_small<<<1, 1024, 0, stream>>>(p, a->slot_offsets, a->perm);
+    route_fused<<<(T + kFusedWgTokens - 1) / kFusedWgTokens, 256, 0, stream>>>(
+        p, counter, a->slot_offsets, a->perm);
     for (int i = 2; i <= 4; ++i)
       if (!record_stage(ev,i, stream)) return MOE_EHIP;
     return hip_status();

@@ -211,9 +211,12 @@ def test_route_worked_example_ties():
     (70, 40, 6, 3, 3, 96),       # fewer routable than k: padding; H not a multiple of 128
     (65, 16, 4, 16, 16, 256),    # all resident, T just above the split-router limit
     (5, 1024, 32, 700, 8192, 64),  # maximum E, k and S
-    (9, 200, 8, 150, 8192, 128),   # one-workgroup selection + bucketing with the maximum S
-    (16, 256, 8, 230, 230, 4096),  # largest batch of the one-workgroup path
-    (17, 256, 8, 230, 230, 4096),  # smallest batch of the multi-kernel path
+    (9, 200, 8, 150, 8192, 128),   # fused selection + bucketing with the maximum S
+    (16, 256, 8, 230, 230, 4096),  # four selection workgroups
+    (17, 256, 8, 230, 230, 4096),  # a partly filled last selection workgroup
+    (64, 256, 8, 230, 230, 4096),  # largest batch of the fused path
+    (64, 256, 32, 250, 8192, 512),  # fused path: most assignments, maximum S
+    (65, 256, 8, 230, 230, 4096),  # smallest batch of the multi-kernel path
 ])
 def test_route_edge_shapes(T, E, k, nr, S, H):
     say(f"moe_route edge T={T} E={E} k={k} routable={nr} S={S} H={H}")
