@@ -585,11 +585,11 @@ constexpr int kZeroPage = 256;                 // zeroed workspace bytes absent 
 // 2 weight-scale and 1 activation-scale loads.
 constexpr int kLoadsPerStage = 15;
 
-// Work list of M-tiles: items[0] = count, then per item (slot, first row of
-// the tile within the slot, index of the slot's first item, the slot's item
-// count), slots ascending.  Also clears the zero page.
+// Work list of M-tiles of tm rows: items[0] = count, then per item (slot,
+// first row of the tile within the slot, index of the slot's first item, the
+// slot's item count), slots ascending.  Also clears the zero page.
 __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int S,
-                                                    int A, int32_t* __restrict__ items,
+                                                    int A, int tm, int32_t* __restrict__ items,
                                                     uint32_t* __restrict__ zero_page) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -599,7 +599,7 @@ __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ 
   int local = 0;
   for (int s = lo; s < hi; ++s) {
     const int a = offsets[s], b = offsets[s + 1];
-    if (b > a && a >= 0 && b <= A) local += (b - a + kTileM - 1) / kTileM;
+    if (b > a && a >= 0 && b <= A) local += (b - a + tm - 1) / tm;
   }
   int incl = local;
 #pragma unroll
@@ -614,11 +614,11 @@ __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ 
   for (int s = lo; s < hi; ++s) {
     const int a = offsets[s], b = offsets[s + 1];
     if (b > a && a >= 0 && b <= A) {
-      const int first = run, cnt = (b - a + kTileM - 1) / kTileM;
+      const int first = run, cnt = (b - a + tm - 1) / tm;
       for (int m = 0; m < cnt; ++m) {
         int32_t* it = items + 1 + 4 * run;
         it[0] = s;
-        it[1] = m * kTileM;
+        it[1] = m * tm;
         it[2] = first;
         it[3] = cnt;
         ++run;
@@ -648,7 +648,7 @@ struct TileRef {
   int slot, p0, rows, nt;
 };
 
-__device__ __forceinline__ bool tile_of(int w, int nN, const int32_t* __restrict__ items,
+__device__ __forceinline__ bool tile_of(int w, int nN, int tm, const int32_t* __restrict__ items,
                                         const int32_t* __restrict__ offsets, TileRef& t) {
   const int item = w / nN;
   if (item >= items[0]) return false;
@@ -661,8 +661,8 @@ __device__ __forceinline__ bool tile_of(int w, int nN, const int32_t* __restrict
   const int m = 8 * mg + lg % gm;
   t.slot = it[0];
   t.nt = lg / gm;
-  t.p0 = offsets[t.slot] + m * kTileM;
-  t.rows = min(kTileM, offsets[t.slot + 1] - t.p0);
+  t.p0 = offsets[t.slot] + m * tm;
+  t.rows = min(tm, offsets[t.slot + 1] - t.p0);
   return true;
 }
 
@@ -728,42 +728,52 @@ __device__ __forceinline__ void pipe_wait(int q, int Q) {
 }
 
 // The four MFMA steps of stage q: 2 weight tiles x 4 column tiles of 32.
-// Every fragment of the stage is read before the first MFMA (the sched
-// barrier keeps the compiler from sinking each read next to its use).
+// The fragments of step s+1 are read from LDS while the MFMAs of step s run
+// (the scheduling barriers keep that order: reads of the next step, then the
+// current step's MFMAs).
+struct StepFrags {
+  uint4 a[2], b[4];
+};
+
+__device__ __forceinline__ void read_step(const uint8_t* st, int s, int wave, int r, int hh,
+                                          int swz, StepFrags& f) {
+  const int pb = ((4 * (s >> 1) + 2 * hh + (s & 1)) ^ swz) * 16;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    f.a[t] = *reinterpret_cast<const uint4*>(st + wave * 8192 + (32 * t + r) * 128 + pb);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    f.b[cb] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * cb + r) * 128 + pb);
+}
+
 __device__ __forceinline__ void pipe_compute(const uint8_t* smem, int q, int wave, int r, int hh,
                                              v16f (&acc)[2][4]) {
   const uint8_t* st = smem + (q % kRing) * kStage;
   const uint8_t* ss = st + kStageA + kStageB;
   const int swz = (r >> 1) & 7;
   uint2 aw[2], bw[4];
-  uint4 a[4][2], b[4][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
     aw[t] = *reinterpret_cast<const uint2*>(ss + wave * 512 + (32 * t + r) * 8);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
     bw[cb] = *reinterpret_cast<const uint2*>(ss + kStageSA + (32 * cb + r) * 8);
+  StepFrags f[2];
+  read_step(st, 0, wave, r, hh, swz, f[0]);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const int pb = ((4 * (s >> 1) + 2 * hh + (s & 1)) ^ swz) * 16;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-      a[s][t] = *reinterpret_cast<const uint4*>(st + wave * 8192 + (32 * t + r) * 128 + pb);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      b[s][cb] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * cb + r) * 128 + pb);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
+    if (s + 1 < 4) read_step(st, s + 1, wave, r, hh, swz, f[(s + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const StepFrags& cur = f[s & 1];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
       const uint32_t bsc = step_scale(bw[cb].x, bw[cb].y, s, hh);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        acc[t][cb] =
-            mfma32(a[s][t], b[s][cb], acc[t][cb], step_scale(aw[t].x, aw[t].y, s, hh), bsc);
+        acc[t][cb] = mfma32(cur.a[t], cur.b[cb], acc[t][cb], step_scale(aw[t].x, aw[t].y, s, hh),
+                            bsc);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -841,7 +851,7 @@ struct PipeArgs {
 __global__ __launch_bounds__(256) void gateup_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
-  if (!tile_of(xcd_work_index(), p.nN, p.items, p.offsets, tr)) return;  // no barrier yet
+  if (!tile_of(xcd_work_index(), p.nN, kTileM, p.items, p.offsets, tr)) return;  // no barrier yet
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
@@ -881,7 +891,7 @@ __global__ __launch_bounds__(256) void gateup_pipe(PipeArgs p) {
 __global__ __launch_bounds__(256) void down_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
-  if (!tile_of(xcd_work_index(), p.nN, p.items, p.offsets, tr)) return;
+  if (!tile_of(xcd_work_index(), p.nN, kTileM, p.items, p.offsets, tr)) return;
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
@@ -922,6 +932,7 @@ __global__ __launch_bounds__(256) void down_pipe(PipeArgs p) {
   }
 }
 
+
 }  // namespace moe
 
 using namespace moe;
@@ -930,31 +941,36 @@ struct ExpertsWs {
   size_t used_off, items_off, zero_off, hq_off, y_off, total;
 };
 
-// Batches of at least this many assignments (T*k), with H and I multiples of
-// 256, take the pipelined path; every other batch the small-batch kernels.
-// Measured crossover on the 4096/2048 model with 166 slots: the small-batch
-// kernels win up to 1024 assignments, the pipelined ones from 2048.
+// Kernel family of a batch: batches of at least kPipeMinA assignments (T*k)
+// with H and I multiples of 256 take the pipelined kernels, every other batch
+// the small-batch kernels.  Measured crossover on the 4096/2048 model with 166
+// slots: the small-batch kernels win up to 1024 assignments, the pipelined
+// ones from 2048.
 constexpr int kPipeMinA = 2048;
 
-static bool use_pipe(int T, int k, int H, int I) {
-  return (size_t)T * k >= (size_t)kPipeMinA && H % 256 == 0 && I % 256 == 0;
+enum Family { kFamSmall, kFamPipe };
+
+static Family family_of(int T, int k, int H, int I) {
+  if ((size_t)T * k >= (size_t)kPipeMinA && H % 256 == 0 && I % 256 == 0) return kFamPipe;
+  return kFamSmall;
 }
 
-// Upper bound on the M-tiles of a batch: one partial tile per used slot plus
-// the full ones.
-static size_t max_tiles(size_t A, int S) {
-  return (A < (size_t)S ? A : (size_t)S) + (A + kTileM - 1) / kTileM;
+// Upper bound on the M-tiles of tm rows of a batch: one partial tile per used
+// slot plus the full ones.
+static size_t max_tiles(size_t A, int S, int tm) {
+  return (A < (size_t)S ? A : (size_t)S) + (A + tm - 1) / tm;
 }
 
 static ExpertsWs experts_ws(int T, int H, int k, int I, int S) {
   ExpertsWs w;
   const size_t A = (size_t)T * k;
-  const bool pipe = use_pipe(T, k, H, I);
+  const Family fam = family_of(T, k, H, I);
+  const bool tiled = fam != kFamSmall;
   w.used_off = 0;
   w.items_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
-  const size_t items = pipe ? (1 + 4 * max_tiles(A, S)) * sizeof(int32_t) : 0;
+  const size_t items = tiled ? (1 + 4 * max_tiles(A, S, kTileM)) * sizeof(int32_t) : 0;
   w.zero_off = up_to(w.items_off + items, 256);
-  w.hq_off = w.zero_off + (pipe ? kZeroPage : 0);
+  w.hq_off = w.zero_off + (tiled ? kZeroPage : 0);
   w.y_off = up_to(w.hq_off + A * mxfp4_row_bytes(I), 256);
   w.total = up_to(w.y_off + A * (size_t)H * sizeof(float), 256);
   return w;
@@ -982,11 +998,14 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   if (a->ws_bytes < W.total) return MOE_EWORKSPACE;
   if (!a->ws || !aligned(a->ws, 256)) return MOE_EINVAL;
   const int A = T * k;
-  const bool pipe = use_pipe(T, k, H, I);
-  const size_t ntile = max_tiles((size_t)A, S);
-  const size_t g1 = up_to(ntile * (size_t)((I + 127) / 128), 8);
-  const size_t g2 = up_to(ntile * (size_t)((H + 255) / 256), 8);
-  if (pipe && (g1 > 0x7FFFFFFFu || g2 > 0x7FFFFFFFu)) return MOE_EUNSUPPORTED;
+  const Family fam = family_of(T, k, H, I);
+  const size_t ntile = max_tiles((size_t)A, S, kTileM);
+  // N-tiles: gate/up 128 rows of I, down 256 rows of H
+  const int nN1 = (I + 127) / 128;
+  const int nN2 = (H + 255) / 256;
+  const size_t g1 = up_to(ntile * (size_t)nN1, 8);
+  const size_t g2 = up_to(ntile * (size_t)nN2, 8);
+  if (fam != kFamSmall && (g1 > 0x7FFFFFFFu || g2 > 0x7FFFFFFFu)) return MOE_EUNSUPPORTED;
   if (S == 0) {
     // nothing routable: every pick is padding, the output is zero
     dim3 grid(T, (H + 1023) / 1024);
@@ -999,11 +1018,11 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   float* y = reinterpret_cast<float*>(ws + W.y_off);
   hipEvent_t* ev = a->stage_events;
 
-  if (pipe) {
+  if (fam == kFamPipe) {
     int32_t* items = reinterpret_cast<int32_t*>(ws + W.items_off);
     uint8_t* zero = ws + W.zero_off;
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
-    build_tiles<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, items,
+    build_tiles<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, kTileM, items,
                                         reinterpret_cast<uint32_t*>(zero));
     PipeArgs t;
     t.act = a->xq;
@@ -1025,14 +1044,14 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     t.I = I;
     t.k = k;
     t.A = A;
-    t.nN = (I + 127) / 128;
+    t.nN = nN1;
     hipExtLaunchKernelGGL(gateup_pipe, dim3((unsigned)g1), dim3(256), 0, stream,
                           ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, 0, t);
     t.act = hq;
     t.arow = t.hrow;
     t.off_c0 = L.off[4];
     t.off_s0 = L.off[5];
-    t.nN = (H + 255) / 256;
+    t.nN = nN2;
     down_pipe<<<(unsigned)g2, 256, 0, stream>>>(t);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   } else {
@@ -1094,7 +1113,7 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   }
   dim3 cgrid(T, (H + 1023) / 1024);
-  if (pipe)
+  if (fam != kFamSmall)
     combine_kernel<uint16_t><<<cgrid, 256, 0, stream>>>(reinterpret_cast<const uint16_t*>(y),
                                                         a->sel_weight, a->sel_slot, T, H, k, S,
                                                         a->out);
