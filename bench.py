@@ -76,6 +76,12 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
 
 
+def gateup_kernel_name(T: int, k: int, H: int, I: int) -> str:
+    """The gate/up kernel moe_experts_forward launches for this batch shape."""
+    tiled = T * k >= 2048 and H % 256 == 0 and I % 256 == 0
+    return "gateup_pipe" if tiled else "gateup_kernel"
+
+
 def gateup_bytes_per_slot(H: int, I: int) -> int:
     return 2 * I * (H // 2 + H // 32)
 
@@ -326,7 +332,7 @@ def main():
                                f"resident={cfg.resident} ring={cfg.ring} S={S}",
                    "T": T, "H": H, "E": E, "k": k, "I": I, "S": S, "rotate": nrot,
                    "zipf_beta": base.beta},
-        "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": gateup_kernel_name(T, k, H, I), "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic_from_profile(name), "algo_bytes_per_launch": gu_bytes,
                      "mean_launch_us": gu_ms * 1e3,
