@@ -24,9 +24,9 @@
 //   half the E2M1 rate).  Lane l supplies row (or column) l%32 and one MX
 //   block of 32 elements with its E8M0 scale; the 32x32 fp32 result sits in
 //   lane l, register v at row 8(v/4) + 4(l/32) + v%4, column l%32.  K is
-//   walked in chunks of 256 (8 MX blocks) in ascending order; step s (0..3)
-//   of chunk c takes blocks 8c + 4(s/2) + (s%2) (lanes 0-31) and
-//   8c + 4(s/2) + 2 + (s%2) (lanes 32-63).
+//   walked in chunks of 128 (4 MX blocks) in ascending order; step s (0, 1)
+//   of chunk c takes block 4c + 2s (lanes 0-31) and 4c + 2s + 1 (lanes
+//   32-63).
 //
 // The families agree to float32 rounding of their sums, not bit for bit.
 #include <hip/hip_ext.h>
@@ -166,12 +166,6 @@ __device__ __forceinline__ v16f zero16() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
-}
-
-// Scale of step s for lane half hh, in byte 0, from the scale bytes 8c..8c+7
-// of chunk c held as two words.
-__device__ __forceinline__ uint32_t step_scale(uint32_t w0, uint32_t w1, int s, int hh) {
-  return ((s >> 1) ? w1 : w0) >> (16 * hh + 8 * (s & 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -564,26 +558,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 // the grid is work items x N-tiles.  Every operand reaches LDS through direct
 // global-to-LDS loads (lane i of a load lands at the LDS base + size * i),
 // issued two K chunks ahead of use into a ring of three stages.  A stage
-// holds one chunk (K = 256: 128 code bytes and 8 scale bytes per row) of the
-// four waves' 64 weight rows each and of the tile's 128 activation rows.
-// Bytes in flight cost no registers, so the one wave per SIMD that the
-// accumulators allow still keeps ~100 KB of loads in flight per CU.
-// The 16-byte block b of a 128-byte stage row r sits at position
-// b ^ ((r >> 1) & 7): the 16 rows a fragment read touches hit 16 distinct
-// 4-bank groups.
+// holds one chunk (K = 128: 64 code bytes and 4 scale bytes per row) of the
+// four waves' 64 weight rows each and of the tile's 128 activation rows; the
+// ring is 78 KB and the kernel fits 256 VGPRs, so two workgroups share a CU
+// and one computes while the other waits at its stage barrier.  The 16-byte
+// block b of a 64-byte stage row r sits at position b ^ ((r >> 2) & 3): a
+// fragment read (32 rows, two blocks) spreads over all 16 four-bank groups,
+// four lanes each.
 // ===========================================================================
 constexpr int kTileM = 128;                    // assignment rows per work item
-constexpr int kStageA = 4 * 64 * 128;          // weight code rows of the four waves
-constexpr int kStageB = kTileM * 128;          // activation code rows
-constexpr int kStageSA = 4 * 64 * 8;           // weight scale bytes
-constexpr int kStageSB = kTileM * 8;           // activation scale bytes
-constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;  // 52,224 bytes
+constexpr int kKc = 128;                       // K elements per stage
+constexpr int kRowC = kKc / 2;                 // code bytes per row per stage (64)
+constexpr int kRowS = kKc / 32;                // scale bytes per row per stage (4)
+constexpr int kStageA = 4 * 64 * kRowC;        // weight code rows of the four waves
+constexpr int kStageB = kTileM * kRowC;        // activation code rows
+constexpr int kStageSA = 4 * 64 * kRowS;       // weight scale bytes
+constexpr int kStageSB = 4 * 256;              // activation scales: 32 rows per wave, each
+                                               // wave's load also fills an unused 128 B
+constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;  // 26,624 bytes
 constexpr int kRing = 3;
-constexpr int kPipeLds = kRing * kStage;       // 156,672 bytes
+constexpr int kAhead = kRing - 1;              // stages issued ahead of the one in use
+constexpr int kPipeLds = kRing * kStage;       // 159,744 bytes
 constexpr int kZeroPage = 256;                 // zeroed workspace bytes absent rows load from
-// Loads issued by each wave per stage: 8 weight-code, 4 activation-code,
-// 2 weight-scale and 1 activation-scale loads.
-constexpr int kLoadsPerStage = 15;
+// Loads issued by each wave per stage: 4 weight-code, 2 activation-code,
+// 1 weight-scale and 1 activation-scale loads.
+constexpr int kLoadsPerStage = 8;
 
 // Work list of M-tiles of tm rows: items[0] = count, then per item (slot,
 // first row of the tile within the slot, index of the slot's first item, the
@@ -692,92 +691,91 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_base) {
 #pragma clang diagnostic pop
 
 // Per-lane sources of the direct loads; stage q reads code bytes
-// [128 q, 128 q + 128) and scale bytes [8 q, 8 q + 8) of every row.
+// [64 q, 64 q + 64) and scale bytes [4 q, 4 q + 4) of every row.
 struct PipeSrc {
-  const uint8_t* a[8];   // weight codes, load j: wave row 8j + lane/8, block already swizzled
-  const uint8_t* as[2];  // weight scales, load j: wave row 32j + lane/2, dword lane%2
-  const uint8_t* b[4];   // activation codes, load j: tile row (4 wave + j) * 8 + lane/8
-  int bstep[4];          // code bytes per stage (128; 0 for an absent row on the zero page)
-  const uint8_t* bs;     // activation scales: tile row 32 wave + lane/2, dword lane%2
-  int bsstep;            // scale bytes per stage (8; 0 for an absent row)
+  const uint8_t* a[4];   // weight codes, load j: wave row 16j + lane/4, block already swizzled
+  const uint8_t* as;     // weight scales: wave row lane
+  const uint8_t* b[2];   // activation codes, load j: tile row (2 wave + j) * 16 + lane/4
+  int bstep[2];          // code bytes per stage (64; 0 for an absent row on the zero page)
+  const uint8_t* bs;     // activation scales: tile row 32 wave + lane % 32
+  int bsstep;            // scale bytes per stage (4; 0 for an absent row)
 };
 
 __device__ __forceinline__ void pipe_issue(uint8_t* smem, const PipeSrc& src, int q, int wave) {
   uint8_t* st = smem + (q % kRing) * kStage;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dma16(src.a[j] + (size_t)q * 128, st + wave * 8192 + j * 1024);
-#pragma unroll
   for (int j = 0; j < 4; ++j)
-    dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + (4 * wave + j) * 1024);
-  uint8_t* ss = st + kStageA + kStageB;
+    dma16(src.a[j] + (size_t)q * kRowC, st + wave * (64 * kRowC) + j * 1024);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) dma4(src.as[j] + (size_t)q * 8, ss + wave * 512 + j * 256);
+  for (int j = 0; j < 2; ++j)
+    dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + (2 * wave + j) * 1024);
+  uint8_t* ss = st + kStageA + kStageB;
+  dma4(src.as + (size_t)q * kRowS, ss + wave * 256);
   dma4(src.bs + (size_t)q * src.bsstep, ss + kStageSA + wave * 256);
 }
 
-// Waits until this wave's loads of stage q have landed (those of stage q+1
-// may still be in flight), then a workgroup barrier makes every wave's share
-// visible and frees the stage read in the previous iteration for reuse.
+// Waits until this wave's loads of stage q have landed (those of the stages
+// after it may still be in flight), then a workgroup barrier makes every
+// wave's share visible and frees the stage read in the previous iteration for
+// reuse.
 __device__ __forceinline__ void pipe_wait(int q, int Q) {
-  static_assert(kLoadsPerStage == 15, "wait count below");
-  if (q + 1 < Q)
-    asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+  static_assert(kLoadsPerStage == 8 && kAhead == 2, "wait counts below");
+  if (q + 1 < Q)  // stage q + 1 was issued after stage q
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 }
 
-// The four MFMA steps of stage q: 2 weight tiles x 4 column tiles of 32.
-// The fragments of step s+1 are read from LDS while the MFMAs of step s run
-// (the scheduling barriers keep that order: reads of the next step, then the
-// current step's MFMAs).
+// The two MFMA steps of stage q: 2 weight tiles x 4 column tiles of 32.  The
+// fragments of step 1 are read from LDS while the MFMAs of step 0 run (the
+// scheduling barriers keep that order).
 struct StepFrags {
   uint4 a[2], b[4];
 };
 
 __device__ __forceinline__ void read_step(const uint8_t* st, int s, int wave, int r, int hh,
                                           int swz, StepFrags& f) {
-  const int pb = ((4 * (s >> 1) + 2 * hh + (s & 1)) ^ swz) * 16;
+  const int pb = ((2 * s + hh) ^ swz) * 16;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    f.a[t] = *reinterpret_cast<const uint4*>(st + wave * 8192 + (32 * t + r) * 128 + pb);
+    f.a[t] = *reinterpret_cast<const uint4*>(st + wave * (64 * kRowC) + (32 * t + r) * kRowC + pb);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
-    f.b[cb] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * cb + r) * 128 + pb);
+    f.b[cb] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * cb + r) * kRowC + pb);
 }
 
 __device__ __forceinline__ void pipe_compute(const uint8_t* smem, int q, int wave, int r, int hh,
                                              v16f (&acc)[2][4]) {
   const uint8_t* st = smem + (q % kRing) * kStage;
   const uint8_t* ss = st + kStageA + kStageB;
-  const int swz = (r >> 1) & 7;
-  uint2 aw[2], bw[4];
+  const int swz = (r >> 2) & 3;
+  uint32_t aw[2], bw[4];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    aw[t] = *reinterpret_cast<const uint2*>(ss + wave * 512 + (32 * t + r) * 8);
+    aw[t] = *reinterpret_cast<const uint32_t*>(ss + wave * 256 + (32 * t + r) * kRowS);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
-    bw[cb] = *reinterpret_cast<const uint2*>(ss + kStageSA + (32 * cb + r) * 8);
+    bw[cb] = *reinterpret_cast<const uint32_t*>(ss + kStageSA + cb * 256 + r * kRowS);
   StepFrags f[2];
   read_step(st, 0, wave, r, hh, swz, f[0]);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    if (s + 1 < 4) read_step(st, s + 1, wave, r, hh, swz, f[(s + 1) & 1]);
+  for (int s = 0; s < 2; ++s) {
+    if (s + 1 < 2) read_step(st, s + 1, wave, r, hh, swz, f[1]);
     __builtin_amdgcn_sched_barrier(0);
-    const StepFrags& cur = f[s & 1];
+    const StepFrags& cur = f[s];
+    const int sh = 8 * (2 * s + hh);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const uint32_t bsc = step_scale(bw[cb].x, bw[cb].y, s, hh);
 #pragma unroll
       for (int t = 0; t < 2; ++t)
-        acc[t][cb] = mfma32(cur.a[t], cur.b[cb], acc[t][cb], step_scale(aw[t].x, aw[t].y, s, hh),
-                            bsc);
+        acc[t][cb] = mfma32(cur.a[t], cur.b[cb], acc[t][cb], aw[t] >> sh, bw[cb] >> sh);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// The whole K loop over Q = K / 256 stages.
+// The whole K loop over Q = K / 128 stages.
 __device__ __forceinline__ void pipe_mainloop(uint8_t* smem, const PipeSrc& src, int Q, int wave,
                                               int lane, v16f (&acc)[2][4]) {
   const int r = lane & 31, hh = lane >> 5;
@@ -785,11 +783,12 @@ __device__ __forceinline__ void pipe_mainloop(uint8_t* smem, const PipeSrc& src,
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[t][cb] = zero16();
-  pipe_issue(smem, src, 0, wave);
-  if (Q > 1) pipe_issue(smem, src, 1, wave);
+#pragma unroll
+  for (int q = 0; q < kAhead; ++q)
+    if (q < Q) pipe_issue(smem, src, q, wave);
   for (int q = 0; q < Q; ++q) {
     pipe_wait(q, Q);
-    if (q + 2 < Q) pipe_issue(smem, src, q + 2, wave);
+    if (q + kAhead < Q) pipe_issue(smem, src, q + kAhead, wave);
     pipe_compute(smem, q, wave, r, hh, acc);
   }
 }
@@ -801,14 +800,14 @@ __device__ __forceinline__ void pipe_weight_src(PipeSrc& src, const uint8_t* con
                                                 const int (&wrow)[2], size_t crow, size_t srow,
                                                 int lane) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int wr = 8 * j + (lane >> 3), t = wr >> 5, rr = wr & 31;
-    const int b = (lane & 7) ^ ((wr >> 1) & 7);
+  for (int j = 0; j < 4; ++j) {
+    const int wr = 16 * j + (lane >> 2), t = wr >> 5, rr = wr & 31;
+    const int b = (lane & 3) ^ ((wr >> 2) & 3);
     src.a[j] = wcodes[t] + (size_t)(wrow[t] + rr) * crow + b * 16;
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    src.as[j] = wscales[j] + (size_t)(wrow[j] + (lane >> 1)) * srow + 4 * (lane & 1);
+  const int t = lane >> 5, rr = lane & 31;
+  const uint8_t* sbase = t ? wscales[1] : wscales[0];
+  src.as = sbase + (size_t)((t ? wrow[1] : wrow[0]) + rr) * srow;
 }
 
 // Activation-side sources: tile row `row` reads from rowptr(row) (codes at +0,
@@ -817,17 +816,17 @@ template <typename RowPtr>
 __device__ __forceinline__ void pipe_act_src(PipeSrc& src, RowPtr rowptr, size_t scale_off,
                                              const uint8_t* zero, int wave, int lane) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (4 * wave + j) * 8 + (lane >> 3);
-    const int b = (lane & 7) ^ ((row >> 1) & 7);
+  for (int j = 0; j < 2; ++j) {
+    const int row = (2 * wave + j) * 16 + (lane >> 2);
+    const int b = (lane & 3) ^ ((row >> 2) & 3);
     const uint8_t* rp = rowptr(row);
     src.b[j] = (rp ? rp : zero) + b * 16;
-    src.bstep[j] = rp ? 128 : 0;
+    src.bstep[j] = rp ? kRowC : 0;
   }
-  const int row = 32 * wave + (lane >> 1);
+  const int row = 32 * wave + (lane & 31);  // lanes 32-63 repeat rows into the unused half
   const uint8_t* rp = rowptr(row);
-  src.bs = (rp ? rp + scale_off : zero) + 4 * (lane & 1);
-  src.bsstep = rp ? 8 : 0;
+  src.bs = rp ? rp + scale_off : zero;
+  src.bsstep = rp ? kRowS : 0;
 }
 
 struct PipeArgs {
@@ -848,7 +847,7 @@ struct PipeArgs {
 
 // Gate/up: N-tile = 128 rows of I; wave w: rows n0 = 32w.. of gate (tile 0)
 // and of up (tile 1); K = H.
-__global__ __launch_bounds__(256) void gateup_pipe(PipeArgs p) {
+__global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
   if (!tile_of(xcd_work_index(), p.nN, kTileM, p.items, p.offsets, tr)) return;  // no barrier yet
@@ -874,7 +873,7 @@ __global__ __launch_bounds__(256) void gateup_pipe(PipeArgs p) {
       },
       (size_t)H / 2, p.zero, wave, lane);
   v16f acc[2][4];
-  pipe_mainloop(smem, src, H / 256, wave, lane, acc);
+  pipe_mainloop(smem, src, H / kKc, wave, lane, acc);
   if (!active) return;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
@@ -888,7 +887,7 @@ __global__ __launch_bounds__(256) void gateup_pipe(PipeArgs p) {
 
 // Down: N-tile = 256 rows of H; wave w: rows n0 = 64w.. (two 32-row tiles);
 // K = I; the B rows are the slot's hq rows p0.. (contiguous).
-__global__ __launch_bounds__(256) void down_pipe(PipeArgs p) {
+__global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
   if (!tile_of(xcd_work_index(), p.nN, kTileM, p.items, p.offsets, tr)) return;
@@ -916,7 +915,7 @@ __global__ __launch_bounds__(256) void down_pipe(PipeArgs p) {
       },
       (size_t)I / 2, p.zero, wave, lane);
   v16f acc[2][4];
-  pipe_mainloop(smem, src, I / 256, wave, lane, acc);
+  pipe_mainloop(smem, src, I / kKc, wave, lane, acc);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int lr = 32 * cb + r;
