@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 // issued two K chunks ahead of use into a ring of three stages.  A stage
 // holds one chunk (K = 128: 64 code bytes and 4 scale bytes per row) of the
 // four waves' 64 weight rows each and of the tile's 128 activation rows; the
-// ring is 78 KB and the kernel fits 256 VGPRs, so two workgroups share a CU
+// ring is 77 KB and the kernel fits 256 VGPRs, so two workgroups share a CU
 // and one computes while the other waits at its stage barrier.  The 16-byte
 // block b of a 64-byte stage row r sits at position b ^ ((r >> 2) & 3): a
 // fragment read (32 rows, two blocks) spreads over all 16 four-bank groups,
@@ -573,12 +573,11 @@ constexpr int kRowS = kKc / 32;                // scale bytes per row per stage 
 constexpr int kStageA = 4 * 64 * kRowC;        // weight code rows of the four waves
 constexpr int kStageB = kTileM * kRowC;        // activation code rows
 constexpr int kStageSA = 4 * 64 * kRowS;       // weight scale bytes
-constexpr int kStageSB = 4 * 256;              // activation scales: 32 rows per wave, each
-                                               // wave's load also fills an unused 128 B
-constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;  // 26,624 bytes
+constexpr int kStageSB = kTileM * kRowS;       // activation scales: 32 rows per wave
+constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;  // 26,112 bytes
 constexpr int kRing = 3;
 constexpr int kAhead = kRing - 1;              // stages issued ahead of the one in use
-constexpr int kPipeLds = kRing * kStage;       // 159,744 bytes
+constexpr int kPipeLds = kRing * kStage;       // 78,336 bytes
 constexpr int kZeroPage = 256;                 // zeroed workspace bytes absent rows load from
 // Loads issued by each wave per stage: 4 weight-code, 2 activation-code,
 // 1 weight-scale and 1 activation-scale loads.
@@ -711,7 +710,8 @@ __device__ __forceinline__ void pipe_issue(uint8_t* smem, const PipeSrc& src, in
     dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + (2 * wave + j) * 1024);
   uint8_t* ss = st + kStageA + kStageB;
   dma4(src.as + (size_t)q * kRowS, ss + wave * 256);
-  dma4(src.bs + (size_t)q * src.bsstep, ss + kStageSA + wave * 256);
+  if ((threadIdx.x & 63) < 32)  // lanes 0-31: one row each (a partial-lane load)
+    dma4(src.bs + (size_t)q * src.bsstep, ss + kStageSA + wave * 128);
 }
 
 // Waits until this wave's loads of stage q have landed (those of the stages
@@ -756,7 +756,7 @@ __device__ __forceinline__ void pipe_compute(const uint8_t* smem, int q, int wav
     aw[t] = *reinterpret_cast<const uint32_t*>(ss + wave * 256 + (32 * t + r) * kRowS);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
-    bw[cb] = *reinterpret_cast<const uint32_t*>(ss + kStageSA + cb * 256 + r * kRowS);
+    bw[cb] = *reinterpret_cast<const uint32_t*>(ss + kStageSA + (32 * cb + r) * kRowS);
   StepFrags f[2];
   read_step(st, 0, wave, r, hh, swz, f[0]);
 #pragma unroll
@@ -823,7 +823,7 @@ __device__ __forceinline__ void pipe_act_src(PipeSrc& src, RowPtr rowptr, size_t
     src.b[j] = (rp ? rp : zero) + b * 16;
     src.bstep[j] = rp ? kRowC : 0;
   }
-  const int row = 32 * wave + (lane & 31);  // lanes 32-63 repeat rows into the unused half
+  const int row = 32 * wave + (lane & 31);  // lanes 32-63 issue no activation-scale load
   const uint8_t* rp = rowptr(row);
   src.bs = rp ? rp + scale_off : zero;
   src.bsstep = rp ? kRowS : 0;
