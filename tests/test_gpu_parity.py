@@ -342,6 +342,10 @@ def test_layer_parity_long_sampled():
     (512, 16, 4, 10, 256, 256),  # 2048 assignments: smallest batch on the pipelined kernels
     (515, 12, 4, 7, 512, 256),   # pipelined: several 128-row tiles, ragged last tile
     (600, 6, 6, 6, 1024, 512),   # every expert picked by every token: 600 rows per slot
+    (9, 8, 2, 6, 512, 96),       # small batch, gate/up scales staged in LDS, ragged I (idle wave)
+    (17, 8, 2, 6, 800, 512),     # small batch, down scales staged, last 256-row block of 32 rows
+    (3, 6, 2, 4, 8192, 64),      # H past the LDS scale-staging limit: scales read per super-chunk
+    (520, 8, 4, 6, 768, 256),    # pipelined, six K chunks for gate/up and two for down
 ])
 def test_layer_edge_shapes(T, E, k, nr, H, I):
     say(f"layer edge T={T} E={E} k={k} routable={nr} H={H} I={I}")
@@ -495,3 +499,29 @@ def test_route_with_demand_equals_separate_call(name):
     assert np.array_equal(g.hist.cpu().numpy(), want_hist)
     assert np.array_equal(g.buf.delta.cpu().numpy(), want_delta)
     check_route(g, oracle_route(g))
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_stage_events_bracket_gateup(name):
+    """Stage events 1 and 2 come from the gate/up kernel's own dispatch: they lie
+    inside the call's other events, and recording them changes no result."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    g = gpu_layer(name)
+    say(f"moe_experts_forward with stage events on {name}")
+    g.route()
+    stream = torch.cuda.current_stream()
+    g.experts(stream)
+    base = g.out_f64()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    for e in evs:
+        e.record(stream)  # creates the HIP events
+    torch.cuda.synchronize()
+    R.experts(g.buf, g.arena.ptr(), g.arena.stride, stream, evs)
+    torch.cuda.synchronize()
+    assert np.array_equal(g.out_f64(), base)
+    t01, t12 = evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2])
+    t23, t34 = evs[2].elapsed_time(evs[3]), evs[3].elapsed_time(evs[4])
+    assert t12 > 0.0
+    assert min(t01, t23, t34) >= 0.0
+    assert evs[0].elapsed_time(evs[4]) >= t12
