@@ -575,24 +575,54 @@ constexpr int kFusedMaxT = 64;
 constexpr int kFusedWgTokens = 2;
 constexpr int kFusedMaxA = kFusedMaxT * MOE_MAX_K;
 
-// Exclusive scan over the workgroup's 256 threads (one value each); `part`
-// holds 4 ints of LDS.  Returns the thread's offset; *total gets the sum.
-// Ends with a barrier.
-__device__ __forceinline__ int wg256_exclusive_scan(int v, int* part, int* total) {
+// One DPP step of an inclusive wave scan: adds the value of the lane that
+// CTRL names (0 where it names none, or in rows outside ROW_MASK).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int scan_add(int v) {
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive scans of two values over the wave: shifts 1, 2, 4, 8 within rows
+// of 16 lanes (row_shr), then row 15 into rows 1 and 3 and lane 31 into rows
+// 2 and 3 (row_bcast), steps of the two scans interleaved.
+__device__ __forceinline__ void wave_inclusive_scan2(int& a, int& b) {
+  a = scan_add<0x111, 0xF>(a);  // row_shr:1
+  b = scan_add<0x111, 0xF>(b);
+  a = scan_add<0x112, 0xF>(a);  // row_shr:2
+  b = scan_add<0x112, 0xF>(b);
+  a = scan_add<0x114, 0xF>(a);  // row_shr:4
+  b = scan_add<0x114, 0xF>(b);
+  a = scan_add<0x118, 0xF>(a);  // row_shr:8
+  b = scan_add<0x118, 0xF>(b);
+  a = scan_add<0x142, 0xA>(a);  // row_bcast:15
+  b = scan_add<0x142, 0xA>(b);
+  a = scan_add<0x143, 0xC>(a);  // row_bcast:31
+  b = scan_add<0x143, 0xC>(b);
+}
+
+// Exclusive scans of two values (one of each per thread) over the
+// workgroup's 256 threads; `part` holds 8 ints of LDS.  Returns the thread's
+// offsets in a and b and the totals in ta and tb.  Ends with a barrier.
+__device__ __forceinline__ void wg256_exclusive_scan2(int& a, int& b, int* part, int& ta,
+                                                      int& tb) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
+  int ia = a, ib = b;
+  wave_inclusive_scan2(ia, ib);
+  if (lane == 63) {
+    part[wv] = ia;
+    part[4 + wv] = ib;
   }
-  if (lane == 63) part[wv] = incl;
   __syncthreads();
-  int run = incl - v;
-  for (int i = 0; i < wv; ++i) run += part[i];
-  *total = part[0] + part[1] + part[2] + part[3];
+  int ra = ia - a, rb = ib - b;
+  for (int i = 0; i < wv; ++i) {
+    ra += part[i];
+    rb += part[4 + i];
+  }
+  ta = part[0] + part[1] + part[2] + part[3];
+  tb = part[4] + part[5] + part[6] + part[7];
   __syncthreads();
-  return run;
+  a = ra;
+  b = rb;
 }
 
 __global__ __launch_bounds__(256) void route_fused(SelectArgs p, uint32_t* __restrict__ counter,
@@ -606,7 +636,7 @@ __global__ __launch_bounds__(256) void route_fused(SelectArgs p, uint32_t* __res
   __shared__ float ts[kFusedMaxA];
   __shared__ int sl[kFusedMaxA];
   __shared__ float elist[kFusedMaxA];  // demand scores bucketed by expert
-  __shared__ int part[2][4];
+  __shared__ int part[8];
   __shared__ int last;
   const int tid = threadIdx.x;
   const int T = p.T, k = p.k, E = p.E, S = p.S, A = T * k;
@@ -639,15 +669,14 @@ __global__ __launch_bounds__(256) void route_fused(SelectArgs p, uint32_t* __res
   __syncthreads();
 
   // ---- bucket offsets: experts one per thread, slots a range per thread ----
-  int etot;
   const int ecount = tid < E ? __popcll(emask[tid]) : 0;
-  eoff[tid] = wg256_exclusive_scan(ecount, part[0], &etot);
   const int per = (S + 255) / 256;
   const int lo = min(S, tid * per), hi = min(S, lo + per);
   int local = 0;
   for (int s = lo; s < hi; ++s) local += __popcll(smask[s]);
-  int total;
-  int run = wg256_exclusive_scan(local, part[1], &total);
+  int eo = ecount, run = local, etot, total;
+  wg256_exclusive_scan2(eo, run, part, etot, total);
+  eoff[tid] = eo;
   for (int s = lo; s < hi; ++s) {
     off[s] = run;
     offsets[s] = run;
