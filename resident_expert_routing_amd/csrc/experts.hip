@@ -214,21 +214,33 @@ __device__ __forceinline__ void store_y_bf16(uint16_t* yr, int n0, int hh, const
                    f32_to_bf16(acc[4 * q + 2]) | (f32_to_bf16(acc[4 * q + 3]) << 16));
 }
 
+// A used slot and its rows [p0, p1) of the bucketed order; s = -1 if none.
+struct SlotRange {
+  int s, p0, p1;
+};
+
+__device__ __forceinline__ bool slot_used(int a, int b, int A) { return b > a && a >= 0 && b <= A; }
+
 // The u-th slot (ascending) that holds assignments, found by the whole
-// workgroup from slot_offsets; -1 if fewer slots are used.  Each thread scans a
-// contiguous range, then a workgroup prefix of the per-thread counts.
-__device__ int wg_nth_used_slot(int u, const int32_t* __restrict__ offsets, int S, int A) {
+// workgroup from slot_offsets (S <= kInlineWorklistMaxS).  Each thread reads
+// its contiguous range of offsets in one batch, then a workgroup prefix of the
+// per-thread counts names the thread that holds slot u; it passes the slot and
+// its two offsets on through LDS.
+__device__ SlotRange wg_nth_used_slot(int u, const int32_t* __restrict__ offsets, int S, int A) {
+  constexpr int kPer = kInlineWorklistMaxS / 256;
   __shared__ int wsum[4];
-  __shared__ int found;
+  __shared__ SlotRange found;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid == 0) found = -1;
+  if (tid == 0) found = SlotRange{-1, 0, 0};
   const int per = (S + 255) / 256;
   const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int ofs[kPer + 1];
+#pragma unroll
+  for (int i = 0; i <= kPer; ++i) ofs[i] = offsets[min(lo + i, S)];  // in bounds: S + 1 entries
   int local = 0;
-  for (int s = lo; s < hi; ++s) {
-    const int a = offsets[s], b = offsets[s + 1];
-    local += (b > a && a >= 0 && b <= A) ? 1 : 0;
-  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    local += (lo + i < hi && slot_used(ofs[i], ofs[i + 1], A)) ? 1 : 0;
   int incl = local;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -239,25 +251,27 @@ __device__ int wg_nth_used_slot(int u, const int32_t* __restrict__ offsets, int 
   __syncthreads();
   int run = incl - local;
   for (int i = 0; i < wv; ++i) run += wsum[i];
-  if (u >= run && u < run + local) {
-    for (int s = lo; s < hi; ++s) {
-      const int a = offsets[s], b = offsets[s + 1];
-      if (b > a && a >= 0 && b <= A) {
-        if (run == u) found = s;
-        ++run;
-      }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (lo + i < hi && slot_used(ofs[i], ofs[i + 1], A)) {
+      if (run == u) found = SlotRange{lo + i, ofs[i], ofs[i + 1]};
+      ++run;
     }
   }
   __syncthreads();
-  return found;
+  // uniform across the workgroup: keep it in scalar registers
+  return SlotRange{__builtin_amdgcn_readfirstlane(found.s), __builtin_amdgcn_readfirstlane(found.p0),
+                   __builtin_amdgcn_readfirstlane(found.p1)};
 }
 
 // Slot of work item u: from the prebuilt list when there is one, else found
 // in place (small slot counts).
-__device__ __forceinline__ int work_slot(int u, const int32_t* used, const int32_t* offsets, int S,
-                                         int A) {
-  if (used) return u < used[0] ? used[1 + u] : -1;
-  return wg_nth_used_slot(u, offsets, S, A);
+__device__ __forceinline__ SlotRange work_slot(int u, const int32_t* used, const int32_t* offsets,
+                                               int S, int A) {
+  if (!used) return wg_nth_used_slot(u, offsets, S, A);
+  if (u >= used[0]) return SlotRange{-1, 0, 0};
+  const int s = used[1 + u];
+  return SlotRange{s, offsets[s], offsets[s + 1]};
 }
 
 // ---------------------------------------------------------------------------
@@ -273,7 +287,7 @@ __global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ o
   int local = 0;
   for (int s = lo; s < hi; ++s) {
     const int a = offsets[s], b = offsets[s + 1];
-    local += (b > a && a >= 0 && b <= A) ? 1 : 0;
+    local += slot_used(a, b, A) ? 1 : 0;
   }
   int incl = local;
 #pragma unroll
@@ -287,7 +301,7 @@ __global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ o
   for (int i = 0; i < wv; ++i) run += wsum[i];
   for (int s = lo; s < hi; ++s) {
     const int a = offsets[s], b = offsets[s + 1];
-    if (b > a && a >= 0 && b <= A) used[1 + run++] = s;
+    if (slot_used(a, b, A)) used[1 + run++] = s;
   }
   if (tid == 0) {
     int total = 0;
@@ -317,16 +331,38 @@ static bool staged_ok(int K) {
   return K % 512 == 0 && (size_t)kStagedRows * staged_scale_stride(K) <= (size_t)kStagedLdsMax;
 }
 
-// Rows [0, nrows) of a contiguous scale block (rbytes per row, a multiple of
-// 16) into LDS rows of `stride` bytes, by the whole workgroup.
-__device__ __forceinline__ void stage_scale_rows(const uint8_t* __restrict__ src, int nrows,
-                                                 int rbytes, int stride, uint8_t* lds) {
+// Rows [0, nrows) of NM contiguous scale blocks src[m] (rbytes per row, a
+// multiple of 16 and at most 4096) into LDS: row r of block m at
+// lds + (m * mrows + r) * stride.  By the whole workgroup (256 threads); each
+// thread issues up to 8 loads before it writes any of them to LDS, so a batch
+// costs one memory round trip, not one per load.
+template <int NM>
+__device__ __forceinline__ void stage_scale_rows(const uint8_t* const (&src)[NM], int nrows,
+                                                 int rbytes, int stride, int mrows,
+                                                 uint8_t* lds) {
+  constexpr int kJ = 8 / NM;  // rows per thread and block in one batch
   const int per_row = rbytes / 16;
-  const int n = nrows * per_row;
-  for (int q = threadIdx.x; q < n; q += blockDim.x) {
-    const int row = q / per_row, c = q - row * per_row;
-    *reinterpret_cast<uint4*>(lds + row * stride + c * 16) =
-        *reinterpret_cast<const uint4*>(src + (size_t)row * rbytes + c * 16);
+  const int rstep = 256 / per_row;  // rows the workgroup covers per pass
+  const int r0 = threadIdx.x / per_row, c = threadIdx.x - r0 * per_row;
+  if (r0 >= rstep) return;
+  // Rows past the end repeat the last row (same bytes to the same place): no
+  // branch, so the compiler keeps every load of a batch ahead of the stores.
+  for (int j0 = r0; j0 < nrows; j0 += kJ * rstep) {
+    uint4 v[NM][kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int row = min(j0 + j * rstep, nrows - 1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        v[m][j] = *reinterpret_cast<const uint4*>(src[m] + (size_t)row * rbytes + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+      const int row = min(j0 + j * rstep, nrows - 1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        *reinterpret_cast<uint4*>(lds + (m * mrows + row) * stride + c * 16) = v[m][j];
+    }
   }
 }
 
@@ -353,9 +389,9 @@ template <bool FULL>
 __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
   const int nbps = (p.I + 127) / 128;
   const int u = blockIdx.x / nbps, nb = blockIdx.x % nbps;
-  const int s = work_slot(u, p.used, p.offsets, p.S, p.A);
-  if (s < 0) return;
-  const int p0 = p.offsets[s], p1 = p.offsets[s + 1];
+  const SlotRange sr = work_slot(u, p.used, p.offsets, p.S, p.A);
+  if (sr.s < 0) return;
+  const int s = sr.s, p0 = sr.p0, p1 = sr.p1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = nb * 128 + wave * 32;
   const int r = lane & 15, g = lane >> 4;
@@ -372,9 +408,9 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
     extern __shared__ __align__(16) uint8_t wscale[];
     const int sstr = staged_scale_stride(H);
     const int nrow = min(128, p.I - nb * 128);
-    stage_scale_rows(base + p.off_gs + (size_t)nb * 128 * srow, nrow, (int)srow, sstr, wscale);
-    stage_scale_rows(base + p.off_us + (size_t)nb * 128 * srow, nrow, (int)srow, sstr,
-                     wscale + 128 * sstr);
+    const uint8_t* const src[2] = {base + p.off_gs + (size_t)nb * 128 * srow,
+                                   base + p.off_us + (size_t)nb * 128 * srow};
+    stage_scale_rows<2>(src, nrow, (int)srow, sstr, 128, wscale);
     __syncthreads();
     gs0 = wscale + (wave * 32 + r) * sstr;
     us0 = gs0 + 128 * sstr;
@@ -445,9 +481,9 @@ template <bool FULL>
 __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
   const int nbps = (p.H + 255) / 256;
   const int u = blockIdx.x / nbps, nb = blockIdx.x % nbps;
-  const int s = work_slot(u, p.used, p.offsets, p.S, p.A);
-  if (s < 0) return;
-  const int p0 = p.offsets[s], p1 = p.offsets[s + 1];
+  const SlotRange sr = work_slot(u, p.used, p.offsets, p.S, p.A);
+  if (sr.s < 0) return;
+  const int s = sr.s, p0 = sr.p0, p1 = sr.p1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n0 = nb * 256 + wave * 64;
   const int r = lane & 15, g = lane >> 4;
@@ -459,8 +495,8 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
   extern __shared__ __align__(16) uint8_t wscale[];  // FULL: the workgroup's scale rows
   const int sstr = staged_scale_stride(I);
   if (FULL) {
-    stage_scale_rows(base + p.off_ds + (size_t)nb * 256 * srow, min(256, p.H - nb * 256),
-                     (int)srow, sstr, wscale);
+    const uint8_t* const src[1] = {base + p.off_ds + (size_t)nb * 256 * srow};
+    stage_scale_rows<1>(src, min(256, p.H - nb * 256), (int)srow, sstr, 256, wscale);
     __syncthreads();
   }
   if (n0 >= p.H) return;
