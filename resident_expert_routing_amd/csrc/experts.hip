@@ -57,6 +57,11 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f c, u
 
 // One super-chunk of an MXFP4 row as this lane supplies it: codes of blocks
 // 4i+g (i = 0..3) and, in byte 0 of s[i], their scales.
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
 struct RowSC {
   uint4 q[4];
   uint32_t s[4];
@@ -77,6 +82,31 @@ __device__ __forceinline__ void zero_sc(RowSC& r) {
   }
 }
 
+// This lane's code blocks 16sc+g, +4, +8, +12 of a row with a multiple of 16
+// blocks (super-chunk sc).
+__device__ __forceinline__ void load_codes_full(const uint8_t* codes, int sc, int g, RowSC& r) {
+  const uint4* q = reinterpret_cast<const uint4*>(codes + (size_t)sc * 256) + g;
+  r.q[0] = q[0];
+  r.q[1] = q[4];
+  r.q[2] = q[8];
+  r.q[3] = q[12];
+}
+
+// This lane's scale bytes of those blocks, from the 16 scale bytes of the
+// super-chunk.
+__device__ __forceinline__ void split_scales(const uint4 sv, int g, RowSC& r) {
+  const int sh = 8 * g;
+  r.s[0] = sv.x >> sh;
+  r.s[1] = sv.y >> sh;
+  r.s[2] = sv.z >> sh;
+  r.s[3] = sv.w >> sh;
+}
+
+// The scale bytes of the same blocks (16-byte aligned scales).
+__device__ __forceinline__ void load_scales_full(const uint8_t* scales, int sc, int g, RowSC& r) {
+  split_scales(*reinterpret_cast<const uint4*>(scales + sc * 16), g, r);
+}
+
 // Load this lane's share of super-chunk sc of an MXFP4 row.  FULL: the row has
 // a multiple of 16 blocks and 16-byte aligned scales.  Blocks at or past nblk
 // read as zero codes.
@@ -85,17 +115,8 @@ __device__ __forceinline__ void load_row_sc(const uint8_t* codes, const uint8_t*
                                             int g, int nblk, RowSC& r) {
   const int b0 = sc * 16;
   if (FULL) {
-    const uint4* p = reinterpret_cast<const uint4*>(codes + (size_t)b0 * 16) + g;
-    r.q[0] = p[0];
-    r.q[1] = p[4];
-    r.q[2] = p[8];
-    r.q[3] = p[12];
-    const uint4 sv = *reinterpret_cast<const uint4*>(scales + b0);
-    const int sh = 8 * g;
-    r.s[0] = sv.x >> sh;
-    r.s[1] = sv.y >> sh;
-    r.s[2] = sv.z >> sh;
-    r.s[3] = sv.w >> sh;
+    load_codes_full(codes, sc, g, r);
+    load_scales_full(scales, sc, g, r);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -334,13 +355,13 @@ static bool staged_ok(int K) {
 // Rows [0, nrows) of NM contiguous scale blocks src[m] (rbytes per row, a
 // multiple of 16 and at most 4096) into LDS: row r of block m at
 // lds + (m * mrows + r) * stride.  By the whole workgroup (256 threads); each
-// thread issues up to 8 loads before it writes any of them to LDS, so a batch
-// costs one memory round trip, not one per load.
+// thread issues 4 loads per block before it writes any of them to LDS, so a
+// batch costs one memory round trip, not one per load.
 template <int NM>
 __device__ __forceinline__ void stage_scale_rows(const uint8_t* const (&src)[NM], int nrows,
                                                  int rbytes, int stride, int mrows,
                                                  uint8_t* lds) {
-  constexpr int kJ = 8 / NM;  // rows per thread and block in one batch
+  constexpr int kJ = 4;  // rows per thread and block in one batch
   const int per_row = rbytes / 16;
   const int rstep = 256 / per_row;  // rows the workgroup covers per pass
   const int r0 = threadIdx.x / per_row, c = threadIdx.x - r0 * per_row;
@@ -400,10 +421,25 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
   const int nsc = (nblk + 15) / 16;
   const uint8_t* base = p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)H / 2, srow = (size_t)H / 32;
+  const bool wave_ok = n0 < p.I;  // rows past I: the wave only helps to stage
+  const uint8_t* gc0 = base + p.off_gc + (size_t)((wave_ok ? n0 : 0) + r) * crow;
+  const uint8_t* gc1 = gc0 + 16 * crow;
+  const uint8_t* uc0 = base + p.off_uc + (size_t)((wave_ok ? n0 : 0) + r) * crow;
+  const uint8_t* uc1 = uc0 + 16 * crow;
   const uint8_t* gs0;
   const uint8_t* us0;
   int sstep;  // bytes from a tile-0 scale row to its tile-1 row
+  RowSC pre[4];  // FULL: super-chunk 0 codes of the first column block, loaded early
+  int pa = -1;   // FULL: this lane's perm entry of the first column block
   if (FULL) {
+    // Issued before the staging waits, so they are in flight together.
+    if (wave_ok) {
+      load_codes_full(gc0, 0, g, pre[0]);
+      load_codes_full(gc1, 0, g, pre[1]);
+      load_codes_full(uc0, 0, g, pre[2]);
+      load_codes_full(uc1, 0, g, pre[3]);
+    }
+    if (p0 + r < p1) pa = p.perm[p0 + r];
     // gate scales of the workgroup's rows at LDS row 0.., up scales at row 128..
     extern __shared__ __align__(16) uint8_t wscale[];
     const int sstr = staged_scale_stride(H);
@@ -420,25 +456,44 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
     us0 = base + p.off_us + (size_t)(n0 + r) * srow;
     sstep = 16 * (int)srow;
   }
-  if (n0 >= p.I) return;
+  if (!wave_ok) return;
   const uint8_t* gs1 = gs0 + sstep;
   const uint8_t* us1 = us0 + sstep;
-  const uint8_t* gc0 = base + p.off_gc + (size_t)(n0 + r) * crow;
-  const uint8_t* gc1 = gc0 + 16 * crow;
-  const uint8_t* uc0 = base + p.off_uc + (size_t)(n0 + r) * crow;
-  const uint8_t* uc1 = uc0 + 16 * crow;
 
-  for (int cb = p0; cb < p1; cb += 16) {
+  // One block of 16 columns (assignment rows cb..) against the wave's 32 rows
+  // of gate and of up.  The first block of a FULL workgroup takes super-chunk
+  // 0's weight codes and its perm entries from the early loads (a separate
+  // copy of the loop, so those registers are free in the others).
+  auto column_block = [&](int cb, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
     // this lane's column (assignment row) for the B operand
     const int pc = cb + r;
     int t = -1;
     if (pc < p1) {
-      const int a = p.perm[pc];
+      const int a = kFirst ? pa : p.perm[pc];
       if (a >= 0 && a < p.A) t = a / p.k;
     }
     const uint8_t* xc = t >= 0 ? p.xq + (size_t)t * p.xrow : nullptr;
     v4f ag0 = {0.f, 0.f, 0.f, 0.f}, ag1 = ag0, au0 = ag0, au1 = ag0;
-    for (int sc = 0; sc < nsc; ++sc) {
+    int sc0 = 0;
+    if constexpr (kFirst) {
+      // super-chunk 0 from the early loads
+      RowSC x;
+      if (xc)
+        load_row_sc<true>(xc, xc + H / 2, 0, g, nblk, x);
+      else
+        zero_sc(x);
+      load_scales_full(gs0, 0, g, pre[0]);
+      load_scales_full(gs1, 0, g, pre[1]);
+      load_scales_full(us0, 0, g, pre[2]);
+      load_scales_full(us1, 0, g, pre[3]);
+      ag0 = mfma_superchunk(pre[0], x, ag0);
+      ag1 = mfma_superchunk(pre[1], x, ag1);
+      au0 = mfma_superchunk(pre[2], x, au0);
+      au1 = mfma_superchunk(pre[3], x, au1);
+      sc0 = 1;
+    }
+    for (int sc = sc0; sc < nsc; ++sc) {
       RowSC wg0, wg1, wu0, wu1, x;
       load_row_sc<FULL>(gc0, gs0, sc, g, nblk, wg0);
       load_row_sc<FULL>(gc1, gs1, sc, g, nblk, wg1);
@@ -456,7 +511,13 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
     const int pcol = cb + (lane & 15);
     swiglu_quant_store16(ag0, ag1, au0, au1, g,
                          pcol < p1 ? p.hq + (size_t)pcol * p.hrow : nullptr, n0, p.I);
+  };
+  int cb = p0;
+  if constexpr (FULL) {
+    column_block(cb, BoolTag<true>{});
+    cb += 16;
   }
+  for (; cb < p1; cb += 16) column_block(cb, BoolTag<false>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -494,29 +555,62 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
   const size_t crow = (size_t)I / 2, srow = (size_t)I / 32;
   extern __shared__ __align__(16) uint8_t wscale[];  // FULL: the workgroup's scale rows
   const int sstr = staged_scale_stride(I);
-  if (FULL) {
-    const uint8_t* const src[1] = {base + p.off_ds + (size_t)nb * 256 * srow};
-    stage_scale_rows<1>(src, min(256, p.H - nb * 256), (int)srow, sstr, 256, wscale);
-    __syncthreads();
-  }
-  if (n0 >= p.H) return;
   const uint8_t* dc[4];
   const uint8_t* ds[4];
   bool tv[4];
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) {
     tv[tl] = n0 + 16 * tl < p.H;  // whole tile valid (H % 16 == 0)
-    const int row = tv[tl] ? n0 + 16 * tl + r : n0 + r;
+    const int row = tv[tl] ? n0 + 16 * tl + r : nb * 256 + r;  // an idle tile: a row in range
     dc[tl] = base + p.off_dc + (size_t)row * crow;
     ds[tl] = FULL ? wscale + (row - nb * 256) * sstr : base + p.off_ds + (size_t)row * srow;
   }
-  for (int cb = p0; cb < p1; cb += 16) {
+  RowSC pre[4];  // FULL: super-chunk 0 codes of the first column block, loaded early
+  RowSC prex;    // FULL: and of its activation rows (codes; scale bytes in prexs)
+  uint4 prexs;
+  if (FULL) {
+    // Issued before the staging waits, so they are in flight together.
+#pragma unroll
+    for (int tl = 0; tl < 4; ++tl)
+      if (tv[tl]) load_codes_full(dc[tl], 0, g, pre[tl]);
+    if (p0 + r < p1) {
+      const uint8_t* hc = p.hq + (size_t)(p0 + r) * p.hrow;
+      load_codes_full(hc, 0, g, prex);
+      prexs = *reinterpret_cast<const uint4*>(hc + I / 2);
+    } else {
+      zero_sc(prex);
+      prexs = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);  // scale 1
+    }
+    const uint8_t* const src[1] = {base + p.off_ds + (size_t)nb * 256 * srow};
+    stage_scale_rows<1>(src, min(256, p.H - nb * 256), (int)srow, sstr, 256, wscale);
+    __syncthreads();
+  }
+  if (n0 >= p.H) return;
+  // One block of 16 columns (assignment rows cb..) against the wave's 64 rows;
+  // the first block of a FULL workgroup takes super-chunk 0 from the early
+  // loads (a separate copy of the loop, so those registers are free in the
+  // others).
+  auto column_block = [&](int cb, auto first) {
+    constexpr bool kFirst = decltype(first)::value;
     const int pc = cb + r;
     const uint8_t* hc = pc < p1 ? p.hq + (size_t)pc * p.hrow : nullptr;
     v4f acc[4];
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl) acc[tl] = (v4f){0.f, 0.f, 0.f, 0.f};
-    for (int sc = 0; sc < nsc; ++sc) {
+    int sc0 = 0;
+    if constexpr (kFirst) {
+      // super-chunk 0 from the early loads
+      split_scales(prexs, g, prex);
+#pragma unroll
+      for (int tl = 0; tl < 4; ++tl) {
+        if (tv[tl]) {
+          load_scales_full(ds[tl], 0, g, pre[tl]);
+          acc[tl] = mfma_superchunk(pre[tl], prex, acc[tl]);
+        }
+      }
+      sc0 = 1;
+    }
+    for (int sc = sc0; sc < nsc; ++sc) {
       RowSC x;
       if (hc)
         load_row_sc<FULL>(hc, hc + I / 2, sc, g, nblk, x);
@@ -546,7 +640,13 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
         }
       }
     }
+  };
+  int cb = p0;
+  if constexpr (FULL) {
+    column_block(cb, BoolTag<true>{});
+    cb += 16;
   }
+  for (; cb < p1; cb += 16) column_block(cb, BoolTag<false>{});
 }
 
 // ---------------------------------------------------------------------------
