@@ -290,8 +290,8 @@ __device__ SlotRange wg_nth_used_slot(int u, const int32_t* __restrict__ offsets
 __device__ __forceinline__ SlotRange work_slot(int u, const int32_t* used, const int32_t* offsets,
                                                int S, int A) {
   if (!used) return wg_nth_used_slot(u, offsets, S, A);
-  if (u >= used[0]) return SlotRange{-1, 0, 0};
-  const int s = used[1 + u];
+  const int n = used[0], s = used[1 + u];  // both in one round trip: u < min(S, A) < S + 1
+  if (u >= n) return SlotRange{-1, 0, 0};
   return SlotRange{s, offsets[s], offsets[s + 1]};
 }
 
@@ -301,15 +301,18 @@ __device__ __forceinline__ SlotRange work_slot(int u, const int32_t* used, const
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ offsets, int S,
                                                    int A, int32_t* __restrict__ used) {
+  constexpr int kPer = MOE_MAX_S / 1024;
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int per = (S + 1023) / 1024;
   const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int ofs[kPer + 1];  // this thread's offsets, read in one batch
+#pragma unroll
+  for (int i = 0; i <= kPer; ++i) ofs[i] = offsets[min(lo + i, S)];  // in bounds: S + 1 entries
   int local = 0;
-  for (int s = lo; s < hi; ++s) {
-    const int a = offsets[s], b = offsets[s + 1];
-    local += slot_used(a, b, A) ? 1 : 0;
-  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    local += (lo + i < hi && slot_used(ofs[i], ofs[i + 1], A)) ? 1 : 0;
   int incl = local;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -320,10 +323,9 @@ __global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ o
   __syncthreads();
   int run = incl - local;
   for (int i = 0; i < wv; ++i) run += wsum[i];
-  for (int s = lo; s < hi; ++s) {
-    const int a = offsets[s], b = offsets[s + 1];
-    if (slot_used(a, b, A)) used[1 + run++] = s;
-  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (lo + i < hi && slot_used(ofs[i], ofs[i + 1], A)) used[1 + run++] = lo + i;
   if (tid == 0) {
     int total = 0;
     for (int i = 0; i < 16; ++i) total += wsum[i];
