@@ -242,22 +242,20 @@ struct SlotRange {
 
 __device__ __forceinline__ bool slot_used(int a, int b, int A) { return b > a && a >= 0 && b <= A; }
 
-// The u-th slot (ascending) that holds assignments, found by the whole
-// workgroup from slot_offsets (S <= kInlineWorklistMaxS).  Each thread reads
-// its contiguous range of offsets in one batch, then a workgroup prefix of the
-// per-thread counts names the thread that holds slot u; it passes the slot and
-// its two offsets on through LDS.
-__device__ SlotRange wg_nth_used_slot(int u, const int32_t* __restrict__ offsets, int S, int A) {
-  constexpr int kPer = kInlineWorklistMaxS / 256;
-  __shared__ int wsum[4];
-  __shared__ SlotRange found;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (tid == 0) found = SlotRange{-1, 0, 0};
-  const int per = (S + 255) / 256;
-  const int lo = min(S, tid * per), hi = min(S, lo + per);
+// The u-th slot (ascending) that holds assignments, found by one wave from
+// slot_offsets (S <= kInlineWorklistMaxS).  Each lane reads its contiguous
+// range of offsets in one batch; a wave prefix of the per-lane counts names the
+// lane that holds slot u, which hands the slot and its two offsets to the
+// others.
+__device__ SlotRange wave_nth_used_slot(int u, const int32_t* __restrict__ offsets, int S, int A) {
+  constexpr int kPer = kInlineWorklistMaxS / kWave;
+  const int lane = threadIdx.x & 63;
+  const int per = (S + kWave - 1) / kWave;
+  const int lo = min(S, lane * per), hi = min(S, lo + per);
   int ofs[kPer + 1];
 #pragma unroll
-  for (int i = 0; i <= kPer; ++i) ofs[i] = offsets[min(lo + i, S)];  // in bounds: S + 1 entries
+  for (int i = 0; i <= kPer; ++i)  // i <= per: uniform, so only the loads needed are issued
+    ofs[i] = i <= per ? offsets[min(lo + i, S)] : 0;  // in bounds: S + 1 entries
   int local = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i)
@@ -268,28 +266,32 @@ __device__ SlotRange wg_nth_used_slot(int u, const int32_t* __restrict__ offsets
     const int o = __shfl_up(incl, d, kWave);
     if (lane >= d) incl += o;
   }
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
   int run = incl - local;
-  for (int i = 0; i < wv; ++i) run += wsum[i];
+  int fs = -1, fa = 0, fb = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (lo + i < hi && slot_used(ofs[i], ofs[i + 1], A)) {
-      if (run == u) found = SlotRange{lo + i, ofs[i], ofs[i + 1]};
+      if (run == u) {
+        fs = lo + i;
+        fa = ofs[i];
+        fb = ofs[i + 1];
+      }
       ++run;
     }
   }
-  __syncthreads();
-  // uniform across the workgroup: keep it in scalar registers
-  return SlotRange{__builtin_amdgcn_readfirstlane(found.s), __builtin_amdgcn_readfirstlane(found.p0),
-                   __builtin_amdgcn_readfirstlane(found.p1)};
+  const unsigned long long m = __ballot(fs >= 0);
+  if (m == 0ull) return SlotRange{-1, 0, 0};
+  const int L = __ffsll(m) - 1;
+  // uniform across the wave: keep it in scalar registers
+  return SlotRange{__builtin_amdgcn_readlane(fs, L), __builtin_amdgcn_readlane(fa, L),
+                   __builtin_amdgcn_readlane(fb, L)};
 }
 
 // Slot of work item u: from the prebuilt list when there is one, else found
 // in place (small slot counts).
 __device__ __forceinline__ SlotRange work_slot(int u, const int32_t* used, const int32_t* offsets,
                                                int S, int A) {
-  if (!used) return wg_nth_used_slot(u, offsets, S, A);
+  if (!used) return wave_nth_used_slot(u, offsets, S, A);
   const int n = used[0], s = used[1 + u];  // both in one round trip: u < min(S, A) < S + 1
   if (u >= n) return SlotRange{-1, 0, 0};
   return SlotRange{s, offsets[s], offsets[s + 1]};
@@ -336,15 +338,15 @@ __global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ o
 // ===========================================================================
 // Small-batch kernels
 // ===========================================================================
-// Weight scales of the rows a workgroup streams are staged in LDS once.  A
+// Weight scales of the rows a wave streams are staged in LDS once.  A
 // row's scale bytes share one or two cache lines that the K loop would
 // otherwise touch once per super-chunk; between touches the workgroup streams
 // enough code bytes for the line to leave L2, so it would be fetched again
 // from memory every time.  LDS row stride 16*((K/512) | 1) bytes: an odd
 // number of 16-byte units, so the 16 rows of one fragment read fall on 16
 // distinct 4-bank groups.
-constexpr int kStagedRows = 256;            // rows staged per workgroup (at most)
-constexpr int kStagedLdsMax = 64 * 1024;    // LDS budget of the staged scales
+constexpr int kStagedRows = 64;             // rows staged per workgroup (one wave)
+constexpr int kStagedLdsMax = 32 * 1024;    // LDS budget of the staged scales
 
 __host__ __device__ constexpr int staged_scale_stride(int K) { return 16 * ((K / 512) | 1); }
 
@@ -355,18 +357,19 @@ static bool staged_ok(int K) {
 }
 
 // Rows [0, nrows) of NM contiguous scale blocks src[m] (rbytes per row, a
-// multiple of 16 and at most 4096) into LDS: row r of block m at
-// lds + (m * mrows + r) * stride.  By the whole workgroup (256 threads); each
-// thread issues 4 loads per block before it writes any of them to LDS, so a
-// batch costs one memory round trip, not one per load.
+// multiple of 16 and at most 1024) into LDS: row r of block m at
+// lds + (m * mrows + r) * stride.  By one wave; each lane issues 4 loads per
+// block before it writes any of them to LDS, so a batch costs one memory round
+// trip, not one per load.
 template <int NM>
 __device__ __forceinline__ void stage_scale_rows(const uint8_t* const (&src)[NM], int nrows,
                                                  int rbytes, int stride, int mrows,
                                                  uint8_t* lds) {
   constexpr int kJ = 4;  // rows per thread and block in one batch
   const int per_row = rbytes / 16;
-  const int rstep = 256 / per_row;  // rows the workgroup covers per pass
-  const int r0 = threadIdx.x / per_row, c = threadIdx.x - r0 * per_row;
+  const int rstep = kWave / per_row;  // rows the wave covers per pass
+  const int lane = threadIdx.x & 63;
+  const int r0 = lane / per_row, c = lane - r0 * per_row;
   if (r0 >= rstep) return;
   // Rows past the end repeat the last row (same bytes to the same place): no
   // branch, so the compiler keeps every load of a batch ahead of the stores.
@@ -389,10 +392,12 @@ __device__ __forceinline__ void stage_scale_rows(const uint8_t* const (&src)[NM]
   }
 }
 
-// Gate/up + SwiGLU + MXFP4(h).  Workgroup = 4 waves = 128 rows of I of one
-// slot; wave = 32 rows (two 16-row tiles of gate and of up).  Columns are the
-// slot's assignment rows p, 16 per MFMA tile.  Output: hq row p (an MXFP4 row
-// of I elements).
+// Gate/up + SwiGLU + MXFP4(h).  Workgroup = one wave = 32 rows of I of one
+// slot (two 16-row tiles of gate and of up).  Columns are the slot's
+// assignment rows p, 16 per MFMA tile.  Output: hq row p (an MXFP4 row of I
+// elements).  One-wave workgroups let the dispatcher spread the bytes evenly
+// over the CUs: each CU streams at a rate of its own, so the CU with the most
+// work sets the kernel's time.
 // ---------------------------------------------------------------------------
 struct GateUpArgs {
   const uint8_t* xq;
@@ -409,63 +414,52 @@ struct GateUpArgs {
 };
 
 template <bool FULL>
-__global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
-  const int nbps = (p.I + 127) / 128;
-  const int u = blockIdx.x / nbps, nb = blockIdx.x % nbps;
+__global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
+  const int nbps = p.I / 32;
+  const int u = blockIdx.x / nbps, nb = blockIdx.x - u * nbps;
   const SlotRange sr = work_slot(u, p.used, p.offsets, p.S, p.A);
   if (sr.s < 0) return;
   const int s = sr.s, p0 = sr.p0, p1 = sr.p1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = nb * 128 + wave * 32;
+  const int lane = threadIdx.x;
+  const int n0 = nb * 32;
   const int r = lane & 15, g = lane >> 4;
   const int H = p.H;
   const int nblk = H / 32;
   const int nsc = (nblk + 15) / 16;
   const uint8_t* base = p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)H / 2, srow = (size_t)H / 32;
-  const bool wave_ok = n0 < p.I;  // rows past I: the wave only helps to stage
-  const uint8_t* gc0 = base + p.off_gc + (size_t)((wave_ok ? n0 : 0) + r) * crow;
+  const uint8_t* gc0 = base + p.off_gc + (size_t)(n0 + r) * crow;
   const uint8_t* gc1 = gc0 + 16 * crow;
-  const uint8_t* uc0 = base + p.off_uc + (size_t)((wave_ok ? n0 : 0) + r) * crow;
+  const uint8_t* uc0 = base + p.off_uc + (size_t)(n0 + r) * crow;
   const uint8_t* uc1 = uc0 + 16 * crow;
   const uint8_t* gs0;
   const uint8_t* us0;
   int sstep;  // bytes from a tile-0 scale row to its tile-1 row
-  RowSC pre[4];  // FULL: super-chunk 0 codes of the first column block, loaded early
-  int pa = -1;   // FULL: this lane's perm entry of the first column block
+  int pa = -1;  // FULL: this lane's perm entry of the first column block, loaded early
   if (FULL) {
     // Issued before the staging waits, so they are in flight together.
-    if (wave_ok) {
-      load_codes_full(gc0, 0, g, pre[0]);
-      load_codes_full(gc1, 0, g, pre[1]);
-      load_codes_full(uc0, 0, g, pre[2]);
-      load_codes_full(uc1, 0, g, pre[3]);
-    }
     if (p0 + r < p1) pa = p.perm[p0 + r];
-    // gate scales of the workgroup's rows at LDS row 0.., up scales at row 128..
+    // gate scales of the wave's 32 rows at LDS row 0.., up scales at row 32..
     extern __shared__ __align__(16) uint8_t wscale[];
     const int sstr = staged_scale_stride(H);
-    const int nrow = min(128, p.I - nb * 128);
-    const uint8_t* const src[2] = {base + p.off_gs + (size_t)nb * 128 * srow,
-                                   base + p.off_us + (size_t)nb * 128 * srow};
-    stage_scale_rows<2>(src, nrow, (int)srow, sstr, 128, wscale);
+    const uint8_t* const src[2] = {base + p.off_gs + (size_t)n0 * srow,
+                                   base + p.off_us + (size_t)n0 * srow};
+    stage_scale_rows<2>(src, 32, (int)srow, sstr, 32, wscale);
     __syncthreads();
-    gs0 = wscale + (wave * 32 + r) * sstr;
-    us0 = gs0 + 128 * sstr;
+    gs0 = wscale + r * sstr;
+    us0 = gs0 + 32 * sstr;
     sstep = 16 * sstr;
   } else {
     gs0 = base + p.off_gs + (size_t)(n0 + r) * srow;
     us0 = base + p.off_us + (size_t)(n0 + r) * srow;
     sstep = 16 * (int)srow;
   }
-  if (!wave_ok) return;
   const uint8_t* gs1 = gs0 + sstep;
   const uint8_t* us1 = us0 + sstep;
 
   // One block of 16 columns (assignment rows cb..) against the wave's 32 rows
-  // of gate and of up.  The first block of a FULL workgroup takes super-chunk
-  // 0's weight codes and its perm entries from the early loads (a separate
-  // copy of the loop, so those registers are free in the others).
+  // of gate and of up.  The first block of a FULL kernel takes its perm
+  // entries from the early loads.
   auto column_block = [&](int cb, auto first) {
     constexpr bool kFirst = decltype(first)::value;
     // this lane's column (assignment row) for the B operand
@@ -477,25 +471,7 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
     }
     const uint8_t* xc = t >= 0 ? p.xq + (size_t)t * p.xrow : nullptr;
     v4f ag0 = {0.f, 0.f, 0.f, 0.f}, ag1 = ag0, au0 = ag0, au1 = ag0;
-    int sc0 = 0;
-    if constexpr (kFirst) {
-      // super-chunk 0 from the early loads
-      RowSC x;
-      if (xc)
-        load_row_sc<true>(xc, xc + H / 2, 0, g, nblk, x);
-      else
-        zero_sc(x);
-      load_scales_full(gs0, 0, g, pre[0]);
-      load_scales_full(gs1, 0, g, pre[1]);
-      load_scales_full(us0, 0, g, pre[2]);
-      load_scales_full(us1, 0, g, pre[3]);
-      ag0 = mfma_superchunk(pre[0], x, ag0);
-      ag1 = mfma_superchunk(pre[1], x, ag1);
-      au0 = mfma_superchunk(pre[2], x, au0);
-      au1 = mfma_superchunk(pre[3], x, au1);
-      sc0 = 1;
-    }
-    for (int sc = sc0; sc < nsc; ++sc) {
+    for (int sc = 0; sc < nsc; ++sc) {
       RowSC wg0, wg1, wu0, wu1, x;
       load_row_sc<FULL>(gc0, gs0, sc, g, nblk, wg0);
       load_row_sc<FULL>(gc1, gs1, sc, g, nblk, wg1);
@@ -523,9 +499,9 @@ __global__ __launch_bounds__(256) void gateup_kernel(GateUpArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Down projection.  Workgroup = 4 waves = 256 rows of H of one slot; wave = 64
-// rows (four 16-row tiles).  B operand: hq rows of the slot.  Output y[a] (fp32
-// row of H), a = perm[p].
+// Down projection.  Workgroup = one wave = 64 rows of H of one slot (four
+// 16-row tiles).  B operand: hq rows of the slot.  Output y[a] (fp32 row of
+// H), a = perm[p].
 // ---------------------------------------------------------------------------
 struct DownArgs {
   const uint8_t* hq;
@@ -541,21 +517,21 @@ struct DownArgs {
 };
 
 template <bool FULL>
-__global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
-  const int nbps = (p.H + 255) / 256;
-  const int u = blockIdx.x / nbps, nb = blockIdx.x % nbps;
+__global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
+  const int nbps = (p.H + 63) / 64;
+  const int u = blockIdx.x / nbps, nb = blockIdx.x - u * nbps;
   const SlotRange sr = work_slot(u, p.used, p.offsets, p.S, p.A);
   if (sr.s < 0) return;
   const int s = sr.s, p0 = sr.p0, p1 = sr.p1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = nb * 256 + wave * 64;
+  const int lane = threadIdx.x;
+  const int n0 = nb * 64;
   const int r = lane & 15, g = lane >> 4;
   const int I = p.I;
   const int nblk = I / 32;
   const int nsc = (nblk + 15) / 16;
   const uint8_t* base = p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)I / 2, srow = (size_t)I / 32;
-  extern __shared__ __align__(16) uint8_t wscale[];  // FULL: the workgroup's scale rows
+  extern __shared__ __align__(16) uint8_t wscale[];  // FULL: the wave's scale rows
   const int sstr = staged_scale_stride(I);
   const uint8_t* dc[4];
   const uint8_t* ds[4];
@@ -563,9 +539,9 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) {
     tv[tl] = n0 + 16 * tl < p.H;  // whole tile valid (H % 16 == 0)
-    const int row = tv[tl] ? n0 + 16 * tl + r : nb * 256 + r;  // an idle tile: a row in range
+    const int row = tv[tl] ? n0 + 16 * tl + r : n0 + r;  // an idle tile: a row in range
     dc[tl] = base + p.off_dc + (size_t)row * crow;
-    ds[tl] = FULL ? wscale + (row - nb * 256) * sstr : base + p.off_ds + (size_t)row * srow;
+    ds[tl] = FULL ? wscale + (row - n0) * sstr : base + p.off_ds + (size_t)row * srow;
   }
   RowSC pre[4];  // FULL: super-chunk 0 codes of the first column block, loaded early
   RowSC prex;    // FULL: and of its activation rows (codes; scale bytes in prexs)
@@ -583,13 +559,12 @@ __global__ __launch_bounds__(256) void down_kernel(DownArgs p) {
       zero_sc(prex);
       prexs = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);  // scale 1
     }
-    const uint8_t* const src[1] = {base + p.off_ds + (size_t)nb * 256 * srow};
-    stage_scale_rows<1>(src, min(256, p.H - nb * 256), (int)srow, sstr, 256, wscale);
+    const uint8_t* const src[1] = {base + p.off_ds + (size_t)n0 * srow};
+    stage_scale_rows<1>(src, min(64, p.H - n0), (int)srow, sstr, 64, wscale);
     __syncthreads();
   }
-  if (n0 >= p.H) return;
   // One block of 16 columns (assignment rows cb..) against the wave's 64 rows;
-  // the first block of a FULL workgroup takes super-chunk 0 from the early
+  // the first block of a FULL kernel takes super-chunk 0 from the early
   // loads (a separate copy of the loop, so those registers are free in the
   // others).
   auto column_block = [&](int cb, auto first) {
@@ -1219,13 +1194,13 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     g.k = k;
     g.A = A;
     g.S = S;
-    const int gblocks = maxU * ((I + 127) / 128);
+    const int gblocks = maxU * (I / 32);
     hipEvent_t gu0 = ev ? ev[1] : nullptr, gu1 = ev ? ev[2] : nullptr;
     if (staged_ok(H))
-      hipExtLaunchKernelGGL(gateup_kernel<true>, dim3(gblocks), dim3(256),
-                            2 * 128 * staged_scale_stride(H), stream, gu0, gu1, 0, g);
+      hipExtLaunchKernelGGL(gateup_kernel<true>, dim3(gblocks), dim3(kWave),
+                            2 * 32 * staged_scale_stride(H), stream, gu0, gu1, 0, g);
     else
-      hipExtLaunchKernelGGL(gateup_kernel<false>, dim3(gblocks), dim3(256), 0, stream, gu0, gu1,
+      hipExtLaunchKernelGGL(gateup_kernel<false>, dim3(gblocks), dim3(kWave), 0, stream, gu0, gu1,
                             0, g);
     DownArgs d;
     d.hq = hq;
@@ -1242,11 +1217,11 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     d.I = I;
     d.A = A;
     d.S = S;
-    const int dblocks = maxU * ((H + 255) / 256);
+    const int dblocks = maxU * ((H + 63) / 64);
     if (staged_ok(I))
-      down_kernel<true><<<dblocks, 256, 256 * staged_scale_stride(I), stream>>>(d);
+      down_kernel<true><<<dblocks, kWave, 64 * staged_scale_stride(I), stream>>>(d);
     else
-      down_kernel<false><<<dblocks, 256, 0, stream>>>(d);
+      down_kernel<false><<<dblocks, kWave, 0, stream>>>(d);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   }
   dim3 cgrid(T, (H + 1023) / 1024);
