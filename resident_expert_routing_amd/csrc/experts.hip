@@ -646,19 +646,39 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ sel_slot, int T,
                                                       int H, int k, int S,
                                                       uint16_t* __restrict__ out) {
+  constexpr int kB = 8;  // picks whose rows are loaded together
   const int t = blockIdx.x;
   const int h = (blockIdx.y * 256 + threadIdx.x) * 4;
   if (h >= H) return;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int sl = sel_slot[(size_t)t * k + j];
-    if (sl < 0 || sl >= S) continue;
-    const float wj = w[(size_t)t * k + j];
-    const float4 v = load_y4(y, ((size_t)t * k + j) * H + h);
-    a0 = fmaf(wj, v.x, a0);
-    a1 = fmaf(wj, v.y, a1);
-    a2 = fmaf(wj, v.z, a2);
-    a3 = fmaf(wj, v.w, a3);
+  for (int j0 = 0; j0 < k; j0 += kB) {
+    // Every row load of the batch is issued before the first sum: the rows of
+    // picks that are skipped (no slot) are read too (they lie in y, whose A
+    // rows are all allocated) but never added.  With S == 0, y may be null and
+    // nothing is read.
+    bool ok[kB];
+    float wj[kB];
+    float4 v[kB];
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int j = min(j0 + i, k - 1);
+      const int sl = sel_slot[(size_t)t * k + j];
+      ok[i] = j0 + i < k && sl >= 0 && sl < S;
+      wj[i] = w[(size_t)t * k + j];
+    }
+    if (S > 0) {
+#pragma unroll
+      for (int i = 0; i < kB; ++i) v[i] = load_y4(y, ((size_t)t * k + min(j0 + i, k - 1)) * H + h);
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      if (ok[i]) {
+        a0 = fmaf(wj[i], v[i].x, a0);
+        a1 = fmaf(wj[i], v[i].y, a1);
+        a2 = fmaf(wj[i], v[i].z, a2);
+        a3 = fmaf(wj[i], v[i].w, a3);
+      }
+    }
   }
   const uint32_t lo = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
   const uint32_t hi = f32_to_bf16(a2) | (f32_to_bf16(a3) << 16);
