@@ -686,18 +686,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 }
 
 // ===========================================================================
-// Pipelined path for larger batches (rows of 256-multiple length).  A work
+// Pipelined path for larger batches (rows of 512-multiple length).  A work
 // item is one M-tile of up to kTileM consecutive assignment rows of one slot;
 // the grid is work items x N-tiles.  Every operand reaches LDS through direct
-// global-to-LDS loads (lane i of a load lands at the LDS base + size * i),
-// issued two K chunks ahead of use into a ring of three stages.  A stage
-// holds one chunk (K = 128: 64 code bytes and 4 scale bytes per row) of the
-// four waves' 64 weight rows each and of the tile's 128 activation rows; the
-// ring is 77 KB and the kernel fits 256 VGPRs, so two workgroups share a CU
-// and one computes while the other waits at its stage barrier.  The 16-byte
-// block b of a 64-byte stage row r sits at position b ^ ((r >> 2) & 3): a
-// fragment read (32 rows, two blocks) spreads over all 16 four-bank groups,
-// four lanes each.
+// global-to-LDS loads (lane i of a load lands at the LDS base + size * i).
+// Code bytes are issued two K chunks ahead of use into a ring of three
+// stages; a stage holds one chunk (K = 128: 64 code bytes per row) of the
+// four waves' 64 weight rows each and of the tile's 128 activation rows.  The
+// E8M0 scales of four stages (16 bytes per row) are loaded together, one row
+// per lane, into a group buffer beside the ring: a load that touches one cache
+// line per lane then carries 16 bytes instead of 4 (with 4-byte loads every
+// stage, the scale loads were half of the cache lines requested and cost a
+// fifth of the kernel's time).  Ring and group buffer take 78 KB and the
+// kernel fits 256 VGPRs, so two workgroups share a CU and one computes while
+// the other waits at its stage barrier.  The 16-byte block b of a 64-byte
+// stage row r sits at position b ^ ((r >> 2) & 3): a fragment read (32 rows,
+// two blocks) spreads over all 16 four-bank groups, four lanes each.
 // ===========================================================================
 constexpr int kTileM = 128;                    // assignment rows per work item
 constexpr int kKc = 128;                       // K elements per stage
@@ -705,16 +709,19 @@ constexpr int kRowC = kKc / 2;                 // code bytes per row per stage (
 constexpr int kRowS = kKc / 32;                // scale bytes per row per stage (4)
 constexpr int kStageA = 4 * 64 * kRowC;        // weight code rows of the four waves
 constexpr int kStageB = kTileM * kRowC;        // activation code rows
-constexpr int kStageSA = 4 * 64 * kRowS;       // weight scale bytes
-constexpr int kStageSB = kTileM * kRowS;       // activation scales: 32 rows per wave
-constexpr int kStage = kStageA + kStageB + kStageSA + kStageSB;  // 26,112 bytes
+constexpr int kStage = kStageA + kStageB;      // 24,576 bytes
 constexpr int kRing = 3;
 constexpr int kAhead = kRing - 1;              // stages issued ahead of the one in use
-constexpr int kPipeLds = kRing * kStage;       // 78,336 bytes
+constexpr int kGroup = 4;                      // stages whose scales are loaded together
+constexpr int kGroupRow = kGroup * kRowS;      // scale bytes per row per group (16)
+constexpr int kGroupSA = 4 * 64 * kGroupRow;   // weight rows' scales (4,096 bytes)
+constexpr int kGroupSB = kTileM * kGroupRow;   // activation rows' scales: 32 rows per wave
+constexpr int kPipeLds = kRing * kStage + kGroupSA + kGroupSB;  // 79,872 bytes
+static_assert(2 * kPipeLds <= 160 * 1024, "two workgroups per CU");
 constexpr int kZeroPage = 256;                 // zeroed workspace bytes absent rows load from
-// Loads issued by each wave per stage: 4 weight-code, 2 activation-code,
-// 1 weight-scale and 1 activation-scale loads.
-constexpr int kLoadsPerStage = 8;
+// Loads issued by each wave per stage: 4 weight-code and 2 activation-code
+// loads; per group of stages, 1 weight-scale and 1 activation-scale load.
+constexpr int kLoadsPerStage = 6;
 
 // Work list of M-tiles of tm rows: items[0] = count, then per item (slot,
 // first row of the tile within the slot, index of the slot's first item, the
@@ -812,25 +819,17 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_base) {
                : "s"(m0), "v"(g)
                : "memory", "m0");
 }
-
-__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-               :
-               : "s"(m0), "v"(g)
-               : "memory", "m0");
-}
 #pragma clang diagnostic pop
 
 // Per-lane sources of the direct loads; stage q reads code bytes
-// [64 q, 64 q + 64) and scale bytes [4 q, 4 q + 4) of every row.
+// [64 q, 64 q + 64) of every row, group g scale bytes [16 g, 16 g + 16).
 struct PipeSrc {
   const uint8_t* a[4];   // weight codes, load j: wave row 16j + lane/4, block already swizzled
   const uint8_t* as;     // weight scales: wave row lane
   const uint8_t* b[2];   // activation codes, load j: tile row (2 wave + j) * 16 + lane/4
   int bstep[2];          // code bytes per stage (64; 0 for an absent row on the zero page)
   const uint8_t* bs;     // activation scales: tile row 32 wave + lane % 32
-  int bsstep;            // scale bytes per stage (4; 0 for an absent row)
+  int bsstep;            // scale bytes per group (16; 0 for an absent row)
 };
 
 __device__ __forceinline__ void pipe_issue(uint8_t* smem, const PipeSrc& src, int q, int wave) {
@@ -841,20 +840,29 @@ __device__ __forceinline__ void pipe_issue(uint8_t* smem, const PipeSrc& src, in
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + (2 * wave + j) * 1024);
-  uint8_t* ss = st + kStageA + kStageB;
-  dma4(src.as + (size_t)q * kRowS, ss + wave * 256);
-  if ((threadIdx.x & 63) < 32)  // lanes 0-31: one row each (a partial-lane load)
-    dma4(src.bs + (size_t)q * src.bsstep, ss + kStageSA + wave * 128);
 }
 
-// Waits until this wave's loads of stage q have landed (those of the stages
-// after it may still be in flight), then a workgroup barrier makes every
-// wave's share visible and frees the stage read in the previous iteration for
-// reuse.
+// The scale bytes of group g (stages 4g .. 4g+3): 16 bytes per row, row i of
+// the wave's 64 weight rows at lane i, and of its 32 activation rows at lanes
+// 0-31.
+__device__ __forceinline__ void pipe_issue_scales(uint8_t* smem, const PipeSrc& src, int g,
+                                                  int wave) {
+  uint8_t* sg = smem + kRing * kStage;
+  dma16(src.as + (size_t)g * kGroupRow, sg + wave * (64 * kGroupRow));
+  if ((threadIdx.x & 63) < 32)  // lanes 0-31: one row each (a partial-lane load)
+    dma16(src.bs + (size_t)g * src.bsstep, sg + kGroupSA + wave * (32 * kGroupRow));
+}
+
+// Waits until this wave's loads of stage q have landed, with those of its
+// scale group (issued before stage q + 1's loads), then a workgroup barrier
+// makes every wave's share visible and frees the stage read in the previous
+// iteration for reuse.  Issue order: group 0, stages 0 and 1, then in
+// iteration q stage q + 2, preceded by group g + 1 when q = 4g + 3; so
+// after stage q's loads only stage q + 1's six may still be in flight.
 __device__ __forceinline__ void pipe_wait(int q, int Q) {
-  static_assert(kLoadsPerStage == 8 && kAhead == 2, "wait counts below");
-  if (q + 1 < Q)  // stage q + 1 was issued after stage q
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  static_assert(kLoadsPerStage == 6 && kAhead == 2 && kGroup == 4, "wait counts below");
+  if (q + 1 < Q)
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -878,18 +886,29 @@ __device__ __forceinline__ void read_step(const uint8_t* st, int s, int wave, in
     f.b[cb] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * cb + r) * kRowC + pb);
 }
 
-__device__ __forceinline__ void pipe_compute(const uint8_t* smem, int q, int wave, int r, int hh,
-                                             v16f (&acc)[2][4]) {
-  const uint8_t* st = smem + (q % kRing) * kStage;
-  const uint8_t* ss = st + kStageA + kStageB;
-  const int swz = (r >> 2) & 3;
+// This lane's scale words of stage q (4 scale bytes of its rows: weight tile
+// t row r, column tile cb row r), from the group buffer.
+struct StageScales {
   uint32_t aw[2], bw[4];
+};
+
+__device__ __forceinline__ void read_stage_scales(const uint8_t* smem, int q, int wave, int r,
+                                                  StageScales& sc) {
+  const uint8_t* sg = smem + kRing * kStage + (q % kGroup) * kRowS;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
-    aw[t] = *reinterpret_cast<const uint32_t*>(ss + wave * 256 + (32 * t + r) * kRowS);
+    sc.aw[t] = *reinterpret_cast<const uint32_t*>(sg + (wave * 64 + 32 * t + r) * kGroupRow);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
-    bw[cb] = *reinterpret_cast<const uint32_t*>(ss + kStageSA + (32 * cb + r) * kRowS);
+    sc.bw[cb] = *reinterpret_cast<const uint32_t*>(sg + kGroupSA + (32 * cb + r) * kGroupRow);
+}
+
+__device__ __forceinline__ void pipe_compute(const uint8_t* smem, int q, int wave, int r, int hh,
+                                             const StageScales& sc, v16f (&acc)[2][4]) {
+  const uint8_t* st = smem + (q % kRing) * kStage;
+  const int swz = (r >> 2) & 3;
+  const uint32_t* aw = sc.aw;
+  const uint32_t* bw = sc.bw;
   StepFrags f[2];
   read_step(st, 0, wave, r, hh, swz, f[0]);
 #pragma unroll
@@ -916,13 +935,22 @@ __device__ __forceinline__ void pipe_mainloop(uint8_t* smem, const PipeSrc& src,
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[t][cb] = zero16();
+  pipe_issue_scales(smem, src, 0, wave);
 #pragma unroll
   for (int q = 0; q < kAhead; ++q)
     if (q < Q) pipe_issue(smem, src, q, wave);
   for (int q = 0; q < Q; ++q) {
     pipe_wait(q, Q);
+    StageScales sc;
+    read_stage_scales(smem, q, wave, r, sc);
+    if (q % kGroup == kGroup - 1 && q + 1 < Q) {
+      // every wave holds its last scale words of the group: reload the buffer
+      // (stage q's compute hides the load; stage q + 1 waits for it)
+      __syncthreads();
+      pipe_issue_scales(smem, src, (q + 1) / kGroup, wave);
+    }
     if (q + kAhead < Q) pipe_issue(smem, src, q + kAhead, wave);
-    pipe_compute(smem, q, wave, r, hh, acc);
+    pipe_compute(smem, q, wave, r, hh, sc, acc);
   }
 }
 
@@ -959,7 +987,7 @@ __device__ __forceinline__ void pipe_act_src(PipeSrc& src, RowPtr rowptr, size_t
   const int row = 32 * wave + (lane & 31);  // lanes 32-63 issue no activation-scale load
   const uint8_t* rp = rowptr(row);
   src.bs = rp ? rp + scale_off : zero;
-  src.bsstep = rp ? kRowS : 0;
+  src.bsstep = rp ? kGroupRow : 0;
 }
 
 struct PipeArgs {
@@ -1074,8 +1102,8 @@ struct ExpertsWs {
 };
 
 // Kernel family of a batch: batches of at least kPipeMinA assignments (T*k)
-// with H and I multiples of 256 take the pipelined kernels, every other batch
-// the small-batch kernels.  Measured crossover on the 4096/2048 model with 166
+// with H and I multiples of 512 (whole scale groups of 16 bytes per row)
+// take the pipelined kernels, every other batch the small-batch kernels.  Measured crossover on the 4096/2048 model with 166
 // slots: the small-batch kernels win up to 1024 assignments, the pipelined
 // ones from 2048.
 constexpr int kPipeMinA = 2048;
@@ -1083,7 +1111,7 @@ constexpr int kPipeMinA = 2048;
 enum Family { kFamSmall, kFamPipe };
 
 static Family family_of(int T, int k, int H, int I) {
-  if ((size_t)T * k >= (size_t)kPipeMinA && H % 256 == 0 && I % 256 == 0) return kFamPipe;
+  if ((size_t)T * k >= (size_t)kPipeMinA && H % 512 == 0 && I % 512 == 0) return kFamPipe;
   return kFamSmall;
 }
 

@@ -338,14 +338,15 @@ def test_layer_parity_long_sampled():
     (40, 8, 2, 8, 544, 160),     # H, I not multiples of 128
     (300, 8, 2, 5, 256, 128),    # small-batch kernels, many 16-column tiles per slot
     (129, 4, 1, 2, 544, 96),     # partial super-chunks in both GEMMs
-    (511, 16, 4, 10, 256, 256),  # 2044 assignments: largest batch on the small-batch kernels
-    (512, 16, 4, 10, 256, 256),  # 2048 assignments: smallest batch on the pipelined kernels
-    (515, 12, 4, 7, 512, 256),   # pipelined: several 128-row tiles, ragged last tile
+    (511, 16, 4, 10, 512, 512),  # 2044 assignments: largest batch on the small-batch kernels
+    (512, 16, 4, 10, 512, 512),  # 2048 assignments: smallest batch on the pipelined kernels
+    (515, 12, 4, 7, 512, 512),   # pipelined: several 128-row tiles, ragged last tile
     (600, 6, 6, 6, 1024, 512),   # every expert picked by every token: 600 rows per slot
     (9, 8, 2, 6, 512, 96),       # small batch, gate/up scales staged in LDS, ragged I (idle wave)
     (17, 8, 2, 6, 800, 512),     # small batch, down scales staged, last 256-row block of 32 rows
     (3, 6, 2, 4, 8192, 64),      # H past the LDS scale-staging limit: scales read per super-chunk
-    (520, 8, 4, 6, 768, 256),    # pipelined, six K chunks for gate/up and two for down
+    (520, 8, 4, 6, 768, 256),    # 2080 assignments, H not a multiple of 512: small-batch kernels
+    (520, 8, 4, 6, 1536, 1024),  # pipelined: three scale groups for gate/up, two for down
 ])
 def test_layer_edge_shapes(T, E, k, nr, H, I):
     say(f"layer edge T={T} E={E} k={k} routable={nr} H={H} I={I}")
@@ -381,7 +382,7 @@ def test_layer_sparse_slots_prebuilt_worklist():
 def test_layer_sparse_slots_tiled():
     """Pipelined path with used slots spread over 3000 slot ids."""
     say("pipelined layer with 12 routable experts spread over 3000 slots")
-    T, H, E, k, I, S = 600, 256, 16, 4, 256, 3000
+    T, H, E, k, I, S = 600, 512, 16, 4, 512, 3000
     lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=I, n_routable=12, seed=33, bias_scale=0.5)
     rng = np.random.default_rng(3)
     spread = rng.choice(S, size=12, replace=False)
