@@ -127,14 +127,17 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
 // bf16 x fp32 products are exact in float64 and every sum is float64; each
 // z[t,e] is the chain, over h in steps of 4 ascending, of the instruction's
 // float64 sum of its four products added to the running value (one fixed,
-// batch-independent order).  A workgroup owns 32 tokens x 64 experts; wave w
-// owns experts 16w..16w+15 of it (two 16x16 tiles, tokens 0-15 and 16-31).
-// K tiles of 32 are staged in LDS as float32 (exact for bf16 and fp32),
-// k-major with a 16-float pad so a fragment read hits 64 distinct banks, and
-// double-buffered through registers.
+// batch-independent order).  A workgroup owns 16 tokens x 64 experts; wave w
+// owns the 16x16 tile of experts 16w..16w+15.  16-token workgroups put two
+// waves on every SIMD at 2048 tokens (the float64 instruction's issue rate
+// rose from 32 to 45 TFLOP/s with a second wave in a probe; a second
+// accumulator chain in the same wave added little).  K tiles of 32 are staged
+// in LDS as float32 (exact for bf16 and fp32), k-major (the weight rows with a
+// 16-float pad) so a fragment read hits 64 distinct banks, and double-buffered
+// through registers.
 typedef double v4d __attribute__((ext_vector_type(4)));
-constexpr int RM_T = 32, RM_E = 64, RM_K = 32;
-constexpr int RM_XS = RM_T + 16, RM_WS = RM_E + 16;
+constexpr int RM_T = 16, RM_E = 64, RM_K = 32;
+constexpr int RM_XS = RM_T, RM_WS = RM_E + 16;
 
 __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restrict__ x,
                                                        const float* __restrict__ w, int T, int H,
@@ -143,20 +146,24 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
   __shared__ float ws[2][RM_K][RM_WS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.y * RM_T, e0 = blockIdx.x * RM_E;
-  // staging roles: x -- token tid/8, h 4(tid%8)..+3; w -- expert tid/4, h 8(tid%4)..+7
-  const int xt = tid >> 3, xq = tid & 7;
+  // staging roles: x -- token tid/8, h 4(tid%8)..+3 (threads 0-127); w -- expert
+  // tid/4, h 8(tid%4)..+7
+  const int xt = (tid >> 3) & (RM_T - 1), xq = tid & 7;
   const int we = tid >> 2, wq = tid & 3;
-  const bool xin = t0 + xt < T, win = e0 + we < E;
+  const bool xrole = tid < RM_T * 8;
+  const bool xin = xrole && t0 + xt < T, win = e0 + we < E;
   const uint16_t* xrow = x + (size_t)(xin ? t0 + xt : 0) * H + 4 * xq;
   const float* wrow = w + (size_t)(win ? e0 + we : 0) * H + 8 * wq;
   uint2 xv = xin ? *reinterpret_cast<const uint2*>(xrow) : make_uint2(0u, 0u);
   float4 w0 = win ? *reinterpret_cast<const float4*>(wrow) : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 w1 = win ? *reinterpret_cast<const float4*>(wrow + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   auto stage = [&](int b) {
-    xs[b][4 * xq + 0][xt] = bf16_to_f32(xv.x & 0xFFFFu);
-    xs[b][4 * xq + 1][xt] = bf16_to_f32(xv.x >> 16);
-    xs[b][4 * xq + 2][xt] = bf16_to_f32(xv.y & 0xFFFFu);
-    xs[b][4 * xq + 3][xt] = bf16_to_f32(xv.y >> 16);
+    if (xrole) {
+      xs[b][4 * xq + 0][xt] = bf16_to_f32(xv.x & 0xFFFFu);
+      xs[b][4 * xq + 1][xt] = bf16_to_f32(xv.x >> 16);
+      xs[b][4 * xq + 2][xt] = bf16_to_f32(xv.y & 0xFFFFu);
+      xs[b][4 * xq + 3][xt] = bf16_to_f32(xv.y >> 16);
+    }
     ws[b][8 * wq + 0][we] = w0.x;
     ws[b][8 * wq + 1][we] = w0.y;
     ws[b][8 * wq + 2][we] = w0.z;
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
   };
   stage(0);
   __syncthreads();
-  v4d acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
+  v4d acc0 = {0.0, 0.0, 0.0, 0.0};
   const int r = lane & 15, kq = lane >> 4;
   const int ntile = H / RM_K;
   for (int c = 0; c < ntile; ++c) {
@@ -184,23 +191,20 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
     for (int ks = 0; ks < RM_K / 4; ++ks) {
       const int k = 4 * ks + kq;
       const double a0 = (double)xs[b][k][r];
-      const double a1 = (double)xs[b][k][16 + r];
       const double bw = (double)ws[b][k][16 * wave + r];
       acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, bw, acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, bw, acc1, 0, 0, 0);
     }
     if (c + 1 < ntile) stage(b ^ 1);
     __syncthreads();
   }
-  // lane l holds rows (tokens) l/16 + 4v, column (expert) l%16 of each tile
+  // lane l holds rows (tokens) l/16 + 4v, column (expert) l%16 of the tile
   // (the float64 instruction's result layout, confirmed on the hardware)
   const int e = e0 + 16 * wave + r;
   if (e >= E) return;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int ta = t0 + kq + 4 * v, tb = ta + 16;
+    const int ta = t0 + kq + 4 * v;
     if (ta < T) z[(size_t)ta * E + e] = acc0[v];
-    if (tb < T) z[(size_t)tb * E + e] = acc1[v];
   }
 }
 
