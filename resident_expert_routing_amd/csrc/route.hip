@@ -742,10 +742,15 @@ __global__ __launch_bounds__(256) void bucket_hist(const int32_t* __restrict__ s
 
 // One workgroup: offsets = exclusive scan of the slot totals (S+1 entries),
 // and counts[s][c] replaced by the first perm position of chunk c's
-// assignments in slot s.  perm entries past the total are set to -1.  With
-// few chunks a thread walks whole slots; with many, a wave handles one slot
-// at a time (lanes over chunks).  One pass of 1024 threads scans the totals.
+// assignments in slot s.  perm entries past the total are set to -1.  When
+// the S x nchunk counts fit kScanLdsInts, they are first copied to LDS with
+// every load of a thread's batch issued before its stores (one round trip
+// per batch of 8), and a wave handles one slot at a time from LDS (lanes over
+// chunks).  Otherwise, with few chunks a thread walks whole slots in global
+// memory; with many, a wave handles one slot at a time.  One pass of 1024
+// threads scans the totals.
 constexpr int kScanWaveMinChunks = 16;
+constexpr int kScanLdsInts = 24 * 1024;  // counts staged in LDS (dynamic, 96 KB at most)
 
 __global__ __launch_bounds__(1024) void bucket_scan(int32_t* __restrict__ counts, int S,
                                                     int nchunk, int A,
@@ -753,13 +758,27 @@ __global__ __launch_bounds__(1024) void bucket_scan(int32_t* __restrict__ counts
                                                     int32_t* __restrict__ perm) {
   __shared__ int tot[MOE_MAX_S];
   __shared__ int wsum[16];
+  extern __shared__ int cl[];  // staged counts, when they fit
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const bool by_wave = nchunk >= kScanWaveMinChunks;
+  const int ncount = S * nchunk;
+  const bool staged = ncount > 0 && ncount <= kScanLdsInts;
+  const bool by_wave = staged || nchunk >= kScanWaveMinChunks;
+  if (staged) {
+    for (int i0 = 0; i0 < ncount; i0 += 8 * 1024) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = counts[min(i0 + j * 1024 + tid, ncount - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cl[min(i0 + j * 1024 + tid, ncount - 1)] = v[j];  // same value
+    }
+    __syncthreads();
+  }
+  // count c of slot s, from LDS when staged
+  auto cnt = [&](int s, int c) { return staged ? cl[s * nchunk + c] : counts[(size_t)s * nchunk + c]; };
   if (by_wave) {
     for (int s = wv; s < S; s += 16) {
-      const int32_t* cs = counts + (size_t)s * nchunk;
       int v = 0;
-      for (int c = lane; c < nchunk; c += 64) v += cs[c];
+      for (int c = lane; c < nchunk; c += 64) v += cnt(s, c);
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
       if (lane == 0) tot[s] = v;
@@ -803,7 +822,7 @@ __global__ __launch_bounds__(1024) void bucket_scan(int32_t* __restrict__ counts
       int carry = tot[s];
       for (int c0 = 0; c0 < nchunk; c0 += 64) {
         const int c = c0 + lane;
-        const int v = c < nchunk ? cs[c] : 0;
+        const int v = c < nchunk ? cnt(s, c) : 0;
         int inc = v;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
@@ -974,7 +993,9 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
                                                moe_demand_ws_bytes_internal(T, E));
   const size_t mask_lds = (size_t)(S > 0 ? S : 1) * sizeof(unsigned long long);
   if (S > 0) bucket_hist<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts);
-  bucket_scan<<<1, 1024, 0, stream>>>(counts, S, nbc, A, a->slot_offsets, a->perm);
+  const size_t scan_lds =
+      (size_t)S * nbc <= (size_t)kScanLdsInts ? (size_t)S * nbc * sizeof(int32_t) : 0;
+  bucket_scan<<<1, 1024, scan_lds, stream>>>(counts, S, nbc, A, a->slot_offsets, a->perm);
   if (!record_stage(ev,3, stream)) return MOE_EHIP;
   if (S > 0) bucket_place<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts, a->perm);
   if (!record_stage(ev,4, stream)) return MOE_EHIP;
