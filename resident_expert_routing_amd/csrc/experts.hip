@@ -630,16 +630,35 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
 // Combine: out[t] = sum_j (ascending) w[t,j] * y[t*k+j] in float32, rounded
 // once to bf16.  y rows are float32 (small-batch kernels) or bf16 (pipelined).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float4 load_y4(const float* y, size_t i) {
-  return *reinterpret_cast<const float4*>(y + i);
-}
+// The kEl elements of a y row from element i on, as float32.
+template <typename YT>
+struct YRow;
+template <>
+struct YRow<float> {  // small-batch kernels: float32 rows, 4 elements (16 bytes) per thread
+  static constexpr int kEl = 4;
+  __device__ static void load(const float* y, size_t i, float (&o)[kEl]) {
+    const float4 v = *reinterpret_cast<const float4*>(y + i);
+    o[0] = v.x;
+    o[1] = v.y;
+    o[2] = v.z;
+    o[3] = v.w;
+  }
+};
+template <>
+struct YRow<uint16_t> {  // pipelined kernels: bf16 rows, 8 elements (16 bytes) per thread
+  static constexpr int kEl = 8;
+  __device__ static void load(const uint16_t* y, size_t i, float (&o)[kEl]) {
+    const uint4 v = *reinterpret_cast<const uint4*>(y + i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = bf16_to_f32(w[q] & 0xFFFFu);
+      o[2 * q + 1] = bf16_to_f32(w[q] >> 16);
+    }
+  }
+};
 
-__device__ __forceinline__ float4 load_y4(const uint16_t* y, size_t i) {
-  const uint2 v = *reinterpret_cast<const uint2*>(y + i);
-  return make_float4(bf16_to_f32(v.x & 0xFFFFu), bf16_to_f32(v.x >> 16),
-                     bf16_to_f32(v.y & 0xFFFFu), bf16_to_f32(v.y >> 16));
-}
-
+// One thread per YRow<YT>::kEl consecutive elements of a token's output row.
 template <typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const float* __restrict__ w,
@@ -647,10 +666,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       int H, int k, int S,
                                                       uint16_t* __restrict__ out) {
   constexpr int kB = 8;  // picks whose rows are loaded together
+  constexpr int kEl = YRow<YT>::kEl;
   const int t = blockIdx.x;
-  const int h = (blockIdx.y * 256 + threadIdx.x) * 4;
-  if (h >= H) return;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  const int h = (blockIdx.y * 256 + threadIdx.x) * kEl;
+  if (h >= H) return;  // H % 32 == 0: a thread's elements are all in the row or all past it
+  float acc[kEl];
+#pragma unroll
+  for (int e = 0; e < kEl; ++e) acc[e] = 0.f;
   for (int j0 = 0; j0 < k; j0 += kB) {
     // Every row load of the batch is issued before the first sum: the rows of
     // picks that are skipped (no slot) are read too (they lie in y, whose A
@@ -658,7 +680,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
     // nothing is read.
     bool ok[kB];
     float wj[kB];
-    float4 v[kB];
+    float v[kB][kEl];
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
       const int j = min(j0 + i, k - 1);
@@ -668,21 +690,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
     }
     if (S > 0) {
 #pragma unroll
-      for (int i = 0; i < kB; ++i) v[i] = load_y4(y, ((size_t)t * k + min(j0 + i, k - 1)) * H + h);
+      for (int i = 0; i < kB; ++i)
+        YRow<YT>::load(y, ((size_t)t * k + min(j0 + i, k - 1)) * H + h, v[i]);
     }
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
       if (ok[i]) {
-        a0 = fmaf(wj[i], v[i].x, a0);
-        a1 = fmaf(wj[i], v[i].y, a1);
-        a2 = fmaf(wj[i], v[i].z, a2);
-        a3 = fmaf(wj[i], v[i].w, a3);
+#pragma unroll
+        for (int e = 0; e < kEl; ++e) acc[e] = fmaf(wj[i], v[i][e], acc[e]);
       }
     }
   }
-  const uint32_t lo = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
-  const uint32_t hi = f32_to_bf16(a2) | (f32_to_bf16(a3) << 16);
-  *reinterpret_cast<uint2*>(out + (size_t)t * H + h) = make_uint2(lo, hi);
+  uint16_t* o = out + (size_t)t * H + h;  // 8-byte aligned: four elements per store
+#pragma unroll
+  for (int e = 0; e < kEl; e += 4)
+    *reinterpret_cast<uint2*>(o + e) =
+        make_uint2(f32_to_bf16(acc[e]) | (f32_to_bf16(acc[e + 1]) << 16),
+                   f32_to_bf16(acc[e + 2]) | (f32_to_bf16(acc[e + 3]) << 16));
 }
 
 // ===========================================================================
@@ -1168,7 +1192,7 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   if (fam != kFamSmall && (g1 > 0x7FFFFFFFu || g2 > 0x7FFFFFFFu)) return MOE_EUNSUPPORTED;
   if (S == 0) {
     // nothing routable: every pick is padding, the output is zero
-    dim3 grid(T, (H + 1023) / 1024);
+    dim3 grid(T, (H + 256 * YRow<float>::kEl - 1) / (256 * YRow<float>::kEl));
     combine_kernel<float><<<grid, 256, 0, stream>>>(nullptr, a->sel_weight, a->sel_slot, T, H,
                                                     k, S, a->out);
     return hip_status();
@@ -1272,14 +1296,16 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
       down_kernel<false><<<dblocks, kWave, 0, stream>>>(d);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   }
-  dim3 cgrid(T, (H + 1023) / 1024);
-  if (fam != kFamSmall)
-    combine_kernel<uint16_t><<<cgrid, 256, 0, stream>>>(reinterpret_cast<const uint16_t*>(y),
-                                                        a->sel_weight, a->sel_slot, T, H, k, S,
-                                                        a->out);
-  else
-    combine_kernel<float><<<cgrid, 256, 0, stream>>>(y, a->sel_weight, a->sel_slot, T, H, k, S,
-                                                     a->out);
+  // a workgroup covers 256 threads x YRow<YT>::kEl elements of a token's row
+  if (fam != kFamSmall) {
+    const int per = 256 * YRow<uint16_t>::kEl;
+    combine_kernel<uint16_t><<<dim3(T, (H + per - 1) / per), 256, 0, stream>>>(
+        reinterpret_cast<const uint16_t*>(y), a->sel_weight, a->sel_slot, T, H, k, S, a->out);
+  } else {
+    const int per = 256 * YRow<float>::kEl;
+    combine_kernel<float><<<dim3(T, (H + per - 1) / per), 256, 0, stream>>>(
+        y, a->sel_weight, a->sel_slot, T, H, k, S, a->out);
+  }
   if (!record_stage(ev, 4, stream)) return MOE_EHIP;
   return hip_status();
 }
