@@ -347,6 +347,9 @@ def test_layer_parity_long_sampled():
     (3, 6, 2, 4, 8192, 64),      # H past the LDS scale-staging limit: scales read per super-chunk
     (520, 8, 4, 6, 768, 256),    # 2080 assignments, H not a multiple of 512: small-batch kernels
     (520, 8, 4, 6, 1536, 1024),  # pipelined: three scale groups for gate/up, two for down
+    (40, 16, 12, 14, 256, 128),  # k = 12: the combine adds a batch of 8 picks, then one of 4
+    (20, 40, 32, 36, 256, 128),  # k = 32 (the maximum): four batches of 8 picks
+    (200, 40, 12, 30, 512, 512),  # pipelined (2400 assignments) with k = 12, bf16 y rows
 ])
 def test_layer_edge_shapes(T, E, k, nr, H, I):
     say(f"layer edge T={T} E={E} k={k} routable={nr} H={H} I={I}")
