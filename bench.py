@@ -78,7 +78,7 @@ def copy_calibration():
 
 def gateup_kernel_name(T: int, k: int, H: int, I: int) -> str:
     """The gate/up kernel moe_experts_forward launches for this batch shape."""
-    tiled = T * k >= 2048 and H % 256 == 0 and I % 256 == 0
+    tiled = T * k >= 2048 and H % 512 == 0 and I % 512 == 0
     return "gateup_pipe" if tiled else "gateup_kernel"
 
 
@@ -208,6 +208,77 @@ def bench_arena40(args):
                    "GB_per_s_h2d": len(ev) * sa.arena.slot_bytes / replan_s / 1e9},
     }
     print(json.dumps(result), flush=True)
+
+
+def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5):
+    """Layer calls of the long chunk with the hot read (route, pick the heaviest
+    miss, copy its 20 MB from page-locked host memory into the coldest arena
+    expert's slot on a side stream, route again, experts after the copy) and
+    without it, each timed on the host around the call with a synchronisation;
+    the copy alone is timed with events on the side stream.  Never part of
+    `value`: the copy crosses PCIe."""
+    import numpy as np
+    import torch
+    from resident_expert_routing_amd import runtime as R
+
+    dev = x.device
+    es0 = lay.expert_slot.astype(np.int32)
+    hist = torch.zeros(E, dtype=torch.float64, device=dev)
+    es = torch.from_numpy(es0).to(dev)
+    n_arena = lay.extra["n_resident"]
+
+    def plain():
+        es.copy_(torch.from_numpy(es0))
+        R.route(buf, x, w_router, bias, es, stream, hist_row=hist)
+        R.experts(buf, arena.ptr(), arena.stride, stream)
+
+    def with_hot():
+        es.copy_(torch.from_numpy(es0))
+        hot = R.HotReader(es0, n_arena, dev)
+        hot._pinned = pinned  # the expert's page-locked copy is made once, outside the timing
+        picked = R.layer_step_hot(buf, x, w_router, bias, es, hist, arena, hot, lay.expert_bytes,
+                                  stream)
+        return picked, hot
+
+    pinned = {}
+    # warm: make the page-locked copy of the expert that will be loaded
+    picked, hot = with_hot()
+    torch.cuda.synchronize()
+    if picked is None:
+        return {"loaded": None, "note": "no pick with a share of at least 0.2 in this chunk"}
+    pinned.update(hot._pinned)
+    times = {"plain": [], "hot": []}
+    for _ in range(reps):
+        for kind, fn in (("plain", plain), ("hot", with_hot)):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            times[kind].append(time.perf_counter() - t0)
+    # the copy alone, timed on the side stream
+    hot = R.HotReader(es0, n_arena, dev)
+    src = pinned[next(iter(pinned))]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    slot = int(es0[picked[1]])
+    from resident_expert_routing_amd import binding as B
+    with torch.cuda.stream(hot.side):
+        e0.record(hot.side)
+    B.check(B.arena_load_slot(arena.mem, arena.stride, arena.S, slot, src, arena.slot_bytes,
+                              hot.side, None), "arena_load_slot")
+    with torch.cuda.stream(hot.side):
+        e1.record(hot.side)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1)
+    # put the evicted expert's bytes back, so the arena is as the bench found it
+    arena.upload(lambda s: lay.content_bytes(lay.slot_content()[s]), slots=[slot])
+    torch.cuda.synchronize()
+    return {"loaded": int(picked[0]), "evicted": int(picked[1]), "slot": slot,
+            "bytes_h2d": int(arena.slot_bytes),
+            "ms_layer_with_hot_read": 1e3 * float(np.median(times["hot"])),
+            "ms_layer_without": 1e3 * float(np.median(times["plain"])),
+            "ms_copy": copy_ms, "GB_per_s_copy": arena.slot_bytes / (copy_ms * 1e-3) / 1e9,
+            "timing": "host clock around each call with synchronisations (median of "
+                      f"{reps}); the copy alone with events on the side stream"}
 
 
 def main():
@@ -343,6 +414,9 @@ def main():
                   "mxfp4_tflops": flops / (ms_step * 1e-3) / 1e12, "wall_s": wall},
     }
     log(f"gate/up: {gu_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
+    if name == "long":
+        result["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
+                                             stream)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one layer call")
         result["cpu_baseline"] = cpu_baseline(base, k)

@@ -133,7 +133,8 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *          sel_weight [T][k] float; slot_offsets [S+1] int32; perm [T*k] int32;
  *          xq [T][moe_mxfp4_row_bytes(H)] uint8 (16-byte aligned).
  * Workspace: moe_workspace_bytes(MOE_OP_ROUTE, T, H, E, k, 0, S) bytes, 256-byte
- *          aligned.  Contents on return are unspecified.
+ *          aligned.  Contents on return are unspecified, except the router's
+ *          dot products (see reuse_logits).
  * T = 0 is valid (only slot_offsets is written, all zero).
  * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
  *          `stream` when T > 0: before the router logits, before selection,
@@ -149,6 +150,16 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *          float64 result): hist_row[e] += delta[e], delta (if non-null) gets
  *          the per-call demand.  For small batches this runs inside the
  *          selection kernel and saves a launch.
+ * reuse_logits: nonzero skips the router's dot products: they are taken from
+ *          the workspace, and xq is left as written, by the previous moe_route
+ *          call made with the same T, H, E, x, w_router, xq and ws (nothing
+ *          else may have written ws or xq since); expert_slot, S, bias and the
+ *          output buffers may differ.  Selection, renormalisation and
+ *          bucketing run as usual, so the results equal those of a call
+ *          without the flag.  For a hot read: route again over a changed
+ *          routable set without recomputing the products.  On every return
+ *          with T > 0 the first T*E*8 bytes of ws hold them (float64 [T][E],
+ *          x . w_router before the bias).
  */
 #define MOE_STAGE_EVENTS 5
 
@@ -171,6 +182,7 @@ typedef struct moe_route_args {
   hipEvent_t* stage_events;
   double* hist_row;
   float* delta;
+  int reuse_logits;
 } moe_route_args;
 
 int moe_route(const moe_route_args* args, hipStream_t stream);

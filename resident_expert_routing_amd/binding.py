@@ -49,7 +49,7 @@ class RouteArgs(ctypes.Structure):
                 ("slot_offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
                 ("xq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
                 ("stage_events", ctypes.c_void_p), ("hist_row", ctypes.c_void_p),
-                ("delta", ctypes.c_void_p)]
+                ("delta", ctypes.c_void_p), ("reuse_logits", ctypes.c_int)]
 
 
 class ExpertsArgs(ctypes.Structure):
@@ -185,12 +185,14 @@ def moe_workspace_bytes(op: int, T: int, H: int, E: int, k: int, I: int, S: int)
 
 def moe_route(T, H, E, k, S, x, w_router, bias, expert_slot, topk_expert, topk_score,
               sel_expert, sel_weight, sel_slot, slot_offsets, perm, xq, ws, ws_bytes,
-              stream=None, stage_events=None, hist_row=None, delta=None) -> int:
+              stream=None, stage_events=None, hist_row=None, delta=None,
+              reuse_logits=False) -> int:
     keep, evp = _events(stage_events)
     a = RouteArgs(int(T), int(H), int(E), int(k), int(S), _ptr(x), _ptr(w_router), _ptr(bias),
                   _ptr(expert_slot), _ptr(topk_expert), _ptr(topk_score), _ptr(sel_expert),
                   _ptr(sel_weight), _ptr(sel_slot), _ptr(slot_offsets), _ptr(perm), _ptr(xq),
-                  _ptr(ws), int(ws_bytes), evp, _ptr(hist_row), _ptr(delta))
+                  _ptr(ws), int(ws_bytes), evp, _ptr(hist_row), _ptr(delta),
+                  1 if reuse_logits else 0)
     return int(load().moe_route(ctypes.byref(a), _stream(stream)))
 
 

@@ -935,7 +935,11 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
                                                   route_z_bytes(T, E) +
                                                   moe_demand_ws_bytes_internal(T, E));
   if (!record_stage(ev,0, stream)) return MOE_EHIP;
-  if (small_router) {
+  if (a->reuse_logits) {
+    // z and xq stay from the previous call; only the fused kernel's counter,
+    // which the router would zero, needs clearing
+    if (fused) fill_i32<<<1, 256, 0, stream>>>(reinterpret_cast<int32_t*>(counter), 1, 0);
+  } else if (small_router) {
     const int nrb = E * ((T + RS_T - 1) / RS_T);
     const size_t nx = ((size_t)T * H + 255) / 256;
     const int nxb = (int)(nx < 1024 ? nx : 1024);
@@ -963,7 +967,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   p.sel_slot = a->sel_slot;
   p.xq = a->xq;
   p.xq_row = xq_row;
-  p.quantize_x = small_router ? 0 : 1;
+  p.quantize_x = (small_router || a->reuse_logits) ? 0 : 1;
   p.hist = nullptr;
   p.delta = nullptr;
   const int A = T * k;

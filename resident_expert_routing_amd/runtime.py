@@ -82,13 +82,16 @@ class Arena:
 
 
 def route(buf: LayerBuffers, x, w_router, bias, expert_slot, stream=None,
-          stage_events=None, hist_row=None) -> None:
-    """moe_route; with hist_row it also accumulates this batch's demand."""
+          stage_events=None, hist_row=None, reuse_logits=False) -> None:
+    """moe_route; with hist_row it also accumulates this batch's demand.
+    reuse_logits: the previous route on these buffers had the same x and
+    w_router (only the routable set changed): skip the router's products."""
     B.check(B.moe_route(buf.T, buf.H, buf.E, buf.k, buf.S, x, w_router, bias, expert_slot,
                         buf.topk_expert, buf.topk_score, buf.sel_expert, buf.sel_weight,
                         buf.sel_slot, buf.slot_offsets, buf.perm, buf.xq, buf.ws_route,
                         buf.ws_route_bytes, stream, stage_events, hist_row,
-                        buf.delta if hist_row is not None else None), "moe_route")
+                        buf.delta if hist_row is not None else None, reuse_logits),
+            "moe_route")
 
 
 def demand(buf: LayerBuffers, hist_row, stream=None, delta=True) -> None:
@@ -156,13 +159,14 @@ def layer_step_hot(buf: LayerBuffers, x, w_router, bias, expert_slot_dev, hist_r
     """One layer call with a hot read before the experts (long prefill chunks).
 
     Route with demand, decide and start the copy, route again over the new
-    routable set (overlapping the copy), then run the experts after the copy.
+    routable set (the router's products reused; overlapping the copy), then
+    run the experts after the copy.
     """
     stream = stream if stream is not None else torch.cuda.current_stream(hot.device)
     route(buf, x, w_router, bias, expert_slot_dev, stream, hist_row=hist_row)
     picked = hot.pick_and_load(buf, expert_slot_dev, hist_row, arena, expert_bytes_fn, stream)
     if picked is not None:
-        route(buf, x, w_router, bias, expert_slot_dev, stream)
+        route(buf, x, w_router, bias, expert_slot_dev, stream, reuse_logits=True)
         stream.wait_event(hot.done)
     experts(buf, arena.ptr(), arena.stride, stream)
     return picked

@@ -205,6 +205,49 @@ def test_route_worked_example_ties():
     assert buf.perm.cpu().numpy().tolist() == [3, 0, 4, 1, 5, 2]
 
 
+@pytest.mark.parametrize("T,E,k", [(40, 32, 4), (300, 32, 4), (9, 200, 8)])
+def test_route_reuse_logits(T, E, k):
+    """A second moe_route over a changed routable set with the router's products
+    reused gives exactly what a fresh call over that set gives (fused path for
+    T <= 64, multi-kernel path above)."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    say(f"moe_route reuse_logits T={T} E={E} k={k}")
+    H = 256
+    lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=32, n_routable=E // 2, seed=T + E,
+                              bias_scale=0.5)
+    S = E // 2
+    es1 = lay.expert_slot.copy()
+    dev = torch.device("cuda", 0)
+    buf = R.LayerBuffers(T, H, E, k, 32, S, dev)
+    x = to_dev(lay.x_bits.view(np.int16))
+    w, b = to_dev(lay.w_router), to_dev(lay.bias)
+    keys = ("topk_expert", "topk_score", "sel_expert", "sel_weight", "sel_slot",
+            "slot_offsets", "perm", "xq")
+
+    def outputs():
+        torch.cuda.synchronize()
+        return {key: getattr(buf, key).cpu().numpy().copy() for key in keys}
+
+    # a hot read's table change: the most picked routable expert leaves, a
+    # non-routable one takes its slot
+    R.route(buf, x, w, b, to_dev(es1))
+    picks = outputs()["sel_expert"]
+    gone = int(np.bincount(picks[picks >= 0], minlength=E).argmax())
+    came = int(np.flatnonzero(es1 < 0)[0])
+    es2 = es1.copy()
+    es2[came], es2[gone] = es1[gone], -1
+    R.route(buf, x, w, b, to_dev(es2))
+    fresh = outputs()
+    R.route(buf, x, w, b, to_dev(es1))
+    first = outputs()
+    R.route(buf, x, w, b, to_dev(es2), reuse_logits=True)
+    again = outputs()
+    for key in keys:
+        assert np.array_equal(again[key], fresh[key]), key
+    assert not np.array_equal(first["sel_slot"], fresh["sel_slot"]), "the table change mattered"
+
+
 @pytest.mark.parametrize("T,E,k,nr,S,H", [
     (1, 16, 4, 10, 10, 256),     # single token
     (13, 16, 4, 10, 10, 256),    # ragged token count
