@@ -377,11 +377,32 @@ def main():
     gu_ms = float(np.mean([a_.elapsed_time(b_) for a_, b_ in ev]))
     ms_step_ev = r0.elapsed_time(r1) / K
 
+    # ---- routing alone (router, selection, demand, bucketing, MXFP4 rows) ----
+    q0, q1 = mk(), mk()
+    torch.cuda.synchronize()
+    q0.record(stream)
+    for i in range(K):
+        R.route(buf, xs[i % nrot], w_router, bias, expert_slot, stream, hist_row=hist)
+    q1.record(stream)
+    torch.cuda.synchronize()
+    route_us = q0.elapsed_time(q1) * 1e3 / K
+
     A = T * k
     u_steps = [U[i % nrot] for i in range(K)]
     gu_bytes = float(np.mean([u * gateup_bytes_per_slot(H, I) for u in u_steps])) \
         + T * (H // 2 + H // 32) + A * (I // 2 + I // 32)
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    gu_flops = 4.0 * H * I * A
+    # roofline of the gate/up kernel: memory-bound below the MXFP4 ridge
+    # (peak flops / peak bytes), matrix-bound above it
+    ridge = MXFP4_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if gu_flops / gu_bytes > ridge:
+        roof = {"bound": "mfma", "achieved": gu_flops / (gu_ms * 1e-3) / 1e12,
+                "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": gu_bytes / (gu_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    achieved = roof["achieved"]
     layer_bytes = float(np.mean([u * expert_bytes(H, I) for u in u_steps])) + H * E * 4 + 2 * T * H * 2
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
     flops = 6.0 * H * I * A
@@ -403,17 +424,19 @@ def main():
                                f"resident={cfg.resident} ring={cfg.ring} S={S}",
                    "T": T, "H": H, "E": E, "k": k, "I": I, "S": S, "rotate": nrot,
                    "zipf_beta": base.beta},
-        "roofline": {"bound": "hbm", "kernel": gateup_kernel_name(T, k, H, I), "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+        "roofline": {**roof, "kernel": gateup_kernel_name(T, k, H, I),
                      "traffic": traffic_from_profile(name), "algo_bytes_per_launch": gu_bytes,
-                     "mean_launch_us": gu_ms * 1e3,
+                     "algo_flops_per_launch": gu_flops, "mean_launch_us": gu_ms * 1e3,
                      "ms_per_step_with_these_events": ms_step_ev},
         "layer": {"algo_bytes_per_step": layer_bytes, "GB_per_s": layer_gbs,
                   "hbm_frac": layer_gbs / HBM_PEAK_GBS, "distinct_slots_used": U,
                   "assignments_per_s": A * K / (total_ms * 1e-3),
-                  "mxfp4_tflops": flops / (ms_step * 1e-3) / 1e12, "wall_s": wall},
+                  "mxfp4_tflops": flops / (ms_step * 1e-3) / 1e12,
+                  "mxfp4_frac": flops / (ms_step * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS,
+                  "routing_us_per_call": route_us, "wall_s": wall},
     }
-    log(f"gate/up: {gu_ms * 1e3:.1f} us, {achieved:.0f} GB/s")
+    log(f"gate/up: {gu_ms * 1e3:.1f} us, {achieved:.0f} {roof['unit']}; "
+        f"routing alone {route_us:.1f} us per call")
     if name == "long":
         result["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
                                              stream)
