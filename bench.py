@@ -210,6 +210,45 @@ def bench_arena40(args):
     print(json.dumps(result), flush=True)
 
 
+def achievable_peak(bound: str, dev) -> dict:
+    """The device's achievable peak for the roofline's bound, measured now with
+    the library's microbenchmarks: an 8 GiB read (32x the Infinity Cache,
+    16-byte loads, four in flight per thread; three launches back to back, so
+    the launch ramps weigh little) or a loop of the MXFP4 32x32x64
+    instruction; the best of the repetitions."""
+    import torch
+    from resident_expert_routing_amd import binding as B
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    best = 0.0
+    if bound == "hbm":
+        n, grid, back = 8 << 30, 8192, 3
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            e0, e1 = mk(), mk()
+            e0.record()
+            for _ in range(back):
+                B.check(B.moe_test_stream_read(src, n, sink, grid), "moe_test_stream_read")
+            e1.record()
+            torch.cuda.synchronize()
+            best = max(best, back * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        del src
+        return {"achievable_peak": best, "achievable_how": "moe_test_stream_read: 3 reads of "
+                "8 GiB back to back, best of 3"}
+    iters, grid = 1000, 1024
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    flops = grid * 4 * iters * 8 * 2.0 * 32 * 32 * 64
+    for _ in range(6):
+        e0, e1 = mk(), mk()
+        e0.record()
+        B.check(B.moe_test_mfma_loop(iters, sink, grid), "moe_test_mfma_loop")
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return {"achievable_peak": best, "achievable_how": "moe_test_mfma_loop: 32x32x64 MXFP4 "
+            "instruction, 8 chains per wave, best of 6 launches"}
+
+
 def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5):
     """Layer calls of the long chunk with the hot read (route, pick the heaviest
     miss, copy its 20 MB from page-locked host memory into the coldest arena
@@ -402,6 +441,8 @@ def main():
         roof = {"bound": "hbm", "achieved": gu_bytes / (gu_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    roof.update(achievable_peak(roof["bound"], dev))
+    roof["achievable_frac"] = roof["achieved"] / roof["achievable_peak"]
     achieved = roof["achieved"]
     layer_bytes = float(np.mean([u * expert_bytes(H, I) for u in u_steps])) + H * E * 4 + 2 * T * H * 2
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9

@@ -334,6 +334,34 @@ int moe_replan(const double* hist, const int32_t* expert_slot, int L, int E, int
 int moe_test_mxfp4_probe(int shape, const uint8_t* a, const uint8_t* a_scale, const uint8_t* b,
                          const uint8_t* b_scale, float* d, hipStream_t stream);
 
+/*
+ * moe_test_stream_read -- test-only microbenchmark: the achievable memory read
+ * rate on this device, against which the expert kernels' rooflines are also
+ * read (the vendor peak is the other).  `grid` workgroups of 256 threads read
+ * src[0, bytes) once, 16 bytes per thread per load, four loads in flight per
+ * thread, consecutive threads on consecutive 16-byte units; each thread
+ * writes the XOR of what it read to sink[workgroup * 256 + thread] (so the
+ * loads cannot be dropped).  src: device memory, 16-byte aligned, bytes a
+ * positive multiple of 16; sink: device memory of grid * 256 uint32, owned by
+ * the caller.  MOE_EINVAL for a null pointer, misalignment, bytes not a
+ * positive multiple of 16 or grid outside [1, 65536].
+ */
+int moe_test_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid,
+                         hipStream_t stream);
+
+/*
+ * moe_test_mfma_loop -- test-only microbenchmark: the achievable rate of the
+ * v_mfma_scale_f32_32x32x64_f8f6f4 instruction with E2M1 operands (the
+ * pipelined expert kernels' instruction).  `grid` workgroups of 256 threads;
+ * every wave runs `iters` rounds of 8 independent accumulator chains (one
+ * instruction each, 2*32*32*64 flops), so the launch does
+ * grid * 4 * iters * 8 * 131072 flops; each thread writes the sum of its
+ * accumulators to sink[workgroup * 256 + thread].  sink: device memory of
+ * grid * 256 floats.  MOE_EINVAL for a null sink, iters outside [1, 1<<20] or
+ * grid outside [1, 65536].
+ */
+int moe_test_mfma_loop(int iters, float* sink, int grid, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

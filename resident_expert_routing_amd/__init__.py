@@ -10,10 +10,12 @@ from . import binding
 from .binding import (MoeError, arena_load_slot, check, moe_demand_accumulate,
                       moe_experts_forward, moe_hot_pick, moe_mxfp4_row_bytes, moe_replan, moe_route,
                       moe_slot_bytes, moe_slot_sections, moe_status_string,
-                      moe_test_mxfp4_probe, moe_workspace_bytes)
+                      moe_test_mfma_loop, moe_test_mxfp4_probe, moe_test_stream_read,
+                      moe_workspace_bytes)
 
 binding.load()
 
 __all__ = ["binding", "MoeError", "arena_load_slot", "check", "moe_demand_accumulate",
            "moe_experts_forward", "moe_hot_pick", "moe_mxfp4_row_bytes", "moe_replan", "moe_route", "moe_slot_bytes",
-           "moe_slot_sections", "moe_status_string", "moe_test_mxfp4_probe", "moe_workspace_bytes"]
+           "moe_slot_sections", "moe_status_string", "moe_test_mfma_loop", "moe_test_mxfp4_probe",
+           "moe_test_stream_read", "moe_workspace_bytes"]

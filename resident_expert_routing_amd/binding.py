@@ -30,7 +30,8 @@ MOE_MAX_S = 8192
 
 EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
-           "arena_load_slot", "moe_hot_pick", "moe_replan", "moe_test_mxfp4_probe")
+           "arena_load_slot", "moe_hot_pick", "moe_replan", "moe_test_mxfp4_probe",
+           "moe_test_stream_read", "moe_test_mfma_loop")
 
 
 class MoeError(RuntimeError):
@@ -106,6 +107,10 @@ def load() -> ctypes.CDLL:
     lib.moe_replan.restype = i
     lib.moe_test_mxfp4_probe.argtypes = [i, vp, vp, vp, vp, vp, vp]
     lib.moe_test_mxfp4_probe.restype = i
+    lib.moe_test_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i, vp]
+    lib.moe_test_stream_read.restype = i
+    lib.moe_test_mfma_loop.argtypes = [i, vp, i, vp]
+    lib.moe_test_mfma_loop.restype = i
     _lib = lib
     return lib
 
@@ -242,3 +247,12 @@ def moe_test_mxfp4_probe(shape, a, a_scale, b, b_scale, d, stream=None) -> int:
 def check(status: int, what: str = "moe") -> None:
     if status != MOE_OK:
         raise MoeError(status, what)
+
+
+def moe_test_stream_read(src, nbytes, sink, grid, stream=None) -> int:
+    return int(load().moe_test_stream_read(_ptr(src), int(nbytes), _ptr(sink), int(grid),
+                                           _stream(stream)))
+
+
+def moe_test_mfma_loop(iters, sink, grid, stream=None) -> int:
+    return int(load().moe_test_mfma_loop(int(iters), _ptr(sink), int(grid), _stream(stream)))

@@ -1,6 +1,7 @@
-// Test-only probe of the block-scaled MXFP4 matrix instructions the expert
-// kernels use: one wave, one MFMA on raw per-lane operands, results as the
-// lanes hold them.
+// Test-only probes: the block-scaled MXFP4 matrix instructions the expert
+// kernels use (one wave, one MFMA on raw per-lane operands, results as the
+// lanes hold them), and two microbenchmarks of the achievable read and MXFP4
+// matrix rates.
 #include "common.hpp"
 
 namespace moe {
@@ -33,7 +34,64 @@ __global__ __launch_bounds__(64) void mxfp4_probe(const uint8_t* a, const uint8_
       o[q] = make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
   }
 }
+// Achievable read rate: each thread reads 16-byte units i, i + G, i + 2G,
+// i + 3G (G = threads in the grid) per round, all four in flight together.
+__global__ __launch_bounds__(256) void stream_read(const uint4* __restrict__ src, size_t n16,
+                                                   uint32_t* __restrict__ sink) {
+  const size_t G = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0u;
+  for (; i + 3 * G < n16; i += 4 * G) {
+    const uint4 a = src[i], b = src[i + G], c = src[i + 2 * G], d = src[i + 3 * G];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
+           d.z ^ d.w;
+  }
+  for (; i < n16; i += G) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+// Achievable MXFP4 matrix rate: 8 independent 32x32x64 accumulator chains per
+// wave; the operands come from the lane index, so nothing folds away.
+__global__ __launch_bounds__(256) void mfma_loop(int iters, float* __restrict__ sink) {
+  const int l = threadIdx.x;
+  const pv8i A = {l, l + 1, l + 2, l + 3, 0, 0, 0, 0};
+  const pv8i B = {3 * l, l ^ 5, l + 7, l ^ 9, 0, 0, 0, 0};
+  pv16f c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[j][i] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c[j], 4, 4, 0, 100 + j, 0, 120);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += c[j][i];
+  sink[(size_t)blockIdx.x * 256 + l] = s;
+}
 }  // namespace moe
+
+extern "C" MOE_EXPORT int moe_test_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                                               int grid, hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || grid < 1 || grid > 65536)
+    return MOE_EINVAL;
+  if (!moe::aligned(src, 16)) return MOE_EINVAL;
+  moe::stream_read<<<grid, 256, 0, stream>>>(static_cast<const uint4*>(src), bytes / 16, sink);
+  return moe::hip_status();
+}
+
+extern "C" MOE_EXPORT int moe_test_mfma_loop(int iters, float* sink, int grid, hipStream_t stream) {
+  if (!sink || iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536) return MOE_EINVAL;
+  moe::mfma_loop<<<grid, 256, 0, stream>>>(iters, sink);
+  return moe::hip_status();
+}
 
 extern "C" MOE_EXPORT int moe_test_mxfp4_probe(int shape, const uint8_t* a, const uint8_t* a_scale,
                                                const uint8_t* b, const uint8_t* b_scale, float* d,

@@ -174,6 +174,15 @@ def test_probe_rejects():
     assert B.moe_test_mxfp4_probe(0, None, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
     assert B.moe_test_mxfp4_probe(1, FAKE + 4, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
     assert B.moe_test_mxfp4_probe(2, FAKE, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL
+    # microbenchmarks: validation before any HIP call
+    assert B.moe_test_stream_read(None, 256, FAKE, 4) == B.MOE_EINVAL
+    assert B.moe_test_stream_read(FAKE, 0, FAKE, 4) == B.MOE_EINVAL
+    assert B.moe_test_stream_read(FAKE, 24, FAKE, 4) == B.MOE_EINVAL
+    assert B.moe_test_stream_read(FAKE + 8, 256, FAKE, 4) == B.MOE_EINVAL
+    assert B.moe_test_stream_read(FAKE, 256, FAKE, 0) == B.MOE_EINVAL
+    assert B.moe_test_mfma_loop(10, None, 4) == B.MOE_EINVAL
+    assert B.moe_test_mfma_loop(0, FAKE, 4) == B.MOE_EINVAL
+    assert B.moe_test_mfma_loop(10, FAKE, 70000) == B.MOE_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
