@@ -145,7 +145,12 @@ def _event(e) -> int | None:
         return None
     if isinstance(e, int):
         return e
-    return int(e.cuda_event)
+    h = int(e.cuda_event)
+    if h == 0:
+        # torch creates the HIP event on its first record; a null handle would
+        # make the library skip the record and a later wait on it a no-op
+        raise ValueError("torch.cuda.Event has no HIP event yet: record it once before passing it")
+    return h
 
 
 def _events(evs):

@@ -408,6 +408,7 @@ struct GateUpArgs {
   const int32_t* offsets;
   const int32_t* perm;
   const int32_t* used;  // prebuilt work list, or null: found in place
+  int32_t* slots;       // out: (slot, p0, p1) of work item u at 3u (slot -1: none), for down
   uint8_t* hq;
   size_t hrow;
   int T, H, I, k, A, S;
@@ -418,6 +419,11 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
   const int nbps = p.I / 32;
   const int u = blockIdx.x / nbps, nb = blockIdx.x - u * nbps;
   const SlotRange sr = work_slot(u, p.used, p.offsets, p.S, p.A);
+  if (nb == 0 && threadIdx.x == 0) {  // the down kernel takes its work items from here
+    p.slots[3 * u] = sr.s;
+    p.slots[3 * u + 1] = sr.p0;
+    p.slots[3 * u + 2] = sr.p1;
+  }
   if (sr.s < 0) return;
   const int s = sr.s, p0 = sr.p0, p1 = sr.p1;
   const int lane = threadIdx.x;
@@ -511,7 +517,7 @@ struct DownArgs {
   size_t off_dc, off_ds;
   const int32_t* offsets;
   const int32_t* perm;
-  const int32_t* used;  // prebuilt work list, or null: found in place
+  const int32_t* slots;  // (slot, p0, p1) of work item u at 3u, written by the gate/up kernel
   float* y;
   int H, I, A, S;
 };
@@ -520,7 +526,10 @@ template <bool FULL>
 __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
   const int nbps = (p.H + 63) / 64;
   const int u = blockIdx.x / nbps, nb = blockIdx.x - u * nbps;
-  const SlotRange sr = work_slot(u, p.used, p.offsets, p.S, p.A);
+  // one round trip: the gate/up kernel of this call found the slot
+  const SlotRange sr = {__builtin_amdgcn_readfirstlane(p.slots[3 * u]),
+                        __builtin_amdgcn_readfirstlane(p.slots[3 * u + 1]),
+                        __builtin_amdgcn_readfirstlane(p.slots[3 * u + 2])};
   if (sr.s < 0) return;
   const int s = sr.s, p0 = sr.p0, p1 = sr.p1;
   const int lane = threadIdx.x;
@@ -1152,7 +1161,9 @@ static ExpertsWs experts_ws(int T, int H, int k, int I, int S) {
   const bool tiled = fam != kFamSmall;
   w.used_off = 0;
   w.items_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
-  const size_t items = tiled ? (1 + 4 * max_tiles(A, S, kTileM)) * sizeof(int32_t) : 0;
+  // pipelined: the M-tile list; small batches: (slot, p0, p1) per work item
+  const size_t items = tiled ? (1 + 4 * max_tiles(A, S, kTileM)) * sizeof(int32_t)
+                             : 3 * (A < (size_t)S ? A : (size_t)S) * sizeof(int32_t);
   w.zero_off = up_to(w.items_off + items, 256);
   w.hq_off = w.zero_off + (tiled ? kZeroPage : 0);
   w.y_off = up_to(w.hq_off + A * mxfp4_row_bytes(I), 256);
@@ -1258,6 +1269,8 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     g.offsets = a->slot_offsets;
     g.perm = a->perm;
     g.used = prebuilt ? used : nullptr;
+    int32_t* slots = reinterpret_cast<int32_t*>(ws + W.items_off);
+    g.slots = slots;
     g.hq = hq;
     g.hrow = mxfp4_row_bytes(I);
     g.T = T;
@@ -1283,7 +1296,7 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     d.off_ds = L.off[5];
     d.offsets = a->slot_offsets;
     d.perm = a->perm;
-    d.used = prebuilt ? used : nullptr;
+    d.slots = slots;
     d.y = y;
     d.H = H;
     d.I = I;

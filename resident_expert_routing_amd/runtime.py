@@ -125,6 +125,7 @@ class HotReader:
         self.out = torch.empty(2, dtype=torch.int32, device=device)
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
+        self.done.record(self.side)   # creates the HIP event the library records after a copy
         self._pinned = {}
 
     def pinned(self, host_bytes: np.ndarray) -> torch.Tensor:
@@ -207,6 +208,7 @@ class SharedArena:
         self.device = device
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
+        self.done.record(self.side)   # creates the HIP event the library records after a copy
         self._pinned = {}
 
     def upload(self, pair_bytes_fn) -> None:

@@ -218,3 +218,19 @@ def test_hot_pick_rejects():
     assert h(FAKE, FAKE, 8, 40, 16, FAKE, 10, 10, FAKE, 0.2, FAKE) == B.MOE_EUNSUPPORTED
     assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, float("nan"), FAKE) == B.MOE_EINVAL
     assert h(FAKE, FAKE, 8, 4, 16, FAKE, -1, 10, FAKE, 0.2, FAKE) == B.MOE_EINVAL
+
+
+def test_unrecorded_torch_event_is_refused():
+    """A torch.cuda.Event gets its HIP event on its first record; passing one
+    before that would hand the library a null event (no record after a copy,
+    so a later wait on it would order nothing): the binding refuses it."""
+    class Unrecorded:
+        cuda_event = 0
+
+    class Recorded:
+        cuda_event = 0x1000
+
+    with pytest.raises(ValueError):
+        B._event(Unrecorded())
+    assert B._event(Recorded()) == 0x1000
+    assert B._event(None) is None
