@@ -60,6 +60,8 @@ def parse():
                     choices=["decode", "prefill", "long", "tiny", "arena40"])
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak microbenchmarks (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -441,8 +443,9 @@ def main():
         roof = {"bound": "hbm", "achieved": gu_bytes / (gu_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof.update(achievable_peak(roof["bound"], dev))
-    roof["achievable_frac"] = roof["achieved"] / roof["achievable_peak"]
+    if not args.no_peaks:
+        roof.update(achievable_peak(roof["bound"], dev))
+        roof["achievable_frac"] = roof["achieved"] / roof["achievable_peak"]
     achieved = roof["achieved"]
     layer_bytes = float(np.mean([u * expert_bytes(H, I) for u in u_steps])) + H * E * 4 + 2 * T * H * 2
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
