@@ -74,6 +74,7 @@ extern "C" {
 #define MOE_OP_ROUTE 0
 #define MOE_OP_DEMAND 1
 #define MOE_OP_EXPERTS 2
+#define MOE_OP_HOT_PICK 3
 
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 32
@@ -284,14 +285,23 @@ int arena_load_slot(uint8_t* arena, size_t slot_stride, int num_slots, int slot,
  *            hist_row[e], ties to the lower id; -1 if none.
  * Inputs : topk_expert, topk_score [T][k] as written by moe_route; expert_slot
  *          [E]; hist_row [E] double (the history after this call's demand).
- * Output : out [2] int32 (device).  One kernel; no workspace.
+ * Output : out [2] int32 (device).
+ * Workspace: moe_workspace_bytes(MOE_OP_HOT_PICK, T, 0, 0, 0, 0, 0) bytes,
+ *          256-byte aligned (16 B per token-pass workgroup, at most 256 of them;
+ *          0 when T == 0).  Two kernels on `stream`: a token pass over
+ *          min(ceil(T/256), 256) workgroups writes each one's best miss, then
+ *          one workgroup takes the best of those and the coldest expert.
+ *          Returns MOE_EWORKSPACE if ws_bytes is short, MOE_EINVAL for null or
+ *          misaligned pointers, a negative size or a threshold that is NaN or
+ *          negative, MOE_EUNSUPPORTED past the k, E, S limits.
  * The caller reads out, copies expert e*'s bytes into c's slot with
  * arena_load_slot, sets expert_slot[e*] = old slot of c and expert_slot[c] = -1,
  * routes again without demand, and orders moe_experts_forward after the copy.
  */
 int moe_hot_pick(const int32_t* topk_expert, const float* topk_score, int T, int k, int E,
                  const int32_t* expert_slot, int S, int n_arena, const double* hist_row,
-                 double threshold, int32_t* out, hipStream_t stream);
+                 double threshold, int32_t* out, void* ws, size_t ws_bytes,
+                 hipStream_t stream);
 
 /*
  * moe_replan -- re-plan of one arena shared by all layers (TideLM README, "How

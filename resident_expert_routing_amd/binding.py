@@ -24,6 +24,7 @@ MOE_EHIP = -4
 MOE_OP_ROUTE = 0
 MOE_OP_DEMAND = 1
 MOE_OP_EXPERTS = 2
+MOE_OP_HOT_PICK = 3
 MOE_MAX_E = 1024
 MOE_MAX_K = 32
 MOE_MAX_S = 8192
@@ -101,7 +102,8 @@ def load() -> ctypes.CDLL:
     lib.moe_experts_forward.restype = i
     lib.arena_load_slot.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
     lib.arena_load_slot.restype = i
-    lib.moe_hot_pick.argtypes = [vp, vp, i, i, i, vp, i, i, vp, ctypes.c_double, vp, vp]
+    lib.moe_hot_pick.argtypes = [vp, vp, i, i, i, vp, i, i, vp, ctypes.c_double, vp, vp, sz,
+                                 vp]
     lib.moe_hot_pick.restype = i
     lib.moe_replan.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, ctypes.POINTER(i)]
     lib.moe_replan.restype = i
@@ -230,10 +232,11 @@ def arena_load_slot(arena, slot_stride, num_slots, slot, host_src, nbytes, side_
 
 
 def moe_hot_pick(topk_expert, topk_score, T, k, E, expert_slot, S, n_arena, hist_row, threshold,
-                 out, stream=None) -> int:
+                 out, ws=None, ws_bytes=0, stream=None) -> int:
     return int(load().moe_hot_pick(_ptr(topk_expert), _ptr(topk_score), int(T), int(k), int(E),
                                    _ptr(expert_slot), int(S), int(n_arena), _ptr(hist_row),
-                                   float(threshold), _ptr(out), _stream(stream)))
+                                   float(threshold), _ptr(out), _ptr(ws), int(ws_bytes),
+                                   _stream(stream)))
 
 
 def moe_replan(hist, expert_slot, L, E, k, n_swap, evict, load, new_expert_slot, n_done) -> int:

@@ -127,6 +127,13 @@ class HotReader:
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
         self._pinned = {}
+        self.ws = None   # token-pass partials of moe_hot_pick, grown to the largest batch seen
+
+    def workspace(self, T: int) -> torch.Tensor:
+        need = B.moe_workspace_bytes(B.MOE_OP_HOT_PICK, T, 0, 0, 0, 0, 0)
+        if self.ws is None or self.ws.numel() < need:
+            self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        return self.ws
 
     def pinned(self, host_bytes: np.ndarray) -> torch.Tensor:
         key = id(host_bytes)
@@ -137,9 +144,10 @@ class HotReader:
     def pick_and_load(self, buf: LayerBuffers, expert_slot_dev, hist_row, arena: Arena,
                       expert_bytes_fn, stream):
         """Returns (e_star, c, slot) after enqueueing the copy, or None."""
+        ws = self.workspace(buf.T)
         B.check(B.moe_hot_pick(buf.topk_expert, buf.topk_score, buf.T, buf.k, buf.E,
                                expert_slot_dev, buf.S, self.n_arena, hist_row, self.threshold,
-                               self.out, stream), "moe_hot_pick")
+                               self.out, ws, ws.numel(), stream), "moe_hot_pick")
         self.side.wait_stream(stream)
         e_star, c = (int(v) for v in self.out.cpu())   # waits for the decision
         if e_star < 0 or c < 0:

@@ -218,6 +218,13 @@ def test_hot_pick_rejects():
     assert h(FAKE, FAKE, 8, 40, 16, FAKE, 10, 10, FAKE, 0.2, FAKE) == B.MOE_EUNSUPPORTED
     assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, float("nan"), FAKE) == B.MOE_EINVAL
     assert h(FAKE, FAKE, 8, 4, 16, FAKE, -1, 10, FAKE, 0.2, FAKE) == B.MOE_EINVAL
+    need = B.moe_workspace_bytes(B.MOE_OP_HOT_PICK, 8, 0, 0, 0, 0, 0)
+    assert need == 256
+    assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, 0.2, FAKE, FAKE, need - 1) == B.MOE_EWORKSPACE
+    assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, 0.2, FAKE, None, need) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, 0.2, FAKE, FAKE + 8, need) == B.MOE_EINVAL
+    assert B.moe_workspace_bytes(B.MOE_OP_HOT_PICK, 0, 0, 0, 0, 0, 0) == 0
+    assert B.moe_workspace_bytes(B.MOE_OP_HOT_PICK, 10 ** 7, 0, 0, 0, 0, 0) == 256 * 16
 
 
 def test_unrecorded_torch_event_is_refused():

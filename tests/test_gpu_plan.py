@@ -34,10 +34,13 @@ def gpu_pick(te, ts, es, hist, n_arena, threshold=0.2):
     E = es.shape[0]
     S = int(es.max()) + 1 if (es >= 0).any() else 0
     out = torch.full((2,), 7, dtype=torch.int32, device="cuda")
+    need = m.moe_workspace_bytes(m.MOE_OP_HOT_PICK, T, 0, 0, 0, 0, 0)
+    # stale partials from an earlier call must not leak into this one
+    ws = torch.full((need + 256,), 0x7F, dtype=torch.uint8, device="cuda")
     m.check(m.moe_hot_pick(to_dev(te.astype(np.int32)) if T else None,
                            to_dev(ts.astype(np.float32)) if T else None, T, k, E,
                            to_dev(es.astype(np.int32)), S, n_arena, to_dev(hist.astype(np.float64)),
-                           threshold, out), "moe_hot_pick")
+                           threshold, out, ws, need), "moe_hot_pick")
     torch.cuda.synchronize()
     return [int(v) for v in out.cpu()]
 
@@ -77,6 +80,24 @@ def test_hot_pick_random_tables_with_ties():
             cases += 1
     say(f"hot_pick: {cases} of 60 random tables had a qualifying miss")
     assert cases > 20
+
+
+def test_hot_pick_grid_stride_many_tokens():
+    """More tokens than 256 workgroups x 256 threads: every workgroup walks
+    several tokens, and the best miss sits in the last, ragged stretch."""
+    rng = np.random.default_rng(5)
+    T, E, k = 70001, 64, 4
+    te = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    ts = (rng.integers(1, 9, size=(T, k)) / 16.0).astype(np.float32)
+    es = np.full(E, -1, dtype=np.int32)
+    es[:40] = np.arange(40)
+    ts[T - 3, :] = [1.0, 1e-3, 1e-3, 1e-3]
+    te[T - 3, :] = [50, 0, 1, 2]          # expert 50 is not resident
+    hist = rng.integers(0, 4, size=E).astype(np.float64)
+    want = oracle_pick(te, ts, es, hist, 30, 0.2)
+    got = gpu_pick(te, ts, es, hist, 30, 0.2)
+    assert want is not None and want[0] == 50
+    assert got == want, (got, want)
 
 
 def test_hot_pick_empty_batch():
