@@ -803,11 +803,18 @@ __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ 
   }
 }
 
-// Work index of this workgroup.  Workgroups are dispatched round-robin over
-// the 8 XCDs; this mapping gives each XCD a contiguous range of work indices.
-// gridDim.x is a multiple of 8.
-__device__ __forceinline__ int xcd_work_index() {
-  return (int)((blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3));
+// Work index of this workgroup for n work indices.  Workgroups are dispatched
+// round-robin over the 8 XCDs; this mapping gives XCD x the contiguous range
+// [x R, x R + R) of R = ceil(n / 8) indices, so all eight share the work the
+// batch actually has (the grid is sized for an upper bound of it).  Returns
+// -1 for a workgroup with no index.  gridDim.x is a multiple of 8 and at
+// least n rounded up to one.
+__device__ __forceinline__ int xcd_work_index(int n) {
+  const int R = (n + 7) / 8;
+  const int j = (int)(blockIdx.x >> 3);
+  if (j >= R) return -1;
+  const int w = (int)(blockIdx.x & 7u) * R + j;
+  return w < n ? w : -1;
 }
 
 // The (M-tile, N-tile) of work index w.  A slot's items x nN tiles are
@@ -821,6 +828,7 @@ struct TileRef {
 
 __device__ __forceinline__ bool tile_of(int w, int nN, int tm, const int32_t* __restrict__ items,
                                         const int32_t* __restrict__ offsets, TileRef& t) {
+  if (w < 0) return false;
   const int item = w / nN;
   if (item >= items[0]) return false;
   const int32_t* it = items + 1 + 4 * item;
@@ -1044,7 +1052,7 @@ struct PipeArgs {
 __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
-  if (!tile_of(xcd_work_index(), p.nN, kTileM, p.items, p.offsets, tr)) return;  // no barrier yet
+  if (!tile_of(xcd_work_index(p.items[0] * p.nN), p.nN, kTileM, p.items, p.offsets, tr)) return;  // no barrier yet
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
@@ -1084,7 +1092,7 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
 __global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
-  if (!tile_of(xcd_work_index(), p.nN, kTileM, p.items, p.offsets, tr)) return;
+  if (!tile_of(xcd_work_index(p.items[0] * p.nN), p.nN, kTileM, p.items, p.offsets, tr)) return;
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
