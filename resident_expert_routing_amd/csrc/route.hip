@@ -79,13 +79,21 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
     float4 wv[kRouterChunk / 4];
 #pragma unroll
     for (int q = 0; q < kRouterChunk / 4; ++q) wv[q] = w4[q];
+    // every token's x chunk is loaded before the first chain starts (tokens
+    // past the batch load its last one and are never stored): loads inside
+    // `if (i < nt)` were issued one token at a time, a round trip each
+    uint4 xv_all[RS_T][kRouterChunk / 8];
 #pragma unroll
     for (int i = 0; i < RS_T; ++i) {
-      if (i < nt) {
-        const uint4* x4 = reinterpret_cast<const uint4*>(x + (size_t)(t0 + i) * H + h0);
-        uint4 xv[kRouterChunk / 8];
+      const uint4* x4 =
+          reinterpret_cast<const uint4*>(x + (size_t)(t0 + min(i, nt - 1)) * H + h0);
 #pragma unroll
-        for (int q = 0; q < kRouterChunk / 8; ++q) xv[q] = x4[q];
+      for (int q = 0; q < kRouterChunk / 8; ++q) xv_all[i][q] = x4[q];
+    }
+#pragma unroll
+    for (int i = 0; i < RS_T; ++i) {
+      {
+        const uint4 (&xv)[kRouterChunk / 8] = xv_all[i];
         double s = 0.0;
 #pragma unroll
         for (int q = 0; q < kRouterChunk / 8; ++q) {
@@ -98,7 +106,7 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
             s = fma((double)bf16_to_f32(bits), (double)ww[r], s);
           }
         }
-        part[i][c] = s;
+        if (i < nt) part[i][c] = s;
       }
     }
   }
