@@ -499,6 +499,25 @@ __device__ void select_token(const SelectArgs& p, int t, int role) {
   const int nper = (E + 63) / 64;
 
   // ---- logits plus bias ----
+  // every load is issued before the first use (lanes past E load expert
+  // E - 1 and drop it): loads under the per-expert branch went one round trip
+  // at a time
+  double zl[NPER];
+  float bl[NPER];
+  int sl[NPER];
+  // without a bias the loads read the (E-entry) slot table and are dropped:
+  // a load under `if (bias)` made the compiler wait for it before the next
+  const bool has_bias = p.bias != nullptr;
+  const float* bsrc = has_bias ? p.bias : reinterpret_cast<const float*>(p.expert_slot);
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    zl[i] = p.z[(size_t)t * E + e];
+    bl[i] = bsrc[e];
+    sl[i] = p.expert_slot[e];
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) bl[i] = has_bias ? bl[i] : 0.f;
   double z[NPER];
   uint32_t valid = 0, routable = 0;
   int slot_of[NPER];
@@ -508,9 +527,9 @@ __device__ void select_token(const SelectArgs& p, int t, int role) {
     slot_of[i] = -1;
     const int e = lane + 64 * i;
     if (i < nper && e < E) {
-      z[i] = p.z[(size_t)t * E + e] + (p.bias ? (double)p.bias[e] : 0.0);
+      z[i] = zl[i] + (double)bl[i];
       valid |= 1u << i;
-      const int s = p.expert_slot[e];
+      const int s = sl[i];
       if (s >= 0 && s < p.S) {
         routable |= 1u << i;
         slot_of[i] = s;
