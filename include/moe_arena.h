@@ -292,7 +292,8 @@ int arena_load_slot(uint8_t* arena, size_t slot_stride, int num_slots, int slot,
  *          min(ceil(T/256), 256) workgroups writes each one's best miss, then
  *          one workgroup takes the best of those and the coldest expert.
  *          Returns MOE_EWORKSPACE if ws_bytes is short, MOE_EINVAL for null or
- *          misaligned pointers, a negative size or a threshold that is NaN or
+ *          misaligned pointers (4 bytes for the int32/float arrays, 8 for
+ *          hist_row, 256 for ws), a negative size or a threshold that is NaN or
  *          negative, MOE_EUNSUPPORTED past the k, E, S limits.
  * The caller reads out, copies expert e*'s bytes into c's slot with
  * arena_load_slot, sets expert_slot[e*] = old slot of c and expert_slot[c] = -1,

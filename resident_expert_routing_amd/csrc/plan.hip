@@ -150,7 +150,8 @@ extern "C" MOE_EXPORT int moe_hot_pick(const int32_t* topk_expert, const float* 
   if (k > MOE_MAX_K || E > MOE_MAX_E || S > MOE_MAX_S) return MOE_EUNSUPPORTED;
   if (!expert_slot || !hist_row || !out) return MOE_EINVAL;
   if (T > 0 && (!topk_expert || !topk_score)) return MOE_EINVAL;
-  if (!aligned(hist_row, 8) || !aligned(out, 4)) return MOE_EINVAL;
+  if (!aligned(hist_row, 8) || !aligned(out, 4) || !aligned(expert_slot, 4)) return MOE_EINVAL;
+  if (T > 0 && (!aligned(topk_expert, 4) || !aligned(topk_score, 4))) return MOE_EINVAL;
   if (!(threshold >= 0.0)) return MOE_EINVAL;  // also rejects NaN
   const size_t need = moe_hot_pick_ws_bytes_internal(T);
   if (ws_bytes < need) return MOE_EWORKSPACE;

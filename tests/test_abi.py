@@ -218,6 +218,11 @@ def test_hot_pick_rejects():
     assert h(FAKE, FAKE, 8, 40, 16, FAKE, 10, 10, FAKE, 0.2, FAKE) == B.MOE_EUNSUPPORTED
     assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, float("nan"), FAKE) == B.MOE_EINVAL
     assert h(FAKE, FAKE, 8, 4, 16, FAKE, -1, 10, FAKE, 0.2, FAKE) == B.MOE_EINVAL
+    for bad in range(3):  # a misaligned topk_expert, topk_score or expert_slot
+        args = [FAKE, FAKE, FAKE]
+        args[bad] = FAKE + 2
+        assert h(args[0], args[1], 8, 4, 16, args[2], 10, 10, FAKE, 0.2, FAKE, FAKE, 256) \
+            == B.MOE_EINVAL
     need = B.moe_workspace_bytes(B.MOE_OP_HOT_PICK, 8, 0, 0, 0, 0, 0)
     assert need == 256
     assert h(FAKE, FAKE, 8, 4, 16, FAKE, 10, 10, FAKE, 0.2, FAKE, FAKE, need - 1) == B.MOE_EWORKSPACE
