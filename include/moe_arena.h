@@ -227,12 +227,24 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  * Output : out [T][H] bf16.
  * Workspace: moe_workspace_bytes(MOE_OP_EXPERTS, T, H, 0, k, I, S) bytes.
  * Any copy into a slot the call reads (arena_load_slot) must be ordered before
- * it by the caller (hipStreamWaitEvent on the load's event).
+ * it: by the caller (hipStreamWaitEvent on the load's event), or, for one
+ * slot, through defer_slot.
+ * defer_slot, defer_event: -1 and NULL, or a slot in [0, S) whose bytes are
+ *          still being written and the event recorded after that write (the
+ *          hot read: arena_load_slot's `done`).  The call then runs the
+ *          gate/up products of every other slot first, makes `stream` wait for
+ *          defer_event, and runs that slot's and everything after them, so the
+ *          copy overlaps the first part; the output is the same as a call made
+ *          after the copy.  Batches taking the small-batch kernels (T*k <
+ *          2048, or H or I not a multiple of 512) wait for the event before
+ *          any work.  MOE_EINVAL for defer_slot outside [-1, S) or a deferred
+ *          slot without an event.
  * stage_events (host array, nullable): MOE_STAGE_EVENTS events on `stream`
  *          when T > 0 and S > 0: [0] before the work list; [1] and [2] the
  *          start and the end of the gate/up kernel itself, taken from its
  *          dispatch (hipExtLaunchKernel), so their interval is that kernel's
- *          duration; [3] after the down kernel; [4] after the combine.  A null
+ *          duration (with a deferred slot, of the gate/up pass over the other
+ *          slots); [3] after the down kernel; [4] after the combine.  A null
  *          entry is not recorded.  Recording changes no result.
  */
 typedef struct moe_experts_args {
@@ -248,6 +260,8 @@ typedef struct moe_experts_args {
   void* ws;
   size_t ws_bytes;
   hipEvent_t* stage_events;
+  int defer_slot;
+  hipEvent_t defer_event;
 } moe_experts_args;
 
 int moe_experts_forward(const moe_experts_args* args, hipStream_t stream);

@@ -62,7 +62,8 @@ class ExpertsArgs(ctypes.Structure):
                 ("perm", ctypes.c_void_p), ("sel_slot", ctypes.c_void_p),
                 ("sel_weight", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("defer_slot", ctypes.c_int),
+                ("defer_event", ctypes.c_void_p)]
 
 
 MOE_STAGE_EVENTS = 5
@@ -216,11 +217,13 @@ def moe_demand_accumulate(topk_expert, topk_score, T, k, E, hist_row, delta, ws,
 
 
 def moe_experts_forward(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm, sel_slot,
-                        sel_weight, out, ws, ws_bytes, stream=None, stage_events=None) -> int:
+                        sel_weight, out, ws, ws_bytes, stream=None, stage_events=None,
+                        defer_slot=-1, defer_event=None) -> int:
     keep, evp = _events(stage_events)
     a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
                     int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
-                    _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp)
+                    _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp,
+                    int(defer_slot), _event(defer_event))
     return int(load().moe_experts_forward(ctypes.byref(a), _stream(stream)))
 
 

@@ -758,10 +758,14 @@ constexpr int kLoadsPerStage = 6;
 
 // Work list of M-tiles of tm rows: items[0] = count, then per item (slot,
 // first row of the tile within the slot, index of the slot's first item, the
-// slot's item count), slots ascending.  Also clears the zero page.
+// slot's item count), slots ascending.  Also clears the zero page, and
+// writes the first item and the item count of slot defer_slot (0 and 0 when
+// it holds no assignment) to defer_info[0..1] when defer_slot >= 0.
 __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int S,
                                                     int A, int tm, int32_t* __restrict__ items,
-                                                    uint32_t* __restrict__ zero_page) {
+                                                    uint32_t* __restrict__ zero_page,
+                                                    int defer_slot,
+                                                    int32_t* __restrict__ defer_info) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid < kZeroPage / 4) zero_page[tid] = 0u;
@@ -784,7 +788,12 @@ __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ 
   for (int i = 0; i < wv; ++i) run += wsum[i];
   for (int s = lo; s < hi; ++s) {
     const int a = offsets[s], b = offsets[s + 1];
-    if (b > a && a >= 0 && b <= A) {
+    const bool used = b > a && a >= 0 && b <= A;
+    if (s == defer_slot) {  // its one owner thread
+      defer_info[0] = used ? run : 0;
+      defer_info[1] = used ? (b - a + tm - 1) / tm : 0;
+    }
+    if (used) {
       const int first = run, cnt = (b - a + tm - 1) / tm;
       for (int m = 0; m < cnt; ++m) {
         int32_t* it = items + 1 + 4 * run;
@@ -1045,6 +1054,8 @@ struct PipeArgs {
   size_t hrow;
   uint16_t* y;  // down output, bf16 rows
   int H, I, k, A, nN;
+  int skip_slot;        // gate/up: tiles of this slot are left out (-1: none)
+  const int32_t* only;  // gate/up: null, or (first item, item count) of the one slot to run
 };
 
 // Gate/up: N-tile = 128 rows of I; wave w: rows n0 = 32w.. of gate (tile 0)
@@ -1052,7 +1063,15 @@ struct PipeArgs {
 __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
-  if (!tile_of(xcd_work_index(p.items[0] * p.nN), p.nN, kTileM, p.items, p.offsets, tr)) return;  // no barrier yet
+  int w;
+  if (p.only) {  // one slot's tiles: work indices first * nN .. (first + count) * nN
+    const int n = p.only[1] * p.nN;
+    w = (int)blockIdx.x < n ? p.only[0] * p.nN + (int)blockIdx.x : -1;
+  } else {
+    w = xcd_work_index(p.items[0] * p.nN);
+  }
+  // no barrier yet: a workgroup without a tile (or with the left-out slot's) leaves whole
+  if (!tile_of(w, p.nN, kTileM, p.items, p.offsets, tr) || tr.slot == p.skip_slot) return;
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
@@ -1169,8 +1188,9 @@ static ExpertsWs experts_ws(int T, int H, int k, int I, int S) {
   const bool tiled = fam != kFamSmall;
   w.used_off = 0;
   w.items_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
-  // pipelined: the M-tile list; small batches: (slot, p0, p1) per work item
-  const size_t items = tiled ? (1 + 4 * max_tiles(A, S, kTileM)) * sizeof(int32_t)
+  // pipelined: the M-tile list, then the deferred slot's (first item, item
+  // count); small batches: (slot, p0, p1) per work item
+  const size_t items = tiled ? (1 + 4 * max_tiles(A, S, kTileM) + 2) * sizeof(int32_t)
                              : 3 * (A < (size_t)S ? A : (size_t)S) * sizeof(int32_t);
   w.zero_off = up_to(w.items_off + items, 256);
   w.hq_off = w.zero_off + (tiled ? kZeroPage : 0);
@@ -1200,6 +1220,8 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   const ExpertsWs W = experts_ws(T, H, k, I, S);
   if (a->ws_bytes < W.total) return MOE_EWORKSPACE;
   if (!a->ws || !aligned(a->ws, 256)) return MOE_EINVAL;
+  const int defer = a->defer_slot;
+  if (defer < -1 || defer >= S || (defer >= 0 && !a->defer_event)) return MOE_EINVAL;
   const int A = T * k;
   const Family fam = family_of(T, k, H, I);
   const size_t ntile = max_tiles((size_t)A, S, kTileM);
@@ -1223,10 +1245,11 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
 
   if (fam == kFamPipe) {
     int32_t* items = reinterpret_cast<int32_t*>(ws + W.items_off);
+    int32_t* defer_info = items + 1 + 4 * ntile;
     uint8_t* zero = ws + W.zero_off;
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
     build_tiles<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, kTileM, items,
-                                        reinterpret_cast<uint32_t*>(zero));
+                                        reinterpret_cast<uint32_t*>(zero), defer, defer_info);
     PipeArgs t;
     t.act = a->xq;
     t.arow = mxfp4_row_bytes(H);
@@ -1248,8 +1271,20 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     t.k = k;
     t.A = A;
     t.nN = nN1;
+    t.skip_slot = defer;
+    t.only = nullptr;
     hipExtLaunchKernelGGL(gateup_pipe, dim3((unsigned)g1), dim3(256), 0, stream,
                           ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, 0, t);
+    if (defer >= 0) {
+      // the deferred slot's tiles, once its bytes are in place: at most one
+      // assignment per token, so at most ceil(T / 128) M-tiles
+      if (hipStreamWaitEvent(stream, a->defer_event, 0) != hipSuccess) return MOE_EHIP;
+      t.skip_slot = -1;
+      t.only = defer_info;
+      const size_t g3 = (size_t)((T + kTileM - 1) / kTileM) * (size_t)nN1;
+      gateup_pipe<<<(unsigned)g3, 256, 0, stream>>>(t);
+      t.only = nullptr;
+    }
     t.act = hq;
     t.arow = t.hrow;
     t.off_c0 = L.off[4];
@@ -1263,6 +1298,10 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
     // Work list of used slots: built once for large slot counts, else each
     // workgroup finds its slot in place (saves a launch on decode batches).
     const bool prebuilt = S > kInlineWorklistMaxS;
+    // small batches run every slot in one pass: the deferred slot's bytes
+    // must be in place before it
+    if (defer >= 0 && hipStreamWaitEvent(stream, a->defer_event, 0) != hipSuccess)
+      return MOE_EHIP;
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
     if (prebuilt) build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
     GateUpArgs g;

@@ -101,11 +101,12 @@ def demand(buf: LayerBuffers, hist_row, stream=None, delta=True) -> None:
 
 
 def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None,
-            stage_events=None) -> None:
+            stage_events=None, defer_slot: int = -1, defer_event=None) -> None:
     B.check(B.moe_experts_forward(buf.T, buf.H, buf.I, buf.k, buf.S, buf.xq, arena_ptr,
                                   slot_stride, buf.slot_offsets, buf.perm, buf.sel_slot,
                                   buf.sel_weight, buf.out, buf.ws_experts, buf.ws_experts_bytes,
-                                  stream, stage_events), "moe_experts_forward")
+                                  stream, stage_events, defer_slot, defer_event),
+            "moe_experts_forward")
 
 
 class HotReader:
@@ -169,15 +170,17 @@ def layer_step_hot(buf: LayerBuffers, x, w_router, bias, expert_slot_dev, hist_r
 
     Route with demand, decide and start the copy, route again over the new
     routable set (the router's products reused; overlapping the copy), then
-    run the experts after the copy.
+    run the experts with the loaded slot deferred: the other slots' gate/up
+    products run while the copy finishes, that slot's after it.
     """
     stream = stream if stream is not None else torch.cuda.current_stream(hot.device)
     route(buf, x, w_router, bias, expert_slot_dev, stream, hist_row=hist_row)
     picked = hot.pick_and_load(buf, expert_slot_dev, hist_row, arena, expert_bytes_fn, stream)
-    if picked is not None:
-        route(buf, x, w_router, bias, expert_slot_dev, stream, reuse_logits=True)
-        stream.wait_event(hot.done)
-    experts(buf, arena.ptr(), arena.stride, stream)
+    if picked is None:
+        experts(buf, arena.ptr(), arena.stride, stream)
+        return None
+    route(buf, x, w_router, bias, expert_slot_dev, stream, reuse_logits=True)
+    experts(buf, arena.ptr(), arena.stride, stream, defer_slot=picked[2], defer_event=hot.done)
     return picked
 
 

@@ -147,6 +147,9 @@ def _experts(**kw):
     (dict(ws=None), B.MOE_EINVAL),
     (dict(S=9000), B.MOE_EUNSUPPORTED),
     (dict(k=0), B.MOE_EINVAL),
+    (dict(defer_slot=10), B.MOE_EINVAL),
+    (dict(defer_slot=-2), B.MOE_EINVAL),
+    (dict(defer_slot=3), B.MOE_EINVAL),  # a deferred slot needs an event
 ])
 def test_experts_rejects(kw, code):
     assert _experts(**kw) == code

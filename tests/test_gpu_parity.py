@@ -506,6 +506,32 @@ def test_batch_invariance_pipelined_path():
         assert moe.rel_l2(one.out_f64()[0], full[t]) <= OUT_REL_L2, t
 
 
+@pytest.mark.parametrize("name", ["prefill", "decode"])
+def test_deferred_slot_same_output(name):
+    """moe_experts_forward with a deferred slot (its gate/up tiles run after
+    an event, the other slots' before) gives the same output bit for bit, for
+    the busiest slot, a slot with one tile's worth or less, and an unused one."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    g = gpu_layer(name)
+    say(f"deferred slot on {name}: same output as one pass")
+    g.route()
+    g.experts()
+    ref = g.out_f64().copy()
+    off = g.routing()["slot_offsets"].astype(np.int64)
+    counts = np.diff(off[:g.S + 1])
+    busiest = int(np.argmax(counts))
+    small = int(np.flatnonzero((counts > 0) & (counts <= 128))[0])
+    unused = np.flatnonzero(counts == 0)
+    slots = [busiest, small] + ([int(unused[0])] if unused.size else [])
+    ev = torch.cuda.Event()
+    for s in slots:
+        ev.record()
+        g.buf.out.zero_()
+        R.experts(g.buf, g.arena.ptr(), g.arena.stride, defer_slot=s, defer_event=ev)
+        assert np.array_equal(g.out_f64(), ref), (name, s, int(counts[s]))
+
+
 def test_scale_bump_doubles_expert():
     """Adding 1 to every E8M0 scale byte of an expert's down matrix doubles that
     expert's y exactly; with identical experts everywhere the output doubles."""
