@@ -304,10 +304,21 @@ def prepack(seed: int, contents, H: int, I: int, std: float = 0.02, workers: int
         for key in todo:
             _PACK_CACHE[key] = _pack_one(key)
         return
+    # A fresh interpreter per worker ('spawn'): the caller may already have
+    # initialised the GPU, and a forked copy of such a process must not run.
+    # The pool is closed and joined, so no worker ends by a signal.
     import multiprocessing as mp
-    with mp.get_context("fork").Pool(workers) as pool:
-        for key, buf in zip(todo, pool.map(_pack_one, todo)):
-            _PACK_CACHE[key] = buf
+    pool = mp.get_context("spawn").Pool(workers)
+    try:
+        bufs = pool.map(_pack_one, todo)
+        pool.close()
+    except BaseException:
+        pool.terminate()
+        raise
+    finally:
+        pool.join()
+    for key, buf in zip(todo, bufs):
+        _PACK_CACHE[key] = buf
 
 
 @dataclass

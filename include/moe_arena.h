@@ -217,7 +217,10 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  *   h = silu(g) * u, silu(v) = v / (1 + exp(-v))
  *   y[a] = MXFP4(h) . Wd^T               (h encoded like an activation row, along I)
  * then out[t] = sum over j ascending (ascending expert id) of sel_weight[t,j] *
- * y[t*k+j], skipping picks with sel_slot[t,j] < 0, rounded once to bf16.
+ * y[t*k+j], skipping picks with sel_slot[t,j] < 0, summed in float32 and
+ * rounded to bf16.  y is kept in float32 by the small-batch kernels (T*k <
+ * 2048, or H or I not a multiple of 512) and rounded to bf16 per element by
+ * the pipelined kernels before the sum.
  * Only the slots that hold assignments are read.
  *
  * Inputs : xq, slot_offsets, perm, sel_slot, sel_weight as written by moe_route

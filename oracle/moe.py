@@ -231,11 +231,15 @@ def combine(y: np.ndarray, sel_weight: np.ndarray, sel_expert: np.ndarray) -> np
 
 
 def experts_forward(x_bits, sel_expert, sel_weight, sel_slot, slot_bytes_fn, H, I,
-                    act: str = "mxfp4", tokens=None):
+                    act: str = "mxfp4", tokens=None, decoded=None):
     """O9-O11.  slot_bytes_fn(s) returns slot s's packed bytes.
 
     tokens: optional subset of token indices to evaluate (sampled parity);
     returns (out [len(tokens), H], y [len(tokens), k, H]).
+    decoded: optional dict kept by the caller across calls; the decoded
+    weights of each packed byte buffer are stored there (with the buffer, so
+    its id stays valid) and reused.  Decoding is exact, so results are the
+    same with or without it.
     """
     T, k = sel_expert.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
@@ -249,7 +253,13 @@ def experts_forward(x_bits, sel_expert, sel_weight, sel_slot, slot_bytes_fn, H, 
         rows, cols = np.nonzero(ss == s)
         src = slot_bytes_fn(s)
         if id(src) != cached_key:
-            cached_key, cached = id(src), decode_expert(src, H, I)
+            if decoded is not None:
+                if id(src) not in decoded:
+                    decoded[id(src)] = (src, decode_expert(src, H, I))
+                cached = decoded[id(src)][1]
+            else:
+                cached = decode_expert(src, H, I)
+            cached_key = id(src)
         y[rows, cols] = expert_ffn(xhat[rows], cached, act)
     out = combine(y, np.asarray(sel_weight)[tok], np.asarray(sel_expert)[tok])
     return out, y

@@ -67,13 +67,15 @@ class Arena:
     def upload(self, slot_bytes_fn, slots=None, stream=None):
         """Copy packed host bytes into slots (plain torch copies, setup only)."""
         slots = range(self.S) if slots is None else slots
+        # one page-locked copy per distinct host array; the array itself is held
+        # next to it, so its id cannot be reused by another array meanwhile
         cache = {}
         for s in slots:
             host = slot_bytes_fn(s)
             key = id(host)
             if key not in cache:
-                cache[key] = torch.from_numpy(np.ascontiguousarray(host)).pin_memory()
-            self.mem[s * self.stride: s * self.stride + self.slot_bytes].copy_(cache[key],
+                cache[key] = (host, torch.from_numpy(np.ascontiguousarray(host)).pin_memory())
+            self.mem[s * self.stride: s * self.stride + self.slot_bytes].copy_(cache[key][1],
                                                                             non_blocking=True)
         torch.cuda.current_stream(self.mem.device).synchronize()
 
@@ -127,7 +129,7 @@ class HotReader:
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
-        self._pinned = {}
+        self._pinned = {}   # expert id -> its page-locked bytes
         self.ws = None   # token-pass partials of moe_hot_pick, grown to the largest batch seen
 
     def workspace(self, T: int) -> torch.Tensor:
@@ -136,11 +138,12 @@ class HotReader:
             self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
         return self.ws
 
-    def pinned(self, host_bytes: np.ndarray) -> torch.Tensor:
-        key = id(host_bytes)
-        if key not in self._pinned:
-            self._pinned[key] = torch.from_numpy(np.ascontiguousarray(host_bytes)).pin_memory()
-        return self._pinned[key]
+    def pinned(self, e: int, expert_bytes_fn) -> torch.Tensor:
+        """Page-locked copy of expert e's packed bytes (made once per expert)."""
+        if e not in self._pinned:
+            host = np.ascontiguousarray(expert_bytes_fn(e))
+            self._pinned[e] = torch.from_numpy(host).pin_memory()
+        return self._pinned[e]
 
     def pick_and_load(self, buf: LayerBuffers, expert_slot_dev, hist_row, arena: Arena,
                       expert_bytes_fn, stream):
@@ -150,11 +153,12 @@ class HotReader:
                                expert_slot_dev, buf.S, self.n_arena, hist_row, self.threshold,
                                self.out, ws, ws.numel(), stream), "moe_hot_pick")
         self.side.wait_stream(stream)
-        e_star, c = (int(v) for v in self.out.cpu())   # waits for the decision
+        with torch.cuda.stream(stream):   # ordered after moe_hot_pick on `stream`
+            e_star, c = (int(v) for v in self.out.cpu())   # waits for the decision
         if e_star < 0 or c < 0:
             return None
         slot = int(self.es[c])
-        src = self.pinned(expert_bytes_fn(e_star))
+        src = self.pinned(e_star, expert_bytes_fn)
         B.check(B.arena_load_slot(arena.mem, arena.stride, arena.S, slot, src, arena.slot_bytes,
                                   self.side, self.done), "arena_load_slot")
         self.es[e_star], self.es[c] = slot, -1
@@ -220,7 +224,7 @@ class SharedArena:
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
-        self._pinned = {}
+        self._pinned = {}   # (layer, expert) -> its page-locked bytes
 
     def upload(self, pair_bytes_fn) -> None:
         """Fill every slot with the bytes of the (layer, expert) it holds."""
@@ -228,10 +232,12 @@ class SharedArena:
         owner = {int(self.table_host[l, e]): (int(l), int(e)) for l, e in zip(l_idx, e_idx)}
         self.arena.upload(lambda s: pair_bytes_fn(*owner[s]), slots=sorted(owner))
 
-    def _pin(self, host: np.ndarray) -> torch.Tensor:
-        key = id(host)
+    def _pin(self, l: int, e: int, pair_bytes_fn) -> torch.Tensor:
+        """Page-locked copy of pair (l, e)'s packed bytes (made once per pair)."""
+        key = (l, e)
         if key not in self._pinned:
-            self._pinned[key] = torch.from_numpy(np.ascontiguousarray(host)).pin_memory()
+            host = np.ascontiguousarray(pair_bytes_fn(l, e))
+            self._pinned[key] = torch.from_numpy(host).pin_memory()
         return self._pinned[key]
 
     def replan(self, k: int, n_swap: int, pair_bytes_fn, stream=None):
@@ -254,7 +260,7 @@ class SharedArena:
         a = self.arena
         for i in range(n):
             slot = int(self.table_host[ev[i, 0], ev[i, 1]])
-            src = self._pin(pair_bytes_fn(int(ld[i, 0]), int(ld[i, 1])))
+            src = self._pin(int(ld[i, 0]), int(ld[i, 1]), pair_bytes_fn)
             B.check(B.arena_load_slot(a.mem, a.stride, a.S, slot, src, a.slot_bytes, self.side,
                                       self.done if i == n - 1 else None), "arena_load_slot")
         stream.wait_event(self.done)

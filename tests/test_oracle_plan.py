@@ -102,3 +102,30 @@ def test_replan_bruteforce_and_floor():
         assert sorted(new[new >= 0]) == sorted(es[es >= 0])   # slots are conserved
         for (le, ee), (ll, el) in zip(ev, ld):
             assert new[ll, el] == es[le, ee]
+
+
+def test_replan_hand_worked():
+    """Two layers of four experts, worked by hand.
+
+    Resident: layer 0 experts 0, 1, 2 (slots 0, 1, 2); layer 1 experts 0, 1
+    (slots 3, 4).  Histories: layer 0 [5, 1, 0.5, 8], layer 1 [0.25, 3, 6, 8].
+    Residents by ascending history: (1,0) 0.25, (0,2) 0.5, (0,1) 1, (1,1) 3,
+    (0,0) 5.  Non-residents by descending history: (0,3) 8, (1,3) 8 (tie: lower
+    layer first), (1,2) 6.
+    """
+    table = np.array([[0, 1, 2, -1], [3, 4, -1, -1]])
+    hist = np.array([[5.0, 1.0, 0.5, 8.0], [0.25, 3.0, 6.0, 8.0]])
+    # k = 2: (1,0) would leave layer 1 with one expert -> skipped; (0,2) is
+    # taken; then layer 0 is at two and layer 1 at two: nothing else can go.
+    ev, ld, new = plan.replan(hist, table, 2, 2)
+    assert ev == [(0, 2)] and ld == [(0, 3)]
+    assert new.tolist() == [[0, 1, -1, 2], [3, 4, -1, -1]]
+    # k = 1: (1,0) then (0,2) are evicted; (0,3) takes slot 3 (layer 1's, a
+    # slot moving between layers) and (1,3) takes slot 2 (layer 0's).
+    ev, ld, new = plan.replan(hist, table, 2, 1)
+    assert ev == [(1, 0), (0, 2)] and ld == [(0, 3), (1, 3)]
+    assert new.tolist() == [[0, 1, -1, 3], [-1, 4, -1, 2]]
+    # asking for more swaps than the floor allows stops at what can move
+    ev, ld, new = plan.replan(hist, table, 5, 1)
+    assert ev == [(1, 0), (0, 2), (0, 1)] and ld == [(0, 3), (1, 3), (1, 2)]
+    assert new.tolist() == [[0, -1, -1, 3], [-1, 4, 1, 2]]
