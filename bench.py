@@ -7,21 +7,28 @@ renormalisation, bucketing by slot, MXFP4 activations, and the demand
 histogram update) followed by moe_experts_forward (grouped SwiGLU experts on
 MXFP4 arena slots and the fixed-order weighted combine).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all]
 
-Prints one JSON line.  Inputs are seeded synthetic workloads (fixtures/): the
-default is the decode batch (8 tokens, hidden 4096, 256 experts, top-8,
+Prints one JSON line.  Inputs are seeded synthetic workloads (fixtures/).  The
+line's `value` is the decode batch (8 tokens, hidden 4096, 256 experts, top-8,
 SwiGLU intermediate 2048, 166 resident + 64 hot-ring slots, Zipf-skewed
-router).  Steps rotate over 4 token batches and 4 copies of the arena so the
+router): the memory-bound half of the metric.  With the default
+`--workload all` the same line carries, under "workloads", a block for each
+other workload, with its own time per step, roofline and CPU-oracle baseline:
+  prefill  2048 tokens of the same model (memory-bound at this size)
+  long     8192 tokens, hidden 6144, 192 experts (the matrix-bound half)
+  arena40  40 layers x 256 experts sharing one 6666-slot arena, 32 tokens a
+           layer call: demand accumulated over 512 steps, the 5 % re-plan (333
+           slot swaps), then 8 more steps.
+Layer workloads rotate over 4 token batches and 4 copies of the arena so the
 256 MB Infinity Cache cannot serve expert bytes reused from a previous step.
 
 Timing: W warmup steps, then K steps between two events on the launch stream
-(no other instrumentation) give `value` and `ms_per_step`.  A second run of K
-steps records HIP events only around the dominant kernel -- the grouped
-gate/up GEMM, 2/3 of the expert bytes -- for the roofline: achieved =
-algorithmic bytes per launch (distinct slots used x gate+up bytes per slot,
-plus the activation rows it reads and the MXFP4 h rows it writes) / mean
-launch time.
+(no other instrumentation) give `ms_per_step`.  A second run of the K steps
+takes the start and end of the dominant kernel -- the grouped gate/up GEMM,
+2/3 of the expert bytes and flops -- from its own dispatch, for the roofline:
+achieved = algorithmic bytes (or, above the MXFP4 ridge, flops) per launch /
+mean launch time.
 """
 from __future__ import annotations
 
@@ -29,6 +36,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -40,6 +48,9 @@ MXFP4_PEAK_TFLOPS = 10100.0    # MI355X dense MXFP4, vendor figure
 METRIC = "routed tokens/s per MoE layer; % peak HBM GB/s (decode), % MXFP4 MFMA (prefill)"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "resident_expert_routing_amd", "csrc", "experts.hip")
+LAYER_WORKLOADS = ("decode", "prefill", "long", "tiny")
+ARENA40_DEMAND_STEPS = 512     # steps of demand before the re-plan
+ARENA40_AFTER_STEPS = 8        # steps run on the re-planned arena
 
 
 def log(msg: str) -> None:
@@ -56,8 +67,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "long", "tiny", "arena40"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "decode", "prefill", "long", "tiny", "arena40"])
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
@@ -92,11 +103,16 @@ def expert_bytes(H: int, I: int) -> int:
     return 3 * H * I // 2 + 3 * H * I // 32
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per gate/up launch from the committed rocprofv3 PMC summary.
+def row_bytes(K: int) -> int:
+    return (K // 2 + K // 32 + 15) // 16 * 16
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per gate/up launch from the committed rocprofv3 PMC summary
+    (profiles/<kernel>_<workload>_pmc.json).
 
     Returns None if there is no summary or the kernel source changed since."""
-    path = os.path.join(PROFILE_DIR, f"gateup_kernel_{workload}_pmc.json")
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -106,118 +122,59 @@ def traffic_from_profile(workload: str):
     return p.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(lay, k: int):
-    """The oracle (numpy float64) on one full layer call, timed on the host cores."""
-    from oracle import moe
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
-        blas = 1
+        return 1
+
+
+def cpu_baseline(lay, k: int, tokens: int | None = None, what: str | None = None):
+    """The oracle (numpy float64) on one layer call, timed on the host cores.
+    tokens: run the layer on the first `tokens` rows of the batch only (a
+    bounded sample of a large chunk); tokens/s is per token either way."""
+    from oracle import moe
+    blas = blas_threads()
     cfg = lay.cfg
     sc = lay.slot_content()
+    x = lay.x_bits if tokens is None else lay.x_bits[:tokens]
     t0 = time.perf_counter()
-    moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k,
+    moe.layer(x, lay.w_router, lay.bias, lay.expert_slot, k,
               lambda s: lay.content_bytes(sc[s]), cfg.H, cfg.I)
     dt = time.perf_counter() - t0
-    T = lay.x_bits.shape[0]
+    T = x.shape[0]
+    what = what or f"one full {cfg.name} layer call"
     return {"value": T / dt, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
-            "sample": f"one full {cfg.name} layer call ({T} tokens: float64 router, softmax, "
-                      f"top-k, masked top-k, demand, MXFP4 decode of every used expert, SwiGLU, "
-                      f"combine) in {dt:.2f} s; numpy elementwise on 1 thread, BLAS on {blas}",
+            "cpu": cpu_model(),
+            "sample": f"{what} ({T} tokens: float64 router, softmax, top-k, masked top-k, "
+                      f"demand, MXFP4 decode of every used expert, SwiGLU, combine) in "
+                      f"{dt:.2f} s; numpy elementwise on 1 thread, BLAS on {blas}",
             "seconds": dt}
 
 
-def bench_arena40(args):
-    """40 layers x 256 experts sharing one 6666-slot arena, T=32 tokens per layer
-    call; then the 5 % re-plan (333 slot swaps), timed on its own."""
-    import numpy as np
-    import torch
-    import fixtures
-    import resident_expert_routing_amd  # noqa: F401
-    from resident_expert_routing_amd import runtime as R
-
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    model = fixtures.make_arena_model("arena40")
-    cfg = model.cfg
-    L, T, H, E, k, I, S = model.L, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, model.S
-    log(f"arena40: {L} layers, T={T} H={H} E={E} k={k} I={I}, {S} shared slots; packing")
-    model.prepack()
-    sa = R.SharedArena(S, H, I, model.expert_slot_table(), dev)
-    t0 = time.perf_counter()
-    sa.upload(model.pair_bytes)
-    log(f"arena of {S * sa.arena.stride / 1e9:.1f} GB uploaded in {time.perf_counter() - t0:.1f} s")
-    ws = [torch.from_numpy(l.w_router).to(dev) for l in model.layers]
-    bs = [torch.from_numpy(l.bias).to(dev) for l in model.layers]
-    nx = 4
-    xs = [torch.from_numpy(model.tokens(s).view(np.int16)).to(dev) for s in range(nx)]
-    buf = R.LayerBuffers(T, H, E, k, I, S, dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def layer(x, l):
-        R.route(buf, x, ws[l], bs[l], sa.table[l], stream, hist_row=sa.hist[l])
-        R.experts(buf, sa.arena.ptr(), sa.arena.stride, stream)
-
-    def step(s):
-        for l in range(L):
-            layer(xs[s % nx], l)
-
-    used = 0
-    for l in range(L):   # distinct slots per layer call, one step's worth (deterministic)
-        layer(xs[0], l)
-        torch.cuda.synchronize()
-        used += int(np.count_nonzero(np.diff(buf.slot_offsets.cpu().numpy())))
-    for i in range(args.warmup):
-        step(i)
-    K = args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(K):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1)
-    per_layer_us = ms * 1e3 / (K * L)
-    be = expert_bytes(H, I)
-    algo = used / L * be + H * E * 4 + 2 * T * H * 2   # per layer call, mean over the layers
-    n_swap = S // 20
-    torch.cuda.synchronize()
-    r0 = time.perf_counter()
-    ev, ld = sa.replan(k, n_swap, model.pair_bytes, stream)
-    torch.cuda.synchronize()
-    replan_s = time.perf_counter() - r0
-    moved = sum(1 for (le, _), (ll, _) in zip(ev, ld) if le != ll)
-    for i in range(2):   # the layers run on the new tables
-        step(K + i)
-    torch.cuda.synchronize()
-    result = {
-        "metric": METRIC,
-        "value": T / (per_layer_us * 1e-6),
-        "unit": "tokens/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup,
-        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "mxfp4", "data": "synthetic",
-        "config": {"workload": f"arena40: {L} layers x E={E}, T={T} per layer call, H={H} k={k} "
-                               f"I={I}, {S} shared slots", "layers": L, "T": T, "S": S},
-        "layer": {"us_per_layer_call": per_layer_us, "distinct_slots_per_call": used / L,
-                  "algo_bytes_per_call": algo,
-                  "GB_per_s": algo / (per_layer_us * 1e-6) / 1e9,
-                  "hbm_frac": algo / (per_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
-        "replan": {"swaps": len(ev), "cross_layer_swaps": moved,
-                   "bytes_h2d": len(ev) * sa.arena.slot_bytes, "seconds": replan_s,
-                   "GB_per_s_h2d": len(ev) * sa.arena.slot_bytes / replan_s / 1e9},
-    }
-    print(json.dumps(result), flush=True)
+_PEAKS = {}
 
 
 def achievable_peak(bound: str, dev) -> dict:
-    """The device's achievable peak for the roofline's bound, measured now with
-    the library's microbenchmarks: an 8 GiB read (32x the Infinity Cache,
-    16-byte loads, four in flight per thread; three launches back to back, so
-    the launch ramps weigh little) or a loop of the MXFP4 32x32x64
+    """The device's achievable peak for the roofline's bound, measured once per
+    run with the library's microbenchmarks: an 8 GiB read (32x the Infinity
+    Cache, 16-byte loads, four in flight per thread; three launches back to
+    back, so the launch ramps weigh little) or a loop of the MXFP4 32x32x64
     instruction; the best of the repetitions."""
+    if bound in _PEAKS:
+        return _PEAKS[bound]
     import torch
     from resident_expert_routing_amd import binding as B
     mk = lambda: torch.cuda.Event(enable_timing=True)
@@ -235,8 +192,9 @@ def achievable_peak(bound: str, dev) -> dict:
             torch.cuda.synchronize()
             best = max(best, back * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
         del src
-        return {"achievable_peak": best, "achievable_how": "moe_test_stream_read: 3 reads of "
-                "8 GiB back to back, best of 3"}
+        _PEAKS[bound] = {"achievable_peak": best, "achievable_how": "moe_test_stream_read: 3 "
+                         "reads of 8 GiB back to back, best of 3"}
+        return _PEAKS[bound]
     iters, grid = 1000, 1024
     sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
     flops = grid * 4 * iters * 8 * 2.0 * 32 * 32 * 64
@@ -247,8 +205,26 @@ def achievable_peak(bound: str, dev) -> dict:
         e1.record()
         torch.cuda.synchronize()
         best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
-    return {"achievable_peak": best, "achievable_how": "moe_test_mfma_loop: 32x32x64 MXFP4 "
-            "instruction, 8 chains per wave, best of 6 launches"}
+    _PEAKS[bound] = {"achievable_peak": best, "achievable_how": "moe_test_mfma_loop: 32x32x64 "
+                     "MXFP4 instruction, 8 chains per wave, best of 6 launches"}
+    return _PEAKS[bound]
+
+
+def gateup_roofline(gu_us: float, gu_bytes: float, gu_flops: float, args, dev) -> dict:
+    """Roofline of the gate/up kernel: memory-bound below the MXFP4 ridge (peak
+    flops / peak bytes), matrix-bound above it."""
+    ridge = MXFP4_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if gu_flops / gu_bytes > ridge:
+        roof = {"bound": "mfma", "achieved": gu_flops / (gu_us * 1e-6) / 1e12,
+                "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": gu_bytes / (gu_us * 1e-6) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    if not args.no_peaks:
+        roof.update(achievable_peak(roof["bound"], dev))
+        roof["achievable_frac"] = roof["achieved"] / roof["achievable_peak"]
+    return roof
 
 
 def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5):
@@ -260,6 +236,7 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
     `value`: the copy crosses PCIe."""
     import numpy as np
     import torch
+    from resident_expert_routing_amd import binding as B
     from resident_expert_routing_amd import runtime as R
 
     dev = x.device
@@ -267,6 +244,7 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
     hist = torch.zeros(E, dtype=torch.float64, device=dev)
     es = torch.from_numpy(es0).to(dev)
     n_arena = lay.extra["n_resident"]
+    pinned = {}
 
     def plain():
         es.copy_(torch.from_numpy(es0))
@@ -276,18 +254,15 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
     def with_hot():
         es.copy_(torch.from_numpy(es0))
         hot = R.HotReader(es0, n_arena, dev)
-        hot._pinned = pinned  # the expert's page-locked copy is made once, outside the timing
+        hot._pinned = pinned  # page-locked copies are made once, outside the timing
         picked = R.layer_step_hot(buf, x, w_router, bias, es, hist, arena, hot, lay.expert_bytes,
                                   stream)
         return picked, hot
 
-    pinned = {}
-    # warm: make the page-locked copy of the expert that will be loaded
-    picked, hot = with_hot()
+    picked, hot = with_hot()    # warm: makes the page-locked copy of the loaded expert
     torch.cuda.synchronize()
     if picked is None:
         return {"loaded": None, "note": "no pick with a share of at least 0.2 in this chunk"}
-    pinned.update(hot._pinned)
     times = {"plain": [], "hot": []}
     for _ in range(reps):
         for kind, fn in (("plain", plain), ("hot", with_hot)):
@@ -298,10 +273,10 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
             times[kind].append(time.perf_counter() - t0)
     # the copy alone, timed on the side stream
     hot = R.HotReader(es0, n_arena, dev)
-    src = pinned[next(iter(pinned))]
+    hot._pinned = pinned
+    src = hot.pinned(picked[0], lay.expert_bytes)   # the copy made above
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     slot = int(es0[picked[1]])
-    from resident_expert_routing_amd import binding as B
     with torch.cuda.stream(hot.side):
         e0.record(hot.side)
     B.check(B.arena_load_slot(arena.mem, arena.stride, arena.S, slot, src, arena.slot_bytes,
@@ -322,37 +297,21 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
                       f"{reps}); the copy alone with events on the side stream"}
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "this layer build has no multi-GPU path", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.workload == "arena40":
-        bench_arena40(args)
-        return
-
+def layer_workload(name: str, args, dev, steps: int, warmup: int) -> dict:
+    """One layer workload (decode, prefill, long, tiny): times, roofline, layer
+    figures, and the CPU oracle's rate on the host."""
     import numpy as np
     import torch
     import fixtures
-    import resident_expert_routing_amd  # noqa: F401  (loads libmoe_arena.so; fails loudly)
     from resident_expert_routing_amd import runtime as R
 
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    name = args.workload
     base = fixtures.make_layer(name)
     cfg = base.cfg
     T, H, E, k, I, S = base.x_bits.shape[0], cfg.H, cfg.E, cfg.k, cfg.I, base.S
     nrot = max(1, args.rotate)
+    log(f"workload {name}: T={T} H={H} E={E} k={k} I={I} S={S}")
 
     # ---- inputs resident in HBM ----
-    log(f"workload {name}: T={T} H={H} E={E} k={k} I={I} S={S}; packing expert contents")
-    base.prepack()
     layers = [base] + [fixtures.make_layer(name, x_stream=i) for i in range(1, nrot)]
     xs = [torch.from_numpy(l.x_bits.view(np.int16)).to(dev) for l in layers]
     w_router = torch.from_numpy(base.w_router).to(dev)
@@ -382,13 +341,12 @@ def main():
         torch.cuda.synchronize()
         off = buf.slot_offsets.cpu().numpy()
         U.append(int(np.count_nonzero(np.diff(off))))
-
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
     # ---- the timed steps ----
-    K = args.steps
+    K = steps
     mk = lambda: torch.cuda.Event(enable_timing=True)
     start, end = mk(), mk()
     torch.cuda.synchronize()
@@ -401,9 +359,9 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K
-    log(f"timed {K} steps: {ms_step * 1e3:.1f} us/step")
+    log(f"{name}: timed {K} steps: {ms_step * 1e3:.1f} us/step")
 
-    # ---- the dominant kernel, timed with events on its launch stream ----
+    # ---- the dominant kernel, timed from its own dispatch ----
     ev = [(mk(), mk()) for _ in range(K)]
     for a_, b_ in ev:
         a_.record(stream)   # torch creates the HIP event on first record
@@ -431,45 +389,23 @@ def main():
     A = T * k
     u_steps = [U[i % nrot] for i in range(K)]
     gu_bytes = float(np.mean([u * gateup_bytes_per_slot(H, I) for u in u_steps])) \
-        + T * (H // 2 + H // 32) + A * (I // 2 + I // 32)
+        + T * row_bytes(H) + A * row_bytes(I)
     gu_flops = 4.0 * H * I * A
-    # roofline of the gate/up kernel: memory-bound below the MXFP4 ridge
-    # (peak flops / peak bytes), matrix-bound above it
-    ridge = MXFP4_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if gu_flops / gu_bytes > ridge:
-        roof = {"bound": "mfma", "achieved": gu_flops / (gu_ms * 1e-3) / 1e12,
-                "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": gu_bytes / (gu_ms * 1e-3) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    if not args.no_peaks:
-        roof.update(achievable_peak(roof["bound"], dev))
-        roof["achievable_frac"] = roof["achieved"] / roof["achievable_peak"]
-    achieved = roof["achieved"]
-    layer_bytes = float(np.mean([u * expert_bytes(H, I) for u in u_steps])) + H * E * 4 + 2 * T * H * 2
+    roof = gateup_roofline(gu_ms * 1e3, gu_bytes, gu_flops, args, dev)
+    layer_bytes = float(np.mean([u * expert_bytes(H, I) for u in u_steps])) + H * E * 4 \
+        + 2 * T * H * 2
     layer_gbs = layer_bytes / (ms_step * 1e-3) / 1e9
     flops = 6.0 * H * I * A
-
-    result = {
-        "metric": METRIC,
-        "value": T * K / (total_ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
+    block = {
+        "value": T * K / (total_ms * 1e-3), "unit": "tokens/s", "steps": K, "warmup": warmup,
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "mxfp4",
-        "data": "synthetic",
         "config": {"workload": f"{name}: T={T} H={H} E={E} k={k} I={I} "
                                f"resident={cfg.resident} ring={cfg.ring} S={S}",
                    "T": T, "H": H, "E": E, "k": k, "I": I, "S": S, "rotate": nrot,
                    "zipf_beta": base.beta},
         "roofline": {**roof, "kernel": gateup_kernel_name(T, k, H, I),
-                     "traffic": traffic_from_profile(name), "algo_bytes_per_launch": gu_bytes,
+                     "traffic": traffic_from_profile(gateup_kernel_name(T, k, H, I), name),
+                     "algo_bytes_per_launch": gu_bytes,
                      "algo_flops_per_launch": gu_flops, "mean_launch_us": gu_ms * 1e3,
                      "ms_per_step_with_these_events": ms_step_ev},
         "layer": {"algo_bytes_per_step": layer_bytes, "GB_per_s": layer_gbs,
@@ -479,14 +415,211 @@ def main():
                   "mxfp4_frac": flops / (ms_step * 1e-3) / 1e12 / MXFP4_PEAK_TFLOPS,
                   "routing_us_per_call": route_us, "wall_s": wall},
     }
-    log(f"gate/up: {gu_ms * 1e3:.1f} us, {achieved:.0f} {roof['unit']}; "
-        f"routing alone {route_us:.1f} us per call")
+    log(f"{name}: gate/up {gu_ms * 1e3:.1f} us, {roof['achieved']:.0f} {roof['unit']} "
+        f"({roof['frac']:.3f} of peak); layer {layer_gbs:.0f} GB/s, "
+        f"{block['layer']['mxfp4_frac']:.3f} of MXFP4; routing {route_us:.1f} us")
     if name == "long":
-        result["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
-                                             stream)
+        block["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
+                                            stream)
+    del arenas
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on one layer call")
-        result["cpu_baseline"] = cpu_baseline(base, k)
+        log(f"{name}: timing the CPU oracle")
+        if name == "long":   # bounded sample: the first 1024 tokens of the chunk
+            block["cpu_baseline"] = cpu_baseline(
+                base, k, tokens=1024, what="the first 1024 tokens of the 8192-token chunk")
+        else:
+            block["cpu_baseline"] = cpu_baseline(base, k)
+    return block
+
+
+def arena40_workload(args, dev, warmup: int) -> dict:
+    """40 layers x 256 experts sharing one 6666-slot arena, T=32 tokens a layer
+    call.  Demand accumulates over 512 steps (each step: every layer on that
+    step's own tokens), then the 5 % re-plan (333 slot swaps through
+    arena_load_slot, timed on its own), then 8 more steps on the new tables.
+    The first `warmup` of the 512 steps are untimed."""
+    import numpy as np
+    import torch
+    import fixtures
+    from resident_expert_routing_amd import runtime as R
+
+    model = fixtures.make_arena_model("arena40")
+    cfg = model.cfg
+    L, T, H, E, k, I, S = model.L, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, model.S
+    n_steps = ARENA40_DEMAND_STEPS
+    log(f"arena40: {L} layers, T={T} H={H} E={E} k={k} I={I}, {S} shared slots")
+    sa = R.SharedArena(S, H, I, model.expert_slot_table(), dev)
+    t0 = time.perf_counter()
+    sa.upload(model.pair_bytes)
+    log(f"arena of {S * sa.arena.stride / 1e9:.1f} GB uploaded in {time.perf_counter() - t0:.1f} s")
+    ws = [torch.from_numpy(l.w_router).to(dev) for l in model.layers]
+    bs = [torch.from_numpy(l.bias).to(dev) for l in model.layers]
+    n_x = n_steps + ARENA40_AFTER_STEPS
+    xs = torch.from_numpy(np.stack([model.tokens(s).view(np.int16) for s in range(n_x)])).to(dev)
+    buf = R.LayerBuffers(T, H, E, k, I, S, dev)
+    stream = torch.cuda.current_stream(dev)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(s, gu_events=None):
+        for l in range(L):
+            R.route(buf, xs[s], ws[l], bs[l], sa.table[l], stream, hist_row=sa.hist[l])
+            R.experts(buf, sa.arena.ptr(), sa.arena.stride, stream,
+                      None if gu_events is None else [None, *gu_events[l], None, None])
+
+    # distinct slots of every layer call of the first 4 steps (deterministic)
+    used = []
+    for s in range(4):
+        for l in range(L):
+            R.route(buf, xs[s], ws[l], bs[l], sa.table[l], stream)
+            torch.cuda.synchronize()
+            used.append(int(np.count_nonzero(np.diff(buf.slot_offsets.cpu().numpy()))))
+    U = float(np.mean(used))
+
+    sa.hist.zero_()
+    for s in range(warmup):
+        step(s)
+    K = n_steps - warmup
+    e0, e1 = mk(), mk()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for s in range(warmup, n_steps):
+        step(s)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per_layer_us = ms * 1e3 / (K * L)
+    log(f"arena40: {K} timed steps, {per_layer_us:.1f} us per layer call")
+
+    # the gate/up kernel of every layer call of 4 steps (the first 4 step's tokens, whose
+    # distinct slots were counted above), from its own dispatch
+    gu_ev = [[(mk(), mk()) for _ in range(L)] for _ in range(4)]
+    for st in gu_ev:
+        for a_, b_ in st:
+            a_.record(stream)
+            b_.record(stream)
+    torch.cuda.synchronize()
+    hist_keep = sa.hist.clone()
+    for s in range(4):
+        step(s, gu_ev[s])
+    torch.cuda.synchronize()
+    sa.hist.copy_(hist_keep)        # these 4 steps are not part of the 512
+    gu_us = float(np.mean([a_.elapsed_time(b_) for st in gu_ev for a_, b_ in st])) * 1e3
+    gu_bytes = U * gateup_bytes_per_slot(H, I) + T * row_bytes(H) + T * k * row_bytes(I)
+    roof = gateup_roofline(gu_us, gu_bytes, 4.0 * H * I * T * k, args, dev)
+
+    be = expert_bytes(H, I)
+    algo = U * be + H * E * 4 + 2 * T * H * 2   # per layer call, mean over the layer calls
+    n_swap = S // 20
+    torch.cuda.synchronize()
+    r0 = time.perf_counter()
+    ev, ld = sa.replan(k, n_swap, model.pair_bytes, stream)
+    torch.cuda.synchronize()
+    replan_s = time.perf_counter() - r0
+    moved = sum(1 for (le, _), (ll, _) in zip(ev, ld) if le != ll)
+    a0, a1 = mk(), mk()
+    a0.record(stream)
+    for s in range(n_steps, n_x):   # the layers run on the new tables
+        step(s)
+    a1.record(stream)
+    torch.cuda.synchronize()
+    after_us = a0.elapsed_time(a1) * 1e3 / (ARENA40_AFTER_STEPS * L)
+    block = {
+        "value": T / (per_layer_us * 1e-6), "unit": "tokens/s",
+        "steps": K, "warmup": warmup, "ms_per_step": ms / K,
+        "config": {"workload": f"arena40: {L} layers x E={E}, T={T} per layer call, H={H} "
+                               f"k={k} I={I}, {S} shared slots; demand over {n_steps} steps, "
+                               f"re-plan of {n_swap} swaps, {ARENA40_AFTER_STEPS} steps after",
+                   "layers": L, "T": T, "S": S},
+        "roofline": {**roof, "kernel": gateup_kernel_name(T, k, H, I),
+                     "traffic": traffic_from_profile(gateup_kernel_name(T, k, H, I), "arena40"),
+                     "algo_bytes_per_launch": gu_bytes, "mean_launch_us": gu_us,
+                     "launches": 4 * L},
+        "layer": {"us_per_layer_call": per_layer_us, "distinct_slots_per_call": U,
+                  "algo_bytes_per_call": algo,
+                  "GB_per_s": algo / (per_layer_us * 1e-6) / 1e9,
+                  "hbm_frac": algo / (per_layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                  "us_per_layer_call_after_replan": after_us},
+        "replan": {"demand_steps": n_steps, "swaps": len(ev), "cross_layer_swaps": moved,
+                   "bytes_h2d": len(ev) * sa.arena.slot_bytes, "seconds": replan_s,
+                   "GB_per_s_h2d": len(ev) * sa.arena.slot_bytes / replan_s / 1e9},
+    }
+    log(f"arena40: gate/up {gu_us:.1f} us ({roof['frac']:.3f} of peak); layer "
+        f"{block['layer']['GB_per_s']:.0f} GB/s; re-plan {len(ev)} swaps in {replan_s:.3f} s; "
+        f"{after_us:.1f} us per layer call after it")
+    del sa
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("arena40: timing the CPU oracle on one layer call")
+        lay = model.layers[0]
+        lay.x_bits = model.tokens(0)
+        block["cpu_baseline"] = cpu_baseline(
+            lay, k, what="one of the 40 layer calls of a step (layer 0, its own resident set)")
+    return block
+
+
+def prepack(names) -> None:
+    """Pack every expert content the chosen workloads upload, before the GPU
+    is touched (the packer runs in worker processes)."""
+    import fixtures
+    for name in names:
+        if name == "arena40":
+            fixtures.make_arena_model("arena40").prepack()
+        else:
+            fixtures.make_layer(name).prepack()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this layer build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    names = ["decode", "prefill", "long", "arena40"] if args.workload == "all" else [args.workload]
+    log(f"packing expert contents for {', '.join(names)}")
+    prepack(names)
+
+    import torch
+    import resident_expert_routing_amd  # noqa: F401  (loads libmoe_arena.so; fails loudly)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    blocks = {}
+    for name in names:
+        if name == "arena40":
+            blocks[name] = arena40_workload(args, dev, min(args.warmup, 10))
+        elif name == names[0]:
+            blocks[name] = layer_workload(name, args, dev, args.steps, args.warmup)
+        else:   # the other layer workloads: 20 timed steps (the protocol's count for them)
+            blocks[name] = layer_workload(name, args, dev, min(args.steps, 20),
+                                          min(args.warmup, 5))
+    head = blocks[names[0]]
+    result = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": head["config"],
+    }
+    for key in ("roofline", "layer", "replan", "hot_read", "cpu_baseline"):
+        if key in head:
+            result[key] = head[key]
+    if len(names) > 1:
+        result["workloads"] = {n: blocks[n] for n in names[1:]}
     print(json.dumps(result), flush=True)
 
 

@@ -13,6 +13,16 @@ import torch
 from . import binding as B
 
 
+def _pin_cached(cache: dict, host: np.ndarray) -> torch.Tensor:
+    """Page-locked copy of a host byte array, made once per array object.  The
+    entry keeps the array alive, so its id names that array for as long as the
+    entry exists (two experts that share one packed array share one copy)."""
+    key = id(host)
+    if key not in cache:
+        cache[key] = (host, torch.from_numpy(np.ascontiguousarray(host)).pin_memory())
+    return cache[key][1]
+
+
 def _ws(nbytes: int, device) -> torch.Tensor | None:
     if nbytes == 0:
         return None
@@ -129,7 +139,7 @@ class HotReader:
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
-        self._pinned = {}   # expert id -> its page-locked bytes
+        self._pinned = {}   # id of a host array -> (the array, its page-locked copy)
         self.ws = None   # token-pass partials of moe_hot_pick, grown to the largest batch seen
 
     def workspace(self, T: int) -> torch.Tensor:
@@ -139,11 +149,10 @@ class HotReader:
         return self.ws
 
     def pinned(self, e: int, expert_bytes_fn) -> torch.Tensor:
-        """Page-locked copy of expert e's packed bytes (made once per expert)."""
-        if e not in self._pinned:
-            host = np.ascontiguousarray(expert_bytes_fn(e))
-            self._pinned[e] = torch.from_numpy(host).pin_memory()
-        return self._pinned[e]
+        """Page-locked copy of expert e's packed bytes, made once per host
+        array; the array is held next to its copy, so its id cannot be reused
+        by another array while the entry exists."""
+        return _pin_cached(self._pinned, expert_bytes_fn(e))
 
     def pick_and_load(self, buf: LayerBuffers, expert_slot_dev, hist_row, arena: Arena,
                       expert_bytes_fn, stream):
@@ -224,7 +233,7 @@ class SharedArena:
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
-        self._pinned = {}   # (layer, expert) -> its page-locked bytes
+        self._pinned = {}   # id of a host array -> (the array, its page-locked copy)
 
     def upload(self, pair_bytes_fn) -> None:
         """Fill every slot with the bytes of the (layer, expert) it holds."""
@@ -233,12 +242,8 @@ class SharedArena:
         self.arena.upload(lambda s: pair_bytes_fn(*owner[s]), slots=sorted(owner))
 
     def _pin(self, l: int, e: int, pair_bytes_fn) -> torch.Tensor:
-        """Page-locked copy of pair (l, e)'s packed bytes (made once per pair)."""
-        key = (l, e)
-        if key not in self._pinned:
-            host = np.ascontiguousarray(pair_bytes_fn(l, e))
-            self._pinned[key] = torch.from_numpy(host).pin_memory()
-        return self._pinned[key]
+        """Page-locked copy of pair (l, e)'s packed bytes (one per host array)."""
+        return _pin_cached(self._pinned, pair_bytes_fn(l, e))
 
     def replan(self, k: int, n_swap: int, pair_bytes_fn, stream=None):
         """Returns (evict [(l,e)], load [(l,e)]) once the copies are enqueued and
