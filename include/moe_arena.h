@@ -69,6 +69,7 @@ extern "C" {
 #define MOE_EUNSUPPORTED -2  /* H or I not a multiple of 32, k > min(E, 32), E > 1024, S > 8192 */
 #define MOE_EWORKSPACE -3    /* ws_bytes below moe_workspace_bytes(...) */
 #define MOE_EHIP -4          /* a HIP launch or copy reported an error */
+#define MOE_ESCRATCH -5      /* the batch needs more than the library's own scratch holds */
 
 /* Workspace selectors for moe_workspace_bytes. */
 #define MOE_OP_ROUTE 0
@@ -268,6 +269,29 @@ typedef struct moe_experts_args {
 } moe_experts_args;
 
 int moe_experts_forward(const moe_experts_args* args, hipStream_t stream);
+
+/*
+ * moe_experts_forward_noalloc -- moe_experts_forward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results,
+ * except that args->ws must be NULL and args->ws_bytes 0: the workspace is a
+ * device array of MOE_NOALLOC_SCRATCH_BYTES (16 MiB) inside the library, one
+ * copy per GPU, kept until the process ends.  The call allocates nothing and
+ * calls no allocating routine; the array's device address is looked up once
+ * per device (on the first call made with that device current) and reused.
+ * `stream` must belong to the current device.
+ * Limit: batches whose moe_workspace_bytes(MOE_OP_EXPERTS, ...) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES are refused with MOE_ESCRATCH before any HIP call
+ * (for example up to 900 assignments T*k at H = 4096: decode batches).
+ * Every call on one GPU uses the same array and leaves its contents there:
+ * calls that may overlap on one GPU (different streams, no ordering between
+ * them) race and give wrong results; order them on one stream or with events.
+ * Errors: as moe_experts_forward; MOE_EINVAL also for a non-null ws or a
+ * nonzero ws_bytes; MOE_EHIP if the array's address cannot be found.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int moe_experts_forward_noalloc(const moe_experts_args* args, hipStream_t stream);
 
 /*
  * arena_load_slot -- copy one expert, read by the host, into a slot or hot-ring

@@ -21,6 +21,8 @@ MOE_EINVAL = -1
 MOE_EUNSUPPORTED = -2
 MOE_EWORKSPACE = -3
 MOE_EHIP = -4
+MOE_ESCRATCH = -5
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 MOE_OP_ROUTE = 0
 MOE_OP_DEMAND = 1
 MOE_OP_EXPERTS = 2
@@ -31,6 +33,7 @@ MOE_MAX_S = 8192
 
 EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
+           "moe_experts_forward_noalloc",
            "arena_load_slot", "moe_hot_pick", "moe_replan", "moe_test_mxfp4_probe",
            "moe_test_stream_read", "moe_test_mfma_loop")
 
@@ -101,6 +104,8 @@ def load() -> ctypes.CDLL:
     lib.moe_demand_accumulate.restype = i
     lib.moe_experts_forward.argtypes = [ctypes.POINTER(ExpertsArgs), vp]
     lib.moe_experts_forward.restype = i
+    lib.moe_experts_forward_noalloc.argtypes = [ctypes.POINTER(ExpertsArgs), vp]
+    lib.moe_experts_forward_noalloc.restype = i
     lib.arena_load_slot.argtypes = [vp, sz, i, i, vp, sz, vp, vp]
     lib.arena_load_slot.restype = i
     lib.moe_hot_pick.argtypes = [vp, vp, i, i, i, vp, i, i, vp, ctypes.c_double, vp, vp, sz,
@@ -225,6 +230,18 @@ def moe_experts_forward(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, per
                     _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp,
                     int(defer_slot), _event(defer_event))
     return int(load().moe_experts_forward(ctypes.byref(a), _stream(stream)))
+
+
+def moe_experts_forward_noalloc(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm,
+                                sel_slot, sel_weight, out, stream=None, stage_events=None,
+                                defer_slot=-1, defer_event=None, ws=None, ws_bytes=0) -> int:
+    """moe_experts_forward with the library's own scratch (ws must stay None / 0)."""
+    keep, evp = _events(stage_events)
+    a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
+                    int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
+                    _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp,
+                    int(defer_slot), _event(defer_event))
+    return int(load().moe_experts_forward_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 def arena_load_slot(arena, slot_stride, num_slots, slot, host_src, nbytes, side_stream=None,

@@ -19,6 +19,9 @@ extern "C" MOE_EXPORT const char* moe_status_string(int status) {
       return "MOE_EUNSUPPORTED: H or I not a multiple of 32, k > min(E, 32), E > 1024 or S > 8192";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
     case MOE_EHIP: return "MOE_EHIP: a HIP launch or copy failed";
+    case MOE_ESCRATCH:
+      return "MOE_ESCRATCH: the batch needs more workspace than the library's own scratch "
+             "(MOE_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown moe status";
   }
 }

@@ -31,6 +31,8 @@
 // The families agree to float32 rounding of their sums, not bit for bit.
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -1204,12 +1206,22 @@ size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S) {
   return experts_ws(T, H, k, I, S).total;
 }
 
-extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
+// Shape checks shared by both entry points (no HIP call).
+static int experts_check_shape(const moe_experts_args* a) {
   if (!a) return MOE_EINVAL;
   const int T = a->T, H = a->H, I = a->I, k = a->k, S = a->S;
   if (T < 0 || H <= 0 || I <= 0 || k <= 0 || S < 0) return MOE_EINVAL;
   if (H % 32 != 0 || I % 32 != 0 || k > MOE_MAX_K || S > MOE_MAX_S) return MOE_EUNSUPPORTED;
   if ((size_t)T * k > (size_t)INT32_MAX) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// Every argument check of a call that runs with workspace (ws, ws_bytes); no
+// HIP call.  MOE_OK means experts_launch may run it.
+static int experts_validate(const moe_experts_args* a, const void* ws, size_t ws_bytes) {
+  const int r = experts_check_shape(a);
+  if (r != MOE_OK) return r;
+  const int T = a->T, H = a->H, I = a->I, k = a->k, S = a->S;
   if (T == 0) return MOE_OK;
   if (!a->xq || !a->slot_offsets || !a->perm || !a->sel_slot || !a->sel_weight || !a->out)
     return MOE_EINVAL;
@@ -1218,10 +1230,26 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   if (a->slot_stride < L.total || a->slot_stride % 256 != 0) return MOE_EINVAL;
   if (!aligned(a->xq, 16) || !aligned(a->arena, 256) || !aligned(a->out, 8)) return MOE_EINVAL;
   const ExpertsWs W = experts_ws(T, H, k, I, S);
-  if (a->ws_bytes < W.total) return MOE_EWORKSPACE;
-  if (!a->ws || !aligned(a->ws, 256)) return MOE_EINVAL;
+  if (ws_bytes < W.total) return MOE_EWORKSPACE;
+  if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   const int defer = a->defer_slot;
   if (defer < -1 || defer >= S || (defer >= 0 && !a->defer_event)) return MOE_EINVAL;
+  if (family_of(T, k, H, I) != kFamSmall) {
+    const size_t ntile = max_tiles((size_t)T * k, S, kTileM);
+    if (up_to(ntile * (size_t)((I + 127) / 128), 8) > 0x7FFFFFFFu ||
+        up_to(ntile * (size_t)((H + 255) / 256), 8) > 0x7FFFFFFFu)
+      return MOE_EUNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+// Enqueues the work of a validated call with workspace ws.
+static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t stream) {
+  const int T = a->T, H = a->H, I = a->I, k = a->k, S = a->S;
+  if (T == 0) return MOE_OK;
+  const SlotLayout L = slot_layout(H, I);
+  const ExpertsWs W = experts_ws(T, H, k, I, S);
+  const int defer = a->defer_slot;
   const int A = T * k;
   const Family fam = family_of(T, k, H, I);
   const size_t ntile = max_tiles((size_t)A, S, kTileM);
@@ -1230,7 +1258,6 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   const int nN2 = (H + 255) / 256;
   const size_t g1 = up_to(ntile * (size_t)nN1, 8);
   const size_t g2 = up_to(ntile * (size_t)nN2, 8);
-  if (fam != kFamSmall && (g1 > 0x7FFFFFFFu || g2 > 0x7FFFFFFFu)) return MOE_EUNSUPPORTED;
   if (S == 0) {
     // nothing routable: every pick is padding, the output is zero
     dim3 grid(T, (H + 256 * YRow<float>::kEl - 1) / (256 * YRow<float>::kEl));
@@ -1238,7 +1265,7 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
                                                     k, S, a->out);
     return hip_status();
   }
-  uint8_t* ws = static_cast<uint8_t*>(a->ws);
+  uint8_t* ws = static_cast<uint8_t*>(ws_ptr);
   uint8_t* hq = ws + W.hq_off;
   float* y = reinterpret_cast<float*>(ws + W.y_off);
   hipEvent_t* ev = a->stage_events;
@@ -1368,4 +1395,55 @@ extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStre
   }
   if (!record_stage(ev, 4, stream)) return MOE_EHIP;
   return hip_status();
+}
+
+extern "C" MOE_EXPORT int moe_experts_forward(const moe_experts_args* a, hipStream_t stream) {
+  const int r = a ? experts_validate(a, a->ws, a->ws_bytes) : MOE_EINVAL;
+  if (r != MOE_OK) return r;
+  return experts_launch(a, a->ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// moe_experts_forward_noalloc: the same call with the workspace taken from a
+// device array of the library's own (kNoAllocScratch bytes, one copy per GPU,
+// held until the process ends).  Its device address is looked up once per
+// device, with that device current, and kept; host code never passes the
+// array's name itself to a kernel (on the host it is only a stand-in).
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratch = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratch];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];  // per device: the array's device address
+
+// The scratch array's address on the current device (looked up on the first
+// call there); null if the lookup fails.
+static void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+extern "C" MOE_EXPORT int moe_experts_forward_noalloc(const moe_experts_args* a,
+                                                      hipStream_t stream) {
+  int r = experts_check_shape(a);
+  if (r != MOE_OK) return r;
+  if (a->ws || a->ws_bytes) return MOE_EINVAL;  // the workspace is the library's own
+  if (a->T == 0) return MOE_OK;
+  const size_t need = experts_ws(a->T, a->H, a->k, a->I, a->S).total;
+  if (need > kNoAllocScratch) return MOE_ESCRATCH;
+  // every other check, against a stand-in for the scratch (256-aligned, not read)
+  r = experts_validate(a, reinterpret_cast<const void*>(uintptr_t{256}), kNoAllocScratch);
+  if (r != MOE_OK) return r;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_EHIP;
+  return experts_launch(a, ws, stream);
 }

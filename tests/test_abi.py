@@ -249,3 +249,20 @@ def test_unrecorded_torch_event_is_refused():
         B._event(Unrecorded())
     assert B._event(Recorded()) == 0x1000
     assert B._event(None) is None
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """moe_experts_forward_noalloc: a workspace argument, or a batch larger
+    than the library's scratch, is refused without touching HIP (CPU)."""
+    T, H, k, I, S = 2048, 4096, 8, 2048, 166
+    assert B.moe_workspace_bytes(B.MOE_OP_EXPERTS, T, H, 0, k, I, S) > \
+        B.MOE_NOALLOC_SCRATCH_BYTES
+    args = (H, I, k, S, FAKE, FAKE, B.moe_slot_bytes(H, I), FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert B.moe_experts_forward_noalloc(T, *args) == B.MOE_ESCRATCH
+    assert B.moe_experts_forward_noalloc(8, *args, ws=FAKE, ws_bytes=1 << 24) == B.MOE_EINVAL
+    assert B.moe_experts_forward_noalloc(8, 4096, 2048, 8, 230, 0, FAKE, B.moe_slot_bytes(
+        4096, 2048), FAKE, FAKE, FAKE, FAKE, FAKE) == B.MOE_EINVAL          # null xq
+    assert B.moe_experts_forward_noalloc(8, 4080, 2048, 8, 230, FAKE, FAKE, 1 << 24, FAKE,
+                                         FAKE, FAKE, FAKE, FAKE) == B.MOE_EUNSUPPORTED
+    assert B.moe_experts_forward_noalloc(0, *args) == B.MOE_OK           # empty batch: nothing
+    assert B.status_string(B.MOE_ESCRATCH).startswith("MOE_ESCRATCH")
