@@ -51,6 +51,7 @@ KERNEL_SRC = os.path.join(ROOT, "resident_expert_routing_amd", "csrc", "experts.
 LAYER_WORKLOADS = ("decode", "prefill", "long", "tiny")
 ARENA40_DEMAND_STEPS = 512     # steps of demand before the re-plan
 ARENA40_AFTER_STEPS = 8        # steps run on the re-planned arena
+RING_SLOTS, RING_PER_STEP, RING_STEPS = 64, 8, 32   # the hot ring's cost measurement
 
 
 def log(msg: str) -> None:
@@ -448,17 +449,19 @@ def arena40_workload(args, dev, warmup: int) -> dict:
     model = fixtures.make_arena_model("arena40")
     cfg = model.cfg
     L, T, H, E, k, I, S = model.L, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, model.S
+    S_all = S + RING_SLOTS     # the hot ring's entries sit on top of the arena's slots
     n_steps = ARENA40_DEMAND_STEPS
-    log(f"arena40: {L} layers, T={T} H={H} E={E} k={k} I={I}, {S} shared slots")
-    sa = R.SharedArena(S, H, I, model.expert_slot_table(), dev)
+    log(f"arena40: {L} layers, T={T} H={H} E={E} k={k} I={I}, {S} shared slots "
+        f"+ {RING_SLOTS} ring entries")
+    sa = R.SharedArena(S_all, H, I, model.expert_slot_table(), dev)
     t0 = time.perf_counter()
     sa.upload(model.pair_bytes)
     log(f"arena of {S * sa.arena.stride / 1e9:.1f} GB uploaded in {time.perf_counter() - t0:.1f} s")
     ws = [torch.from_numpy(l.w_router).to(dev) for l in model.layers]
     bs = [torch.from_numpy(l.bias).to(dev) for l in model.layers]
-    n_x = n_steps + ARENA40_AFTER_STEPS
+    n_x = n_steps + ARENA40_AFTER_STEPS + RING_STEPS
     xs = torch.from_numpy(np.stack([model.tokens(s).view(np.int16) for s in range(n_x)])).to(dev)
-    buf = R.LayerBuffers(T, H, E, k, I, S, dev)
+    buf = R.LayerBuffers(T, H, E, k, I, S_all, dev)
     stream = torch.cuda.current_stream(dev)
     mk = lambda: torch.cuda.Event(enable_timing=True)
 
@@ -520,11 +523,13 @@ def arena40_workload(args, dev, warmup: int) -> dict:
     moved = sum(1 for (le, _), (ll, _) in zip(ev, ld) if le != ll)
     a0, a1 = mk(), mk()
     a0.record(stream)
-    for s in range(n_steps, n_x):   # the layers run on the new tables
+    for s in range(n_steps, n_steps + ARENA40_AFTER_STEPS):   # the layers on the new tables
         step(s)
     a1.record(stream)
     torch.cuda.synchronize()
     after_us = a0.elapsed_time(a1) * 1e3 / (ARENA40_AFTER_STEPS * L)
+    ring_block = hot_ring_cost(model, sa, buf, ws, bs, xs, n_steps + ARENA40_AFTER_STEPS, S,
+                               stream, dev)
     block = {
         "value": T / (per_layer_us * 1e-6), "unit": "tokens/s",
         "steps": K, "warmup": warmup, "ms_per_step": ms / K,
@@ -544,6 +549,7 @@ def arena40_workload(args, dev, warmup: int) -> dict:
         "replan": {"demand_steps": n_steps, "swaps": len(ev), "cross_layer_swaps": moved,
                    "bytes_h2d": len(ev) * sa.arena.slot_bytes, "seconds": replan_s,
                    "GB_per_s_h2d": len(ev) * sa.arena.slot_bytes / replan_s / 1e9},
+        "hot_ring": ring_block,
     }
     log(f"arena40: gate/up {gu_us:.1f} us ({roof['frac']:.3f} of peak); layer "
         f"{block['layer']['GB_per_s']:.0f} GB/s; re-plan {len(ev)} swaps in {replan_s:.3f} s; "
@@ -558,6 +564,64 @@ def arena40_workload(args, dev, warmup: int) -> dict:
         block["cpu_baseline"] = cpu_baseline(
             lay, k, what="one of the 40 layer calls of a step (layer 0, its own resident set)")
     return block
+
+
+def hot_ring_cost(model, sa, buf, ws, bs, xs, s0, ring_slot0, stream, dev) -> dict:
+    """Decode steps with the asynchronous hot ring against the same steps
+    without it (TideLM README, "How adaptive expert loading works", item 3,
+    DeepSeek bullet: the pages report the ring's decode cost as a rate with
+    and without it).  Both runs start from the same tables and tokens; with
+    the ring, each step's heaviest misses are planned on the device after the
+    step, copied into ring entries on a side stream while the next step runs,
+    and routable from the step after.  Timed with events on the layer stream
+    around RING_STEPS steps (the host waits for a plan one step behind, so the
+    GPU never idles for it)."""
+    import torch
+    from resident_expert_routing_amd import runtime as R
+    L = model.L
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    table_keep = sa.table.clone()
+    hist_keep = sa.hist.clone()
+
+    def run(with_ring):
+        sa.table.copy_(table_keep)
+        ring = R.HotRing(sa, ring_slot0, RING_SLOTS, RING_PER_STEP, model.pair_bytes, dev) \
+            if with_ring else None
+        torch.cuda.synchronize()
+        e0, e1 = mk(), mk()
+        e0.record(stream)
+        for i in range(RING_STEPS):
+            if ring:
+                ring.before_step(i, stream)
+            for l in range(L):
+                R.route(buf, xs[s0 + i], ws[l], bs[l], sa.table[l], stream, hist_row=sa.hist[l],
+                        delta=ring.delta_row(l) if ring else None)
+                R.experts(buf, sa.arena.ptr(), sa.arena.stride, stream)
+            if ring:
+                ring.after_step(i, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (RING_STEPS * L)
+        # assignments the last step's last layer sent to ring slots (a sample of the effect)
+        routed_ring = int((buf.sel_slot >= ring_slot0).sum())
+        out = {"us_per_layer_call": us, "tokens_per_s": xs.shape[1] / (us * 1e-6)}
+        if ring:
+            out.update({"picks": sum(len(v) for v in ring.picks.values()),
+                        "bytes_h2d": ring.bytes_copied,
+                        "last_layer_assignments_on_ring_slots": routed_ring})
+        return out
+
+    off = run(False)
+    on = run(True)
+    sa.table.copy_(table_keep)
+    sa.hist.copy_(hist_keep)
+    torch.cuda.synchronize()
+    log(f"hot ring: {on['us_per_layer_call']:.1f} us per layer call with it, "
+        f"{off['us_per_layer_call']:.1f} without ({on['picks']} picks, "
+        f"{on['bytes_h2d'] / 1e9:.2f} GB copied)")
+    return {"ring_entries": RING_SLOTS, "picks_per_step": RING_PER_STEP, "steps": RING_STEPS,
+            "on": on, "off": off,
+            "rate_ratio_on_over_off": off["us_per_layer_call"] / on["us_per_layer_call"]}
 
 
 def prepack(names) -> None:

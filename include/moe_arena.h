@@ -80,6 +80,9 @@ extern "C" {
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 32
 #define MOE_MAX_S 8192
+#define MOE_MAX_RING_PAIRS 16384  /* L*E of a ring plan */
+#define MOE_MAX_RING 1024         /* ring entries */
+#define MOE_MAX_RING_PER_STEP 64  /* picks of one ring plan */
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char* moe_status_string(int status);
@@ -371,6 +374,51 @@ int moe_hot_pick(const int32_t* topk_expert, const float* topk_score, int T, int
  */
 int moe_replan(const double* hist, const int32_t* expert_slot, int L, int E, int k, int n_swap,
                int32_t* evict, int32_t* load, int32_t* new_expert_slot, int* n_done);
+
+/*
+ * moe_ring_plan -- one step's plan for the hot ring (TideLM README, "How
+ * adaptive expert loading works", item 3, DeepSeek bullet: after each step the
+ * heaviest misses are read into a ring of slots of their own while the next
+ * step runs, routable from the step after until the ring wraps; every lane's
+ * misses feed one plan).  One kernel on `stream`, one workgroup.
+ *
+ *   Candidates: pairs p = l*E + e with expert_slot[p] < 0 (not routable),
+ *   not held by any ring entry, and miss_weight[p] > 0 (finite).
+ *   Picks: the first min(per_step, R) candidates by larger weight, then lower
+ *   p.  Pick i takes ring entry r = (head + i) mod R (global slot
+ *   ring_slot0 + r); the pair the entry held before is evicted, and if
+ *   expert_slot routes it to that slot it is set to -1 at once (the slot is
+ *   about to be overwritten).  The new pairs are NOT made routable here: the
+ *   caller copies their bytes (arena_load_slot into slot ring_slot0 + r) and
+ *   then calls moe_ring_install.
+ * Inputs : miss_weight [L][E] float -- the step's demand per pair (e.g. the
+ *          `delta` rows moe_route wrote for each layer of the step).
+ * In/out : expert_slot [L][E] int32 (the layers' slot tables, one array);
+ *          ring [1 + R] int32: ring[0] = head, ring[1 + r] = pair held by
+ *          entry r or -1 (start from head 0 and all -1).
+ * Output : plan [1 + 3*per_step] int32: plan[0] = number of picks n, then
+ *          (r, l, e) per pick.
+ * The kernel runs after the step's layers in stream order, so no kernel of the
+ * step still reads an evicted slot; copies into the plan's slots must wait for
+ * it (an event recorded after this call).
+ * Errors: MOE_EINVAL for null or misaligned pointers (4 bytes), L, E, R <= 0,
+ * ring_slot0 < 0 or per_step <= 0; MOE_EUNSUPPORTED for L*E >
+ * MOE_MAX_RING_PAIRS, R > MOE_MAX_RING, per_step > MOE_MAX_RING_PER_STEP or
+ * ring_slot0 + R > MOE_MAX_S.
+ */
+int moe_ring_plan(const float* miss_weight, int32_t* expert_slot, int L, int E, int32_t* ring,
+                  int R, int ring_slot0, int per_step, int32_t* plan, hipStream_t stream);
+
+/*
+ * moe_ring_install -- make a ring plan's pairs routable once their bytes are
+ * in place: for each pick (r, l, e) of `plan` (as moe_ring_plan wrote it)
+ * whose ring entry still holds that pair (ring[1 + r] == l*E + e),
+ * expert_slot[l*E + e] = ring_slot0 + r.  Entries taken over by a later plan
+ * in the meantime are skipped.  Order it after the copies' events.
+ * Errors: as moe_ring_plan (plan must be non-null and 4-byte aligned).
+ */
+int moe_ring_install(const int32_t* plan, int32_t* expert_slot, int L, int E,
+                     const int32_t* ring, int R, int ring_slot0, hipStream_t stream);
 
 /*
  * moe_test_mxfp4_probe -- test-only: one wave runs one block-scaled MXFP4

@@ -91,3 +91,62 @@ def replan(hist: np.ndarray, expert_slot: np.ndarray, n_swap: int, k: int):
         new[ll, el] = es[le, ee]
         new[le, ee] = -1
     return evicted, loaded, new
+
+
+# ----------------------------------------------------------------------------
+# Hot ring (TideLM README, "How adaptive expert loading works", item 3,
+# DeepSeek bullet, and "Settings worth knowing": the ring's slots sit on top
+# of the arena budget).  After each step the heaviest misses of that step --
+# every lane's tokens feed one plan -- are read into ring slots of their own
+# while the next step runs, and are routable from the step after it until the
+# ring wraps round onto them.
+#
+# State: ring[r] = the pair id l*E + e held (or being filled) by ring entry r,
+# -1 if empty; head = the entry the next pick overwrites.  Ring entry r is
+# global slot slot0 + r.
+# ----------------------------------------------------------------------------
+def ring_plan(miss_weight, table, ring, head, per_step, slot0):
+    """One step's ring plan.
+
+    miss_weight [L][E]: the step's demand of every (layer, expert) -- the sum
+    of the routing scores of the picks the router wanted (item 1's record for
+    this step).  Candidates: pairs that are not routable (table < 0), are not
+    already in the ring, and have weight > 0.  The first min(per_step, R) of
+    them by (larger weight, then lower pair id) take ring entries head, head+1,
+    ... (mod R) in that order.  The pair an entry held before is evicted: if
+    the table routes it to that entry's slot it becomes non-routable at once
+    (the copy will overwrite the slot), otherwise the table is left alone.
+    The new pairs stay non-routable until ring_install.
+
+    Returns (plan [(r, l, e)], new table, new ring, new head).
+    """
+    w = np.asarray(miss_weight, dtype=np.float64)
+    tab = np.asarray(table).copy()
+    L, E = tab.shape
+    ring = list(int(v) for v in ring)
+    R = len(ring)
+    in_ring = {p for p in ring if p >= 0}
+    cands = [(-w[l, e], l * E + e) for l in range(L) for e in range(E)
+             if tab[l, e] < 0 and w[l, e] > 0 and l * E + e not in in_ring]
+    cands.sort()
+    plan = []
+    for i, (_, p) in enumerate(cands[:min(per_step, R)]):
+        r = (head + i) % R
+        old = ring[r]
+        if old >= 0 and tab[old // E, old % E] == slot0 + r:
+            tab[old // E, old % E] = -1
+        ring[r] = p
+        plan.append((r, p // E, p % E))
+    return plan, tab, ring, (head + len(plan)) % R if R else 0
+
+
+def ring_install(plan, table, ring, slot0):
+    """Make a plan's pairs routable once their bytes are in place: each
+    (r, l, e) whose ring entry still holds (l, e) gets table[l, e] = slot0 + r
+    (an entry taken over by a later plan meanwhile is skipped)."""
+    tab = np.asarray(table).copy()
+    L, E = tab.shape
+    for r, l, e in plan:
+        if ring[r] == l * E + e:
+            tab[l, e] = slot0 + r
+    return tab

@@ -30,10 +30,13 @@ MOE_OP_HOT_PICK = 3
 MOE_MAX_E = 1024
 MOE_MAX_K = 32
 MOE_MAX_S = 8192
+MOE_MAX_RING_PAIRS = 16384
+MOE_MAX_RING = 1024
+MOE_MAX_RING_PER_STEP = 64
 
 EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
-           "moe_experts_forward_noalloc",
+           "moe_experts_forward_noalloc", "moe_ring_plan", "moe_ring_install",
            "arena_load_slot", "moe_hot_pick", "moe_replan", "moe_test_mxfp4_probe",
            "moe_test_stream_read", "moe_test_mfma_loop")
 
@@ -113,6 +116,10 @@ def load() -> ctypes.CDLL:
     lib.moe_hot_pick.restype = i
     lib.moe_replan.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, ctypes.POINTER(i)]
     lib.moe_replan.restype = i
+    lib.moe_ring_plan.argtypes = [vp, vp, i, i, vp, i, i, i, vp, vp]
+    lib.moe_ring_plan.restype = i
+    lib.moe_ring_install.argtypes = [vp, vp, i, i, vp, i, i, vp]
+    lib.moe_ring_install.restype = i
     lib.moe_test_mxfp4_probe.argtypes = [i, vp, vp, vp, vp, vp, vp]
     lib.moe_test_mxfp4_probe.restype = i
     lib.moe_test_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i, vp]
@@ -265,6 +272,18 @@ def moe_replan(hist, expert_slot, L, E, k, n_swap, evict, load, new_expert_slot,
     return int(load_lib().moe_replan(_host(hist), _host(expert_slot), int(L), int(E), int(k),
                                      int(n_swap), _host(evict), _host(load),
                                      _host(new_expert_slot), ctypes.byref(n_done)))
+
+
+def moe_ring_plan(miss_weight, expert_slot, L, E, ring, R, ring_slot0, per_step, plan,
+                  stream=None) -> int:
+    return int(load().moe_ring_plan(_ptr(miss_weight), _ptr(expert_slot), int(L), int(E),
+                                    _ptr(ring), int(R), int(ring_slot0), int(per_step),
+                                    _ptr(plan), _stream(stream)))
+
+
+def moe_ring_install(plan, expert_slot, L, E, ring, R, ring_slot0, stream=None) -> int:
+    return int(load().moe_ring_install(_ptr(plan), _ptr(expert_slot), int(L), int(E), _ptr(ring),
+                                       int(R), int(ring_slot0), _stream(stream)))
 
 
 def moe_test_mxfp4_probe(shape, a, a_scale, b, b_scale, d, stream=None) -> int:

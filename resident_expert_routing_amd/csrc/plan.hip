@@ -133,9 +133,137 @@ __global__ __launch_bounds__(1024) void hot_pick_final(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Hot ring (TideLM README, "How adaptive expert loading works", item 3,
+// DeepSeek bullet): after each step the step's heaviest misses take ring
+// entries in round-robin order.  One workgroup; a pair's key packs its weight
+// and its id in 64 bits (larger weight first, then lower id) so that one
+// unsigned maximum orders candidates.  Each pick is one workgroup maximum over
+// a fresh scan of the pairs (weights and table stay in L2 after the first
+// round); pairs held by the ring or already picked are marked in an LDS bitmap.
+// ---------------------------------------------------------------------------
+constexpr int kRingThreads = 1024;
+
+__device__ __forceinline__ uint64_t ring_key(float w, int p) {
+  // w > 0 and finite: its bits order like its value
+  return ((uint64_t)__float_as_uint(w) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+}
+
+__global__ __launch_bounds__(kRingThreads) void ring_plan_kernel(
+    const float* __restrict__ w, int32_t* __restrict__ table, int n, int E,
+    int32_t* __restrict__ ring, int R, int slot0, int per_step, int32_t* __restrict__ plan) {
+  __shared__ uint32_t taken[MOE_MAX_RING_PAIRS / 32];  // in the ring, or picked this call
+  __shared__ uint64_t part[kRingThreads / 64];
+  __shared__ int32_t chosen[MOE_MAX_RING_PER_STEP];
+  __shared__ uint64_t winner;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < (n + 31) / 32; i += kRingThreads) taken[i] = 0u;
+  __syncthreads();
+  for (int r = tid; r < R; r += kRingThreads) {
+    const int p = ring[1 + r];
+    if (p >= 0 && p < n) atomicOr(&taken[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  const int m = per_step < R ? per_step : R;
+  int count = 0;
+  for (; count < m; ++count) {
+    uint64_t best = 0ull;
+    for (int p = tid; p < n; p += kRingThreads) {
+      if ((taken[p >> 5] >> (p & 31)) & 1u) continue;
+      if (table[p] >= 0) continue;  // routable: not a miss
+      const float v = w[p];
+      if (v > 0.f && v <= 3.402823466e38f) {  // NaN and inf never win
+        const uint64_t key = ring_key(v, p);
+        best = key > best ? key : best;
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+      const uint64_t o = __shfl_xor(best, d, kWave);
+      best = o > best ? o : best;
+    }
+    if (lane == 0) part[wv] = best;
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t b = part[0];
+      for (int i = 1; i < kRingThreads / 64; ++i) b = part[i] > b ? part[i] : b;
+      winner = b;
+      if (b != 0ull) {
+        const int p = (int)(0xFFFFFFFFu - (uint32_t)b);
+        chosen[count] = p;
+        taken[p >> 5] |= 1u << (p & 31);
+      }
+    }
+    __syncthreads();
+    if (winner == 0ull) break;  // no candidate left (uniform)
+    __syncthreads();            // part[] and winner are rewritten by the next pick
+  }
+  if (tid == 0) {
+    const int head = ring[0];
+    for (int i = 0; i < count; ++i) {
+      const int r = (head + i) % R;
+      const int old = ring[1 + r];
+      if (old >= 0 && old < n && table[old] == slot0 + r) table[old] = -1;  // evicted
+      const int p = chosen[i];
+      ring[1 + r] = p;
+      plan[1 + 3 * i] = r;
+      plan[2 + 3 * i] = p / E;
+      plan[3 + 3 * i] = p % E;
+    }
+    ring[0] = (head + count) % R;
+    plan[0] = count;
+  }
+}
+
+// Install a plan's pairs whose ring entries still hold them.
+__global__ __launch_bounds__(64) void ring_install_kernel(const int32_t* __restrict__ plan,
+                                                         int32_t* __restrict__ table, int n,
+                                                         int E, const int32_t* __restrict__ ring,
+                                                         int R, int slot0, int max_count) {
+  const int count = min(plan[0], max_count);
+  for (int i = threadIdx.x; i < count; i += 64) {
+    const int r = plan[1 + 3 * i], l = plan[2 + 3 * i], e = plan[3 + 3 * i];
+    if (r < 0 || r >= R || e < 0 || e >= E) continue;
+    const int p = l * E + e;
+    if (p >= 0 && p < n && ring[1 + r] == p) table[p] = slot0 + r;
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+static int ring_args_ok(int L, int E, int R, int ring_slot0, const void* table, const void* ring) {
+  if (L <= 0 || E <= 0 || R <= 0 || ring_slot0 < 0) return MOE_EINVAL;
+  if ((size_t)L * E > (size_t)MOE_MAX_RING_PAIRS || R > MOE_MAX_RING) return MOE_EUNSUPPORTED;
+  if ((size_t)ring_slot0 + R > (size_t)MOE_MAX_S) return MOE_EUNSUPPORTED;
+  if (!table || !ring || !aligned(table, 4) || !aligned(ring, 4)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+extern "C" MOE_EXPORT int moe_ring_plan(const float* miss_weight, int32_t* expert_slot, int L,
+                                        int E, int32_t* ring, int R, int ring_slot0,
+                                        int per_step, int32_t* plan, hipStream_t stream) {
+  const int r = ring_args_ok(L, E, R, ring_slot0, expert_slot, ring);
+  if (r != MOE_OK) return r;
+  if (per_step <= 0) return MOE_EINVAL;
+  if (per_step > MOE_MAX_RING_PER_STEP) return MOE_EUNSUPPORTED;
+  if (!miss_weight || !plan || !aligned(miss_weight, 4) || !aligned(plan, 4)) return MOE_EINVAL;
+  ring_plan_kernel<<<1, kRingThreads, 0, stream>>>(miss_weight, expert_slot, L * E, E, ring, R,
+                                                   ring_slot0, per_step, plan);
+  return hip_status();
+}
+
+extern "C" MOE_EXPORT int moe_ring_install(const int32_t* plan, int32_t* expert_slot, int L,
+                                           int E, const int32_t* ring, int R, int ring_slot0,
+                                           hipStream_t stream) {
+  const int r = ring_args_ok(L, E, R, ring_slot0, expert_slot, ring);
+  if (r != MOE_OK) return r;
+  if (!plan || !aligned(plan, 4)) return MOE_EINVAL;
+  ring_install_kernel<<<1, 64, 0, stream>>>(plan, expert_slot, L * E, E, ring, R, ring_slot0,
+                                            MOE_MAX_RING_PER_STEP);
+  return hip_status();
+}
 
 size_t moe_hot_pick_ws_bytes_internal(int T) {
   return up_to((size_t)hot_pick_wgs(T) * sizeof(Miss), 256);

@@ -94,15 +94,17 @@ class Arena:
 
 
 def route(buf: LayerBuffers, x, w_router, bias, expert_slot, stream=None,
-          stage_events=None, hist_row=None, reuse_logits=False) -> None:
-    """moe_route; with hist_row it also accumulates this batch's demand.
+          stage_events=None, hist_row=None, reuse_logits=False, delta=None) -> None:
+    """moe_route; with hist_row it also accumulates this batch's demand, and
+    writes the per-call demand to `delta` (default: buf.delta).
     reuse_logits: the previous route on these buffers had the same x and
     w_router (only the routable set changed): skip the router's products."""
+    if delta is None and hist_row is not None:
+        delta = buf.delta
     B.check(B.moe_route(buf.T, buf.H, buf.E, buf.k, buf.S, x, w_router, bias, expert_slot,
                         buf.topk_expert, buf.topk_score, buf.sel_expert, buf.sel_weight,
                         buf.sel_slot, buf.slot_offsets, buf.perm, buf.xq, buf.ws_route,
-                        buf.ws_route_bytes, stream, stage_events, hist_row,
-                        buf.delta if hist_row is not None else None, reuse_logits),
+                        buf.ws_route_bytes, stream, stage_events, hist_row, delta, reuse_logits),
             "moe_route")
 
 
@@ -275,3 +277,91 @@ class SharedArena:
             self.table.copy_(staged, non_blocking=True)
         self._staged = staged                   # kept alive until the copy has run
         return ([tuple(map(int, p)) for p in ev[:n]], [tuple(map(int, p)) for p in ld[:n]])
+
+
+class HotRing:
+    """The asynchronous hot ring of a shared arena (TideLM README, "How adaptive
+    expert loading works", item 3, DeepSeek bullet).
+
+    R ring entries are the arena's slots ring_slot0 .. ring_slot0 + R - 1, on
+    top of the resident budget.  Per step s the caller runs
+        ring.before_step(s)      # installs the plan of step s - 2 (its copies done)
+        ... every layer l: route(..., hist_row=hist[l], delta=ring.delta_row(l)) + experts ...
+        ring.after_step(s)       # plans step s's heaviest misses on the GPU
+                                 # (evictions take effect at once), then enqueues
+                                 # the copies of step s - 1's plan on the side stream
+    so the misses of step s are copied while step s + 1 runs and are routable
+    from step s + 2 on.  The plan is taken on the device (moe_ring_plan); the
+    host only reads its few picks back -- one step late, so it never waits for
+    the step it has just enqueued -- and issues arena_load_slot for each.
+    """
+
+    def __init__(self, sa: "SharedArena", ring_slot0: int, R: int, per_step: int,
+                 pair_bytes_fn, device):
+        assert 0 < per_step <= R and 2 * per_step <= R, "a plan must not wrap onto the last one"
+        assert ring_slot0 + R <= sa.arena.S
+        self.sa, self.slot0, self.R, self.per_step = sa, int(ring_slot0), int(R), int(per_step)
+        self.pair_bytes = pair_bytes_fn
+        self.device = device
+        L, E = sa.L, sa.E
+        self.delta = torch.zeros((L, E), dtype=torch.float32, device=device)
+        self.ring = torch.full((1 + R,), -1, dtype=torch.int32, device=device)
+        self.ring[0] = 0
+        n = 1 + 3 * per_step
+        self.plan = [torch.zeros(n, dtype=torch.int32, device=device) for _ in range(2)]
+        self.plan_host = [torch.zeros(n, dtype=torch.int32).pin_memory() for _ in range(2)]
+        self.planned = [torch.cuda.Event() for _ in range(2)]
+        self.copied = [torch.cuda.Event() for _ in range(2)]
+        self.side = torch.cuda.Stream(device)      # default priority
+        self.n_copies = [0, 0]                      # copies issued for the plan in each buffer
+        self.picks = {}                             # step -> [(r, l, e)] as read back
+        self.bytes_copied = 0
+
+    def delta_row(self, l: int) -> torch.Tensor:
+        return self.delta[l]
+
+    def before_step(self, s: int, stream=None) -> None:
+        stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        b = (s - 2) % 2
+        if s >= 2 and self.n_copies[b]:
+            stream.wait_event(self.copied[b])
+            B.check(B.moe_ring_install(self.plan[b], self.sa.table, self.sa.L, self.sa.E,
+                                       self.ring, self.R, self.slot0, stream), "moe_ring_install")
+
+    def after_step(self, s: int, stream=None) -> None:
+        stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        b = s % 2
+        B.check(B.moe_ring_plan(self.delta, self.sa.table, self.sa.L, self.sa.E, self.ring,
+                                self.R, self.slot0, self.per_step, self.plan[b], stream),
+                "moe_ring_plan")
+        with torch.cuda.stream(stream):
+            self.plan_host[b].copy_(self.plan[b], non_blocking=True)
+        self.planned[b].record(stream)
+        self.n_copies[b] = 0
+        if s >= 1:
+            self._copy(s - 1)
+
+    def finish(self, s_last: int) -> None:
+        """After the last step: issue the copies of its plan too (they are then
+        routable from the step after, if the caller runs one)."""
+        self._copy(s_last)
+
+    def _copy(self, s: int) -> None:
+        b = s % 2
+        if s in self.picks:
+            return
+        self.planned[b].synchronize()            # the end of step s (already past, or nearly)
+        n = int(self.plan_host[b][0])
+        picks = [tuple(int(v) for v in self.plan_host[b][1 + 3 * i: 4 + 3 * i]) for i in range(n)]
+        self.picks[s] = picks
+        if not picks:
+            return
+        self.side.wait_event(self.planned[b])    # the evicted entries are no longer read
+        a = self.sa.arena
+        for r, l, e in picks:
+            src = self.sa._pin(l, e, self.pair_bytes)
+            B.check(B.arena_load_slot(a.mem, a.stride, a.S, self.slot0 + r, src, a.slot_bytes,
+                                      self.side, None), "arena_load_slot")
+            self.bytes_copied += a.slot_bytes
+        self.copied[b].record(self.side)
+        self.n_copies[b] = len(picks)

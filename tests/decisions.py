@@ -100,3 +100,38 @@ def check_replan(got_ev, got_ld, got_table, hist, table, n_swap, k):
     floor = np.minimum((table >= 0).sum(axis=1), k)
     assert ((new >= 0).sum(axis=1) >= floor).all(), "a layer fell below k routable experts"
     return oev, old, onew
+
+
+def check_ring_plan(got, weight, table, ring, head, per_step, slot0):
+    """The GPU's ring picks [(r, l, e)] against the oracle's ring_plan on the
+    oracle's float64 step demand.  Equal, or the picked pairs' weights, in
+    order, within HIST_REL of the oracle's (float32 per-call demand against
+    float64 sums), every pick a valid candidate, entries in ring order.
+    Returns the plan to continue the simulation with (the GPU's, once accepted)
+    as (plan, table, ring, head) after applying it."""
+    want = plan.ring_plan(weight, table, ring, head, per_step, slot0)
+    got = [tuple(int(v) for v in p) for p in got]
+    if got == [tuple(p) for p in want[0]]:
+        return want
+    w = np.asarray(weight, dtype=np.float64)
+    tab = np.asarray(table)
+    L, E = tab.shape
+    assert len(got) == len(want[0]), ("ring pick counts differ", got, want[0])
+    in_ring = {p for p in ring if p >= 0}
+    R = len(ring)
+    for i, (r, l, e) in enumerate(got):
+        assert r == (head + i) % R, ("ring entries out of order", got)
+        assert tab[l, e] < 0 and w[l, e] > 0 and l * E + e not in in_ring, ("not a miss", l, e)
+    assert len({(l, e) for _, l, e in got}) == len(got)
+    for (_, gl, ge), (_, wl, we) in zip(got, want[0]):
+        assert hist_close(w[gl, ge], w[wl, we]), ("ring picks differ beyond the margin",
+                                                  (gl, ge, w[gl, ge]), (wl, we, w[wl, we]))
+    # apply the GPU's picks with the oracle's eviction rule
+    tab = tab.copy()
+    ring = list(ring)
+    for r, l, e in got:
+        old = ring[r]
+        if old >= 0 and tab[old // E, old % E] == slot0 + r:
+            tab[old // E, old % E] = -1
+        ring[r] = l * E + e
+    return got, tab, ring, (head + len(got)) % R

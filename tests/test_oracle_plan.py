@@ -129,3 +129,94 @@ def test_replan_hand_worked():
     ev, ld, new = plan.replan(hist, table, 5, 1)
     assert ev == [(1, 0), (0, 2), (0, 1)] and ld == [(0, 3), (1, 3), (1, 2)]
     assert new.tolist() == [[0, -1, -1, 3], [-1, 4, 1, 2]]
+
+
+# ---------------------------------------------------------------------------
+# hot ring
+# ---------------------------------------------------------------------------
+def test_ring_hand_worked():
+    """Two layers of four experts, a ring of 3 entries (global slots 10-12),
+    two picks a step; worked by hand."""
+    table = np.array([[0, -1, 1, -1], [2, -1, -1, -1]])
+    w = np.array([[0.5, 0.3, 0.9, 0.0], [0.2, 0.3, 0.7, 0.1]])
+    # misses: (0,1) 0.3, (1,1) 0.3, (1,2) 0.7, (1,3) 0.1; (0,3) has no weight.
+    # heaviest first, the 0.3 tie to the lower pair id (0,1) = 1 before (1,1) = 5
+    plan_a, t1, ring, head = plan.ring_plan(w, table, [-1, -1, -1], 0, 2, 10)
+    assert plan_a == [(0, 1, 2), (1, 0, 1)] and ring == [6, 1, -1] and head == 2
+    assert np.array_equal(t1, table)              # nothing routable before the install
+    t2 = plan.ring_install(plan_a, t1, ring, 10)
+    assert t2.tolist() == [[0, 11, 1, -1], [2, -1, 10, -1]]
+    # next step: (1,1) takes the empty entry 2, (1,3) wraps onto entry 0 and
+    # evicts (1,2), which stops being routable at once
+    plan_b, t3, ring, head = plan.ring_plan(w, t2, ring, head, 2, 10)
+    assert plan_b == [(2, 1, 1), (0, 1, 3)] and ring == [7, 1, 5] and head == 1
+    assert t3.tolist() == [[0, 11, 1, -1], [2, -1, -1, -1]]
+    t4 = plan.ring_install(plan_b, t3, ring, 10)
+    assert t4.tolist() == [[0, 11, 1, -1], [2, 12, -1, 10]]
+
+
+def test_ring_pending_pairs_not_planned_twice_and_stale_install_skipped():
+    table = np.array([[-1, -1, 0]])
+    w = np.array([[0.4, 0.6, 0.9]])
+    p1, t1, ring, head = plan.ring_plan(w, table, [-1], 0, 1, 5)
+    assert p1 == [(0, 0, 1)] and ring == [1]
+    # planned again before the install: expert 1 is in flight, so expert 0 is
+    # next, and it takes the only entry over
+    p2, t2, ring, head = plan.ring_plan(w, t1, ring, head, 1, 5)
+    assert p2 == [(0, 0, 0)] and ring == [0]
+    t3 = plan.ring_install(p1, t2, ring, 5)       # entry 0 no longer holds expert 1
+    assert t3.tolist() == [[-1, -1, 0]]
+    t4 = plan.ring_install(p2, t3, ring, 5)
+    assert t4.tolist() == [[5, -1, 0]]
+
+
+def brute_ring_picks(w, table, ring, per_step):
+    """Literal "take the heaviest remaining miss" rounds (no sort)."""
+    L, E = table.shape
+    taken = set(p for p in ring if p >= 0)
+    out = []
+    for _ in range(min(per_step, len(ring))):
+        best = None
+        for l in range(L):
+            for e in range(E):
+                p = l * E + e
+                if table[l, e] >= 0 or w[l, e] <= 0 or p in taken:
+                    continue
+                if best is None or w[l, e] > w[best // E, best % E]:
+                    best = p       # strict: an equal weight later in the scan loses
+        if best is None:
+            break
+        taken.add(best)
+        out.append(best)
+    return out
+
+
+def test_ring_bruteforce_and_invariants():
+    rng = np.random.default_rng(8)
+    for trial in range(60):
+        L, E, R = int(rng.integers(1, 4)), int(rng.integers(2, 9)), int(rng.integers(1, 6))
+        slot0 = 100
+        table = np.where(rng.random((L, E)) < 0.4, 0, -1)
+        table[table >= 0] = np.arange(int((table >= 0).sum()))
+        ring, head = [-1] * R, 0
+        pending = []
+        for step in range(6):
+            w = rng.integers(0, 4, size=(L, E)) / 4.0        # ties and zeros
+            per = int(rng.integers(1, R + 1))
+            want = brute_ring_picks(w, table, ring, per)
+            p, t2, ring2, head2 = plan.ring_plan(w, table, ring, head, per, slot0)
+            assert [l * E + e for _, l, e in p] == want
+            assert [r for r, _, _ in p] == [(head + i) % R for i in range(len(p))]
+            assert head2 == (head + len(p)) % R
+            live = [q for q in ring2 if q >= 0]
+            assert len(live) == len(set(live))             # a pair is in the ring once
+            for r, q in enumerate(ring2):                   # routable ring pairs use their slot
+                if q >= 0 and t2[q // E, q % E] >= slot0:
+                    assert t2[q // E, q % E] == slot0 + r
+            for r, q in enumerate(ring):                    # evicted pairs are not routable
+                if q >= 0 and q not in live:
+                    assert t2[q // E, q % E] != slot0 + r
+            table, ring, head = t2, ring2, head2
+            pending.append(p)
+            if len(pending) == 2:                           # installed one step later
+                table = plan.ring_install(pending.pop(0), table, ring, slot0)
