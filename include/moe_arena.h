@@ -70,6 +70,8 @@ extern "C" {
 #define MOE_EWORKSPACE -3    /* ws_bytes below moe_workspace_bytes(...) */
 #define MOE_EHIP -4          /* a HIP launch or copy reported an error */
 #define MOE_ESCRATCH -5      /* the batch needs more than the library's own scratch holds */
+#define MOE_EIO -6           /* a history file could not be opened, read, written or renamed */
+#define MOE_EFORMAT -7       /* a history file is not one of this shape, or is damaged */
 
 /* Workspace selectors for moe_workspace_bytes. */
 #define MOE_OP_ROUTE 0
@@ -419,6 +421,56 @@ int moe_ring_plan(const float* miss_weight, int32_t* expert_slot, int L, int E, 
  */
 int moe_ring_install(const int32_t* plan, int32_t* expert_slot, int L, int E,
                      const int32_t* ring, int R, int ring_slot0, hipStream_t stream);
+
+/*
+ * Demand history across restarts and the arena filled from it (TideLM README,
+ * "How adaptive expert loading works", item 1: every pick the router wants is
+ * recorded per (layer, expert) into a history that persists across restarts;
+ * the arena is filled from it at boot and re-planned after each prompt's
+ * prefill, every few hundred generated tokens and between requests;
+ * "Settings worth knowing": the history lives in a state file, and a
+ * sensitivity setting sets how fast the resident set follows new traffic).
+ *
+ * History file (little-endian):
+ *   bytes 0-7   magic "MOEHIST" followed by the byte 0x01
+ *   bytes 8-11  L (uint32), bytes 12-15 E (uint32)
+ *   bytes 16-23 tokens (uint64): routed tokens the history has seen (the
+ *               caller's count; stored and returned as is)
+ *   then        L*E float64, row-major [L][E], each finite and >= 0
+ *   last 8      FNV-1a 64-bit hash (offset basis 0xcbf29ce484222325, prime
+ *               0x100000001b3) of every byte before it
+ */
+
+/* Writes hist [L][E] (host) to `path`: to path + ".tmp" first, then renamed
+ * over `path`, so a reader never sees a partly written file.  MOE_EINVAL for
+ * null pointers, L or E <= 0, or a negative, NaN or infinite entry; MOE_EIO if
+ * a write or the rename fails.  Host only, no HIP call. */
+int moe_history_save(const char* path, const double* hist, int L, int E, uint64_t tokens);
+
+/* Reads a history written by moe_history_save into hist [L][E] (host) and, if
+ * `tokens` is non-null, its token count.  MOE_EIO if the file cannot be
+ * opened or read; MOE_EFORMAT for another magic, another L or E, a short or
+ * long file, a hash mismatch or an entry that is negative, NaN or infinite;
+ * hist and tokens are written only on MOE_OK.  Host only. */
+int moe_history_load(const char* path, double* hist, int L, int E, uint64_t* tokens);
+
+/* The arena filled from a history at boot: expert_slot [L][E] (host output)
+ * holds min(n_slots, L*E) resident pairs.  Every layer first keeps its
+ * min(k, E) hottest experts (within a layer: larger history, then lower
+ * expert id), so routing can always make k picks; the remaining slots go to
+ * the other pairs in the order (larger history, then rank inside their layer,
+ * then lower layer) -- equal histories, a fresh all-zero one above all, are
+ * shared round-robin between layers.  Slots 0, 1, ... are given to the chosen
+ * pairs in ascending (layer, expert); every other entry is -1.  MOE_EINVAL for
+ * null pointers, L, E, k <= 0, n_slots < L*min(k, E) or a NaN in hist;
+ * MOE_EUNSUPPORTED for E > MOE_MAX_E or k > MOE_MAX_K.  Host only. */
+int moe_boot_plan(const double* hist, int L, int E, int k, int n_slots, int32_t* expert_slot);
+
+/* hist[i] *= factor for i < n (device array), on `stream`: the history's
+ * forgetting before a re-plan (factor 1 keeps everything; a smaller factor
+ * makes the resident set follow new traffic faster).  MOE_EINVAL for a null
+ * or misaligned pointer (8 bytes) or a factor outside [0, 1]. */
+int moe_history_scale(double* hist, size_t n, double factor, hipStream_t stream);
 
 /*
  * moe_test_mxfp4_probe -- test-only: one wave runs one block-scaled MXFP4

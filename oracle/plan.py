@@ -150,3 +150,94 @@ def ring_install(plan, table, ring, slot0):
         if ring[r] == l * E + e:
             tab[l, e] = slot0 + r
     return tab
+
+
+# ----------------------------------------------------------------------------
+# Demand-history planner (TideLM README, "How adaptive expert loading works",
+# item 1: the history persists across restarts, the arena is filled from it at
+# boot and re-planned after each prompt's prefill, every few hundred generated
+# tokens and between requests; "Settings worth knowing": a sensitivity setting
+# sets how fast the resident set follows new traffic, and GLM_ADAPT_EVERY=200
+# the re-plan period in generated tokens).
+# ----------------------------------------------------------------------------
+def boot_fill(hist, n_slots, k):
+    """Resident set and slot table filled from a history at boot.
+
+    Every layer first keeps its min(k, E) hottest experts (so routing always
+    finds k picks); the remaining slots go to the hottest remaining pairs.  A
+    pair's place is (larger history, then its rank inside its layer, then
+    lower layer), so equal histories -- a fresh, all-zero history above all --
+    are shared round-robin between layers instead of filling layer 0 first.
+    Within a layer, rank = position by (larger history, lower expert id).
+    Slots 0, 1, ... go to the chosen pairs in ascending (layer, expert).
+    Returns the [L][E] table (-1 = not resident)."""
+    h = np.asarray(hist, dtype=np.float64)
+    L, E = h.shape
+    floor = min(k, E)
+    if n_slots < L * floor:
+        raise ValueError("fewer slots than the per-layer floor needs")
+    n_slots = min(n_slots, L * E)
+    rank = np.zeros((L, E), dtype=np.int64)
+    for l in range(L):
+        order = sorted(range(E), key=lambda e: (-h[l, e], e))
+        for r, e in enumerate(order):
+            rank[l, e] = r
+    chosen = {(l, e) for l in range(L) for e in range(E) if rank[l, e] < floor}
+    rest = sorted(((-h[l, e], rank[l, e], l, e) for l in range(L) for e in range(E)
+                   if (l, e) not in chosen))
+    for _, _, l, e in rest[:n_slots - len(chosen)]:
+        chosen.add((l, e))
+    table = np.full((L, E), -1, dtype=np.int64)
+    for s, (l, e) in enumerate(sorted(chosen)):
+        table[l, e] = s
+    return table
+
+
+SENSITIVITY_DECAY = {"low": 1.0, "medium": 0.9, "high": 0.75}
+
+
+def decay(hist, factor):
+    """History after forgetting: every entry times `factor` (applied before
+    each re-plan, so older traffic weighs less; factor 1 keeps everything)."""
+    return np.asarray(hist, dtype=np.float64) * float(factor)
+
+
+def gainful_swaps(hist, evicted, loaded):
+    """How many leading swaps of a re-plan gain demand: the i-th swap is kept
+    while the pair it loads has a larger history than the pair it evicts (the
+    lists run coldest-evicted and hottest-loaded first, so the gains only
+    shrink along them)."""
+    h = np.asarray(hist, dtype=np.float64)
+    n = 0
+    for ev, ld in zip(evicted, loaded):
+        if not h[tuple(ld)] > h[tuple(ev)]:
+            break
+        n += 1
+    return n
+
+
+def replan_points(events, every):
+    """Where the cadence re-plans, for a stream of serving events.
+
+    events: ("prefill", request), ("token", request) per generated token, and
+    ("end", request).  A re-plan follows each prefill; during decoding, every
+    `every` generated tokens since the last re-plan; and at the end of a
+    request when tokens were generated since the last one (between requests).
+    Returns the indices of the events after which a re-plan runs."""
+    out, since = [], 0
+    for i, (kind, _) in enumerate(events):
+        if kind == "prefill":
+            out.append(i)
+            since = 0
+        elif kind == "token":
+            since += 1
+            if since >= every:
+                out.append(i)
+                since = 0
+        elif kind == "end":
+            if since > 0:
+                out.append(i)
+            since = 0
+        else:
+            raise ValueError(kind)
+    return out

@@ -22,6 +22,8 @@ MOE_EUNSUPPORTED = -2
 MOE_EWORKSPACE = -3
 MOE_EHIP = -4
 MOE_ESCRATCH = -5
+MOE_EIO = -6
+MOE_EFORMAT = -7
 MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 MOE_OP_ROUTE = 0
 MOE_OP_DEMAND = 1
@@ -37,6 +39,7 @@ MOE_MAX_RING_PER_STEP = 64
 EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
            "moe_experts_forward_noalloc", "moe_ring_plan", "moe_ring_install",
+           "moe_history_save", "moe_history_load", "moe_boot_plan", "moe_history_scale",
            "arena_load_slot", "moe_hot_pick", "moe_replan", "moe_test_mxfp4_probe",
            "moe_test_stream_read", "moe_test_mfma_loop")
 
@@ -120,6 +123,14 @@ def load() -> ctypes.CDLL:
     lib.moe_ring_plan.restype = i
     lib.moe_ring_install.argtypes = [vp, vp, i, i, vp, i, i, vp]
     lib.moe_ring_install.restype = i
+    lib.moe_history_save.argtypes = [ctypes.c_char_p, vp, i, i, ctypes.c_uint64]
+    lib.moe_history_save.restype = i
+    lib.moe_history_load.argtypes = [ctypes.c_char_p, vp, i, i, ctypes.POINTER(ctypes.c_uint64)]
+    lib.moe_history_load.restype = i
+    lib.moe_boot_plan.argtypes = [vp, i, i, i, i, vp]
+    lib.moe_boot_plan.restype = i
+    lib.moe_history_scale.argtypes = [vp, sz, ctypes.c_double, vp]
+    lib.moe_history_scale.restype = i
     lib.moe_test_mxfp4_probe.argtypes = [i, vp, vp, vp, vp, vp, vp]
     lib.moe_test_mxfp4_probe.restype = i
     lib.moe_test_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i, vp]
@@ -284,6 +295,29 @@ def moe_ring_plan(miss_weight, expert_slot, L, E, ring, R, ring_slot0, per_step,
 def moe_ring_install(plan, expert_slot, L, E, ring, R, ring_slot0, stream=None) -> int:
     return int(load().moe_ring_install(_ptr(plan), _ptr(expert_slot), int(L), int(E), _ptr(ring),
                                        int(R), int(ring_slot0), _stream(stream)))
+
+
+def moe_history_save(path: str, hist, L, E, tokens: int = 0) -> int:
+    """Host function: hist is a host float64 [L][E] array."""
+    return int(load_lib().moe_history_save(os.fsencode(path), _host(hist), int(L), int(E),
+                                            ctypes.c_uint64(int(tokens))))
+
+
+def moe_history_load(path: str, hist, L, E, tokens=None) -> int:
+    """Host function: fills the host float64 [L][E] array `hist`; `tokens`, if
+    given, is a ctypes.c_uint64 that receives the stored token count."""
+    return int(load_lib().moe_history_load(os.fsencode(path), _host(hist), int(L), int(E),
+                                            ctypes.byref(tokens) if tokens is not None else None))
+
+
+def moe_boot_plan(hist, L, E, k, n_slots, expert_slot) -> int:
+    """Host function: hist float64 [L][E] in, expert_slot int32 [L][E] out."""
+    return int(load_lib().moe_boot_plan(_host(hist), int(L), int(E), int(k), int(n_slots),
+                                         _host(expert_slot)))
+
+
+def moe_history_scale(hist, n, factor, stream=None) -> int:
+    return int(load().moe_history_scale(_ptr(hist), int(n), float(factor), _stream(stream)))
 
 
 def moe_test_mxfp4_probe(shape, a, a_scale, b, b_scale, d, stream=None) -> int:

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_arena.so")
-SOURCES = ["capi.cpp", "route.hip", "demand.hip", "experts.hip", "plan.hip", "replan.cpp", "probe.hip"]
+SOURCES = ["capi.cpp", "route.hip", "demand.hip", "experts.hip", "plan.hip", "replan.cpp",
+           "history.cpp", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

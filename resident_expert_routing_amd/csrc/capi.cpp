@@ -19,6 +19,8 @@ extern "C" MOE_EXPORT const char* moe_status_string(int status) {
       return "MOE_EUNSUPPORTED: H or I not a multiple of 32, k > min(E, 32), E > 1024 or S > 8192";
     case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace smaller than moe_workspace_bytes()";
     case MOE_EHIP: return "MOE_EHIP: a HIP launch or copy failed";
+    case MOE_EIO: return "MOE_EIO: a history file could not be opened, read, written or renamed";
+    case MOE_EFORMAT: return "MOE_EFORMAT: not a history file of this shape, or a damaged one";
     case MOE_ESCRATCH:
       return "MOE_ESCRATCH: the batch needs more workspace than the library's own scratch "
              "(MOE_NOALLOC_SCRATCH_BYTES) holds";

@@ -5,6 +5,8 @@
 //
 // Deterministic: per chunk of 64 tokens each expert's sum runs over ascending
 // tokens; chunk sums are added in ascending chunk order, in float64.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace moe {
@@ -82,9 +84,26 @@ __global__ __launch_bounds__(1024) void demand_finalize(const double* __restrict
   }
 }
 
+// hist[i] *= factor for every entry (the history's forgetting before a re-plan).
+__global__ __launch_bounds__(256) void history_scale_kernel(double* __restrict__ hist, size_t n,
+                                                           double factor) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    hist[i] *= factor;
+}
+
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" MOE_EXPORT int moe_history_scale(double* hist, size_t n, double factor,
+                                            hipStream_t stream) {
+  if (!hist || !aligned(hist, 8)) return MOE_EINVAL;
+  if (!(factor >= 0.0 && factor <= 1.0)) return MOE_EINVAL;  // also rejects NaN
+  if (n == 0) return MOE_OK;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 1024);
+  history_scale_kernel<<<(unsigned)blocks, 256, 0, stream>>>(hist, n, factor);
+  return hip_status();
+}
 
 size_t moe_demand_ws_bytes_internal(int T, int E) {
   if (T <= kDemandChunk) return 0;

@@ -247,9 +247,11 @@ class SharedArena:
         """Page-locked copy of pair (l, e)'s packed bytes (one per host array)."""
         return _pin_cached(self._pinned, pair_bytes_fn(l, e))
 
-    def replan(self, k: int, n_swap: int, pair_bytes_fn, stream=None):
+    def replan(self, k: int, n_swap: int, pair_bytes_fn, stream=None, gain_only: bool = False):
         """Returns (evict [(l,e)], load [(l,e)]) once the copies are enqueued and
-        the new table is ordered after them on `stream`."""
+        the new table is ordered after them on `stream`.  gain_only: keep only
+        the leading swaps whose loaded pair has a larger history than the pair
+        it evicts (the lists run coldest / hottest first, so gains shrink)."""
         import ctypes
         stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         with torch.cuda.stream(stream):
@@ -261,6 +263,14 @@ class SharedArena:
         B.check(B.moe_replan(hist, self.table_host, self.L, self.E, k, n_swap, ev, ld, new,
                              n_done), "moe_replan")
         n = n_done.value
+        if gain_only:
+            g = 0
+            while g < n and hist[ld[g, 0], ld[g, 1]] > hist[ev[g, 0], ev[g, 1]]:
+                g += 1
+            if g < n:   # the first g swaps of a longer plan are the plan of g swaps
+                B.check(B.moe_replan(hist, self.table_host, self.L, self.E, k, g, ev, ld, new,
+                                     n_done), "moe_replan")
+                n = n_done.value
         if n == 0:
             return [], []
         self.side.wait_stream(stream)       # nothing still reads an evicted slot
@@ -365,3 +375,90 @@ class HotRing:
             self.bytes_copied += a.slot_bytes
         self.copied[b].record(self.side)
         self.n_copies[b] = len(picks)
+
+
+# How much of the history each re-plan keeps (the sensitivity setting: how
+# fast the resident set follows new traffic).
+SENSITIVITY_DECAY = {"low": 1.0, "medium": 0.9, "high": 0.75}
+
+
+def load_history(path: str, L: int, E: int, default: np.ndarray | None = None):
+    """(history [L][E] float64, tokens seen) from a history file; a missing
+    file gives `default` (e.g. a bundled starting history) or zeros.  A damaged
+    file or one of another shape raises."""
+    import ctypes
+    import os
+    hist = np.zeros((L, E), dtype=np.float64)
+    tok = ctypes.c_uint64(0)
+    if not os.path.exists(path):
+        return (np.array(default, dtype=np.float64) if default is not None else hist), 0
+    B.check(B.moe_history_load(path, hist, L, E, tok), f"moe_history_load({path})")
+    return hist, int(tok.value)
+
+
+def boot_table(hist: np.ndarray, k: int, n_slots: int) -> np.ndarray:
+    """The arena filled from a history at boot (moe_boot_plan)."""
+    hist = np.ascontiguousarray(hist, dtype=np.float64)
+    L, E = hist.shape
+    table = np.empty((L, E), dtype=np.int32)
+    B.check(B.moe_boot_plan(hist, L, E, k, n_slots, table), "moe_boot_plan")
+    return table
+
+
+class AdaptiveArena:
+    """The demand-history planner around a SharedArena (TideLM README, "How
+    adaptive expert loading works", item 1: a history that persists across
+    restarts, the arena filled from it at boot, and re-planned after each
+    prompt's prefill, every few hundred generated tokens during long answers,
+    and between requests).
+
+    Each re-plan first scales the device history by the sensitivity's factor
+    (moe_history_scale: older traffic weighs less), then swaps up to
+    `swap_frac` of the arena's slots, keeping only the swaps that gain.
+    The caller reports serving events: on_prefill(), on_tokens(n) with the
+    tokens generated since the last call, on_request_end().
+    """
+
+    def __init__(self, sa: "SharedArena", k: int, pair_bytes_fn, every: int = 200,
+                 sensitivity: str = "medium", swap_frac: float = 0.05, n_arena: int | None = None,
+                 tokens_seen: int = 0):
+        self.sa, self.k, self.pair_bytes = sa, int(k), pair_bytes_fn
+        self.every = int(every)
+        self.factor = SENSITIVITY_DECAY[sensitivity]
+        n_arena = int((sa.table_host >= 0).sum()) if n_arena is None else int(n_arena)
+        self.n_swap = max(1, int(swap_frac * n_arena))
+        self.since = 0
+        self.tokens_seen = int(tokens_seen)
+        self.replans = []           # (reason, evicted, loaded) per re-plan
+
+    def replan(self, reason: str, stream=None):
+        stream = stream if stream is not None else torch.cuda.current_stream(self.sa.device)
+        B.check(B.moe_history_scale(self.sa.hist, self.sa.hist.numel(), self.factor, stream),
+                "moe_history_scale")
+        ev, ld = self.sa.replan(self.k, self.n_swap, self.pair_bytes, stream, gain_only=True)
+        self.replans.append((reason, ev, ld))
+        self.since = 0
+        return ev, ld
+
+    def on_prefill(self, tokens: int, stream=None):
+        self.tokens_seen += int(tokens)
+        return self.replan("prefill", stream)
+
+    def on_tokens(self, n: int, stream=None):
+        self.tokens_seen += int(n)
+        self.since += int(n)
+        if self.since >= self.every:
+            return self.replan("tokens", stream)
+        return None
+
+    def on_request_end(self, stream=None):
+        if self.since > 0:
+            return self.replan("between requests", stream)
+        return None
+
+    def save(self, path: str, stream=None) -> None:
+        stream = stream if stream is not None else torch.cuda.current_stream(self.sa.device)
+        with torch.cuda.stream(stream):
+            hist = np.ascontiguousarray(self.sa.hist.cpu().numpy())
+        B.check(B.moe_history_save(path, hist, self.sa.L, self.sa.E, self.tokens_seen),
+                f"moe_history_save({path})")
