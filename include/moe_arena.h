@@ -78,6 +78,7 @@ extern "C" {
 #define MOE_OP_DEMAND 1
 #define MOE_OP_EXPERTS 2
 #define MOE_OP_HOT_PICK 3
+#define MOE_OP_EXPERTS_SHARED 4  /* moe_experts_forward with a shared expert */
 
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 32
@@ -228,13 +229,24 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  * 2048, or H or I not a multiple of 512) and rounded to bf16 per element by
  * the pipelined kernels before the sum.
  * Only the slots that hold assignments are read.
+ * shared_expert (nullable): one more SwiGLU expert in the slot format (256-byte
+ *          aligned, moe_slot_bytes(H, I) bytes, anywhere in device memory),
+ *          the layer's shared expert (colibri cluster page, shared-expert item:
+ *          it takes every row, unweighted, and its row is added at one fixed
+ *          point).  It runs on every token inside the same gate/up and down
+ *          launches as the routed slots (one more work item), and out[t] =
+ *          (the routed sum above) + y_shared[t], added after the last routed
+ *          pick, in float32, before the one rounding to bf16.  With it, the
+ *          workspace is moe_workspace_bytes(MOE_OP_EXPERTS_SHARED, ...) and
+ *          the call runs even when S == 0.
  *
  * Inputs : xq, slot_offsets, perm, sel_slot, sel_weight as written by moe_route
  *          for the same T, k, S; arena (256-byte aligned), slot_stride (multiple
  *          of 256, >= moe_slot_bytes(H, I)).  Indices out of range are skipped,
  *          never dereferenced.
  * Output : out [T][H] bf16.
- * Workspace: moe_workspace_bytes(MOE_OP_EXPERTS, T, H, 0, k, I, S) bytes.
+ * Workspace: moe_workspace_bytes(MOE_OP_EXPERTS, T, H, 0, k, I, S) bytes
+ *          (MOE_OP_EXPERTS_SHARED with a shared expert).
  * Any copy into a slot the call reads (arena_load_slot) must be ordered before
  * it: by the caller (hipStreamWaitEvent on the load's event), or, for one
  * slot, through defer_slot.
@@ -271,6 +283,7 @@ typedef struct moe_experts_args {
   hipEvent_t* stage_events;
   int defer_slot;
   hipEvent_t defer_event;
+  const uint8_t* shared_expert;
 } moe_experts_args;
 
 int moe_experts_forward(const moe_experts_args* args, hipStream_t stream);

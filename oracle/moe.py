@@ -231,7 +231,7 @@ def combine(y: np.ndarray, sel_weight: np.ndarray, sel_expert: np.ndarray) -> np
 
 
 def experts_forward(x_bits, sel_expert, sel_weight, sel_slot, slot_bytes_fn, H, I,
-                    act: str = "mxfp4", tokens=None, decoded=None):
+                    act: str = "mxfp4", tokens=None, decoded=None, shared_bytes=None):
     """O9-O11.  slot_bytes_fn(s) returns slot s's packed bytes.
 
     tokens: optional subset of token indices to evaluate (sampled parity);
@@ -240,6 +240,10 @@ def experts_forward(x_bits, sel_expert, sel_weight, sel_slot, slot_bytes_fn, H, 
     weights of each packed byte buffer are stored there (with the buffer, so
     its id stays valid) and reused.  Decoding is exact, so results are the
     same with or without it.
+    shared_bytes: optional packed bytes of the layer's shared expert (the
+    colibri cluster page's shared-expert item: it takes every row, unweighted,
+    and its row is added at one fixed point).  Reading: its output is added
+    after the routed picks, with weight 1 -- see shared_combine.
     """
     T, k = sel_expert.shape
     tok = np.arange(T) if tokens is None else np.asarray(tokens)
@@ -262,16 +266,24 @@ def experts_forward(x_bits, sel_expert, sel_weight, sel_slot, slot_bytes_fn, H, 
             cached_key = id(src)
         y[rows, cols] = expert_ffn(xhat[rows], cached, act)
     out = combine(y, np.asarray(sel_weight)[tok], np.asarray(sel_expert)[tok])
+    if shared_bytes is not None:
+        out = shared_combine(out, expert_ffn(xhat, decode_expert(shared_bytes, H, I), act))
     return out, y
 
 
+def shared_combine(routed_out: np.ndarray, y_shared: np.ndarray) -> np.ndarray:
+    """The shared expert's row joins a token's output unweighted, after the
+    routed picks' weighted sum (the one fixed point where it is added)."""
+    return routed_out + y_shared
+
+
 def layer(x_bits, w_router, bias, expert_slot, k, slot_bytes_fn, H, I, act="mxfp4",
-          tokens=None):
-    """The whole layer call: O1-O11."""
+          tokens=None, shared_bytes=None):
+    """The whole layer call: O1-O11 (with the shared expert, if given)."""
     r = route(x_bits, w_router, bias, expert_slot, k)
     r["delta"] = demand_fast(r["topk_expert"], r["topk_score"], r["p"].shape[1])
     out, y = experts_forward(x_bits, r["sel_expert"], r["sel_weight"], r["sel_slot"],
-                             slot_bytes_fn, H, I, act, tokens)
+                             slot_bytes_fn, H, I, act, tokens, shared_bytes=shared_bytes)
     r["out"] = out
     r["y"] = y
     return r

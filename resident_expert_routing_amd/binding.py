@@ -29,6 +29,7 @@ MOE_OP_ROUTE = 0
 MOE_OP_DEMAND = 1
 MOE_OP_EXPERTS = 2
 MOE_OP_HOT_PICK = 3
+MOE_OP_EXPERTS_SHARED = 4
 MOE_MAX_E = 1024
 MOE_MAX_K = 32
 MOE_MAX_S = 8192
@@ -72,7 +73,7 @@ class ExpertsArgs(ctypes.Structure):
                 ("sel_weight", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
                 ("stage_events", ctypes.c_void_p), ("defer_slot", ctypes.c_int),
-                ("defer_event", ctypes.c_void_p)]
+                ("defer_event", ctypes.c_void_p), ("shared_expert", ctypes.c_void_p)]
 
 
 MOE_STAGE_EVENTS = 5
@@ -241,24 +242,25 @@ def moe_demand_accumulate(topk_expert, topk_score, T, k, E, hist_row, delta, ws,
 
 def moe_experts_forward(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm, sel_slot,
                         sel_weight, out, ws, ws_bytes, stream=None, stage_events=None,
-                        defer_slot=-1, defer_event=None) -> int:
+                        defer_slot=-1, defer_event=None, shared_expert=None) -> int:
     keep, evp = _events(stage_events)
     a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
                     int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
                     _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp,
-                    int(defer_slot), _event(defer_event))
+                    int(defer_slot), _event(defer_event), _ptr(shared_expert))
     return int(load().moe_experts_forward(ctypes.byref(a), _stream(stream)))
 
 
 def moe_experts_forward_noalloc(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm,
                                 sel_slot, sel_weight, out, stream=None, stage_events=None,
-                                defer_slot=-1, defer_event=None, ws=None, ws_bytes=0) -> int:
+                                defer_slot=-1, defer_event=None, ws=None, ws_bytes=0,
+                                shared_expert=None) -> int:
     """moe_experts_forward with the library's own scratch (ws must stay None / 0)."""
     keep, evp = _events(stage_events)
     a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
                     int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
                     _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp,
-                    int(defer_slot), _event(defer_event))
+                    int(defer_slot), _event(defer_event), _ptr(shared_expert))
     return int(load().moe_experts_forward_noalloc(ctypes.byref(a), _stream(stream)))
 
 

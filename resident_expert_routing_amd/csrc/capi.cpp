@@ -6,7 +6,7 @@
 
 size_t moe_route_ws_bytes_internal(int T, int H, int E, int S);
 size_t moe_demand_ws_bytes_internal(int T, int E);
-size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S);
+size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S, bool shared);
 size_t moe_hot_pick_ws_bytes_internal(int T);
 
 using namespace moe;
@@ -58,8 +58,9 @@ extern "C" MOE_EXPORT size_t moe_workspace_bytes(int op, int T, int H, int E, in
       if (E <= 0) return bad;
       return moe_demand_ws_bytes_internal(T, E);
     case MOE_OP_EXPERTS:
+    case MOE_OP_EXPERTS_SHARED:
       if (H <= 0 || I <= 0 || k <= 0 || S < 0 || H % 32 != 0 || I % 32 != 0) return bad;
-      return moe_experts_ws_bytes_internal(T, H, k, I, S);
+      return moe_experts_ws_bytes_internal(T, H, k, I, S, op == MOE_OP_EXPERTS_SHARED);
     case MOE_OP_HOT_PICK:
       return moe_hot_pick_ws_bytes_internal(T);
     default:

@@ -413,14 +413,19 @@ struct GateUpArgs {
   int32_t* slots;       // out: (slot, p0, p1) of work item u at 3u (slot -1: none), for down
   uint8_t* hq;
   size_t hrow;
+  const uint8_t* shared;  // the shared expert's slot bytes, or null
   int T, H, I, k, A, S;
+  int maxU;               // work item maxU is the shared expert's (rows A .. A+T, token p - A)
 };
 
 template <bool FULL>
 __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
   const int nbps = p.I / 32;
   const int u = blockIdx.x / nbps, nb = blockIdx.x - u * nbps;
-  const SlotRange sr = work_slot(u, p.used, p.offsets, p.S, p.A);
+  // the shared expert's item: slot id S (never a routed slot), rows A .. A+T
+  const bool sh = p.shared && u == p.maxU;
+  const SlotRange sr = sh ? SlotRange{p.S, p.A, p.A + p.T}
+                          : work_slot(u, p.used, p.offsets, p.S, p.A);
   if (nb == 0 && threadIdx.x == 0) {  // the down kernel takes its work items from here
     p.slots[3 * u] = sr.s;
     p.slots[3 * u + 1] = sr.p0;
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
   const int H = p.H;
   const int nblk = H / 32;
   const int nsc = (nblk + 15) / 16;
-  const uint8_t* base = p.arena + (size_t)s * p.stride;
+  const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)H / 2, srow = (size_t)H / 32;
   const uint8_t* gc0 = base + p.off_gc + (size_t)(n0 + r) * crow;
   const uint8_t* gc1 = gc0 + 16 * crow;
@@ -446,7 +451,7 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
   int pa = -1;  // FULL: this lane's perm entry of the first column block, loaded early
   if (FULL) {
     // Issued before the staging waits, so they are in flight together.
-    if (p0 + r < p1) pa = p.perm[p0 + r];
+    if (!sh && p0 + r < p1) pa = p.perm[p0 + r];
     // gate scales of the wave's 32 rows at LDS row 0.., up scales at row 32..
     extern __shared__ __align__(16) uint8_t wscale[];
     const int sstr = staged_scale_stride(H);
@@ -474,8 +479,12 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
     const int pc = cb + r;
     int t = -1;
     if (pc < p1) {
-      const int a = kFirst ? pa : p.perm[pc];
-      if (a >= 0 && a < p.A) t = a / p.k;
+      if (sh) {
+        t = pc - p.A;  // the shared expert takes every token, in order
+      } else {
+        const int a = kFirst ? pa : p.perm[pc];
+        if (a >= 0 && a < p.A) t = a / p.k;
+      }
     }
     const uint8_t* xc = t >= 0 ? p.xq + (size_t)t * p.xrow : nullptr;
     v4f ag0 = {0.f, 0.f, 0.f, 0.f}, ag1 = ag0, au0 = ag0, au1 = ag0;
@@ -521,6 +530,7 @@ struct DownArgs {
   const int32_t* perm;
   const int32_t* slots;  // (slot, p0, p1) of work item u at 3u, written by the gate/up kernel
   float* y;
+  const uint8_t* shared;  // the shared expert's slot bytes (slot id S), or null
   int H, I, A, S;
 };
 
@@ -534,13 +544,14 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
                         __builtin_amdgcn_readfirstlane(p.slots[3 * u + 2])};
   if (sr.s < 0) return;
   const int s = sr.s, p0 = sr.p0, p1 = sr.p1;
+  const bool sh = s == p.S;  // the shared expert: y row = its hq row (A + token)
   const int lane = threadIdx.x;
   const int n0 = nb * 64;
   const int r = lane & 15, g = lane >> 4;
   const int I = p.I;
   const int nblk = I / 32;
   const int nsc = (nblk + 15) / 16;
-  const uint8_t* base = p.arena + (size_t)s * p.stride;
+  const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)I / 2, srow = (size_t)I / 32;
   extern __shared__ __align__(16) uint8_t wscale[];  // FULL: the wave's scale rows
   const int sstr = staged_scale_stride(I);
@@ -616,8 +627,8 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
     const int c = lane & 15;
     const int pcol = cb + c;
     if (pcol < p1) {
-      const int a = p.perm[pcol];
-      if (a >= 0 && a < p.A) {
+      const int a = sh ? pcol : p.perm[pcol];
+      if (a >= 0 && (sh || a < p.A)) {
         float* yr = p.y + (size_t)a * p.H;
 #pragma unroll
         for (int tl = 0; tl < 4; ++tl) {
@@ -670,11 +681,14 @@ struct YRow<uint16_t> {  // pipelined kernels: bf16 rows, 8 elements (16 bytes) 
 };
 
 // One thread per YRow<YT>::kEl consecutive elements of a token's output row.
+// ysh: the shared expert's rows (row t for token t), added unweighted after
+// the routed picks, or null.
 template <typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ sel_slot, int T,
                                                       int H, int k, int S,
+                                                      const YT* __restrict__ ysh,
                                                       uint16_t* __restrict__ out) {
   constexpr int kB = 8;  // picks whose rows are loaded together
   constexpr int kEl = YRow<YT>::kEl;
@@ -711,6 +725,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
         for (int e = 0; e < kEl; ++e) acc[e] = fmaf(wj[i], v[i][e], acc[e]);
       }
     }
+  }
+  if (ysh) {
+    float v[kEl];
+    YRow<YT>::load(ysh, (size_t)t * H + h, v);
+#pragma unroll
+    for (int e = 0; e < kEl; ++e) acc[e] += v[e];
   }
   uint16_t* o = out + (size_t)t * H + h;  // 8-byte aligned: four elements per store
 #pragma unroll
@@ -760,14 +780,15 @@ constexpr int kLoadsPerStage = 6;
 
 // Work list of M-tiles of tm rows: items[0] = count, then per item (slot,
 // first row of the tile within the slot, index of the slot's first item, the
-// slot's item count), slots ascending.  Also clears the zero page, and
-// writes the first item and the item count of slot defer_slot (0 and 0 when
-// it holds no assignment) to defer_info[0..1] when defer_slot >= 0.
+// slot's item count), slots ascending; with a shared expert (Tsh = T rows),
+// its tiles follow as slot S.  Also clears the zero page, and writes the
+// first item and the item count of slot defer_slot (0 and 0 when it holds no
+// assignment) to defer_info[0..1] when defer_slot >= 0.
 __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ offsets, int S,
                                                     int A, int tm, int32_t* __restrict__ items,
                                                     uint32_t* __restrict__ zero_page,
                                                     int defer_slot,
-                                                    int32_t* __restrict__ defer_info) {
+                                                    int32_t* __restrict__ defer_info, int Tsh) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid < kZeroPage / 4) zero_page[tid] = 0u;
@@ -810,7 +831,15 @@ __global__ __launch_bounds__(1024) void build_tiles(const int32_t* __restrict__ 
   if (tid == 0) {
     int total = 0;
     for (int i = 0; i < 16; ++i) total += wsum[i];
-    items[0] = total;
+    const int nsh = (Tsh + tm - 1) / tm;  // the shared expert's tiles, last
+    for (int m = 0; m < nsh; ++m) {
+      int32_t* it = items + 1 + 4 * (total + m);
+      it[0] = S;
+      it[1] = m * tm;
+      it[2] = total;
+      it[3] = nsh;
+    }
+    items[0] = total + nsh;
   }
 }
 
@@ -837,8 +866,10 @@ struct TileRef {
   int slot, p0, rows, nt;
 };
 
+// Slot S is the shared expert: rows A + m*tm.. of the A + Tsh rows.
 __device__ __forceinline__ bool tile_of(int w, int nN, int tm, const int32_t* __restrict__ items,
-                                        const int32_t* __restrict__ offsets, TileRef& t) {
+                                        const int32_t* __restrict__ offsets, int S, int A,
+                                        int Tsh, TileRef& t) {
   if (w < 0) return false;
   const int item = w / nN;
   if (item >= items[0]) return false;
@@ -851,8 +882,13 @@ __device__ __forceinline__ bool tile_of(int w, int nN, int tm, const int32_t* __
   const int m = 8 * mg + lg % gm;
   t.slot = it[0];
   t.nt = lg / gm;
-  t.p0 = offsets[t.slot] + m * tm;
-  t.rows = min(tm, offsets[t.slot + 1] - t.p0);
+  if (t.slot == S) {
+    t.p0 = A + m * tm;
+    t.rows = min(tm, A + Tsh - t.p0);
+  } else {
+    t.p0 = offsets[t.slot] + m * tm;
+    t.rows = min(tm, offsets[t.slot + 1] - t.p0);
+  }
   return true;
 }
 
@@ -1058,6 +1094,8 @@ struct PipeArgs {
   int H, I, k, A, nN;
   int skip_slot;        // gate/up: tiles of this slot are left out (-1: none)
   const int32_t* only;  // gate/up: null, or (first item, item count) of the one slot to run
+  const uint8_t* shared;  // the shared expert's slot bytes (its tiles are slot S), or null
+  int S, T;
 };
 
 // Gate/up: N-tile = 128 rows of I; wave w: rows n0 = 32w.. of gate (tile 0)
@@ -1073,15 +1111,18 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
     w = xcd_work_index(p.items[0] * p.nN);
   }
   // no barrier yet: a workgroup without a tile (or with the left-out slot's) leaves whole
-  if (!tile_of(w, p.nN, kTileM, p.items, p.offsets, tr) || tr.slot == p.skip_slot) return;
+  if (!tile_of(w, p.nN, kTileM, p.items, p.offsets, p.S, p.A, p.shared ? p.T : 0, tr) ||
+      tr.slot == p.skip_slot)
+    return;
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
+  const bool sh = s == p.S;  // the shared expert: row p is token p - A
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int H = p.H;
   const int n0 = tr.nt * 128 + wave * 32;
   const bool active = n0 < p.I;
   const int nb = active ? n0 : 0;  // an idle wave still loads (row 0) and meets every barrier
-  const uint8_t* base = p.arena + (size_t)s * p.stride;
+  const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
   const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c1};
   const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s1};
   const int wrow[2] = {nb, nb};
@@ -1091,6 +1132,7 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
       src,
       [&](int row) -> const uint8_t* {
         if (row >= rows) return nullptr;
+        if (sh) return p.act + (size_t)(p0 + row - p.A) * p.arow;
         const int a = p.perm[p0 + row];
         return (a >= 0 && a < p.A) ? p.act + (size_t)(a / p.k) * p.arow : nullptr;
       },
@@ -1113,13 +1155,16 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
 __global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
-  if (!tile_of(xcd_work_index(p.items[0] * p.nN), p.nN, kTileM, p.items, p.offsets, tr)) return;
+  if (!tile_of(xcd_work_index(p.items[0] * p.nN), p.nN, kTileM, p.items, p.offsets, p.S, p.A,
+               p.shared ? p.T : 0, tr))
+    return;
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
+  const bool sh = s == p.S;  // the shared expert: y row = its hq row (A + token)
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int I = p.I;
   const int n0 = tr.nt * 256 + wave * 64;
-  const uint8_t* base = p.arena + (size_t)s * p.stride;
+  const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
   const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c0};
   const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s0};
   bool tv[2];
@@ -1143,8 +1188,8 @@ __global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
   for (int cb = 0; cb < 4; ++cb) {
     const int lr = 32 * cb + r;
     if (lr < rows) {
-      const int a = p.perm[p0 + lr];
-      if (a >= 0 && a < p.A) {
+      const int a = sh ? p0 + lr : p.perm[p0 + lr];
+      if (a >= 0 && (sh || a < p.A)) {
         uint16_t* yr = p.y + (size_t)a * p.H;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -1183,27 +1228,35 @@ static size_t max_tiles(size_t A, int S, int tm) {
   return (A < (size_t)S ? A : (size_t)S) + (A + tm - 1) / tm;
 }
 
-static ExpertsWs experts_ws(int T, int H, int k, int I, int S) {
+// M-tiles of the shared expert's T rows (0 without one).
+static size_t shared_tiles(int T, bool shared) {
+  return shared ? (size_t)(T + kTileM - 1) / kTileM : 0;
+}
+
+static ExpertsWs experts_ws(int T, int H, int k, int I, int S, bool shared) {
   ExpertsWs w;
   const size_t A = (size_t)T * k;
+  const size_t rows = A + (shared ? (size_t)T : 0);  // hq and y: routed rows, then shared ones
   const Family fam = family_of(T, k, H, I);
   const bool tiled = fam != kFamSmall;
   w.used_off = 0;
   w.items_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
   // pipelined: the M-tile list, then the deferred slot's (first item, item
   // count); small batches: (slot, p0, p1) per work item
-  const size_t items = tiled ? (1 + 4 * max_tiles(A, S, kTileM) + 2) * sizeof(int32_t)
-                             : 3 * (A < (size_t)S ? A : (size_t)S) * sizeof(int32_t);
+  const size_t ntile = max_tiles(A, S, kTileM) + shared_tiles(T, shared);
+  const size_t nwork = (A < (size_t)S ? A : (size_t)S) + (shared ? 1 : 0);
+  const size_t items = tiled ? (1 + 4 * ntile + 2) * sizeof(int32_t)
+                             : 3 * nwork * sizeof(int32_t);
   w.zero_off = up_to(w.items_off + items, 256);
   w.hq_off = w.zero_off + (tiled ? kZeroPage : 0);
-  w.y_off = up_to(w.hq_off + A * mxfp4_row_bytes(I), 256);
-  w.total = up_to(w.y_off + A * (size_t)H * sizeof(float), 256);
+  w.y_off = up_to(w.hq_off + rows * mxfp4_row_bytes(I), 256);
+  w.total = up_to(w.y_off + rows * (size_t)H * sizeof(float), 256);
   return w;
 }
 
-size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S) {
+size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S, bool shared) {
   if (T <= 0) return 0;
-  return experts_ws(T, H, k, I, S).total;
+  return experts_ws(T, H, k, I, S, shared).total;
 }
 
 // Shape checks shared by both entry points (no HIP call).
@@ -1229,13 +1282,15 @@ static int experts_validate(const moe_experts_args* a, const void* ws, size_t ws
   const SlotLayout L = slot_layout(H, I);
   if (a->slot_stride < L.total || a->slot_stride % 256 != 0) return MOE_EINVAL;
   if (!aligned(a->xq, 16) || !aligned(a->arena, 256) || !aligned(a->out, 8)) return MOE_EINVAL;
-  const ExpertsWs W = experts_ws(T, H, k, I, S);
+  const bool shared = a->shared_expert != nullptr;
+  if (!aligned(a->shared_expert, 256)) return MOE_EINVAL;
+  const ExpertsWs W = experts_ws(T, H, k, I, S, shared);
   if (ws_bytes < W.total) return MOE_EWORKSPACE;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   const int defer = a->defer_slot;
   if (defer < -1 || defer >= S || (defer >= 0 && !a->defer_event)) return MOE_EINVAL;
   if (family_of(T, k, H, I) != kFamSmall) {
-    const size_t ntile = max_tiles((size_t)T * k, S, kTileM);
+    const size_t ntile = max_tiles((size_t)T * k, S, kTileM) + shared_tiles(T, shared);
     if (up_to(ntile * (size_t)((I + 127) / 128), 8) > 0x7FFFFFFFu ||
         up_to(ntile * (size_t)((H + 255) / 256), 8) > 0x7FFFFFFFu)
       return MOE_EUNSUPPORTED;
@@ -1248,21 +1303,22 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
   const int T = a->T, H = a->H, I = a->I, k = a->k, S = a->S;
   if (T == 0) return MOE_OK;
   const SlotLayout L = slot_layout(H, I);
-  const ExpertsWs W = experts_ws(T, H, k, I, S);
+  const bool shared = a->shared_expert != nullptr;
+  const ExpertsWs W = experts_ws(T, H, k, I, S, shared);
   const int defer = a->defer_slot;
   const int A = T * k;
   const Family fam = family_of(T, k, H, I);
-  const size_t ntile = max_tiles((size_t)A, S, kTileM);
+  const size_t ntile = max_tiles((size_t)A, S, kTileM) + shared_tiles(T, shared);
   // N-tiles: gate/up 128 rows of I, down 256 rows of H
   const int nN1 = (I + 127) / 128;
   const int nN2 = (H + 255) / 256;
   const size_t g1 = up_to(ntile * (size_t)nN1, 8);
   const size_t g2 = up_to(ntile * (size_t)nN2, 8);
-  if (S == 0) {
+  if (S == 0 && !shared) {
     // nothing routable: every pick is padding, the output is zero
     dim3 grid(T, (H + 256 * YRow<float>::kEl - 1) / (256 * YRow<float>::kEl));
     combine_kernel<float><<<grid, 256, 0, stream>>>(nullptr, a->sel_weight, a->sel_slot, T, H,
-                                                    k, S, a->out);
+                                                    k, S, nullptr, a->out);
     return hip_status();
   }
   uint8_t* ws = static_cast<uint8_t*>(ws_ptr);
@@ -1276,7 +1332,8 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     uint8_t* zero = ws + W.zero_off;
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
     build_tiles<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, kTileM, items,
-                                        reinterpret_cast<uint32_t*>(zero), defer, defer_info);
+                                        reinterpret_cast<uint32_t*>(zero), defer, defer_info,
+                                        shared ? T : 0);
     PipeArgs t;
     t.act = a->xq;
     t.arow = mxfp4_row_bytes(H);
@@ -1300,6 +1357,9 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     t.nN = nN1;
     t.skip_slot = defer;
     t.only = nullptr;
+    t.shared = a->shared_expert;
+    t.S = S;
+    t.T = T;
     hipExtLaunchKernelGGL(gateup_pipe, dim3((unsigned)g1), dim3(256), 0, stream,
                           ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, 0, t);
     if (defer >= 0) {
@@ -1353,7 +1413,10 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     g.k = k;
     g.A = A;
     g.S = S;
-    const int gblocks = maxU * (I / 32);
+    g.shared = a->shared_expert;
+    g.maxU = maxU;
+    const int nwork = maxU + (shared ? 1 : 0);  // the shared expert's item last
+    const int gblocks = nwork * (I / 32);
     hipEvent_t gu0 = ev ? ev[1] : nullptr, gu1 = ev ? ev[2] : nullptr;
     if (staged_ok(H))
       hipExtLaunchKernelGGL(gateup_kernel<true>, dim3(gblocks), dim3(kWave),
@@ -1376,22 +1439,26 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     d.I = I;
     d.A = A;
     d.S = S;
-    const int dblocks = maxU * ((H + 63) / 64);
+    d.shared = a->shared_expert;
+    const int dblocks = nwork * ((H + 63) / 64);
     if (staged_ok(I))
       down_kernel<true><<<dblocks, kWave, 64 * staged_scale_stride(I), stream>>>(d);
     else
       down_kernel<false><<<dblocks, kWave, 0, stream>>>(d);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   }
-  // a workgroup covers 256 threads x YRow<YT>::kEl elements of a token's row
+  // a workgroup covers 256 threads x YRow<YT>::kEl elements of a token's row; the
+  // shared expert's rows follow the A routed ones
   if (fam != kFamSmall) {
     const int per = 256 * YRow<uint16_t>::kEl;
+    const uint16_t* yb = reinterpret_cast<const uint16_t*>(y);
     combine_kernel<uint16_t><<<dim3(T, (H + per - 1) / per), 256, 0, stream>>>(
-        reinterpret_cast<const uint16_t*>(y), a->sel_weight, a->sel_slot, T, H, k, S, a->out);
+        yb, a->sel_weight, a->sel_slot, T, H, k, S, shared ? yb + (size_t)A * H : nullptr,
+        a->out);
   } else {
     const int per = 256 * YRow<float>::kEl;
     combine_kernel<float><<<dim3(T, (H + per - 1) / per), 256, 0, stream>>>(
-        y, a->sel_weight, a->sel_slot, T, H, k, S, a->out);
+        y, a->sel_weight, a->sel_slot, T, H, k, S, shared ? y + (size_t)A * H : nullptr, a->out);
   }
   if (!record_stage(ev, 4, stream)) return MOE_EHIP;
   return hip_status();
@@ -1438,7 +1505,7 @@ extern "C" MOE_EXPORT int moe_experts_forward_noalloc(const moe_experts_args* a,
   if (r != MOE_OK) return r;
   if (a->ws || a->ws_bytes) return MOE_EINVAL;  // the workspace is the library's own
   if (a->T == 0) return MOE_OK;
-  const size_t need = experts_ws(a->T, a->H, a->k, a->I, a->S).total;
+  const size_t need = experts_ws(a->T, a->H, a->k, a->I, a->S, a->shared_expert != nullptr).total;
   if (need > kNoAllocScratch) return MOE_ESCRATCH;
   // every other check, against a stand-in for the scratch (256-aligned, not read)
   r = experts_validate(a, reinterpret_cast<const void*>(uintptr_t{256}), kNoAllocScratch);

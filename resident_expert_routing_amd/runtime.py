@@ -40,6 +40,7 @@ class LayerBuffers:
     I: int
     S: int
     device: torch.device
+    shared: bool = False    # workspace for a shared expert too
 
     def __post_init__(self):
         T, H, E, k, I, S, dev = self.T, self.H, self.E, self.k, self.I, self.S, self.device
@@ -58,7 +59,8 @@ class LayerBuffers:
         self.delta = torch.empty(E, **f32)
         self.ws_route_bytes = B.moe_workspace_bytes(B.MOE_OP_ROUTE, T, H, E, k, I, S)
         self.ws_demand_bytes = B.moe_workspace_bytes(B.MOE_OP_DEMAND, T, H, E, k, I, S)
-        self.ws_experts_bytes = B.moe_workspace_bytes(B.MOE_OP_EXPERTS, T, H, E, k, I, S)
+        self.ws_experts_bytes = B.moe_workspace_bytes(
+            B.MOE_OP_EXPERTS_SHARED if self.shared else B.MOE_OP_EXPERTS, T, H, E, k, I, S)
         self.ws_route = _ws(self.ws_route_bytes, dev)
         self.ws_demand = _ws(self.ws_demand_bytes, dev)
         self.ws_experts = _ws(self.ws_experts_bytes, dev)
@@ -115,11 +117,15 @@ def demand(buf: LayerBuffers, hist_row, stream=None, delta=True) -> None:
 
 
 def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None,
-            stage_events=None, defer_slot: int = -1, defer_event=None) -> None:
+            stage_events=None, defer_slot: int = -1, defer_event=None,
+            shared_expert=None) -> None:
+    """moe_experts_forward; shared_expert: a device tensor holding the layer's
+    shared expert in the slot format (buf must be made with shared=True)."""
     B.check(B.moe_experts_forward(buf.T, buf.H, buf.I, buf.k, buf.S, buf.xq, arena_ptr,
                                   slot_stride, buf.slot_offsets, buf.perm, buf.sel_slot,
                                   buf.sel_weight, buf.out, buf.ws_experts, buf.ws_experts_bytes,
-                                  stream, stage_events, defer_slot, defer_event),
+                                  stream, stage_events, defer_slot, defer_event,
+                                  shared_expert),
             "moe_experts_forward")
 
 

@@ -28,9 +28,14 @@ def test_boot_fill_hand_worked():
     hist = np.array([[4.0, 0.0, 2.0, 2.0], [1.0, 3.0, 0.0, 3.0]])
     t = plan.boot_fill(hist, 5, 1)
     assert t.tolist() == [[0, -1, 1, 2], [-1, 3, -1, 4]]
-    # the floor wins over a hotter pair of another layer: k = 2, four slots
+    # k = 2, four slots: each layer's two hottest, in (layer, expert) order
     t = plan.boot_fill(hist, 4, 2)
     assert t.tolist() == [[0, -1, 1, -1], [-1, 2, -1, 3]]
+    # the floor wins over hotter pairs of another layer: layer 0 [9, 8, 7, 6] is
+    # hotter everywhere than layer 1 [1, 0, 0, 0], yet layer 1 keeps experts 0
+    # and 1 (ties at 0 go to the lower id)
+    t = plan.boot_fill(np.array([[9.0, 8.0, 7.0, 6.0], [1.0, 0.0, 0.0, 0.0]]), 4, 2)
+    assert t.tolist() == [[0, 1, -1, -1], [2, 3, -1, -1]]
     # more slots than pairs: everything resident
     assert (plan.boot_fill(hist, 100, 1) >= 0).all()
     with pytest.raises(ValueError):

@@ -109,3 +109,34 @@ def test_decode_expert_sections():
     for got, src in ((g, wg), (u, wu), (d, wd)):
         assert np.array_equal(got, mxfp4.quantise(src.astype(np.float64)))
         assert np.abs(got - src).max() <= np.abs(src).max() / 2   # coarse but tight enough
+
+
+def test_shared_expert_closed_forms():
+    """Shared expert (colibri cluster page, shared-expert item: every row,
+    unweighted, added at one fixed point):
+    - every routed expert and the shared one identical -> out = 2 FFN(x^)
+      for any routing and mask (the routed weights sum to 1);
+    - a shared expert whose weights are all zero adds exactly nothing;
+    - no routable expert at all -> out = the shared expert's FFN alone."""
+    H, I, E, k = 64, 32, 12, 4
+    buf = fixtures.pack_expert(*_weights(H, I, 81))
+    W = moe.decode_expert(buf, H, I)
+    zero = fixtures.pack_expert(*[np.zeros_like(w) for w in _weights(H, I, 1)])
+    for seed, nr in ((4, 12), (5, 6)):
+        lay = fixtures.tiny_layer(T=9, H=H, E=E, k=k, I=I, n_routable=nr, seed=seed,
+                                  bias_scale=1.0)
+        xhat = moe.quantise_rows(moe.bf16_to_f64(lay.x_bits))
+        r = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k, lambda s: buf, H, I,
+                      shared_bytes=buf)
+        assert np.allclose(r["out"], 2 * moe.expert_ffn(xhat, W), rtol=1e-12, atol=1e-15)
+        other = fixtures.pack_expert(*_weights(H, I, 82 + seed))
+        plain = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k,
+                          lambda s: other, H, I)
+        with0 = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k,
+                          lambda s: other, H, I, shared_bytes=zero)
+        assert np.array_equal(plain["out"], with0["out"])
+    lay = fixtures.tiny_layer(T=5, H=H, E=E, k=k, I=I, n_routable=0, seed=6)
+    r = moe.layer(lay.x_bits, lay.w_router, lay.bias, lay.expert_slot, k, lambda s: buf, H, I,
+                  shared_bytes=buf)
+    xhat = moe.quantise_rows(moe.bf16_to_f64(lay.x_bits))
+    assert np.allclose(r["out"], moe.expert_ffn(xhat, W), rtol=1e-12, atol=1e-15)

@@ -103,3 +103,29 @@ def test_combine_drops_last_pick(monkeypatch):
     orig = moe.combine
     monkeypatch.setattr(moe, "combine", lambda y, w, se: orig(y[:, :-1], w[:, :-1], se[:, :-1]))
     _fails(tf.check_identical_experts)
+
+
+def test_shared_expert_weighted_or_dropped(monkeypatch):
+    monkeypatch.setattr(moe, "shared_combine", lambda out, ys: out + 0.5 * ys)
+    _fails(tf.test_shared_expert_closed_forms)
+    monkeypatch.setattr(moe, "shared_combine", lambda out, ys: out)
+    _fails(tf.test_shared_expert_closed_forms)
+
+
+def test_ring_plan_ignores_pending(monkeypatch):
+    """A ring plan that forgets the pairs already in flight picks one twice."""
+    import test_oracle_plan as tp
+    from oracle import plan
+    orig = plan.ring_plan
+    monkeypatch.setattr(plan, "ring_plan",
+                        lambda w, t, ring, head, per, s0: orig(w, t, [-1] * len(ring), head,
+                                                               per, s0))
+    _fails(tp.test_ring_pending_pairs_not_planned_twice_and_stale_install_skipped)
+
+
+def test_boot_fill_without_floor(monkeypatch):
+    import test_history_host as th
+    from oracle import plan
+    orig = plan.boot_fill
+    monkeypatch.setattr(plan, "boot_fill", lambda h, n, k: orig(h, n, 0))
+    _fails(th.test_boot_fill_hand_worked)
