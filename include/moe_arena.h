@@ -120,6 +120,21 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *             larger batches it is the chain over h in steps of 4 of the
  *             float64 matrix instruction; then the bias.  Within each regime a
  *             token's z does not depend on the rest of the batch.
+ *             Larger batches with H a multiple of 512 (H <= 8192) first compute every z on
+ *             the bf16 matrix instruction (w split exactly into three bf16
+ *             parts, float32 sums per 128-wide slice of h, float64 across
+ *             slices) with a bound on its error, 34 * 8.13 * 2^-24 *
+ *             ||x_t|| * max_e ||w_e|| (a model of the instruction's rounding:
+ *             at most twice the error of 16 round-to-nearest additions);
+ *             every token whose k-th and (k+1)-th logits -- over all experts
+ *             or over the routable ones -- are within twice that bound is
+ *             selected again after the experts that can still be picked (those
+ *             not below its k-th value by more than twice the bound, in either
+ *             order) get float64 logits (a fused multiply-add chain per lane
+ *             over H/64 consecutive h, then a fixed-order wave sum); every
+ *             other expert is provably out of its top-k.  So the picks are
+ *             those of float64 logits.  Probabilities of the other
+ *             tokens come from the bounded logits (typically ~1e-6 relative).
  *   p[t,:]  = softmax over all E experts of z[t,:] (float64).
  *   topk    = the k experts with the largest z (ties to the lower id), listed in
  *             ascending id, with score p[t,e]: the picks demand is recorded over.
@@ -167,7 +182,10 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *          without the flag.  For a hot read: route again over a changed
  *          routable set without recomputing the products.  On every return
  *          with T > 0 the first T*E*8 bytes of ws hold them (float64 [T][E],
- *          x . w_router before the bias).
+ *          x . w_router before the bias; for larger batches, the bounded
+ *          bf16-instruction values except for the tokens recomputed exactly).
+ *          With reuse_logits the selection certifies the stored values again
+ *          against the new routable set.
  */
 #define MOE_STAGE_EVENTS 5
 

@@ -53,24 +53,18 @@ __device__ void quantize_x_elements(const uint16_t* __restrict__ x, int T, int H
 // rows instead (one element per thread), alongside the dot products.
 // Workgroup 0 also zeroes `counter` (nullable) for the selection kernel that
 // follows.
+typedef double v4d __attribute__((ext_vector_type(4)));
 constexpr int RS_T = 8;
 constexpr int RS_MAX_CHUNKS = 256;
 constexpr int RS_RUN = 16;
-__global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restrict__ x,
-                                                        const float* __restrict__ w, int T, int H,
-                                                        int E, double* __restrict__ z,
-                                                        uint8_t* __restrict__ xq, size_t xq_row,
-                                                        int nrb, uint32_t* __restrict__ counter) {
-  if (counter && blockIdx.x == 0 && threadIdx.x == 0) *counter = 0u;
-  if ((int)blockIdx.x >= nrb) {
-    quantize_x_elements(x, T, H, xq, xq_row, (size_t)(blockIdx.x - nrb) * 256 + threadIdx.x,
-                        (size_t)(gridDim.x - nrb) * 256);
-    return;
-  }
+// z[tok[i], e] for the nt (<= RS_T) tokens tok[0..nt) and one expert, by the
+// whole workgroup (thread c owns chunk c).
+__device__ __forceinline__ void small_dot_block(const uint16_t* __restrict__ x,
+                                                const float* __restrict__ w, int H, int E,
+                                                double* __restrict__ z, int e, const int* tok,
+                                                int nt) {
   __shared__ double part[RS_T][RS_MAX_CHUNKS + 1];
-  const int ntg = (T + RS_T - 1) / RS_T;
-  const int e = blockIdx.x / ntg, t0 = (blockIdx.x % ntg) * RS_T;
-  const int nt = min(RS_T, T - t0);
+  __shared__ double runs[RS_T][RS_MAX_CHUNKS / RS_RUN];
   const int nchunk = H / kRouterChunk;  // H % 32 == 0
   const int c = threadIdx.x;
   if (c < nchunk) {
@@ -85,8 +79,7 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
     uint4 xv_all[RS_T][kRouterChunk / 8];
 #pragma unroll
     for (int i = 0; i < RS_T; ++i) {
-      const uint4* x4 =
-          reinterpret_cast<const uint4*>(x + (size_t)(t0 + min(i, nt - 1)) * H + h0);
+      const uint4* x4 = reinterpret_cast<const uint4*>(x + (size_t)tok[min(i, nt - 1)] * H + h0);
 #pragma unroll
       for (int q = 0; q < kRouterChunk / 8; ++q) xv_all[i][q] = x4[q];
     }
@@ -112,7 +105,6 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
   }
   __syncthreads();
   // thread (token i, run q) adds the chunk sums of run q
-  __shared__ double runs[RS_T][RS_MAX_CHUNKS / RS_RUN];
   const int nrun = (nchunk + RS_RUN - 1) / RS_RUN;
   {
     const int i = c / nrun, q = c % nrun;
@@ -127,7 +119,84 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
   if (c < nt) {
     double acc = 0.0;
     for (int q = 0; q < nrun; ++q) acc += runs[c][q];
-    z[(size_t)(t0 + c) * E + e] = acc;
+    z[(size_t)tok[c] * E + e] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restrict__ x,
+                                                        const float* __restrict__ w, int T, int H,
+                                                        int E, double* __restrict__ z,
+                                                        uint8_t* __restrict__ xq, size_t xq_row,
+                                                        int nrb, uint32_t* __restrict__ counter) {
+  if (counter && blockIdx.x == 0 && threadIdx.x == 0) *counter = 0u;
+  if ((int)blockIdx.x >= nrb) {
+    quantize_x_elements(x, T, H, xq, xq_row, (size_t)(blockIdx.x - nrb) * 256 + threadIdx.x,
+                        (size_t)(gridDim.x - nrb) * 256);
+    return;
+  }
+  const int ntg = (T + RS_T - 1) / RS_T;
+  const int e = blockIdx.x / ntg, t0 = (blockIdx.x % ntg) * RS_T;
+  const int nt = min(RS_T, T - t0);
+  int tok[RS_T];
+#pragma unroll
+  for (int i = 0; i < RS_T; ++i) tok[i] = t0 + i;
+  small_dot_block(x, w, H, E, z, e, tok, nt);
+}
+
+// Float64 logits where a flagged token's picks can still change.  With every
+// stored z~ within `bound` of its exact value, an expert whose z~ (bias
+// included) is below the k-th stored value minus twice the bound has at least
+// k experts certainly above it, so it is out of the top-k; only the experts at
+// or above that line (in the order over all experts, and over the routable
+// ones) can be picked.  Those get the float64 logit, every other entry keeps
+// its z~, and the token is selected again: the picks are the float64 logits'.
+// One workgroup per listed token (a fixed grid walks the list), its four waves
+// taking the candidates in turn; lane l sums h in [l H/64, (l+1) H/64) as a
+// fused multiply-add chain, then the wave adds the lanes' sums in the fixed
+// DPP order.
+__global__ __launch_bounds__(256) void router_f64_candidates(
+    const uint16_t* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    const int32_t* __restrict__ expert_slot, int H, int E, int S, double* __restrict__ z,
+    const int32_t* __restrict__ tlist, const double* __restrict__ cert) {
+  const int n = tlist[0];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per = H / 64;  // H % 512 == 0
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {  // uniform
+    const int t = tlist[1 + i];
+    const double ku = cert[3 * (size_t)t], km = cert[3 * (size_t)t + 1];
+    const double line = 2.0 * cert[3 * (size_t)t + 2];
+    const uint16_t* xr = x + (size_t)t * H + (size_t)lane * per;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      bool cand = false;
+      if (e < E) {
+        const double v = z[(size_t)t * E + e] + (bias ? (double)bias[e] : 0.0);
+        const int sl = expert_slot[e];
+        cand = v >= ku - line || (sl >= 0 && sl < S && v >= km - line);
+      }
+      uint64_t m = __ballot(cand);
+      for (int j = 0; m; ++j) {  // uniform; wave j % 4 takes the j-th candidate
+        const int c = e0 + __builtin_ctzll(m);
+        m &= m - 1;
+        if ((j & 3) != wave) continue;
+        const float* wr = w + (size_t)c * H + (size_t)lane * per;
+        double acc = 0.0;
+        for (int h = 0; h < per; h += 8) {  // per = H/64, a multiple of 8
+          const uint4 xv = *reinterpret_cast<const uint4*>(xr + h);
+          const float4 wa = *reinterpret_cast<const float4*>(wr + h);
+          const float4 wb = *reinterpret_cast<const float4*>(wr + h + 4);
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+          const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const uint32_t bits = (j & 1) ? (xw[j >> 1] >> 16) : (xw[j >> 1] & 0xFFFFu);
+            acc = fma((double)bf16_to_f32(bits), (double)ww[j], acc);
+          }
+        }
+        const double sum = wave_sum(acc);
+        if (lane == 0) z[(size_t)t * E + c] = sum;
+      }
+    }
   }
 }
 
@@ -143,24 +212,35 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
 // in LDS as float32 (exact for bf16 and fp32), k-major (the weight rows with a
 // 16-float pad) so a fragment read hits 64 distinct banks, and double-buffered
 // through registers.
-typedef double v4d __attribute__((ext_vector_type(4)));
 constexpr int RM_T = 16, RM_E = 64, RM_K = 32;
 constexpr int RM_XS = RM_T, RM_WS = RM_E + 16;
 
+// tlist (nullable): the tokens to compute, tlist[0] = n then n token ids
+// ascending; tile row i is then token tlist[1 + t0 + i] (workgroups past n
+// leave at once).  Without it, tile row i is token t0 + i.
 __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restrict__ x,
                                                        const float* __restrict__ w, int T, int H,
-                                                       int E, double* __restrict__ z) {
+                                                       int E, double* __restrict__ z,
+                                                       const int32_t* __restrict__ tlist) {
   __shared__ float xs[2][RM_K][RM_XS];
   __shared__ float ws[2][RM_K][RM_WS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int t0 = blockIdx.y * RM_T, e0 = blockIdx.x * RM_E;
+  const int nt = tlist ? tlist[0] : T;  // rows of this call
+  if (t0 >= nt) return;                  // uniform: before any barrier
+  // token of tile row i (i < RM_T), or -1
+  auto token_of = [&](int i) -> int {
+    if (t0 + i >= nt) return -1;
+    return tlist ? tlist[1 + t0 + i] : t0 + i;
+  };
   // staging roles: x -- token tid/8, h 4(tid%8)..+3 (threads 0-127); w -- expert
   // tid/4, h 8(tid%4)..+7
   const int xt = (tid >> 3) & (RM_T - 1), xq = tid & 7;
   const int we = tid >> 2, wq = tid & 3;
   const bool xrole = tid < RM_T * 8;
-  const bool xin = xrole && t0 + xt < T, win = e0 + we < E;
-  const uint16_t* xrow = x + (size_t)(xin ? t0 + xt : 0) * H + 4 * xq;
+  const int xtok = token_of(xt);
+  const bool xin = xrole && xtok >= 0, win = e0 + we < E;
+  const uint16_t* xrow = x + (size_t)(xin ? xtok : 0) * H + 4 * xq;
   const float* wrow = w + (size_t)(win ? e0 + we : 0) * H + 8 * wq;
   uint2 xv = xin ? *reinterpret_cast<const uint2*>(xrow) : make_uint2(0u, 0u);
   float4 w0 = win ? *reinterpret_cast<const float4*>(wrow) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -211,10 +291,217 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
   if (e >= E) return;
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const int ta = t0 + kq + 4 * v;
-    if (ta < T) z[(size_t)ta * E + e] = acc0[v];
+    const int ta = token_of(kq + 4 * v);
+    if (ta >= 0) z[(size_t)ta * E + e] = acc0[v];
   }
 }
+
+// ---------------------------------------------------------------------------
+// Larger batches, first pass: the logits on the bf16 matrix cores
+// (v_mfma_f32_32x32x16_bf16).  Every fp32 router weight splits exactly into
+// three bf16 parts, w = w1 + w2 + w3 (w1 = w cut to 8 significant bits, w2 =
+// the rest cut the same way, w3 = what remains, at most 8 bits: split_w_bf16x3,
+// once per call), so every product x*w_i is exact in fp32.  Per 64-wide slice
+// of h, the products of each part go to an fp32 accumulator of their own (a
+// chain of 4 instructions each); at the end of the slice the three are added,
+// w1's first, to a float64 sum.  Bound on the result's error (the selection
+// uses it to decide which tokens need float64 logits): if one instruction's
+// result (accumulator plus 16 exact products) is off by at most c*u times
+// (|accumulator| + sum of |products|), c = 34 and u = 2^-24 (sixteen rounded
+// additions, each allowed twice the rounding of round-to-nearest), a chain of
+// 4 instructions is off by at most 4*c*u times the sum of |products| of its
+// part; with |w2| + |w3| < 2^-7 (1 + 2^-7) |w| that is c*u*4 (1 + 2^-7 (1 +
+// 2^-7)) <= 4.04 c u times sum_h |x_h w_h| per slice, and over the slices
+// (float64 additions adding ~1e-16 relative) |z~ - z| <= 4.04 c u ||x_t||
+// ||w_e|| (Cauchy-Schwarz).  Workgroup: MT tokens x 64 experts, one wave per
+// 32 x 32 tile, h staged in LDS 64 at a time.  Every z[t,e] is a fixed chain of
+// its own operands: batch-independent.
+// ---------------------------------------------------------------------------
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int RB_E = 64, RB_K = 64;
+constexpr int RB_LD = RB_K + 8;  // bf16 per LDS row: 144 bytes (16-byte pad)
+
+__device__ __forceinline__ uint32_t bf16_hi(float v) { return __float_as_uint(v) >> 16; }
+
+// w [E][H] fp32 -> planes [3][E][H] bf16 with w = w1 + w2 + w3 exactly, and
+// wnorm2[e] = ||w_e||^2 (float64 sums of exact squares; one workgroup per row).
+// Also zeroes *count (the flagged-token count of the selection that follows).
+__global__ __launch_bounds__(256) void split_w_bf16x3(const float* __restrict__ w, int E, int H,
+                                                      uint16_t* __restrict__ planes,
+                                                      double* __restrict__ wnorm2,
+                                                      int32_t* __restrict__ count) {
+  __shared__ double part[4];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  if (e == 0 && tid == 0) *count = 0;
+  const float* row = w + (size_t)e * H;
+  const size_t plane = (size_t)E * H;
+  double nrm = 0.0;
+  for (int h = 4 * tid; h < H; h += 1024) {  // H % 64 == 0: whole float4s
+    const float4 v4 = *reinterpret_cast<const float4*>(row + h);
+    const float f[4] = {v4.x, v4.y, v4.z, v4.w};
+    uint32_t p[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = f[j];
+      nrm += (double)v * (double)v;
+      const uint32_t h1 = bf16_hi(v);
+      const float r1 = v - __uint_as_float(h1 << 16);   // exact
+      const uint32_t h2 = bf16_hi(r1);
+      const float r2 = r1 - __uint_as_float(h2 << 16);  // exact, at most 8 bits
+      const uint32_t h3 = bf16_hi(r2);
+      p[0][j >> 1] |= h1 << (16 * (j & 1));
+      p[1][j >> 1] |= h2 << (16 * (j & 1));
+      p[2][j >> 1] |= h3 << (16 * (j & 1));
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      *reinterpret_cast<uint2*>(planes + q * plane + (size_t)e * H + h) = make_uint2(p[q][0], p[q][1]);
+  }
+  nrm = wave_sum(nrm);
+  if ((tid & 63) == 0) part[tid >> 6] = nrm;
+  __syncthreads();
+  if (tid == 0) wnorm2[e] = ((part[0] + part[1]) + part[2]) + part[3];
+}
+
+// Workgroup: 128 tokens x 64 experts, 8 waves (4 x 2 tiles of 32 x 32), h in
+// [z*H/KS, (z+1)*H/KS) for blockIdx.z = z: the float64 sum of those slices
+// goes to zpart[z][t][e] (the selection adds the KS parts in order of z).
+constexpr int RB_MT = 128, RB_THREADS = 512;
+__global__ __launch_bounds__(RB_THREADS) void router_bf16x3(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ planes,
+                                                           int T, int H, int E, int KS,
+                                                           double* __restrict__ zpart) {
+  constexpr int MT = RB_MT, NTH = RB_THREADS;
+  constexpr int XU = MT * RB_K / 8 / NTH;        // 16-byte x units per thread per stage (2)
+  constexpr int WU = 3 * RB_E * RB_K / 8 / NTH;  // 16-byte plane units per thread per stage (3)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[3][MT][RB_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t wsp[3][3][RB_E][RB_LD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.y * MT, e0 = blockIdx.x * RB_E;
+  const int hk = H / KS;                 // a multiple of RB_K
+  const int hbeg = blockIdx.z * hk;
+  const size_t plane = (size_t)E * H;
+  // staging: x unit u = tid + NTH*i: row u/8, 16-byte column u%8; plane unit
+  // u = tid + NTH*i: plane u/512, row (u/8)%64, column u%8
+  const uint16_t* xsrc[XU];
+  bool xin[XU];
+#pragma unroll
+  for (int i = 0; i < XU; ++i) {
+    const int u = tid + NTH * i, row = u >> 3;
+    xin[i] = t0 + row < T;
+    xsrc[i] = x + (size_t)(xin[i] ? t0 + row : 0) * H + hbeg + 8 * (u & 7);
+  }
+  const uint16_t* wsrc[WU];
+  bool win[WU];
+#pragma unroll
+  for (int i = 0; i < WU; ++i) {
+    const int u = tid + NTH * i, q = u >> 9, row = (u >> 3) & 63;
+    win[i] = e0 + row < E;
+    wsrc[i] = planes + q * plane + (size_t)(win[i] ? e0 + row : 0) * H + hbeg + 8 * (u & 7);
+  }
+  // Three chunks in flight: chunk c is in LDS buffer c % 3 while the loads
+  // of chunks c+1 and c+2 (registers set (c+1) % 3, (c+2) % 3) are under way;
+  // phase c issues chunk c+3's loads into set c % 3 (staged in phase c), runs
+  // chunk c's instructions, and stages chunk c+1.
+  const int nchunk = hk / RB_K;
+  uint4 xv[3][XU], wv[3][WU];
+  auto load = [&](int c, auto set) {
+    constexpr int S = decltype(set)::value;
+    const int h0 = c * RB_K;
+    const bool in = c < nchunk;
+#pragma unroll
+    for (int i = 0; i < XU; ++i)
+      xv[S][i] = (in && xin[i]) ? *reinterpret_cast<const uint4*>(xsrc[i] + h0)
+                                : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = 0; i < WU; ++i)
+      wv[S][i] = (in && win[i]) ? *reinterpret_cast<const uint4*>(wsrc[i] + h0)
+                                : make_uint4(0u, 0u, 0u, 0u);
+  };
+  auto stage = [&](auto set) {
+    constexpr int S = decltype(set)::value;
+#pragma unroll
+    for (int i = 0; i < XU; ++i) {
+      const int u = tid + NTH * i;
+      *reinterpret_cast<uint4*>(&xs[S][u >> 3][8 * (u & 7)]) = xv[S][i];
+    }
+#pragma unroll
+    for (int i = 0; i < WU; ++i) {
+      const int u = tid + NTH * i;
+      *reinterpret_cast<uint4*>(&wsp[S][u >> 9][(u >> 3) & 63][8 * (u & 7)]) = wv[S][i];
+    }
+  };
+  const int wr = wave >> 1, wcl = wave & 1;  // the wave's 32 x 32 tile
+  const int r = lane & 31, kh = 8 * (lane >> 5);
+  v16f acc[3];
+  double zs[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    acc[0][v] = 0.f;
+    acc[1][v] = 0.f;
+    acc[2][v] = 0.f;
+    zs[v] = 0.0;
+  }
+  auto compute = [&](auto set) {
+    constexpr int S = decltype(set)::value;
+#pragma unroll
+    for (int st = 0; st < RB_K / 16; ++st) {
+      const int kk = 16 * st + kh;
+      const v8bf a = *reinterpret_cast<const v8bf*>(&xs[S][32 * wr + r][kk]);
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const v8bf bq = *reinterpret_cast<const v8bf*>(&wsp[S][q][32 * wcl + r][kk]);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[q], 0, 0, 0);
+      }
+    }
+    // end of a 64-wide slice: w1's sum, then w2's, then w3's, into float64
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        zs[v] += (double)acc[q][v];
+        acc[q][v] = 0.f;
+      }
+    }
+  };
+  load(0, IntTag<0>{});
+  load(1, IntTag<1>{});
+  load(2, IntTag<2>{});
+  stage(IntTag<0>{});
+  __syncthreads();
+  // one phase; the sets are static: J = c % 3
+  auto phase = [&](int c, auto j) {
+    constexpr int J = decltype(j)::value, J1 = (J + 1) % 3;
+    load(c + 3, IntTag<J>{});     // set J was staged in the previous phase
+    compute(IntTag<J>{});
+    if (c + 1 < nchunk) stage(IntTag<J1>{});
+    __syncthreads();
+  };
+  for (int c = 0; c < nchunk; c += 3) {
+    phase(c, IntTag<0>{});
+    if (c + 1 < nchunk) phase(c + 1, IntTag<1>{});
+    if (c + 2 < nchunk) phase(c + 2, IntTag<2>{});
+  }
+  // lane l, register v: token row 8(v/4) + 4(l/32) + v%4, expert column l%32
+  const int e = e0 + 32 * wcl + r;
+  if (e >= E) return;
+  double* zp = zpart + (size_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int t = t0 + 32 * wr + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    if (t < T) zp[(size_t)t * E + e] = zs[v];
+  }
+}
+
+// Error constant of router_bf16x3: |z~ - z| <= kRouteBound * ||x_t|| * max ||w_e||
+// (34 * 2^-24 * 4.04, raised by 1 % for the roundings of the norms and of
+// the float64 additions).
+constexpr double kRouteBound = 34.0 * 5.9604644775390625e-8 * 4.04 * 1.01;
 
 // ---------------------------------------------------------------------------
 // Per-token selection: one wave per token, expert e = lane + 64*i.
@@ -398,7 +685,7 @@ __device__ __forceinline__ void selected_positions(uint32_t sel, int nper, int* 
 }
 
 struct SelectArgs {
-  const double* z;  // [T][E] logits without bias
+  double* z;  // [T][E] logits without bias
   const float* bias;
   const int32_t* expert_slot;
   const uint16_t* x;
@@ -413,6 +700,20 @@ struct SelectArgs {
   int quantize_x;   // encode the activation row here (else the router kernel did)
   double* hist;     // nullable: demand accumulated by the one-workgroup kernel
   float* delta;
+  // Logits from router_bf16x3 (nullable otherwise): token t is appended to
+  // the list flags[1 ..] (count in flags[0], zeroed beforehand) when its k-th
+  // and (k+1)-th logits, in either order (all experts; routable experts), lie
+  // within twice the bound of each other, so its picks need float64 logits;
+  // wnorm2: ||w_e||^2 per expert.
+  int32_t* flags;
+  double* cert;           // per token: k-th value (all experts), k-th (routable), bound
+  const double* wnorm2;
+  // nullable: select only the tokens tlist[1 .. tlist[0]] (the second pass)
+  const int32_t* tlist;
+  // nullable: router_bf16x3's KS partial sums [KS][T][E]; the selection adds
+  // them in order (z = ((p0 + p1) + p2) + ...) and stores the sum in z
+  const double* zpart;
+  int KS;
 };
 
 // Routed picks of token t (bit i of msel: expert lane+64i), in ascending id,
@@ -448,13 +749,16 @@ __device__ __forceinline__ void select_write_routed(const SelectArgs& p, int t, 
 }
 
 // MXFP4 activation row of token t (when p.quantize_x): lane per 32-block.
-__device__ __forceinline__ void quantize_row(const SelectArgs& p, int t) {
-  if (!p.quantize_x) return;
+// Returns ||x_t||^2 (float64 sums of exact squares, wave-uniform), or -1 when
+// the row was not read.
+__device__ __forceinline__ double quantize_row(const SelectArgs& p, int t) {
+  if (!p.quantize_x) return -1.0;
   const int lane = threadIdx.x & 63;
   const int H = p.H;
   const int nblk = H / 32;
   const uint16_t* xr = p.x + (size_t)t * H;
   uint8_t* qr = p.xq + (size_t)t * p.xq_row;
+  double sq = 0.0;
   for (int b = lane; b < nblk; b += 64) {
     const uint4* src = reinterpret_cast<const uint4*>(xr + b * 32);
     float v[32];
@@ -470,7 +774,10 @@ __device__ __forceinline__ void quantize_row(const SelectArgs& p, int t) {
     }
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int i = 0; i < 32; ++i) {
+      amax = fmaxf(amax, fabsf(v[i]));
+      sq += (double)v[i] * (double)v[i];
+    }
     uint32_t words[4] = {0u, 0u, 0u, 0u};
     uint32_t scale = 0u;
     if (amax > 0.f) {
@@ -482,6 +789,65 @@ __device__ __forceinline__ void quantize_row(const SelectArgs& p, int t) {
     *reinterpret_cast<uint4*>(qr + (size_t)b * 16) =
         make_uint4(words[0], words[1], words[2], words[3]);
     qr[H / 2 + b] = (uint8_t)scale;
+  }
+  return wave_sum(sq);
+}
+
+// Certification of token t's picks made on router_bf16x3's logits: the k-th
+// and (k+1)-th values in both orders (z here includes the bias) must differ
+// by more than twice the logits' error bound kRouteBound * ||x_t|| * max
+// ||w_e||; otherwise the token is flagged for the exact float64 logits.
+// ||x_t||^2 is summed in float64 from exact float32 squares.
+template <int NPER>
+__device__ void certify_token(const SelectArgs& p, int t, const double* z, uint32_t valid,
+                              uint32_t routable, uint32_t usel, uint32_t msel, double xn2) {
+  const int lane = threadIdx.x & 63;
+  const int nper = (p.E + 63) / 64;
+  double ku = INFINITY, nu = -INFINITY, km = INFINITY, nm = -INFINITY, wmax = 0.0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    if (i >= nper || !((valid >> i) & 1u)) continue;
+    const double v = z[i];
+    if ((usel >> i) & 1u) ku = fmin(ku, v); else nu = fmax(nu, v);
+    if ((routable >> i) & 1u) {
+      if ((msel >> i) & 1u) km = fmin(km, v); else nm = fmax(nm, v);
+    }
+    wmax = fmax(wmax, p.wnorm2[lane + 64 * i]);
+  }
+  ku = -wave_max(-ku);
+  nu = wave_max(nu);
+  km = -wave_max(-km);
+  nm = wave_max(nm);
+  wmax = wave_max(wmax);
+  double xn = xn2;
+  if (xn < 0.0) {  // the row was not read for the activation encoding
+    const uint16_t* xr = p.x + (size_t)t * p.H;
+    xn = 0.0;
+    for (int h = 8 * lane; h < p.H; h += 512) {
+      const uint4 u = *reinterpret_cast<const uint4*>(xr + h);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double a = (double)bf16_to_f32(wd[q] & 0xFFFFu);
+        const double b = (double)bf16_to_f32(wd[q] >> 16);
+        xn += a * a + b * b;
+      }
+    }
+    xn = wave_sum(xn);
+  }
+  const double bound = kRouteBound * sqrt(xn) * sqrt(wmax);
+  // no (k+1)-th value (every candidate picked): nothing to certify in that order
+  const bool close_u = nu != -INFINITY && !(ku - nu > 2.0 * bound);
+  const bool close_m = nm != -INFINITY && !(km - nm > 2.0 * bound);
+  if (lane == 0) {
+    if (close_u || close_m) {
+      // the list's order does not matter: every listed token is handled on its own
+      const int slot = (int)atomicAdd(reinterpret_cast<unsigned*>(p.flags), 1u);
+      p.flags[1 + slot] = t;
+    }
+    p.cert[3 * (size_t)t] = ku;
+    p.cert[3 * (size_t)t + 1] = km;   // +inf when nothing is routable
+    p.cert[3 * (size_t)t + 2] = bound;
   }
 }
 
@@ -512,9 +878,20 @@ __device__ void select_token(const SelectArgs& p, int t, int role) {
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = min(lane + 64 * i, E - 1);
-    zl[i] = p.z[(size_t)t * E + e];
+    zl[i] = p.zpart ? p.zpart[(size_t)t * E + e] : p.z[(size_t)t * E + e];
     bl[i] = bsrc[e];
     sl[i] = p.expert_slot[e];
+  }
+  if (p.zpart) {  // the K parts of router_bf16x3, added in order and kept in z
+    const size_t part = (size_t)p.T * E;
+    for (int q = 1; q < p.KS; ++q) {
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        zl[i] += p.zpart[q * part + (size_t)t * E + min(lane + 64 * i, E - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < NPER; ++i)
+      if (lane + 64 * i < E) p.z[(size_t)t * E + lane + 64 * i] = zl[i];
   }
 #pragma unroll
   for (int i = 0; i < NPER; ++i) bl[i] = has_bias ? bl[i] : 0.f;
@@ -576,14 +953,20 @@ __device__ void select_token(const SelectArgs& p, int t, int role) {
     }
   }
   if (do_m) select_write_routed<NPER>(p, t, msel, got, ex, denom, slot_of);
-  if (role & kSelRouted) quantize_row(p, t);
+  double xn2 = -1.0;
+  if (role & kSelRouted) xn2 = quantize_row(p, t);
+  if (p.flags && role == kSelBoth) certify_token<NPER>(p, t, z, valid, routable, usel, msel, xn2);
 }
 
 template <int NPER>
 __global__ __launch_bounds__(256) void route_select(SelectArgs p) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= p.T) return;  // wave-uniform
-  select_token<NPER>(p, t, kSelBoth);
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (!p.tlist) {
+    if (i < p.T) select_token<NPER>(p, i, kSelBoth);  // wave-uniform
+    return;
+  }
+  const int n = p.tlist[0];  // a fixed grid walks the list
+  for (int j = i; j < n; j += gridDim.x * 4) select_token<NPER>(p, p.tlist[1 + j], kSelBoth);
 }
 
 // ---------------------------------------------------------------------------
@@ -915,9 +1298,44 @@ static size_t route_bucket_bytes(int T, int S) {
   return up_to(nchunk * (size_t)(S > 0 ? S : 1) * sizeof(int32_t), 256);
 }
 
+// The certified path (router_bf16x3): ||w_e||^2 [E] float64, flags [T] int32
+// and the flagged-token list [1 + T] int32.
+// K parts of router_bf16x3 (1, 2, 4 or 8, each a whole number of 64-wide
+// slices): one workgroup runs per CU (its LDS ring takes 135 KB), so the
+// split that keeps the most of the 256 CUs busy over the launch's rounds,
+// the fewest parts among equals.
+static int route_ksplit(int T, int H, int E) {
+  const long tiles = (long)((T + 127) / 128) * ((E + 63) / 64);
+  int best = 1;
+  double best_use = 0.0;
+  for (int ks = 1; ks <= 8 && (H / ks) % 64 == 0 && H % ks == 0; ks *= 2) {
+    const long wgs = tiles * ks;
+    const double use = (double)wgs / (256.0 * (double)((wgs + 255) / 256));
+    if (use > best_use + 1e-9) {
+      best = ks;
+      best_use = use;
+    }
+  }
+  return best;
+}
+
+// H a multiple of 512: whole 64-wide slices, and whole 16-byte x loads for each
+// lane's H/64 elements in router_f64_candidates.
+static bool route_approx(int T, int H) {
+  return T > kSplitRouterMaxT && H % 512 == 0 && H / kRouterChunk <= RS_MAX_CHUNKS;
+}
+static size_t route_cert_bytes(int T, int H, int E) {
+  return up_to((size_t)E * sizeof(double), 256) +
+         up_to((size_t)(T + 1) * sizeof(int32_t), 256) +   // flagged tokens: count, ids
+         up_to((size_t)3 * E * H * sizeof(uint16_t), 256) +  // the bf16 planes of w
+         up_to((size_t)3 * T * sizeof(double), 256) +         // per token: k-th values, bound
+         up_to((size_t)route_ksplit(T, H, E) * T * E * sizeof(double), 256);  // K parts of z
+}
+
 static size_t route_ws_bytes(int T, int H, int E, int S) {
   if (T <= 0) return 0;
-  return route_z_bytes(T, E) + moe_demand_ws_bytes_internal(T, E) + route_bucket_bytes(T, S);
+  return route_z_bytes(T, E) + moe_demand_ws_bytes_internal(T, E) + route_bucket_bytes(T, S) +
+         (route_approx(T, H) ? route_cert_bytes(T, H, E) : 0);
 }
 
 size_t moe_route_ws_bytes_internal(int T, int H, int E, int S) {
@@ -961,20 +1379,37 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   uint32_t* counter = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a->ws) +
                                                   route_z_bytes(T, E) +
                                                   moe_demand_ws_bytes_internal(T, E));
+  const bool approx = !small_router && route_approx(T, H);
+  uint8_t* cert = static_cast<uint8_t*>(a->ws) + route_z_bytes(T, E) +
+                  moe_demand_ws_bytes_internal(T, E) + route_bucket_bytes(T, S);
+  double* wnorm2 = reinterpret_cast<double*>(cert);
+  int32_t* flags = reinterpret_cast<int32_t*>(cert + up_to((size_t)E * sizeof(double), 256));
+  uint16_t* planes = reinterpret_cast<uint16_t*>(
+      reinterpret_cast<uint8_t*>(flags) + up_to((size_t)(T + 1) * sizeof(int32_t), 256));
+  double* cert_info = reinterpret_cast<double*>(
+      reinterpret_cast<uint8_t*>(planes) + up_to((size_t)3 * E * H * sizeof(uint16_t), 256));
+  double* zpart = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(cert_info) +
+                                            up_to((size_t)3 * T * sizeof(double), 256));
+  const int ks = route_ksplit(T, H, E);
   if (!record_stage(ev,0, stream)) return MOE_EHIP;
   if (a->reuse_logits) {
     // z and xq stay from the previous call; only the fused kernel's counter,
-    // which the router would zero, needs clearing
+    // which the router would zero, and the flagged-token count need clearing
     if (fused) fill_i32<<<1, 256, 0, stream>>>(reinterpret_cast<int32_t*>(counter), 1, 0);
+    if (approx) fill_i32<<<1, 256, 0, stream>>>(flags, 1, 0);
   } else if (small_router) {
     const int nrb = E * ((T + RS_T - 1) / RS_T);
     const size_t nx = ((size_t)T * H + 255) / 256;
     const int nxb = (int)(nx < 1024 ? nx : 1024);
     router_small_f64<<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, a->xq, xq_row,
                                                     nrb, fused ? counter : nullptr);
+  } else if (approx) {
+    split_w_bf16x3<<<E, 256, 0, stream>>>(a->w_router, E, H, planes, wnorm2, flags);
+    router_bf16x3<<<dim3((E + RB_E - 1) / RB_E, (T + RB_MT - 1) / RB_MT, ks), RB_THREADS, 0,
+                    stream>>>(a->x, planes, T, H, E, ks, zpart);
   } else {
     dim3 grid((E + RM_E - 1) / RM_E, (T + RM_T - 1) / RM_T);
-    router_full_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z);
+    router_full_f64<<<grid, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, nullptr);
   }
   if (!record_stage(ev,1, stream)) return MOE_EHIP;
   SelectArgs p;
@@ -997,6 +1432,12 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   p.quantize_x = (small_router || a->reuse_logits) ? 0 : 1;
   p.hist = nullptr;
   p.delta = nullptr;
+  p.flags = approx ? flags : nullptr;
+  p.cert = cert_info;
+  p.zpart = (approx && !a->reuse_logits) ? zpart : nullptr;
+  p.KS = ks;
+  p.wnorm2 = wnorm2;
+  p.tlist = nullptr;
   const int A = T * k;
   if (fused) {
     // selection, demand and bucketing in one kernel; the remaining stage
@@ -1013,6 +1454,21 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     route_select<4><<<(T + 3) / 4, 256, 0, stream>>>(p);
   else
     route_select<16><<<(T + 3) / 4, 256, 0, stream>>>(p);
+  if (approx) {
+    // the flagged tokens: exact float64 logits, then their picks again (the
+    // grids are sized for every token; workgroups past the list leave at once)
+    router_f64_candidates<<<T < 2048 ? T : 2048, 256, 0, stream>>>(
+        a->x, a->w_router, a->bias, a->expert_slot, H, E, S, z, flags, cert_info);
+    p.flags = nullptr;
+    p.zpart = nullptr;   // z now holds the sums, with the float64 candidates
+    p.tlist = flags;
+    p.quantize_x = 0;
+    const int nwg = (T + 3) / 4 < 512 ? (T + 3) / 4 : 512;
+    if (E <= 256)
+      route_select<4><<<nwg, 256, 0, stream>>>(p);
+    else
+      route_select<16><<<nwg, 256, 0, stream>>>(p);
+  }
   if (a->hist_row) {
     const int st = moe_demand_launch_internal(a->topk_expert, a->topk_score, T, k, E, a->hist_row,
                                               a->delta, dws, stream);

@@ -70,8 +70,14 @@ def test_workspace_sizes():
     # bucket counts (chunks of 64 tokens x slots, 256-byte aligned)
     up = lambda v: (v + 255) // 256 * 256
     assert ws(B.MOE_OP_ROUTE, 8, 4096, 256, 8, 0, 230) == 8 * 256 * 8 + up(230 * 4)
+    # larger batches with H a multiple of 512 add the certified router's
+    # ||w_e||^2 (float64 [E]), the flagged-token list ([1 + T] int32)
     assert ws(B.MOE_OP_ROUTE, 2048, 4096, 256, 8, 0, 166) == \
-        2048 * 256 * 8 + 32 * 256 * 8 + up(32 * 166 * 4)
+        2048 * 256 * 8 + 32 * 256 * 8 + up(32 * 166 * 4) + up(256 * 8) + up(2049 * 4) \
+        + 3 * 256 * 4096 * 2 + 3 * 2048 * 8 \
+        + 4 * 2048 * 256 * 8       # bf16 planes of w, per-token bounds, four K parts of z
+    assert ws(B.MOE_OP_ROUTE, 100, 96, 16, 4, 0, 10) == \
+        up(100 * 16 * 8) + 2 * 16 * 8 + up(2 * 10 * 4)   # H % 64 != 0: no certification
     assert ws(B.MOE_OP_DEMAND, 64, 0, 256, 8, 0, 0) == 0
     assert ws(B.MOE_OP_DEMAND, 65, 0, 256, 8, 0, 0) == 2 * 256 * 8
     e = ws(B.MOE_OP_EXPERTS, 8, 4096, 0, 8, 2048, 230)

@@ -276,6 +276,40 @@ def test_route_edge_shapes(T, E, k, nr, S, H):
     check_route(g, oracle_route(g))
 
 
+@pytest.mark.parametrize("T,H,near", [(256, 512, False), (300, 1024, True), (2048, 4096, True)])
+def test_route_certified_path_ties_and_near_ties(T, H, near):
+    """Batches above 64 tokens with H a multiple of 512 route on bounded bf16
+    logits and re-select, on float64 logits, every token whose k-th and
+    (k+1)-th logits are within twice the bound.  Router rows repeated in
+    groups of four make logits tie exactly in every token; with `near`, the
+    repeats differ by j * 2^-20 in one weight, so the logits differ by far
+    less than the bound.  Nearly every token then takes the second pass, and
+    its picks -- exact ties to the lower expert id -- must be the oracle's.
+    The weights are multiples of 2^-20 below 1, so every product and partial
+    sum is exact in float64 and the oracle's ties do not depend on its
+    summation order either."""
+    E, k, nr = 64, 8, 40
+    lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=128, n_routable=nr, seed=T + H,
+                              bias_scale=0.0)
+    w = (np.round(lay.w_router.astype(np.float64) * 4096) / 4096).astype(np.float32)
+    for g in range(0, E, 4):
+        w[g + 1:g + 4] = w[g]
+        if near:
+            for j in range(1, 4):
+                w[g + j, j] += np.float32(j * 2.0 ** -20)
+    lay.w_router = w
+    lay.bias = np.zeros(E, dtype=np.float32)
+    # activations below 2^-8 in magnitude are set to zero, so that a product's
+    # lowest bit (>= 2^-35) and the largest partial sum (< 2^7) fit 53 bits
+    xf = fixtures.bf16_bits_to_f32(lay.x_bits)
+    lay.x_bits = np.where(np.abs(xf) < 2.0 ** -8, np.uint16(0), lay.x_bits).astype(np.uint16)
+    say(f"certified routing: T={T} H={H}, router rows repeated in fours "
+        f"({'near ties' if near else 'exact ties'})")
+    g = GpuLayer(lay)
+    g.route()
+    check_route(g, oracle_route(g))
+
+
 def _init_route_only(g, lay, es, S):
     import torch
     from resident_expert_routing_amd import runtime as R
