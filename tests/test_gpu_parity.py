@@ -260,6 +260,9 @@ def test_route_reuse_logits(T, E, k):
     (64, 256, 8, 230, 230, 4096),  # largest batch of the fused path
     (64, 256, 32, 250, 8192, 512),  # fused path: most assignments, maximum S
     (65, 256, 8, 230, 230, 4096),  # smallest batch of the multi-kernel path
+    (8, 256, 32, 250, 8192, 512),  # one-launch decode path: most assignments, maximum S
+    (3, 33, 6, 4, 40, 256),        # one-launch decode path: odd E, fewer routable than k
+    (8, 256, 8, 230, 230, 4096),   # largest batch of the one-launch decode path
 ])
 def test_route_edge_shapes(T, E, k, nr, S, H):
     say(f"moe_route edge T={T} E={E} k={k} routable={nr} S={S} H={H}")
@@ -321,6 +324,39 @@ def _init_route_only(g, lay, es, S):
     g.expert_slot = to_dev(es.astype(np.int32))
     g.buf = R.LayerBuffers(g.T, g.H, g.E, g.k, g.I, S, torch.device("cuda", 0))
     g.hist = torch.zeros(g.E, dtype=torch.float64, device=torch.device("cuda", 0))
+
+
+@pytest.mark.parametrize("fill", ["random", "ones", "again"])
+def test_route_decode_workspace_contents(fill):
+    """The one-launch decode path keeps its completion counter in the
+    workspace: whatever the workspace holds before the call (random bytes,
+    all ones, the previous call's state), the picks, slots, bucketing and
+    demand are the oracle's."""
+    import torch
+    lay = fixtures.tiny_layer(T=8, H=512, E=64, k=6, I=32, n_routable=40, seed=91,
+                              bias_scale=0.5)
+    g = GpuLayer.__new__(GpuLayer)
+    _init_route_only(g, lay, lay.expert_slot.copy(), 40)
+    ws = g.buf.ws_route
+    if fill == "random":
+        gen = torch.Generator(device="cpu").manual_seed(5)
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=gen).to(ws.device))
+    elif fill == "ones":
+        ws.fill_(255)
+    else:
+        g.route()
+    from resident_expert_routing_amd import runtime as R
+    say(f"decode routing with a workspace of {fill} contents")
+    g.hist.zero_()
+    R.route(g.buf, g.x, g.w_router, g.bias, g.expert_slot, hist_row=g.hist)
+    torch.cuda.synchronize()
+    r = oracle_route(g)
+    check_route(g, r)
+    want = moe.demand(r["topk_expert"], r["topk_score"], g.E)
+    hist = g.hist.cpu().numpy()
+    nz = want > 0
+    assert (hist[~nz] == 0).all()
+    assert np.all(np.abs(hist[nz] - want[nz]) <= DEMAND_REL * want[nz])
 
 
 def test_route_empty_batch():
