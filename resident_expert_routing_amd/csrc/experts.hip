@@ -892,22 +892,6 @@ __device__ __forceinline__ bool tile_of(int w, int nN, int tm, const int32_t* __
   return true;
 }
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// Direct loads to LDS at lds_base + size * lane (lds_base is wave-uniform and
-// goes to M0).  Inline assembly, so that the compiler does not add a wait for
-// every outstanding load before each LDS read: the pipeline waits for them
-// explicitly (pipe_wait).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is written here on purpose
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(m0), "v"(g)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Per-lane sources of the direct loads; stage q reads code bytes
 // [64 q, 64 q + 64) of every row, group g scale bytes [16 g, 16 g + 16).

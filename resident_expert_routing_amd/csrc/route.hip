@@ -317,14 +317,9 @@ __global__ __launch_bounds__(256) void router_full_f64(const uint16_t* __restric
 // 32 x 32 tile, h staged in LDS 64 at a time.  Every z[t,e] is a fixed chain of
 // its own operands: batch-independent.
 // ---------------------------------------------------------------------------
-template <int V>
-struct IntTag {
-  static constexpr int value = V;
-};
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 constexpr int RB_E = 64, RB_K = 64;
-constexpr int RB_LD = RB_K + 8;  // bf16 per LDS row: 144 bytes (16-byte pad)
 
 __device__ __forceinline__ uint32_t bf16_hi(float v) { return __float_as_uint(v) >> 16; }
 
@@ -371,73 +366,67 @@ __global__ __launch_bounds__(256) void split_w_bf16x3(const float* __restrict__ 
 // Workgroup: 128 tokens x 64 experts, 8 waves (4 x 2 tiles of 32 x 32), h in
 // [z*H/KS, (z+1)*H/KS) for blockIdx.z = z: the float64 sum of those slices
 // goes to zpart[z][t][e] (the selection adds the KS parts in order of z).
+// Operands reach LDS by direct global-to-LDS loads into a ring of three
+// 40 KB stages (64 h of the 128 x rows and of the three planes' 64 rows), two
+// stages issued ahead; each load moves 8 rows x 128 bytes.  The 16-byte block
+// b of a 128-byte LDS row r sits at b ^ ((r >> 1) & 7), so a fragment read
+// (32 rows, one block each) is free of bank conflicts.  Rows past T or E read
+// row 0 of the batch: their results are never stored.
 constexpr int RB_MT = 128, RB_THREADS = 512;
+constexpr int RB_ROW = 2 * RB_K;                          // bytes per LDS row per stage
+constexpr int RB_XB = RB_MT * RB_ROW;                     // x rows of a stage (16 KB)
+constexpr int RB_WB = 3 * RB_E * RB_ROW;                  // the planes' rows (24 KB)
+constexpr int RB_STAGE = RB_XB + RB_WB;
+constexpr int RB_RING = 3;
+constexpr int RB_XL = RB_XB / 1024 / (RB_THREADS / 64);  // x loads per wave per stage (2)
+constexpr int RB_WL = RB_WB / 1024 / (RB_THREADS / 64);  // plane loads per wave per stage (3)
+static_assert(RB_XL == 2 && RB_WL == 3, "vmcnt below counts 5 loads per stage");
+
+__device__ __forceinline__ int rb_swz(int row) { return (row >> 1) & 7; }
+
 __global__ __launch_bounds__(RB_THREADS) void router_bf16x3(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ planes,
                                                            int T, int H, int E, int KS,
                                                            double* __restrict__ zpart) {
-  constexpr int MT = RB_MT, NTH = RB_THREADS;
-  constexpr int XU = MT * RB_K / 8 / NTH;        // 16-byte x units per thread per stage (2)
-  constexpr int WU = 3 * RB_E * RB_K / 8 / NTH;  // 16-byte plane units per thread per stage (3)
-  __shared__ __attribute__((aligned(16))) uint16_t xs[3][MT][RB_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t wsp[3][3][RB_E][RB_LD];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.y * MT, e0 = blockIdx.x * RB_E;
-  const int hk = H / KS;                 // a multiple of RB_K
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RB_RING * RB_STAGE];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int t0 = blockIdx.y * RB_MT, e0 = blockIdx.x * RB_E;
+  const int hk = H / KS;  // a multiple of RB_K
   const int hbeg = blockIdx.z * hk;
   const size_t plane = (size_t)E * H;
-  // staging: x unit u = tid + NTH*i: row u/8, 16-byte column u%8; plane unit
-  // u = tid + NTH*i: plane u/512, row (u/8)%64, column u%8
-  const uint16_t* xsrc[XU];
-  bool xin[XU];
+  // load j of the wave: x rows 8 (RB_XL w + j) + lane/8, or plane unit
+  // u = RB_WL w + j: plane u / 8, rows 8 (u % 8) + lane/8; lane i lands at
+  // position i % 8 of its row, so it reads block (i % 8) ^ swz(row)
+  const uint8_t* xsrc[RB_XL];
 #pragma unroll
-  for (int i = 0; i < XU; ++i) {
-    const int u = tid + NTH * i, row = u >> 3;
-    xin[i] = t0 + row < T;
-    xsrc[i] = x + (size_t)(xin[i] ? t0 + row : 0) * H + hbeg + 8 * (u & 7);
+  for (int j = 0; j < RB_XL; ++j) {
+    const int row = 8 * (RB_XL * wave + j) + (lane >> 3);
+    const int b = (lane & 7) ^ rb_swz(row);
+    xsrc[j] = reinterpret_cast<const uint8_t*>(x + (size_t)(t0 + row < T ? t0 + row : 0) * H +
+                                               hbeg + 8 * b);
   }
-  const uint16_t* wsrc[WU];
-  bool win[WU];
+  const uint8_t* wsrc[RB_WL];
 #pragma unroll
-  for (int i = 0; i < WU; ++i) {
-    const int u = tid + NTH * i, q = u >> 9, row = (u >> 3) & 63;
-    win[i] = e0 + row < E;
-    wsrc[i] = planes + q * plane + (size_t)(win[i] ? e0 + row : 0) * H + hbeg + 8 * (u & 7);
+  for (int j = 0; j < RB_WL; ++j) {
+    const int u = RB_WL * wave + j, q = u >> 3, row = 8 * (u & 7) + (lane >> 3);
+    const int b = (lane & 7) ^ rb_swz(row);
+    wsrc[j] = reinterpret_cast<const uint8_t*>(planes + q * plane +
+                                               (size_t)(e0 + row < E ? e0 + row : 0) * H + hbeg +
+                                               8 * b);
   }
-  // Three chunks in flight: chunk c is in LDS buffer c % 3 while the loads
-  // of chunks c+1 and c+2 (registers set (c+1) % 3, (c+2) % 3) are under way;
-  // phase c issues chunk c+3's loads into set c % 3 (staged in phase c), runs
-  // chunk c's instructions, and stages chunk c+1.
   const int nchunk = hk / RB_K;
-  uint4 xv[3][XU], wv[3][WU];
-  auto load = [&](int c, auto set) {
-    constexpr int S = decltype(set)::value;
-    const int h0 = c * RB_K;
-    const bool in = c < nchunk;
+  auto issue = [&](int c) {
+    uint8_t* st = smem + (c % RB_RING) * RB_STAGE;
 #pragma unroll
-    for (int i = 0; i < XU; ++i)
-      xv[S][i] = (in && xin[i]) ? *reinterpret_cast<const uint4*>(xsrc[i] + h0)
-                                : make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < RB_XL; ++j)
+      dma16(xsrc[j] + (size_t)c * RB_ROW, st + (RB_XL * wave + j) * 1024);
 #pragma unroll
-    for (int i = 0; i < WU; ++i)
-      wv[S][i] = (in && win[i]) ? *reinterpret_cast<const uint4*>(wsrc[i] + h0)
-                                : make_uint4(0u, 0u, 0u, 0u);
-  };
-  auto stage = [&](auto set) {
-    constexpr int S = decltype(set)::value;
-#pragma unroll
-    for (int i = 0; i < XU; ++i) {
-      const int u = tid + NTH * i;
-      *reinterpret_cast<uint4*>(&xs[S][u >> 3][8 * (u & 7)]) = xv[S][i];
-    }
-#pragma unroll
-    for (int i = 0; i < WU; ++i) {
-      const int u = tid + NTH * i;
-      *reinterpret_cast<uint4*>(&wsp[S][u >> 9][(u >> 3) & 63][8 * (u & 7)]) = wv[S][i];
-    }
+    for (int j = 0; j < RB_WL; ++j)
+      dma16(wsrc[j] + (size_t)c * RB_ROW, st + RB_XB + (RB_WL * wave + j) * 1024);
   };
   const int wr = wave >> 1, wcl = wave & 1;  // the wave's 32 x 32 tile
-  const int r = lane & 31, kh = 8 * (lane >> 5);
+  const int r = lane & 31, hh = lane >> 5;
+  const int swz = rb_swz(r);  // = swz(32 wr + r) = swz(32 wcl + r)
   v16f acc[3];
   double zs[16];
 #pragma unroll
@@ -447,15 +436,26 @@ __global__ __launch_bounds__(RB_THREADS) void router_bf16x3(const uint16_t* __re
     acc[2][v] = 0.f;
     zs[v] = 0.0;
   }
-  auto compute = [&](auto set) {
-    constexpr int S = decltype(set)::value;
+  issue(0);
+  if (nchunk > 1) issue(1);
+  for (int c = 0; c < nchunk; ++c) {
+    // after chunk c's loads only chunk c + 1's five may still be in flight
+    if (c + 1 < nchunk)
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's share landed; chunk c - 1's slot is free
+    if (c + 2 < nchunk) issue(c + 2);
+    const uint8_t* st = smem + (c % RB_RING) * RB_STAGE;
+    const uint8_t* xa = st + (32 * wr + r) * RB_ROW;
+    const uint8_t* wb = st + RB_XB + (32 * wcl + r) * RB_ROW;
 #pragma unroll
-    for (int st = 0; st < RB_K / 16; ++st) {
-      const int kk = 16 * st + kh;
-      const v8bf a = *reinterpret_cast<const v8bf*>(&xs[S][32 * wr + r][kk]);
+    for (int s = 0; s < RB_K / 16; ++s) {
+      const int pos = ((2 * s + hh) ^ swz) * 16;
+      const v8bf a = *reinterpret_cast<const v8bf*>(xa + pos);
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
-        const v8bf bq = *reinterpret_cast<const v8bf*>(&wsp[S][q][32 * wcl + r][kk]);
+        const v8bf bq = *reinterpret_cast<const v8bf*>(wb + q * (RB_E * RB_ROW) + pos);
         acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[q], 0, 0, 0);
       }
     }
@@ -468,24 +468,6 @@ __global__ __launch_bounds__(RB_THREADS) void router_bf16x3(const uint16_t* __re
         acc[q][v] = 0.f;
       }
     }
-  };
-  load(0, IntTag<0>{});
-  load(1, IntTag<1>{});
-  load(2, IntTag<2>{});
-  stage(IntTag<0>{});
-  __syncthreads();
-  // one phase; the sets are static: J = c % 3
-  auto phase = [&](int c, auto j) {
-    constexpr int J = decltype(j)::value, J1 = (J + 1) % 3;
-    load(c + 3, IntTag<J>{});     // set J was staged in the previous phase
-    compute(IntTag<J>{});
-    if (c + 1 < nchunk) stage(IntTag<J1>{});
-    __syncthreads();
-  };
-  for (int c = 0; c < nchunk; c += 3) {
-    phase(c, IntTag<0>{});
-    if (c + 1 < nchunk) phase(c + 1, IntTag<1>{});
-    if (c + 2 < nchunk) phase(c + 2, IntTag<2>{});
   }
   // lane l, register v: token row 8(v/4) + 4(l/32) + v%4, expert column l%32
   const int e = e0 + 32 * wcl + r;
