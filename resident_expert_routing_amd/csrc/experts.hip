@@ -289,53 +289,28 @@ __device__ SlotRange wave_nth_used_slot(int u, const int32_t* __restrict__ offse
                    __builtin_amdgcn_readlane(fb, L)};
 }
 
-// Slot of work item u: from the prebuilt list when there is one, else found
-// in place (small slot counts).
-__device__ __forceinline__ SlotRange work_slot(int u, const int32_t* used, const int32_t* offsets,
-                                               int S, int A) {
-  if (!used) return wave_nth_used_slot(u, offsets, S, A);
-  const int n = used[0], s = used[1 + u];  // both in one round trip: u < min(S, A) < S + 1
-  if (u >= n) return SlotRange{-1, 0, 0};
-  return SlotRange{s, offsets[s], offsets[s + 1]};
+// Slot of work item u.  Small slot counts: the u-th used slot, found in place.
+// Larger ones (sel_slot given): work item u is position u of the bucketed
+// order, and it does the work of its slot when it is the slot's first
+// position (perm, sel_slot and slot_offsets come from one moe_route call);
+// every other position's item is empty.  Three dependent loads, where a scan
+// of thousands of offsets would not fit, and no list to build beforehand.
+__device__ __forceinline__ SlotRange work_slot(int u, const int32_t* __restrict__ sel_slot,
+                                               const int32_t* __restrict__ perm,
+                                               const int32_t* __restrict__ offsets, int S,
+                                               int A) {
+  if (!sel_slot) return wave_nth_used_slot(u, offsets, S, A);
+  if (u >= A) return SlotRange{-1, 0, 0};
+  const int a = __builtin_amdgcn_readfirstlane(perm[u]);
+  if (a < 0 || a >= A) return SlotRange{-1, 0, 0};
+  const int s = __builtin_amdgcn_readfirstlane(sel_slot[a]);
+  if (s < 0 || s >= S) return SlotRange{-1, 0, 0};
+  const int p0 = __builtin_amdgcn_readfirstlane(offsets[s]);
+  const int p1 = __builtin_amdgcn_readfirstlane(offsets[s + 1]);
+  if (p0 != u || !slot_used(p0, p1, A)) return SlotRange{-1, 0, 0};
+  return SlotRange{s, p0, p1};
 }
 
-// ---------------------------------------------------------------------------
-// Work list: the slots that hold assignments, ascending, from slot_offsets.
-// used[0] = count, used[1..] = slot ids.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void build_used(const int32_t* __restrict__ offsets, int S,
-                                                   int A, int32_t* __restrict__ used) {
-  constexpr int kPer = MOE_MAX_S / 1024;
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int per = (S + 1023) / 1024;
-  const int lo = min(S, tid * per), hi = min(S, lo + per);
-  int ofs[kPer + 1];  // this thread's offsets, read in one batch
-#pragma unroll
-  for (int i = 0; i <= kPer; ++i) ofs[i] = offsets[min(lo + i, S)];  // in bounds: S + 1 entries
-  int local = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    local += (lo + i < hi && slot_used(ofs[i], ofs[i + 1], A)) ? 1 : 0;
-  int incl = local;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wsum[wv] = incl;
-  __syncthreads();
-  int run = incl - local;
-  for (int i = 0; i < wv; ++i) run += wsum[i];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (lo + i < hi && slot_used(ofs[i], ofs[i + 1], A)) used[1 + run++] = lo + i;
-  if (tid == 0) {
-    int total = 0;
-    for (int i = 0; i < 16; ++i) total += wsum[i];
-    used[0] = total;
-  }
-}
 
 // ===========================================================================
 // Small-batch kernels
@@ -409,7 +384,7 @@ struct GateUpArgs {
   size_t off_gc, off_gs, off_uc, off_us;
   const int32_t* offsets;
   const int32_t* perm;
-  const int32_t* used;  // prebuilt work list, or null: found in place
+  const int32_t* sel_slot;  // large slot counts: item u = bucketed position u (else null)
   int32_t* slots;       // out: (slot, p0, p1) of work item u at 3u (slot -1: none), for down
   uint8_t* hq;
   size_t hrow;
@@ -425,7 +400,7 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
   // the shared expert's item: slot id S (never a routed slot), rows A .. A+T
   const bool sh = p.shared && u == p.maxU;
   const SlotRange sr = sh ? SlotRange{p.S, p.A, p.A + p.T}
-                          : work_slot(u, p.used, p.offsets, p.S, p.A);
+                          : work_slot(u, p.sel_slot, p.perm, p.offsets, p.S, p.A);
   if (nb == 0 && threadIdx.x == 0) {  // the down kernel takes its work items from here
     p.slots[3 * u] = sr.s;
     p.slots[3 * u + 1] = sr.p0;
@@ -1189,7 +1164,7 @@ __global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
 using namespace moe;
 
 struct ExpertsWs {
-  size_t used_off, items_off, zero_off, hq_off, y_off, total;
+  size_t items_off, zero_off, hq_off, y_off, total;
 };
 
 // Kernel family of a batch: batches of at least kPipeMinA assignments (T*k)
@@ -1223,12 +1198,12 @@ static ExpertsWs experts_ws(int T, int H, int k, int I, int S, bool shared) {
   const size_t rows = A + (shared ? (size_t)T : 0);  // hq and y: routed rows, then shared ones
   const Family fam = family_of(T, k, H, I);
   const bool tiled = fam != kFamSmall;
-  w.used_off = 0;
-  w.items_off = up_to((size_t)(S + 2) * sizeof(int32_t), 256);
+  w.items_off = 0;
   // pipelined: the M-tile list, then the deferred slot's (first item, item
   // count); small batches: (slot, p0, p1) per work item
   const size_t ntile = max_tiles(A, S, kTileM) + shared_tiles(T, shared);
-  const size_t nwork = (A < (size_t)S ? A : (size_t)S) + (shared ? 1 : 0);
+  const size_t nwork = (S > kInlineWorklistMaxS ? A : (A < (size_t)S ? A : (size_t)S)) +
+                       (shared ? 1 : 0);
   const size_t items = tiled ? (1 + 4 * ntile + 2) * sizeof(int32_t)
                              : 3 * nwork * sizeof(int32_t);
   w.zero_off = up_to(w.items_off + items, 256);
@@ -1364,17 +1339,15 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     down_pipe<<<(unsigned)g2, 256, 0, stream>>>(t);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   } else {
-    int32_t* used = reinterpret_cast<int32_t*>(ws + W.used_off);
-    const int maxU = S < A ? S : A;
-    // Work list of used slots: built once for large slot counts, else each
-    // workgroup finds its slot in place (saves a launch on decode batches).
-    const bool prebuilt = S > kInlineWorklistMaxS;
+    // work items: the used slots, found in place, for small slot counts; the
+    // bucketed positions (an item per slot's first position) for larger ones
+    const bool by_position = S > kInlineWorklistMaxS;
+    const int maxU = by_position ? A : (S < A ? S : A);
     // small batches run every slot in one pass: the deferred slot's bytes
     // must be in place before it
     if (defer >= 0 && hipStreamWaitEvent(stream, a->defer_event, 0) != hipSuccess)
       return MOE_EHIP;
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
-    if (prebuilt) build_used<<<1, 1024, 0, stream>>>(a->slot_offsets, S, A, used);
     GateUpArgs g;
     g.xq = a->xq;
     g.xrow = mxfp4_row_bytes(H);
@@ -1386,7 +1359,7 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     g.off_us = L.off[3];
     g.offsets = a->slot_offsets;
     g.perm = a->perm;
-    g.used = prebuilt ? used : nullptr;
+    g.sel_slot = by_position ? a->sel_slot : nullptr;
     int32_t* slots = reinterpret_cast<int32_t*>(ws + W.items_off);
     g.slots = slots;
     g.hq = hq;

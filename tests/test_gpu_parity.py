@@ -518,10 +518,12 @@ def test_layer_edge_shapes(T, E, k, nr, H, I):
     _layer_parity(GpuLayer(lay))
 
 
-def test_layer_sparse_slots_prebuilt_worklist():
-    """More than 1024 slots: the expert kernels take their work from a list
-    built once instead of scanning slot_offsets in every workgroup."""
-    say("layer with 12 routable experts spread over 2000 slots")
+@pytest.mark.parametrize("shared", [False, True])
+def test_layer_sparse_slots_by_position(shared):
+    """More than 1024 slots: a work item of the small-batch kernels is a
+    position of the bucketed order, busy when it is its slot's first position;
+    with a shared expert, its item follows all T*k positions."""
+    say(f"layer with 12 routable experts spread over 2000 slots, shared expert: {shared}")
     T, H, E, k, I, S = 24, 256, 16, 4, 128, 2000
     lay = fixtures.tiny_layer(T=T, H=H, E=E, k=k, I=I, n_routable=12, seed=31, bias_scale=0.5)
     rng = np.random.default_rng(2)
@@ -539,7 +541,23 @@ def test_layer_sparse_slots_prebuilt_worklist():
     g.arena.mem.zero_()
     g.arena.upload(lambda s: lay.expert_bytes(slot_expert[s]), slots=spread)
     g.slot_bytes_fn = lambda: (lambda s: lay.expert_bytes(slot_expert[s]))
-    _layer_parity(g)
+    if not shared:
+        _layer_parity(g)
+        return
+    wg, wu, wd = fixtures.expert_weights(41, 999, H, I)
+    sb = fixtures.pack_expert(wg, wu, wd)
+    g.buf = R.LayerBuffers(T, H, E, k, I, S, torch.device("cuda", 0), shared=True)
+    g.route()
+    R.experts(g.buf, g.arena.ptr(), g.arena.stride, shared_expert=to_dev(sb))
+    out = g.out_f64()
+    r = oracle_route(g)
+    check_route(g, r)
+    o, _ = moe.experts_forward(g.x_bits, r["sel_expert"], r["sel_weight"], r["sel_slot"],
+                               g.slot_bytes_fn(), H, I, shared_bytes=sb)
+    err = moe.rel_l2(out, o)
+    per = np.linalg.norm(out - o, axis=1) / np.maximum(np.linalg.norm(o, axis=1), 1e-300)
+    say(f"  rel-L2 {err:.3e}, max per token {per.max():.3e}")
+    assert err <= OUT_REL_L2 and per.max() <= TOKEN_REL_L2_MAX
 
 
 def test_layer_sparse_slots_tiled():
