@@ -245,7 +245,7 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
     hist = torch.zeros(E, dtype=torch.float64, device=dev)
     es = torch.from_numpy(es0).to(dev)
     n_arena = lay.extra["n_resident"]
-    pinned = {}
+    pins = R.PinnedCopies()
 
     def plain():
         es.copy_(torch.from_numpy(es0))
@@ -255,7 +255,7 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
     def with_hot():
         es.copy_(torch.from_numpy(es0))
         hot = R.HotReader(es0, n_arena, dev)
-        hot._pinned = pinned  # page-locked copies are made once, outside the timing
+        hot.pins = pins  # page-locked copies are made once, outside the timing
         picked = R.layer_step_hot(buf, x, w_router, bias, es, hist, arena, hot, lay.expert_bytes,
                                   stream)
         return picked, hot
@@ -274,7 +274,7 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
             times[kind].append(time.perf_counter() - t0)
     # the copy alone, timed on the side stream
     hot = R.HotReader(es0, n_arena, dev)
-    hot._pinned = pinned
+    hot.pins = pins
     src = hot.pinned(picked[0], lay.expert_bytes)   # the copy made above
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     slot = int(es0[picked[1]])
@@ -606,7 +606,7 @@ def hot_ring_cost(model, sa, buf, ws, bs, xs, s0, ring_slot0, stream, dev) -> di
         routed_ring = int((buf.sel_slot >= ring_slot0).sum())
         out = {"us_per_layer_call": us, "tokens_per_s": xs.shape[1] / (us * 1e-6)}
         if ring:
-            out.update({"picks": sum(len(v) for v in ring.picks.values()),
+            out.update({"picks": ring.n_picks,
                         "bytes_h2d": ring.bytes_copied,
                         "last_layer_assignments_on_ring_slots": routed_ring})
         return out

@@ -13,14 +13,50 @@ import torch
 from . import binding as B
 
 
-def _pin_cached(cache: dict, host: np.ndarray) -> torch.Tensor:
-    """Page-locked copy of a host byte array, made once per array object.  The
-    entry keeps the array alive, so its id names that array for as long as the
-    entry exists (two experts that share one packed array share one copy)."""
-    key = id(host)
-    if key not in cache:
-        cache[key] = (host, torch.from_numpy(np.ascontiguousarray(host)).pin_memory())
-    return cache[key][1]
+class PinnedCopies:
+    """Page-locked copies of host byte arrays for arena_load_slot, made once per
+    array object (experts that share one packed array share one copy).  An
+    entry holds its array, so the array's id names that entry for as long as it
+    lives.  Past `budget` bytes the least recently used entries are dropped,
+    each only once every copy that reads it has completed (the events recorded
+    after those copies)."""
+
+    def __init__(self, budget: int = 16 << 30):
+        from collections import OrderedDict
+        self.entries = OrderedDict()  # id(array) -> [array, page-locked copy, [events]]
+        self.bytes = 0
+        self.budget = int(budget)
+
+    def get(self, host: np.ndarray) -> torch.Tensor:
+        key = id(host)
+        e = self.entries.get(key)
+        if e is None:
+            e = [host, torch.from_numpy(np.ascontiguousarray(host)).pin_memory(), []]
+            self.entries[key] = e
+            self.bytes += e[1].numel()
+            self._trim(keep=key)
+        else:
+            self.entries.move_to_end(key)
+        return e[1]
+
+    def used_on(self, host: np.ndarray, stream) -> None:
+        """A copy reading host's page-locked copy is enqueued on `stream`."""
+        e = self.entries[id(host)]
+        e[2] = [ev for ev in e[2] if not ev.query()]
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        e[2].append(ev)
+
+    def _trim(self, keep: int) -> None:
+        for key in list(self.entries):
+            if self.bytes <= self.budget:
+                return
+            if key == keep:
+                continue
+            _, pinned, events = self.entries[key]
+            if all(ev.query() for ev in events):
+                del self.entries[key]
+                self.bytes -= pinned.numel()
 
 
 def _ws(nbytes: int, device) -> torch.Tensor | None:
@@ -147,7 +183,7 @@ class HotReader:
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
-        self._pinned = {}   # id of a host array -> (the array, its page-locked copy)
+        self.pins = PinnedCopies()
         self.ws = None   # token-pass partials of moe_hot_pick, grown to the largest batch seen
 
     def workspace(self, T: int) -> torch.Tensor:
@@ -157,10 +193,8 @@ class HotReader:
         return self.ws
 
     def pinned(self, e: int, expert_bytes_fn) -> torch.Tensor:
-        """Page-locked copy of expert e's packed bytes, made once per host
-        array; the array is held next to its copy, so its id cannot be reused
-        by another array while the entry exists."""
-        return _pin_cached(self._pinned, expert_bytes_fn(e))
+        """Page-locked copy of expert e's packed bytes (PinnedCopies)."""
+        return self.pins.get(expert_bytes_fn(e))
 
     def pick_and_load(self, buf: LayerBuffers, expert_slot_dev, hist_row, arena: Arena,
                       expert_bytes_fn, stream):
@@ -175,9 +209,11 @@ class HotReader:
         if e_star < 0 or c < 0:
             return None
         slot = int(self.es[c])
-        src = self.pinned(e_star, expert_bytes_fn)
+        host = expert_bytes_fn(e_star)
+        src = self.pins.get(host)
         B.check(B.arena_load_slot(arena.mem, arena.stride, arena.S, slot, src, arena.slot_bytes,
                                   self.side, self.done), "arena_load_slot")
+        self.pins.used_on(host, self.side)
         self.es[e_star], self.es[c] = slot, -1
         with torch.cuda.stream(stream):
             expert_slot_dev[e_star] = slot
@@ -241,7 +277,7 @@ class SharedArena:
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
-        self._pinned = {}   # id of a host array -> (the array, its page-locked copy)
+        self.pins = PinnedCopies()
 
     def upload(self, pair_bytes_fn) -> None:
         """Fill every slot with the bytes of the (layer, expert) it holds."""
@@ -249,9 +285,14 @@ class SharedArena:
         owner = {int(self.table_host[l, e]): (int(l), int(e)) for l, e in zip(l_idx, e_idx)}
         self.arena.upload(lambda s: pair_bytes_fn(*owner[s]), slots=sorted(owner))
 
-    def _pin(self, l: int, e: int, pair_bytes_fn) -> torch.Tensor:
-        """Page-locked copy of pair (l, e)'s packed bytes (one per host array)."""
-        return _pin_cached(self._pinned, pair_bytes_fn(l, e))
+    def load_pair(self, slot: int, l: int, e: int, pair_bytes_fn, stream, done_event=None) -> None:
+        """Enqueue the copy of pair (l, e)'s packed bytes into `slot` on `stream`
+        (from its page-locked copy, PinnedCopies)."""
+        host = pair_bytes_fn(l, e)
+        a = self.arena
+        B.check(B.arena_load_slot(a.mem, a.stride, a.S, slot, self.pins.get(host), a.slot_bytes,
+                                  stream, done_event), "arena_load_slot")
+        self.pins.used_on(host, stream)
 
     def replan(self, k: int, n_swap: int, pair_bytes_fn, stream=None, gain_only: bool = False):
         """Returns (evict [(l,e)], load [(l,e)]) once the copies are enqueued and
@@ -283,9 +324,8 @@ class SharedArena:
         a = self.arena
         for i in range(n):
             slot = int(self.table_host[ev[i, 0], ev[i, 1]])
-            src = self._pin(int(ld[i, 0]), int(ld[i, 1]), pair_bytes_fn)
-            B.check(B.arena_load_slot(a.mem, a.stride, a.S, slot, src, a.slot_bytes, self.side,
-                                      self.done if i == n - 1 else None), "arena_load_slot")
+            self.load_pair(slot, int(ld[i, 0]), int(ld[i, 1]), pair_bytes_fn, self.side,
+                           self.done if i == n - 1 else None)
         stream.wait_event(self.done)
         self.table_host = new
         staged = torch.from_numpy(new.copy()).pin_memory()
@@ -310,10 +350,12 @@ class HotRing:
     from step s + 2 on.  The plan is taken on the device (moe_ring_plan); the
     host only reads its few picks back -- one step late, so it never waits for
     the step it has just enqueued -- and issues arena_load_slot for each.
+    keep_picks: keep every step's picks in `picks` (tests); otherwise only their
+    count, `n_picks`, so a long serving run holds no growing log.
     """
 
     def __init__(self, sa: "SharedArena", ring_slot0: int, R: int, per_step: int,
-                 pair_bytes_fn, device):
+                 pair_bytes_fn, device, keep_picks: bool = False):
         assert 0 < per_step <= R and 2 * per_step <= R, "a plan must not wrap onto the last one"
         assert ring_slot0 + R <= sa.arena.S
         self.sa, self.slot0, self.R, self.per_step = sa, int(ring_slot0), int(R), int(per_step)
@@ -330,7 +372,9 @@ class HotRing:
         self.copied = [torch.cuda.Event() for _ in range(2)]
         self.side = torch.cuda.Stream(device)      # default priority
         self.n_copies = [0, 0]                      # copies issued for the plan in each buffer
-        self.picks = {}                             # step -> [(r, l, e)] as read back
+        self.read_through = -1                      # the last step whose plan was read back
+        self.picks = {} if keep_picks else None     # step -> [(r, l, e)], when kept
+        self.n_picks = 0
         self.bytes_copied = 0
 
     def delta_row(self, l: int) -> torch.Tensor:
@@ -364,21 +408,21 @@ class HotRing:
 
     def _copy(self, s: int) -> None:
         b = s % 2
-        if s in self.picks:
+        if s <= self.read_through:
             return
+        self.read_through = s
         self.planned[b].synchronize()            # the end of step s (already past, or nearly)
         n = int(self.plan_host[b][0])
         picks = [tuple(int(v) for v in self.plan_host[b][1 + 3 * i: 4 + 3 * i]) for i in range(n)]
-        self.picks[s] = picks
+        if self.picks is not None:
+            self.picks[s] = picks
+        self.n_picks += n
         if not picks:
             return
         self.side.wait_event(self.planned[b])    # the evicted entries are no longer read
-        a = self.sa.arena
         for r, l, e in picks:
-            src = self.sa._pin(l, e, self.pair_bytes)
-            B.check(B.arena_load_slot(a.mem, a.stride, a.S, self.slot0 + r, src, a.slot_bytes,
-                                      self.side, None), "arena_load_slot")
-            self.bytes_copied += a.slot_bytes
+            self.sa.load_pair(self.slot0 + r, l, e, self.pair_bytes, self.side)
+            self.bytes_copied += self.sa.arena.slot_bytes
         self.copied[b].record(self.side)
         self.n_copies[b] = len(picks)
 

@@ -57,7 +57,7 @@ def test_hot_ring_multi_step():
     dev = torch.device("cuda", 0)
     sa = R_.SharedArena(S, cfg.H, cfg.I, table0, dev)
     sa.upload(model.pair_bytes)
-    ring = R_.HotRing(sa, n_arena, R, PER_STEP, model.pair_bytes, dev)
+    ring = R_.HotRing(sa, n_arena, R, PER_STEP, model.pair_bytes, dev, keep_picks=True)
     buf = R_.LayerBuffers(cfg.T, cfg.H, E, cfg.k, cfg.I, S, dev)
     stream = torch.cuda.current_stream(dev)
     ws = [to_dev(l.w_router) for l in model.layers]
