@@ -13,6 +13,7 @@ this package.  The product path never calls it.
 
 Parity status per function (pins live in tests/test_oracle_*.py):
   mxfp4.decode / mxfp4.encode     pinned (exhaustive closed form, hand-worked golden blocks)
+  mxfp6.decode / mxfp6.encode     pinned (exhaustive table, hand-worked packing and ties, brute force)
   moe.router_logits               pinned (correctly rounded fsum on small shapes)
   moe.softmax / moe.renormalise   pinned (sums, closed forms, k=1)
   moe.topk / moe.masked_topk      pinned (brute force; literal miss-replacement procedure)
@@ -25,4 +26,4 @@ Parity status per function (pins live in tests/test_oracle_*.py):
   SwiGLU form: parity unpinned by the pages (fixed by the readings recorded in
   the design notes).
 """
-from . import mxfp4, moe, plan  # noqa: F401
+from . import mxfp4, mxfp6, moe, plan  # noqa: F401

@@ -28,7 +28,7 @@ import math
 
 import numpy as np
 
-from . import mxfp4
+from . import mxfp4, mxfp6
 
 
 # ----------------------------------------------------------------------------
@@ -202,10 +202,15 @@ def silu(v: np.ndarray) -> np.ndarray:
 
 
 def quantise_rows(x: np.ndarray, act: str = "mxfp4") -> np.ndarray:
-    """O9 applied along each row (act='bf16' is the no-quantiser diagnostic)."""
+    """O9 applied along each row: activations in MXFP4, or in MXFP6 (E2M3) for
+    the activation-format variant; act='bf16' is the no-quantiser diagnostic."""
     if act == "bf16":
         return np.asarray(x, dtype=np.float64)
-    return mxfp4.quantise(x)
+    if act == "mxfp4":
+        return mxfp4.quantise(x)
+    if act == "mxfp6":
+        return mxfp6.quantise(x)
+    raise ValueError(f"unknown activation format {act!r}")
 
 
 def expert_ffn(xhat: np.ndarray, weights, act: str = "mxfp4") -> np.ndarray:

@@ -129,3 +129,46 @@ def test_boot_fill_without_floor(monkeypatch):
     orig = plan.boot_fill
     monkeypatch.setattr(plan, "boot_fill", lambda h, n, k: orig(h, n, 0))
     _fails(th.test_boot_fill_hand_worked)
+
+
+# ---- MXFP6 (E2M3) ----
+import test_oracle_mxfp6 as t6  # noqa: E402
+from oracle import mxfp6  # noqa: E402
+
+
+def test_mxfp6_wrong_value(monkeypatch):
+    bad = mxfp6.VALUE.copy()
+    bad[19] = 2.625
+    monkeypatch.setattr(mxfp6, "VALUE", bad)
+    _fails(t6.test_decode_exhaustive)
+
+
+def test_mxfp6_wrong_tie_rule(monkeypatch):
+    monkeypatch.setattr(mxfp6, "_MANT_ODD", 1 - mxfp6._MANT_ODD)
+    _fails(t6.test_ties_to_even_mantissa_and_scale)
+    _fails(t6.test_bf16_window_exact_rounding)
+
+
+def test_mxfp6_element_bits_swapped(monkeypatch):
+    orig = mxfp6.pack
+
+    def pack(codes):   # the two 3-bit halves of every code exchanged
+        c = np.asarray(codes, dtype=np.uint8)
+        return orig(((c & 7) << 3) | (c >> 3))
+    monkeypatch.setattr(mxfp6, "pack", pack)
+    _fails(t6.test_packing_hand_worked)
+
+
+def test_mxfp6_scale_from_fp4_exponent(monkeypatch):
+    orig = np.frexp
+
+    class NP:  # the block exponent one too large (as if the element maximum were 2^3)
+        def __getattr__(self, k):
+            return getattr(np, k)
+
+        @staticmethod
+        def frexp(a):
+            m, e = orig(a)
+            return m, e + 1
+    monkeypatch.setattr(mxfp6, "np", NP())
+    _fails(t6.test_round_trip_every_value_at_many_scales)
