@@ -22,6 +22,8 @@ other workload, with its own time per step, roofline and CPU-oracle baseline:
            slot swaps), then 8 more steps.
 Layer workloads rotate over 4 token batches and 4 copies of the arena so the
 256 MB Infinity Cache cannot serve expert bytes reused from a previous step.
+The decode and prefill blocks also time, under "act_mxfp6", the
+activation-format variant (activation and h rows in MXFP6, same weights).
 
 Timing: W warmup steps, then K steps between two events on the launch stream
 (no other instrumentation) give `ms_per_step`.  A second run of the K steps
@@ -106,6 +108,11 @@ def expert_bytes(H: int, I: int) -> int:
 
 def row_bytes(K: int) -> int:
     return (K // 2 + K // 32 + 15) // 16 * 16
+
+
+def row6_bytes(K: int) -> int:
+    """An MXFP6 activation row: 24 code bytes and a scale byte per 32 elements."""
+    return (K // 32 * 25 + 15) // 16 * 16
 
 
 def traffic_from_profile(kernel: str, workload: str):
@@ -226,6 +233,57 @@ def gateup_roofline(gu_us: float, gu_bytes: float, gu_flops: float, args, dev) -
         roof.update(achievable_peak(roof["bound"], dev))
         roof["achievable_frac"] = roof["achieved"] / roof["achievable_peak"]
     return roof
+
+
+def act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot, arenas, hist, U,
+                     stream, steps: int, warmup: int, args, dev) -> dict:
+    """The activation-format variant on the same inputs: activation and h rows
+    in MXFP6 (E2M3), weights unchanged; every batch size on the small-batch
+    kernels.  Same step and timing protocol as the MXFP4 line."""
+    import numpy as np
+    import torch
+    from resident_expert_routing_amd import binding as B
+    from resident_expert_routing_amd import runtime as R
+    nrot = len(arenas)
+    buf = R.LayerBuffers(T, H, E, k, I, S, dev, act_format=B.MOE_ACT_MXFP6)
+
+    def step(i, ev_e=None):
+        j = i % nrot
+        R.route(buf, xs[j], w_router, bias, expert_slot, stream, hist_row=hist)
+        R.experts(buf, arenas[j].ptr(), arenas[j].stride, stream, ev_e)
+
+    for i in range(warmup):
+        step(i)
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    start, end = mk(), mk()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ev = [(mk(), mk()) for _ in range(steps)]
+    for a_, b_ in ev:
+        a_.record(stream)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(i, [None, ev[i][0], ev[i][1], None, None])
+    torch.cuda.synchronize()
+    gu_us = float(np.mean([a_.elapsed_time(b_) for a_, b_ in ev])) * 1e3
+    A = T * k
+    u_steps = [U[i % nrot] for i in range(steps)]
+    gu_bytes = float(np.mean([u * gateup_bytes_per_slot(H, I) for u in u_steps])) \
+        + T * row6_bytes(H) + A * row6_bytes(I)
+    roof = gateup_roofline(gu_us, gu_bytes, 4.0 * H * I * A, args, dev)
+    out = {"value": T * steps / (total_ms * 1e-3), "unit": "tokens/s", "steps": steps,
+           "ms_per_step": total_ms / steps, "dtype": "mxfp4 weights x mxfp6 activations",
+           "roofline": {**roof, "kernel": "gateup_kernel", "algo_bytes_per_launch": gu_bytes,
+                        "mean_launch_us": gu_us}}
+    log(f"  MXFP6 activations: {total_ms / steps * 1e3:.1f} us/step, gate/up {gu_us:.1f} us "
+        f"({roof['frac']:.3f} of peak {roof['unit']})")
+    return out
 
 
 def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5):
@@ -422,6 +480,10 @@ def layer_workload(name: str, args, dev, steps: int, warmup: int) -> dict:
     if name == "long":
         block["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
                                             stream)
+    if name in ("decode", "prefill"):
+        block["act_mxfp6"] = act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot,
+                                              arenas, hist, U, stream, K, min(warmup, 5), args,
+                                              dev)
     del arenas
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -679,7 +741,7 @@ def main():
         "data": "synthetic",
         "config": head["config"],
     }
-    for key in ("roofline", "layer", "replan", "hot_read", "cpu_baseline"):
+    for key in ("roofline", "layer", "replan", "hot_read", "act_mxfp6", "cpu_baseline"):
         if key in head:
             result[key] = head[key]
     if len(names) > 1:

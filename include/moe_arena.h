@@ -38,6 +38,15 @@
  *               to the even mantissa, saturation at +-6, sign bit copied from
  *               the input, and scale byte 0 with all-zero codes for a block
  *               whose amax is 0.
+ *   MXFP6 row : the activation-format variant (act_format = MOE_ACT_MXFP6):
+ *               K/32 blocks of 24 bytes of E2M3 codes (code = sign<<5 |
+ *               exponent<<3 | mantissa, exponent bias 1; element i of a block
+ *               at bits [6i, 6i+6) of its 24 bytes read as one little-endian
+ *               number -- the operand layout of the block-scaled matrix
+ *               instruction), followed, at byte 3K/4, by the K/32 E8M0 scale
+ *               bytes; moe_act_row_bytes(K, MOE_ACT_MXFP6) bytes (padded to
+ *               16).  Encoded like MXFP4 activation rows (same X, OCP MX v1.0
+ *               FP6 E2M3 values, saturation at +-7.5).
  *   slot      : one SwiGLU expert, six sections, each starting on a 256-byte
  *               boundary (offsets from moe_slot_sections):
  *                 gate codes [I][H/2] | gate scales [I][H/32] |
@@ -79,6 +88,7 @@ extern "C" {
 #define MOE_OP_EXPERTS 2
 #define MOE_OP_HOT_PICK 3
 #define MOE_OP_EXPERTS_SHARED 4  /* moe_experts_forward with a shared expert */
+#define MOE_OP_ACT_MXFP6 0x10    /* or-ed into MOE_OP_EXPERTS(_SHARED): act_format MXFP6 */
 
 #define MOE_MAX_E 1024
 #define MOE_MAX_K 32
@@ -93,6 +103,18 @@ const char* moe_status_string(int status);
 /* Bytes of one MXFP4 row of K elements (K % 32 == 0): K/2 + K/32 rounded up to 16. */
 size_t moe_mxfp4_row_bytes(int K);
 
+/* Activation formats (moe_route_args.act_format, moe_experts_args.act_format):
+ * the activation rows xq and the experts' intermediate rows h in MXFP4 (the
+ * default) or in MXFP6 (E2M3 elements: the activation-format variant; better
+ * accuracy, 1.5x the activation bytes).  The weights are MXFP4 either way. */
+#define MOE_ACT_MXFP4 0
+#define MOE_ACT_MXFP6 1
+
+/* Bytes of one activation row of K elements in a format: moe_mxfp4_row_bytes(K)
+ * or 3K/4 + K/32 rounded up to 16 (MXFP6); 0 for K not a positive multiple of
+ * 32 or an unknown format. */
+size_t moe_act_row_bytes(int K, int act_format);
+
 /* Byte size of one packed expert slot (the slot format above); 0 if H or I is
  * not a positive multiple of 32. */
 size_t moe_slot_bytes(int H, int I);
@@ -103,8 +125,10 @@ size_t moe_slot_bytes(int H, int I);
 int moe_slot_sections(int H, int I, size_t* out6);
 
 /* Workspace bytes an operation needs for the given shape (0 if none; the
- * workspace pointer may then be NULL).  op is one of MOE_OP_*.  Unused
- * arguments are ignored.  Returns (size_t)-1 for an invalid op or shape. */
+ * workspace pointer may then be NULL).  op is one of MOE_OP_*; for the
+ * experts' MXFP6 activation variant, MOE_OP_EXPERTS or MOE_OP_EXPERTS_SHARED
+ * or-ed with MOE_OP_ACT_MXFP6.  Unused arguments are ignored.  Returns
+ * (size_t)-1 for an invalid op or shape. */
 size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
 
 /*
@@ -154,7 +178,7 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *          zero); expert_slot [E] int32.
  * Outputs: topk_expert, sel_expert, sel_slot [T][k] int32; topk_score,
  *          sel_weight [T][k] float; slot_offsets [S+1] int32; perm [T*k] int32;
- *          xq [T][moe_mxfp4_row_bytes(H)] uint8 (16-byte aligned).
+ *          xq [T][moe_act_row_bytes(H, act_format)] uint8 (16-byte aligned).
  * Workspace: moe_workspace_bytes(MOE_OP_ROUTE, T, H, E, k, 0, S) bytes, 256-byte
  *          aligned.  Contents on return are unspecified, except the router's
  *          dot products (see reuse_logits).
@@ -186,6 +210,9 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  *          bf16-instruction values except for the tokens recomputed exactly).
  *          With reuse_logits the selection certifies the stored values again
  *          against the new routable set.
+ * act_format: MOE_ACT_MXFP4 (xq rows in MXFP4) or MOE_ACT_MXFP6 (MXFP6 rows,
+ *          for the experts' activation-format variant); anything else is
+ *          MOE_EINVAL.
  */
 #define MOE_STAGE_EVENTS 5
 
@@ -209,6 +236,7 @@ typedef struct moe_route_args {
   double* hist_row;
   float* delta;
   int reuse_logits;
+  int act_format;
 } moe_route_args;
 
 int moe_route(const moe_route_args* args, hipStream_t stream);
@@ -257,6 +285,12 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  *          pick, in float32, before the one rounding to bf16.  With it, the
  *          workspace is moe_workspace_bytes(MOE_OP_EXPERTS_SHARED, ...) and
  *          the call runs even when S == 0.
+ * act_format: the format of xq (as moe_route wrote it) and of h.  With
+ *          MOE_ACT_MXFP6 the products take E2M3 activations against the MXFP4
+ *          weights (the block-scaled instruction at the E2M1 x E2M3 setting;
+ *          g, u and y otherwise as above, h encoded as an MXFP6 row) and every
+ *          batch size runs on the small-batch kernels; H and I must be
+ *          multiples of 512 (else MOE_EUNSUPPORTED).  Other values: MOE_EINVAL.
  *
  * Inputs : xq, slot_offsets, perm, sel_slot, sel_weight as written by moe_route
  *          for the same T, k, S; arena (256-byte aligned), slot_stride (multiple
@@ -264,7 +298,8 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  *          never dereferenced.
  * Output : out [T][H] bf16.
  * Workspace: moe_workspace_bytes(MOE_OP_EXPERTS, T, H, 0, k, I, S) bytes
- *          (MOE_OP_EXPERTS_SHARED with a shared expert).
+ *          (MOE_OP_EXPERTS_SHARED with a shared expert; either or-ed with
+ *          MOE_OP_ACT_MXFP6 when act_format is MOE_ACT_MXFP6).
  * Any copy into a slot the call reads (arena_load_slot) must be ordered before
  * it: by the caller (hipStreamWaitEvent on the load's event), or, for one
  * slot, through defer_slot.
@@ -302,6 +337,7 @@ typedef struct moe_experts_args {
   int defer_slot;
   hipEvent_t defer_event;
   const uint8_t* shared_expert;
+  int act_format;
 } moe_experts_args;
 
 int moe_experts_forward(const moe_experts_args* args, hipStream_t stream);
@@ -316,7 +352,7 @@ int moe_experts_forward(const moe_experts_args* args, hipStream_t stream);
  * calls no allocating routine; the array's device address is looked up once
  * per device (on the first call made with that device current) and reused.
  * `stream` must belong to the current device.
- * Limit: batches whose moe_workspace_bytes(MOE_OP_EXPERTS, ...) exceeds
+ * Limit: batches whose moe_workspace_bytes(...) for the call's op exceeds
  * MOE_NOALLOC_SCRATCH_BYTES are refused with MOE_ESCRATCH before any HIP call
  * (for example up to 900 assignments T*k at H = 4096: decode batches).
  * Every call on one GPU uses the same array and leaves its contents there:

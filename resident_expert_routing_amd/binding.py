@@ -30,6 +30,9 @@ MOE_OP_DEMAND = 1
 MOE_OP_EXPERTS = 2
 MOE_OP_HOT_PICK = 3
 MOE_OP_EXPERTS_SHARED = 4
+MOE_OP_ACT_MXFP6 = 0x10
+MOE_ACT_MXFP4 = 0
+MOE_ACT_MXFP6 = 1
 MOE_MAX_E = 1024
 MOE_MAX_K = 32
 MOE_MAX_S = 8192
@@ -37,7 +40,8 @@ MOE_MAX_RING_PAIRS = 16384
 MOE_MAX_RING = 1024
 MOE_MAX_RING_PER_STEP = 64
 
-EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_slot_bytes", "moe_slot_sections",
+EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_act_row_bytes", "moe_slot_bytes",
+           "moe_slot_sections",
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
            "moe_experts_forward_noalloc", "moe_ring_plan", "moe_ring_install",
            "moe_history_save", "moe_history_load", "moe_boot_plan", "moe_history_scale",
@@ -61,7 +65,8 @@ class RouteArgs(ctypes.Structure):
                 ("slot_offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
                 ("xq", ctypes.c_void_p), ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
                 ("stage_events", ctypes.c_void_p), ("hist_row", ctypes.c_void_p),
-                ("delta", ctypes.c_void_p), ("reuse_logits", ctypes.c_int)]
+                ("delta", ctypes.c_void_p), ("reuse_logits", ctypes.c_int),
+                ("act_format", ctypes.c_int)]
 
 
 class ExpertsArgs(ctypes.Structure):
@@ -73,7 +78,8 @@ class ExpertsArgs(ctypes.Structure):
                 ("sel_weight", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
                 ("stage_events", ctypes.c_void_p), ("defer_slot", ctypes.c_int),
-                ("defer_event", ctypes.c_void_p), ("shared_expert", ctypes.c_void_p)]
+                ("defer_event", ctypes.c_void_p), ("shared_expert", ctypes.c_void_p),
+                ("act_format", ctypes.c_int)]
 
 
 MOE_STAGE_EVENTS = 5
@@ -99,6 +105,8 @@ def load() -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_mxfp4_row_bytes.argtypes = [i]
     lib.moe_mxfp4_row_bytes.restype = sz
+    lib.moe_act_row_bytes.argtypes = [i, i]
+    lib.moe_act_row_bytes.restype = sz
     lib.moe_slot_bytes.argtypes = [i, i]
     lib.moe_slot_bytes.restype = sz
     lib.moe_slot_sections.argtypes = [i, i, ctypes.POINTER(sz)]
@@ -204,6 +212,10 @@ def moe_mxfp4_row_bytes(K: int) -> int:
     return int(load().moe_mxfp4_row_bytes(int(K)))
 
 
+def moe_act_row_bytes(K: int, act_format: int) -> int:
+    return int(load().moe_act_row_bytes(int(K), int(act_format)))
+
+
 def moe_slot_bytes(H: int, I: int) -> int:
     return int(load().moe_slot_bytes(int(H), int(I)))
 
@@ -223,13 +235,13 @@ def moe_workspace_bytes(op: int, T: int, H: int, E: int, k: int, I: int, S: int)
 def moe_route(T, H, E, k, S, x, w_router, bias, expert_slot, topk_expert, topk_score,
               sel_expert, sel_weight, sel_slot, slot_offsets, perm, xq, ws, ws_bytes,
               stream=None, stage_events=None, hist_row=None, delta=None,
-              reuse_logits=False) -> int:
+              reuse_logits=False, act_format=MOE_ACT_MXFP4) -> int:
     keep, evp = _events(stage_events)
     a = RouteArgs(int(T), int(H), int(E), int(k), int(S), _ptr(x), _ptr(w_router), _ptr(bias),
                   _ptr(expert_slot), _ptr(topk_expert), _ptr(topk_score), _ptr(sel_expert),
                   _ptr(sel_weight), _ptr(sel_slot), _ptr(slot_offsets), _ptr(perm), _ptr(xq),
                   _ptr(ws), int(ws_bytes), evp, _ptr(hist_row), _ptr(delta),
-                  1 if reuse_logits else 0)
+                  1 if reuse_logits else 0, int(act_format))
     return int(load().moe_route(ctypes.byref(a), _stream(stream)))
 
 
@@ -242,25 +254,26 @@ def moe_demand_accumulate(topk_expert, topk_score, T, k, E, hist_row, delta, ws,
 
 def moe_experts_forward(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm, sel_slot,
                         sel_weight, out, ws, ws_bytes, stream=None, stage_events=None,
-                        defer_slot=-1, defer_event=None, shared_expert=None) -> int:
+                        defer_slot=-1, defer_event=None, shared_expert=None,
+                        act_format=MOE_ACT_MXFP4) -> int:
     keep, evp = _events(stage_events)
     a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
                     int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
                     _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp,
-                    int(defer_slot), _event(defer_event), _ptr(shared_expert))
+                    int(defer_slot), _event(defer_event), _ptr(shared_expert), int(act_format))
     return int(load().moe_experts_forward(ctypes.byref(a), _stream(stream)))
 
 
 def moe_experts_forward_noalloc(T, H, I, k, S, xq, arena, slot_stride, slot_offsets, perm,
                                 sel_slot, sel_weight, out, stream=None, stage_events=None,
                                 defer_slot=-1, defer_event=None, ws=None, ws_bytes=0,
-                                shared_expert=None) -> int:
+                                shared_expert=None, act_format=MOE_ACT_MXFP4) -> int:
     """moe_experts_forward with the library's own scratch (ws must stay None / 0)."""
     keep, evp = _events(stage_events)
     a = ExpertsArgs(int(T), int(H), int(I), int(k), int(S), _ptr(xq), _ptr(arena),
                     int(slot_stride), _ptr(slot_offsets), _ptr(perm), _ptr(sel_slot),
                     _ptr(sel_weight), _ptr(out), _ptr(ws), int(ws_bytes), evp,
-                    int(defer_slot), _event(defer_event), _ptr(shared_expert))
+                    int(defer_slot), _event(defer_event), _ptr(shared_expert), int(act_format))
     return int(load().moe_experts_forward_noalloc(ctypes.byref(a), _stream(stream)))
 
 

@@ -6,7 +6,7 @@
 
 size_t moe_route_ws_bytes_internal(int T, int H, int E, int S);
 size_t moe_demand_ws_bytes_internal(int T, int E);
-size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S, bool shared);
+size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S, bool shared, int fmt);
 size_t moe_hot_pick_ws_bytes_internal(int T);
 
 using namespace moe;
@@ -33,6 +33,12 @@ extern "C" MOE_EXPORT size_t moe_mxfp4_row_bytes(int K) {
   return mxfp4_row_bytes(K);
 }
 
+extern "C" MOE_EXPORT size_t moe_act_row_bytes(int K, int act_format) {
+  if (K <= 0 || K % 32 != 0) return 0;
+  if (act_format != MOE_ACT_MXFP4 && act_format != MOE_ACT_MXFP6) return 0;
+  return act_row_bytes(K, act_format);
+}
+
 extern "C" MOE_EXPORT size_t moe_slot_bytes(int H, int I) {
   if (H <= 0 || I <= 0 || H % 32 != 0 || I % 32 != 0) return 0;
   return slot_layout(H, I).total;
@@ -50,6 +56,10 @@ extern "C" MOE_EXPORT size_t moe_workspace_bytes(int op, int T, int H, int E, in
                                                  int S) {
   const size_t bad = (size_t)-1;
   if (T < 0) return bad;
+  // MOE_OP_ACT_MXFP6 selects the MXFP6 activation rows of the experts' workspace
+  const int fmt = (op & MOE_OP_ACT_MXFP6) ? MOE_ACT_MXFP6 : MOE_ACT_MXFP4;
+  op &= ~MOE_OP_ACT_MXFP6;
+  if (fmt == MOE_ACT_MXFP6 && op != MOE_OP_EXPERTS && op != MOE_OP_EXPERTS_SHARED) return bad;
   switch (op) {
     case MOE_OP_ROUTE:
       if (H <= 0 || E <= 0 || H % 32 != 0) return bad;
@@ -60,7 +70,7 @@ extern "C" MOE_EXPORT size_t moe_workspace_bytes(int op, int T, int H, int E, in
     case MOE_OP_EXPERTS:
     case MOE_OP_EXPERTS_SHARED:
       if (H <= 0 || I <= 0 || k <= 0 || S < 0 || H % 32 != 0 || I % 32 != 0) return bad;
-      return moe_experts_ws_bytes_internal(T, H, k, I, S, op == MOE_OP_EXPERTS_SHARED);
+      return moe_experts_ws_bytes_internal(T, H, k, I, S, op == MOE_OP_EXPERTS_SHARED, fmt);
     case MOE_OP_HOT_PICK:
       return moe_hot_pick_ws_bytes_internal(T);
     default:

@@ -25,6 +25,21 @@ inline size_t mxfp4_row_bytes(int K) {
   return up_to((size_t)K / 2 + (size_t)K / 32, 16);
 }
 
+// MXFP6 (E2M3) activation rows: 24 code bytes per 32-element block, then the
+// scale bytes; padded to 16.
+inline size_t mxfp6_row_bytes(int K) {
+  return up_to((size_t)K / 32 * 24 + (size_t)K / 32, 16);
+}
+
+// Byte offset of the scale bytes in an activation row of K elements.
+__host__ __device__ inline size_t act_scale_offset(int K, int fmt) {
+  return fmt == MOE_ACT_MXFP6 ? (size_t)K / 32 * 24 : (size_t)K / 2;
+}
+
+inline size_t act_row_bytes(int K, int fmt) {
+  return fmt == MOE_ACT_MXFP6 ? mxfp6_row_bytes(K) : mxfp4_row_bytes(K);
+}
+
 struct SlotLayout {
   size_t off[6];
   size_t total;
@@ -93,6 +108,26 @@ __device__ __forceinline__ uint32_t e2m1_code(float v, int e) {
   uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
                (a >= 3.5f) + (a > 5.0f);
   return m | ((__float_as_uint(v) >> 31) << 3);
+}
+
+// E2M3 code of v / 2^e (OCP MX FP6 E2M3: sign | 2 exponent bits, bias 1 |
+// 3 mantissa bits): nearest value with ties to the even mantissa, magnitudes
+// above 7.5 saturating; sign bit copied from v.  Within a binade the grid is
+// uniform with 8 steps, so the mantissa is the binade offset times 8 rounded
+// half to even (exact: a power-of-two scaling and a subtraction in the same
+// binade); a round-up to 8 is the next binade's first value.
+__device__ __forceinline__ uint32_t e2m3_code(float v, int e) {
+  const float a = fabsf(__builtin_amdgcn_ldexpf(v, -e));
+  uint32_t mag;
+  if (a < 1.0f) {
+    mag = (uint32_t)__builtin_rintf(a * 8.0f);                 // subnormal: m / 8 (8 -> 1.0)
+  } else {
+    const int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // 0..2 (a < 8)
+    const float m = (__builtin_amdgcn_ldexpf(a, -E) - 1.0f) * 8.0f;
+    mag = (uint32_t)(E + 1) * 8u + (uint32_t)__builtin_rintf(m);
+  }
+  mag = mag > 31u ? 31u : mag;
+  return mag | ((__float_as_uint(v) >> 31) << 5);
 }
 
 // ---------------------------------------------------------------------------

@@ -32,6 +32,7 @@
 #include <hip/hip_ext.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -134,6 +135,73 @@ __device__ __forceinline__ void load_row_sc(const uint8_t* codes, const uint8_t*
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP6 (E2M3) activation operands of the small-batch kernels: a block of 32
+// elements is 24 bytes, element i at bits [6i, 6i+6) -- the six-register
+// operand of the block-scaled instruction with the E2M3 format (lane -> row and
+// K group as for E2M1, pinned by a probe on the hardware).
+// ---------------------------------------------------------------------------
+struct RowSC6 {
+  uint32_t q[4][6];
+  uint32_t s[4];
+};
+
+__device__ __forceinline__ v4f mfma_fp4x6(const uint4& a, const uint32_t (&b)[6], v4f c,
+                                          uint32_t sa, uint32_t sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], 0, 0};
+  // cbsz = 4: A (weights) E2M1; blgp = 2: B (activations) E2M3
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 2, 0, (int)sa, 0,
+                                                          (int)sb);
+}
+
+__device__ __forceinline__ v4f mfma_superchunk(const RowSC& a, const RowSC6& b, v4f c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = mfma_fp4x6(a.q[i], b.q[i], c, a.s[i], b.s[i]);
+  return c;
+}
+
+__device__ __forceinline__ void zero_sc(RowSC6& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 6; ++j) r.q[i][j] = 0u;
+    r.s[i] = 127u;
+  }
+}
+
+// This lane's code blocks 16sc+g, +4, +8, +12 of an MXFP6 row (24 bytes each,
+// 8-byte aligned).
+__device__ __forceinline__ void load_codes6(const uint8_t* codes, int sc, int g, RowSC6& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint2* q = reinterpret_cast<const uint2*>(codes + (size_t)(16 * sc + 4 * i + g) * 24);
+    const uint2 a = q[0], b = q[1], c = q[2];
+    r.q[i][0] = a.x;
+    r.q[i][1] = a.y;
+    r.q[i][2] = b.x;
+    r.q[i][3] = b.y;
+    r.q[i][4] = c.x;
+    r.q[i][5] = c.y;
+  }
+}
+
+__device__ __forceinline__ void split_scales(const uint4 sv, int g, RowSC6& r) {
+  const int sh = 8 * g;
+  r.s[0] = sv.x >> sh;
+  r.s[1] = sv.y >> sh;
+  r.s[2] = sv.z >> sh;
+  r.s[3] = sv.w >> sh;
+}
+
+// Super-chunk sc of an MXFP6 row whose length is a multiple of 512 (scales
+// 16-byte aligned at `scales`).
+__device__ __forceinline__ void load_row_sc6(const uint8_t* codes, const uint8_t* scales, int sc,
+                                             int g, RowSC6& r) {
+  load_codes6(codes, sc, g, r);
+  split_scales(*reinterpret_cast<const uint4*>(scales + sc * 16), g, r);
+}
+
 // SwiGLU of one column of a wave's 32 rows of I and its MXFP4 encoding
 // (16x16x128 result layout).  Lane (c = lane&15, g) holds rows n0+4g+v (tile
 // 0) and n0+16+4g+v (tile 1) of gate (ag*) and up (au*) for column c; the 32
@@ -169,6 +237,45 @@ __device__ __forceinline__ void swiglu_quant_store16(const v4f& ag0, const v4f& 
     *reinterpret_cast<uint16_t*>(hr + n0 / 2 + 2 * g) = w0;
     *reinterpret_cast<uint16_t*>(hr + n0 / 2 + 8 + 2 * g) = w1;
     if (g == 0) hr[I / 2 + n0 / 32] = (uint8_t)scale;
+  }
+}
+
+// The same SwiGLU column encoded as an MXFP6 row: rows n0+4g.. are elements
+// 4g..4g+3 of the block (bytes 3g..3g+2 of its 24), rows n0+16+4g.. bytes
+// 12+3g..; the scale byte at 3I/4 + n0/32.
+__device__ __forceinline__ void swiglu_quant_store16_fp6(const v4f& ag0, const v4f& ag1,
+                                                         const v4f& au0, const v4f& au1, int g,
+                                                         uint8_t* hr, int n0, int I) {
+  float h[8];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    h[v] = silu_mul(ag0[v], au0[v]);
+    h[4 + v] = silu_mul(ag1[v], au1[v]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(h[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  uint32_t codes[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  uint32_t scale = 0u;
+  if (amax > 0.f) {
+    const int e = mx_block_exp(amax);
+    scale = (uint32_t)(e + 127);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) codes[i] = e2m3_code(h[i], e);
+  }
+  if (hr) {
+    const uint32_t w0 = codes[0] | (codes[1] << 6) | (codes[2] << 12) | (codes[3] << 18);
+    const uint32_t w1 = codes[4] | (codes[5] << 6) | (codes[6] << 12) | (codes[7] << 18);
+    uint8_t* b = hr + (size_t)(n0 / 32) * 24 + 3 * g;
+    b[0] = (uint8_t)w0;
+    b[1] = (uint8_t)(w0 >> 8);
+    b[2] = (uint8_t)(w0 >> 16);
+    b[12] = (uint8_t)w1;
+    b[13] = (uint8_t)(w1 >> 8);
+    b[14] = (uint8_t)(w1 >> 16);
+    if (g == 0) hr[(size_t)I / 32 * 24 + n0 / 32] = (uint8_t)scale;
   }
 }
 
@@ -393,8 +500,11 @@ struct GateUpArgs {
   int maxU;               // work item maxU is the shared expert's (rows A .. A+T, token p - A)
 };
 
-template <bool FULL>
+// FP6: activations and h in MXFP6 (FULL only).
+template <bool FULL, bool FP6>
 __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
+  static_assert(FULL || !FP6, "MXFP6 activations need whole super-chunks");
+  using XRow = typename std::conditional<FP6, RowSC6, RowSC>::type;
   const int nbps = p.I / 32;
   const int u = blockIdx.x / nbps, nb = blockIdx.x - u * nbps;
   // the shared expert's item: slot id S (never a routed slot), rows A .. A+T
@@ -464,23 +574,29 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
     const uint8_t* xc = t >= 0 ? p.xq + (size_t)t * p.xrow : nullptr;
     v4f ag0 = {0.f, 0.f, 0.f, 0.f}, ag1 = ag0, au0 = ag0, au1 = ag0;
     for (int sc = 0; sc < nsc; ++sc) {
-      RowSC wg0, wg1, wu0, wu1, x;
+      RowSC wg0, wg1, wu0, wu1;
+      XRow x;
       load_row_sc<FULL>(gc0, gs0, sc, g, nblk, wg0);
       load_row_sc<FULL>(gc1, gs1, sc, g, nblk, wg1);
       load_row_sc<FULL>(uc0, us0, sc, g, nblk, wu0);
       load_row_sc<FULL>(uc1, us1, sc, g, nblk, wu1);
-      if (xc)
-        load_row_sc<FULL>(xc, xc + H / 2, sc, g, nblk, x);
-      else
+      if (!xc)
         zero_sc(x);
+      else if constexpr (FP6)
+        load_row_sc6(xc, xc + act_scale_offset(H, MOE_ACT_MXFP6), sc, g, x);
+      else
+        load_row_sc<FULL>(xc, xc + H / 2, sc, g, nblk, x);
       ag0 = mfma_superchunk(wg0, x, ag0);
       ag1 = mfma_superchunk(wg1, x, ag1);
       au0 = mfma_superchunk(wu0, x, au0);
       au1 = mfma_superchunk(wu1, x, au1);
     }
     const int pcol = cb + (lane & 15);
-    swiglu_quant_store16(ag0, ag1, au0, au1, g,
-                         pcol < p1 ? p.hq + (size_t)pcol * p.hrow : nullptr, n0, p.I);
+    uint8_t* hr = pcol < p1 ? p.hq + (size_t)pcol * p.hrow : nullptr;
+    if constexpr (FP6)
+      swiglu_quant_store16_fp6(ag0, ag1, au0, au1, g, hr, n0, p.I);
+    else
+      swiglu_quant_store16(ag0, ag1, au0, au1, g, hr, n0, p.I);
   };
   int cb = p0;
   if constexpr (FULL) {
@@ -509,8 +625,11 @@ struct DownArgs {
   int H, I, A, S;
 };
 
-template <bool FULL>
+// FP6: h rows in MXFP6 (FULL only).
+template <bool FULL, bool FP6>
 __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
+  static_assert(FULL || !FP6, "MXFP6 activations need whole super-chunks");
+  using XRow = typename std::conditional<FP6, RowSC6, RowSC>::type;
   const int nbps = (p.H + 63) / 64;
   const int u = blockIdx.x / nbps, nb = blockIdx.x - u * nbps;
   // one round trip: the gate/up kernel of this call found the slot
@@ -541,7 +660,7 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
     ds[tl] = FULL ? wscale + (row - n0) * sstr : base + p.off_ds + (size_t)row * srow;
   }
   RowSC pre[4];  // FULL: super-chunk 0 codes of the first column block, loaded early
-  RowSC prex;    // FULL: and of its activation rows (codes; scale bytes in prexs)
+  XRow prex;     // FULL: and of its activation rows (codes; scale bytes in prexs)
   uint4 prexs;
   if (FULL) {
     // Issued before the staging waits, so they are in flight together.
@@ -550,8 +669,12 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
       if (tv[tl]) load_codes_full(dc[tl], 0, g, pre[tl]);
     if (p0 + r < p1) {
       const uint8_t* hc = p.hq + (size_t)(p0 + r) * p.hrow;
-      load_codes_full(hc, 0, g, prex);
-      prexs = *reinterpret_cast<const uint4*>(hc + I / 2);
+      if constexpr (FP6)
+        load_codes6(hc, 0, g, prex);
+      else
+        load_codes_full(hc, 0, g, prex);
+      prexs = *reinterpret_cast<const uint4*>(hc + act_scale_offset(I, FP6 ? MOE_ACT_MXFP6
+                                                                             : MOE_ACT_MXFP4));
     } else {
       zero_sc(prex);
       prexs = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);  // scale 1
@@ -585,11 +708,13 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
       sc0 = 1;
     }
     for (int sc = sc0; sc < nsc; ++sc) {
-      RowSC x;
-      if (hc)
-        load_row_sc<FULL>(hc, hc + I / 2, sc, g, nblk, x);
-      else
+      XRow x;
+      if (!hc)
         zero_sc(x);
+      else if constexpr (FP6)
+        load_row_sc6(hc, hc + act_scale_offset(I, MOE_ACT_MXFP6), sc, g, x);
+      else
+        load_row_sc<FULL>(hc, hc + I / 2, sc, g, nblk, x);
 #pragma unroll
       for (int tl = 0; tl < 4; ++tl) {
         if (tv[tl]) {
@@ -1176,8 +1301,11 @@ constexpr int kPipeMinA = 2048;
 
 enum Family { kFamSmall, kFamPipe };
 
-static Family family_of(int T, int k, int H, int I) {
-  if ((size_t)T * k >= (size_t)kPipeMinA && H % 512 == 0 && I % 512 == 0) return kFamPipe;
+// MXFP6 activations run on the small-batch kernels at every batch size.
+static Family family_of(int T, int k, int H, int I, int fmt) {
+  if (fmt == MOE_ACT_MXFP4 && (size_t)T * k >= (size_t)kPipeMinA && H % 512 == 0 &&
+      I % 512 == 0)
+    return kFamPipe;
   return kFamSmall;
 }
 
@@ -1192,11 +1320,11 @@ static size_t shared_tiles(int T, bool shared) {
   return shared ? (size_t)(T + kTileM - 1) / kTileM : 0;
 }
 
-static ExpertsWs experts_ws(int T, int H, int k, int I, int S, bool shared) {
+static ExpertsWs experts_ws(int T, int H, int k, int I, int S, bool shared, int fmt) {
   ExpertsWs w;
   const size_t A = (size_t)T * k;
   const size_t rows = A + (shared ? (size_t)T : 0);  // hq and y: routed rows, then shared ones
-  const Family fam = family_of(T, k, H, I);
+  const Family fam = family_of(T, k, H, I, fmt);
   const bool tiled = fam != kFamSmall;
   w.items_off = 0;
   // pipelined: the M-tile list, then the deferred slot's (first item, item
@@ -1208,14 +1336,14 @@ static ExpertsWs experts_ws(int T, int H, int k, int I, int S, bool shared) {
                              : 3 * nwork * sizeof(int32_t);
   w.zero_off = up_to(w.items_off + items, 256);
   w.hq_off = w.zero_off + (tiled ? kZeroPage : 0);
-  w.y_off = up_to(w.hq_off + rows * mxfp4_row_bytes(I), 256);
+  w.y_off = up_to(w.hq_off + rows * act_row_bytes(I, fmt), 256);
   w.total = up_to(w.y_off + rows * (size_t)H * sizeof(float), 256);
   return w;
 }
 
-size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S, bool shared) {
+size_t moe_experts_ws_bytes_internal(int T, int H, int k, int I, int S, bool shared, int fmt) {
   if (T <= 0) return 0;
-  return experts_ws(T, H, k, I, S, shared).total;
+  return experts_ws(T, H, k, I, S, shared, fmt).total;
 }
 
 // Shape checks shared by both entry points (no HIP call).
@@ -1225,6 +1353,10 @@ static int experts_check_shape(const moe_experts_args* a) {
   if (T < 0 || H <= 0 || I <= 0 || k <= 0 || S < 0) return MOE_EINVAL;
   if (H % 32 != 0 || I % 32 != 0 || k > MOE_MAX_K || S > MOE_MAX_S) return MOE_EUNSUPPORTED;
   if ((size_t)T * k > (size_t)INT32_MAX) return MOE_EINVAL;
+  if (a->act_format != MOE_ACT_MXFP4 && a->act_format != MOE_ACT_MXFP6) return MOE_EINVAL;
+  // MXFP6 rows run on the whole-super-chunk kernels only
+  if (a->act_format == MOE_ACT_MXFP6 && (!staged_ok(H) || !staged_ok(I)))
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -1243,12 +1375,13 @@ static int experts_validate(const moe_experts_args* a, const void* ws, size_t ws
   if (!aligned(a->xq, 16) || !aligned(a->arena, 256) || !aligned(a->out, 8)) return MOE_EINVAL;
   const bool shared = a->shared_expert != nullptr;
   if (!aligned(a->shared_expert, 256)) return MOE_EINVAL;
-  const ExpertsWs W = experts_ws(T, H, k, I, S, shared);
+  const int fmt = a->act_format;
+  const ExpertsWs W = experts_ws(T, H, k, I, S, shared, fmt);
   if (ws_bytes < W.total) return MOE_EWORKSPACE;
   if (!ws || !aligned(ws, 256)) return MOE_EINVAL;
   const int defer = a->defer_slot;
   if (defer < -1 || defer >= S || (defer >= 0 && !a->defer_event)) return MOE_EINVAL;
-  if (family_of(T, k, H, I) != kFamSmall) {
+  if (family_of(T, k, H, I, fmt) != kFamSmall) {
     const size_t ntile = max_tiles((size_t)T * k, S, kTileM) + shared_tiles(T, shared);
     if (up_to(ntile * (size_t)((I + 127) / 128), 8) > 0x7FFFFFFFu ||
         up_to(ntile * (size_t)((H + 255) / 256), 8) > 0x7FFFFFFFu)
@@ -1263,10 +1396,11 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
   if (T == 0) return MOE_OK;
   const SlotLayout L = slot_layout(H, I);
   const bool shared = a->shared_expert != nullptr;
-  const ExpertsWs W = experts_ws(T, H, k, I, S, shared);
+  const int fmt = a->act_format;
+  const ExpertsWs W = experts_ws(T, H, k, I, S, shared, fmt);
   const int defer = a->defer_slot;
   const int A = T * k;
-  const Family fam = family_of(T, k, H, I);
+  const Family fam = family_of(T, k, H, I, fmt);
   const size_t ntile = max_tiles((size_t)A, S, kTileM) + shared_tiles(T, shared);
   // N-tiles: gate/up 128 rows of I, down 256 rows of H
   const int nN1 = (I + 127) / 128;
@@ -1350,7 +1484,7 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     if (!record_stage(ev, 0, stream)) return MOE_EHIP;
     GateUpArgs g;
     g.xq = a->xq;
-    g.xrow = mxfp4_row_bytes(H);
+    g.xrow = act_row_bytes(H, fmt);
     g.arena = a->arena;
     g.stride = a->slot_stride;
     g.off_gc = L.off[0];
@@ -1363,7 +1497,7 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     int32_t* slots = reinterpret_cast<int32_t*>(ws + W.items_off);
     g.slots = slots;
     g.hq = hq;
-    g.hrow = mxfp4_row_bytes(I);
+    g.hrow = act_row_bytes(I, fmt);
     g.T = T;
     g.H = H;
     g.I = I;
@@ -1375,12 +1509,16 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     const int nwork = maxU + (shared ? 1 : 0);  // the shared expert's item last
     const int gblocks = nwork * (I / 32);
     hipEvent_t gu0 = ev ? ev[1] : nullptr, gu1 = ev ? ev[2] : nullptr;
-    if (staged_ok(H))
-      hipExtLaunchKernelGGL(gateup_kernel<true>, dim3(gblocks), dim3(kWave),
-                            2 * 32 * staged_scale_stride(H), stream, gu0, gu1, 0, g);
+    const size_t glds = 2 * 32 * staged_scale_stride(H);
+    if (fmt == MOE_ACT_MXFP6)  // validated: staged_ok(H) and staged_ok(I)
+      hipExtLaunchKernelGGL(gateup_kernel<true, true>, dim3(gblocks), dim3(kWave), glds, stream,
+                            gu0, gu1, 0, g);
+    else if (staged_ok(H))
+      hipExtLaunchKernelGGL(gateup_kernel<true, false>, dim3(gblocks), dim3(kWave), glds, stream,
+                            gu0, gu1, 0, g);
     else
-      hipExtLaunchKernelGGL(gateup_kernel<false>, dim3(gblocks), dim3(kWave), 0, stream, gu0, gu1,
-                            0, g);
+      hipExtLaunchKernelGGL(gateup_kernel<false, false>, dim3(gblocks), dim3(kWave), 0, stream,
+                            gu0, gu1, 0, g);
     DownArgs d;
     d.hq = hq;
     d.hrow = g.hrow;
@@ -1398,10 +1536,13 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     d.S = S;
     d.shared = a->shared_expert;
     const int dblocks = nwork * ((H + 63) / 64);
-    if (staged_ok(I))
-      down_kernel<true><<<dblocks, kWave, 64 * staged_scale_stride(I), stream>>>(d);
+    const size_t dlds = 64 * staged_scale_stride(I);
+    if (fmt == MOE_ACT_MXFP6)
+      down_kernel<true, true><<<dblocks, kWave, dlds, stream>>>(d);
+    else if (staged_ok(I))
+      down_kernel<true, false><<<dblocks, kWave, dlds, stream>>>(d);
     else
-      down_kernel<false><<<dblocks, kWave, 0, stream>>>(d);
+      down_kernel<false, false><<<dblocks, kWave, 0, stream>>>(d);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   }
   // a workgroup covers 256 threads x YRow<YT>::kEl elements of a token's row; the
@@ -1462,7 +1603,8 @@ extern "C" MOE_EXPORT int moe_experts_forward_noalloc(const moe_experts_args* a,
   if (r != MOE_OK) return r;
   if (a->ws || a->ws_bytes) return MOE_EINVAL;  // the workspace is the library's own
   if (a->T == 0) return MOE_OK;
-  const size_t need = experts_ws(a->T, a->H, a->k, a->I, a->S, a->shared_expert != nullptr).total;
+  const size_t need =
+      experts_ws(a->T, a->H, a->k, a->I, a->S, a->shared_expert != nullptr, a->act_format).total;
   if (need > kNoAllocScratch) return MOE_ESCRATCH;
   // every other check, against a stand-in for the scratch (256-aligned, not read)
   r = experts_validate(a, reinterpret_cast<const void*>(uintptr_t{256}), kNoAllocScratch);

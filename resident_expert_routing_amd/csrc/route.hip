@@ -17,31 +17,52 @@ namespace moe {
 // runs of chunk sums) and router_full_f64 (the float64 matrix instruction).
 // ---------------------------------------------------------------------------
 
-// MXFP4 activation rows, one element per thread: each aligned group of 32
-// threads encodes one block (amax by shuffles within the group), even lanes
-// write a byte of two codes, lane 0 the scale.  gid and gstride are multiples
-// of 32 and T*H is a multiple of 32, so a group is always whole.
+// Activation rows, one element per thread: each aligned group of 32 threads
+// encodes one block (amax by shuffles within the group).  MXFP4: even lanes
+// write a byte of two codes; MXFP6: every fourth lane writes the 3 bytes of
+// four codes.  Lane 0 writes the scale.  gid and gstride are multiples of 32
+// and T*H is a multiple of 32, so a group is always whole.
 __device__ void quantize_x_elements(const uint16_t* __restrict__ x, int T, int H,
                                     uint8_t* __restrict__ xq, size_t xq_row, size_t gid,
-                                    size_t gstride) {
+                                    size_t gstride, int fmt) {
   const size_t n = (size_t)T * H;
+  const size_t sc_off = act_scale_offset(H, fmt);
   for (size_t q = gid; q < n; q += gstride) {
     const int t = (int)(q / H), h = (int)(q % H);
     const float v = bf16_to_f32(x[q]);
     float a = fabsf(v);
 #pragma unroll
     for (int d = 16; d >= 1; d >>= 1) a = fmaxf(a, __shfl_xor(a, d, 32));
-    uint32_t code = 0u, scale = 0u;
-    if (a > 0.f) {
-      const int e = mx_block_exp(a);
-      code = e2m1_code(v, e);
-      scale = (uint32_t)(e + 127);
-    }
-    const uint32_t odd = __shfl_down(code, 1, 32);
     const int li = (int)(q & 31);
     uint8_t* row = xq + (size_t)t * xq_row;
-    if ((li & 1) == 0) row[h / 2] = (uint8_t)(code | (odd << 4));
-    if (li == 0) row[H / 2 + h / 32] = (uint8_t)scale;
+    uint32_t scale = 0u;
+    if (fmt == MOE_ACT_MXFP6) {
+      uint32_t code = 0u;
+      if (a > 0.f) {
+        const int e = mx_block_exp(a);
+        code = e2m3_code(v, e);
+        scale = (uint32_t)(e + 127);
+      }
+      const uint32_t c1 = __shfl_down(code, 1, 32), c2 = __shfl_down(code, 2, 32),
+                     c3 = __shfl_down(code, 3, 32);
+      if ((li & 3) == 0) {
+        const uint32_t w = code | (c1 << 6) | (c2 << 12) | (c3 << 18);  // elements li..li+3
+        uint8_t* dst = row + (size_t)(h / 32) * 24 + (li / 4) * 3;
+        dst[0] = (uint8_t)w;
+        dst[1] = (uint8_t)(w >> 8);
+        dst[2] = (uint8_t)(w >> 16);
+      }
+    } else {
+      uint32_t code = 0u;
+      if (a > 0.f) {
+        const int e = mx_block_exp(a);
+        code = e2m1_code(v, e);
+        scale = (uint32_t)(e + 127);
+      }
+      const uint32_t odd = __shfl_down(code, 1, 32);
+      if ((li & 1) == 0) row[h / 2] = (uint8_t)(code | (odd << 4));
+    }
+    if (li == 0) row[sc_off + h / 32] = (uint8_t)scale;
   }
 }
 
@@ -127,11 +148,12 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
                                                         const float* __restrict__ w, int T, int H,
                                                         int E, double* __restrict__ z,
                                                         uint8_t* __restrict__ xq, size_t xq_row,
-                                                        int nrb, uint32_t* __restrict__ counter) {
+                                                        int fmt, int nrb,
+                                                        uint32_t* __restrict__ counter) {
   if (counter && blockIdx.x == 0 && threadIdx.x == 0) *counter = 0u;
   if ((int)blockIdx.x >= nrb) {
     quantize_x_elements(x, T, H, xq, xq_row, (size_t)(blockIdx.x - nrb) * 256 + threadIdx.x,
-                        (size_t)(gridDim.x - nrb) * 256);
+                        (size_t)(gridDim.x - nrb) * 256, fmt);
     return;
   }
   const int ntg = (T + RS_T - 1) / RS_T;
@@ -680,6 +702,7 @@ struct SelectArgs {
   uint8_t* xq;
   size_t xq_row;
   int quantize_x;   // encode the activation row here (else the router kernel did)
+  int act_format;   // MOE_ACT_MXFP4 or MOE_ACT_MXFP6
   double* hist;     // nullable: demand accumulated by the one-workgroup kernel
   float* delta;
   // Logits from router_bf16x3 (nullable otherwise): token t is appended to
@@ -730,14 +753,18 @@ __device__ __forceinline__ void select_write_routed(const SelectArgs& p, int t, 
   }
 }
 
-// MXFP4 activation row of token t (when p.quantize_x): lane per 32-block.
-// Returns ||x_t||^2 (float64 sums of exact squares, wave-uniform), or -1 when
-// the row was not read.
+// Activation row of token t (when p.quantize_x): lane per 32-block, MXFP4 or
+// MXFP6 (FP6; the kernels are instantiated per format, so each keeps the
+// registers of its own encoder).  Returns ||x_t||^2 (float64 sums of exact squares,
+// wave-uniform), or -1 when the row was not read.
+template <bool FP6>
 __device__ __forceinline__ double quantize_row(const SelectArgs& p, int t) {
   if (!p.quantize_x) return -1.0;
   const int lane = threadIdx.x & 63;
   const int H = p.H;
   const int nblk = H / 32;
+  constexpr bool fp6 = FP6;
+  const size_t sc_off = act_scale_offset(H, FP6 ? MOE_ACT_MXFP6 : MOE_ACT_MXFP4);
   const uint16_t* xr = p.x + (size_t)t * H;
   uint8_t* qr = p.xq + (size_t)t * p.xq_row;
   double sq = 0.0;
@@ -760,17 +787,35 @@ __device__ __forceinline__ double quantize_row(const SelectArgs& p, int t) {
       amax = fmaxf(amax, fabsf(v[i]));
       sq += (double)v[i] * (double)v[i];
     }
-    uint32_t words[4] = {0u, 0u, 0u, 0u};
     uint32_t scale = 0u;
-    if (amax > 0.f) {
-      const int e = mx_block_exp(amax);
-      scale = (uint32_t)(e + 127);
+    if constexpr (fp6) {
+      uint32_t words[6] = {0u, 0u, 0u, 0u, 0u, 0u};  // element i at bits [6i, 6i+6)
+      if (amax > 0.f) {
+        const int e = mx_block_exp(amax);
+        scale = (uint32_t)(e + 127);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) words[i >> 3] |= e2m1_code(v[i], e) << (4 * (i & 7));
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t c = e2m3_code(v[i], e);
+          words[(6 * i) >> 5] |= c << ((6 * i) & 31);
+          if (((6 * i) & 31) > 26) words[((6 * i) >> 5) + 1] |= c >> (32 - ((6 * i) & 31));
+        }
+      }
+      uint2* dst = reinterpret_cast<uint2*>(qr + (size_t)b * 24);  // 8-byte aligned
+      dst[0] = make_uint2(words[0], words[1]);
+      dst[1] = make_uint2(words[2], words[3]);
+      dst[2] = make_uint2(words[4], words[5]);
+    } else {
+      uint32_t words[4] = {0u, 0u, 0u, 0u};
+      if (amax > 0.f) {
+        const int e = mx_block_exp(amax);
+        scale = (uint32_t)(e + 127);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) words[i >> 3] |= e2m1_code(v[i], e) << (4 * (i & 7));
+      }
+      *reinterpret_cast<uint4*>(qr + (size_t)b * 16) =
+          make_uint4(words[0], words[1], words[2], words[3]);
     }
-    *reinterpret_cast<uint4*>(qr + (size_t)b * 16) =
-        make_uint4(words[0], words[1], words[2], words[3]);
-    qr[H / 2 + b] = (uint8_t)scale;
+    qr[sc_off + b] = (uint8_t)scale;
   }
   return wave_sum(sq);
 }
@@ -840,7 +885,7 @@ __device__ void certify_token(const SelectArgs& p, int t, const double* z, uint3
 constexpr int kSelDemand = 1, kSelRouted = 2, kSelBoth = 3;
 
 // One wave, token t.  Activation rows are encoded too when p.quantize_x.
-template <int NPER>
+template <int NPER, bool FP6>
 __device__ void select_token(const SelectArgs& p, int t, int role) {
   const int lane = threadIdx.x & 63;
   const int E = p.E, k = p.k;
@@ -936,19 +981,20 @@ __device__ void select_token(const SelectArgs& p, int t, int role) {
   }
   if (do_m) select_write_routed<NPER>(p, t, msel, got, ex, denom, slot_of);
   double xn2 = -1.0;
-  if (role & kSelRouted) xn2 = quantize_row(p, t);
+  if (role & kSelRouted) xn2 = quantize_row<FP6>(p, t);
   if (p.flags && role == kSelBoth) certify_token<NPER>(p, t, z, valid, routable, usel, msel, xn2);
 }
 
-template <int NPER>
+template <int NPER, bool FP6>
 __global__ __launch_bounds__(256) void route_select(SelectArgs p) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (!p.tlist) {
-    if (i < p.T) select_token<NPER>(p, i, kSelBoth);  // wave-uniform
+    if (i < p.T) select_token<NPER, FP6>(p, i, kSelBoth);  // wave-uniform
     return;
   }
   const int n = p.tlist[0];  // a fixed grid walks the list
-  for (int j = i; j < n; j += gridDim.x * 4) select_token<NPER>(p, p.tlist[1 + j], kSelBoth);
+  for (int j = i; j < n; j += gridDim.x * 4)
+    select_token<NPER, FP6>(p, p.tlist[1 + j], kSelBoth);
 }
 
 // ---------------------------------------------------------------------------
@@ -1040,7 +1086,8 @@ __global__ __launch_bounds__(256) void route_fused(SelectArgs p, uint32_t* __res
   if (p.hist && tid < E) h_old = p.hist[tid];  // used only by the last workgroup
   // waves 2j and 2j+1: demand and routed picks of token kFusedWgTokens*b + j
   const int t = blockIdx.x * kFusedWgTokens + (tid >> 7);
-  if (t < T) select_token<4>(p, t, (tid >> 6) & 1 ? kSelRouted : kSelDemand);
+  // the small router encodes x (quantize_x is 0 here): the MXFP4 instance serves both formats
+  if (t < T) select_token<4, false>(p, t, (tid >> 6) & 1 ? kSelRouted : kSelDemand);
   __threadfence();  // this workgroup's picks, visible device-wide before it counts itself
   __syncthreads();
   if (tid == 0) last = atomicAdd(counter, 1u) == gridDim.x - 1;
@@ -1333,6 +1380,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   if ((size_t)T * k > (size_t)INT32_MAX || (size_t)T * H > ((size_t)1 << 40)) return MOE_EINVAL;
   if (!a->slot_offsets) return MOE_EINVAL;
   if (a->hist_row && !aligned(a->hist_row, 8)) return MOE_EINVAL;
+  if (a->act_format != MOE_ACT_MXFP4 && a->act_format != MOE_ACT_MXFP6) return MOE_EINVAL;
   if (T > 0) {
     if (!a->x || !a->w_router || !a->expert_slot || !a->topk_expert || !a->topk_score ||
         !a->sel_expert || !a->sel_weight || !a->sel_slot || !a->perm || !a->xq)
@@ -1353,7 +1401,8 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   double* z = static_cast<double*>(a->ws);
   void* dws = static_cast<uint8_t*>(a->ws) + route_z_bytes(T, E);
   const int nchunk = H / kRouterChunk;
-  const size_t xq_row = mxfp4_row_bytes(H);
+  const int fmt = a->act_format;
+  const size_t xq_row = act_row_bytes(H, fmt);
   const bool small_router = T <= kSplitRouterMaxT && nchunk <= RS_MAX_CHUNKS;
   // the fused kernel's completion counter: the first word of the bucket-count
   // area, which that path does not use otherwise
@@ -1384,7 +1433,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     const size_t nx = ((size_t)T * H + 255) / 256;
     const int nxb = (int)(nx < 1024 ? nx : 1024);
     router_small_f64<<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, a->xq, xq_row,
-                                                    nrb, fused ? counter : nullptr);
+                                                    fmt, nrb, fused ? counter : nullptr);
   } else if (approx) {
     split_w_bf16x3<<<E, 256, 0, stream>>>(a->w_router, E, H, planes, wnorm2, flags);
     router_bf16x3<<<dim3((E + RB_E - 1) / RB_E, (T + RB_MT - 1) / RB_MT, ks), RB_THREADS, 0,
@@ -1412,6 +1461,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
   p.xq = a->xq;
   p.xq_row = xq_row;
   p.quantize_x = (small_router || a->reuse_logits) ? 0 : 1;
+  p.act_format = fmt;
   p.hist = nullptr;
   p.delta = nullptr;
   p.flags = approx ? flags : nullptr;
@@ -1432,10 +1482,17 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
       if (!record_stage(ev,i, stream)) return MOE_EHIP;
     return hip_status();
   }
-  if (E <= 256)
-    route_select<4><<<(T + 3) / 4, 256, 0, stream>>>(p);
-  else
-    route_select<16><<<(T + 3) / 4, 256, 0, stream>>>(p);
+  const bool fp6 = fmt == MOE_ACT_MXFP6;
+  auto launch_select = [&](unsigned nwg) {
+    if (E <= 256) {
+      if (fp6) route_select<4, true><<<nwg, 256, 0, stream>>>(p);
+      else route_select<4, false><<<nwg, 256, 0, stream>>>(p);
+    } else {
+      if (fp6) route_select<16, true><<<nwg, 256, 0, stream>>>(p);
+      else route_select<16, false><<<nwg, 256, 0, stream>>>(p);
+    }
+  };
+  launch_select((unsigned)((T + 3) / 4));
   if (approx) {
     // the flagged tokens: exact float64 logits, then their picks again (the
     // grids are sized for every token; workgroups past the list leave at once)
@@ -1446,10 +1503,7 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     p.tlist = flags;
     p.quantize_x = 0;
     const int nwg = (T + 3) / 4 < 512 ? (T + 3) / 4 : 512;
-    if (E <= 256)
-      route_select<4><<<nwg, 256, 0, stream>>>(p);
-    else
-      route_select<16><<<nwg, 256, 0, stream>>>(p);
+    launch_select((unsigned)nwg);
   }
   if (a->hist_row) {
     const int st = moe_demand_launch_internal(a->topk_expert, a->topk_score, T, k, E, a->hist_row,

@@ -77,6 +77,7 @@ class LayerBuffers:
     S: int
     device: torch.device
     shared: bool = False    # workspace for a shared expert too
+    act_format: int = 0     # B.MOE_ACT_MXFP4 or B.MOE_ACT_MXFP6 (xq and h rows)
 
     def __post_init__(self):
         T, H, E, k, I, S, dev = self.T, self.H, self.E, self.k, self.I, self.S, self.device
@@ -89,14 +90,18 @@ class LayerBuffers:
         self.sel_slot = torch.empty((T, k), **i32)
         self.slot_offsets = torch.empty(S + 1, **i32)
         self.perm = torch.empty(T * k, **i32)
-        self.xq_row = B.moe_mxfp4_row_bytes(H)
+        self.xq_row = B.moe_act_row_bytes(H, self.act_format)
+        if self.xq_row == 0:
+            raise ValueError(f"activation format {self.act_format} with H={H}")
         self.xq = torch.empty((T, self.xq_row), dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, H), dtype=torch.int16, device=dev)  # bf16 bits
         self.delta = torch.empty(E, **f32)
         self.ws_route_bytes = B.moe_workspace_bytes(B.MOE_OP_ROUTE, T, H, E, k, I, S)
         self.ws_demand_bytes = B.moe_workspace_bytes(B.MOE_OP_DEMAND, T, H, E, k, I, S)
-        self.ws_experts_bytes = B.moe_workspace_bytes(
-            B.MOE_OP_EXPERTS_SHARED if self.shared else B.MOE_OP_EXPERTS, T, H, E, k, I, S)
+        op = B.MOE_OP_EXPERTS_SHARED if self.shared else B.MOE_OP_EXPERTS
+        if self.act_format == B.MOE_ACT_MXFP6:
+            op |= B.MOE_OP_ACT_MXFP6
+        self.ws_experts_bytes = B.moe_workspace_bytes(op, T, H, E, k, I, S)
         self.ws_route = _ws(self.ws_route_bytes, dev)
         self.ws_demand = _ws(self.ws_demand_bytes, dev)
         self.ws_experts = _ws(self.ws_experts_bytes, dev)
@@ -142,7 +147,8 @@ def route(buf: LayerBuffers, x, w_router, bias, expert_slot, stream=None,
     B.check(B.moe_route(buf.T, buf.H, buf.E, buf.k, buf.S, x, w_router, bias, expert_slot,
                         buf.topk_expert, buf.topk_score, buf.sel_expert, buf.sel_weight,
                         buf.sel_slot, buf.slot_offsets, buf.perm, buf.xq, buf.ws_route,
-                        buf.ws_route_bytes, stream, stage_events, hist_row, delta, reuse_logits),
+                        buf.ws_route_bytes, stream, stage_events, hist_row, delta, reuse_logits,
+                        buf.act_format),
             "moe_route")
 
 
@@ -161,7 +167,7 @@ def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None,
                                   slot_stride, buf.slot_offsets, buf.perm, buf.sel_slot,
                                   buf.sel_weight, buf.out, buf.ws_experts, buf.ws_experts_bytes,
                                   stream, stage_events, defer_slot, defer_event,
-                                  shared_expert),
+                                  shared_expert, buf.act_format),
             "moe_experts_forward")
 
 

@@ -28,7 +28,7 @@ def to_dev(a, dtype=None):
 class GpuLayer:
     """One workload layer on the device: inputs, arena, buffers."""
 
-    def __init__(self, lay, T=None, x_bits=None, expert_slot=None, arena=None):
+    def __init__(self, lay, T=None, x_bits=None, expert_slot=None, arena=None, act_format=0):
         import torch
         from resident_expert_routing_amd import runtime as R
         self.lay = lay
@@ -43,7 +43,8 @@ class GpuLayer:
         self.w_router = to_dev(lay.w_router)
         self.bias = to_dev(lay.bias)
         self.expert_slot = to_dev(self.expert_slot_np.astype(np.int32))
-        self.buf = R.LayerBuffers(self.T, self.H, self.E, self.k, self.I, self.S, device())
+        self.buf = R.LayerBuffers(self.T, self.H, self.E, self.k, self.I, self.S, device(),
+                                  act_format=act_format)
         if arena is None:
             lay.prepack()
             arena = R.Arena(self.S, self.H, self.I, device())

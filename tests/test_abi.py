@@ -63,6 +63,21 @@ def test_layout_helpers_match_documented_format():
         B.moe_slot_sections(64, 48)
 
 
+def test_activation_row_bytes():
+    """MXFP4 rows as moe_mxfp4_row_bytes; MXFP6 rows 24 code bytes per block of
+    32 then a scale byte per block, padded to 16."""
+    from oracle import mxfp6
+    assert B.moe_act_row_bytes(4096, B.MOE_ACT_MXFP4) == B.moe_mxfp4_row_bytes(4096)
+    for K in (32, 96, 512, 2048, 4096, 7168):
+        want = (mxfp6.row_bytes(K) + 15) // 16 * 16
+        assert B.moe_act_row_bytes(K, B.MOE_ACT_MXFP6) == want
+    assert B.moe_act_row_bytes(4096, B.MOE_ACT_MXFP6) == 3200
+    assert B.moe_act_row_bytes(100, B.MOE_ACT_MXFP6) == 0
+    assert B.moe_act_row_bytes(0, B.MOE_ACT_MXFP4) == 0
+    assert B.moe_act_row_bytes(4096, 2) == 0
+    assert B.moe_act_row_bytes(4096, -1) == 0
+
+
 def test_workspace_sizes():
     ws = B.moe_workspace_bytes
     assert ws(B.MOE_OP_ROUTE, 0, 4096, 256, 8, 0, 230) == 0
@@ -83,6 +98,16 @@ def test_workspace_sizes():
     e = ws(B.MOE_OP_EXPERTS, 8, 4096, 0, 8, 2048, 230)
     assert e >= 64 * (1088 + 4096 * 4) and e % 256 == 0
     assert ws(7, 8, 4096, 256, 8, 2048, 230) == (1 << 64) - 1
+    # MXFP6 activations: h rows of 3I/4 + I/32 bytes; the flag only with the experts ops
+    f6 = ws(B.MOE_OP_EXPERTS | B.MOE_OP_ACT_MXFP6, 8, 4096, 0, 8, 2048, 230)
+    assert f6 >= 64 * (1600 + 4096 * 4) and f6 > e and f6 % 256 == 0
+    assert ws(B.MOE_OP_EXPERTS_SHARED | B.MOE_OP_ACT_MXFP6, 8, 4096, 0, 8, 2048, 230) >= \
+        72 * (1600 + 4096 * 4)
+    assert ws(B.MOE_OP_ROUTE | B.MOE_OP_ACT_MXFP6, 8, 4096, 256, 8, 0, 230) == (1 << 64) - 1
+    # the pipelined family's tile list is absent for MXFP6 (small-batch kernels only)
+    big4 = ws(B.MOE_OP_EXPERTS, 4096, 4096, 0, 8, 2048, 166)
+    big6 = ws(B.MOE_OP_EXPERTS | B.MOE_OP_ACT_MXFP6, 4096, 4096, 0, 8, 2048, 166)
+    assert big6 > 0 and big4 > 0
     assert ws(B.MOE_OP_ROUTE, 8, 100, 256, 8, 0, 230) == (1 << 64) - 1
 
 
@@ -111,6 +136,8 @@ def _route(**kw):
     (dict(ws=None), B.MOE_EINVAL),
     (dict(x=FAKE + 2), B.MOE_EINVAL),
     (dict(xq=FAKE + 8), B.MOE_EINVAL),
+    (dict(act_format=2), B.MOE_EINVAL),
+    (dict(act_format=-1), B.MOE_EINVAL),
 ])
 def test_route_rejects(kw, code):
     assert _route(**kw) == code
@@ -156,6 +183,10 @@ def _experts(**kw):
     (dict(defer_slot=10), B.MOE_EINVAL),
     (dict(defer_slot=-2), B.MOE_EINVAL),
     (dict(defer_slot=3), B.MOE_EINVAL),  # a deferred slot needs an event
+    (dict(act_format=2), B.MOE_EINVAL),
+    (dict(act_format=B.MOE_ACT_MXFP6), B.MOE_EUNSUPPORTED),  # H, I not multiples of 512
+    (dict(act_format=B.MOE_ACT_MXFP6, H=512, I=512, slot_stride=B.moe_slot_bytes(512, 512),
+          ws_bytes=100), B.MOE_EWORKSPACE),
 ])
 def test_experts_rejects(kw, code):
     assert _experts(**kw) == code
