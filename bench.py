@@ -203,19 +203,31 @@ def achievable_peak(bound: str, dev) -> dict:
         _PEAKS[bound] = {"achievable_peak": best, "achievable_how": "moe_test_stream_read: 3 "
                          "reads of 8 GiB back to back, best of 3"}
         return _PEAKS[bound]
+    _PEAKS[bound] = {"achievable_peak": mfma_loop_rate(dev, 0),
+                     "achievable_how": "moe_test_mfma_loop: 32x32x64 MXFP4 instruction, 8 chains "
+                     "per wave, best of 6 launches"}
+    return _PEAKS[bound]
+
+
+def mfma_loop_rate(dev, act_format: int) -> float:
+    """TFLOP/s of the 32x32x64 block-scaled instruction loop, E2M1 A operands
+    and E2M1 (0) or E2M3 (1) B operands; best of 6 launches."""
+    import torch
+    from resident_expert_routing_amd import binding as B
+    mk = lambda: torch.cuda.Event(enable_timing=True)
     iters, grid = 1000, 1024
     sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
     flops = grid * 4 * iters * 8 * 2.0 * 32 * 32 * 64
+    best = 0.0
     for _ in range(6):
         e0, e1 = mk(), mk()
         e0.record()
-        B.check(B.moe_test_mfma_loop(iters, sink, grid), "moe_test_mfma_loop")
+        B.check(B.moe_test_mfma_loop(iters, sink, grid, act_format=act_format),
+                "moe_test_mfma_loop")
         e1.record()
         torch.cuda.synchronize()
         best = max(best, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
-    _PEAKS[bound] = {"achievable_peak": best, "achievable_how": "moe_test_mfma_loop: 32x32x64 "
-                     "MXFP4 instruction, 8 chains per wave, best of 6 launches"}
-    return _PEAKS[bound]
+    return best
 
 
 def gateup_roofline(gu_us: float, gu_bytes: float, gu_flops: float, args, dev) -> dict:
@@ -281,6 +293,9 @@ def act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot, arenas, 
            "ms_per_step": total_ms / steps, "dtype": "mxfp4 weights x mxfp6 activations",
            "roofline": {**roof, "kernel": "gateup_kernel", "algo_bytes_per_launch": gu_bytes,
                         "mean_launch_us": gu_us}}
+    if not args.no_peaks:   # the instruction's rate with E2M3 against E2M1 B operands
+        out["mfma_loop_tflops"] = {"e2m1_x_e2m1": mfma_loop_rate(dev, 0),
+                                   "e2m1_x_e2m3": mfma_loop_rate(dev, 1)}
     log(f"  MXFP6 activations: {total_ms / steps * 1e3:.1f} us/step, gate/up {gu_us:.1f} us "
         f"({roof['frac']:.3f} of peak {roof['unit']})")
     return out

@@ -570,16 +570,17 @@ int moe_test_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid
 
 /*
  * moe_test_mfma_loop -- test-only microbenchmark: the achievable rate of the
- * v_mfma_scale_f32_32x32x64_f8f6f4 instruction with E2M1 operands (the
- * pipelined expert kernels' instruction).  `grid` workgroups of 256 threads;
+ * v_mfma_scale_f32_32x32x64_f8f6f4 instruction (the pipelined expert kernels'
+ * instruction) with E2M1 A and, by act_format, E2M1 (MOE_ACT_MXFP4) or E2M3
+ * (MOE_ACT_MXFP6) B operands.  `grid` workgroups of 256 threads;
  * every wave runs `iters` rounds of 8 independent accumulator chains (one
  * instruction each, 2*32*32*64 flops), so the launch does
  * grid * 4 * iters * 8 * 131072 flops; each thread writes the sum of its
  * accumulators to sink[workgroup * 256 + thread].  sink: device memory of
- * grid * 256 floats.  MOE_EINVAL for a null sink, iters outside [1, 1<<20] or
- * grid outside [1, 65536].
+ * grid * 256 floats.  MOE_EINVAL for a null sink, iters outside [1, 1<<20],
+ * grid outside [1, 65536] or an unknown act_format.
  */
-int moe_test_mfma_loop(int iters, float* sink, int grid, hipStream_t stream);
+int moe_test_mfma_loop(int iters, int act_format, float* sink, int grid, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -144,7 +144,7 @@ def load() -> ctypes.CDLL:
     lib.moe_test_mxfp4_probe.restype = i
     lib.moe_test_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i, vp]
     lib.moe_test_stream_read.restype = i
-    lib.moe_test_mfma_loop.argtypes = [i, vp, i, vp]
+    lib.moe_test_mfma_loop.argtypes = [i, i, vp, i, vp]
     lib.moe_test_mfma_loop.restype = i
     _lib = lib
     return lib
@@ -350,5 +350,6 @@ def moe_test_stream_read(src, nbytes, sink, grid, stream=None) -> int:
                                            _stream(stream)))
 
 
-def moe_test_mfma_loop(iters, sink, grid, stream=None) -> int:
-    return int(load().moe_test_mfma_loop(int(iters), _ptr(sink), int(grid), _stream(stream)))
+def moe_test_mfma_loop(iters, sink, grid, stream=None, act_format=MOE_ACT_MXFP4) -> int:
+    return int(load().moe_test_mfma_loop(int(iters), int(act_format), _ptr(sink), int(grid),
+                                         _stream(stream)))

@@ -53,12 +53,15 @@ __global__ __launch_bounds__(256) void stream_read(const uint4* __restrict__ src
   sink[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
-// Achievable MXFP4 matrix rate: 8 independent 32x32x64 accumulator chains per
-// wave; the operands come from the lane index, so nothing folds away.
+// Achievable block-scaled matrix rate: 8 independent 32x32x64 accumulator
+// chains per wave; A in E2M1, B in E2M1 or (FP6) E2M3; the operands come from
+// the lane index, so nothing folds away.
+template <bool FP6>
 __global__ __launch_bounds__(256) void mfma_loop(int iters, float* __restrict__ sink) {
   const int l = threadIdx.x;
   const pv8i A = {l, l + 1, l + 2, l + 3, 0, 0, 0, 0};
-  const pv8i B = {3 * l, l ^ 5, l + 7, l ^ 9, 0, 0, 0, 0};
+  const pv8i B = {3 * l, l ^ 5, l + 7, l ^ 9, FP6 ? l + 11 : 0, FP6 ? l ^ 13 : 0, 0, 0};
+  constexpr int kBfmt = FP6 ? 2 : 4;  // blgp: E2M3 or E2M1
   pv16f c[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
@@ -67,7 +70,8 @@ __global__ __launch_bounds__(256) void mfma_loop(int iters, float* __restrict__ 
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c[j], 4, 4, 0, 100 + j, 0, 120);
+      c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c[j], 4, kBfmt, 0, 100 + j, 0,
+                                                             120);
   }
   float s = 0.f;
 #pragma unroll
@@ -87,9 +91,14 @@ extern "C" MOE_EXPORT int moe_test_stream_read(const void* src, size_t bytes, ui
   return moe::hip_status();
 }
 
-extern "C" MOE_EXPORT int moe_test_mfma_loop(int iters, float* sink, int grid, hipStream_t stream) {
+extern "C" MOE_EXPORT int moe_test_mfma_loop(int iters, int act_format, float* sink, int grid,
+                                             hipStream_t stream) {
   if (!sink || iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536) return MOE_EINVAL;
-  moe::mfma_loop<<<grid, 256, 0, stream>>>(iters, sink);
+  if (act_format != MOE_ACT_MXFP4 && act_format != MOE_ACT_MXFP6) return MOE_EINVAL;
+  if (act_format == MOE_ACT_MXFP6)
+    moe::mfma_loop<true><<<grid, 256, 0, stream>>>(iters, sink);
+  else
+    moe::mfma_loop<false><<<grid, 256, 0, stream>>>(iters, sink);
   return moe::hip_status();
 }
 

@@ -223,6 +223,7 @@ def test_probe_rejects():
     assert B.moe_test_mfma_loop(10, None, 4) == B.MOE_EINVAL
     assert B.moe_test_mfma_loop(0, FAKE, 4) == B.MOE_EINVAL
     assert B.moe_test_mfma_loop(10, FAKE, 70000) == B.MOE_EINVAL
+    assert B.moe_test_mfma_loop(10, FAKE, 4, act_format=2) == B.MOE_EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

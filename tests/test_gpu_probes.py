@@ -26,16 +26,17 @@ def test_stream_read_reads_every_word_once():
     assert got == want
 
 
-def test_mfma_loop_accumulates():
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_mfma_loop_accumulates(fmt):
     import torch
     from resident_expert_routing_amd import binding as B
     grid = 2
     dev = torch.device("cuda", 0)
     s1 = torch.empty(grid * 256, dtype=torch.float32, device=dev)
     s2 = torch.empty_like(s1)
-    say("mfma_loop with 1 and 2 rounds")
-    B.check(B.moe_test_mfma_loop(1, s1, grid), "moe_test_mfma_loop")
-    B.check(B.moe_test_mfma_loop(2, s2, grid), "moe_test_mfma_loop")
+    say(f"mfma_loop with 1 and 2 rounds, B format {fmt}")
+    B.check(B.moe_test_mfma_loop(1, s1, grid, act_format=fmt), "moe_test_mfma_loop")
+    B.check(B.moe_test_mfma_loop(2, s2, grid, act_format=fmt), "moe_test_mfma_loop")
     torch.cuda.synchronize()
     a, b = s1.cpu().numpy(), s2.cpu().numpy()
     assert np.isfinite(a).all() and np.abs(a).sum() > 0
