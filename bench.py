@@ -22,7 +22,7 @@ other workload, with its own time per step, roofline and CPU-oracle baseline:
            slot swaps), then 8 more steps.
 Layer workloads rotate over 4 token batches and 4 copies of the arena so the
 256 MB Infinity Cache cannot serve expert bytes reused from a previous step.
-The decode and prefill blocks also time, under "act_mxfp6", the
+The decode, prefill and long blocks also time, under "act_mxfp6", the
 activation-format variant (activation and h rows in MXFP6, same weights).
 
 Timing: W warmup steps, then K steps between two events on the launch stream
@@ -289,9 +289,10 @@ def act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot, arenas, 
     gu_bytes = float(np.mean([u * gateup_bytes_per_slot(H, I) for u in u_steps])) \
         + T * row6_bytes(H) + A * row6_bytes(I)
     roof = gateup_roofline(gu_us, gu_bytes, 4.0 * H * I * A, args, dev)
+    kernel = "gateup_pipe6" if gateup_kernel_name(T, k, H, I) == "gateup_pipe" else "gateup_kernel"
     out = {"value": T * steps / (total_ms * 1e-3), "unit": "tokens/s", "steps": steps,
            "ms_per_step": total_ms / steps, "dtype": "mxfp4 weights x mxfp6 activations",
-           "roofline": {**roof, "kernel": "gateup_kernel", "algo_bytes_per_launch": gu_bytes,
+           "roofline": {**roof, "kernel": kernel, "algo_bytes_per_launch": gu_bytes,
                         "mean_launch_us": gu_us}}
     if not args.no_peaks:   # the instruction's rate with E2M3 against E2M1 B operands
         out["mfma_loop_tflops"] = {"e2m1_x_e2m1": mfma_loop_rate(dev, 0),
@@ -495,7 +496,7 @@ def layer_workload(name: str, args, dev, steps: int, warmup: int) -> dict:
     if name == "long":
         block["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
                                             stream)
-    if name in ("decode", "prefill"):
+    if name in ("decode", "prefill", "long"):
         block["act_mxfp6"] = act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot,
                                               arenas, hist, U, stream, K, min(warmup, 5), args,
                                               dev)

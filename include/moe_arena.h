@@ -288,9 +288,9 @@ int moe_demand_accumulate(const int32_t* topk_expert, const float* topk_score, i
  * act_format: the format of xq (as moe_route wrote it) and of h.  With
  *          MOE_ACT_MXFP6 the products take E2M3 activations against the MXFP4
  *          weights (the block-scaled instruction at the E2M1 x E2M3 setting;
- *          g, u and y otherwise as above, h encoded as an MXFP6 row) and every
- *          batch size runs on the small-batch kernels; H and I must be
- *          multiples of 512 (else MOE_EUNSUPPORTED).  Other values: MOE_EINVAL.
+ *          g, u and y otherwise as above, h encoded as an MXFP6 row), on both
+ *          kernel families; H and I must be multiples of 512 and at most
+ *          15872 (else MOE_EUNSUPPORTED).  Other values: MOE_EINVAL.
  *
  * Inputs : xq, slot_offsets, perm, sel_slot, sel_weight as written by moe_route
  *          for the same T, k, S; arena (256-byte aligned), slot_stride (multiple

@@ -1284,6 +1284,328 @@ __global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
 }
 
 
+// ===========================================================================
+// Pipelined kernels with MXFP6 activation rows (act_format MOE_ACT_MXFP6).
+// A B row takes 96 bytes per 128-element stage instead of 64, so the tile
+// shape changes to stay within half of a CU's LDS: each wave owns one 32-row
+// weight tile (gate/up: rows 0-15 gate and 16-31 up of the same 16 rows of
+// I; down: 32 rows of H) against the tile's 128 columns.  A stage is 8 KB of
+// weight codes and 12 KB of activation codes; with the two 2 KB scale-group
+// buffers the three-stage ring takes 64 KB, so two workgroups share a CU as
+// in the MXFP4 kernels.  The instruction is the same 32x32x64 block-scaled
+// one with E2M1 A and E2M3 B operands (measured at the E2M1 x E2M1 rate).
+// ===========================================================================
+constexpr int kRowB6 = kKc / 32 * 24;            // activation code bytes per row per stage (96)
+constexpr int kStageA6 = 4 * 32 * kRowC;         // weight code rows of the four waves (8 KB)
+constexpr int kStageB6 = kTileM * kRowB6;        // activation code rows (12 KB)
+constexpr int kStage6 = kStageA6 + kStageB6;
+constexpr int kGroupSA6 = 4 * 32 * kGroupRow;    // weight rows' scales (2 KB)
+constexpr int kPipeLds6 = kRing * kStage6 + kGroupSA6 + kGroupSB;  // 65,536 bytes
+static_assert(2 * kPipeLds6 <= 160 * 1024, "two workgroups per CU");
+static_assert(kZeroPage >= kRowB6, "an absent activation row reads a stage from the zero page");
+// Loads issued by each wave per stage: 2 weight-code and 3 activation-code
+// loads; per group, two half-wave scale loads.
+constexpr int kLoadsPerStage6 = 5;
+
+struct PipeSrc6 {
+  const uint8_t* a[2];   // weight codes, load j: wave row 16j + lane/4, block already swizzled
+  const uint8_t* as;     // weight scales (lanes 0-31): wave row lane
+  const uint8_t* b[3];   // activation codes, load j: 16-byte unit 64j + lane of the wave's rows
+  int bstep[3];          // code bytes per stage (96; 0 for an absent row on the zero page)
+  const uint8_t* bs;     // activation scales (lanes 0-31): tile row 32 wave + lane
+  int bsstep;            // scale bytes per group (16; 0 for an absent row)
+};
+
+__device__ __forceinline__ void pipe6_issue(uint8_t* smem, const PipeSrc6& src, int q, int wave) {
+  uint8_t* st = smem + (q % kRing) * kStage6;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    dma16(src.a[j] + (size_t)q * kRowC, st + wave * (32 * kRowC) + j * 1024);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA6 + wave * (32 * kRowB6) + j * 1024);
+}
+
+__device__ __forceinline__ void pipe6_issue_scales(uint8_t* smem, const PipeSrc6& src, int g,
+                                                   int wave) {
+  uint8_t* sg = smem + kRing * kStage6;
+  if ((threadIdx.x & 63) < 32) {  // lanes 0-31: one row each (partial-lane loads)
+    dma16(src.as + (size_t)g * kGroupRow, sg + wave * (32 * kGroupRow));
+    dma16(src.bs + (size_t)g * src.bsstep, sg + kGroupSA6 + wave * (32 * kGroupRow));
+  }
+}
+
+// As pipe_wait, with five loads per stage.
+__device__ __forceinline__ void pipe6_wait(int q, int Q) {
+  static_assert(kLoadsPerStage6 == 5 && kAhead == 2 && kGroup == 4, "wait counts below");
+  if (q + 1 < Q)
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+__device__ __forceinline__ v16f mfma32x6(const uint4& a, const uint32_t (&b)[6], v16f c,
+                                         uint32_t sa, uint32_t sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], 0, 0};
+  // cbsz = 4: A (weights) E2M1; blgp = 2: B (activations) E2M3
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 2, 0, (int)sa, 0,
+                                                         (int)sb);
+}
+
+struct StepFrags6 {
+  uint4 a;
+  uint32_t b[4][6];
+};
+
+// Fragments of MFMA step s: the wave's weight row r (16 bytes of block 2s+hh,
+// swizzled as in the MXFP4 kernels) and, per column tile, the 24 bytes of
+// block 2s+hh of activation row 32cb+r, read as the two 16-byte units that
+// hold them (an odd block starts 8 bytes into its first unit).
+__device__ __forceinline__ void read_step6(const uint8_t* st, int s, int wave, int r, int hh,
+                                           int swz, StepFrags6& f) {
+  const int pb = ((2 * s + hh) ^ swz) * 16;
+  f.a = *reinterpret_cast<const uint4*>(st + wave * (32 * kRowC) + r * kRowC + pb);
+  const int blk = 2 * s + hh;
+  const int u0 = 16 * ((3 * blk) >> 1);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const uint8_t* rp = st + kStageA6 + (32 * cb + r) * kRowB6 + u0;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(rp);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(rp + 16);
+    f.b[cb][0] = hh ? x0.z : x0.x;
+    f.b[cb][1] = hh ? x0.w : x0.y;
+    f.b[cb][2] = hh ? x1.x : x0.z;
+    f.b[cb][3] = hh ? x1.y : x0.w;
+    f.b[cb][4] = hh ? x1.z : x1.x;
+    f.b[cb][5] = hh ? x1.w : x1.y;
+  }
+}
+
+// This lane's scale words of stage q (4 scale bytes of its weight row r and
+// of each column tile's row r), from the group buffer.
+struct StageScales6 {
+  uint32_t aw, bw[4];
+};
+
+__device__ __forceinline__ void read_stage_scales6(const uint8_t* smem, int q, int wave, int r,
+                                                   StageScales6& sc) {
+  const uint8_t* sg = smem + kRing * kStage6 + (q % kGroup) * kRowS;
+  sc.aw = *reinterpret_cast<const uint32_t*>(sg + (wave * 32 + r) * kGroupRow);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+    sc.bw[cb] = *reinterpret_cast<const uint32_t*>(sg + kGroupSA6 + (32 * cb + r) * kGroupRow);
+}
+
+__device__ __forceinline__ void pipe6_compute(const uint8_t* smem, int q, int wave, int r, int hh,
+                                              const StageScales6& sc, v16f (&acc)[4]) {
+  const uint8_t* st = smem + (q % kRing) * kStage6;
+  const int swz = (r >> 2) & 3;
+  StepFrags6 f[2];
+  read_step6(st, 0, wave, r, hh, swz, f[0]);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (s + 1 < 2) read_step6(st, s + 1, wave, r, hh, swz, f[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    const StepFrags6& cur = f[s];
+    const int sh = 8 * (2 * s + hh);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      acc[cb] = mfma32x6(cur.a, cur.b[cb], acc[cb], sc.aw >> sh, sc.bw[cb] >> sh);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The K loop over Q = K / 128 stages; issue order and waits as pipe_mainloop.
+__device__ __forceinline__ void pipe6_mainloop(uint8_t* smem, const PipeSrc6& src, int Q, int wave,
+                                               int lane, v16f (&acc)[4]) {
+  const int r = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) acc[cb] = zero16();
+  pipe6_issue_scales(smem, src, 0, wave);
+#pragma unroll
+  for (int q = 0; q < kAhead; ++q)
+    if (q < Q) pipe6_issue(smem, src, q, wave);
+  for (int q = 0; q < Q; ++q) {
+    pipe6_wait(q, Q);
+    StageScales6 sc;
+    read_stage_scales6(smem, q, wave, r, sc);
+    if (q % kGroup == kGroup - 1 && q + 1 < Q) {
+      // every wave holds its last scale words of the group: reload the buffer
+      __syncthreads();
+      pipe6_issue_scales(smem, src, (q + 1) / kGroup, wave);
+    }
+    if (q + kAhead < Q) pipe6_issue(smem, src, q + kAhead, wave);
+    pipe6_compute(smem, q, wave, r, hh, sc, acc);
+  }
+}
+
+// Weight-side sources: wave row wr (0..31) of the stage is row
+// wrow[wr / 16] + wr % 16 of the section at wcodes[wr / 16] / wscales[wr / 16].
+__device__ __forceinline__ void pipe6_weight_src(PipeSrc6& src, const uint8_t* const (&wcodes)[2],
+                                                 const uint8_t* const (&wscales)[2],
+                                                 const int (&wrow)[2], size_t crow, size_t srow,
+                                                 int lane) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int wr = 16 * j + (lane >> 2), t = wr >> 4, rr = wr & 15;
+    const int b = (lane & 3) ^ ((wr >> 2) & 3);
+    src.a[j] = wcodes[t] + (size_t)(wrow[t] + rr) * crow + b * 16;
+  }
+  const int wr = lane & 31, t = wr >> 4, rr = wr & 15;  // lanes 32-63 issue no scale load
+  src.as = (t ? wscales[1] : wscales[0]) + (size_t)((t ? wrow[1] : wrow[0]) + rr) * srow;
+}
+
+// Activation-side sources: the wave's tile rows 32 wave .. +31, 96 code bytes
+// a stage each, as 192 16-byte units (unit c: row c / 6, bytes 16 (c % 6)..);
+// rowptr(row) gives the row (codes at +0, scales at +scale_off) or null for
+// an absent row, which reads the zero page.
+template <typename RowPtr>
+__device__ __forceinline__ void pipe6_act_src(PipeSrc6& src, RowPtr rowptr, size_t scale_off,
+                                              const uint8_t* zero, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int c = 64 * j + lane;
+    const int row = 32 * wave + c / 6, u = c % 6;
+    const uint8_t* rp = rowptr(row);
+    src.b[j] = (rp ? rp : zero) + u * 16;
+    src.bstep[j] = rp ? kRowB6 : 0;
+  }
+  const int row = 32 * wave + (lane & 31);
+  const uint8_t* rp = rowptr(row);
+  src.bs = rp ? rp + scale_off : zero;
+  src.bsstep = rp ? kGroupRow : 0;
+}
+
+// Gate/up with MXFP6 rows: N-tile = 64 rows of I; wave w: the 16 rows
+// n0 = 64 nt + 16 w of gate (tile rows 0-15) and of up (16-31); K = H.  Two
+// waves hold one MX block of h (32 rows of I): each writes its partial
+// maximum per column to LDS, and both read the pair's.
+__global__ __launch_bounds__(256, 2) void gateup_pipe6(PipeArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds6];
+  TileRef tr;
+  int w;
+  if (p.only) {
+    const int n = p.only[1] * p.nN;
+    w = (int)blockIdx.x < n ? p.only[0] * p.nN + (int)blockIdx.x : -1;
+  } else {
+    w = xcd_work_index(p.items[0] * p.nN);
+  }
+  if (!tile_of(w, p.nN, kTileM, p.items, p.offsets, p.S, p.A, p.shared ? p.T : 0, tr) ||
+      tr.slot == p.skip_slot)
+    return;
+  const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
+  const bool sh = s == p.S;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int H = p.H;
+  const int n0 = tr.nt * 64 + wave * 16;  // I % 64 == 0: every wave's rows exist
+  const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
+  const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c1};
+  const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s1};
+  const int wrow[2] = {n0, n0};
+  PipeSrc6 src;
+  pipe6_weight_src(src, wc, wsc, wrow, (size_t)H / 2, (size_t)H / 32, lane);
+  pipe6_act_src(
+      src,
+      [&](int row) -> const uint8_t* {
+        if (row >= rows) return nullptr;
+        if (sh) return p.act + (size_t)(p0 + row - p.A) * p.arow;
+        const int a = p.perm[p0 + row];
+        return (a >= 0 && a < p.A) ? p.act + (size_t)(a / p.k) * p.arow : nullptr;
+      },
+      (size_t)H / 32 * 24, p.zero, wave, lane);
+  v16f acc[4];
+  pipe6_mainloop(smem, src, H / kKc, wave, lane, acc);
+  // h = silu(gate) * up: lane (column 32cb + r, half hh) holds rows
+  // 8(v/4) + 4hh + v%4 (v < 8) of the wave's 16, gate at v and up at v + 8
+  float h[4][8];
+  float* part = reinterpret_cast<float*>(smem);  // [wave][cb][32] partial maxima
+  __syncthreads();  // every wave is done with the ring
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    float m = 0.f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      h[cb][v] = silu_mul(acc[cb][v], acc[cb][v + 8]);
+      m = fmaxf(m, fabsf(h[cb][v]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    if (hh == 0) part[(wave * 4 + cb) * 32 + r] = m;
+  }
+  __syncthreads();
+  const int half = wave & 1;        // which 16 rows of the pair's block
+  const int blk = (n0 - 16 * half) / 32;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int lr = 32 * cb + r;
+    const float amax =
+        fmaxf(part[(wave * 4 + cb) * 32 + r], part[((wave ^ 1) * 4 + cb) * 32 + r]);
+    uint32_t code[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t scale = 0u;
+    if (amax > 0.f) {
+      const int e = mx_block_exp(amax);
+      scale = (uint32_t)(e + 127);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) code[v] = e2m3_code(h[cb][v], e);
+    }
+    if (lr < rows) {
+      // block elements 16 half + 8q + 4hh .. +3 (q = 0, 1): 24 bits at byte
+      // 12 half + 6q + 3hh of the block's codes
+      uint8_t* hb = p.hq + (size_t)(p0 + lr) * p.hrow + (size_t)blk * 24 + 12 * half + 3 * hh;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t w24 = code[4 * q] | (code[4 * q + 1] << 6) | (code[4 * q + 2] << 12) |
+                             (code[4 * q + 3] << 18);
+        hb[6 * q] = (uint8_t)w24;
+        hb[6 * q + 1] = (uint8_t)(w24 >> 8);
+        hb[6 * q + 2] = (uint8_t)(w24 >> 16);
+      }
+      if (half == 0 && hh == 0)
+        p.hq[(size_t)(p0 + lr) * p.hrow + (size_t)p.I / 32 * 24 + blk] = (uint8_t)scale;
+    }
+  }
+}
+
+// Down with MXFP6 hq rows: N-tile = 128 rows of H; wave w: the 32 rows
+// n0 = 128 nt + 32 w; K = I; B rows: the slot's hq rows p0.. (contiguous).
+__global__ __launch_bounds__(256, 2) void down_pipe6(PipeArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds6];
+  TileRef tr;
+  if (!tile_of(xcd_work_index(p.items[0] * p.nN), p.nN, kTileM, p.items, p.offsets, p.S, p.A,
+               p.shared ? p.T : 0, tr))
+    return;
+  const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
+  const bool sh = s == p.S;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 31, hh = lane >> 5;
+  const int I = p.I;
+  const int n0 = tr.nt * 128 + wave * 32;  // H % 128 == 0: every wave's rows exist
+  const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
+  const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c0};
+  const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s0};
+  const int wrow[2] = {n0, n0 + 16};
+  PipeSrc6 src;
+  pipe6_weight_src(src, wc, wsc, wrow, (size_t)I / 2, (size_t)I / 32, lane);
+  pipe6_act_src(
+      src,
+      [&](int row) -> const uint8_t* {
+        return row < rows ? p.act + (size_t)(p0 + row) * p.arow : nullptr;
+      },
+      (size_t)I / 32 * 24, p.zero, wave, lane);
+  v16f acc[4];
+  pipe6_mainloop(smem, src, I / kKc, wave, lane, acc);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int lr = 32 * cb + r;
+    if (lr < rows) {
+      const int a = sh ? p0 + lr : p.perm[p0 + lr];
+      if (a >= 0 && (sh || a < p.A)) store_y_bf16(p.y + (size_t)a * p.H, n0, hh, acc[cb]);
+    }
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -1301,13 +1623,18 @@ constexpr int kPipeMinA = 2048;
 
 enum Family { kFamSmall, kFamPipe };
 
-// MXFP6 activations run on the small-batch kernels at every batch size.
+// MXFP6 activation rows take the same crossover, with their own pipelined
+// kernels (gateup_pipe6 / down_pipe6).
 static Family family_of(int T, int k, int H, int I, int fmt) {
-  if (fmt == MOE_ACT_MXFP4 && (size_t)T * k >= (size_t)kPipeMinA && H % 512 == 0 &&
-      I % 512 == 0)
-    return kFamPipe;
+  (void)fmt;
+  if ((size_t)T * k >= (size_t)kPipeMinA && H % 512 == 0 && I % 512 == 0) return kFamPipe;
   return kFamSmall;
 }
+
+// N-tiles of the pipelined kernels: gate/up rows of I and down rows of H per
+// workgroup, by activation format.
+static int pipe_ntile_gateup(int fmt) { return fmt == MOE_ACT_MXFP6 ? 64 : 128; }
+static int pipe_ntile_down(int fmt) { return fmt == MOE_ACT_MXFP6 ? 128 : 256; }
 
 // Upper bound on the M-tiles of tm rows of a batch: one partial tile per used
 // slot plus the full ones.
@@ -1383,8 +1710,9 @@ static int experts_validate(const moe_experts_args* a, const void* ws, size_t ws
   if (defer < -1 || defer >= S || (defer >= 0 && !a->defer_event)) return MOE_EINVAL;
   if (family_of(T, k, H, I, fmt) != kFamSmall) {
     const size_t ntile = max_tiles((size_t)T * k, S, kTileM) + shared_tiles(T, shared);
-    if (up_to(ntile * (size_t)((I + 127) / 128), 8) > 0x7FFFFFFFu ||
-        up_to(ntile * (size_t)((H + 255) / 256), 8) > 0x7FFFFFFFu)
+    const int n1 = pipe_ntile_gateup(fmt), n2 = pipe_ntile_down(fmt);
+    if (up_to(ntile * (size_t)((I + n1 - 1) / n1), 8) > 0x7FFFFFFFu ||
+        up_to(ntile * (size_t)((H + n2 - 1) / n2), 8) > 0x7FFFFFFFu)
       return MOE_EUNSUPPORTED;
   }
   return MOE_OK;
@@ -1402,9 +1730,10 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
   const int A = T * k;
   const Family fam = family_of(T, k, H, I, fmt);
   const size_t ntile = max_tiles((size_t)A, S, kTileM) + shared_tiles(T, shared);
-  // N-tiles: gate/up 128 rows of I, down 256 rows of H
-  const int nN1 = (I + 127) / 128;
-  const int nN2 = (H + 255) / 256;
+  // N-tiles: gate/up 128 rows of I, down 256 rows of H (MXFP6 rows: 64 and 128)
+  const bool fp6 = fmt == MOE_ACT_MXFP6;
+  const int nN1 = (I + pipe_ntile_gateup(fmt) - 1) / pipe_ntile_gateup(fmt);
+  const int nN2 = (H + pipe_ntile_down(fmt) - 1) / pipe_ntile_down(fmt);
   const size_t g1 = up_to(ntile * (size_t)nN1, 8);
   const size_t g2 = up_to(ntile * (size_t)nN2, 8);
   if (S == 0 && !shared) {
@@ -1429,7 +1758,7 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
                                         shared ? T : 0);
     PipeArgs t;
     t.act = a->xq;
-    t.arow = mxfp4_row_bytes(H);
+    t.arow = act_row_bytes(H, fmt);
     t.arena = a->arena;
     t.stride = a->slot_stride;
     t.off_c0 = L.off[0];
@@ -1441,7 +1770,7 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     t.items = items;
     t.zero = zero;
     t.hq = hq;
-    t.hrow = mxfp4_row_bytes(I);
+    t.hrow = act_row_bytes(I, fmt);
     t.y = reinterpret_cast<uint16_t*>(y);
     t.H = H;
     t.I = I;
@@ -1453,8 +1782,8 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     t.shared = a->shared_expert;
     t.S = S;
     t.T = T;
-    hipExtLaunchKernelGGL(gateup_pipe, dim3((unsigned)g1), dim3(256), 0, stream,
-                          ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, 0, t);
+    hipExtLaunchKernelGGL(fp6 ? gateup_pipe6 : gateup_pipe, dim3((unsigned)g1), dim3(256), 0,
+                          stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, 0, t);
     if (defer >= 0) {
       // the deferred slot's tiles, once its bytes are in place: at most one
       // assignment per token, so at most ceil(T / 128) M-tiles
@@ -1462,7 +1791,10 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
       t.skip_slot = -1;
       t.only = defer_info;
       const size_t g3 = (size_t)((T + kTileM - 1) / kTileM) * (size_t)nN1;
-      gateup_pipe<<<(unsigned)g3, 256, 0, stream>>>(t);
+      if (fp6)
+        gateup_pipe6<<<(unsigned)g3, 256, 0, stream>>>(t);
+      else
+        gateup_pipe<<<(unsigned)g3, 256, 0, stream>>>(t);
       t.only = nullptr;
     }
     t.act = hq;
@@ -1470,7 +1802,10 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     t.off_c0 = L.off[4];
     t.off_s0 = L.off[5];
     t.nN = nN2;
-    down_pipe<<<(unsigned)g2, 256, 0, stream>>>(t);
+    if (fp6)
+      down_pipe6<<<(unsigned)g2, 256, 0, stream>>>(t);
+    else
+      down_pipe<<<(unsigned)g2, 256, 0, stream>>>(t);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   } else {
     // work items: the used slots, found in place, for small slot counts; the
