@@ -247,7 +247,7 @@ def gateup_roofline(gu_us: float, gu_bytes: float, gu_flops: float, args, dev) -
     return roof
 
 
-def act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot, arenas, hist, U,
+def act_mxfp6_timing(name, T, H, E, k, I, S, xs, w_router, bias, expert_slot, arenas, hist, U,
                      stream, steps: int, warmup: int, args, dev) -> dict:
     """The activation-format variant on the same inputs: activation and h rows
     in MXFP6 (E2M3), weights unchanged; every batch size on the small-batch
@@ -289,11 +289,13 @@ def act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot, arenas, 
     gu_bytes = float(np.mean([u * gateup_bytes_per_slot(H, I) for u in u_steps])) \
         + T * row6_bytes(H) + A * row6_bytes(I)
     roof = gateup_roofline(gu_us, gu_bytes, 4.0 * H * I * A, args, dev)
-    kernel = "gateup_pipe6" if gateup_kernel_name(T, k, H, I) == "gateup_pipe" else "gateup_kernel"
+    kernel = "gateup_pipe6" if gateup_kernel_name(T, k, H, I) == "gateup_pipe" else "gateup_kernel6"
     out = {"value": T * steps / (total_ms * 1e-3), "unit": "tokens/s", "steps": steps,
            "ms_per_step": total_ms / steps, "dtype": "mxfp4 weights x mxfp6 activations",
-           "roofline": {**roof, "kernel": kernel, "algo_bytes_per_launch": gu_bytes,
-                        "mean_launch_us": gu_us}}
+           "roofline": {**roof, "kernel": kernel,
+                        "traffic": traffic_from_profile(kernel, name),
+                        "algo_bytes_per_launch": gu_bytes,
+                        "algo_flops_per_launch": 4.0 * H * I * A, "mean_launch_us": gu_us}}
     if not args.no_peaks:   # the instruction's rate with E2M3 against E2M1 B operands
         out["mfma_loop_tflops"] = {"e2m1_x_e2m1": mfma_loop_rate(dev, 0),
                                    "e2m1_x_e2m3": mfma_loop_rate(dev, 1)}
@@ -497,9 +499,9 @@ def layer_workload(name: str, args, dev, steps: int, warmup: int) -> dict:
         block["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
                                             stream)
     if name in ("decode", "prefill", "long"):
-        block["act_mxfp6"] = act_mxfp6_timing(T, H, E, k, I, S, xs, w_router, bias, expert_slot,
-                                              arenas, hist, U, stream, K, min(warmup, 5), args,
-                                              dev)
+        block["act_mxfp6"] = act_mxfp6_timing(name, T, H, E, k, I, S, xs, w_router, bias,
+                                              expert_slot, arenas, hist, U, stream, K,
+                                              min(warmup, 5), args, dev)
     del arenas
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
