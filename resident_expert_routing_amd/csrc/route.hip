@@ -172,53 +172,81 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
 // or above that line (in the order over all experts, and over the routable
 // ones) can be picked.  Those get the float64 logit, every other entry keeps
 // its z~, and the token is selected again: the picks are the float64 logits'.
-// One workgroup per listed token (a fixed grid walks the list), its four waves
-// taking the candidates in turn; lane l sums h in [l H/64, (l+1) H/64) as a
-// fused multiply-add chain, then the wave adds the lanes' sums in the fixed
-// DPP order.
+// One workgroup per listed token (a fixed grid walks the list).  The token's
+// candidates are decided first, from the bounded logits, into an LDS mask per
+// 64 experts; a barrier then separates those reads from the rewrites of z, and
+// the four waves take the candidates in turn.  Lane l sums h in
+// [l H/64, (l+1) H/64) as a fused multiply-add chain, then the wave adds the
+// lanes' sums in the fixed DPP order.
 __global__ __launch_bounds__(256) void router_f64_candidates(
     const uint16_t* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
     const int32_t* __restrict__ expert_slot, int H, int E, int S, double* __restrict__ z,
     const int32_t* __restrict__ tlist, const double* __restrict__ cert) {
+  constexpr int kPass = 64;  // elements per lane whose loads are issued together
+  __shared__ uint64_t cmask[MOE_MAX_E / 64];
   const int n = tlist[0];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int per = H / 64;  // H % 512 == 0
+  const int per = H / 64;  // H % 512 == 0, H <= 8192: at most two passes
+  const int nb = (E + 63) / 64;
   for (int i = blockIdx.x; i < n; i += gridDim.x) {  // uniform
     const int t = tlist[1 + i];
     const double ku = cert[3 * (size_t)t], km = cert[3 * (size_t)t + 1];
     const double line = 2.0 * cert[3 * (size_t)t + 2];
-    const uint16_t* xr = x + (size_t)t * H + (size_t)lane * per;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + lane;
+    for (int b = wave; b < nb; b += 4) {
+      const int e = 64 * b + lane;
       bool cand = false;
       if (e < E) {
         const double v = z[(size_t)t * E + e] + (bias ? (double)bias[e] : 0.0);
         const int sl = expert_slot[e];
         cand = v >= ku - line || (sl >= 0 && sl < S && v >= km - line);
       }
-      uint64_t m = __ballot(cand);
-      for (int j = 0; m; ++j) {  // uniform; wave j % 4 takes the j-th candidate
-        const int c = e0 + __builtin_ctzll(m);
+      const uint64_t m = __ballot(cand);
+      if (lane == 0) cmask[b] = m;
+    }
+    __syncthreads();  // every candidate decided before any z of the token is rewritten
+    const uint16_t* xr = x + (size_t)t * H + (size_t)lane * per;
+    int j = 0;  // candidate rank over all blocks; wave j % 4 takes it
+    for (int b = 0; b < nb; ++b) {
+      uint64_t m = cmask[b];
+      for (; m; ++j) {  // uniform
+        const int c = 64 * b + __builtin_ctzll(m);
         m &= m - 1;
         if ((j & 3) != wave) continue;
         const float* wr = w + (size_t)c * H + (size_t)lane * per;
-        double acc = 0.0;
-        for (int h = 0; h < per; h += 8) {  // per = H/64, a multiple of 8
-          const uint4 xv = *reinterpret_cast<const uint4*>(xr + h);
-          const float4 wa = *reinterpret_cast<const float4*>(wr + h);
-          const float4 wb = *reinterpret_cast<const float4*>(wr + h + 4);
-          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-          const float ww[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+        double acc = 0.0;  // h ascending over the lane's range (per = H/64, a multiple of 8)
+        for (int h0 = 0; h0 < per; h0 += kPass) {
+          // every load of the pass before its first product: one memory round
+          // trip per pass instead of one per 8 elements
+          uint4 xv[kPass / 8];
+          float4 wv[kPass / 4];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t bits = (j & 1) ? (xw[j >> 1] >> 16) : (xw[j >> 1] & 0xFFFFu);
-            acc = fma((double)bf16_to_f32(bits), (double)ww[j], acc);
+          for (int q = 0; q < kPass / 8; ++q) {
+            if (h0 + 8 * q < per) {
+              xv[q] = *reinterpret_cast<const uint4*>(xr + h0 + 8 * q);
+              wv[2 * q] = *reinterpret_cast<const float4*>(wr + h0 + 8 * q);
+              wv[2 * q + 1] = *reinterpret_cast<const float4*>(wr + h0 + 8 * q + 4);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < kPass / 8; ++q) {
+            if (h0 + 8 * q < per) {
+              const uint32_t xw[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
+              const float ww[8] = {wv[2 * q].x,     wv[2 * q].y,     wv[2 * q].z,
+                                   wv[2 * q].w,     wv[2 * q + 1].x, wv[2 * q + 1].y,
+                                   wv[2 * q + 1].z, wv[2 * q + 1].w};
+#pragma unroll
+              for (int jj = 0; jj < 8; ++jj) {
+                const uint32_t bits = (jj & 1) ? (xw[jj >> 1] >> 16) : (xw[jj >> 1] & 0xFFFFu);
+                acc = fma((double)bf16_to_f32(bits), (double)ww[jj], acc);
+              }
+            }
           }
         }
         const double sum = wave_sum(acc);
         if (lane == 0) z[(size_t)t * E + c] = sum;
       }
     }
+    __syncthreads();  // cmask is rewritten for the next token only after every wave read it
   }
 }
 
@@ -1305,6 +1333,77 @@ __global__ __launch_bounds__(256) void bucket_place(const int32_t* __restrict__ 
   }
 }
 
+// Placement with the scan folded in, for count tables of at most
+// kFusedScanMaxInts entries and S <= kFusedScanMaxS: every workgroup reads
+// the whole S x nchunk table (slot totals, and per slot the counts of the
+// chunks before its own), scans the totals, and places its chunk's
+// assignments at offsets[s] + (earlier chunks of s) + rank.  Workgroup 0
+// writes offsets; perm positions past the total are set to -1, spread over
+// the workgroups.  Same perm and offsets as bucket_scan then bucket_place.
+constexpr int kFusedScanMaxS = 2048;
+constexpr int kFusedScanMaxInts = 32 * 1024;
+
+__global__ __launch_bounds__(256) void bucket_place_scan(const int32_t* __restrict__ sel_slot,
+                                                         int T, int k, int S, int nchunk, int A,
+                                                         const int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ perm) {
+  extern __shared__ unsigned long long bits[];  // S token masks, then tot[S], pre[S]
+  int* tot = reinterpret_cast<int*>(bits + S);
+  int* pre = tot + S;
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c = blockIdx.x;
+  for (int s = tid; s < S; s += 256) {
+    const int32_t* cs = counts + (size_t)s * nchunk;
+    int ts = 0, ps = 0;
+#pragma unroll 8
+    for (int q = 0; q < nchunk; ++q) {
+      const int v = cs[q];
+      ts += v;
+      ps += q < c ? v : 0;
+    }
+    tot[s] = ts;
+    pre[s] = ps;
+  }
+  chunk_token_masks(sel_slot, T, k, S, bits);  // begins and ends with a barrier
+  // exclusive scan of the totals: thread tid owns slots [lo, hi)
+  const int per = (S + 255) / 256;
+  const int lo = min(S, tid * per), hi = min(S, lo + per);
+  int local = 0;
+  for (int s = lo; s < hi; ++s) local += tot[s];
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int i = 0; i < wv; ++i) run += wsum[i];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  for (int s = lo; s < hi; ++s) {
+    const int n = tot[s];
+    tot[s] = run;  // exclusive offset of slot s
+    if (c == 0) offsets[s] = run;
+    run += n;
+  }
+  if (c == 0 && tid == 0) offsets[S] = total;
+  __syncthreads();
+  const int t0 = c * kBucketChunk;
+  const int n = min(kBucketChunk, T - t0) * k;
+  for (int i = tid; i < n; i += 256) {
+    const int s = sel_slot[(size_t)t0 * k + i];
+    if (s >= 0 && s < S) {
+      const int tl = i / k;
+      const int rank = __popcll(bits[s] & ((1ull << tl) - 1ull));
+      perm[tot[s] + pre[s] + rank] = t0 * k + i;
+    }
+  }
+  for (int a = total + c * 256 + tid; a < A; a += nchunk * 256) perm[a] = -1;
+}
+
 __global__ void fill_i32(int32_t* p, int n, int v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -1516,11 +1615,19 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
                                                moe_demand_ws_bytes_internal(T, E));
   const size_t mask_lds = (size_t)(S > 0 ? S : 1) * sizeof(unsigned long long);
   if (S > 0) bucket_hist<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts);
-  const size_t scan_lds =
-      (size_t)S * nbc <= (size_t)kScanLdsInts ? (size_t)S * nbc * sizeof(int32_t) : 0;
-  bucket_scan<<<1, 1024, scan_lds, stream>>>(counts, S, nbc, A, a->slot_offsets, a->perm);
-  if (!record_stage(ev,3, stream)) return MOE_EHIP;
-  if (S > 0) bucket_place<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts, a->perm);
+  if (S > 0 && S <= kFusedScanMaxS && (size_t)S * nbc <= (size_t)kFusedScanMaxInts) {
+    // small count tables: every placement workgroup scans them itself
+    if (!record_stage(ev,3, stream)) return MOE_EHIP;
+    bucket_place_scan<<<nbc, 256, (size_t)S * 16, stream>>>(a->sel_slot, T, k, S, nbc, A, counts,
+                                                            a->slot_offsets, a->perm);
+  } else {
+    const size_t scan_lds =
+        (size_t)S * nbc <= (size_t)kScanLdsInts ? (size_t)S * nbc * sizeof(int32_t) : 0;
+    bucket_scan<<<1, 1024, scan_lds, stream>>>(counts, S, nbc, A, a->slot_offsets, a->perm);
+    if (!record_stage(ev,3, stream)) return MOE_EHIP;
+    if (S > 0)
+      bucket_place<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts, a->perm);
+  }
   if (!record_stage(ev,4, stream)) return MOE_EHIP;
   return hip_status();
 }
