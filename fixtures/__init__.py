@@ -152,8 +152,26 @@ class SlotLayout:
         return _up256(off + sz)
 
 
+def tile_codes(codes: np.ndarray) -> np.ndarray:
+    """Row-major packed codes [N, B] (N % 16 == 0, B bytes a row) -> the slot's
+    code order: row blocks of 16 rows, each a run of tiles of 64 code bytes
+    (128 elements) of all 16 rows (the last tile of a block narrower when B %
+    64 != 0), a tile's rows one after another."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    n, nb = codes.shape
+    assert n % 16 == 0
+    full = nb // 64 * 64
+    blocks = codes.reshape(n // 16, 16, nb)
+    head = blocks[:, :, :full].reshape(n // 16, 16, full // 64, 64).transpose(0, 2, 1, 3)
+    parts = [head.reshape(n // 16, -1)]
+    if full < nb:
+        parts.append(blocks[:, :, full:].reshape(n // 16, -1))
+    return np.concatenate(parts, axis=1).reshape(-1)
+
+
 def pack_expert(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
-    """Pack one SwiGLU expert (gate [I,H], up [I,H], down [H,I]) into slot bytes."""
+    """Pack one SwiGLU expert (gate [I,H], up [I,H], down [H,I]) into slot bytes:
+    codes in tiles of 16 rows x 64 bytes (tile_codes), scales row by row."""
     I, H = wg.shape
     lay = SlotLayout(H, I)
     buf = np.zeros(lay.nbytes, dtype=np.uint8)
@@ -163,7 +181,7 @@ def pack_expert(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
         c, s = pack_mxfp4_rows(mat)
         co, cs = lay.sections[cname]
         so, ss = lay.sections[sname]
-        buf[co:co + cs] = c.reshape(-1)
+        buf[co:co + cs] = tile_codes(c)
         buf[so:so + ss] = s.reshape(-1)
     return buf
 

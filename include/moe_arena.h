@@ -52,7 +52,14 @@
  *                 gate codes [I][H/2] | gate scales [I][H/32] |
  *                 up codes   [I][H/2] | up scales   [I][H/32] |
  *                 down codes [H][I/2] | down scales [H][I/32]
- *               rows are contraction-contiguous (row n holds output n's weights).
+ *               A matrix's MXFP4 rows (row n: output n's weights, K/2 code
+ *               bytes, K/32 scale bytes) are stored as follows.  Scales: row
+ *               by row, [N][K/32].  Codes: in tiles of 16 rows x 64 code
+ *               bytes (128 elements): byte j of row n sits at
+ *                 (n/16)*16*(K/2) + (j/64)*1024 + (n%16)*w + j%64,
+ *               w = min(64, K/2 - 64*(j/64)) (64, or the width of a last
+ *               partial tile), so a tile's 16 row pieces are one 1 KB run
+ *               (N, a multiple of 32, splits into whole 16-row blocks).
  *   arena     : S slots at arena + s*slot_stride; slot ids are global: arena
  *               slots first, hot-ring slots after them (TideLM README, "Settings
  *               worth knowing": the ring's slots are on top of the budget).

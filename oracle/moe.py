@@ -60,15 +60,30 @@ def slot_sections(H: int, I: int) -> dict:
     return out
 
 
+def code_position(n: np.ndarray, j: np.ndarray, nbytes: int) -> np.ndarray:
+    """Offset, within a code section, of byte j of row n's packed codes (a row
+    has nbytes code bytes).  The section is cut into row blocks of 16 rows;
+    a block holds, one after another, the tiles of its rows' bytes
+    [64c, 64c + w_c) for c = 0, 1, ... (w_c = 64, or what is left for the
+    last), and a tile stores its 16 rows one after another, w_c bytes each.
+    """
+    c = j // 64
+    w = np.minimum(64, nbytes - 64 * c)
+    return (n // 16) * (16 * nbytes) + c * (16 * 64) + (n % 16) * w + (j - 64 * c)
+
+
 def decode_expert(slot_bytes: np.ndarray, H: int, I: int):
-    """Packed slot bytes -> float64 (Wg [I,H], Wu [I,H], Wd [H,I])."""
+    """Packed slot bytes -> float64 (Wg [I,H], Wu [I,H], Wd [H,I]).
+
+    Codes are read at code_position (tiles of 16 rows); scales are row by row."""
     sec = slot_sections(H, I)
     b = np.asarray(slot_bytes, dtype=np.uint8)
 
     def mat(prefix):
         co, r, c = sec[prefix + "_codes"]
         so, rs, cs = sec[prefix + "_scales"]
-        codes = b[co:co + r * c].reshape(r, c)
+        pos = code_position(np.arange(r)[:, None], np.arange(c)[None, :], c)
+        codes = b[co:co + r * c][pos]
         scales = b[so:so + rs * cs].reshape(rs, cs)
         return mxfp4.decode(codes, scales)
     return mat("gate"), mat("up"), mat("down")

@@ -136,6 +136,58 @@ __device__ __forceinline__ void load_row_sc(const uint8_t* codes, const uint8_t*
 }
 
 // ---------------------------------------------------------------------------
+// Weight codes.  A slot's code sections are stored in tiles of 16 rows x 64
+// bytes (128 elements): tile (row block b = row / 16, K-chunk c) starts at
+// b * 16 * (K/2) + c * 1024, its rows one after another, each w_c bytes wide
+// (64, or what is left of the row for a last partial chunk).  So every 16-byte
+// unit a load instruction of the kernels reads for 16 rows lies in one 1 KB
+// run of memory.  `blk` is the start of a 16-row block.
+// ---------------------------------------------------------------------------
+constexpr int kTileBytes = 1024;  // one tile: 16 rows x 64 code bytes
+
+__device__ __forceinline__ const uint8_t* wcode_unit(const uint8_t* blk, size_t crow, int r,
+                                                     int bi) {
+  const int c = bi >> 2;
+  const int w = min(64, (int)crow - 64 * c);
+  return blk + (size_t)c * kTileBytes + r * w + (bi & 3) * 16;
+}
+
+// This lane's code units of super-chunk sc (K % 512 == 0): chunks 4sc + i,
+// unit g, row r of the block.
+__device__ __forceinline__ void load_wcodes_full(const uint8_t* blk, int sc, int r, int g,
+                                                 RowSC& w) {
+  const uint8_t* q = blk + (size_t)sc * 4 * kTileBytes + r * 64 + g * 16;
+  w.q[0] = *reinterpret_cast<const uint4*>(q);
+  w.q[1] = *reinterpret_cast<const uint4*>(q + kTileBytes);
+  w.q[2] = *reinterpret_cast<const uint4*>(q + 2 * kTileBytes);
+  w.q[3] = *reinterpret_cast<const uint4*>(q + 3 * kTileBytes);
+}
+
+// Super-chunk sc of weight row r of the block at blk (codes) with its scale
+// row at `scales`; FULL as load_row_sc.  Blocks at or past nblk read as zero.
+template <bool FULL>
+__device__ __forceinline__ void load_wrow_sc(const uint8_t* blk, size_t crow, int r,
+                                             const uint8_t* scales, int sc, int g, int nblk,
+                                             RowSC& w) {
+  if (FULL) {
+    load_wcodes_full(blk, sc, r, g, w);
+    load_scales_full(scales, sc, g, w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int bi = sc * 16 + 4 * i + g;
+      if (bi < nblk) {
+        w.q[i] = *reinterpret_cast<const uint4*>(wcode_unit(blk, crow, r, bi));
+        w.s[i] = scales[bi];
+      } else {
+        w.q[i] = make_uint4(0u, 0u, 0u, 0u);
+        w.s[i] = 127u;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // MXFP6 (E2M3) activation operands of the small-batch kernels: a block of 32
 // elements is 24 bytes, element i at bits [6i, 6i+6) -- the six-register
 // operand of the block-scaled instruction with the E2M3 format (lane -> row and
@@ -526,9 +578,10 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
   const int nsc = (nblk + 15) / 16;
   const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
   const size_t crow = (size_t)H / 2, srow = (size_t)H / 32;
-  const uint8_t* gc0 = base + p.off_gc + (size_t)(n0 + r) * crow;
+  // 16-row code blocks of the two tiles (rows n0.., n0 + 16..)
+  const uint8_t* gc0 = base + p.off_gc + (size_t)n0 * crow;
   const uint8_t* gc1 = gc0 + 16 * crow;
-  const uint8_t* uc0 = base + p.off_uc + (size_t)(n0 + r) * crow;
+  const uint8_t* uc0 = base + p.off_uc + (size_t)n0 * crow;
   const uint8_t* uc1 = uc0 + 16 * crow;
   const uint8_t* gs0;
   const uint8_t* us0;
@@ -576,10 +629,10 @@ __global__ __launch_bounds__(kWave, 3) void gateup_kernel(GateUpArgs p) {
     for (int sc = 0; sc < nsc; ++sc) {
       RowSC wg0, wg1, wu0, wu1;
       XRow x;
-      load_row_sc<FULL>(gc0, gs0, sc, g, nblk, wg0);
-      load_row_sc<FULL>(gc1, gs1, sc, g, nblk, wg1);
-      load_row_sc<FULL>(uc0, us0, sc, g, nblk, wu0);
-      load_row_sc<FULL>(uc1, us1, sc, g, nblk, wu1);
+      load_wrow_sc<FULL>(gc0, crow, r, gs0, sc, g, nblk, wg0);
+      load_wrow_sc<FULL>(gc1, crow, r, gs1, sc, g, nblk, wg1);
+      load_wrow_sc<FULL>(uc0, crow, r, us0, sc, g, nblk, wu0);
+      load_wrow_sc<FULL>(uc1, crow, r, us1, sc, g, nblk, wu1);
       if (!xc)
         zero_sc(x);
       else if constexpr (FP6)
@@ -655,9 +708,10 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
 #pragma unroll
   for (int tl = 0; tl < 4; ++tl) {
     tv[tl] = n0 + 16 * tl < p.H;  // whole tile valid (H % 16 == 0)
-    const int row = tv[tl] ? n0 + 16 * tl + r : n0 + r;  // an idle tile: a row in range
-    dc[tl] = base + p.off_dc + (size_t)row * crow;
-    ds[tl] = FULL ? wscale + (row - n0) * sstr : base + p.off_ds + (size_t)row * srow;
+    const int row0 = tv[tl] ? n0 + 16 * tl : n0;  // an idle tile: a block in range
+    dc[tl] = base + p.off_dc + (size_t)row0 * crow;  // the tile's 16-row code block
+    ds[tl] = FULL ? wscale + (row0 + r - n0) * sstr
+                  : base + p.off_ds + (size_t)(row0 + r) * srow;
   }
   RowSC pre[4];  // FULL: super-chunk 0 codes of the first column block, loaded early
   XRow prex;     // FULL: and of its activation rows (codes; scale bytes in prexs)
@@ -666,7 +720,7 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
     // Issued before the staging waits, so they are in flight together.
 #pragma unroll
     for (int tl = 0; tl < 4; ++tl)
-      if (tv[tl]) load_codes_full(dc[tl], 0, g, pre[tl]);
+      if (tv[tl]) load_wcodes_full(dc[tl], 0, r, g, pre[tl]);
     if (p0 + r < p1) {
       const uint8_t* hc = p.hq + (size_t)(p0 + r) * p.hrow;
       if constexpr (FP6)
@@ -719,7 +773,7 @@ __global__ __launch_bounds__(kWave, 3) void down_kernel(DownArgs p) {
       for (int tl = 0; tl < 4; ++tl) {
         if (tv[tl]) {
           RowSC w;
-          load_row_sc<FULL>(dc[tl], ds[tl], sc, g, nblk, w);
+          load_wrow_sc<FULL>(dc[tl], crow, r, ds[tl], sc, g, nblk, w);
           acc[tl] = mfma_superchunk(w, x, acc[tl]);
         }
       }
@@ -1007,8 +1061,8 @@ struct PipeSrc {
 __device__ __forceinline__ void pipe_issue(uint8_t* smem, const PipeSrc& src, int q, int wave) {
   uint8_t* st = smem + (q % kRing) * kStage;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    dma16(src.a[j] + (size_t)q * kRowC, st + wave * (64 * kRowC) + j * 1024);
+  for (int j = 0; j < 4; ++j)  // stage q of a 16-row block: its tile q, 1 KB
+    dma16(src.a[j] + (size_t)q * kTileBytes, st + wave * (64 * kRowC) + j * 1024);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + (2 * wave + j) * 1024);
@@ -1134,9 +1188,12 @@ __device__ __forceinline__ void pipe_weight_src(PipeSrc& src, const uint8_t* con
                                                 int lane) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int wr = 16 * j + (lane >> 2), t = wr >> 5, rr = wr & 31;
+    // load j: the 16-row block wrow[t] + (16j % 32).. (a tile row lane/4,
+    // unit (lane % 4) ^ swizzle); stage q reads the block's tile q
+    const int wr = 16 * j + (lane >> 2), t = wr >> 5;
     const int b = (lane & 3) ^ ((wr >> 2) & 3);
-    src.a[j] = wcodes[t] + (size_t)(wrow[t] + rr) * crow + b * 16;
+    src.a[j] = wcodes[t] + (size_t)(wrow[t] + ((16 * j) & 31)) * crow + (lane >> 2) * kRowC +
+               b * 16;
   }
   const int t = lane >> 5, rr = lane & 31;
   const uint8_t* sbase = t ? wscales[1] : wscales[0];
@@ -1319,8 +1376,8 @@ struct PipeSrc6 {
 __device__ __forceinline__ void pipe6_issue(uint8_t* smem, const PipeSrc6& src, int q, int wave) {
   uint8_t* st = smem + (q % kRing) * kStage6;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    dma16(src.a[j] + (size_t)q * kRowC, st + wave * (32 * kRowC) + j * 1024);
+  for (int j = 0; j < 2; ++j)  // stage q of a 16-row block: its tile q, 1 KB
+    dma16(src.a[j] + (size_t)q * kTileBytes, st + wave * (32 * kRowC) + j * 1024);
 #pragma unroll
   for (int j = 0; j < 3; ++j)
     dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA6 + wave * (32 * kRowB6) + j * 1024);
@@ -1449,9 +1506,10 @@ __device__ __forceinline__ void pipe6_weight_src(PipeSrc6& src, const uint8_t* c
                                                  int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int wr = 16 * j + (lane >> 2), t = wr >> 4, rr = wr & 15;
+    // load j: the 16-row block at wrow[j] (a tile row lane/4, unit (lane % 4) ^ swizzle)
+    const int wr = 16 * j + (lane >> 2);
     const int b = (lane & 3) ^ ((wr >> 2) & 3);
-    src.a[j] = wcodes[t] + (size_t)(wrow[t] + rr) * crow + b * 16;
+    src.a[j] = wcodes[j] + (size_t)wrow[j] * crow + (lane >> 2) * kRowC + b * 16;
   }
   const int wr = lane & 31, t = wr >> 4, rr = wr & 15;  // lanes 32-63 issue no scale load
   src.as = (t ? wscales[1] : wscales[0]) + (size_t)((t ? wrow[1] : wrow[0]) + rr) * srow;

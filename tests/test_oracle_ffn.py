@@ -140,3 +140,30 @@ def test_shared_expert_closed_forms():
                   shared_bytes=buf)
     xhat = moe.quantise_rows(moe.bf16_to_f64(lay.x_bits))
     assert np.allclose(r["out"], moe.expert_ffn(xhat, W), rtol=1e-12, atol=1e-15)
+
+
+def test_slot_code_tiles_hand_worked():
+    """Code bytes of a slot section in tiles of 16 rows x 64 bytes, worked by
+    hand for 32 rows of 80 code bytes (K = 160: one full tile and one 16-byte
+    tile per row block):
+      row 0, byte 0  -> 0;  row 1, byte 0 -> 64 (second row of the first tile);
+      row 0, byte 64 -> 1024 (first row of the block's 16-byte tile);
+      row 17, byte 70 -> 1280 (block 1) + 1024 + 1*16 + 6 = 2326;
+      row 31, byte 79 -> 1280 + 1024 + 15*16 + 15 = 2559 (the last byte)."""
+    pos = moe.code_position
+    want = {(0, 0): 0, (1, 0): 64, (0, 64): 1024, (17, 70): 2326, (31, 79): 2559,
+            (16, 0): 1280, (15, 63): 15 * 64 + 63}
+    for (n, j), p in want.items():
+        assert int(pos(np.array(n), np.array(j), 80)) == p, (n, j)
+    # every byte lands once
+    allp = pos(np.arange(32)[:, None], np.arange(80)[None, :], 80)
+    assert sorted(allp.reshape(-1).tolist()) == list(range(32 * 80))
+    # the packer puts byte (n, j) of its row-major codes where the formula says
+    codes = (np.arange(32)[:, None] * 7 + np.arange(80)[None, :] * 3).astype(np.uint8)
+    tiled = fixtures.tile_codes(codes)
+    assert np.array_equal(tiled[allp], codes)
+    # whole tiles only: a 64-byte tile of 16 rows is 1 KB, rows contiguous
+    c2 = (np.arange(16)[:, None] * 5 + np.arange(128)[None, :]).astype(np.uint8)
+    t2 = fixtures.tile_codes(c2)
+    assert np.array_equal(t2[:1024].reshape(16, 64), c2[:, :64])
+    assert np.array_equal(t2[1024:].reshape(16, 64), c2[:, 64:])

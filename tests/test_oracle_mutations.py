@@ -172,3 +172,19 @@ def test_mxfp6_scale_from_fp4_exponent(monkeypatch):
             return m, e + 1
     monkeypatch.setattr(mxfp6, "np", NP())
     _fails(t6.test_round_trip_every_value_at_many_scales)
+
+
+def test_slot_codes_read_row_major(monkeypatch):
+    # the oracle reading code bytes row by row instead of in 16-row tiles
+    monkeypatch.setattr(moe, "code_position", lambda n, j, nb: n * nb + j)
+    _fails(tf.test_slot_code_tiles_hand_worked)
+
+
+def test_slot_tiles_unit_major(monkeypatch):
+    # inside a tile, the 16-byte units of all 16 rows first, then the next unit
+    def pos(n, j, nb):
+        c = j // 64
+        return (n // 16) * (16 * nb) + c * 1024 + ((j - 64 * c) // 16) * 256 + (n % 16) * 16 \
+            + j % 16
+    monkeypatch.setattr(moe, "code_position", pos)
+    _fails(tf.test_slot_code_tiles_hand_worked)
