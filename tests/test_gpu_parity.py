@@ -733,3 +733,25 @@ def test_stage_events_bracket_gateup(name):
     assert t12 > 0.0
     assert min(t01, t23, t34) >= 0.0
     assert evs[0].elapsed_time(evs[4]) >= t12
+
+
+@pytest.mark.parametrize("act", [0, 1])
+def test_fused_down_combine_bit_identical(act):
+    """Batches of up to 32 tokens run down and combine as one kernel; 33
+    tokens take the two-kernel path.  The first 32 tokens give the same bits
+    either way (same instruction sequence per y element, same fused
+    multiply-adds in pick order)."""
+    say(f"fused down+combine (T=32) against the two-kernel path (T=33), act_format {act}")
+    lay = fixtures.tiny_layer(T=33, H=1024, E=64, k=8, I=512, n_routable=40, seed=57,
+                              bias_scale=0.5)
+    full = GpuLayer(lay, act_format=act)
+    full.route()
+    full.experts()
+    part = GpuLayer(lay, T=32, x_bits=lay.x_bits[:32], arena=full.arena, act_format=act)
+    part.route()
+    part.experts()
+    a = part.buf.out.cpu().numpy()
+    b = full.buf.out.cpu().numpy()[:32]
+    assert np.array_equal(a, b)
+    if act == 0:  # MXFP6 parity of the fused path: the decode cases of test_gpu_mxfp6
+        _layer_parity(part)
