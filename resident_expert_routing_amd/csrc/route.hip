@@ -68,7 +68,9 @@ __device__ void quantize_x_elements(const uint16_t* __restrict__ x, int T, int H
 
 // Small T (decode batches): a workgroup owns one expert and up to RS_T tokens;
 // thread c owns chunk c for all of them (the router chunk is loaded once, RS_T
-// independent fma chains); the chunk sums meet in LDS.  They are added in runs
+// independent fma chains) -- or, with at most 128 chunks (SPLIT), threads c and
+// c + 128 own chunk c for half of the tokens each, so every thread works and
+// holds half the x registers; the chunk sums meet in LDS.  They are added in runs
 // of RS_RUN consecutive chunks (ascending, from 0), and the run sums in
 // ascending order (from 0).  Workgroups from `nrb` on encode the activation
 // rows instead (one element per thread), alongside the dot products.
@@ -80,14 +82,18 @@ constexpr int RS_MAX_CHUNKS = 256;
 constexpr int RS_RUN = 16;
 // z[tok[i], e] for the nt (<= RS_T) tokens tok[0..nt) and one expert, by the
 // whole workgroup (thread c owns chunk c).
+template <bool SPLIT>
 __device__ __forceinline__ void small_dot_block(const uint16_t* __restrict__ x,
                                                 const float* __restrict__ w, int H, int E,
                                                 double* __restrict__ z, int e, const int* tok,
                                                 int nt) {
   __shared__ double part[RS_T][RS_MAX_CHUNKS + 1];
   __shared__ double runs[RS_T][RS_MAX_CHUNKS / RS_RUN];
-  const int nchunk = H / kRouterChunk;  // H % 32 == 0
-  const int c = threadIdx.x;
+  const int nchunk = H / kRouterChunk;  // H % 32 == 0 (SPLIT: at most 128 chunks)
+  // SPLIT: thread (c, half) takes chunk c for tokens 4 half .. 4 half + 3
+  constexpr int kTok = SPLIT ? RS_T / 2 : RS_T;
+  const int c = SPLIT ? (int)(threadIdx.x & 127) : (int)threadIdx.x;
+  const int ibeg = SPLIT ? (int)(threadIdx.x >> 7) * kTok : 0;
   if (c < nchunk) {
     const int h0 = c * kRouterChunk;
     const float4* w4 = reinterpret_cast<const float4*>(w + (size_t)e * H + h0);
@@ -97,17 +103,19 @@ __device__ __forceinline__ void small_dot_block(const uint16_t* __restrict__ x,
     // every token's x chunk is loaded before the first chain starts (tokens
     // past the batch load its last one and are never stored): loads inside
     // `if (i < nt)` were issued one token at a time, a round trip each
-    uint4 xv_all[RS_T][kRouterChunk / 8];
+    uint4 xv_all[kTok][kRouterChunk / 8];
 #pragma unroll
-    for (int i = 0; i < RS_T; ++i) {
+    for (int ii = 0; ii < kTok; ++ii) {
+      const int i = ibeg + ii;
       const uint4* x4 = reinterpret_cast<const uint4*>(x + (size_t)tok[min(i, nt - 1)] * H + h0);
 #pragma unroll
-      for (int q = 0; q < kRouterChunk / 8; ++q) xv_all[i][q] = x4[q];
+      for (int q = 0; q < kRouterChunk / 8; ++q) xv_all[ii][q] = x4[q];
     }
 #pragma unroll
-    for (int i = 0; i < RS_T; ++i) {
+    for (int ii = 0; ii < kTok; ++ii) {
+      const int i = ibeg + ii;
       {
-        const uint4 (&xv)[kRouterChunk / 8] = xv_all[i];
+        const uint4 (&xv)[kRouterChunk / 8] = xv_all[ii];
         double s = 0.0;
 #pragma unroll
         for (int q = 0; q < kRouterChunk / 8; ++q) {
@@ -127,8 +135,9 @@ __device__ __forceinline__ void small_dot_block(const uint16_t* __restrict__ x,
   __syncthreads();
   // thread (token i, run q) adds the chunk sums of run q
   const int nrun = (nchunk + RS_RUN - 1) / RS_RUN;
+  const int tc = threadIdx.x;
   {
-    const int i = c / nrun, q = c % nrun;
+    const int i = tc / nrun, q = tc % nrun;
     if (i < nt) {
       double acc = 0.0;
       const int c1 = min(nchunk, (q + 1) * RS_RUN);
@@ -137,13 +146,14 @@ __device__ __forceinline__ void small_dot_block(const uint16_t* __restrict__ x,
     }
   }
   __syncthreads();
-  if (c < nt) {
+  if (tc < nt) {
     double acc = 0.0;
-    for (int q = 0; q < nrun; ++q) acc += runs[c][q];
-    z[(size_t)tok[c] * E + e] = acc;
+    for (int q = 0; q < nrun; ++q) acc += runs[tc][q];
+    z[(size_t)tok[tc] * E + e] = acc;
   }
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restrict__ x,
                                                         const float* __restrict__ w, int T, int H,
                                                         int E, double* __restrict__ z,
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(256) void router_small_f64(const uint16_t* __restri
   int tok[RS_T];
 #pragma unroll
   for (int i = 0; i < RS_T; ++i) tok[i] = t0 + i;
-  small_dot_block(x, w, H, E, z, e, tok, nt);
+  small_dot_block<SPLIT>(x, w, H, E, z, e, tok, nt);
 }
 
 // Float64 logits where a flagged token's picks can still change.  With every
@@ -1531,8 +1541,14 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     const int nrb = E * ((T + RS_T - 1) / RS_T);
     const size_t nx = ((size_t)T * H + 255) / 256;
     const int nxb = (int)(nx < 1024 ? nx : 1024);
-    router_small_f64<<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, a->xq, xq_row,
-                                                    fmt, nrb, fused ? counter : nullptr);
+    if (nchunk <= 128)
+      router_small_f64<true><<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z, a->xq,
+                                                            xq_row, fmt, nrb,
+                                                            fused ? counter : nullptr);
+    else
+      router_small_f64<false><<<nrb + nxb, 256, 0, stream>>>(a->x, a->w_router, T, H, E, z,
+                                                             a->xq, xq_row, fmt, nrb,
+                                                             fused ? counter : nullptr);
   } else if (approx) {
     split_w_bf16x3<<<E, 256, 0, stream>>>(a->w_router, E, H, planes, wnorm2, flags);
     router_bf16x3<<<dim3((E + RB_E - 1) / RB_E, (T + RB_MT - 1) / RB_MT, ks), RB_THREADS, 0,
