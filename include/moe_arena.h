@@ -192,7 +192,8 @@ size_t moe_workspace_bytes(int op, int T, int H, int E, int k, int I, int S);
  * T = 0 is valid (only slot_offsets is written, all zero).
  * stage_events (host array, nullable): MOE_STAGE_EVENTS events recorded on
  *          `stream` when T > 0: before the router logits, before selection,
- *          before bucket counting, before the scatter, and after it -- so a
+ *          before bucket counting (with hist_row, larger batches count the
+ *          demand's chunk sums there too), before the scatter, and after it -- so a
  *          caller can time each kernel stage.  For T <= 64, E <= 256 and
  *          H <= 8192, selection and bucketing run as one kernel and the last
  *          three events are recorded together after it.  A null entry is not

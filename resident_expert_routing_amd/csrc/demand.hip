@@ -8,52 +8,37 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "demand_sums.hpp"
 
 namespace moe {
 
 // Partial (or, with part == null, final) demand of chunk blockIdx.x.  With
-// E <= 256 the chunk's picks are first spread into a [token][expert] score
-// table (zero where a token did not pick the expert; a token's picks are
-// distinct experts), so each expert's sum is a 64-step loop over the tokens in
-// ascending order -- adding the zeros changes no bit of the sum.
-constexpr int kDemandTableE = 256;
-
+// E <= kDemandTableE the chunk goes through the LDS score table; above it each
+// expert's sum scans the chunk's picks in order (still ascending tokens).
 __global__ __launch_bounds__(1024) void demand_chunks(const int32_t* __restrict__ te,
                                                       const float* __restrict__ ts, int T, int k,
                                                       int E, double* __restrict__ part,
                                                       double* __restrict__ hist,
                                                       float* __restrict__ delta) {
+  const int c = blockIdx.x;
+  if (E <= kDemandTableE) {
+    __shared__ float table[kDemandChunk][kDemandTableE];
+    demand_chunk_table(te, ts, T, k, E, c, table, part, hist, delta);
+    return;
+  }
   __shared__ int se[kDemandChunk * MOE_MAX_K];
   __shared__ float ss[kDemandChunk * MOE_MAX_K];
-  __shared__ float table[kDemandChunk][kDemandTableE];
-  const int c = blockIdx.x;
   const int t0 = c * kDemandChunk;
-  const int nt = min(kDemandChunk, T - t0);
-  const int n = nt * k;
-  const bool use_table = E <= kDemandTableE;
-  if (use_table) {
-    for (int i = threadIdx.x; i < kDemandChunk * kDemandTableE; i += blockDim.x)
-      (&table[0][0])[i] = 0.f;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const int e = te[(size_t)t0 * k + i];
-      if (e >= 0 && e < E) table[i / k][e] = ts[(size_t)t0 * k + i];
-    }
-  } else {
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      se[i] = te[(size_t)t0 * k + i];
-      ss[i] = ts[(size_t)t0 * k + i];
-    }
+  const int n = min(kDemandChunk, T - t0) * k;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    se[i] = te[(size_t)t0 * k + i];
+    ss[i] = ts[(size_t)t0 * k + i];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     double acc = 0.0;
-    if (use_table) {
-      for (int t = 0; t < nt; ++t) acc += (double)table[t][e];
-    } else {
-      for (int i = 0; i < n; ++i)
-        if (se[i] == e) acc += (double)ss[i];
-    }
+    for (int i = 0; i < n; ++i)
+      if (se[i] == e) acc += (double)ss[i];
     if (part) {
       part[(size_t)c * E + e] = acc;
     } else {
@@ -63,25 +48,10 @@ __global__ __launch_bounds__(1024) void demand_chunks(const int32_t* __restrict_
   }
 }
 
-// Chunk partials added in ascending chunk order; the loads of a group of 16
-// chunks are issued before their additions.
 __global__ __launch_bounds__(1024) void demand_finalize(const double* __restrict__ part, int nchunk,
                                                         int E, double* __restrict__ hist,
                                                         float* __restrict__ delta) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    double acc = 0.0;
-    int c = 0;
-    for (; c + 16 <= nchunk; c += 16) {
-      double v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = part[(size_t)(c + i) * E + e];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc += v[i];
-    }
-    for (; c < nchunk; ++c) acc += part[(size_t)c * E + e];
-    hist[e] += acc;
-    if (delta) delta[e] = (float)acc;
-  }
+  demand_finalize_sums(part, nchunk, E, hist, delta);
 }
 
 // hist[i] *= factor for every entry (the history's forgetting before a re-plan).

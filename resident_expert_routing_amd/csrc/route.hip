@@ -6,7 +6,10 @@
 // router then picks only resident (or hot-ring) experts, a miss replaced by the
 // next-best resident expert; the chosen weights are renormalised.  Rows are
 // then named by index per slot (colibri cluster page, COLIEX01 v2 paragraph).
+#include <algorithm>
+
 #include "common.hpp"
+#include "demand_sums.hpp"
 
 namespace moe {
 
@@ -1217,6 +1220,25 @@ __global__ __launch_bounds__(256) void bucket_hist(const int32_t* __restrict__ s
     counts[(size_t)s * nchunk + blockIdx.x] = __popcll(bits[s]);
 }
 
+// bucket_hist with, first, the demand partial of the same chunk of tokens
+// (E <= kDemandTableE): part[c][e] as moe_demand_accumulate's chunk sums.  The
+// dynamic LDS (max(kDemandTableBytes, S * 8) bytes) holds the score table,
+// then the token masks.
+__global__ __launch_bounds__(256) void bucket_hist_demand(const int32_t* __restrict__ sel_slot,
+                                                          int T, int k, int S, int nchunk,
+                                                          int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ te,
+                                                          const float* __restrict__ ts, int E,
+                                                          double* __restrict__ part) {
+  extern __shared__ unsigned long long bits[];
+  demand_chunk_table(te, ts, T, k, E, blockIdx.x, reinterpret_cast<float(*)[kDemandTableE]>(bits),
+                     part, nullptr, nullptr);
+  __syncthreads();  // the table's last reads before the masks overwrite it
+  chunk_token_masks(sel_slot, T, k, S, bits);
+  for (int s = threadIdx.x; s < S; s += blockDim.x)
+    counts[(size_t)s * nchunk + blockIdx.x] = __popcll(bits[s]);
+}
+
 // One workgroup: offsets = exclusive scan of the slot totals (S+1 entries),
 // and counts[s][c] replaced by the first perm position of chunk c's
 // assignments in slot s.  perm entries past the total are set to -1.  When
@@ -1350,6 +1372,8 @@ __global__ __launch_bounds__(256) void bucket_place(const int32_t* __restrict__ 
 // assignments at offsets[s] + (earlier chunks of s) + rank.  Workgroup 0
 // writes offsets; perm positions past the total are set to -1, spread over
 // the workgroups.  Same perm and offsets as bucket_scan then bucket_place.
+// With dpart non-null the grid has one more workgroup, which finishes the
+// demand from the chunk partials that bucket_hist_demand wrote.
 constexpr int kFusedScanMaxS = 2048;
 constexpr int kFusedScanMaxInts = 32 * 1024;
 
@@ -1357,7 +1381,16 @@ __global__ __launch_bounds__(256) void bucket_place_scan(const int32_t* __restri
                                                          int T, int k, int S, int nchunk, int A,
                                                          const int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ perm) {
+                                                         int32_t* __restrict__ perm,
+                                                         const double* __restrict__ dpart, int E,
+                                                         double* __restrict__ hist,
+                                                         float* __restrict__ delta) {
+  if (blockIdx.x == nchunk) {
+    // the extra workgroup (launched when dpart is non-null): the demand's
+    // chunk partials added into hist
+    demand_finalize_sums(dpart, nchunk, E, hist, delta);
+    return;
+  }
   extern __shared__ unsigned long long bits[];  // S token masks, then tot[S], pre[S]
   int* tot = reinterpret_cast<int*>(bits + S);
   int* pre = tot + S;
@@ -1620,22 +1653,34 @@ extern "C" MOE_EXPORT int moe_route(const moe_route_args* a, hipStream_t stream)
     const int nwg = (T + 3) / 4 < 512 ? (T + 3) / 4 : 512;
     launch_select((unsigned)nwg);
   }
-  if (a->hist_row) {
+  const int nbc = (T + kBucketChunk - 1) / kBucketChunk;
+  const bool fused_scan =
+      S > 0 && S <= kFusedScanMaxS && (size_t)S * nbc <= (size_t)kFusedScanMaxInts;
+  // the demand's chunk sums ride on the bucket counting, its final sums on
+  // the placement (same chunks of 64 tokens; same float64 sums and order)
+  const bool demand_in_buckets = a->hist_row && fused_scan && E <= kDemandTableE &&
+                                 T > kDemandChunk && kDemandChunk == kBucketChunk;
+  if (a->hist_row && !demand_in_buckets) {
     const int st = moe_demand_launch_internal(a->topk_expert, a->topk_score, T, k, E, a->hist_row,
                                               a->delta, dws, stream);
     if (st != MOE_OK) return st;
   }
   if (!record_stage(ev,2, stream)) return MOE_EHIP;
-  const int nbc = (T + kBucketChunk - 1) / kBucketChunk;
   int32_t* counts = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(a->ws) + route_z_bytes(T, E) +
                                                moe_demand_ws_bytes_internal(T, E));
   const size_t mask_lds = (size_t)(S > 0 ? S : 1) * sizeof(unsigned long long);
-  if (S > 0) bucket_hist<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts);
-  if (S > 0 && S <= kFusedScanMaxS && (size_t)S * nbc <= (size_t)kFusedScanMaxInts) {
+  double* dpart = demand_in_buckets ? static_cast<double*>(dws) : nullptr;
+  if (demand_in_buckets)
+    bucket_hist_demand<<<nbc, 256, std::max(mask_lds, kDemandTableBytes), stream>>>(
+        a->sel_slot, T, k, S, nbc, counts, a->topk_expert, a->topk_score, E, dpart);
+  else if (S > 0)
+    bucket_hist<<<nbc, 256, mask_lds, stream>>>(a->sel_slot, T, k, S, nbc, counts);
+  if (fused_scan) {
     // small count tables: every placement workgroup scans them itself
     if (!record_stage(ev,3, stream)) return MOE_EHIP;
-    bucket_place_scan<<<nbc, 256, (size_t)S * 16, stream>>>(a->sel_slot, T, k, S, nbc, A, counts,
-                                                            a->slot_offsets, a->perm);
+    bucket_place_scan<<<nbc + (dpart ? 1 : 0), 256, (size_t)S * 16, stream>>>(
+        a->sel_slot, T, k, S, nbc, A, counts, a->slot_offsets, a->perm, dpart, E, a->hist_row,
+        a->delta);
   } else {
     const size_t scan_lds =
         (size_t)S * nbc <= (size_t)kScanLdsInts ? (size_t)S * nbc * sizeof(int32_t) : 0;

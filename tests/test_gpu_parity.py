@@ -687,13 +687,16 @@ def test_scale_bump_doubles_expert():
     assert np.array_equal(bumped, 2 * base)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "prefill"])
-def test_route_with_demand_equals_separate_call(name):
-    """moe_route with hist_row gives bit-for-bit the demand of moe_demand_accumulate."""
+@pytest.mark.parametrize("name,T", [("tiny", None), ("decode", None), ("prefill", None),
+                                    ("prefill", 1000), ("long", None)])
+def test_route_with_demand_equals_separate_call(name, T):
+    """moe_route with hist_row gives bit-for-bit the demand of moe_demand_accumulate
+    (larger batches: chunk sums beside the bucket counts, final sums beside the
+    placement; T=1000 ends on a part chunk of 40 tokens)."""
     import torch
     from resident_expert_routing_amd import runtime as R
-    g = gpu_layer(name)
-    say(f"moe_route with fused demand on {name}")
+    g = gpu_layer(name, T=T)
+    say(f"moe_route with fused demand on {name} T={g.T}")
     g.route()
     g.hist.zero_()
     g.demand()
