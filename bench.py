@@ -23,7 +23,8 @@ other workload, with its own time per step, roofline and CPU-oracle baseline:
 Layer workloads rotate over 4 token batches and 4 copies of the arena so the
 256 MB Infinity Cache cannot serve expert bytes reused from a previous step.
 The decode, prefill and long blocks also time, under "act_mxfp6", the
-activation-format variant (activation and h rows in MXFP6, same weights).
+activation-format variant (activation and h rows in MXFP6, same weights);
+--no-act-mxfp6 leaves that leg out.
 
 Timing: W warmup steps, then K steps between two events on the launch stream
 (no other instrumentation) give `ms_per_step`.  A second run of the K steps
@@ -76,6 +77,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the achievable-peak microbenchmarks (for profiler runs)")
+    ap.add_argument("--no-act-mxfp6", action="store_true",
+                    help="skip the MXFP6 activation-row leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (to scale HBM byte counters)")
     return ap.parse_args()
@@ -498,7 +501,7 @@ def layer_workload(name: str, args, dev, steps: int, warmup: int) -> dict:
     if name == "long":
         block["hot_read"] = hot_read_timing(base, xs[0], w_router, bias, arenas[0], buf, E,
                                             stream)
-    if name in ("decode", "prefill", "long"):
+    if name in ("decode", "prefill", "long") and not args.no_act_mxfp6:
         block["act_mxfp6"] = act_mxfp6_timing(name, T, H, E, k, I, S, xs, w_router, bias,
                                               expert_slot, arenas, hist, U, stream, K,
                                               min(warmup, 5), args, dev)
