@@ -1279,7 +1279,8 @@ __device__ __forceinline__ void pipe_mainloop(uint8_t* smem, const PipeSrc& src,
 
 // Weight-side sources: wave row wr (0..63) of the stage is row wrow[wr / 32] +
 // wr % 32 of the section at wcodes[wr / 32] / wscales[wr / 32].
-__device__ __forceinline__ void pipe_weight_src(PipeSrc& src, const uint8_t* const (&wcodes)[2],
+template <typename Src>
+__device__ __forceinline__ void pipe_weight_src(Src& src, const uint8_t* const (&wcodes)[2],
                                                 const uint8_t* const (&wscales)[2],
                                                 const int (&wrow)[2], size_t crow, size_t srow,
                                                 int lane) {
@@ -1439,31 +1440,30 @@ __global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
 
 
 // ===========================================================================
-// Pipelined kernels with MXFP6 activation rows (act_format MOE_ACT_MXFP6).
-// A B row takes 96 bytes per 128-element stage instead of 64, so the tile
-// shape changes to stay within half of a CU's LDS: each wave owns one 32-row
-// weight tile (gate/up: rows 0-15 gate and 16-31 up of the same 16 rows of
-// I; down: 32 rows of H) against the tile's 128 columns.  A stage is 8 KB of
-// weight codes and 12 KB of activation codes; with the two 2 KB scale-group
-// buffers the three-stage ring takes 64 KB, so two workgroups share a CU as
-// in the MXFP4 kernels.  The instruction is the same 32x32x64 block-scaled
-// one with E2M1 A and E2M3 B operands (measured at the E2M1 x E2M1 rate).
+// Pipelined kernels with MXFP6 activation rows (act_format MOE_ACT_MXFP6):
+// the MXFP4 kernels' tiles -- each wave two 32-row weight tiles (gate/up:
+// rows n0.. of gate and of up, 128 rows of I per workgroup; down: 64 rows of
+// H, 256 per workgroup) against the 128 columns -- with E2M3 B operands.  A B
+// row takes 96 bytes per 128-element stage instead of 64, so a stage is 16 KB
+// of weight codes and 12 KB of activation codes, and the ring holds two
+// stages, one issued ahead: 62 KB with the scale-group buffer, two workgroups
+// per CU.  (With two workgroups per CU a ring of two stages ran the MXFP4
+// kernels as fast as a ring of three; these tiles read each activation row
+// for half as many N-tiles as one 32-row tile per wave did.)  The instruction
+// is the same 32x32x64 block-scaled one with E2M1 A and E2M3 B operands
+// (measured at the E2M1 x E2M1 rate).
 // ===========================================================================
 constexpr int kRowB6 = kKc / 32 * 24;            // activation code bytes per row per stage (96)
-constexpr int kStageA6 = 4 * 32 * kRowC;         // weight code rows of the four waves (8 KB)
+constexpr int kRing6 = 2;
 constexpr int kStageB6 = kTileM * kRowB6;        // activation code rows (12 KB)
-constexpr int kStage6 = kStageA6 + kStageB6;
-constexpr int kGroupSA6 = 4 * 32 * kGroupRow;    // weight rows' scales (2 KB)
-constexpr int kPipeLds6 = kRing * kStage6 + kGroupSA6 + kGroupSB;  // 65,536 bytes
+constexpr int kStage6 = kStageA + kStageB6;      // 28 KB
+constexpr int kPipeLds6 = kRing6 * kStage6 + kGroupSA + kGroupSB;  // 63,488 bytes
 static_assert(2 * kPipeLds6 <= 160 * 1024, "two workgroups per CU");
 static_assert(kZeroPage >= kRowB6, "an absent activation row reads a stage from the zero page");
-// Loads issued by each wave per stage: 2 weight-code and 3 activation-code
-// loads; per group, two half-wave scale loads.
-constexpr int kLoadsPerStage6 = 5;
 
 struct PipeSrc6 {
-  const uint8_t* a[2];   // weight codes, load j: wave row 16j + lane/4, block already swizzled
-  const uint8_t* as;     // weight scales (lanes 0-31): wave row lane
+  const uint8_t* a[4];   // weight codes, as PipeSrc
+  const uint8_t* as;     // weight scales, as PipeSrc
   const uint8_t* b[3];   // activation codes, load j: 16-byte unit 64j + lane of the wave's rows
   int bstep[3];          // code bytes per stage (96; 0 for an absent row on the zero page)
   const uint8_t* bs;     // activation scales (lanes 0-31): tile row 32 wave + lane
@@ -1471,31 +1471,30 @@ struct PipeSrc6 {
 };
 
 __device__ __forceinline__ void pipe6_issue(uint8_t* smem, const PipeSrc6& src, int q, int wave) {
-  uint8_t* st = smem + (q % kRing) * kStage6;
+  uint8_t* st = smem + (q % kRing6) * kStage6;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)  // stage q of a 16-row block: its tile q, 1 KB
-    dma16(src.a[j] + (size_t)q * kTileBytes, st + wave * (32 * kRowC) + j * 1024);
+  for (int j = 0; j < 4; ++j)  // stage q of a 16-row block: its tile q, 1 KB
+    dma16(src.a[j] + (size_t)q * kTileBytes, st + wave * (64 * kRowC) + j * 1024);
 #pragma unroll
   for (int j = 0; j < 3; ++j)
-    dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA6 + wave * (32 * kRowB6) + j * 1024);
+    dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + wave * (32 * kRowB6) + j * 1024);
 }
 
+// The scale bytes of group g: the wave's 64 weight rows at lanes 0-63, its
+// 32 activation rows at lanes 0-31 (the layout of pipe_issue_scales).
 __device__ __forceinline__ void pipe6_issue_scales(uint8_t* smem, const PipeSrc6& src, int g,
                                                    int wave) {
-  uint8_t* sg = smem + kRing * kStage6;
-  if ((threadIdx.x & 63) < 32) {  // lanes 0-31: one row each (partial-lane loads)
-    dma16(src.as + (size_t)g * kGroupRow, sg + wave * (32 * kGroupRow));
-    dma16(src.bs + (size_t)g * src.bsstep, sg + kGroupSA6 + wave * (32 * kGroupRow));
-  }
+  uint8_t* sg = smem + kRing6 * kStage6;
+  dma16(src.as + (size_t)g * kGroupRow, sg + wave * (64 * kGroupRow));
+  if ((threadIdx.x & 63) < 32)
+    dma16(src.bs + (size_t)g * src.bsstep, sg + kGroupSA + wave * (32 * kGroupRow));
 }
 
-// As pipe_wait, with five loads per stage.
-__device__ __forceinline__ void pipe6_wait(int q, int Q) {
-  static_assert(kLoadsPerStage6 == 5 && kAhead == 2 && kGroup == 4, "wait counts below");
-  if (q + 1 < Q)
-    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// A ring of two stages: every load issued so far (stage q's, and its scale
+// group's) has landed; then the barrier makes them visible and frees the
+// stage read in the previous iteration.
+__device__ __forceinline__ void pipe6_wait() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 }
 
@@ -1509,23 +1508,25 @@ __device__ __forceinline__ v16f mfma32x6(const uint4& a, const uint32_t (&b)[6],
 }
 
 struct StepFrags6 {
-  uint4 a;
+  uint4 a[2];
   uint32_t b[4][6];
 };
 
-// Fragments of MFMA step s: the wave's weight row r (16 bytes of block 2s+hh,
-// swizzled as in the MXFP4 kernels) and, per column tile, the 24 bytes of
-// block 2s+hh of activation row 32cb+r, read as the two 16-byte units that
-// hold them (an odd block starts 8 bytes into its first unit).
+// Fragments of MFMA step s: the wave's weight tiles t at row r (16 bytes of
+// block 2s+hh, swizzled as in the MXFP4 kernels) and, per column tile, the
+// 24 bytes of block 2s+hh of activation row 32cb+r, read as the two 16-byte
+// units that hold them (an odd block starts 8 bytes into its first unit).
 __device__ __forceinline__ void read_step6(const uint8_t* st, int s, int wave, int r, int hh,
                                            int swz, StepFrags6& f) {
   const int pb = ((2 * s + hh) ^ swz) * 16;
-  f.a = *reinterpret_cast<const uint4*>(st + wave * (32 * kRowC) + r * kRowC + pb);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    f.a[t] = *reinterpret_cast<const uint4*>(st + wave * (64 * kRowC) + (32 * t + r) * kRowC + pb);
   const int blk = 2 * s + hh;
   const int u0 = 16 * ((3 * blk) >> 1);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
-    const uint8_t* rp = st + kStageA6 + (32 * cb + r) * kRowB6 + u0;
+    const uint8_t* rp = st + kStageA + (32 * cb + r) * kRowB6 + u0;
     const uint4 x0 = *reinterpret_cast<const uint4*>(rp);
     const uint4 x1 = *reinterpret_cast<const uint4*>(rp + 16);
     f.b[cb][0] = hh ? x0.z : x0.x;
@@ -1537,24 +1538,22 @@ __device__ __forceinline__ void read_step6(const uint8_t* st, int s, int wave, i
   }
 }
 
-// This lane's scale words of stage q (4 scale bytes of its weight row r and
-// of each column tile's row r), from the group buffer.
-struct StageScales6 {
-  uint32_t aw, bw[4];
-};
-
+// This lane's scale words of stage q, from the group buffer (as
+// read_stage_scales).
 __device__ __forceinline__ void read_stage_scales6(const uint8_t* smem, int q, int wave, int r,
-                                                   StageScales6& sc) {
-  const uint8_t* sg = smem + kRing * kStage6 + (q % kGroup) * kRowS;
-  sc.aw = *reinterpret_cast<const uint32_t*>(sg + (wave * 32 + r) * kGroupRow);
+                                                   StageScales& sc) {
+  const uint8_t* sg = smem + kRing6 * kStage6 + (q % kGroup) * kRowS;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    sc.aw[t] = *reinterpret_cast<const uint32_t*>(sg + (wave * 64 + 32 * t + r) * kGroupRow);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
-    sc.bw[cb] = *reinterpret_cast<const uint32_t*>(sg + kGroupSA6 + (32 * cb + r) * kGroupRow);
+    sc.bw[cb] = *reinterpret_cast<const uint32_t*>(sg + kGroupSA + (32 * cb + r) * kGroupRow);
 }
 
 __device__ __forceinline__ void pipe6_compute(const uint8_t* smem, int q, int wave, int r, int hh,
-                                              const StageScales6& sc, v16f (&acc)[4]) {
-  const uint8_t* st = smem + (q % kRing) * kStage6;
+                                              const StageScales& sc, v16f (&acc)[2][4]) {
+  const uint8_t* st = smem + (q % kRing6) * kStage6;
   const int swz = (r >> 2) & 3;
   StepFrags6 f[2];
   read_step6(st, 0, wave, r, hh, swz, f[0]);
@@ -1565,51 +1564,38 @@ __device__ __forceinline__ void pipe6_compute(const uint8_t* smem, int q, int wa
     const StepFrags6& cur = f[s];
     const int sh = 8 * (2 * s + hh);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-      acc[cb] = mfma32x6(cur.a, cur.b[cb], acc[cb], sc.aw >> sh, sc.bw[cb] >> sh);
+    for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[t][cb] = mfma32x6(cur.a[t], cur.b[cb], acc[t][cb], sc.aw[t] >> sh, sc.bw[cb] >> sh);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// The K loop over Q = K / 128 stages; issue order and waits as pipe_mainloop.
+// The K loop over Q = K / 128 stages: stage q + 1 is issued into the other
+// ring stage once the barrier of iteration q has freed it.
 __device__ __forceinline__ void pipe6_mainloop(uint8_t* smem, const PipeSrc6& src, int Q, int wave,
-                                               int lane, v16f (&acc)[4]) {
+                                               int lane, v16f (&acc)[2][4]) {
   const int r = lane & 31, hh = lane >> 5;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = zero16();
-  pipe6_issue_scales(smem, src, 0, wave);
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-  for (int q = 0; q < kAhead; ++q)
-    if (q < Q) pipe6_issue(smem, src, q, wave);
+    for (int cb = 0; cb < 4; ++cb) acc[t][cb] = zero16();
+  pipe6_issue_scales(smem, src, 0, wave);
+  pipe6_issue(smem, src, 0, wave);
   for (int q = 0; q < Q; ++q) {
-    pipe6_wait(q, Q);
-    StageScales6 sc;
+    pipe6_wait();
+    StageScales sc;
     read_stage_scales6(smem, q, wave, r, sc);
     if (q % kGroup == kGroup - 1 && q + 1 < Q) {
       // every wave holds its last scale words of the group: reload the buffer
       __syncthreads();
       pipe6_issue_scales(smem, src, (q + 1) / kGroup, wave);
     }
-    if (q + kAhead < Q) pipe6_issue(smem, src, q + kAhead, wave);
+    if (q + 1 < Q) pipe6_issue(smem, src, q + 1, wave);
     pipe6_compute(smem, q, wave, r, hh, sc, acc);
   }
-}
-
-// Weight-side sources: wave row wr (0..31) of the stage is row
-// wrow[wr / 16] + wr % 16 of the section at wcodes[wr / 16] / wscales[wr / 16].
-__device__ __forceinline__ void pipe6_weight_src(PipeSrc6& src, const uint8_t* const (&wcodes)[2],
-                                                 const uint8_t* const (&wscales)[2],
-                                                 const int (&wrow)[2], size_t crow, size_t srow,
-                                                 int lane) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    // load j: the 16-row block at wrow[j] (a tile row lane/4, unit (lane % 4) ^ swizzle)
-    const int wr = 16 * j + (lane >> 2);
-    const int b = (lane & 3) ^ ((wr >> 2) & 3);
-    src.a[j] = wcodes[j] + (size_t)wrow[j] * crow + (lane >> 2) * kRowC + b * 16;
-  }
-  const int wr = lane & 31, t = wr >> 4, rr = wr & 15;  // lanes 32-63 issue no scale load
-  src.as = (t ? wscales[1] : wscales[0]) + (size_t)((t ? wrow[1] : wrow[0]) + rr) * srow;
 }
 
 // Activation-side sources: the wave's tile rows 32 wave .. +31, 96 code bytes
@@ -1633,10 +1619,44 @@ __device__ __forceinline__ void pipe6_act_src(PipeSrc6& src, RowPtr rowptr, size
   src.bsstep = rp ? kGroupRow : 0;
 }
 
-// Gate/up with MXFP6 rows: N-tile = 64 rows of I; wave w: the 16 rows
-// n0 = 64 nt + 16 w of gate (tile rows 0-15) and of up (16-31); K = H.  Two
-// waves hold one MX block of h (32 rows of I): each writes its partial
-// maximum per column to LDS, and both read the pair's.
+// h = silu(gate) * up for one column of a 32-row weight tile pair, as
+// swiglu_quant_store32, encoded as MXFP6 (E2M3): the lane's rows
+// 8q + 4hh .. +3 are block elements whose 24 bits sit at byte 6q + 3hh of the
+// block's 24 code bytes.
+__device__ __forceinline__ void swiglu_quant_store32_fp6(const v16f& G, const v16f& U, int hh,
+                                                         uint8_t* hr, int n0, int I) {
+  float h[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) h[v] = silu_mul(G[v], U[v]);
+  float amax = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(h[v]));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  uint32_t code[16];
+  uint32_t scale = 0u;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) code[v] = 0u;
+  if (amax > 0.f) {
+    const int e = mx_block_exp(amax);
+    scale = (uint32_t)(e + 127);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) code[v] = e2m3_code(h[v], e);
+  }
+  if (hr) {
+    uint8_t* hb = hr + (size_t)(n0 / 32) * 24 + 3 * hh;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w24 = code[4 * q] | (code[4 * q + 1] << 6) | (code[4 * q + 2] << 12) |
+                           (code[4 * q + 3] << 18);
+      hb[6 * q] = (uint8_t)w24;
+      hb[6 * q + 1] = (uint8_t)(w24 >> 8);
+      hb[6 * q + 2] = (uint8_t)(w24 >> 16);
+    }
+    if (hh == 0) hr[(size_t)I / 32 * 24 + n0 / 32] = (uint8_t)scale;
+  }
+}
+
+// Gate/up with MXFP6 rows: tiles as gateup_pipe (N-tile = 128 rows of I).
 __global__ __launch_bounds__(256, 2) void gateup_pipe6(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds6];
   TileRef tr;
@@ -1655,13 +1675,15 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe6(PipeArgs p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int H = p.H;
-  const int n0 = tr.nt * 64 + wave * 16;  // I % 64 == 0: every wave's rows exist
+  const int n0 = tr.nt * 128 + wave * 32;
+  const bool active = n0 < p.I;
+  const int nb = active ? n0 : 0;  // an idle wave still loads (row 0) and meets every barrier
   const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
   const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c1};
   const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s1};
-  const int wrow[2] = {n0, n0};
+  const int wrow[2] = {nb, nb};
   PipeSrc6 src;
-  pipe6_weight_src(src, wc, wsc, wrow, (size_t)H / 2, (size_t)H / 32, lane);
+  pipe_weight_src(src, wc, wsc, wrow, (size_t)H / 2, (size_t)H / 32, lane);
   pipe6_act_src(
       src,
       [&](int row) -> const uint8_t* {
@@ -1671,60 +1693,20 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe6(PipeArgs p) {
         return (a >= 0 && a < p.A) ? p.act + (size_t)(a / p.k) * p.arow : nullptr;
       },
       (size_t)H / 32 * 24, p.zero, wave, lane);
-  v16f acc[4];
+  v16f acc[2][4];
   pipe6_mainloop(smem, src, H / kKc, wave, lane, acc);
-  // h = silu(gate) * up: lane (column 32cb + r, half hh) holds rows
-  // 8(v/4) + 4hh + v%4 (v < 8) of the wave's 16, gate at v and up at v + 8
-  float h[4][8];
-  float* part = reinterpret_cast<float*>(smem);  // [wave][cb][32] partial maxima
-  __syncthreads();  // every wave is done with the ring
+  if (!active) return;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
-    float m = 0.f;
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      h[cb][v] = silu_mul(acc[cb][v], acc[cb][v + 8]);
-      m = fmaxf(m, fabsf(h[cb][v]));
-    }
-    m = fmaxf(m, __shfl_xor(m, 32, kWave));
-    if (hh == 0) part[(wave * 4 + cb) * 32 + r] = m;
-  }
-  __syncthreads();
-  const int half = wave & 1;        // which 16 rows of the pair's block
-  const int blk = (n0 - 16 * half) / 32;
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int lr = 32 * cb + r;
-    const float amax =
-        fmaxf(part[(wave * 4 + cb) * 32 + r], part[((wave ^ 1) * 4 + cb) * 32 + r]);
-    uint32_t code[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t scale = 0u;
-    if (amax > 0.f) {
-      const int e = mx_block_exp(amax);
-      scale = (uint32_t)(e + 127);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) code[v] = e2m3_code(h[cb][v], e);
-    }
-    if (lr < rows) {
-      // block elements 16 half + 8q + 4hh .. +3 (q = 0, 1): 24 bits at byte
-      // 12 half + 6q + 3hh of the block's codes
-      uint8_t* hb = p.hq + (size_t)(p0 + lr) * p.hrow + (size_t)blk * 24 + 12 * half + 3 * hh;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint32_t w24 = code[4 * q] | (code[4 * q + 1] << 6) | (code[4 * q + 2] << 12) |
-                             (code[4 * q + 3] << 18);
-        hb[6 * q] = (uint8_t)w24;
-        hb[6 * q + 1] = (uint8_t)(w24 >> 8);
-        hb[6 * q + 2] = (uint8_t)(w24 >> 16);
-      }
-      if (half == 0 && hh == 0)
-        p.hq[(size_t)(p0 + lr) * p.hrow + (size_t)p.I / 32 * 24 + blk] = (uint8_t)scale;
+    if (32 * cb < rows) {
+      const int lr = 32 * cb + r;
+      swiglu_quant_store32_fp6(acc[0][cb], acc[1][cb], hh,
+                               lr < rows ? p.hq + (size_t)(p0 + lr) * p.hrow : nullptr, n0, p.I);
     }
   }
 }
 
-// Down with MXFP6 hq rows: N-tile = 128 rows of H; wave w: the 32 rows
-// n0 = 128 nt + 32 w; K = I; B rows: the slot's hq rows p0.. (contiguous).
+// Down with MXFP6 hq rows: tiles as down_pipe (N-tile = 256 rows of H).
 __global__ __launch_bounds__(256, 2) void down_pipe6(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds6];
   TileRef tr;
@@ -1736,27 +1718,38 @@ __global__ __launch_bounds__(256, 2) void down_pipe6(PipeArgs p) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
   const int I = p.I;
-  const int n0 = tr.nt * 128 + wave * 32;  // H % 128 == 0: every wave's rows exist
+  const int n0 = tr.nt * 256 + wave * 64;
   const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
   const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c0};
   const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s0};
-  const int wrow[2] = {n0, n0 + 16};
+  bool tv[2];
+  int wrow[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    tv[t] = n0 + 32 * t < p.H;  // tiles past H load row 0 and are never stored
+    wrow[t] = tv[t] ? n0 + 32 * t : 0;
+  }
   PipeSrc6 src;
-  pipe6_weight_src(src, wc, wsc, wrow, (size_t)I / 2, (size_t)I / 32, lane);
+  pipe_weight_src(src, wc, wsc, wrow, (size_t)I / 2, (size_t)I / 32, lane);
   pipe6_act_src(
       src,
       [&](int row) -> const uint8_t* {
         return row < rows ? p.act + (size_t)(p0 + row) * p.arow : nullptr;
       },
       (size_t)I / 32 * 24, p.zero, wave, lane);
-  v16f acc[4];
+  v16f acc[2][4];
   pipe6_mainloop(smem, src, I / kKc, wave, lane, acc);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) {
     const int lr = 32 * cb + r;
     if (lr < rows) {
       const int a = sh ? p0 + lr : p.perm[p0 + lr];
-      if (a >= 0 && (sh || a < p.A)) store_y_bf16(p.y + (size_t)a * p.H, n0, hh, acc[cb]);
+      if (a >= 0 && (sh || a < p.A)) {
+        uint16_t* yr = p.y + (size_t)a * p.H;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (tv[t]) store_y_bf16(yr, n0 + 32 * t, hh, acc[t][cb]);
+      }
     }
   }
 }
@@ -1787,9 +1780,9 @@ static Family family_of(int T, int k, int H, int I, int fmt) {
 }
 
 // N-tiles of the pipelined kernels: gate/up rows of I and down rows of H per
-// workgroup, by activation format.
-static int pipe_ntile_gateup(int fmt) { return fmt == MOE_ACT_MXFP6 ? 64 : 128; }
-static int pipe_ntile_down(int fmt) { return fmt == MOE_ACT_MXFP6 ? 128 : 256; }
+// workgroup (the same for both activation formats).
+static int pipe_ntile_gateup(int fmt) { (void)fmt; return 128; }
+static int pipe_ntile_down(int fmt) { (void)fmt; return 256; }
 
 // Upper bound on the M-tiles of tm rows of a batch: one partial tile per used
 // slot plus the full ones.
