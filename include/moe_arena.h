@@ -417,13 +417,40 @@ int arena_load_slot(uint8_t* arena, size_t slot_stride, int num_slots, int slot,
  *          hist_row, 256 for ws), a negative size or a threshold that is NaN or
  *          negative, MOE_EUNSUPPORTED past the k, E, S limits.
  * The caller reads out, copies expert e*'s bytes into c's slot with
- * arena_load_slot, sets expert_slot[e*] = old slot of c and expert_slot[c] = -1,
- * routes again without demand, and orders moe_experts_forward after the copy.
+ * arena_load_slot, sets expert_slot[e*] = old slot of c and expert_slot[c] = -1
+ * (moe_hot_install does it on the device), routes again without demand, and
+ * orders moe_experts_forward after the copy.
  */
 int moe_hot_pick(const int32_t* topk_expert, const float* topk_score, int T, int k, int E,
                  const int32_t* expert_slot, int S, int n_arena, const double* hist_row,
                  double threshold, int32_t* out, void* ws, size_t ws_bytes,
                  hipStream_t stream);
+
+/*
+ * moe_hot_install -- applies a moe_hot_pick decision to the slot table on the
+ * device (TideLM README, "How adaptive expert loading works", item 3, GLM-5.3
+ * bullet: the loaded expert is kept in place of the coldest one), so the
+ * layer's second routing can be enqueued without the host having read the
+ * decision first.
+ *
+ *   with (e*, c) = pick[0..1]: if 0 <= e*, c < E, e* != c, expert_slot[e*] is
+ *   not in [0, S) (a miss) and 0 <= expert_slot[c] < min(n_arena, S):
+ *       s = expert_slot[c]; expert_slot[e*] = s; expert_slot[c] = -1;
+ *       slot_out[0] = s;
+ *   otherwise the table is left as it is and slot_out[0] = -1.
+ * Inputs : pick [2] int32 (device; moe_hot_pick's out); expert_slot [E] int32
+ *          (device; updated in place).
+ * Output : slot_out [1] int32 (device, nullable).
+ * One single-thread kernel on `stream`.  The caller orders it after
+ * moe_hot_pick on the same stream, copies e*'s bytes into slot s with
+ * arena_load_slot, and orders moe_experts_forward (slot s deferred) after the
+ * copy; kernels that run between this call and that copy route to slot s but
+ * must not read its bytes.
+ * Errors: MOE_EINVAL for null or misaligned (4-byte) pointers, E <= 0, S < 0 or
+ * n_arena < 0; MOE_EUNSUPPORTED past the E and S limits.
+ */
+int moe_hot_install(const int32_t* pick, int32_t* expert_slot, int E, int S, int n_arena,
+                    int32_t* slot_out, hipStream_t stream);
 
 /*
  * moe_replan -- re-plan of one arena shared by all layers (TideLM README, "How

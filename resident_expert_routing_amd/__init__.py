@@ -9,7 +9,7 @@ library and fails loudly if it has not been built.
 from . import binding
 from .binding import (MOE_OP_DEMAND, MOE_OP_EXPERTS, MOE_OP_HOT_PICK, MOE_OP_ROUTE, MoeError,
                       arena_load_slot, check, moe_demand_accumulate,
-                      moe_experts_forward, moe_hot_pick, moe_mxfp4_row_bytes, moe_replan, moe_route,
+                      moe_experts_forward, moe_hot_install, moe_hot_pick, moe_mxfp4_row_bytes, moe_replan, moe_route,
                       moe_slot_bytes, moe_slot_sections, moe_status_string,
                       moe_test_mfma_loop, moe_test_mxfp4_probe, moe_test_stream_read,
                       moe_workspace_bytes)
@@ -18,6 +18,6 @@ binding.load()
 
 __all__ = ["binding", "MOE_OP_DEMAND", "MOE_OP_EXPERTS", "MOE_OP_HOT_PICK", "MOE_OP_ROUTE",
            "MoeError", "arena_load_slot", "check", "moe_demand_accumulate",
-           "moe_experts_forward", "moe_hot_pick", "moe_mxfp4_row_bytes", "moe_replan", "moe_route", "moe_slot_bytes",
+           "moe_experts_forward", "moe_hot_install", "moe_hot_pick", "moe_mxfp4_row_bytes", "moe_replan", "moe_route", "moe_slot_bytes",
            "moe_slot_sections", "moe_status_string", "moe_test_mfma_loop", "moe_test_mxfp4_probe",
            "moe_test_stream_read", "moe_workspace_bytes"]

@@ -45,7 +45,7 @@ EXPORTS = ("moe_status_string", "moe_mxfp4_row_bytes", "moe_act_row_bytes", "moe
            "moe_workspace_bytes", "moe_route", "moe_demand_accumulate", "moe_experts_forward",
            "moe_experts_forward_noalloc", "moe_ring_plan", "moe_ring_install",
            "moe_history_save", "moe_history_load", "moe_boot_plan", "moe_history_scale",
-           "arena_load_slot", "moe_hot_pick", "moe_replan", "moe_test_mxfp4_probe",
+           "arena_load_slot", "moe_hot_pick", "moe_hot_install", "moe_replan", "moe_test_mxfp4_probe",
            "moe_test_stream_read", "moe_test_mfma_loop")
 
 
@@ -126,6 +126,8 @@ def load() -> ctypes.CDLL:
     lib.moe_hot_pick.argtypes = [vp, vp, i, i, i, vp, i, i, vp, ctypes.c_double, vp, vp, sz,
                                  vp]
     lib.moe_hot_pick.restype = i
+    lib.moe_hot_install.argtypes = [vp, vp, i, i, i, vp, vp]
+    lib.moe_hot_install.restype = i
     lib.moe_replan.argtypes = [vp, vp, i, i, i, i, vp, vp, vp, ctypes.POINTER(i)]
     lib.moe_replan.restype = i
     lib.moe_ring_plan.argtypes = [vp, vp, i, i, vp, i, i, i, vp, vp]
@@ -290,6 +292,11 @@ def moe_hot_pick(topk_expert, topk_score, T, k, E, expert_slot, S, n_arena, hist
                                    _ptr(expert_slot), int(S), int(n_arena), _ptr(hist_row),
                                    float(threshold), _ptr(out), _ptr(ws), int(ws_bytes),
                                    _stream(stream)))
+
+
+def moe_hot_install(pick, expert_slot, E, S, n_arena, slot_out=None, stream=None) -> int:
+    return int(load().moe_hot_install(_ptr(pick), _ptr(expert_slot), int(E), int(S),
+                                      int(n_arena), _ptr(slot_out), _stream(stream)))
 
 
 def moe_replan(hist, expert_slot, L, E, k, n_swap, evict, load, new_expert_slot, n_done) -> int:

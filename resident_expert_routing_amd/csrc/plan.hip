@@ -133,6 +133,28 @@ __global__ __launch_bounds__(1024) void hot_pick_final(
   }
 }
 
+// Applies a hot-read decision to the slot table on the device: the loaded
+// expert takes the evicted expert's arena slot.  One thread; the decision is
+// applied only when e* is a miss and c holds an arena slot, so a stale or
+// empty decision leaves the table as it is.
+__global__ __launch_bounds__(64) void hot_install_kernel(const int32_t* __restrict__ pick,
+                                                         int32_t* __restrict__ expert_slot, int E,
+                                                         int S, int n_arena,
+                                                         int32_t* __restrict__ slot_out) {
+  if (threadIdx.x != 0) return;
+  const int e = pick[0], c = pick[1];
+  int slot = -1;
+  if (e >= 0 && e < E && c >= 0 && c < E && e != c) {
+    const int se = expert_slot[e], sc = expert_slot[c];
+    if (!(se >= 0 && se < S) && sc >= 0 && sc < n_arena && sc < S) {
+      expert_slot[e] = sc;
+      expert_slot[c] = -1;
+      slot = sc;
+    }
+  }
+  if (slot_out) slot_out[0] = slot;
+}
+
 // ---------------------------------------------------------------------------
 // Hot ring (TideLM README, "How adaptive expert loading works", item 3,
 // DeepSeek bullet): after each step the step's heaviest misses take ring
@@ -290,5 +312,15 @@ extern "C" MOE_EXPORT int moe_hot_pick(const int32_t* topk_expert, const float* 
     hot_pick_tokens<<<nb, kHotTokenWg, 0, stream>>>(topk_expert, topk_score, T, k, E,
                                                     expert_slot, S, threshold, part);
   hot_pick_final<<<1, 1024, 0, stream>>>(part, nb, E, expert_slot, S, n_arena, hist_row, out);
+  return hip_status();
+}
+
+extern "C" MOE_EXPORT int moe_hot_install(const int32_t* pick, int32_t* expert_slot, int E, int S,
+                                          int n_arena, int32_t* slot_out, hipStream_t stream) {
+  if (E <= 0 || S < 0 || n_arena < 0) return MOE_EINVAL;
+  if (E > MOE_MAX_E || S > MOE_MAX_S) return MOE_EUNSUPPORTED;
+  if (!pick || !expert_slot || !aligned(pick, 4) || !aligned(expert_slot, 4)) return MOE_EINVAL;
+  if (slot_out && !aligned(slot_out, 4)) return MOE_EINVAL;
+  hot_install_kernel<<<1, 64, 0, stream>>>(pick, expert_slot, E, S, n_arena, slot_out);
   return hip_status();
 }

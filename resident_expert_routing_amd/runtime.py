@@ -174,10 +174,10 @@ def experts(buf: LayerBuffers, arena_ptr, slot_stride: int, stream=None,
 class HotReader:
     """Host side of the hot read for one layer.
 
-    The decision runs on the GPU (moe_hot_pick); the host reads the two ids,
-    copies the missing expert's bytes from page-locked memory into the coldest
-    expert's slot with arena_load_slot on a side stream, and updates the
-    device expert_slot table on the layer's stream.
+    The decision and the slot-table update run on the GPU (moe_hot_pick, then
+    moe_hot_install on the layer's stream); the host reads the decision from a
+    page-locked buffer, copies the missing expert's bytes from page-locked
+    memory into the slot it now owns with arena_load_slot on a side stream.
     """
 
     def __init__(self, expert_slot_host: np.ndarray, n_arena: int, device, threshold: float = 0.2):
@@ -185,7 +185,11 @@ class HotReader:
         self.n_arena = int(n_arena)
         self.threshold = float(threshold)
         self.device = device
-        self.out = torch.empty(2, dtype=torch.int32, device=device)
+        # (e*, c) from moe_hot_pick, then the slot moe_hot_install gave e* (-1: none)
+        self.out = torch.empty(3, dtype=torch.int32, device=device)
+        self.out_host = torch.empty(3, dtype=torch.int32).pin_memory()
+        self.out_ready = torch.cuda.Event()
+        self.installed = torch.cuda.Event()
         self.side = torch.cuda.Stream(device)   # default priority
         self.done = torch.cuda.Event()
         self.done.record(self.side)   # creates the HIP event the library records after a copy
@@ -202,47 +206,89 @@ class HotReader:
         """Page-locked copy of expert e's packed bytes (PinnedCopies)."""
         return self.pins.get(expert_bytes_fn(e))
 
-    def pick_and_load(self, buf: LayerBuffers, expert_slot_dev, hist_row, arena: Arena,
-                      expert_bytes_fn, stream):
-        """Returns (e_star, c, slot) after enqueueing the copy, or None."""
+    def enqueue_decision(self, buf: LayerBuffers, expert_slot_dev, hist_row, stream) -> None:
+        """Enqueues the decision and the table update on `stream` and records
+        `installed` after them; read_decision() then copies the decision to
+        page-locked host memory on the side stream."""
         ws = self.workspace(buf.T)
         B.check(B.moe_hot_pick(buf.topk_expert, buf.topk_score, buf.T, buf.k, buf.E,
                                expert_slot_dev, buf.S, self.n_arena, hist_row, self.threshold,
                                self.out, ws, ws.numel(), stream), "moe_hot_pick")
-        self.side.wait_stream(stream)
-        with torch.cuda.stream(stream):   # ordered after moe_hot_pick on `stream`
-            e_star, c = (int(v) for v in self.out.cpu())   # waits for the decision
-        if e_star < 0 or c < 0:
+        B.check(B.moe_hot_install(self.out, expert_slot_dev, buf.E, buf.S, self.n_arena,
+                                  self.out[2:], stream), "moe_hot_install")
+        self.installed.record(stream)
+
+    def read_decision(self) -> None:
+        """The decision's copy to the host, on the side stream after `installed`
+        (so the layer's stream can go on meanwhile); the side stream is then
+        also ordered after everything enqueued on the layer's stream before the
+        decision -- the copy into a slot must follow every kernel that reads it."""
+        self.side.wait_event(self.installed)
+        with torch.cuda.stream(self.side):
+            self.out_host.copy_(self.out, non_blocking=True)
+            self.out_ready.record(self.side)
+
+    def wait_decision(self):
+        """Waits for the enqueued decision: (e_star, c, slot), or None when
+        nothing is read (the table was left as it was)."""
+        self.out_ready.synchronize()
+        e_star, c, slot = (int(v) for v in self.out_host)
+        if slot < 0:
             return None
-        slot = int(self.es[c])
+        self.es[e_star], self.es[c] = slot, -1
+        return e_star, c, slot
+
+    def decide(self, buf: LayerBuffers, expert_slot_dev, hist_row, stream):
+        """enqueue_decision() and wait_decision(): returns (e_star, c, slot), or
+        None.  The device table already routes e_star to `slot` when this returns."""
+        self.enqueue_decision(buf, expert_slot_dev, hist_row, stream)
+        self.read_decision()
+        return self.wait_decision()
+
+    def load(self, picked, arena: Arena, expert_bytes_fn) -> None:
+        """Enqueues the copy of the picked expert's bytes into its slot on the
+        side stream; `done` is recorded after it."""
+        e_star, _, slot = picked
         host = expert_bytes_fn(e_star)
         src = self.pins.get(host)
         B.check(B.arena_load_slot(arena.mem, arena.stride, arena.S, slot, src, arena.slot_bytes,
                                   self.side, self.done), "arena_load_slot")
         self.pins.used_on(host, self.side)
-        self.es[e_star], self.es[c] = slot, -1
-        with torch.cuda.stream(stream):
-            expert_slot_dev[e_star] = slot
-            expert_slot_dev[c] = -1
-        return e_star, c, slot
+
+    def pick_and_load(self, buf: LayerBuffers, expert_slot_dev, hist_row, arena: Arena,
+                      expert_bytes_fn, stream):
+        """decide() and load(): returns (e_star, c, slot) after enqueueing the
+        copy, or None."""
+        picked = self.decide(buf, expert_slot_dev, hist_row, stream)
+        if picked is not None:
+            self.load(picked, arena, expert_bytes_fn)
+        return picked
 
 
 def layer_step_hot(buf: LayerBuffers, x, w_router, bias, expert_slot_dev, hist_row,
                    arena: Arena, hot: HotReader, expert_bytes_fn, stream=None):
     """One layer call with a hot read before the experts (long prefill chunks).
 
-    Route with demand, decide and start the copy, route again over the new
-    routable set (the router's products reused; overlapping the copy), then
-    run the experts with the loaded slot deferred: the other slots' gate/up
-    products run while the copy finishes, that slot's after it.
+    Route with demand; decide and update the slot table on the device; route
+    again over the table as it now stands (the router's products reused) while
+    the decision travels to the host on the side stream; start the copy on the
+    side stream; run the
+    experts with the loaded slot deferred: the other slots' gate/up products run
+    while the copy finishes, that slot's after it.  The second routing is
+    enqueued before the decision is known, so the layer's stream never waits for
+    the host; when nothing qualifies it repeats the first routing's result (the
+    table is unchanged), one selection and bucketing pass spent for nothing.
     """
     stream = stream if stream is not None else torch.cuda.current_stream(hot.device)
     route(buf, x, w_router, bias, expert_slot_dev, stream, hist_row=hist_row)
-    picked = hot.pick_and_load(buf, expert_slot_dev, hist_row, arena, expert_bytes_fn, stream)
+    hot.enqueue_decision(buf, expert_slot_dev, hist_row, stream)
+    route(buf, x, w_router, bias, expert_slot_dev, stream, reuse_logits=True)
+    hot.read_decision()
+    picked = hot.wait_decision()
     if picked is None:
         experts(buf, arena.ptr(), arena.stride, stream)
         return None
-    route(buf, x, w_router, bias, expert_slot_dev, stream, reuse_logits=True)
+    hot.load(picked, arena, expert_bytes_fn)
     experts(buf, arena.ptr(), arena.stride, stream, defer_slot=picked[2], defer_event=hot.done)
     return picked
 

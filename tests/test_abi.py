@@ -273,6 +273,19 @@ def test_hot_pick_rejects():
     assert B.moe_workspace_bytes(B.MOE_OP_HOT_PICK, 10 ** 7, 0, 0, 0, 0, 0) == 256 * 16
 
 
+def test_hot_install_rejects():
+    h = B.moe_hot_install
+    assert h(None, FAKE, 16, 10, 10) == B.MOE_EINVAL
+    assert h(FAKE, None, 16, 10, 10) == B.MOE_EINVAL
+    assert h(FAKE + 2, FAKE, 16, 10, 10) == B.MOE_EINVAL
+    assert h(FAKE, FAKE + 2, 16, 10, 10) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 16, 10, 10, FAKE + 2) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 0, 10, 10) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 16, -1, 10) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, 16, 10, -1) == B.MOE_EINVAL
+    assert h(FAKE, FAKE, B.MOE_MAX_E + 1, 10, 10) == B.MOE_EUNSUPPORTED
+
+
 def test_unrecorded_torch_event_is_refused():
     """A torch.cuda.Event gets its HIP event on its first record; passing one
     before that would hand the library a null event (no record after a copy,

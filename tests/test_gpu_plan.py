@@ -121,6 +121,32 @@ def test_hot_pick_ring_excluded_decode():
     assert 0 <= lay.expert_slot[got[1]] < n_arena
 
 
+def test_hot_install_applies_only_a_valid_decision():
+    """moe_hot_install: e* takes c's arena slot and c leaves the table; any
+    other decision (nothing picked, e* already routable, c on a ring slot or
+    not resident, e* == c, ids out of range) leaves the table as it was."""
+    import torch
+    from resident_expert_routing_amd import binding as B
+    E, S, n_arena = 12, 8, 6
+    # experts 0-5 hold arena slots 0-5, expert 6 and 7 ring slots 6-7, 8-11 none
+    es0 = np.array([3, 0, 5, 1, 4, 2, 6, 7, -1, -1, -1, -1], dtype=np.int32)
+    cases = [((9, 2), 5), ((8, 1), 0), ((-1, 2), -1), ((9, -1), -1), ((0, 2), -1),
+             ((9, 6), -1), ((9, 8), -1), ((9, 9), -1), ((12, 2), -1), ((9, 12), -1)]
+    for (e, c), want in cases:
+        es = to_dev(es0)
+        pick = to_dev(np.array([e, c], dtype=np.int32))
+        out = torch.full((1,), 99, dtype=torch.int32, device=es.device)
+        assert B.moe_hot_install(pick, es, E, S, n_arena, out) == B.MOE_OK
+        assert B.moe_hot_install(pick, es, E, S, n_arena) == B.MOE_OK  # again, no output
+        torch.cuda.synchronize()
+        want_es = es0.copy()
+        if want >= 0:
+            want_es[e], want_es[c] = es0[c], -1
+        assert int(out.item()) == want, ((e, c), int(out.item()))
+        # the second call sees the updated table: e* is no longer a miss
+        assert np.array_equal(es.cpu().numpy(), want_es), (e, c)
+
+
 def test_hot_read_layer_long():
     """Long prefill chunk: the full hot-read call against the oracle."""
     import torch
