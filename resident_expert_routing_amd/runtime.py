@@ -272,12 +272,12 @@ def layer_step_hot(buf: LayerBuffers, x, w_router, bias, expert_slot_dev, hist_r
     Route with demand; decide and update the slot table on the device; route
     again over the table as it now stands (the router's products reused) while
     the decision travels to the host on the side stream; start the copy on the
-    side stream; run the
-    experts with the loaded slot deferred: the other slots' gate/up products run
-    while the copy finishes, that slot's after it.  The second routing is
-    enqueued before the decision is known, so the layer's stream never waits for
-    the host; when nothing qualifies it repeats the first routing's result (the
-    table is unchanged), one selection and bucketing pass spent for nothing.
+    side stream; run the experts with the loaded slot deferred: the other
+    slots' gate/up products run while the copy finishes, that slot's after it.
+    The second routing is enqueued before the decision is known, so the layer's
+    stream never waits for the host; when nothing qualifies it repeats the first
+    routing's result (the table is unchanged), one selection and bucketing pass
+    spent for nothing.
     """
     stream = stream if stream is not None else torch.cuda.current_stream(hot.device)
     route(buf, x, w_router, bias, expert_slot_dev, stream, hist_row=hist_row)
