@@ -307,7 +307,7 @@ def act_mxfp6_timing(name, T, H, E, k, I, S, xs, w_router, bias, expert_slot, ar
     return out
 
 
-def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5):
+def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 11):
     """Layer calls of the long chunk with the hot read (route, pick the heaviest
     miss, copy its 20 MB from page-locked host memory into the coldest arena
     expert's slot on a side stream, route again, experts after the copy) and
@@ -322,19 +322,23 @@ def hot_read_timing(lay, x, w_router, bias, arena, buf, E, stream, reps: int = 5
     dev = x.device
     es0 = lay.expert_slot.astype(np.int32)
     hist = torch.zeros(E, dtype=torch.float64, device=dev)
-    es = torch.from_numpy(es0).to(dev)
+    es0_dev = torch.from_numpy(es0).to(dev)
+    es = es0_dev.clone()
     n_arena = lay.extra["n_resident"]
     pins = R.PinnedCopies()
+    # one reader for every call, as a serving loop keeps one per layer (its
+    # stream, events and page-locked buffers are made once, outside the timing)
+    hot = R.HotReader(es0, n_arena, dev)
+    hot.pins = pins
 
     def plain():
-        es.copy_(torch.from_numpy(es0))
+        es.copy_(es0_dev)   # the table as the chunk found it (also before each hot call)
         R.route(buf, x, w_router, bias, es, stream, hist_row=hist)
         R.experts(buf, arena.ptr(), arena.stride, stream)
 
     def with_hot():
-        es.copy_(torch.from_numpy(es0))
-        hot = R.HotReader(es0, n_arena, dev)
-        hot.pins = pins  # page-locked copies are made once, outside the timing
+        es.copy_(es0_dev)
+        hot.es[:] = es0
         picked = R.layer_step_hot(buf, x, w_router, bias, es, hist, arena, hot, lay.expert_bytes,
                                   stream)
         return picked, hot
