@@ -998,16 +998,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 // global-to-LDS loads (lane i of a load lands at the LDS base + size * i).
 // Code bytes are issued two K chunks ahead of use into a ring of three
 // stages; a stage holds one chunk (K = 128: 64 code bytes per row) of the
-// four waves' 64 weight rows each and of the tile's 128 activation rows.  The
-// E8M0 scales of four stages (16 bytes per row) are loaded together, one row
-// per lane, into a group buffer beside the ring: a load that touches one cache
-// line per lane then carries 16 bytes instead of 4 (with 4-byte loads every
-// stage, the scale loads were half of the cache lines requested and cost a
-// fifth of the kernel's time).  Ring and group buffer take 78 KB and the
-// kernel fits 256 VGPRs, so two workgroups share a CU and one computes while
-// the other waits at its stage barrier.  The 16-byte block b of a 64-byte
-// stage row r sits at position b ^ ((r >> 2) & 3): a fragment read (32 rows,
-// two blocks) spreads over all 16 four-bank groups, four lanes each.
+// N-tile's 256 weight rows (four groups of 64) and of the M-tile's 128
+// activation rows.  The E8M0 scales of four stages (16 bytes per row) are
+// loaded together, one row per lane, into a group buffer beside the ring: a
+// load that touches one cache line per lane then carries 16 bytes instead of
+// 4 (with 4-byte loads every stage, the scale loads were half of the cache
+// lines requested and cost a fifth of the kernel's time).  Ring and group
+// buffer take 78 KB, so two workgroups share a CU.  With MXFP4 rows a
+// workgroup is eight waves, each multiplying one weight group by half of the
+// M-tile's columns (128 accumulator registers fewer than four waves with all
+// columns each), so the kernels fit 128 VGPRs and every SIMD keeps four waves:
+// a wave stalls handing its loads to the memory pipeline for about half of
+// each stage, and four waves hide more of that than two (gate/up 3 % faster at
+// prefill and 6 % at the long chunk than four-wave workgroups).  The 16-byte
+// block b of a 64-byte stage row r sits at position b ^ ((r >> 2) & 3): a
+// fragment read (32 rows, two blocks) spreads over all 16 four-bank groups,
+// four lanes each.
 // ===========================================================================
 constexpr int kTileM = 128;                    // assignment rows per work item
 constexpr int kKc = 128;                       // K elements per stage
@@ -1025,9 +1031,12 @@ constexpr int kGroupSB = kTileM * kGroupRow;   // activation rows' scales: 32 ro
 constexpr int kPipeLds = kRing * kStage + kGroupSA + kGroupSB;  // 79,872 bytes
 static_assert(2 * kPipeLds <= 160 * 1024, "two workgroups per CU");
 constexpr int kZeroPage = 256;                 // zeroed workspace bytes absent rows load from
-// Loads issued by each wave per stage: 4 weight-code and 2 activation-code
-// loads; per group of stages, 1 weight-scale and 1 activation-scale load.
-constexpr int kLoadsPerStage = 6;
+constexpr int kPipeWaves = 8;                  // waves per workgroup (MXFP4 rows)
+constexpr int kScalePart = 48 * kGroupRow;     // a wave's part of the group buffer (768 bytes)
+static_assert(kPipeWaves * kScalePart == kGroupSA + kGroupSB, "group buffer parts");
+// Loads issued by each wave per stage (MXFP4 rows): 2 weight-code and 1
+// activation-code load; per group of stages, 1 scale load.
+constexpr int kLoadsPerStage = 3;
 
 // Work list of M-tiles of tm rows: items[0] = count, then per item (slot,
 // first row of the tile within the slot, index of the slot's first item, the
@@ -1144,128 +1153,90 @@ __device__ __forceinline__ bool tile_of(int w, int nN, int tm, const int32_t* __
 }
 
 
-// Per-lane sources of the direct loads; stage q reads code bytes
-// [64 q, 64 q + 64) of every row, group g scale bytes [16 g, 16 g + 16).
+// Per-wave sources of the direct loads.  Eight waves; wave w loads, per stage,
+// the 16-row weight-code blocks 2 (w % 2) and 2 (w % 2) + 1 of weight group
+// w / 2 (a group is 64 rows: tile 0 rows 0-31, tile 1 rows 32-63) and the 16
+// activation rows 16 w ..; per group of stages one scale load (lanes 0-31:
+// weight row 32 (w % 2) + lane of group w / 2; lanes 32-47: activation row
+// 16 w + lane - 32; lanes 48-63 load nothing).
 struct PipeSrc {
-  const uint8_t* a[4];   // weight codes, load j: wave row 16j + lane/4, block already swizzled
-  const uint8_t* as;     // weight scales: wave row lane
-  const uint8_t* b[2];   // activation codes, load j: tile row (2 wave + j) * 16 + lane/4
-  int bstep[2];          // code bytes per stage (64; 0 for an absent row on the zero page)
-  const uint8_t* bs;     // activation scales: tile row 32 wave + lane % 32
-  int bsstep;            // scale bytes per group (16; 0 for an absent row)
+  const uint8_t* a[2];  // weight-code blocks, block already swizzled per lane
+  int adst[2];          // their offsets in a stage
+  const uint8_t* b;     // activation codes (zero page for an absent row)
+  int bstep;            // code bytes per stage (64; 0 for an absent row)
+  const uint8_t* s;     // this lane's scale row
+  int sstep;            // scale bytes per group (16; 0 for an absent row)
+};
+
+struct TileSrc {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  int row0;  // first of the tile's 32 rows
 };
 
 __device__ __forceinline__ void pipe_issue(uint8_t* smem, const PipeSrc& src, int q, int wave) {
   uint8_t* st = smem + (q % kRing) * kStage;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)  // stage q of a 16-row block: its tile q, 1 KB
-    dma16(src.a[j] + (size_t)q * kTileBytes, st + wave * (64 * kRowC) + j * 1024);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    dma16(src.b[j] + (size_t)q * src.bstep[j], st + kStageA + (2 * wave + j) * 1024);
+  for (int j = 0; j < 2; ++j)  // stage q of a 16-row block: its tile q, 1 KB
+    dma16(src.a[j] + (size_t)q * kTileBytes, st + src.adst[j]);
+  dma16(src.b + (size_t)q * src.bstep, st + kStageA + wave * 1024);
 }
 
-// The scale bytes of group g (stages 4g .. 4g+3): 16 bytes per row, row i of
-// the wave's 64 weight rows at lane i, and of its 32 activation rows at lanes
-// 0-31.
+// The scale bytes of group g (stages 4g .. 4g+3): 16 bytes per row, in the
+// wave's 768-byte part of the group buffer (lane i at 16 i).
 __device__ __forceinline__ void pipe_issue_scales(uint8_t* smem, const PipeSrc& src, int g,
                                                   int wave) {
   uint8_t* sg = smem + kRing * kStage;
-  dma16(src.as + (size_t)g * kGroupRow, sg + wave * (64 * kGroupRow));
-  if ((threadIdx.x & 63) < 32)  // lanes 0-31: one row each (a partial-lane load)
-    dma16(src.bs + (size_t)g * src.bsstep, sg + kGroupSA + wave * (32 * kGroupRow));
+  if ((threadIdx.x & 63) < 48)  // a partial-lane load
+    dma16(src.s + (size_t)g * src.sstep, sg + wave * kScalePart);
 }
 
 // Waits until this wave's loads of stage q have landed, with those of its
 // scale group (issued before stage q + 1's loads), then a workgroup barrier
 // makes every wave's share visible and frees the stage read in the previous
 // iteration for reuse.  Issue order: group 0, stages 0 and 1, then in
-// iteration q stage q + 2, preceded by group g + 1 when q = 4g + 3; so
-// after stage q's loads only stage q + 1's six may still be in flight.
+// iteration q stage q + 2, preceded by group g + 1 when q = 4g + 3; so after
+// stage q's loads only stage q + 1's three may still be in flight.
 __device__ __forceinline__ void pipe_wait(int q, int Q) {
-  static_assert(kLoadsPerStage == 6 && kAhead == 2 && kGroup == 4, "wait counts below");
+  static_assert(kLoadsPerStage == 3 && kAhead == 2 && kGroup == 4, "wait counts below");
   if (q + 1 < Q)
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 }
 
-// The two MFMA steps of stage q: 2 weight tiles x 4 column tiles of 32.  The
-// fragments of step 1 are read from LDS while the MFMAs of step 0 run (the
-// scheduling barriers keep that order).
-struct StepFrags {
-  uint4 a[2], b[4];
-};
-
-__device__ __forceinline__ void read_step(const uint8_t* st, int s, int wave, int r, int hh,
-                                          int swz, StepFrags& f) {
-  const int pb = ((2 * s + hh) ^ swz) * 16;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    f.a[t] = *reinterpret_cast<const uint4*>(st + wave * (64 * kRowC) + (32 * t + r) * kRowC + pb);
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-    f.b[cb] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * cb + r) * kRowC + pb);
-}
-
-// This lane's scale words of stage q (4 scale bytes of its rows: weight tile
-// t row r, column tile cb row r), from the group buffer.
-struct StageScales {
-  uint32_t aw[2], bw[4];
-};
-
-__device__ __forceinline__ void read_stage_scales(const uint8_t* smem, int q, int wave, int r,
-                                                  StageScales& sc) {
-  const uint8_t* sg = smem + kRing * kStage + (q % kGroup) * kRowS;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    sc.aw[t] = *reinterpret_cast<const uint32_t*>(sg + (wave * 64 + 32 * t + r) * kGroupRow);
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
-    sc.bw[cb] = *reinterpret_cast<const uint32_t*>(sg + kGroupSA + (32 * cb + r) * kGroupRow);
-}
-
-__device__ __forceinline__ void pipe_compute(const uint8_t* smem, int q, int wave, int r, int hh,
-                                             const StageScales& sc, v16f (&acc)[2][4]) {
-  const uint8_t* st = smem + (q % kRing) * kStage;
-  const int swz = (r >> 2) & 3;
-  const uint32_t* aw = sc.aw;
-  const uint32_t* bw = sc.bw;
-  StepFrags f[2];
-  read_step(st, 0, wave, r, hh, swz, f[0]);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    if (s + 1 < 2) read_step(st, s + 1, wave, r, hh, swz, f[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    const StepFrags& cur = f[s];
-    const int sh = 8 * (2 * s + hh);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        acc[t][cb] = mfma32(cur.a[t], cur.b[cb], acc[t][cb], aw[t] >> sh, bw[cb] >> sh);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// The whole K loop over Q = K / 128 stages.
+// The K loop over Q = K / 128 stages.  Wave w multiplies weight group w % 4
+// (two 32-row tiles) by column half w / 4 (two 32-column tiles of the
+// M-tile): two MFMA steps of 2 x 2 32x32x64 instructions per stage.
 __device__ __forceinline__ void pipe_mainloop(uint8_t* smem, const PipeSrc& src, int Q, int wave,
-                                              int lane, v16f (&acc)[2][4]) {
+                                              int lane, v16f (&acc)[2][2]) {
   const int r = lane & 31, hh = lane >> 5;
+  const int g = wave & 3, ch = wave >> 2;
+  const int swz = (r >> 2) & 3;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[t][cb] = zero16();
+    for (int c = 0; c < 2; ++c) acc[t][c] = zero16();
   pipe_issue_scales(smem, src, 0, wave);
 #pragma unroll
   for (int q = 0; q < kAhead; ++q)
     if (q < Q) pipe_issue(smem, src, q, wave);
   for (int q = 0; q < Q; ++q) {
     pipe_wait(q, Q);
-    StageScales sc;
-    read_stage_scales(smem, q, wave, r, sc);
+    // scale words of stage q: weight tile t row r was loaded by wave 2g + t at
+    // lane r; activation row C by wave C / 16 at lane 32 + C % 16
+    const uint8_t* sg = smem + kRing * kStage + (q % kGroup) * kRowS;
+    uint32_t aw[2], bw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      aw[t] = *reinterpret_cast<const uint32_t*>(sg + (2 * g + t) * kScalePart + r * kGroupRow);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int C = 32 * (2 * ch + c) + r;
+      bw[c] = *reinterpret_cast<const uint32_t*>(sg + (C >> 4) * kScalePart +
+                                                 (32 + (C & 15)) * kGroupRow);
+    }
     if (q % kGroup == kGroup - 1 && q + 1 < Q) {
       // every wave holds its last scale words of the group: reload the buffer
       // (stage q's compute hides the load; stage q + 1 waits for it)
@@ -1273,9 +1244,70 @@ __device__ __forceinline__ void pipe_mainloop(uint8_t* smem, const PipeSrc& src,
       pipe_issue_scales(smem, src, (q + 1) / kGroup, wave);
     }
     if (q + kAhead < Q) pipe_issue(smem, src, q + kAhead, wave);
-    pipe_compute(smem, q, wave, r, hh, sc, acc);
+    const uint8_t* st = smem + (q % kRing) * kStage;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int pb = ((2 * s + hh) ^ swz) * 16;
+      uint4 fa[2], fb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        fa[t] = *reinterpret_cast<const uint4*>(st + g * (64 * kRowC) + (32 * t + r) * kRowC + pb);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        fb[c] = *reinterpret_cast<const uint4*>(st + kStageA + (32 * (2 * ch + c) + r) * kRowC +
+                                                pb);
+      const int sh = 8 * (2 * s + hh);
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          acc[t][c] = mfma32(fa[t], fb[c], acc[t][c], aw[t] >> sh, bw[c] >> sh);
+    }
   }
 }
+
+// Weight-side sources of wave `wave`: tile(wg, t) names the codes, scales and
+// first row of tile t of weight group wg.
+template <typename TileFn>
+__device__ __forceinline__ void pipe_weight_sources(PipeSrc& src, TileFn tile, size_t crow,
+                                                    size_t srow, int wave, int lane) {
+  const int wg = wave >> 1;
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int j = 2 * (wave & 1) + jj;  // block j of the group: tile j / 2, rows 16 (j % 2)..
+    const TileSrc ts = tile(wg, j >> 1);
+    const int wr = 16 * j + (lane >> 2);  // the lane's row within the group
+    const int b = (lane & 3) ^ ((wr >> 2) & 3);
+    src.a[jj] = ts.codes + (size_t)(ts.row0 + 16 * (j & 1)) * crow + (lane >> 2) * kRowC + b * 16;
+    src.adst[jj] = wg * (64 * kRowC) + j * 1024;
+  }
+  const TileSrc ts = tile(wg, wave & 1);
+  src.s = ts.scales + (size_t)(ts.row0 + (lane & 31)) * srow;  // used by lanes 0-31
+  src.sstep = kGroupRow;
+}
+
+// Activation-side sources: tile row `row` reads from rowptr(row) (codes at +0,
+// scales at +scale_off) or, when absent, from the zero page.
+template <typename RowPtr>
+__device__ __forceinline__ void pipe_act_sources(PipeSrc& src, RowPtr rowptr, size_t scale_off,
+                                                 const uint8_t* zero, int wave, int lane) {
+  const int row = 16 * wave + (lane >> 2);
+  const int b = (lane & 3) ^ ((row >> 2) & 3);
+  const uint8_t* rp = rowptr(row);
+  src.b = (rp ? rp : zero) + b * 16;
+  src.bstep = rp ? kRowC : 0;
+  if (lane >= 32) {  // lanes 32-47 load activation scale rows (48-63 load nothing)
+    const uint8_t* sp = rowptr(16 * wave + (lane & 15));
+    src.s = sp ? sp + scale_off : zero;
+    src.sstep = sp ? kGroupRow : 0;
+  }
+}
+
+// This lane's scale words of stage q (4 scale bytes of its rows: weight tile
+// t row r, column tile cb row r), from the group buffer.
+struct StageScales {
+  uint32_t aw[2], bw[4];
+};
 
 // Weight-side sources: wave row wr (0..63) of the stage is row wrow[wr / 32] +
 // wr % 32 of the section at wcodes[wr / 32] / wscales[wr / 32].
@@ -1298,25 +1330,6 @@ __device__ __forceinline__ void pipe_weight_src(Src& src, const uint8_t* const (
   src.as = sbase + (size_t)((t ? wrow[1] : wrow[0]) + rr) * srow;
 }
 
-// Activation-side sources: tile row `row` reads from rowptr(row) (codes at +0,
-// scales at +scale_off) or, when absent, from the zero page.
-template <typename RowPtr>
-__device__ __forceinline__ void pipe_act_src(PipeSrc& src, RowPtr rowptr, size_t scale_off,
-                                             const uint8_t* zero, int wave, int lane) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (2 * wave + j) * 16 + (lane >> 2);
-    const int b = (lane & 3) ^ ((row >> 2) & 3);
-    const uint8_t* rp = rowptr(row);
-    src.b[j] = (rp ? rp : zero) + b * 16;
-    src.bstep[j] = rp ? kRowC : 0;
-  }
-  const int row = 32 * wave + (lane & 31);  // lanes 32-63 issue no activation-scale load
-  const uint8_t* rp = rowptr(row);
-  src.bs = rp ? rp + scale_off : zero;
-  src.bsstep = rp ? kGroupRow : 0;
-}
-
 struct PipeArgs {
   const uint8_t* act;  // gate/up: xq rows by token; down: hq rows by position p
   size_t arow;
@@ -1337,9 +1350,9 @@ struct PipeArgs {
   int S, T;
 };
 
-// Gate/up: N-tile = 128 rows of I; wave w: rows n0 = 32w.. of gate (tile 0)
-// and of up (tile 1); K = H.
-__global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
+// Gate/up: N-tile = 128 rows of I; weight group g: rows n0 = 32g.. of gate
+// (tile 0) and of up (tile 1); K = H.
+__global__ __launch_bounds__(kPipeWaves * kWave, 2) void gateup_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
   int w;
@@ -1355,19 +1368,21 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
     return;
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
   const bool sh = s == p.S;  // the shared expert: row p is token p - A
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
+  const int g = wave & 3, ch = wave >> 2;
   const int H = p.H;
-  const int n0 = tr.nt * 128 + wave * 32;
-  const bool active = n0 < p.I;
-  const int nb = active ? n0 : 0;  // an idle wave still loads (row 0) and meets every barrier
+  const int nt0 = tr.nt * 128;
   const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
-  const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c1};
-  const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s1};
-  const int wrow[2] = {nb, nb};
   PipeSrc src;
-  pipe_weight_src(src, wc, wsc, wrow, (size_t)H / 2, (size_t)H / 32, lane);
-  pipe_act_src(
+  pipe_weight_sources(
+      src,
+      [&](int wg, int t) {
+        return TileSrc{base + (t ? p.off_c1 : p.off_c0), base + (t ? p.off_s1 : p.off_s0),
+                       nt0 + 32 * wg};
+      },
+      (size_t)H / 2, (size_t)H / 32, wave, lane);
+  pipe_act_sources(
       src,
       [&](int row) -> const uint8_t* {
         if (row >= rows) return nullptr;
@@ -1376,22 +1391,23 @@ __global__ __launch_bounds__(256, 2) void gateup_pipe(PipeArgs p) {
         return (a >= 0 && a < p.A) ? p.act + (size_t)(a / p.k) * p.arow : nullptr;
       },
       (size_t)H / 2, p.zero, wave, lane);
-  v16f acc[2][4];
+  v16f acc[2][2];
   pipe_mainloop(smem, src, H / kKc, wave, lane, acc);
-  if (!active) return;
+  const int n0 = nt0 + 32 * g;  // I % 128 == 0 on this path: every group is in range
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int c = 0; c < 2; ++c) {
+    const int cb = 2 * ch + c;
     if (32 * cb < rows) {
       const int lr = 32 * cb + r;
-      swiglu_quant_store32(acc[0][cb], acc[1][cb], hh,
-                         lr < rows ? p.hq + (size_t)(p0 + lr) * p.hrow : nullptr, n0, p.I);
+      swiglu_quant_store32(acc[0][c], acc[1][c], hh,
+                           lr < rows ? p.hq + (size_t)(p0 + lr) * p.hrow : nullptr, n0, p.I);
     }
   }
 }
 
-// Down: N-tile = 256 rows of H; wave w: rows n0 = 64w.. (two 32-row tiles);
-// K = I; the B rows are the slot's hq rows p0.. (contiguous).
-__global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
+// Down: N-tile = 256 rows of H; weight group g: rows n0 = 64g.. (two 32-row
+// tiles); K = I; the B rows are the slot's hq rows p0.. (contiguous).
+__global__ __launch_bounds__(kPipeWaves * kWave, 2) void down_pipe(PipeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kPipeLds];
   TileRef tr;
   if (!tile_of(xcd_work_index(p.items[0] * p.nN), p.nN, kTileM, p.items, p.offsets, p.S, p.A,
@@ -1399,40 +1415,39 @@ __global__ __launch_bounds__(256, 2) void down_pipe(PipeArgs p) {
     return;
   const int s = tr.slot, p0 = tr.p0, rows = tr.rows;
   const bool sh = s == p.S;  // the shared expert: y row = its hq row (A + token)
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int r = lane & 31, hh = lane >> 5;
+  const int g = wave & 3, ch = wave >> 2;
   const int I = p.I;
-  const int n0 = tr.nt * 256 + wave * 64;
+  const int nt0 = tr.nt * 256;
   const uint8_t* base = sh ? p.shared : p.arena + (size_t)s * p.stride;
-  const uint8_t* const wc[2] = {base + p.off_c0, base + p.off_c0};
-  const uint8_t* const wsc[2] = {base + p.off_s0, base + p.off_s0};
-  bool tv[2];
-  int wrow[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    tv[t] = n0 + 32 * t < p.H;  // tiles past H load row 0 and are never stored
-    wrow[t] = tv[t] ? n0 + 32 * t : 0;
-  }
   PipeSrc src;
-  pipe_weight_src(src, wc, wsc, wrow, (size_t)I / 2, (size_t)I / 32, lane);
-  pipe_act_src(
+  pipe_weight_sources(
+      src,
+      [&](int wg, int t) {
+        const int row = nt0 + 64 * wg + 32 * t;  // tiles past H load row 0, never stored
+        return TileSrc{base + p.off_c0, base + p.off_s0, row < p.H ? row : 0};
+      },
+      (size_t)I / 2, (size_t)I / 32, wave, lane);
+  pipe_act_sources(
       src,
       [&](int row) -> const uint8_t* {
         return row < rows ? p.act + (size_t)(p0 + row) * p.arow : nullptr;
       },
       (size_t)I / 2, p.zero, wave, lane);
-  v16f acc[2][4];
+  v16f acc[2][2];
   pipe_mainloop(smem, src, I / kKc, wave, lane, acc);
+  const int n0 = nt0 + 64 * g;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int lr = 32 * cb + r;
+  for (int c = 0; c < 2; ++c) {
+    const int lr = 32 * (2 * ch + c) + r;
     if (lr < rows) {
       const int a = sh ? p0 + lr : p.perm[p0 + lr];
       if (a >= 0 && (sh || a < p.A)) {
         uint16_t* yr = p.y + (size_t)a * p.H;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          if (tv[t]) store_y_bf16(yr, n0 + 32 * t, hh, acc[t][cb]);
+          if (n0 + 32 * t < p.H) store_y_bf16(yr, n0 + 32 * t, hh, acc[t][c]);
       }
     }
   }
@@ -1930,8 +1945,9 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     t.shared = a->shared_expert;
     t.S = S;
     t.T = T;
-    hipExtLaunchKernelGGL(fp6 ? gateup_pipe6 : gateup_pipe, dim3((unsigned)g1), dim3(256), 0,
-                          stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr, 0, t);
+    hipExtLaunchKernelGGL(fp6 ? gateup_pipe6 : gateup_pipe, dim3((unsigned)g1),
+                          dim3(fp6 ? 256 : kPipeWaves * kWave), 0, stream, ev ? ev[1] : nullptr,
+                          ev ? ev[2] : nullptr, 0, t);
     if (defer >= 0) {
       // the deferred slot's tiles, once its bytes are in place: at most one
       // assignment per token, so at most ceil(T / 128) M-tiles
@@ -1942,7 +1958,7 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
       if (fp6)
         gateup_pipe6<<<(unsigned)g3, 256, 0, stream>>>(t);
       else
-        gateup_pipe<<<(unsigned)g3, 256, 0, stream>>>(t);
+        gateup_pipe<<<(unsigned)g3, kPipeWaves * kWave, 0, stream>>>(t);
       t.only = nullptr;
     }
     t.act = hq;
@@ -1953,7 +1969,7 @@ static int experts_launch(const moe_experts_args* a, void* ws_ptr, hipStream_t s
     if (fp6)
       down_pipe6<<<(unsigned)g2, 256, 0, stream>>>(t);
     else
-      down_pipe<<<(unsigned)g2, 256, 0, stream>>>(t);
+      down_pipe<<<(unsigned)g2, kPipeWaves * kWave, 0, stream>>>(t);
     if (!record_stage(ev, 3, stream)) return MOE_EHIP;
   } else {
     // work items: the used slots, found in place, for small slot counts; the
