@@ -641,11 +641,12 @@ def test_batch_invariance_pipelined_path():
         assert moe.rel_l2(one.out_f64()[0], full[t]) <= OUT_REL_L2, t
 
 
-@pytest.mark.parametrize("name", ["prefill", "decode"])
+@pytest.mark.parametrize("name", ["prefill", "decode", "long"])
 def test_deferred_slot_same_output(name):
     """moe_experts_forward with a deferred slot (its gate/up tiles run after
     an event, the other slots' before) gives the same output bit for bit, for
-    the busiest slot, a slot with one tile's worth or less, and an unused one."""
+    the busiest slot, the least used one and an unused one (long: 256-row
+    M-tiles)."""
     import torch
     from resident_expert_routing_amd import runtime as R
     g = gpu_layer(name)
@@ -656,7 +657,8 @@ def test_deferred_slot_same_output(name):
     off = g.routing()["slot_offsets"].astype(np.int64)
     counts = np.diff(off[:g.S + 1])
     busiest = int(np.argmax(counts))
-    small = int(np.flatnonzero((counts > 0) & (counts <= 128))[0])
+    used = np.flatnonzero(counts > 0)
+    small = int(used[np.argmin(counts[used])])
     unused = np.flatnonzero(counts == 0)
     slots = [busiest, small] + ([int(unused[0])] if unused.size else [])
     ev = torch.cuda.Event()
