@@ -1010,7 +1010,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
 // columns each), so the kernels fit 128 VGPRs and every SIMD keeps four waves:
 // a wave stalls handing its loads to the memory pipeline for about half of
 // each stage, and four waves hide more of that than two (gate/up 3 % faster at
-// prefill and 6 % at the long chunk than four-wave workgroups).  The 16-byte
+// the prefill and the long chunk than four-wave workgroups).  The 16-byte
 // block b of a 64-byte stage row r sits at position b ^ ((r >> 2) & 3): a
 // fragment read (32 rows, two blocks) spreads over all 16 four-bank groups,
 // four lanes each.
@@ -1019,7 +1019,7 @@ constexpr int kTileM = 128;                    // assignment rows per work item
 constexpr int kKc = 128;                       // K elements per stage
 constexpr int kRowC = kKc / 2;                 // code bytes per row per stage (64)
 constexpr int kRowS = kKc / 32;                // scale bytes per row per stage (4)
-constexpr int kStageA = 4 * 64 * kRowC;        // weight code rows of the four waves
+constexpr int kStageA = 4 * 64 * kRowC;        // weight code rows of the four weight groups
 constexpr int kStageB = kTileM * kRowC;        // activation code rows
 constexpr int kStage = kStageA + kStageB;      // 24,576 bytes
 constexpr int kRing = 3;
